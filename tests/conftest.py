@@ -1,0 +1,23 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _host_builds():
+    """The CPU reference and the input generator are plain C; build them once if absent."""
+    import oracle
+    import synth
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build(force=True)
+    synth._load()
+    yield
