@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of LRKV factored decode on one MI355X.
+
+One step is one decode step of the whole path on a batch of sequences:
+  append the new token's projected rows -> absorb the query (p = q B^K) ->
+  split-L partial pass -> split merge + B^V epilogue,
+all through the C ABI on one HIP stream, with the inputs resident in HBM.
+Before the timed region the caches hold L - 1 - warmup rows per sequence, so
+the first timed step decodes over exactly L rows; every step appends one row,
+so step k decodes over L + k rows.
+
+Output: one JSON line with the metric (cached-token·heads/s over the timed
+steps), achieved HBM bandwidth, the roofline of the dominant kernel (the
+split pass, timed live with HIP events on the launch stream) and the CPU
+reference timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LRKV decode cached-token·heads/s and achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_digest() -> str:
+    import glob
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "rank_shared_kv_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, launch_bytes: float):
+    """HBM traffic per split launch from the committed rocprofv3 counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_digest = re.search(r"kernel sources digest:\s*`?([0-9a-f]{16})", text)
+    m_bytes = re.search(r"HBM bytes per split launch \(scaled\):\s*([0-9.eE+]+)", text)
+    if not m_digest or not m_bytes or m_digest.group(1) != kernel_sources_digest():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, lens, budget_s: float):
+    """The fp64 CPU reference, as it stands, on (b, h) pairs of this workload until ~budget_s of wall time."""
+    import numpy as np
+    import oracle
+    import synth
+
+    threads = oracle._threads(None)
+    done_tokens, elapsed, npairs = 0, 0.0, 0
+    seqs = list(range(w.batch))
+    for b in seqs:
+        n = int(lens[b])
+        s = synth.gen_sequence(w, 0, b, n)
+        q = synth.gen_small(w, 0, "q")[b:b + 1]
+        Bk, Bv = synth.gen_small(w, 0, "B_k"), synth.gen_small(w, 0, "B_v")
+        one = np.array([n], dtype=np.int32)
+        heads = list(range(w.H))
+        step = max(1, threads)
+        for i in range(0, len(heads), step):
+            pairs = [(0, h) for h in heads[i:i + step]]
+            t0 = time.perf_counter()
+            oracle.lrkv_decode(w.dtype, q, s["k_shared"][None], s["v_shared"][None], s["z_k"][None], s["z_v"][None],
+                               Bk, Bv, one, pairs=pairs, threads=threads)
+            elapsed += time.perf_counter() - t0
+            done_tokens += n * len(pairs)
+            npairs += len(pairs)
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    return {"value": done_tokens / elapsed, "unit": "cached-token·heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"{npairs} of {w.batch * w.H} (sequence, head) pairs of this workload at its full lengths "
+                      f"({done_tokens} cached-token·heads, {elapsed:.1f} s wall, fp64 rebuild-then-attend, "
+                      f"OpenMP over pairs)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_context")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU-reference wall time (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rank_shared_kv_amd as lk
+    import synth
+    from synth import device as sdev
+
+    w = synth.WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    lens_full = synth.seq_lengths(w)
+    L_cap = int(lens_full.max()) + K
+    start_lens = lens_full - 1 - W
+    assert int(start_lens.min()) >= 0
+    log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
+        f"steps={K} warmup={W}")
+    t0 = time.time()
+    dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens_full)
+    dev["seq_lens"].copy_(torch.from_numpy(start_lens.astype(np.int32)).cuda())
+    rows = sdev.new_rows(w)
+    torch.cuda.synchronize()
+    log(f"bench: inputs resident in HBM ({time.time() - t0:.1f} s to generate and copy)")
+
+    dtype_code = lk.LRKV_F32 if w.dtype == "f32" else lk.LRKV_BF16
+    dims = lk.make_dims(w.batch, w.H, w.d_h, w.r, L_cap, dtype_code)
+    cache = lk.make_cache(dev["k_shared"], dev["v_shared"], dev["z_k"] if w.r else None,
+                          dev["z_v"] if w.r else None, dev["seq_lens"])
+    max_len = L_cap
+    nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
+    ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+    p = torch.empty((w.batch, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, w.H, w.d_h), dtype=torch.float32, device="cuda")
+    S, chunk = lk.lrkv_decode_num_splits(dims, max_len)
+    stream = torch.cuda.current_stream()
+    pp = p if w.r else None
+    bv = dev["B_v"] if w.r else None
+    zk_new = rows["zk_new"] if w.r else None
+    zv_new = rows["zv_new"] if w.r else None
+
+    ev_pairs = []
+
+    def step(timed: bool):
+        lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+        if w.r:
+            lk.lrkv_absorb_query(dims, dev["q"], dev["B_k"], p, stream)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        lk.lrkv_decode_partial(dims, cache, max_len, dev["q"], pp, ws, nbytes, stream)
+        if timed:
+            e1.record(stream)
+            ev_pairs.append((e0, e1))
+        lk.lrkv_decode_merge(dims, dev["seq_lens"], max_len, bv, out, ws, nbytes, stream)
+
+    for _ in range(W):
+        step(False)
+    torch.cuda.synchronize()
+    assert dev["seq_lens"].cpu().numpy().tolist() == (lens_full - 1).tolist()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(K):
+        step(True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    split_ms = [a.elapsed_time(b) for a, b in ev_pairs]
+    final_lens = dev["seq_lens"].cpu().numpy()
+    assert final_lens.tolist() == (lens_full - 1 + K).tolist()
+    assert bool(torch.isfinite(out).all())
+
+    # work per timed step k: every sequence decodes over lens_full + k rows
+    token_heads = sum(int(np.sum(lens_full + k, dtype=np.int64)) * w.H for k in range(K))
+    value = token_heads / (total_ms / 1e3)
+    s_bytes = w.elem_bytes
+    cache_bytes_per_step = [lk.lrkv_cache_bytes(dims, (lens_full + k).tolist()) for k in range(K)]
+    q_bytes = w.batch * w.H * w.d_h * s_bytes
+    p_bytes = w.batch * w.H * w.r * 4
+    basis_bytes = 2 * w.H * w.d_h * w.r * s_bytes
+    out_bytes = w.batch * w.H * w.d_h * 4
+    step_bytes = sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes
+    split_bytes = sum(cache_bytes_per_step) / K + q_bytes + p_bytes
+    split_avg_ms = sum(split_ms) / len(split_ms)
+    split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
+    step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
+    flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
+    mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    traffic = read_traffic(w.name, split_bytes)
+    log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); split pass {split_avg_ms * 1e3:.1f} us "
+        f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"bench: timing the CPU reference (~{args.cpu_budget:.0f} s)")
+        cpu = cpu_baseline(w, lens_full, args.cpu_budget)
+        log(f"bench: CPU reference {cpu['value']:.3e} token·heads/s on {cpu['cores']} threads")
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "cached-token·heads/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+                   "L": int(lens_full.max()), "lengths": "uniform" if w.ragged_lo is None else
+                   f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
+                   "splits": S, "chunk_tokens": chunk},
+        "hbm_gbps_step": step_gbps,
+        "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": split_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic, "kernel": "split pass (lrkv_decode_partial)",
+                     "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
+        "mfma_util_shared_score": mfma_util,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * lrkv.h -- C ABI of the LRKV (low-rank key-value attention) decode library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method: every head's key and value projections are a shared dense
+ * projection plus a per-head rank-r residual, W_h = W_shared + U_h B_h^T
+ * ("Low-Rank Key Value Attention: Chinese reading notes", sec. 2.1,
+ * Eqs. (2)-(5); "Low-Rank Key Value Attention | What a shared cache can
+ * preserve", sec. 3).  The decode cache therefore holds, per token, one shared
+ * key row and one shared value row (d_h wide each) and, per head, a key latent
+ * and a value latent (r wide each).  Decoding never rebuilds per-head keys or
+ * values: it absorbs B^K into the query, adds the shared and private logits
+ * before a single softmax, and maps the weighted private value sum through
+ * B^V once per head (reading notes sec. 2.4, Eqs. (6)-(7); review sec. 3,
+ * "Associative decode" and Algorithm 2).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * Pointers named "device" point to GPU memory allocated by the caller; the
+ * library never allocates, frees or retains them after the call returns.
+ * All tensors are dense, row-major, without padding between rows.  Unless a
+ * function says otherwise, device pointers must be 16-byte aligned.
+ * Element types: q, cache rows and B bases share one dtype (lrkv_dtype);
+ * p and out are always fp32; seq_lens is int32.  Arithmetic is fp32 with fp32
+ * accumulation for both dtypes.
+ * `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ * call only enqueues work on that stream and never synchronises; device
+ * faults surface at the caller's next synchronisation.
+ * Argument checks run on the host before any HIP call; a rejected call
+ * enqueues nothing.  Functions return LRKV_OK or an error code; the text of
+ * the last error on the calling thread is available from lrkv_last_error().
+ * The library has no global mutable state besides that per-thread message,
+ * so calls from several threads on different streams are independent.
+ */
+#ifndef LRKV_H
+#define LRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LRKV_OK = 0,
+    LRKV_ERR_INVALID_ARG = 1, /* NULL pointer, bad size, misaligned pointer, max_len > L_cap, ... */
+    LRKV_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement (see lrkv_decode) */
+    LRKV_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than lrkv_decode_workspace_bytes */
+    LRKV_ERR_HIP = 4          /* a kernel launch failed */
+} lrkv_status;
+
+typedef enum {
+    LRKV_F32 = 0,  /* IEEE binary32 */
+    LRKV_BF16 = 1  /* bfloat16 (upper half of binary32) */
+} lrkv_dtype;
+
+/* Problem sizes, in the pages' notation (reading notes sec. 2.1 symbol table). */
+typedef struct {
+    int32_t batch; /* sequences, >= 1 */
+    int32_t H;     /* query heads, >= 1 */
+    int32_t d_h;   /* head width, >= 1 */
+    int32_t r;     /* residual rank, >= 0; r = 0 is MQA-style sharing of one K/V */
+    int32_t L_cap; /* rows allocated per sequence in every cache tensor, >= 1 */
+    int32_t dtype; /* lrkv_dtype of q, the cache rows and B^K, B^V */
+} lrkv_dims;
+
+/* The factored cache of one layer (review sec. 3, Algorithm 1): device pointers.
+ *   k_shared, v_shared  [batch][L_cap][d_h]   rows x W_shared^K, x W_shared^V
+ *   z_k, z_v            [batch][H][L_cap][r]  latents x U_h^K, x U_h^V; may be NULL iff r == 0
+ *   seq_lens            [batch] int32         live rows per sequence: rows 0 .. seq_lens[b]-1
+ * For decode the current query's own token must already be appended, so
+ * seq_lens[b] counts it; every live row is visible to the query. */
+typedef struct {
+    void* k_shared;
+    void* v_shared;
+    void* z_k;
+    void* z_v;
+    int32_t* seq_lens;
+} lrkv_cache;
+
+/* Absorb the key basis into the query: p[b][h][i] = sum_c q[b][h][c] * B_k[h][c][i]
+ * (reading notes sec. 2.4 Eq. (6); review sec. 3, Algorithm 2: one small
+ * product per head per step).
+ *   q    device [batch][H][d_h]  (dims->dtype)
+ *   B_k  device [H][d_h][r]      (dims->dtype)
+ *   p    device [batch][H][r]    fp32 out
+ * r == 0: nothing to do, returns LRKV_OK (q, B_k, p may be NULL). */
+lrkv_status lrkv_absorb_query(const lrkv_dims* dims, const void* q, const void* B_k, float* p, void* stream);
+
+/* Append one token's projected rows to every sequence (review sec. 3,
+ * Algorithm 1: shared rows once, both private latents per head at the
+ * matching token index; reading notes sec. 2.3).
+ *   k_new, v_new    device [batch][d_h]      (dims->dtype)
+ *   zk_new, zv_new  device [batch][H][r]     (dims->dtype); may be NULL iff r == 0
+ * For each b the row is written at index seq_lens[b] (read on the device) and
+ * seq_lens[b] is then incremented on the device.  A sequence that is already
+ * full (seq_lens[b] >= L_cap) or has a negative length is left unchanged and
+ * nothing is written for it. */
+lrkv_status lrkv_cache_append(const lrkv_dims* dims, const lrkv_cache* cache, const void* k_new, const void* v_new,
+                              const void* zk_new, const void* zv_new, void* stream);
+
+/* Bytes of device workspace lrkv_decode / lrkv_decode_partial need for these
+ * dims and this max_len.  Host arithmetic only.  Returns 0 for invalid dims. */
+size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
+
+/* Number of sequence splits (S) the decode uses for these dims and max_len,
+ * and the tokens per split (*chunk_tokens, may be NULL).  Host arithmetic only.
+ * Returns 0 for invalid dims or max_len == 0. */
+int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens);
+
+/* One decode step against the factored history (review sec. 3, Algorithm 2
+ * and its fused online-softmax form; reading notes sec. 2.4 Eqs. (6)-(7)):
+ *   s_j = (q_h . k_shared[j] + p_h . z_k[h][j]) / sqrt(d_h),  j < seq_lens[b]
+ *   a   = softmax(s)   (one softmax over the summed logits)
+ *   out[b][h] = sum_j a_j v_shared[j] + (sum_j a_j z_v[h][j]) (B_v[h])^T
+ * Inputs:
+ *   cache      the factored cache; seq_lens[b] must lie in [0, max_len]
+ *   max_len    host upper bound of seq_lens, 0 <= max_len <= L_cap
+ *   q          device [batch][H][d_h] (dims->dtype)
+ *   p          device [batch][H][r] fp32, from lrkv_absorb_query for this q and B_k; may be NULL iff r == 0
+ *   B_v        device [H][d_h][r] (dims->dtype); may be NULL iff r == 0
+ *   out        device [batch][H][d_h] fp32 (written completely; 0 for a sequence with no live rows)
+ *   workspace  device, >= lrkv_decode_workspace_bytes(dims, max_len) bytes, 256-byte aligned
+ * Lengths outside [0, max_len] are clamped into it on the device (memory safe,
+ * result then undefined).  The work is split along the sequence into S chunks
+ * whose partial softmax states are merged in a fixed order, so results are
+ * bitwise reproducible for fixed dims and max_len.
+ * Supported: d_h <= 256, r <= 256, H * (d_h + r + 2) * 4 <= 64 KiB; the fast
+ * bf16 kernels cover d_h in {64, 128}, r in {0, 8, 16, 32, 48, 64}, H a multiple of
+ * 8 up to 32; other valid shapes use the general kernels. */
+lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                        const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* The two halves of lrkv_decode, for callers that time or distribute them.
+ * lrkv_decode_partial writes the per-split softmax states (running max in
+ * log2 units, denominator, shared-value sum, private-value sum) to the
+ * workspace; lrkv_decode_merge combines them in split order and applies B_v.
+ * Both must be given the same dims, cache.seq_lens contents and max_len. */
+lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                                const float* p, void* workspace, size_t workspace_bytes, void* stream);
+lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
+                              float* out, const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Cache payload in bytes, counted as the pages count it (numel x element size
+ * of the live rows): 2 * s * sum_b L_b * (d_h + H * r), s = 4 (fp32) or 2 (bf16)
+ * (reading notes sec. 2.5 Eqs. (8)-(9); review sec. 4).  host_seq_lens is a
+ * host array [batch]; NULL counts L_cap rows for every sequence.  Negative
+ * lengths count as 0 and lengths above L_cap as L_cap.  Returns 0 for invalid dims. */
+uint64_t lrkv_cache_bytes(const lrkv_dims* dims, const int32_t* host_seq_lens);
+
+/* Static text for a status code. */
+const char* lrkv_status_str(lrkv_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* lrkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRKV_H */

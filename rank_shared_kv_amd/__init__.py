@@ -1,0 +1,164 @@
+"""Python binding of the LRKV decode library (liblrkv.so, C ABI in include/lrkv.h).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+behind the C ABI.  Tensors are passed as torch tensors on the GPU (their
+data pointers are handed over) or as raw integer device addresses; `stream`
+is a torch.cuda.Stream, a raw hipStream_t integer, or None for torch's
+current stream.  There is no CPU fallback: if the library is not built the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblrkv.so")
+
+LRKV_OK = 0
+LRKV_ERR_INVALID_ARG = 1
+LRKV_ERR_UNSUPPORTED = 2
+LRKV_ERR_WORKSPACE = 3
+LRKV_ERR_HIP = 4
+LRKV_F32 = 0
+LRKV_BF16 = 1
+
+EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
+            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_cache_bytes", "lrkv_status_str",
+            "lrkv_last_error")
+
+
+class LrkvError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func}: {status_name(status)}: {detail}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    """lrkv_dims: batch, H, d_h, r, L_cap, dtype."""
+    _fields_ = [("batch", ctypes.c_int32), ("H", ctypes.c_int32), ("d_h", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("L_cap", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Cache(ctypes.Structure):
+    """lrkv_cache: device pointers k_shared, v_shared, z_k, z_v, seq_lens."""
+    _fields_ = [("k_shared", ctypes.c_void_p), ("v_shared", ctypes.c_void_p), ("z_k", ctypes.c_void_p),
+                ("z_v", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree liblrkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python rank_shared_kv_amd/_build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        D, C = ctypes.POINTER(Dims), ctypes.POINTER(Cache)
+        sig = {
+            "lrkv_absorb_query": ([D, vp, vp, vp, vp], ctypes.c_int),
+            "lrkv_cache_append": ([D, C, vp, vp, vp, vp, vp], ctypes.c_int),
+            "lrkv_decode_workspace_bytes": ([D, i32], sz),
+            "lrkv_decode_num_splits": ([D, i32, ctypes.POINTER(i32)], i32),
+            "lrkv_decode": ([D, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_decode_partial": ([D, C, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_cache_bytes": ([D, vp], ctypes.c_uint64),
+            "lrkv_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "lrkv_last_error": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return lib().lrkv_status_str(status).decode()
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not getattr(x, "is_cuda", False):
+            raise ValueError("tensor arguments must live on the GPU")
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):  # numpy array (host arrays only where the C ABI says host)
+        return x.ctypes.data
+    raise TypeError(f"cannot pass {type(x)} as a pointer")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, func: str):
+    if status != LRKV_OK:
+        raise LrkvError(status, func, lib().lrkv_last_error().decode())
+
+
+def make_dims(batch: int, H: int, d_h: int, r: int, L_cap: int, dtype: int) -> Dims:
+    return Dims(batch, H, d_h, r, L_cap, dtype)
+
+
+def make_cache(k_shared, v_shared, z_k, z_v, seq_lens) -> Cache:
+    return Cache(_ptr(k_shared), _ptr(v_shared), _ptr(z_k), _ptr(z_v), _ptr(seq_lens))
+
+
+def lrkv_absorb_query(dims: Dims, q, B_k, p, stream=None) -> None:
+    _check(lib().lrkv_absorb_query(ctypes.byref(dims), _ptr(q), _ptr(B_k), _ptr(p), _stream(stream)),
+           "lrkv_absorb_query")
+
+
+def lrkv_cache_append(dims: Dims, cache: Cache, k_new, v_new, zk_new, zv_new, stream=None) -> None:
+    _check(lib().lrkv_cache_append(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(zk_new),
+                                   _ptr(zv_new), _stream(stream)), "lrkv_cache_append")
+
+
+def lrkv_decode_workspace_bytes(dims: Dims, max_len: int) -> int:
+    return int(lib().lrkv_decode_workspace_bytes(ctypes.byref(dims), max_len))
+
+
+def lrkv_decode_num_splits(dims: Dims, max_len: int) -> Tuple[int, int]:
+    chunk = ctypes.c_int32(0)
+    s = lib().lrkv_decode_num_splits(ctypes.byref(dims), max_len, ctypes.byref(chunk))
+    return int(s), int(chunk.value)
+
+
+def lrkv_decode(dims: Dims, cache: Cache, max_len: int, q, p, B_v, out, workspace, workspace_bytes: int,
+                stream=None) -> None:
+    _check(lib().lrkv_decode(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(q), _ptr(p), _ptr(B_v), _ptr(out),
+                             _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode")
+
+
+def lrkv_decode_partial(dims: Dims, cache: Cache, max_len: int, q, p, workspace, workspace_bytes: int,
+                        stream=None) -> None:
+    _check(lib().lrkv_decode_partial(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(q), _ptr(p),
+                                     _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_partial")
+
+
+def lrkv_decode_merge(dims: Dims, seq_lens, max_len: int, B_v, out, workspace, workspace_bytes: int,
+                      stream=None) -> None:
+    _check(lib().lrkv_decode_merge(ctypes.byref(dims), _ptr(seq_lens), max_len, _ptr(B_v), _ptr(out),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_merge")
+
+
+def lrkv_cache_bytes(dims: Dims, host_seq_lens: Optional[Sequence[int]] = None) -> int:
+    if host_seq_lens is None:
+        return int(lib().lrkv_cache_bytes(ctypes.byref(dims), None))
+    arr = (ctypes.c_int32 * len(host_seq_lens))(*[int(x) for x in host_seq_lens])
+    return int(lib().lrkv_cache_bytes(ctypes.byref(dims), ctypes.cast(arr, ctypes.c_void_p)))

@@ -1,0 +1,91 @@
+// Query absorption and cache append.
+//
+// absorb:  p_h = q_h B^K_h, one d_h x r product per (sequence, head) and step
+//          ("Low-Rank Key Value Attention: Chinese reading notes", sec. 2.4
+//          Eq. (6); "Low-Rank Key Value Attention | What a shared cache can
+//          preserve", sec. 3, Algorithm 2).  fp32 result, fp32 accumulation in
+//          a fixed order over d_h.
+// append:  write one token's shared rows and per-head latents at index
+//          seq_lens[b] and advance seq_lens[b] (review sec. 3, Algorithm 1;
+//          reading notes sec. 2.3).
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+template <typename T>
+__global__ void __launch_bounds__(64) absorb_kernel(int H, int d_h, int r, const T* __restrict__ q,
+                                                    const T* __restrict__ B_k, float* __restrict__ p) {
+    const int bh = blockIdx.x;  // b * H + h
+    const int h = bh % H;
+    const T* qrow = q + (size_t)bh * d_h;
+    const T* basis = B_k + (size_t)h * d_h * r;
+    for (int i = threadIdx.x; i < r; i += blockDim.x) {
+        float acc = 0.f;
+        for (int c = 0; c < d_h; ++c) acc = fmaf(elem<T>::load(qrow, c), elem<T>::load(basis, (size_t)c * r + i), acc);
+        p[(size_t)bh * r + i] = acc;
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int L_cap, T* __restrict__ k_shared,
+                                                     T* __restrict__ v_shared, T* __restrict__ z_k,
+                                                     T* __restrict__ z_v, int32_t* __restrict__ seq_lens,
+                                                     const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                                     const T* __restrict__ zk_new, const T* __restrict__ zv_new) {
+    __shared__ int row;
+    const int b = blockIdx.x;
+    if (threadIdx.x == 0) {
+        const int L = seq_lens[b];
+        row = (L >= 0 && L < L_cap) ? L : -1;
+    }
+    __syncthreads();
+    const int j = row;
+    if (j < 0) return;  // full or invalid: nothing written, length unchanged
+    const size_t srow = ((size_t)b * L_cap + j) * d_h;
+    for (int c = threadIdx.x; c < d_h; c += blockDim.x) {
+        k_shared[srow + c] = k_new[(size_t)b * d_h + c];
+        v_shared[srow + c] = v_new[(size_t)b * d_h + c];
+    }
+    for (int idx = threadIdx.x; idx < H * r; idx += blockDim.x) {
+        const int h = idx / r, i = idx - h * r;
+        const size_t dst = (((size_t)b * H + h) * L_cap + j) * r + i;
+        const size_t src = ((size_t)b * H + h) * r + i;
+        z_k[dst] = zk_new[src];
+        z_v[dst] = zv_new[src];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) seq_lens[b] = j + 1;
+}
+
+}  // namespace
+
+hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
+                         hipStream_t stream) {
+    dim3 grid(batch * H), block(64);
+    if (dtype == 0)
+        hipLaunchKernelGGL(absorb_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
+                           (const float*)B_k, p);
+    else
+        hipLaunchKernelGGL(absorb_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
+                           (const uint16_t*)B_k, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype, void* k_shared, void* v_shared,
+                         void* z_k, void* z_v, int32_t* seq_lens, const void* k_new, const void* v_new,
+                         const void* zk_new, const void* zv_new, hipStream_t stream) {
+    dim3 grid(batch), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(append_kernel<float>, grid, block, 0, stream, H, d_h, r, L_cap, (float*)k_shared,
+                           (float*)v_shared, (float*)z_k, (float*)z_v, seq_lens, (const float*)k_new,
+                           (const float*)v_new, (const float*)zk_new, (const float*)zv_new);
+    else
+        hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, L_cap, (uint16_t*)k_shared,
+                           (uint16_t*)v_shared, (uint16_t*)z_k, (uint16_t*)z_v, seq_lens, (const uint16_t*)k_new,
+                           (const uint16_t*)v_new, (const uint16_t*)zk_new, (const uint16_t*)zv_new);
+    return hipGetLastError();
+}
+
+}  // namespace lrkv

@@ -1,0 +1,147 @@
+// General split kernel for LRKV decode: any supported (d_h, r, H), fp32 or
+// bf16 inputs, fp32 arithmetic.  Used for fp32 problems and for shapes the
+// MFMA kernel does not cover.
+//
+// One workgroup owns one (sequence b, split of `chunk` tokens) for all H
+// heads.  Per tile of kTile tokens the shared key/value rows are staged once
+// in LDS (as fp32) and reused by every head; each head then
+//   scores  s_j = (q_h . k_j + p_h . z^K_{h,j}) * log2(e)/sqrt(d_h)
+//   updates its running max, denominator and both numerators (online softmax)
+// -- the fused single-softmax form of "Low-Rank Key Value Attention | What a
+// shared cache can preserve", sec. 3 (paragraph after Algorithm 2), of the
+// summed-logit score in "Low-Rank Key Value Attention: Chinese reading notes",
+// sec. 2.4 Eqs. (6)-(7).  The running state of all heads lives in LDS; the
+// split's final state is written to the workspace for the merge kernel.
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+constexpr int kTile = 32;     // tokens per tile (lanes 0..31 and 32..63 split each dot product)
+constexpr int kThreads = 256;  // 4 waves
+
+__host__ __device__ inline size_t general_lds_floats(int H, int d_h, int r) {
+    return (size_t)kTile * (d_h + 1)      // K tile, padded rows
+           + (size_t)kTile * d_h          // V tile
+           + (size_t)H * (d_h + r)        // numerators
+           + 2 * (size_t)H                // running max, denominator
+           + 4 * (size_t)kTile;           // per-wave weights
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
+    extern __shared__ float smem[];
+    const int H = a.H, D = a.d_h, R = a.r, rec = partial_record_floats(D, R);
+    float* Kt = smem;                          // [kTile][D + 1]
+    float* Vt = Kt + kTile * (D + 1);          // [kTile][D]
+    float* acc = Vt + kTile * D;               // [H][D + R]
+    float* mrow = acc + (size_t)H * (D + R);   // [H]
+    float* lrow = mrow + H;                    // [H]
+    float* ebuf = lrow + H;                    // [4][kTile]
+
+    const int b = blockIdx.y, split = blockIdx.x;
+    int Lb = a.seq_lens[b];
+    Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
+    const int t_begin = split * a.chunk;
+    if (t_begin >= Lb) return;  // no live rows in this split; the merge skips it
+    const int t_end = min(t_begin + a.chunk, Lb);
+
+    const T* ks = (const T*)a.k_shared + (size_t)b * a.L_cap * D;
+    const T* vs = (const T*)a.v_shared + (size_t)b * a.L_cap * D;
+    const T* zk = (const T*)a.z_k;
+    const T* zv = (const T*)a.z_v;
+    const T* q = (const T*)a.q;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float scale = kLog2e / sqrtf((float)D);
+
+    for (int i = tid; i < H * (D + R); i += kThreads) acc[i] = 0.f;
+    for (int i = tid; i < H; i += kThreads) {
+        mrow[i] = -INFINITY;
+        lrow[i] = 0.f;
+    }
+
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+        const int nvalid = min(kTile, t_end - t0);
+        __syncthreads();  // previous tile fully consumed (and state initialised)
+        for (int idx = tid; idx < kTile * D; idx += kThreads) {
+            const int t = idx / D, c = idx - t * D;
+            const int row = t0 + (t < nvalid ? t : nvalid - 1);  // stay on live rows
+            Kt[t * (D + 1) + c] = elem<T>::load(ks, (size_t)row * D + c);
+            Vt[t * D + c] = elem<T>::load(vs, (size_t)row * D + c);
+        }
+        __syncthreads();
+
+        const int t = lane & 31, half = lane >> 5;
+        const bool live = t < nvalid;
+        const int c_lo = half * ((D + 1) / 2), c_hi = min(D, (half + 1) * ((D + 1) / 2));
+        const int i_lo = half * ((R + 1) / 2), i_hi = min(R, (half + 1) * ((R + 1) / 2));
+        for (int h = wave; h < H; h += kThreads / 64) {
+            const size_t bh = (size_t)b * H + h;
+            const size_t zrow = (bh * a.L_cap + (size_t)(t0 + (live ? t : 0))) * R;
+            // score: shared part on the LDS tile, private part on the latent row
+            float sc = 0.f;
+            for (int c = c_lo; c < c_hi; ++c) sc = fmaf(elem<T>::load(q, bh * D + c), Kt[t * (D + 1) + c], sc);
+            for (int i = i_lo; i < i_hi; ++i) sc = fmaf(a.p[bh * R + i], elem<T>::load(zk, zrow + i), sc);
+            sc += __shfl_xor(sc, 32);
+            const float s2 = live ? sc * scale : -INFINITY;
+            float tmax = s2;
+            for (int o = 16; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+            const float m_old = mrow[h];
+            const float m_new = fmaxf(m_old, tmax);
+            const float alpha = fast_exp2(m_old - m_new);
+            const float e = live ? fast_exp2(s2 - m_new) : 0.f;
+            float esum = e;
+            for (int o = 16; o >= 1; o >>= 1) esum += __shfl_xor(esum, o);
+            if (lane < kTile) ebuf[wave * kTile + lane] = e;
+            wave_lds_sync();
+            if (lane == 0) {
+                mrow[h] = m_new;
+                lrow[h] = alpha * lrow[h] + esum;
+            }
+            float* acc_h = acc + (size_t)h * (D + R);
+            for (int c = lane; c < D; c += 64) {
+                float sum = 0.f;
+                for (int u = 0; u < nvalid; ++u) sum = fmaf(ebuf[wave * kTile + u], Vt[u * D + c], sum);
+                acc_h[c] = alpha * acc_h[c] + sum;
+            }
+            for (int i = lane; i < R; i += 64) {
+                float sum = 0.f;
+                const size_t z0 = (bh * a.L_cap + (size_t)t0) * R + i;
+                for (int u = 0; u < nvalid; ++u) sum = fmaf(ebuf[wave * kTile + u], elem<T>::load(zv, z0 + (size_t)u * R), sum);
+                acc_h[D + i] = alpha * acc_h[D + i] + sum;
+            }
+            wave_lds_sync();  // ebuf reused by this wave's next head
+        }
+    }
+    __syncthreads();
+    float* out = a.ws + ((size_t)b * a.num_splits + split) * H * rec;
+    for (int idx = tid; idx < H * rec; idx += kThreads) {
+        const int h = idx / rec, k = idx - h * rec;
+        float v = 0.f;
+        if (k < D + R) v = acc[(size_t)h * (D + R) + k];
+        else if (k == D + R) v = mrow[h];
+        else if (k == D + R + 1) v = lrow[h];
+        out[idx] = v;
+    }
+}
+
+}  // namespace
+
+size_t general_lds_bytes(int H, int d_h, int r) { return general_lds_floats(H, d_h, r) * sizeof(float); }
+
+bool general_path_supports(int H, int d_h, int r) {
+    return d_h >= 1 && d_h <= 256 && r >= 0 && r <= 256 && H >= 1 && general_lds_bytes(H, d_h, r) <= 65536;
+}
+
+hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream) {
+    dim3 grid(a.num_splits, a.batch), block(kThreads);
+    const size_t lds = general_lds_bytes(a.H, a.d_h, a.r);
+    if (a.dtype == 0)
+        hipLaunchKernelGGL(split_general_kernel<float>, grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL(split_general_kernel<uint16_t>, grid, block, lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace lrkv

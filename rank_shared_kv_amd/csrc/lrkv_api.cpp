@@ -1,0 +1,303 @@
+// C ABI of the LRKV decode library: argument checks, split planning and
+// kernel launches.  Everything here is host code; no HIP call is made before
+// a call's arguments have been checked, and nothing runs at load time.
+#include "../../include/lrkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+lrkv_status fail(lrkv_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+lrkv_status ok() {
+    g_last_error[0] = '\0';
+    return LRKV_OK;
+}
+
+lrkv_status hip_fail(hipError_t e, const char* what) {
+    return fail(LRKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dims_valid(const lrkv_dims* d) {
+    return d && d->batch >= 1 && d->batch <= 65535 && d->H >= 1 && d->H <= 1024 && d->d_h >= 1 && d->d_h <= 4096 &&
+           d->r >= 0 && d->r <= 4096 && d->L_cap >= 1 && d->L_cap <= (1 << 28) &&
+           (d->dtype == LRKV_F32 || d->dtype == LRKV_BF16);
+}
+
+lrkv_status check_dims(const lrkv_dims* d) {
+    if (!d) return fail(LRKV_ERR_INVALID_ARG, "dims is NULL");
+    if (!dims_valid(d))
+        return fail(LRKV_ERR_INVALID_ARG, "invalid dims (batch=%d H=%d d_h=%d r=%d L_cap=%d dtype=%d)", d->batch, d->H,
+                    d->d_h, d->r, d->L_cap, d->dtype);
+    return LRKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+lrkv_status need_ptr(const void* p, const char* name) {
+    if (!p) return fail(LRKV_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(LRKV_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return LRKV_OK;
+}
+
+#define LRKV_TRY(expr)                  \
+    do {                                \
+        lrkv_status _s = (expr);        \
+        if (_s != LRKV_OK) return _s;   \
+    } while (0)
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    long x = strtol(v, &end, 10);
+    return (end && *end == '\0' && x > 0 && x < (1L << 30)) ? (int)x : dflt;
+}
+
+// Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes
+// are known on the host without a device.  The token tile is the kernel's
+// unit of work; a split is a whole number of tiles.  The number of splits is
+// chosen so the split kernel launches about `target` workgroups in total
+// (MI355X has 256 CUs; a few workgroups per CU keep its memory pipes busy),
+// and never more than kMaxSplits per sequence.  The plan does not depend on r
+// so that problems differing only in rank reduce in the same order.
+constexpr int kMaxSplits = 4096;
+
+bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
+    using namespace lrkv;
+    SplitPlan p{};
+    if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype)) {
+        p.path = SplitPath::kMfmaBf16;
+        p.waves = env_int("LRKV_WAVES", 4);
+        if (p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8) p.waves = 4;
+    } else if (general_path_supports(d.H, d.d_h, d.r)) {
+        p.path = SplitPath::kGeneral;
+        p.waves = 4;
+    } else {
+        return false;
+    }
+    const int tile = (p.path == SplitPath::kMfmaBf16) ? 32 * p.waves : 32;
+    if (max_len <= 0) {
+        p.chunk = tile;
+        p.num_splits = 0;
+        *out = p;
+        return true;
+    }
+    const long tiles_per_seq = (max_len + tile - 1) / tile;
+    const long total_tiles = tiles_per_seq * d.batch;
+    const int target = env_int("LRKV_TARGET_WGS", 1024);
+    long tiles_per_split = (total_tiles + target - 1) / target;
+    tiles_per_split = std::max<long>(tiles_per_split, (tiles_per_seq + kMaxSplits - 1) / kMaxSplits);
+    tiles_per_split = std::max<long>(1, std::min(tiles_per_split, tiles_per_seq));
+    const int forced = env_int("LRKV_CHUNK", 0);
+    if (forced > 0) tiles_per_split = std::max<long>(1, std::min<long>((forced + tile - 1) / tile, tiles_per_seq));
+    p.chunk = (int)(tiles_per_split * tile);
+    p.num_splits = (int)((max_len + p.chunk - 1) / p.chunk);
+    if (p.num_splits > kMaxSplits) return false;
+    *out = p;
+    return true;
+}
+
+size_t workspace_bytes(const lrkv_dims& d, const lrkv::SplitPlan& p) {
+    return sizeof(float) * (size_t)d.batch * (size_t)p.num_splits * (size_t)d.H *
+           (size_t)lrkv::partial_record_floats(d.d_h, d.r);
+}
+
+lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan) {
+    LRKV_TRY(check_dims(dims));
+    if (max_len < 0 || max_len > dims->L_cap)
+        return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
+    if (!plan_split(*dims, max_len, plan))
+        return fail(LRKV_ERR_UNSUPPORTED, "no kernel for H=%d d_h=%d r=%d dtype=%d", dims->H, dims->d_h, dims->r,
+                    dims->dtype);
+    return LRKV_OK;
+}
+
+lrkv_status check_workspace(const lrkv_dims& d, const lrkv::SplitPlan& p, const void* ws, size_t ws_bytes) {
+    const size_t need = workspace_bytes(d, p);
+    if (need == 0) return LRKV_OK;
+    if (!ws) return fail(LRKV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(LRKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (ws_bytes < need) return fail(LRKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+    return LRKV_OK;
+}
+
+lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, const void* q, const float* p,
+                        void* ws, const lrkv::SplitPlan& plan, hipStream_t stream) {
+    using namespace lrkv;
+    if (plan.num_splits == 0) return LRKV_OK;
+    DecodeArgs a{};
+    a.batch = d.batch;
+    a.H = d.H;
+    a.d_h = d.d_h;
+    a.r = d.r;
+    a.L_cap = d.L_cap;
+    a.dtype = d.dtype;
+    a.max_len = max_len;
+    a.chunk = plan.chunk;
+    a.num_splits = plan.num_splits;
+    a.k_shared = c.k_shared;
+    a.v_shared = c.v_shared;
+    a.z_k = c.z_k;
+    a.z_v = c.z_v;
+    a.seq_lens = c.seq_lens;
+    a.q = q;
+    a.p = p;
+    a.ws = (float*)ws;
+    hipError_t e = (plan.path == SplitPath::kMfmaBf16) ? launch_split_mfma(a, plan.waves, stream)
+                                                        : launch_split_general(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+    return LRKV_OK;
+}
+
+lrkv_status check_cache(const lrkv_dims& d, const lrkv_cache* c, bool need_latents) {
+    if (!c) return fail(LRKV_ERR_INVALID_ARG, "cache is NULL");
+    LRKV_TRY(need_ptr(c->k_shared, "cache.k_shared"));
+    LRKV_TRY(need_ptr(c->v_shared, "cache.v_shared"));
+    LRKV_TRY(need_ptr(c->seq_lens, "cache.seq_lens"));
+    if (d.r > 0 && need_latents) {
+        LRKV_TRY(need_ptr(c->z_k, "cache.z_k"));
+        LRKV_TRY(need_ptr(c->z_v, "cache.z_v"));
+    }
+    return LRKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lrkv_status_str(lrkv_status s) {
+    switch (s) {
+        case LRKV_OK: return "LRKV_OK";
+        case LRKV_ERR_INVALID_ARG: return "LRKV_ERR_INVALID_ARG";
+        case LRKV_ERR_UNSUPPORTED: return "LRKV_ERR_UNSUPPORTED";
+        case LRKV_ERR_WORKSPACE: return "LRKV_ERR_WORKSPACE";
+        case LRKV_ERR_HIP: return "LRKV_ERR_HIP";
+    }
+    return "LRKV_UNKNOWN_STATUS";
+}
+
+const char* lrkv_last_error(void) { return g_last_error; }
+
+uint64_t lrkv_cache_bytes(const lrkv_dims* dims, const int32_t* host_seq_lens) {
+    if (!dims_valid(dims)) return 0;
+    const uint64_t s = dims->dtype == LRKV_F32 ? 4 : 2;
+    uint64_t rows = 0;
+    for (int b = 0; b < dims->batch; ++b) {
+        int64_t L = host_seq_lens ? host_seq_lens[b] : dims->L_cap;
+        L = std::max<int64_t>(0, std::min<int64_t>(L, dims->L_cap));
+        rows += (uint64_t)L;
+    }
+    return 2ull * s * rows * ((uint64_t)dims->d_h + (uint64_t)dims->H * (uint64_t)dims->r);
+}
+
+size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len) {
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p)) return 0;
+    return workspace_bytes(*dims, p);
+}
+
+int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens) {
+    if (!dims_valid(dims) || max_len <= 0 || max_len > dims->L_cap) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p)) return 0;
+    if (chunk_tokens) *chunk_tokens = p.chunk;
+    return p.num_splits;
+}
+
+lrkv_status lrkv_absorb_query(const lrkv_dims* dims, const void* q, const void* B_k, float* p, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (dims->r == 0) return ok();
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(B_k, "B_k"));
+    LRKV_TRY(need_ptr(p, "p"));
+    hipError_t e = lrkv::launch_absorb(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, q, B_k, p,
+                                       (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "absorb kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_cache_append(const lrkv_dims* dims, const lrkv_cache* cache, const void* k_new, const void* v_new,
+                              const void* zk_new, const void* zv_new, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(k_new, "k_new"));
+    LRKV_TRY(need_ptr(v_new, "v_new"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(zk_new, "zk_new"));
+        LRKV_TRY(need_ptr(zv_new, "zv_new"));
+    }
+    hipError_t e = lrkv::launch_append(dims->batch, dims->H, dims->d_h, dims->r, dims->L_cap, dims->dtype,
+                                       cache->k_shared, cache->v_shared, cache->z_k, cache->z_v, cache->seq_lens,
+                                       k_new, v_new, zk_new, zv_new, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                                const float* p, void* workspace, size_t workspace_bytes_, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(q, "q"));
+    if (dims->r > 0) LRKV_TRY(need_ptr(p, "p"));
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
+    return ok();
+}
+
+lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
+                              float* out, const void* workspace, size_t workspace_bytes_, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan));
+    LRKV_TRY(need_ptr(seq_lens, "seq_lens"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) LRKV_TRY(need_ptr(B_v, "B_v"));
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                                      plan.num_splits, seq_lens, B_v, out, (const float*)workspace,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                        const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes_,
+                        void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(p, "p"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                                      plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+}  // extern "C"

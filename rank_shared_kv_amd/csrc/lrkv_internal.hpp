@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (lrkv_api.cpp) and the kernel
+// translation units.  Every launcher only enqueues; arguments have already
+// been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lrkv {
+
+struct DecodeArgs {
+    int batch, H, d_h, r, L_cap, dtype;
+    int max_len;         // host bound of seq_lens
+    int chunk;           // tokens per split
+    int num_splits;      // S
+    const void* k_shared;
+    const void* v_shared;
+    const void* z_k;
+    const void* z_v;
+    const int32_t* seq_lens;
+    const void* q;
+    const float* p;
+    float* ws;           // [batch][S][H][record]
+};
+
+// Which split kernel a problem uses.
+enum class SplitPath { kGeneral, kMfmaBf16 };
+
+// Decode split plan: pure host arithmetic (no device query), so workspace
+// sizes are known without a GPU.
+struct SplitPlan {
+    SplitPath path;
+    int chunk;       // tokens per split (multiple of the kernel's token tile)
+    int num_splits;  // ceil(max_len / chunk)
+    int waves;       // waves per workgroup of the split kernel
+};
+
+bool mfma_path_supports(int H, int d_h, int r, int dtype);
+bool general_path_supports(int H, int d_h, int r);
+size_t general_lds_bytes(int H, int d_h, int r);
+
+hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
+                         hipStream_t stream);
+hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype, void* k_shared, void* v_shared,
+                         void* z_k, void* z_v, int32_t* seq_lens, const void* k_new, const void* v_new,
+                         const void* zk_new, const void* zv_new, hipStream_t stream);
+hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_split_mfma(const DecodeArgs& a, int waves, hipStream_t stream);
+hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
+                        const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream);
+
+}  // namespace lrkv

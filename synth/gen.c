@@ -3,12 +3,13 @@
  * CPU reference.  It holds no attention arithmetic: it only turns
  * (seed, element index) into numbers with a stated distribution.
  *
- * Generator: counter based.  Element k of a stream with seed S uses two 64-bit
- * words  w = mix64(S ^ mix64(2k + c)), c in {0, 1}, where mix64 is the
- * SplitMix64 output function (Steele, Lea, Flood, "Fast splittable
- * pseudorandom number generators", OOPSLA 2014).  The top 53 bits of each word
- * give a uniform u in (0, 1); the pair goes through the Box-Muller transform
- * (Box and Muller, 1958), cosine branch only, to give one N(0, 1) sample.
+ * Generator: counter based.  Elements 2k and 2k+1 of a stream with seed S
+ * share two 64-bit words  w_c = mix64(S ^ mix64(2k + c)), c in {0, 1}, where
+ * mix64 is the SplitMix64 output function (Steele, Lea, Flood, "Fast
+ * splittable pseudorandom number generators", OOPSLA 2014).  The top 53 bits
+ * of each word give uniforms u1, u2 in (0, 1); the Box-Muller transform (Box
+ * and Muller, 1958) turns them into two independent N(0, 1) samples:
+ * element 2k = sqrt(-2 ln u1) cos(2 pi u2), element 2k+1 = the same with sin.
  * Because every element depends only on (S, k), any slice of a tensor can be
  * regenerated on its own and the result does not depend on the thread count.
  *
@@ -16,6 +17,7 @@
  * (round to nearest even, by the C conversion), and for bf16 the fp32 value is
  * rounded again to bf16 (round to nearest even on the 16 dropped bits).
  */
+#define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -36,10 +38,33 @@ static inline double unit_open(uint64_t seed, uint64_t counter) {
 
 static inline double normal_at(uint64_t seed, uint64_t k) {
     const double two_pi = 6.283185307179586476925286766559;
-    double u1 = unit_open(seed, 2 * k);
-    double u2 = unit_open(seed, 2 * k + 1);
-    return sqrt(-2.0 * log(u1)) * cos(two_pi * u2);
+    const uint64_t pair = k >> 1;
+    double u1 = unit_open(seed, 2 * pair);
+    double u2 = unit_open(seed, 2 * pair + 1);
+    double rad = sqrt(-2.0 * log(u1));
+    return (k & 1) ? rad * sin(two_pi * u2) : rad * cos(two_pi * u2);
 }
+
+/* Fill out[0..n) with elements offset .. offset+n-1, computing each pair once. */
+#define FILL_PAIRS(CONVERT)                                                              \
+    do {                                                                                 \
+        const double two_pi = 6.283185307179586476925286766559;                         \
+        uint64_t first = offset, last = offset + n; /* [first, last) */                 \
+        uint64_t p0 = first >> 1, p1 = (last + 1) >> 1;                                 \
+        _Pragma("omp parallel for num_threads(nthreads) schedule(static)")              \
+        for (uint64_t p = p0; p < p1; ++p) {                                             \
+            double u1 = unit_open(seed, 2 * p), u2 = unit_open(seed, 2 * p + 1);        \
+            double rad = sqrt(-2.0 * log(u1)), sn, cs;                                   \
+            sincos(two_pi * u2, &sn, &cs);                                               \
+            uint64_t e0 = 2 * p, e1 = 2 * p + 1;                                         \
+            if (e0 >= first && e0 < last) out[e0 - first] = CONVERT(stddev * (rad * cs)); \
+            if (e1 >= first && e1 < last) out[e1 - first] = CONVERT(stddev * (rad * sn)); \
+        }                                                                                \
+    } while (0)
+
+#define CONV_F32(x) ((float)(x))
+#define CONV_BF16(x) f32_to_bf16_rne((float)(x))
+#define CONV_F64(x) (x)
 
 static inline uint16_t f32_to_bf16_rne(float f) {
     uint32_t u;
@@ -52,21 +77,21 @@ static inline uint16_t f32_to_bf16_rne(float f) {
 
 /* out[k] = fp32(std * N(0,1) at counter offset + k), k in [0, n) */
 void synth_normal_f32(uint64_t seed, double stddev, uint64_t offset, float* out, size_t n, int nthreads) {
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-    for (size_t k = 0; k < n; ++k) out[k] = (float)(stddev * normal_at(seed, offset + k));
+    FILL_PAIRS(CONV_F32);
 }
 
 /* out[k] = bf16 bits of fp32(std * N(0,1) at counter offset + k) */
 void synth_normal_bf16(uint64_t seed, double stddev, uint64_t offset, uint16_t* out, size_t n, int nthreads) {
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-    for (size_t k = 0; k < n; ++k) out[k] = f32_to_bf16_rne((float)(stddev * normal_at(seed, offset + k)));
+    FILL_PAIRS(CONV_BF16);
 }
 
 /* out[k] = fp64 std * N(0,1) at counter offset + k (no rounding) */
 void synth_normal_f64(uint64_t seed, double stddev, uint64_t offset, double* out, size_t n, int nthreads) {
-#pragma omp parallel for num_threads(nthreads) schedule(static)
-    for (size_t k = 0; k < n; ++k) out[k] = stddev * normal_at(seed, offset + k);
+    FILL_PAIRS(CONV_F64);
 }
+
+/* one element (for checks of the bulk fill) */
+double synth_normal_one(uint64_t seed, uint64_t k) { return normal_at(seed, k); }
 
 /* out[k] uniform integer in [lo, hi] (inclusive) at counter offset + k */
 void synth_uniform_int(uint64_t seed, int32_t lo, int32_t hi, uint64_t offset, int32_t* out, size_t n) {

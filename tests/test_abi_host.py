@@ -1,0 +1,203 @@
+"""Host-side checks of the C ABI (no GPU needed; no kernel is launched).
+
+* the shared library loads and exports every function include/lrkv.h declares;
+* lrkv_cache_bytes reproduces the cache accounting printed on the pages;
+* argument checks reject bad calls before any HIP call;
+* the split plan and workspace size are consistent host arithmetic.
+"""
+import json
+import math
+import os
+import re
+
+import pytest
+
+import rank_shared_kv_amd as lk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "lrkv.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*[A-Za-z_][\w \*]*?[\s\*](lrkv_\w+)\s*\(", header, re.M))
+    assert declared, "no declarations parsed from include/lrkv.h"
+    L = lk.lib()
+    for name in sorted(declared):
+        assert hasattr(L, name), f"{name} declared in lrkv.h but not exported"
+    assert declared == set(lk.EXPORTED)
+
+
+def _bytes(H, d_h, r, L, dtype=lk.LRKV_BF16, batch=1, lens=None):
+    dims = lk.make_dims(batch, H, d_h, r, max(1, L), dtype)
+    return lk.lrkv_cache_bytes(dims, lens)
+
+
+def _mha_bytes(H, d_h, L, s=2, batch=1):
+    # MHA payload per token and layer is 2 H d_h elements (reading notes, sec. 1 cache table)
+    return 2 * s * batch * L * H * d_h
+
+
+def test_cache_fraction_table():
+    g = _golden("cache_accounting.json")
+    for row in g["table7_fractions_percent"]:
+        frac = _bytes(row["H"], row["d_h"], row["r"], 2048) / _mha_bytes(row["H"], row["d_h"], 2048)
+        assert abs(100 * frac - row["percent"]) < 0.005 + 1e-9, row
+    for row in g["rank_sweep_percent"]:
+        frac = _bytes(6, 128, row["r"], 2048) / _mha_bytes(6, 128, 2048)
+        assert abs(100 * frac - row["percent"]) < 0.05 + 1e-9, row
+
+
+def test_elements_per_token_example():
+    e = _golden("cache_accounting.json")["elements_example"]
+    lrkv_elems = _bytes(e["H"], e["d_h"], e["r"], 1) // 2  # bf16: 2 bytes per element
+    assert lrkv_elems == e["lrkv"]
+    assert 2 * e["H"] * e["d_h"] == e["mha"]
+    assert abs(100 * lrkv_elems / e["mha"] - e["kept_percent"]) < 0.005
+    assert abs(100 - 100 * lrkv_elems / e["mha"] - e["saved_percent"]) < 0.005
+
+
+def test_layout_example_bytes():
+    x = _golden("cache_accounting.json")["layout_example"]
+    per_layer = _bytes(x["H"], x["d_h"], x["r"], x["tokens"])
+    total = x["layers"] * per_layer
+    assert x["layers"] * _mha_bytes(x["H"], x["d_h"], x["tokens"]) == x["mha_bytes"]
+    assert x["mha_bytes"] / 2**20 == x["mha_mib"]
+    assert total / 2**20 == x["lrkv_mib"]
+    assert x["layers"] * _bytes(x["H"], x["d_h"], x["r"], x["tokens_long"]) / 2**20 == x["lrkv_mib_long"]
+    assert x["layers"] * _mha_bytes(x["H"], x["d_h"], x["tokens_long"]) / 2**20 == x["mha_mib_long"]
+
+
+def test_rank_ceiling_and_padding():
+    g = _golden("cache_accounting.json")
+    for key in ("rank_ceiling", "gqa6_parity"):
+        c = g[key]
+        H, d_h, cap = c["H"], c["d_h"], c["c"]
+        frac = lambda r: _bytes(H, d_h, r, 64) / _mha_bytes(H, d_h, 64)
+        assert frac(c["r_max"]) <= cap + 1e-12 < frac(c["r_max"] + 1), key
+    p = g["padded"]
+    assert abs(100 * _bytes(p["H"], p["d_h"], p["r"], 64) / _mha_bytes(p["H"], p["d_h"], 64) - p["percent"]) < 0.005
+
+
+def test_tensor_parallel_replication():
+    t = _golden("cache_accounting.json")["tp_replicated"]
+    H, d_h, r, P = t["H"], t["d_h"], t["r"], t["P"]
+    single = _bytes(H, d_h, r, 64)
+    shared_only = _bytes(H, d_h, 0, 64)  # r = 0 leaves only the shared block
+    replicated = single + (P - 1) * shared_only
+    mha = _mha_bytes(H, d_h, 64)
+    assert abs(100 * single / mha - t["single_percent"]) < 0.05
+    assert abs(100 * replicated / mha - t["replicated_percent"]) < 0.05
+
+
+def test_full_rank_and_break_even():
+    for H in (4, 6, 18, 32):
+        d_h = 128
+        assert _bytes(H, d_h, d_h, 64) / _mha_bytes(H, d_h, 64) == pytest.approx(1 + 1 / H, rel=1e-12)
+        r_star = d_h * (1 - 1 / H)
+        for r in range(0, d_h + 1):
+            saves = _bytes(H, d_h, r, 64) < _mha_bytes(H, d_h, 64)
+            assert saves == (r < r_star), (H, r)
+
+
+def test_cache_bytes_ragged_and_dtype():
+    dims = lk.make_dims(3, 4, 16, 2, 100, lk.LRKV_F32)
+    assert lk.lrkv_cache_bytes(dims, [10, 0, 50]) == 2 * 4 * 60 * (16 + 4 * 2)
+    assert lk.lrkv_cache_bytes(dims, [-5, 200, 1]) == 2 * 4 * (0 + 100 + 1) * (16 + 8)
+    assert lk.lrkv_cache_bytes(dims) == 2 * 4 * 300 * 24
+    bad = lk.make_dims(0, 4, 16, 2, 100, lk.LRKV_F32)
+    assert lk.lrkv_cache_bytes(bad) == 0
+
+
+# ---- argument checks: each call must fail on the host before any HIP call ----
+
+A = 1 << 20  # a fake 16-byte-aligned device address; never dereferenced on these paths
+
+
+def _dims():
+    return lk.make_dims(2, 8, 64, 8, 256, lk.LRKV_BF16)
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except lk.LrkvError as e:
+        return e.status
+    return lk.LRKV_OK
+
+
+def test_invalid_dims_rejected():
+    for bad in [lk.make_dims(0, 8, 64, 8, 256, 1), lk.make_dims(2, 0, 64, 8, 256, 1), lk.make_dims(2, 8, 0, 8, 256, 1),
+                lk.make_dims(2, 8, 64, -1, 256, 1), lk.make_dims(2, 8, 64, 8, 0, 1), lk.make_dims(2, 8, 64, 8, 256, 7)]:
+        cache = lk.Cache(A, A, A, A, A)
+        assert _status(lk.lrkv_absorb_query, bad, A, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+        assert _status(lk.lrkv_cache_append, bad, cache, A, A, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+        assert _status(lk.lrkv_decode, bad, cache, 10, A, A, A, A, A, 1 << 30, 0) == lk.LRKV_ERR_INVALID_ARG
+        assert lk.lrkv_decode_workspace_bytes(bad, 10) == 0
+
+
+def test_null_and_misaligned_pointers_rejected():
+    d = _dims()
+    ws = lk.lrkv_decode_workspace_bytes(d, 256)
+    good = lk.Cache(A, A, A, A, A)
+    for field in ("k_shared", "v_shared", "z_k", "z_v", "seq_lens"):
+        for badval in (None, A + 2):
+            c = lk.Cache(A, A, A, A, A)
+            setattr(c, field, badval)
+            assert _status(lk.lrkv_decode, d, c, 256, A, A, A, A, 1 << 12, ws, 0) == lk.LRKV_ERR_INVALID_ARG, field
+            assert _status(lk.lrkv_cache_append, d, c, A, A, A, A, 0) == lk.LRKV_ERR_INVALID_ARG, field
+    for i in range(4):  # q, p, B_v, out
+        args = [A, A, A, A]
+        args[i] = None
+        assert _status(lk.lrkv_decode, d, good, 256, *args, 1 << 12, ws, 0) == lk.LRKV_ERR_INVALID_ARG, i
+    assert _status(lk.lrkv_absorb_query, d, None, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_absorb_query, d, A, A, A + 4, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_cache_append, d, good, A, None, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode_merge, d, None, 256, A, A, 1 << 12, ws, 0) == lk.LRKV_ERR_INVALID_ARG
+
+
+def test_max_len_and_workspace_rejected():
+    d = _dims()
+    c = lk.Cache(A, A, A, A, A)
+    need = lk.lrkv_decode_workspace_bytes(d, 256)
+    assert need > 0
+    assert _status(lk.lrkv_decode, d, c, 257, A, A, A, A, 1 << 12, need, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode, d, c, -1, A, A, A, A, 1 << 12, need, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode, d, c, 256, A, A, A, A, 1 << 12, need - 1, 0) == lk.LRKV_ERR_WORKSPACE
+    assert _status(lk.lrkv_decode, d, c, 256, A, A, A, A, None, need, 0) == lk.LRKV_ERR_WORKSPACE
+    assert _status(lk.lrkv_decode, d, c, 256, A, A, A, A, (1 << 12) + 16, need, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode_partial, d, c, 256, A, A, 1 << 12, need - 4, 0) == lk.LRKV_ERR_WORKSPACE
+
+
+def test_unsupported_shape_rejected():
+    d = lk.make_dims(1, 4, 300, 4, 64, lk.LRKV_F32)  # d_h beyond every kernel
+    c = lk.Cache(A, A, A, A, A)
+    assert _status(lk.lrkv_decode, d, c, 64, A, A, A, A, 1 << 12, 1 << 20, 0) == lk.LRKV_ERR_UNSUPPORTED
+    assert lk.lrkv_decode_workspace_bytes(d, 64) == 0
+
+
+def test_r0_needs_no_latents():
+    d = lk.make_dims(2, 8, 64, 0, 256, lk.LRKV_F32)
+    # absorb is a no-op for r == 0 and touches nothing
+    lk.lrkv_absorb_query(d, None, None, None, 0)
+
+
+def test_split_plan_arithmetic():
+    for (B, H, d_h, r, L, dt) in [(1, 4, 16, 4, 64, 0), (8, 8, 64, 8, 2048, 1), (16, 16, 128, 48, 8192, 1),
+                                  (4, 32, 128, 64, 32768, 1), (64, 32, 128, 32, 32768, 1), (64, 32, 128, 0, 32768, 0)]:
+        d = lk.make_dims(B, H, d_h, r, L, dt)
+        S, chunk = lk.lrkv_decode_num_splits(d, L)
+        assert S == math.ceil(L / chunk) and chunk % 32 == 0 and 1 <= S <= 4096
+        rec = ((d_h + r + 2) + 3) // 4 * 4
+        assert lk.lrkv_decode_workspace_bytes(d, L) == 4 * B * S * H * rec
+        # the plan depends on the shape and max_len, not on the rank
+        assert lk.lrkv_decode_num_splits(lk.make_dims(B, H, d_h, 0, L, dt), L) == (S, chunk)
+    d = lk.make_dims(2, 8, 64, 8, 256, 1)
+    assert lk.lrkv_decode_num_splits(d, 0) == (0, 0)
+    assert lk.lrkv_decode_workspace_bytes(d, 0) == 0

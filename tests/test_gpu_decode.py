@@ -1,0 +1,195 @@
+"""GPU parity of the LRKV decode library against the CPU reference.
+
+All calls go through the C ABI (rank_shared_kv_amd -> liblrkv.so).  Outputs
+are compared element by element with the fp64 reference on the same seeded
+inputs, with the metric max over (b, h) of ||gpu - ref||_inf / ||ref||_inf:
+1e-5 for fp32 inputs, 2e-3 for bf16 caches with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rank_shared_kv_amd as lk
+import synth
+from synth import device as sdev
+
+pytestmark = pytest.mark.gpu
+
+from gpu_harness import TOL, cache_of, compare, dims_of, gpu_decode, oracle_pairs, say  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lk.lib()
+    yield
+
+
+def _all_pairs(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.H)]
+
+
+def _run_and_check(w, lengths=None, L_cap=None, pairs=None, label=None, split_calls=False):
+    lens = synth.seq_lengths(w) if lengths is None else np.asarray(lengths, dtype=np.int32)
+    cap = L_cap or w.cap
+    label = label or w.name
+    say(f"[case] {label}: B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_cap={cap} lens[:8]={lens[:8].tolist()}")
+    dev = sdev.fill_layer(w, 0, L_cap=cap, lengths=lens)
+    max_len = int(lens.max(initial=0))
+    got = gpu_decode(w, dev, max_len, L_cap=cap, split_calls=split_calls)
+    pairs = pairs or _all_pairs(w)
+    ref = oracle_pairs(w, 0, lens, pairs)
+    compare(w, got, ref, pairs, label)
+    return got, dev
+
+
+def test_tiny_fp32_all_pairs():
+    _run_and_check(synth.WORKLOADS["tiny_fp32"])
+
+
+def test_small_bf16_all_pairs():
+    _run_and_check(synth.WORKLOADS["small_bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(8, 64, 16), (16, 128, 48), (32, 128, 64), (8, 64, 8), (32, 128, 32)])
+def test_ragged_edges(dtype, shape):
+    """Lengths 0, 1, tile boundaries +-1 and a few tiles, with the split plan forced to several splits."""
+    H, d_h, r = shape
+    w = synth.WORKLOADS["ragged"].with_(name=f"edges_{dtype}_{H}_{d_h}_{r}", batch=8, H=H, d_h=d_h, r=r,
+                                        dtype=dtype, L=700, L_cap=704, ragged_lo=None)
+    lens = [0, 1, 31, 32, 33, 127, 129, 700]
+    pairs = [(b, h) for b in range(8) for h in sorted({0, H // 2, H - 1})]
+    _run_and_check(w, lengths=lens, L_cap=704, pairs=pairs)
+
+
+def test_r0_fp32_matches_mqa_reference():
+    w = synth.WORKLOADS["ragged_mqa_fp32"].with_(batch=4)
+    lens = np.array([512, 1000, 3001, 777], dtype=np.int32)
+    say(f"[case] r=0 fp32 vs MQA reference, lens={lens.tolist()}")
+    dev = sdev.fill_layer(w, 0, L_cap=w.cap, lengths=lens)
+    got = gpu_decode(w, dev, int(lens.max()))
+    pairs = [(b, h) for b in range(4) for h in (0, 7, 31)]
+    ref = oracle_pairs(w, 0, lens, pairs, mqa=True)
+    compare(w, got, ref, pairs, "r0_fp32_vs_mqa")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_r0_equals_zero_latents_bitwise(dtype):
+    """The private branch adds exact zeros: r = 0 and r > 0 with zero latents agree bit for bit."""
+    w0 = synth.WORKLOADS["ragged"].with_(name="r0", batch=3, H=32, d_h=128, r=0, dtype=dtype, L=600, L_cap=608,
+                                         ragged_lo=None)
+    lens = np.array([600, 45, 257], dtype=np.int32)
+    say(f"[case] r=0 vs zero latents, {dtype}")
+    dev0 = sdev.fill_layer(w0, 0, L_cap=608, lengths=lens)
+    out0 = gpu_decode(w0, dev0, 600, L_cap=608)
+    w32 = w0.with_(r=32)
+    dev32 = dict(dev0)
+    dev32["z_k"] = torch.zeros((3, 32, 608, 32), dtype=dev0["k_shared"].dtype, device="cuda")
+    dev32["z_v"] = torch.zeros_like(dev32["z_k"])
+    dev32["B_k"] = sdev.to_device(synth.gen_small(w32, 0, "B_k"))
+    dev32["B_v"] = sdev.to_device(synth.gen_small(w32, 0, "B_v"))
+    out32 = gpu_decode(w32, dev32, 600, L_cap=608)
+    assert torch.equal(out0, out32)
+
+
+def test_partial_plus_merge_equals_decode_and_is_deterministic():
+    w = synth.WORKLOADS["small_bf16"]
+    lens = synth.seq_lengths(w)
+    dev = sdev.fill_layer(w, 0)
+    a = gpu_decode(w, dev, int(lens.max()))
+    b = gpu_decode(w, dev, int(lens.max()), split_calls=True)
+    c = gpu_decode(w, dev, int(lens.max()))
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_batch_independence():
+    """Changing one sequence's cache leaves the other sequences' outputs bit for bit unchanged."""
+    w = synth.WORKLOADS["small_bf16"].with_(batch=4, L=300)
+    lens = np.array([300, 120, 300, 7], dtype=np.int32)
+    dev = sdev.fill_layer(w, 0, lengths=lens)
+    a = gpu_decode(w, dev, 300)
+    dev["k_shared"][1].mul_(-1.5)
+    dev["z_v"][1].add_(1.0)
+    b = gpu_decode(w, dev, 300)
+    for s in (0, 2, 3):
+        assert torch.equal(a[s], b[s])
+    assert not torch.equal(a[1], b[1])
+
+
+def test_absorb_matches_float64_product():
+    w = synth.WORKLOADS["long_context"].with_(batch=2)
+    q = synth.gen_small(w, 0, "q")
+    Bk = synth.gen_small(w, 0, "B_k")
+    dims = dims_of(w)
+    p = torch.empty((2, w.H, w.r), dtype=torch.float32, device="cuda")
+    lk.lrkv_absorb_query(dims, sdev.to_device(q), sdev.to_device(Bk), p)
+    torch.cuda.synchronize()
+    qf, Bf = synth.bf16_bits_to_f32(q).astype(np.float64), synth.bf16_bits_to_f32(Bk).astype(np.float64)
+    ref = np.einsum("bhc,hcr->bhr", qf, Bf)
+    err = np.max(np.abs(p.cpu().numpy() - ref)) / np.max(np.abs(ref))
+    assert err < 1e-6, err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_then_decode(dtype):
+    """Append one token after a prefill of L-1 rows: rows land at seq_lens[b], lengths advance, decode agrees."""
+    w = synth.WORKLOADS["ragged"].with_(name=f"append_{dtype}", batch=3, H=16, d_h=128, r=48, dtype=dtype, L=260,
+                                        L_cap=264, ragged_lo=None)
+    full = np.array([260, 33, 1], dtype=np.int32)
+    say(f"[case] append after prefill {dtype}")
+    dev = sdev.fill_layer(w, 0, L_cap=264, lengths=full)
+    ref_dev = {k: v.clone() for k, v in dev.items()}
+    # remove the last row of each sequence, then append it back through the library
+    host = {b: synth.gen_sequence(w, 0, b, int(full[b])) for b in range(3)}
+    k_new = np.stack([host[b]["k_shared"][-1] for b in range(3)])
+    v_new = np.stack([host[b]["v_shared"][-1] for b in range(3)])
+    zk_new = np.stack([host[b]["z_k"][:, -1] for b in range(3)])
+    zv_new = np.stack([host[b]["z_v"][:, -1] for b in range(3)])
+    for b in range(3):
+        n = int(full[b]) - 1
+        dev["k_shared"][b, n:].zero_()
+        dev["v_shared"][b, n:].zero_()
+        dev["z_k"][b, :, n:].zero_()
+        dev["z_v"][b, :, n:].zero_()
+    dev["seq_lens"] = torch.from_numpy(full - 1).cuda()
+    dims = dims_of(w, 264)
+    lk.lrkv_cache_append(dims, cache_of(dev, w.r), sdev.to_device(k_new), sdev.to_device(v_new),
+                         sdev.to_device(zk_new), sdev.to_device(zv_new))
+    torch.cuda.synchronize()
+    assert dev["seq_lens"].cpu().numpy().tolist() == full.tolist()
+    for k in ("k_shared", "v_shared", "z_k", "z_v"):
+        assert torch.equal(dev[k], ref_dev[k]), k
+    got = gpu_decode(w, dev, 260, L_cap=264)
+    pairs = [(b, h) for b in range(3) for h in range(0, 16, 5)]
+    compare(w, got, oracle_pairs(w, 0, full, pairs), pairs, f"append_{dtype}")
+
+
+def test_append_to_full_sequence_is_dropped():
+    w = synth.WORKLOADS["small_bf16"].with_(batch=2, L=16)
+    lens = np.array([16, 15], dtype=np.int32)
+    dev = sdev.fill_layer(w, 0, lengths=lens)
+    before = {k: v.clone() for k, v in dev.items()}
+    rows = sdev.new_rows(w)
+    lk.lrkv_cache_append(dims_of(w), cache_of(dev, w.r), rows["k_new"], rows["v_new"], rows["zk_new"],
+                         rows["zv_new"])
+    torch.cuda.synchronize()
+    assert dev["seq_lens"].cpu().tolist() == [16, 16]
+    assert torch.equal(dev["k_shared"][0], before["k_shared"][0])   # full: untouched
+    assert torch.equal(dev["k_shared"][1, 15], rows["k_new"][1])     # appended at row 15
+    assert torch.equal(dev["z_v"][1, :, 15], rows["zv_new"][1])
+
+
+def test_empty_and_zero_max_len():
+    w = synth.WORKLOADS["small_bf16"].with_(batch=3, L=64)
+    lens = np.array([0, 0, 0], dtype=np.int32)
+    dev = sdev.fill_layer(w, 0, lengths=lens)
+    out = gpu_decode(w, dev, 0)
+    assert torch.count_nonzero(out) == 0
+    lens = np.array([0, 64, 0], dtype=np.int32)
+    dev = sdev.fill_layer(w, 0, lengths=lens)
+    out = gpu_decode(w, dev, 64)
+    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
+    assert torch.count_nonzero(out[1]) > 0
