@@ -102,7 +102,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU-reference wall time (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copied {n * 4} bytes 5 times")
+        return
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
@@ -118,7 +130,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     K, W = args.steps, args.warmup
     lens_full = synth.seq_lengths(w)
-    L_cap = int(lens_full.max()) + K
+    # room for the appended rows, rounded up to whole 256-row pages
+    L_cap = (int(lens_full.max()) + K + 255) // 256 * 256
     start_lens = lens_full - 1 - W
     assert int(start_lens.min()) >= 0
     log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
@@ -134,7 +147,7 @@ def main():
     dims = lk.make_dims(w.batch, w.H, w.d_h, w.r, L_cap, dtype_code)
     cache = lk.make_cache(dev["k_shared"], dev["v_shared"], dev["z_k"] if w.r else None,
                           dev["z_v"] if w.r else None, dev["seq_lens"])
-    max_len = L_cap
+    max_len = int(lens_full.max()) + K  # host bound on every length reached in this run
     nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
     ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
     p = torch.empty((w.batch, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")

@@ -105,8 +105,9 @@ lrkv_status lrkv_cache_append(const lrkv_dims* dims, const lrkv_cache* cache, co
 size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
 
 /* Number of sequence splits (S) the decode uses for these dims and max_len,
- * and the tokens per split (*chunk_tokens, may be NULL).  Host arithmetic only.
- * Returns 0 for invalid dims or max_len == 0. */
+ * and the split granule in rows (*chunk_tokens, may be NULL): split s of
+ * sequence b holds live rows iff s * granule < seq_lens[b].  Host arithmetic
+ * only.  Returns 0 for invalid dims or max_len == 0. */
 int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens);
 
 /* One decode step against the factored history (review sec. 3, Algorithm 2

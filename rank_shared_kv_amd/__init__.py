@@ -14,7 +14,8 @@ import os
 from typing import Optional, Sequence, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblrkv.so")
+# LRKV_LIBRARY selects another build of the same library (tuning experiments); default: in-tree
+LIB_PATH = os.environ.get("LRKV_LIBRARY") or os.path.join(_HERE, "liblrkv.so")
 
 LRKV_OK = 0
 LRKV_ERR_INVALID_ARG = 1

@@ -27,14 +27,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out_path: str = LIB_PATH, defines=()) -> str:
     srcs = []
     for s in SOURCES:
         path = os.path.join(CSRC, s)
         # .cpp files are host code that includes HIP headers; compile them as HIP too
         srcs += (["-x", "hip", path] if s.endswith(".cpp") else [path])
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+    tmp = out_path + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -44,9 +44,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-o", default=LIB_PATH)
+    ap.add_argument("-D", action="append", default=[])
+    args = ap.parse_args()
+    print(build(verbose=args.v, out_path=args.o, defines=args.D))

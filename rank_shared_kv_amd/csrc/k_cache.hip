@@ -14,17 +14,37 @@
 namespace lrkv {
 namespace {
 
+// One workgroup per (b, h): thread (i, quarter) sums a quarter of the d_h terms
+// for coordinate i, the four quarters are added in a fixed order in LDS.
+constexpr int kAbsorbThreads = 256;
+
 template <typename T>
-__global__ void __launch_bounds__(64) absorb_kernel(int H, int d_h, int r, const T* __restrict__ q,
-                                                    const T* __restrict__ B_k, float* __restrict__ p) {
+__global__ void __launch_bounds__(kAbsorbThreads) absorb_kernel(int H, int d_h, int r, const T* __restrict__ q,
+                                                                const T* __restrict__ B_k, float* __restrict__ p) {
+    __shared__ float part[kAbsorbThreads];
     const int bh = blockIdx.x;  // b * H + h
     const int h = bh % H;
     const T* qrow = q + (size_t)bh * d_h;
     const T* basis = B_k + (size_t)h * d_h * r;
-    for (int i = threadIdx.x; i < r; i += blockDim.x) {
-        float acc = 0.f;
-        for (int c = 0; c < d_h; ++c) acc = fmaf(elem<T>::load(qrow, c), elem<T>::load(basis, (size_t)c * r + i), acc);
-        p[(size_t)bh * r + i] = acc;
+    const int tid = threadIdx.x, i0 = tid & 63, quarter = tid >> 6;
+    const int c_per = (d_h + 3) / 4;
+    const int c_lo = quarter * c_per, c_hi = min(d_h, c_lo + c_per);
+    // every thread runs the same number of iterations (barriers inside)
+    for (int ib = 0; ib < r; ib += 64) {
+        const int i = ib + i0;
+        float a0 = 0.f, a1 = 0.f;
+        if (i < r) {
+            int c = c_lo;
+            for (; c + 1 < c_hi; c += 2) {
+                a0 = fmaf(elem<T>::load(qrow, c), elem<T>::load(basis, (size_t)c * r + i), a0);
+                a1 = fmaf(elem<T>::load(qrow, c + 1), elem<T>::load(basis, (size_t)(c + 1) * r + i), a1);
+            }
+            if (c < c_hi) a0 = fmaf(elem<T>::load(qrow, c), elem<T>::load(basis, (size_t)c * r + i), a0);
+        }
+        part[tid] = a0 + a1;
+        __syncthreads();
+        if (quarter == 0 && i < r) p[(size_t)bh * r + i] = ((part[i0] + part[64 + i0]) + part[128 + i0]) + part[192 + i0];
+        __syncthreads();
     }
 }
 
@@ -63,7 +83,7 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
 
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
                          hipStream_t stream) {
-    dim3 grid(batch * H), block(64);
+    dim3 grid(batch * H), block(kAbsorbThreads);
     if (dtype == 0)
         hipLaunchKernelGGL(absorb_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
                            (const float*)B_k, p);

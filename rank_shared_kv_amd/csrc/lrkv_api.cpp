@@ -72,28 +72,28 @@ int env_int(const char* name, int dflt) {
 }
 
 // Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes
-// are known on the host without a device.  The token tile is the kernel's
-// unit of work; a split is a whole number of tiles.  The number of splits is
-// chosen so the split kernel launches about `target` workgroups in total
-// (MI355X has 256 CUs; a few workgroups per CU keep its memory pipes busy),
-// and never more than kMaxSplits per sequence.  The plan does not depend on r
-// so that problems differing only in rank reduce in the same order.
+// are known on the host without a device.  A plan is (S splits per sequence,
+// granule g): split s of sequence b holds live rows iff s * g < L_b.  The
+// general kernel gives split s the contiguous rows [s*g, (s+1)*g); the MFMA
+// kernel deals g-row tiles round-robin over the S splits.  S is chosen so the
+// split kernel launches about one round of resident workgroups (MI355X has
+// 256 CUs), never more than kMaxSplits per sequence.  The plan does not
+// depend on r so that problems differing only in rank reduce in the same order.
 constexpr int kMaxSplits = 4096;
 
 bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
     using namespace lrkv;
     SplitPlan p{};
-    if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype)) {
+    if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
-        p.waves = env_int("LRKV_WAVES", 4);
-        if (p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8) p.waves = 4;
+        p.occupancy = env_int("LRKV_OCCUPANCY", 2) == 1 ? 1 : 2;
     } else if (general_path_supports(d.H, d.d_h, d.r)) {
         p.path = SplitPath::kGeneral;
-        p.waves = 4;
+        p.occupancy = 1;
     } else {
         return false;
     }
-    const int tile = (p.path == SplitPath::kMfmaBf16) ? 32 * p.waves : 32;
+    const int tile = (p.path == SplitPath::kMfmaBf16) ? mfma_rows_per_tile(d.H) : 32;
     if (max_len <= 0) {
         p.chunk = tile;
         p.num_splits = 0;
@@ -101,16 +101,36 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
         return true;
     }
     const long tiles_per_seq = (max_len + tile - 1) / tile;
-    const long total_tiles = tiles_per_seq * d.batch;
-    const int target = env_int("LRKV_TARGET_WGS", 1024);
-    long tiles_per_split = (total_tiles + target - 1) / target;
-    tiles_per_split = std::max<long>(tiles_per_split, (tiles_per_seq + kMaxSplits - 1) / kMaxSplits);
-    tiles_per_split = std::max<long>(1, std::min(tiles_per_split, tiles_per_seq));
-    const int forced = env_int("LRKV_CHUNK", 0);
-    if (forced > 0) tiles_per_split = std::max<long>(1, std::min<long>((forced + tile - 1) / tile, tiles_per_seq));
-    p.chunk = (int)(tiles_per_split * tile);
-    p.num_splits = (int)((max_len + p.chunk - 1) / p.chunk);
-    if (p.num_splits > kMaxSplits) return false;
+    if (p.path == SplitPath::kMfmaBf16) {
+        // Rows are dealt round-robin in tiles over the splits of a sequence, so any split count works;
+        // aim for one resident round of workgroups (occupancy x 256 CUs) over the whole batch.
+        const long target = env_int("LRKV_TARGET_WGS", 256 * p.occupancy);
+        long S = std::max<long>(1, target / d.batch);
+        const int forced = env_int("LRKV_SPLITS", 0);
+        if (forced > 0) S = forced;
+        S = std::min<long>(std::min<long>(S, tiles_per_seq), kMaxSplits);
+        p.interleave = env_int("LRKV_INTERLEAVE", 2) == 1 ? 1 : 0;
+        if (p.interleave) {
+            p.chunk = tile;  // granule: split s holds rows iff s * tile < L_b
+            p.num_splits = (int)S;
+        } else {
+            const long tiles_per_split = (tiles_per_seq + S - 1) / S;
+            p.chunk = (int)(tiles_per_split * tile);
+            p.num_splits = (int)((max_len + p.chunk - 1) / p.chunk);
+        }
+    } else {
+        // contiguous chunks of whole tiles, about `target` workgroups over the batch
+        const long total_tiles = tiles_per_seq * d.batch;
+        const int target = env_int("LRKV_TARGET_WGS", 1024);
+        long tiles_per_split = (total_tiles + target - 1) / target;
+        tiles_per_split = std::max<long>(tiles_per_split, (tiles_per_seq + kMaxSplits - 1) / kMaxSplits);
+        tiles_per_split = std::max<long>(1, std::min(tiles_per_split, tiles_per_seq));
+        const int forced = env_int("LRKV_CHUNK", 0);
+        if (forced > 0) tiles_per_split = std::max<long>(1, std::min<long>((forced + tile - 1) / tile, tiles_per_seq));
+        p.chunk = (int)(tiles_per_split * tile);
+        p.num_splits = (int)((max_len + p.chunk - 1) / p.chunk);
+        if (p.num_splits > kMaxSplits) return false;
+    }
     *out = p;
     return true;
 }
@@ -153,6 +173,7 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.max_len = max_len;
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
+    a.interleave = plan.interleave;
     a.k_shared = c.k_shared;
     a.v_shared = c.v_shared;
     a.z_k = c.z_k;
@@ -161,7 +182,7 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.q = q;
     a.p = p;
     a.ws = (float*)ws;
-    hipError_t e = (plan.path == SplitPath::kMfmaBf16) ? launch_split_mfma(a, plan.waves, stream)
+    hipError_t e = (plan.path == SplitPath::kMfmaBf16) ? launch_split_mfma(a, plan.occupancy, stream)
                                                         : launch_split_general(a, stream);
     if (e != hipSuccess) return hip_fail(e, "split kernel launch");
     return LRKV_OK;

@@ -12,8 +12,9 @@ namespace lrkv {
 struct DecodeArgs {
     int batch, H, d_h, r, L_cap, dtype;
     int max_len;         // host bound of seq_lens
-    int chunk;           // tokens per split
+    int chunk;           // split granule in rows: split s holds live rows iff s * chunk < L_b
     int num_splits;      // S
+    int interleave;      // MFMA kernel: 1 = tiles dealt round-robin over splits, 0 = contiguous chunks
     const void* k_shared;
     const void* v_shared;
     const void* z_k;
@@ -33,10 +34,12 @@ struct SplitPlan {
     SplitPath path;
     int chunk;       // tokens per split (multiple of the kernel's token tile)
     int num_splits;  // ceil(max_len / chunk)
-    int waves;       // waves per workgroup of the split kernel
+    int occupancy;   // MFMA kernel: waves per SIMD it is compiled for (1 or 2)
+    int interleave;  // MFMA kernel: 1 = tiles dealt round-robin over the splits, 0 = contiguous chunks
 };
 
-bool mfma_path_supports(int H, int d_h, int r, int dtype);
+bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);
+int mfma_rows_per_tile(int H);  // rows one MFMA-kernel workgroup advances per step
 bool general_path_supports(int H, int d_h, int r);
 size_t general_lds_bytes(int H, int d_h, int r);
 
@@ -46,7 +49,7 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
                          void* z_k, void* z_v, int32_t* seq_lens, const void* k_new, const void* v_new,
                          const void* zk_new, const void* zv_new, hipStream_t stream);
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_split_mfma(const DecodeArgs& a, int waves, hipStream_t stream);
+hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream);
 

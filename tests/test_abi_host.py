@@ -193,7 +193,7 @@ def test_split_plan_arithmetic():
                                   (4, 32, 128, 64, 32768, 1), (64, 32, 128, 32, 32768, 1), (64, 32, 128, 0, 32768, 0)]:
         d = lk.make_dims(B, H, d_h, r, L, dt)
         S, chunk = lk.lrkv_decode_num_splits(d, L)
-        assert S == math.ceil(L / chunk) and chunk % 32 == 0 and 1 <= S <= 4096
+        assert 1 <= S <= math.ceil(L / chunk) and chunk % 32 == 0 and S <= 4096
         rec = ((d_h + r + 2) + 3) // 4 * 4
         assert lk.lrkv_decode_workspace_bytes(d, L) == 4 * B * S * H * rec
         # the plan depends on the shape and max_len, not on the rank

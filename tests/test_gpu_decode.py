@@ -193,3 +193,27 @@ def test_empty_and_zero_max_len():
     out = gpu_decode(w, dev, 64)
     assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
     assert torch.count_nonzero(out[1]) > 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(32, 128, 64), (16, 128, 48), (8, 64, 8), (32, 128, 0)])
+def test_rows_past_the_end_are_never_used(dtype, shape):
+    """Rows at or past seq_lens[b] hold NaN: outputs must stay finite and equal the clean run bit for bit."""
+    H, d_h, r = shape
+    w = synth.WORKLOADS["ragged"].with_(name=f"poison_{dtype}_{H}_{r}", batch=4, H=H, d_h=d_h, r=r, dtype=dtype,
+                                        L=300, L_cap=320, ragged_lo=None)
+    lens = np.array([300, 33, 1, 95], dtype=np.int32)
+    say(f"[case] NaN past the end, {dtype} H={H} d_h={d_h} r={r}")
+    dev = sdev.fill_layer(w, 0, L_cap=320, lengths=lens)
+    clean = gpu_decode(w, dev, 300, L_cap=320)
+    nan = float("nan")
+    for b in range(4):
+        n = int(lens[b])
+        dev["k_shared"][b, n:] = nan
+        dev["v_shared"][b, n:] = nan
+        if r > 0:
+            dev["z_k"][b, :, n:] = nan
+            dev["z_v"][b, :, n:] = nan
+    dirty = gpu_decode(w, dev, 300, L_cap=320)
+    assert bool(torch.isfinite(dirty).all())
+    assert torch.equal(clean, dirty)
