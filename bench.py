@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_context")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of CPU-reference wall time (0: skip)")
+    ap.add_argument("--capacity", type=int, default=0,
+                    help="cache rows allocated per sequence (default: the context plus the timed appends, "
+                         "rounded up to 256)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -132,6 +135,9 @@ def main():
     lens_full = synth.seq_lengths(w)
     # room for the appended rows, rounded up to whole 256-row pages
     L_cap = (int(lens_full.max()) + K + 255) // 256 * 256
+    if args.capacity:
+        assert args.capacity >= int(lens_full.max()) + K and args.capacity % 32 == 0
+        L_cap = args.capacity
     start_lens = lens_full - 1 - W
     assert int(start_lens.min()) >= 0
     log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
@@ -231,7 +237,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
-                   "L": int(lens_full.max()), "lengths": "uniform" if w.ragged_lo is None else
+                   "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
                    "splits": S, "chunk_tokens": chunk},
         "hbm_gbps_step": step_gbps,

@@ -67,8 +67,13 @@ typedef struct {
 
 /* The factored cache of one layer (review sec. 3, Algorithm 1): device pointers.
  *   k_shared, v_shared  [batch][L_cap][d_h]   rows x W_shared^K, x W_shared^V
- *   z_k, z_v            [batch][H][L_cap][r]  latents x U_h^K, x U_h^V; may be NULL iff r == 0
+ *   z_k, z_v            [batch][L_cap][H][r]  latents x U_h^K, x U_h^V; may be NULL iff r == 0
  *   seq_lens            [batch] int32         live rows per sequence: rows 0 .. seq_lens[b]-1
+ * The latents are stored token-major: element z[b][j][h][i] is head h's
+ * coordinate i for token j, so one token's H x r latents form one contiguous
+ * row (the logical per-head tensor z_h[b][j][i] of the pages, transposed).
+ * A decode step then streams every cache tensor linearly, and per-head latent
+ * regions never sit at a common large stride, whatever L_cap is.
  * For decode the current query's own token must already be appended, so
  * seq_lens[b] counts it; every live row is visible to the query. */
 typedef struct {

@@ -7,7 +7,8 @@
 //          a fixed order over d_h.
 // append:  write one token's shared rows and per-head latents at index
 //          seq_lens[b] and advance seq_lens[b] (review sec. 3, Algorithm 1;
-//          reading notes sec. 2.3).
+//          reading notes sec. 2.3).  Latents are token-major, so one token's
+//          H x r latents land in one contiguous row.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
 
@@ -70,7 +71,7 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
     }
     for (int idx = threadIdx.x; idx < H * r; idx += blockDim.x) {
         const int h = idx / r, i = idx - h * r;
-        const size_t dst = (((size_t)b * H + h) * L_cap + j) * r + i;
+        const size_t dst = (((size_t)b * L_cap + j) * H + h) * r + i;  // token-major latents
         const size_t src = ((size_t)b * H + h) * r + i;
         z_k[dst] = zk_new[src];
         z_v[dst] = zv_new[src];

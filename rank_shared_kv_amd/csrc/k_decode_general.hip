@@ -78,7 +78,8 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
         const int i_lo = half * ((R + 1) / 2), i_hi = min(R, (half + 1) * ((R + 1) / 2));
         for (int h = wave; h < H; h += kThreads / 64) {
             const size_t bh = (size_t)b * H + h;
-            const size_t zrow = (bh * a.L_cap + (size_t)(t0 + (live ? t : 0))) * R;
+            // latents are token-major: row t of sequence b holds every head's r coordinates
+            const size_t zrow = (((size_t)b * a.L_cap + (size_t)(t0 + (live ? t : 0))) * H + h) * R;
             // score: shared part on the LDS tile, private part on the latent row
             float sc = 0.f;
             for (int c = c_lo; c < c_hi; ++c) sc = fmaf(elem<T>::load(q, bh * D + c), Kt[t * (D + 1) + c], sc);
@@ -107,8 +108,9 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
             }
             for (int i = lane; i < R; i += 64) {
                 float sum = 0.f;
-                const size_t z0 = (bh * a.L_cap + (size_t)t0) * R + i;
-                for (int u = 0; u < nvalid; ++u) sum = fmaf(ebuf[wave * kTile + u], elem<T>::load(zv, z0 + (size_t)u * R), sum);
+                const size_t z0 = (((size_t)b * a.L_cap + (size_t)t0) * H + h) * R + i;
+                for (int u = 0; u < nvalid; ++u)
+                    sum = fmaf(ebuf[wave * kTile + u], elem<T>::load(zv, z0 + (size_t)u * H * R), sum);
                 acc_h[D + i] = alpha * acc_h[D + i] + sum;
             }
             wave_lds_sync();  // ebuf reused by this wave's next head

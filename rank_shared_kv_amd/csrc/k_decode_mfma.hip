@@ -27,10 +27,11 @@
 //     key fragments are loaded from HBM straight into the MFMA A layout;
 //   * the value tile is transposed into LDS (V^T[d_h][32 rows]);
 //   * private scores p_h . z^K_{h,j} on the VALU: latent rows are read from HBM
-//     into registers, 8 lanes per row (each lane owns r/8 coordinates), 8 heads
-//     per load instruction; lane s reads row k^s at step k, so a 3-stage
-//     transpose-reduce over lanes (xor 4, 2, 1) needs no selects and leaves
-//     each lane with one finished score;
+//     into registers, 8 lanes per head (each lane owns r/8 coordinates); the
+//     latents are stored token-major, so one load instruction reads one token's
+//     latents of 8 consecutive heads, 8*r*2 contiguous bytes; the 8 partial dots
+//     of 8 rows are combined by a 3-stage transpose-reduce over lanes (DPP half
+//     mirror, xor 2, xor 1) that leaves each lane with one finished score;
 //   * scores meet in the MFMA result layout (lane = one head, 8 rows) through a
 //     small LDS exchange; online softmax there (max across lanes xor 16, 32);
 //   * shared values O^T[d_h x 16] += V^T[d_h x 32] P^T[32 x 16] on MFMA, with P
@@ -216,6 +217,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
 
     const int n16 = lane & 15, g4 = lane >> 4;  // MFMA layout: column (head or value column), row group
     const int hh = lane >> 3, sl = lane & 7;    // latent layout: head within octet, coordinate slice
+    const bool sb0 = sl & 1, sb1 = (sl >> 1) & 1, sb2 = (sl >> 2) & 1;
     const int srow = lane / C::LPR, schunk = lane % C::LPR;  // value-tile load layout
     const float scale = kLog2e / sqrtf((float)D);
 
@@ -230,31 +232,23 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         for (int e = 0; e < EPL; ++e) acc_pr[o][e] = 0.f;
 
     // ---- buffer descriptors of this sequence and fixed per-lane byte offsets ----
-    const uint32_t row_bytes_sh = D * 2, row_bytes_lat = R * 2;
+    // latents are token-major ([L_cap][H][r] per sequence): one latent row holds every head
+    const uint32_t row_bytes_sh = D * 2, row_bytes_lat = H * R * 2;
     const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + (size_t)b * a.L_cap * D,
                                                  (uint32_t)a.L_cap * row_bytes_sh);
     const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const uint16_t*)a.v_shared + (size_t)b * a.L_cap * D,
                                                  (uint32_t)a.L_cap * row_bytes_sh);
     __amdgpu_buffer_rsrc_t rs_zk = rs_k, rs_zv = rs_v;
-    // lane sl reads row k^sl of a key-latent sub-block at step k.  When r*2 is a power of two the row
-    // bits of the offset are disjoint from the rest, so the permuted offset is one XOR away.
-    constexpr bool kPow2Row = (R > 0) && ((R & (R - 1)) == 0);
-    uint32_t vo_zk[kPow2Row ? 1 : 8], vo_zv = 0;
+    uint32_t vo_zv = 0;  // lane offset of (head 16*hg + hh, coordinate slice sl) in the latent tensors
     if constexpr (R > 0) {
-        const uint32_t lat_bytes = (uint32_t)H * a.L_cap * row_bytes_lat;
+        const uint32_t lat_bytes = (uint32_t)H * a.L_cap * (R * 2);
         rs_zk = buf_rsrc((const uint16_t*)a.z_k + (size_t)b * H * a.L_cap * R, lat_bytes);
         rs_zv = buf_rsrc((const uint16_t*)a.z_v + (size_t)b * H * a.L_cap * R, lat_bytes);
-        vo_zv = (uint32_t)(16 * hg + hh) * a.L_cap * row_bytes_lat + sl * EPL * 2;
-        if constexpr (kPow2Row) {
-            vo_zk[0] = vo_zv + (uint32_t)sl * row_bytes_lat;
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) vo_zk[k] = vo_zv + (uint32_t)(k ^ sl) * row_bytes_lat;
-        }
+        vo_zv = (uint32_t)(16 * hg + hh) * R * 2 + sl * EPL * 2;
     }
     const uint32_t vo_kf = (uint32_t)n16 * row_bytes_sh + 16 * g4;              // key fragment rows n16, 16 + n16
     const uint32_t vo_vt = (uint32_t)(4 * srow) * row_bytes_sh + 16 * schunk;  // value tile rows 4*srow + 0..3
-    const uint32_t oct_bytes = 8u * a.L_cap * row_bytes_lat;
+    const uint32_t oct_bytes = 8u * R * 2;  // next head octet within a latent row
 
     // ---- the load ring ----
     uint32_t ring[NSLOT][SDW];
@@ -297,13 +291,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             const __amdgpu_buffer_rsrc_t rs = (phase == 0) ? rs_zk : rs_zv;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                uint32_t vo;
-                if (phase == 0) {
-                    if constexpr (kPow2Row) vo = (vo_zk[0] ^ (uint32_t)(k * R * 2)) + 8 * sub * row_bytes_lat;
-                    else vo = vo_zk[k] + 8 * sub * row_bytes_lat;
-                } else {
-                    vo = vo_zv + (k + 8 * sub) * row_bytes_lat;
-                }
+                // one instruction reads row 8*sub + k of 8 consecutive heads: 8*r*2 contiguous bytes
+                const uint32_t vo = vo_zv + (k + 8 * sub) * row_bytes_lat;
                 if constexpr (EPL == 8) {
                     const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat);
                     ring[slot][4 * k] = w.x;
@@ -432,14 +421,26 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                         }
                         part[k] = acc;
                     }
-                    // transpose-reduce across the 8 lanes of a row (lane sl read row k^sl at step k):
-                    // stage 1 pairs lanes sl, 7-sl (half mirror), stage 2 sl, sl^2, stage 3 sl, sl^1.
+                    // transpose-reduce across the 8 lanes of a head: part[k] is this lane's slice of
+                    // row k.  Stage 1 pairs lanes sl, 7-sl (half mirror) and each keeps the rows whose
+                    // bit 2 equals its own; stages 2 and 3 do the same on bits 1 and 0 with lanes
+                    // sl^2 and sl^1.  Lane sl ends with the whole score of row 8*sub + sl.
                     float q4[4], q2[2];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) q4[k] = part[k] + dpp<kDppHalfMirror>(part[7 - k]);
+                    for (int k = 0; k < 4; ++k) {
+                        const float keep = sb2 ? part[k + 4] : part[k];
+                        const float send = sb2 ? part[k] : part[k + 4];
+                        q4[k] = keep + dpp<kDppHalfMirror>(send);
+                    }
 #pragma unroll
-                    for (int k = 0; k < 2; ++k) q2[k] = q4[k] + dpp<kDppXor2>(q4[k ^ 2]);
-                    xb[(8 * oi + hh) * C::XS + 8 * sub + sl] = q2[0] + dpp<kDppXor1>(q2[1]);
+                    for (int k = 0; k < 2; ++k) {
+                        const float keep = sb1 ? q4[k + 2] : q4[k];
+                        const float send = sb1 ? q4[k] : q4[k + 2];
+                        q2[k] = keep + dpp<kDppXor2>(send);
+                    }
+                    const float keep = sb0 ? q2[1] : q2[0];
+                    const float send = sb0 ? q2[0] : q2[1];
+                    xb[(8 * oi + hh) * C::XS + 8 * sub + sl] = keep + dpp<kDppXor1>(send);
                 } else {
                     if (sub == 0) {
                         const float al = xb[(8 * oi + hh) * C::XS + 32];

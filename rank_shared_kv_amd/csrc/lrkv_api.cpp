@@ -1,7 +1,7 @@
 // C ABI of the LRKV decode library: argument checks, split planning and
 // kernel launches.  Everything here is host code; no HIP call is made before
 // a call's arguments have been checked, and nothing runs at load time.
-#include "../../include/lrkv.h"
+#include "lrkv.h"
 
 #include <hip/hip_runtime.h>
 
@@ -79,6 +79,10 @@ int env_int(const char* name, int dflt) {
 // split kernel launches about one round of resident workgroups (MI355X has
 // 256 CUs), never more than kMaxSplits per sequence.  The plan does not
 // depend on r so that problems differing only in rank reduce in the same order.
+// Tuning overrides (read at every call, so they must not change between a
+// workspace query and the decode that uses it): LRKV_OCCUPANCY (1 or 2 waves
+// per SIMD), LRKV_INTERLEAVE (1 round-robin tiles, 2 contiguous chunks),
+// LRKV_TARGET_WGS, LRKV_SPLITS, LRKV_CHUNK.
 constexpr int kMaxSplits = 4096;
 
 bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
@@ -86,7 +90,7 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
     SplitPlan p{};
     if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
-        p.occupancy = env_int("LRKV_OCCUPANCY", 2) == 1 ? 1 : 2;
+        p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
     } else if (general_path_supports(d.H, d.d_h, d.r)) {
         p.path = SplitPath::kGeneral;
         p.occupancy = 1;
@@ -109,7 +113,7 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
         const int forced = env_int("LRKV_SPLITS", 0);
         if (forced > 0) S = forced;
         S = std::min<long>(std::min<long>(S, tiles_per_seq), kMaxSplits);
-        p.interleave = env_int("LRKV_INTERLEAVE", 2) == 1 ? 1 : 0;
+        p.interleave = env_int("LRKV_INTERLEAVE", 1) == 2 ? 0 : 1;
         if (p.interleave) {
             p.chunk = tile;  // granule: split s holds rows iff s * tile < L_b
             p.num_splits = (int)S;

@@ -2,6 +2,8 @@
 
 Large caches are generated one sequence at a time on the host and copied into
 preallocated device tensors, so host memory stays at one sequence's worth.
+The generators (and the oracle) index latents per head, [b][h][j][i]; the
+device cache stores them token-major, [b][j][h][i].
 """
 from __future__ import annotations
 
@@ -35,8 +37,8 @@ def alloc_cache(w: Workload, L_cap: Optional[int] = None, device="cuda") -> Dict
     r = max(w.r, 0)
     return {"k_shared": torch.zeros((w.batch, cap, w.d_h), dtype=dt, device=device),
             "v_shared": torch.zeros((w.batch, cap, w.d_h), dtype=dt, device=device),
-            "z_k": torch.zeros((w.batch, w.H, cap, r), dtype=dt, device=device),
-            "z_v": torch.zeros((w.batch, w.H, cap, r), dtype=dt, device=device)}
+            "z_k": torch.zeros((w.batch, cap, w.H, r), dtype=dt, device=device),
+            "z_v": torch.zeros((w.batch, cap, w.H, r), dtype=dt, device=device)}
 
 
 def fill_layer(w: Workload, layer: int = 0, L_cap: Optional[int] = None, lengths: Optional[np.ndarray] = None,
@@ -54,8 +56,9 @@ def fill_layer(w: Workload, layer: int = 0, L_cap: Optional[int] = None, lengths
         dev["k_shared"][b, :n].copy_(to_device(s["k_shared"], device))
         dev["v_shared"][b, :n].copy_(to_device(s["v_shared"], device))
         if w.r > 0:
-            dev["z_k"][b, :, :n].copy_(to_device(s["z_k"], device))
-            dev["z_v"][b, :, :n].copy_(to_device(s["z_v"], device))
+            # generated per head ([H][n][r]); stored token-major ([n][H][r])
+            dev["z_k"][b, :n].copy_(to_device(s["z_k"], device).transpose(0, 1))
+            dev["z_v"][b, :n].copy_(to_device(s["z_v"], device).transpose(0, 1))
     dev["q"] = to_device(gen_small(w, layer, "q"), device)
     if w.r > 0:
         dev["B_k"] = to_device(gen_small(w, layer, "B_k"), device)

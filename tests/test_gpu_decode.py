@@ -87,7 +87,7 @@ def test_r0_equals_zero_latents_bitwise(dtype):
     out0 = gpu_decode(w0, dev0, 600, L_cap=608)
     w32 = w0.with_(r=32)
     dev32 = dict(dev0)
-    dev32["z_k"] = torch.zeros((3, 32, 608, 32), dtype=dev0["k_shared"].dtype, device="cuda")
+    dev32["z_k"] = torch.zeros((3, 608, 32, 32), dtype=dev0["k_shared"].dtype, device="cuda")
     dev32["z_v"] = torch.zeros_like(dev32["z_k"])
     dev32["B_k"] = sdev.to_device(synth.gen_small(w32, 0, "B_k"))
     dev32["B_v"] = sdev.to_device(synth.gen_small(w32, 0, "B_v"))
@@ -152,8 +152,8 @@ def test_append_then_decode(dtype):
         n = int(full[b]) - 1
         dev["k_shared"][b, n:].zero_()
         dev["v_shared"][b, n:].zero_()
-        dev["z_k"][b, :, n:].zero_()
-        dev["z_v"][b, :, n:].zero_()
+        dev["z_k"][b, n:].zero_()
+        dev["z_v"][b, n:].zero_()
     dev["seq_lens"] = torch.from_numpy(full - 1).cuda()
     dims = dims_of(w, 264)
     lk.lrkv_cache_append(dims, cache_of(dev, w.r), sdev.to_device(k_new), sdev.to_device(v_new),
@@ -179,7 +179,7 @@ def test_append_to_full_sequence_is_dropped():
     assert dev["seq_lens"].cpu().tolist() == [16, 16]
     assert torch.equal(dev["k_shared"][0], before["k_shared"][0])   # full: untouched
     assert torch.equal(dev["k_shared"][1, 15], rows["k_new"][1])     # appended at row 15
-    assert torch.equal(dev["z_v"][1, :, 15], rows["zv_new"][1])
+    assert torch.equal(dev["z_v"][1, 15], rows["zv_new"][1])
 
 
 def test_empty_and_zero_max_len():
@@ -212,8 +212,8 @@ def test_rows_past_the_end_are_never_used(dtype, shape):
         dev["k_shared"][b, n:] = nan
         dev["v_shared"][b, n:] = nan
         if r > 0:
-            dev["z_k"][b, :, n:] = nan
-            dev["z_v"][b, :, n:] = nan
+            dev["z_k"][b, n:] = nan
+            dev["z_v"][b, n:] = nan
     dirty = gpu_decode(w, dev, 300, L_cap=320)
     assert bool(torch.isfinite(dirty).all())
     assert torch.equal(clean, dirty)
