@@ -37,6 +37,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def launch_config(w, steps: int, capacity: int = 0):
+    """(L_cap, max_len) of a benchmark run of `steps` timed steps on workload w: room for the appended rows,
+    rounded up to whole 256-row pages, unless a capacity is given.  The full-size parity tests use the same."""
+    import synth
+    L_max = int(synth.seq_lengths(w).max())
+    L_cap = (L_max + steps + 255) // 256 * 256
+    if capacity:
+        assert capacity >= L_max + steps and capacity % 32 == 0
+        L_cap = capacity
+    return L_cap, L_max + steps
+
+
 def kernel_sources_digest() -> str:
     import glob
     h = hashlib.sha256()
@@ -133,11 +145,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     K, W = args.steps, args.warmup
     lens_full = synth.seq_lengths(w)
-    # room for the appended rows, rounded up to whole 256-row pages
-    L_cap = (int(lens_full.max()) + K + 255) // 256 * 256
-    if args.capacity:
-        assert args.capacity >= int(lens_full.max()) + K and args.capacity % 32 == 0
-        L_cap = args.capacity
+    L_cap, max_len = launch_config(w, K, args.capacity)
     start_lens = lens_full - 1 - W
     assert int(start_lens.min()) >= 0
     log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
@@ -153,7 +161,6 @@ def main():
     dims = lk.make_dims(w.batch, w.H, w.d_h, w.r, L_cap, dtype_code)
     cache = lk.make_cache(dev["k_shared"], dev["v_shared"], dev["z_k"] if w.r else None,
                           dev["z_v"] if w.r else None, dev["seq_lens"])
-    max_len = int(lens_full.max()) + K  # host bound on every length reached in this run
     nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
     ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
     p = torch.empty((w.batch, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")

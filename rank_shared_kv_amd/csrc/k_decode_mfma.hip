@@ -328,17 +328,24 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         last_blk = min(nb, (split + 1) * (a.chunk / kRows));
     }
     const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
+    // Sequence b walks its blocks starting b/batch of the way along (the same blocks, rotated order).
+    // Otherwise every sequence reads the same relative position of its cache region at the same time,
+    // and with some region strides those concurrent streams crowd the same HBM channels.
+    const int rot = (int)(((long)nmine * b) / a.batch);
     if (nmine > 0) {
 #pragma unroll
-        for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * first_blk, u);
+        for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * (first_blk + rot * step_blk), u);
     }
 
     for (int it = 0; it < nmine; ++it) {
-        const int blk = first_blk + it * step_blk;
+        int itr = it + rot;
+        if (itr >= nmine) itr -= nmine;
+        const int blk = first_blk + itr * step_blk;
         const int t0 = kRows * blk;
         const int nvalid = min(kRows, Lb - t0);
         // next block of this row lane; on the last block the prefetch re-reads this block (always in bounds)
-        const int t0_pf = (it + 1 < nmine) ? t0 + kRows * step_blk : t0;
+        const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
+        const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
         f32x4_t s_sh[2];
         float ev[8];
 

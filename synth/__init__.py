@@ -12,6 +12,10 @@ Tensor layouts (row-major, element counts):
   B_k        [H, d_h, r]              B_v likewise
   seq_lens   [batch] int32            live rows per sequence
 
+These are the logical (per-head) layouts that the CPU reference reads.  The
+GPU library stores latents token-major, [batch, L_cap, H, r]; synth.device
+transposes when it copies a cache to the device.
+
 Only the live rows (j < seq_lens[b]) of the caches are generated; rows beyond
 are zero.  Element (b, j, c) of k_shared uses counter b*L_cap*d_h + j*d_h + c,
 so any sequence can be regenerated alone and gives the same values.
