@@ -1,0 +1,297 @@
+// MFMA split kernel for fp32 decode with r = 0 on gfx950 (CDNA4, wave64).
+//
+// With rank 0 the factored cache holds only the shared key and value rows, and
+// every head attends over them: the MQA special case of LRKV ("Low-Rank Key
+// Value Attention: Chinese reading notes", sec. 2.1 and the cache table of
+// sec. 1; "Low-Rank Key Value Attention | What a shared cache can preserve",
+// sec. 3, where rank 0 removes the private branch).  Per sequence b and head h:
+//   s_j = q_h . k_j / sqrt(d_h),  a = softmax(s),  o_h = sum_j a_j v_j.
+// Both products are dense contractions over all heads of a group at once, so
+// both run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: fp32 products,
+// fp32 accumulation).  The kernel writes the same per-split online-softmax
+// records as the bf16 kernel; the merge kernel combines them.
+//
+// Work decomposition (as in the bf16 kernel): a workgroup of 4 waves owns one
+// (b, split); a wave owns 16 heads (MFMA N) on one row lane of 32-row blocks,
+// blocks dealt round-robin over all (split, row lane) slots.  Per block:
+//   S^T[32 rows x 16 heads] = K[32 x d_h] Q^T         (two 16-row halves)
+//   online softmax on S^T in the MFMA result layout (lane = head, 8 rows)
+//   O^T[d_h x 16 heads]    += V^T[d_h x 32 rows] P^T
+// The contraction index of each product is permuted so that every lane loads
+// 16 contiguous bytes per global load and no operand goes through LDS:
+//   * score product, k-step t of a half: lane (row n, group g) supplies
+//     K[n][16 (t/4) + 4 g + t%4] and Q[head n][same column] -- four
+//     consecutive k-steps come from one 16-byte load;
+//   * value product, k-step t (rows of half t/4): lane (column slot n, group g)
+//     supplies V[16 (t/4) + 4 g + t%4][64 p + 4 n + s] for column block
+//     cb = 4 p + s, and P^T[that row][head] is exactly the softmax weight the
+//     lane already holds from the score layout.
+// The accumulator of column block cb = 4 p + s then holds, in lane (head n,
+// group g) and register i, o_h at column 64 p + 16 g + 4 i + s.
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRows = 32;
+constexpr int kWaves = 4;
+
+template <int D, int H, int OCC>
+struct CfgF32 {
+    static constexpr int NHG = (H + 15) / 16;        // head groups of 16 (MFMA N)
+    static constexpr int NTL = kWaves / NHG;          // row lanes per workgroup
+    static constexpr int KLD = D / 16;                // 16-byte loads per lane per key half
+    static constexpr int VP = D / 64;                 // 64-column blocks of a value row
+    static constexpr int UDW = D / 4;                 // dwords per unit (key half or value half)
+    static constexpr int NU = 4;                      // units per block: K half 0, K half 1, V half 0, V half 1
+    static constexpr int NSLOT = (OCC == 1) ? 4 : 2;  // ring depth (divides NU)
+    static constexpr int CB = D / 16;                 // column blocks of the value product
+    static constexpr int REC = ((D + 2) + 3) & ~3;
+    static constexpr int MW_BYTES = kWaves * 16 * 4;
+    static constexpr int LDS_BYTES = MW_BYTES + H * REC * 4;
+    static_assert(D % 64 == 0, "head width");
+    static_assert(H % 8 == 0 && H <= 32, "head count");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int D, int H, int OCC>
+__global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(DecodeArgs a) {
+    using C = CfgF32<D, H, OCC>;
+    constexpr int NSLOT = C::NSLOT, NU = C::NU, UDW = C::UDW;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    float* mw_lds = (float*)lds;               // [waves][16] running maxima
+    float* mg = (float*)(lds + C::MW_BYTES);   // [H][REC] merged records
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hg = wave % C::NHG, tl = wave / C::NHG;
+    const int b = blockIdx.y, split = blockIdx.x;
+    int Lb = a.seq_lens[b];
+    Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
+    if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
+    const int nb = (Lb + kRows - 1) / kRows;
+
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int head = 16 * hg + n16;
+    const float scale = kLog2e / sqrtf((float)D);
+
+    // query fragments, kept for the whole kernel: qf[4 m + j] = q[head][16 m + 4 g4 + j] (zero for padded heads)
+    float qf[4 * C::KLD];
+    {
+        const float* qg = (const float*)a.q + ((size_t)b * H + (head < H ? head : 0)) * D;
+#pragma unroll
+        for (int m = 0; m < C::KLD; ++m) {
+            const f32x4_t v = *(const f32x4_t*)(qg + 16 * m + 4 * g4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qf[4 * m + j] = (head < H) ? v[j] : 0.f;
+        }
+    }
+
+    const uint32_t row_bytes = D * 4;
+    const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const float*)a.k_shared + (size_t)b * a.L_cap * D,
+                                                 (uint32_t)a.L_cap * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const float*)a.v_shared + (size_t)b * a.L_cap * D,
+                                                 (uint32_t)a.L_cap * row_bytes);
+    const uint32_t vo_k = (uint32_t)n16 * row_bytes + 16 * g4;       // row n16 of the half, columns 4 g4 + 16 m
+    const uint32_t vo_v = (uint32_t)(4 * g4) * row_bytes + 16 * n16;  // rows 4 g4 + tt, columns 64 p + 4 n16
+
+    uint32_t ring[NSLOT][UDW];
+    auto issue = [&](int u, int t0, int slot) {
+        const int so = (t0 + 16 * (u & 1)) * (int)row_bytes;
+        if (u < 2) {
+#pragma unroll
+            for (int m = 0; m < C::KLD; ++m) {
+                const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, vo_k + 64 * m, so, 0);
+                ring[slot][4 * m] = v.x;
+                ring[slot][4 * m + 1] = v.y;
+                ring[slot][4 * m + 2] = v.z;
+                ring[slot][4 * m + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int p = 0; p < C::VP; ++p) {
+                    const v4u_t v =
+                        __builtin_amdgcn_raw_buffer_load_b128(rs_v, vo_v + tt * row_bytes + 256 * p, so, 0);
+                    const int o = 4 * (tt * C::VP + p);
+                    ring[slot][o] = v.x;
+                    ring[slot][o + 1] = v.y;
+                    ring[slot][o + 2] = v.z;
+                    ring[slot][o + 3] = v.w;
+                }
+        }
+    };
+
+    f32x4_t acc[C::CB];
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    int first_blk, step_blk, last_blk;
+    if (a.interleave) {
+        first_blk = split * C::NTL + tl;
+        step_blk = a.num_splits * C::NTL;
+        last_blk = nb;
+    } else {
+        first_blk = split * (a.chunk / kRows) + tl;
+        step_blk = C::NTL;
+        last_blk = min(nb, (split + 1) * (a.chunk / kRows));
+    }
+    const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
+    // sequence b walks its blocks starting b/batch of the way along (same blocks, rotated order)
+    const int rot = (int)(((long)nmine * b) / a.batch);
+    if (nmine > 0) {
+#pragma unroll
+        for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * (first_blk + rot * step_blk), u);
+    }
+
+    for (int it = 0; it < nmine; ++it) {
+        int itr = it + rot;
+        if (itr >= nmine) itr -= nmine;
+        const int t0 = kRows * (first_blk + itr * step_blk);
+        const int nvalid = min(kRows, Lb - t0);
+        const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
+        const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
+        f32x4_t s_sh[2];
+        float ev[8];
+
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            {
+                const int un = u + NSLOT - 1;
+                if (un < NU) issue(un, t0, un % NSLOT);
+                else issue(un - NU, t0_pf, un % NSLOT);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            uint32_t* cur = ring[u % NSLOT];
+            if (u < 2) {
+                // S^T half u on the matrix cores
+                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4 * C::KLD; ++t)
+                    s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur[t]), qf[t], s, 0, 0, 0);
+                s_sh[u] = s;
+                if (u == 1) {
+                    // online softmax: lane (head n16, g4) holds rows 4 g4 + i and 16 + 4 g4 + i
+                    float sc[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sc[i] = (4 * g4 + i < nvalid) ? s_sh[0][i] * scale : -INFINITY;
+                        sc[4 + i] = (16 + 4 * g4 + i < nvalid) ? s_sh[1][i] * scale : -INFINITY;
+                    }
+                    float tmax = sc[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                    const float m_new = fmaxf(m_run, tmax);
+                    const float alpha = fast_exp2(m_run - m_new);
+                    m_run = m_new;
+                    float esum = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        ev[i] = fast_exp2(sc[i] - m_new);
+                        esum += ev[i];
+                    }
+                    l_run = fmaf(alpha, l_run, esum);
+#pragma unroll
+                    for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
+                }
+            } else {
+                const int h = u - 2;  // value half: rows 16 h + 4 g4 + tt
+                if (nvalid < kRows) {
+                    // last block of the sequence: rows past the end hold arbitrary values; zero them
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        if (16 * h + 4 * g4 + tt >= nvalid) {
+#pragma unroll
+                            for (int k = 0; k < 4 * C::VP; ++k) cur[4 * tt * C::VP + k] = 0u;
+                        }
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int p = 0; p < C::VP; ++p)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {
+                            const int cb = 4 * p + s;
+                            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __uint_as_float(cur[4 * (tt * C::VP + p) + s]), ev[4 * h + tt], acc[cb], 0, 0, 0);
+                        }
+            }
+        }
+    }
+
+    // ---- merge the row lanes of each head group (fixed order), one record per head ----
+    l_run += __shfl_xor(l_run, 16);  // every lane of a head holds the same partial sum of its rows
+    l_run += __shfl_xor(l_run, 32);
+    if (g4 == 0) mw_lds[wave * 16 + n16] = m_run;
+    __syncthreads();
+    float M = -INFINITY;
+    for (int t = 0; t < C::NTL; ++t) M = fmaxf(M, mw_lds[(t * C::NHG + hg) * 16 + n16]);
+    const float f = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+    for (int t = 0; t < C::NTL; ++t) {
+        if (tl == t && head < H) {
+            float* row = mg + head * C::REC;
+#pragma unroll
+            for (int p = 0; p < C::VP; ++p)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4_t v = f32x4_t{acc[4 * p][i], acc[4 * p + 1][i], acc[4 * p + 2][i], acc[4 * p + 3][i]} * f;
+                    f32x4_t* dst = (f32x4_t*)(row + 64 * p + 16 * g4 + 4 * i);
+                    *dst = (t == 0) ? v : (*dst + v);
+                }
+            if (g4 == 0) {
+                const float lv = l_run * f;
+                row[D + 1] = (t == 0) ? lv : row[D + 1] + lv;
+                if (t == 0) row[D] = M;
+            }
+        }
+        __syncthreads();
+    }
+    float* out = a.ws + ((size_t)b * a.num_splits + split) * H * C::REC;
+    for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
+}
+
+template <int D, int H, int OCC>
+hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
+    using C = CfgF32<D, H, OCC>;
+    auto kern = split_mfma_f32_kernel<D, H, OCC>;
+    hipLaunchKernelGGL(kern, dim3(a.num_splits, a.batch), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_h(const DecodeArgs& a, int occ, hipStream_t stream) {
+    switch (a.H) {
+        case 8: return occ == 1 ? launch_one<D, 8, 1>(a, stream) : launch_one<D, 8, 2>(a, stream);
+        case 16: return occ == 1 ? launch_one<D, 16, 1>(a, stream) : launch_one<D, 16, 2>(a, stream);
+        case 32: return occ == 1 ? launch_one<D, 32, 1>(a, stream) : launch_one<D, 32, 2>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap) {
+    if (dtype != 0 || r != 0) return false;
+    if (L_cap % kRows != 0) return false;  // blocks never leave the allocation
+    if ((long long)L_cap * d_h * 4 >= (1LL << 31)) return false;  // 32-bit buffer offsets
+    if (d_h != 64 && d_h != 128) return false;
+    return H == 8 || H == 16 || H == 32;
+}
+
+hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream) {
+    if (a.d_h == 64) return launch_h<64>(a, occupancy, stream);
+    if (a.d_h == 128) return launch_h<128>(a, occupancy, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lrkv

@@ -91,13 +91,17 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
     if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
         p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
+    } else if (mfma_f32_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+        p.path = SplitPath::kMfmaF32;
+        p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
     } else if (general_path_supports(d.H, d.d_h, d.r)) {
         p.path = SplitPath::kGeneral;
         p.occupancy = 1;
     } else {
         return false;
     }
-    const int tile = (p.path == SplitPath::kMfmaBf16) ? mfma_rows_per_tile(d.H) : 32;
+    const bool mfma = p.path != SplitPath::kGeneral;
+    const int tile = mfma ? mfma_rows_per_tile(d.H) : 32;  // both MFMA kernels use the same block schedule
     if (max_len <= 0) {
         p.chunk = tile;
         p.num_splits = 0;
@@ -105,7 +109,7 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
         return true;
     }
     const long tiles_per_seq = (max_len + tile - 1) / tile;
-    if (p.path == SplitPath::kMfmaBf16) {
+    if (mfma) {
         // Rows are dealt round-robin in tiles over the splits of a sequence, so any split count works;
         // aim for one resident round of workgroups (occupancy x 256 CUs) over the whole batch.
         const long target = env_int("LRKV_TARGET_WGS", 256 * p.occupancy);
@@ -186,8 +190,9 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.q = q;
     a.p = p;
     a.ws = (float*)ws;
-    hipError_t e = (plan.path == SplitPath::kMfmaBf16) ? launch_split_mfma(a, plan.occupancy, stream)
-                                                        : launch_split_general(a, stream);
+    hipError_t e = (plan.path == SplitPath::kMfmaBf16)  ? launch_split_mfma(a, plan.occupancy, stream)
+                   : (plan.path == SplitPath::kMfmaF32) ? launch_split_mfma_f32(a, plan.occupancy, stream)
+                                                         : launch_split_general(a, stream);
     if (e != hipSuccess) return hip_fail(e, "split kernel launch");
     return LRKV_OK;
 }

@@ -26,7 +26,7 @@ struct DecodeArgs {
 };
 
 // Which split kernel a problem uses.
-enum class SplitPath { kGeneral, kMfmaBf16 };
+enum class SplitPath { kGeneral, kMfmaBf16, kMfmaF32 };
 
 // Decode split plan: pure host arithmetic (no device query), so workspace
 // sizes are known without a GPU.
@@ -38,7 +38,8 @@ struct SplitPlan {
     int interleave;  // MFMA kernel: 1 = tiles dealt round-robin over the splits, 0 = contiguous chunks
 };
 
-bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);
+bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);      // bf16 MFMA kernel
+bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap);  // fp32 MFMA kernel (r = 0)
 int mfma_rows_per_tile(int H);  // rows one MFMA-kernel workgroup advances per step
 bool general_path_supports(int H, int d_h, int r);
 size_t general_lds_bytes(int H, int d_h, int r);
@@ -50,6 +51,7 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
                          const void* zk_new, const void* zv_new, hipStream_t stream);
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
+hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream);
 

@@ -76,23 +76,58 @@ def test_r0_fp32_matches_mqa_reference():
     compare(w, got, ref, pairs, "r0_fp32_vs_mqa")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_r0_equals_zero_latents_bitwise(dtype):
-    """The private branch adds exact zeros: r = 0 and r > 0 with zero latents agree bit for bit."""
-    w0 = synth.WORKLOADS["ragged"].with_(name="r0", batch=3, H=32, d_h=128, r=0, dtype=dtype, L=600, L_cap=608,
+def _r0_and_zero_latents(dtype, H, d_h, r):
+    """Outputs of the same problem with r = 0 and with rank r but all latents zero."""
+    w0 = synth.WORKLOADS["ragged"].with_(name="r0", batch=3, H=H, d_h=d_h, r=0, dtype=dtype, L=600, L_cap=608,
                                          ragged_lo=None)
     lens = np.array([600, 45, 257], dtype=np.int32)
-    say(f"[case] r=0 vs zero latents, {dtype}")
     dev0 = sdev.fill_layer(w0, 0, L_cap=608, lengths=lens)
     out0 = gpu_decode(w0, dev0, 600, L_cap=608)
-    w32 = w0.with_(r=32)
-    dev32 = dict(dev0)
-    dev32["z_k"] = torch.zeros((3, 608, 32, 32), dtype=dev0["k_shared"].dtype, device="cuda")
-    dev32["z_v"] = torch.zeros_like(dev32["z_k"])
-    dev32["B_k"] = sdev.to_device(synth.gen_small(w32, 0, "B_k"))
-    dev32["B_v"] = sdev.to_device(synth.gen_small(w32, 0, "B_v"))
-    out32 = gpu_decode(w32, dev32, 600, L_cap=608)
-    assert torch.equal(out0, out32)
+    wr = w0.with_(r=r)
+    devr = dict(dev0)
+    devr["z_k"] = torch.zeros((3, 608, H, r), dtype=dev0["k_shared"].dtype, device="cuda")
+    devr["z_v"] = torch.zeros_like(devr["z_k"])
+    devr["B_k"] = sdev.to_device(synth.gen_small(wr, 0, "B_k"))
+    devr["B_v"] = sdev.to_device(synth.gen_small(wr, 0, "B_v"))
+    outr = gpu_decode(wr, devr, 600, L_cap=608)
+    return out0, outr
+
+
+@pytest.mark.parametrize("dtype,H,d_h,r", [("bf16", 32, 128, 32), ("bf16", 16, 64, 8), ("f32", 4, 16, 4),
+                                           ("f32", 8, 32, 16)])
+def test_r0_equals_zero_latents_bitwise(dtype, H, d_h, r):
+    """The private branch adds exact zeros: r = 0 and r > 0 with zero latents agree bit for bit when the same
+    kernel runs both (bf16 matrix-core kernel; general kernel for these fp32 shapes)."""
+    say(f"[case] r=0 vs zero latents, {dtype} H={H} d_h={d_h} r={r}")
+    out0, outr = _r0_and_zero_latents(dtype, H, d_h, r)
+    assert torch.equal(out0, outr)
+
+
+def test_r0_fp32_matrix_kernel_matches_zero_latents():
+    """fp32 with r = 0 runs on the fp32 matrix-core kernel, r > 0 on the general kernel: same result within
+    the fp32 tolerance."""
+    say("[case] r=0 fp32 (matrix cores) vs r=32 zero latents (general kernel)")
+    out0, outr = _r0_and_zero_latents("f32", 32, 128, 32)
+    g, o = out0.double().cpu().numpy(), outr.double().cpu().numpy()
+    err = max(np.abs(g[b, h] - o[b, h]).max() / np.abs(o[b, h]).max() for b in range(3) for h in range(32))
+    say(f"  max rel diff {err:.3e}")
+    assert err <= TOL["f32"]
+
+
+@pytest.mark.parametrize("H,d_h", [(8, 64), (16, 128), (32, 128), (32, 64)])
+def test_r0_fp32_edges_match_mqa_reference(H, d_h):
+    """fp32 r = 0 (matrix-core kernel): lengths 0, 1, tile boundaries +-1 and a few tiles, against the
+    reference's MQA path."""
+    w = synth.WORKLOADS["ragged_mqa_fp32"].with_(name=f"r0_edges_{H}_{d_h}", batch=8, H=H, d_h=d_h, L=700,
+                                                 L_cap=704, ragged_lo=None)
+    lens = np.array([0, 1, 31, 32, 33, 127, 129, 700], dtype=np.int32)
+    say(f"[case] r=0 fp32 edges H={H} d_h={d_h} lens={lens.tolist()}")
+    dev = sdev.fill_layer(w, 0, L_cap=704, lengths=lens)
+    got = gpu_decode(w, dev, 700, L_cap=704)
+    pairs = [(b, h) for b in range(1, 8) for h in sorted({0, H // 2, H - 1})]
+    ref = oracle_pairs(w, 0, lens, pairs, mqa=True)
+    compare(w, got, ref, pairs, f"r0_fp32_edges_{H}_{d_h}")
+    assert torch.equal(got[0], torch.zeros_like(got[0]))  # empty sequence
 
 
 def test_partial_plus_merge_equals_decode_and_is_deterministic():
@@ -196,7 +231,7 @@ def test_empty_and_zero_max_len():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(32, 128, 64), (16, 128, 48), (8, 64, 8), (32, 128, 0)])
+@pytest.mark.parametrize("shape", [(32, 128, 64), (16, 128, 48), (8, 64, 8), (32, 128, 0), (8, 64, 0)])
 def test_rows_past_the_end_are_never_used(dtype, shape):
     """Rows at or past seq_lens[b] hold NaN: outputs must stay finite and equal the clean run bit for bit."""
     H, d_h, r = shape
