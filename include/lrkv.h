@@ -106,13 +106,18 @@ lrkv_status lrkv_cache_append(const lrkv_dims* dims, const lrkv_cache* cache, co
                               const void* zk_new, const void* zv_new, void* stream);
 
 /* Bytes of device workspace lrkv_decode / lrkv_decode_partial need for these
- * dims and this max_len.  Host arithmetic only.  Returns 0 for invalid dims. */
+ * dims and this max_len: G x H x align4(d_h + r + 2) floats, G as returned by
+ * lrkv_decode_num_splits.  Host arithmetic only.  Returns 0 for invalid dims. */
 size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
 
-/* Number of sequence splits (S) the decode uses for these dims and max_len,
- * and the split granule in rows (*chunk_tokens, may be NULL): split s of
- * sequence b holds live rows iff s * granule < seq_lens[b].  Host arithmetic
- * only.  Returns 0 for invalid dims or max_len == 0. */
+/* Split plan of the decode for these dims and max_len: returns G, the number
+ * of partial records per head the workspace holds (the split kernel launches
+ * G workgroups for the whole batch), and the split granule in rows
+ * (*chunk_tokens, may be NULL).  On the device the G workgroups are dealt to
+ * the sequences in proportion to their live lengths, at least one each;
+ * split s of sequence b takes the granule-row tiles s, s + S_b, s + 2 S_b, ...
+ * of the sequence and holds live rows iff s * granule < seq_lens[b].
+ * Host arithmetic only.  Returns 0 for invalid dims or max_len == 0. */
 int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens);
 
 /* One decode step against the factored history (review sec. 3, Algorithm 2
@@ -129,12 +134,14 @@ int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* 
  *   out        device [batch][H][d_h] fp32 (written completely; 0 for a sequence with no live rows)
  *   workspace  device, >= lrkv_decode_workspace_bytes(dims, max_len) bytes, 256-byte aligned
  * Lengths outside [0, max_len] are clamped into it on the device (memory safe,
- * result then undefined).  The work is split along the sequence into S chunks
- * whose partial softmax states are merged in a fixed order, so results are
- * bitwise reproducible for fixed dims and max_len.
- * Supported: d_h <= 256, r <= 256, H * (d_h + r + 2) * 4 <= 64 KiB; the fast
- * bf16 kernels cover d_h in {64, 128}, r in {0, 8, 16, 32, 48, 64}, H a multiple of
- * 8 up to 32; other valid shapes use the general kernels. */
+ * result then undefined).  The work of every sequence is split along the
+ * sequence (see lrkv_decode_num_splits) and the splits' partial softmax states
+ * are merged in a fixed order, so results are bitwise reproducible for fixed
+ * dims, max_len and seq_lens contents.
+ * Supported: d_h <= 256, r <= 256, H * (d_h + r + 2) * 4 <= 64 KiB.  Matrix-core
+ * kernels cover bf16 with d_h in {64, 128}, r in {0, 8, 16, 32, 48, 64} and fp32
+ * with r = 0, d_h in {64, 128}, both for H in {8, 16, 32} and L_cap a multiple
+ * of 32; other valid shapes use the general kernels. */
 lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
                         const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes,
                         void* stream);

@@ -2,8 +2,9 @@
 // bf16 inputs, fp32 arithmetic.  Used for fp32 problems and for shapes the
 // MFMA kernel does not cover.
 //
-// One workgroup owns one (sequence b, split of `chunk` tokens) for all H
-// heads.  Per tile of kTile tokens the shared key/value rows are staged once
+// One workgroup owns one (sequence b, split) for all H heads; splits are dealt
+// to sequences by length and a split takes every S_b-th tile of kTile tokens
+// of its sequence.  Per tile the shared key/value rows are staged once
 // in LDS (as fp32) and reused by every head; each head then
 //   scores  s_j = (q_h . k_j + p_h . z^K_{h,j}) * log2(e)/sqrt(d_h)
 //   updates its running max, denominator and both numerators (online softmax)
@@ -40,12 +41,13 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     float* lrow = mrow + H;                    // [H]
     float* ebuf = lrow + H;                    // [4][kTile]
 
-    const int b = blockIdx.y, split = blockIdx.x;
-    int Lb = a.seq_lens[b];
-    Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
-    const int t_begin = split * a.chunk;
-    if (t_begin >= Lb) return;  // no live rows in this split; the merge skips it
-    const int t_end = min(t_begin + a.chunk, Lb);
+    // which sequence and split (splits dealt to sequences by length); split s of sequence b takes the
+    // tiles s, s + S_b, s + 2 S_b, ... of the sequence
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const int b = wslot.b, split = wslot.s;
+    if (b < 0) return;
+    const int Lb = clamped_len(a.seq_lens, b, a.max_len);
+    if (split * kTile >= Lb) return;  // no live rows in this split; the merge skips it
 
     const T* ks = (const T*)a.k_shared + (size_t)b * a.L_cap * D;
     const T* vs = (const T*)a.v_shared + (size_t)b * a.L_cap * D;
@@ -61,8 +63,8 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
         lrow[i] = 0.f;
     }
 
-    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        const int nvalid = min(kTile, t_end - t0);
+    for (int t0 = split * kTile; t0 < Lb; t0 += wslot.S_b * kTile) {
+        const int nvalid = min(kTile, Lb - t0);
         __syncthreads();  // previous tile fully consumed (and state initialised)
         for (int idx = tid; idx < kTile * D; idx += kThreads) {
             const int t = idx / D, c = idx - t * D;
@@ -117,7 +119,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    float* out = a.ws + ((size_t)b * a.num_splits + split) * H * rec;
+    float* out = a.ws + (size_t)blockIdx.x * H * rec;  // record of workgroup w = W_b + split
     for (int idx = tid; idx < H * rec; idx += kThreads) {
         const int h = idx / rec, k = idx - h * rec;
         float v = 0.f;
@@ -130,6 +132,8 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
 
 }  // namespace
 
+int general_rows_per_tile() { return kTile; }
+
 size_t general_lds_bytes(int H, int d_h, int r) { return general_lds_floats(H, d_h, r) * sizeof(float); }
 
 bool general_path_supports(int H, int d_h, int r) {
@@ -137,7 +141,7 @@ bool general_path_supports(int H, int d_h, int r) {
 }
 
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream) {
-    dim3 grid(a.num_splits, a.batch), block(kThreads);
+    dim3 grid(a.num_splits), block(kThreads);
     const size_t lds = general_lds_bytes(a.H, a.d_h, a.r);
     if (a.dtype == 0)
         hipLaunchKernelGGL(split_general_kernel<float>, grid, block, lds, stream, a);

@@ -172,14 +172,13 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     uint16_t* vt = (uint16_t*)my;
     float* xb = (float*)(my + C::VT_BYTES);
 
-    // Which 32-row blocks this workgroup's row lanes take:
-    //   interleaved: blocks are dealt round-robin over all (split, row lane) slots, slot
-    //                (split, tl) takes blocks split*NTL + tl + k*S*NTL;
-    //   contiguous:  split s owns rows [s*chunk, (s+1)*chunk) and its row lanes take every
-    //                NTL-th block of that range.
-    const int b = blockIdx.y, split = blockIdx.x;
-    int Lb = a.seq_lens[b];
-    Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
+    // Which sequence and split this workgroup handles (splits dealt to sequences by length), and
+    // which 32-row blocks its row lanes take: blocks are dealt round-robin over the (split, row lane)
+    // slots of the sequence, slot (split, tl) takes blocks split*NTL + tl + k*S_b*NTL.
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const int b = wslot.b, split = wslot.s;
+    if (b < 0) return;
+    const int Lb = clamped_len(a.seq_lens, b, a.max_len);
     if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
     const int nb = (Lb + kRows - 1) / kRows;  // blocks of this sequence
 
@@ -317,16 +316,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         }
     };
 
-    int first_blk, step_blk, last_blk;  // this row lane: blocks first, first + step, ... < last
-    if (a.interleave) {
-        first_blk = split * C::NTL + tl;
-        step_blk = a.num_splits * C::NTL;
-        last_blk = nb;
-    } else {
-        first_blk = split * (a.chunk / kRows) + tl;
-        step_blk = C::NTL;
-        last_blk = min(nb, (split + 1) * (a.chunk / kRows));
-    }
+    const int first_blk = split * C::NTL + tl, step_blk = wslot.S_b * C::NTL, last_blk = nb;
     const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
     // Sequence b walks its blocks starting b/batch of the way along (the same blocks, rotated order).
     // Otherwise every sequence reads the same relative position of its cache region at the same time,
@@ -576,7 +566,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         }
         __syncthreads();
     }
-    float* out = a.ws + ((size_t)b * a.num_splits + split) * H * C::REC;
+    float* out = a.ws + (size_t)blockIdx.x * H * C::REC;  // record of workgroup w = W_b + split
     for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
 }
 
@@ -586,7 +576,7 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     auto kern = split_mfma_kernel<D, R, H, OCC>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.num_splits, a.batch), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@
 // records as the bf16 kernel; the merge kernel combines them.
 //
 // Work decomposition (as in the bf16 kernel): a workgroup of 4 waves owns one
-// (b, split); a wave owns 16 heads (MFMA N) on one row lane of 32-row blocks,
-// blocks dealt round-robin over all (split, row lane) slots.  Per block:
+// (b, split), splits dealt to sequences by length; a wave owns 16 heads (MFMA
+// N) on one row lane of 32-row blocks, blocks dealt round-robin over the
+// sequence's (split, row lane) slots.  Per block:
 //   S^T[32 rows x 16 heads] = K[32 x d_h] Q^T         (two 16-row halves)
 //   online softmax on S^T in the MFMA result layout (lane = head, 8 rows)
 //   O^T[d_h x 16 heads]    += V^T[d_h x 32 rows] P^T
@@ -71,9 +72,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hg = wave % C::NHG, tl = wave / C::NHG;
-    const int b = blockIdx.y, split = blockIdx.x;
-    int Lb = a.seq_lens[b];
-    Lb = Lb < 0 ? 0 : (Lb > a.max_len ? a.max_len : Lb);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const int b = wslot.b, split = wslot.s;
+    if (b < 0) return;
+    const int Lb = clamped_len(a.seq_lens, b, a.max_len);
     if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
     const int nb = (Lb + kRows - 1) / kRows;
 
@@ -134,16 +136,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    int first_blk, step_blk, last_blk;
-    if (a.interleave) {
-        first_blk = split * C::NTL + tl;
-        step_blk = a.num_splits * C::NTL;
-        last_blk = nb;
-    } else {
-        first_blk = split * (a.chunk / kRows) + tl;
-        step_blk = C::NTL;
-        last_blk = min(nb, (split + 1) * (a.chunk / kRows));
-    }
+    const int first_blk = split * C::NTL + tl, step_blk = wslot.S_b * C::NTL, last_blk = nb;
     const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
     // sequence b walks its blocks starting b/batch of the way along (same blocks, rotated order)
     const int rot = (int)(((long)nmine * b) / a.batch);
@@ -256,7 +249,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
         }
         __syncthreads();
     }
-    float* out = a.ws + ((size_t)b * a.num_splits + split) * H * C::REC;
+    float* out = a.ws + (size_t)blockIdx.x * H * C::REC;  // record of workgroup w = W_b + split
     for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
 }
 
@@ -264,7 +257,7 @@ template <int D, int H, int OCC>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     using C = CfgF32<D, H, OCC>;
     auto kern = split_mfma_f32_kernel<D, H, OCC>;
-    hipLaunchKernelGGL(kern, dim3(a.num_splits, a.batch), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 

@@ -11,6 +11,10 @@
 // ("Low-Rank Key Value Attention: Chinese reading notes", sec. 2.4 Eq. (7)).
 // A sequence with no live rows gets out = 0.
 //
+// Split s of sequence b is the partial record of workgroup W_b + s of the
+// split launch (splits dealt to sequences by length; see lrkv_device.hpp);
+// only splits with s * granule < L_b hold live rows.
+//
 // One workgroup of 1024 threads per (b, h): thread (column c, split group j)
 // sums splits s = j, j + 4, ... of column c with four independent partial sums
 // (memory-level parallelism), then the four groups are added in LDS in a fixed
@@ -37,26 +41,28 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(int H, int D, int R, int max_len, int chunk, int S,
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, int D, int R, int max_len, int chunk,
+                                                              int S,
                                                               const int32_t* __restrict__ seq_lens,
                                                               const T* __restrict__ B_v, float* __restrict__ out,
                                                               const float* __restrict__ ws) {
     extern __shared__ float sm[];
-    float* w = sm;                          // [S] split weights
-    float* part = w + S;                    // [kGroups][kCols] per-group column sums
+    float* w = sm;                          // [S - batch + 1] split weights
+    float* part = w + (S - batch + 1);      // [kGroups][kCols] per-group column sums
     float* sums = part + kGroups * kCols;   // [D + R] merged numerators
     float* red = sums + D + R;              // [16] reduction scratch
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int rec = partial_record_floats(D, R);
     float* o = out + ((size_t)b * H + h) * D;
-    int Lb = seq_lens[b];
-    Lb = Lb < 0 ? 0 : (Lb > max_len ? max_len : Lb);
-    const int Sb = min(S, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold live rows
+    const int Lb = clamped_len(seq_lens, b, max_len);
+    int W_b, S_b;
+    sequence_splits(seq_lens, batch, max_len, S, b, &W_b, &S_b);  // every wave computes the same values
+    const int Sb = min(S_b, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold live rows
     if (Sb == 0) {
         for (int c = tid; c < D; c += kMergeThreads) o[c] = 0.f;
         return;
     }
-    const float* base = ws + ((size_t)b * S * H + h) * rec;  // split s at base + s * H * rec
+    const float* base = ws + ((size_t)W_b * H + h) * rec;  // split s at base + s * H * rec
     const size_t sstride = (size_t)H * rec;
 
     float mloc = -INFINITY;
@@ -107,12 +113,15 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int H, int D, int 
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream) {
     dim3 grid(H, batch), block(kMergeThreads);
-    const size_t lds = sizeof(float) * ((size_t)num_splits + kGroups * kCols + (size_t)d_h + r + 16);
+    // a sequence has at most num_splits - batch + 1 splits (every other sequence holds at least one)
+    const size_t max_sb = (size_t)(num_splits - batch + 1);
+    const size_t lds = sizeof(float) * (max_sb + kGroups * kCols + (size_t)d_h + r + 16);
     if (dtype == 0)
-        hipLaunchKernelGGL(merge_kernel<float>, grid, block, lds, stream, H, d_h, r, max_len, chunk, num_splits,
+        hipLaunchKernelGGL(merge_kernel<float>, grid, block, lds, stream, batch, H, d_h, r, max_len, chunk, num_splits,
                            seq_lens, (const float*)B_v, out, ws);
     else
-        hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, block, lds, stream, H, d_h, r, max_len, chunk, num_splits,
+        hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, block, lds, stream, batch, H, d_h, r, max_len, chunk,
+                           num_splits,
                            seq_lens, (const uint16_t*)B_v, out, ws);
     return hipGetLastError();
 }

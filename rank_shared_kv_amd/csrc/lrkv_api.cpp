@@ -72,18 +72,19 @@ int env_int(const char* name, int dflt) {
 }
 
 // Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes
-// are known on the host without a device.  A plan is (S splits per sequence,
-// granule g): split s of sequence b holds live rows iff s * g < L_b.  The
-// general kernel gives split s the contiguous rows [s*g, (s+1)*g); the MFMA
-// kernel deals g-row tiles round-robin over the S splits.  S is chosen so the
-// split kernel launches about one round of resident workgroups (MI355X has
-// 256 CUs), never more than kMaxSplits per sequence.  The plan does not
-// depend on r so that problems differing only in rank reduce in the same order.
+// are known on the host without a device.  A plan is (G workgroups for the
+// whole batch, granule g in rows).  On the device the G workgroups are dealt
+// to the sequences in proportion to their lengths, at least one each
+// (lrkv_device.hpp); split s of sequence b takes the g-row tiles s, s + S_b,
+// ... of the sequence and writes partial record W_b + s.  G aims at one
+// resident round of workgroups (MI355X has 256 CUs; the matrix-core kernels
+// hold `occupancy` workgroups per CU), never fewer than one per sequence nor
+// more than one per tile of every sequence.  The plan does not depend on r
+// within a kernel, so problems differing only in rank reduce in the same order.
 // Tuning overrides (read at every call, so they must not change between a
 // workspace query and the decode that uses it): LRKV_OCCUPANCY (1 or 2 waves
-// per SIMD), LRKV_INTERLEAVE (1 round-robin tiles, 2 contiguous chunks),
-// LRKV_TARGET_WGS, LRKV_SPLITS, LRKV_CHUNK.
-constexpr int kMaxSplits = 4096;
+// per SIMD), LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch).
+constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
 bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
     using namespace lrkv;
@@ -101,51 +102,26 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
         return false;
     }
     const bool mfma = p.path != SplitPath::kGeneral;
-    const int tile = mfma ? mfma_rows_per_tile(d.H) : 32;  // both MFMA kernels use the same block schedule
+    p.chunk = mfma ? mfma_rows_per_tile(d.H) : general_rows_per_tile();
     if (max_len <= 0) {
-        p.chunk = tile;
         p.num_splits = 0;
         *out = p;
         return true;
     }
-    const long tiles_per_seq = (max_len + tile - 1) / tile;
-    if (mfma) {
-        // Rows are dealt round-robin in tiles over the splits of a sequence, so any split count works;
-        // aim for one resident round of workgroups (occupancy x 256 CUs) over the whole batch.
-        const long target = env_int("LRKV_TARGET_WGS", 256 * p.occupancy);
-        long S = std::max<long>(1, target / d.batch);
-        const int forced = env_int("LRKV_SPLITS", 0);
-        if (forced > 0) S = forced;
-        S = std::min<long>(std::min<long>(S, tiles_per_seq), kMaxSplits);
-        p.interleave = env_int("LRKV_INTERLEAVE", 1) == 2 ? 0 : 1;
-        if (p.interleave) {
-            p.chunk = tile;  // granule: split s holds rows iff s * tile < L_b
-            p.num_splits = (int)S;
-        } else {
-            const long tiles_per_split = (tiles_per_seq + S - 1) / S;
-            p.chunk = (int)(tiles_per_split * tile);
-            p.num_splits = (int)((max_len + p.chunk - 1) / p.chunk);
-        }
-    } else {
-        // contiguous chunks of whole tiles, about `target` workgroups over the batch
-        const long total_tiles = tiles_per_seq * d.batch;
-        const int target = env_int("LRKV_TARGET_WGS", 1024);
-        long tiles_per_split = (total_tiles + target - 1) / target;
-        tiles_per_split = std::max<long>(tiles_per_split, (tiles_per_seq + kMaxSplits - 1) / kMaxSplits);
-        tiles_per_split = std::max<long>(1, std::min(tiles_per_split, tiles_per_seq));
-        const int forced = env_int("LRKV_CHUNK", 0);
-        if (forced > 0) tiles_per_split = std::max<long>(1, std::min<long>((forced + tile - 1) / tile, tiles_per_seq));
-        p.chunk = (int)(tiles_per_split * tile);
-        p.num_splits = (int)((max_len + p.chunk - 1) / p.chunk);
-        if (p.num_splits > kMaxSplits) return false;
-    }
+    const long tiles_per_seq = (max_len + p.chunk - 1) / p.chunk;
+    long G = env_int("LRKV_TARGET_WGS", mfma ? 256 * p.occupancy : 1024);
+    const int forced = env_int("LRKV_SPLITS", 0);
+    if (forced > 0) G = (long)forced * d.batch;
+    G = std::min<long>(G, (long)d.batch + kMaxExtraSplits);
+    G = std::min<long>(G, (long)d.batch * tiles_per_seq);
+    G = std::max<long>(G, d.batch);
+    p.num_splits = (int)G;
     *out = p;
     return true;
 }
 
 size_t workspace_bytes(const lrkv_dims& d, const lrkv::SplitPlan& p) {
-    return sizeof(float) * (size_t)d.batch * (size_t)p.num_splits * (size_t)d.H *
-           (size_t)lrkv::partial_record_floats(d.d_h, d.r);
+    return sizeof(float) * (size_t)p.num_splits * (size_t)d.H * (size_t)lrkv::partial_record_floats(d.d_h, d.r);
 }
 
 lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan) {
@@ -181,7 +157,6 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.max_len = max_len;
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
-    a.interleave = plan.interleave;
     a.k_shared = c.k_shared;
     a.v_shared = c.v_shared;
     a.z_k = c.z_k;

@@ -51,4 +51,92 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // log2(e): scores are carried in log2 units so that exp2 (v_exp_f32) applies.
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---------------------------------------------------------------------------
+// Length-proportional split plan, evaluated on the device from seq_lens.
+//
+// A decode launches G workgroups for the whole batch.  They are dealt to the
+// sequences in proportion to each sequence's number of 32-row blocks, at
+// least one each: with G' = G - batch, C_b = blocks of sequences 0..b and
+// T = C_{batch-1},
+//   W_b = b + floor(G' * C_{b-1} / T)      first workgroup of sequence b
+//   S_b = W_{b+1} - W_b                    its number of splits
+// (with T = 0 every sequence gets one workgroup, W_b = b).  Workgroup
+// w = W_b + s handles split s of sequence b and writes partial record w.
+// Split s of sequence b holds live rows iff s * granule < L_b.  The split
+// kernels and the merge kernel evaluate the same integer formulas, so they
+// agree on every W_b and S_b.  All helpers below are wave-level: every lane
+// of the calling wave must call them, and they return wave-uniform values.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int max_len) {
+    const int L = seq_lens[b];
+    return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+__device__ __forceinline__ int len_blocks(int L) { return (L + 31) >> 5; }
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return __builtin_amdgcn_readfirstlane(v);  // equal in every lane
+}
+
+// total blocks T of the batch
+__device__ inline int batch_blocks(const int32_t* seq_lens, int batch, int max_len) {
+    int t = 0;
+    for (int i = (int)(threadIdx.x & 63); i < batch; i += 64) t += len_blocks(clamped_len(seq_lens, i, max_len));
+    return wave_sum_i32(t);
+}
+
+__device__ __forceinline__ int first_workgroup(int b, int blocks_before, int extra, int total) {
+    return b + (total > 0 ? (int)(((long long)extra * blocks_before) / total) : 0);
+}
+
+struct SplitSlot {
+    int b;    // sequence, or -1 if workgroup w has none
+    int s;    // split index within the sequence
+    int S_b;  // splits of the sequence
+};
+
+// The (sequence, split) that workgroup w of a G-workgroup launch handles.
+__device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int max_len, int G, int w) {
+    const int lane = threadIdx.x & 63;
+    const int T = batch_blocks(seq_lens, batch, max_len);
+    const int extra = G - batch;
+    int carry = 0;
+    for (int c0 = 0; c0 < batch; c0 += 64) {
+        const int b = c0 + lane;
+        const int nbk = (b < batch) ? len_blocks(clamped_len(seq_lens, b, max_len)) : 0;
+        int incl = nbk;  // inclusive scan over the lanes of this chunk of 64 sequences
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const int before = carry + incl - nbk;
+        const int W0 = first_workgroup(b, before, extra, T);
+        const int W1 = first_workgroup(b + 1, before + nbk, extra, T);
+        const unsigned long long hit = __ballot(b < batch && w >= W0 && w < W1);
+        if (hit) {
+            // the values are wave-uniform; readfirstlane lets the compiler keep them (and every block
+            // offset derived from them) in scalar registers
+            const int src = __builtin_ctzll(hit);
+            return SplitSlot{__builtin_amdgcn_readfirstlane(__shfl(b, src)),
+                             __builtin_amdgcn_readfirstlane(w - __shfl(W0, src)),
+                             __builtin_amdgcn_readfirstlane(__shfl(W1 - W0, src))};
+        }
+        carry += __shfl(incl, 63);
+    }
+    return SplitSlot{-1, 0, 0};
+}
+
+// First workgroup W_b and split count S_b of sequence b.
+__device__ inline void sequence_splits(const int32_t* seq_lens, int batch, int max_len, int G, int b, int* W_b,
+                                       int* S_b) {
+    const int T = batch_blocks(seq_lens, batch, max_len);
+    int before = 0;
+    for (int i = (int)(threadIdx.x & 63); i < b; i += 64) before += len_blocks(clamped_len(seq_lens, i, max_len));
+    before = wave_sum_i32(before);
+    const int nbk = len_blocks(clamped_len(seq_lens, b, max_len));
+    const int W0 = first_workgroup(b, before, G - batch, T);
+    *W_b = __builtin_amdgcn_readfirstlane(W0);
+    *S_b = __builtin_amdgcn_readfirstlane(first_workgroup(b + 1, before + nbk, G - batch, T) - W0);
+}
+
 }  // namespace lrkv

@@ -13,8 +13,7 @@ struct DecodeArgs {
     int batch, H, d_h, r, L_cap, dtype;
     int max_len;         // host bound of seq_lens
     int chunk;           // split granule in rows: split s holds live rows iff s * chunk < L_b
-    int num_splits;      // S
-    int interleave;      // MFMA kernel: 1 = tiles dealt round-robin over splits, 0 = contiguous chunks
+    int num_splits;      // G: workgroups of the launch = partial records per head (shared by the batch)
     const void* k_shared;
     const void* v_shared;
     const void* z_k;
@@ -22,7 +21,7 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const void* q;
     const float* p;
-    float* ws;           // [batch][S][H][record]
+    float* ws;           // [G][H][record]
 };
 
 // Which split kernel a problem uses.
@@ -32,10 +31,9 @@ enum class SplitPath { kGeneral, kMfmaBf16, kMfmaF32 };
 // sizes are known without a GPU.
 struct SplitPlan {
     SplitPath path;
-    int chunk;       // tokens per split (multiple of the kernel's token tile)
-    int num_splits;  // ceil(max_len / chunk)
-    int occupancy;   // MFMA kernel: waves per SIMD it is compiled for (1 or 2)
-    int interleave;  // MFMA kernel: 1 = tiles dealt round-robin over the splits, 0 = contiguous chunks
+    int chunk;       // split granule in rows (the kernel's tile: rows a split advances per step)
+    int num_splits;  // G: workgroups for the whole batch, dealt to sequences by length on the device
+    int occupancy;   // MFMA kernels: waves per SIMD they are compiled for (1 or 2)
 };
 
 bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);      // bf16 MFMA kernel
@@ -54,5 +52,6 @@ hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t str
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream);
+int general_rows_per_tile();  // rows one general-kernel split advances per step
 
 }  // namespace lrkv

@@ -192,12 +192,18 @@ def test_split_plan_arithmetic():
     for (B, H, d_h, r, L, dt) in [(1, 4, 16, 4, 64, 0), (8, 8, 64, 8, 2048, 1), (16, 16, 128, 48, 8192, 1),
                                   (4, 32, 128, 64, 32768, 1), (64, 32, 128, 32, 32768, 1), (64, 32, 128, 0, 32768, 0)]:
         d = lk.make_dims(B, H, d_h, r, L, dt)
-        S, chunk = lk.lrkv_decode_num_splits(d, L)
-        assert 1 <= S <= math.ceil(L / chunk) and chunk % 32 == 0 and S <= 4096
+        G, chunk = lk.lrkv_decode_num_splits(d, L)
+        # G workgroups for the whole batch: at least one per sequence, at most one per tile of every sequence
+        assert B <= G <= B * math.ceil(L / chunk) and chunk % 32 == 0 and G <= B + 8192
         rec = ((d_h + r + 2) + 3) // 4 * 4
-        assert lk.lrkv_decode_workspace_bytes(d, L) == 4 * B * S * H * rec
-        # the plan depends on the shape and max_len, not on the rank
-        assert lk.lrkv_decode_num_splits(lk.make_dims(B, H, d_h, 0, L, dt), L) == (S, chunk)
+        assert lk.lrkv_decode_workspace_bytes(d, L) == 4 * G * H * rec
+        # within a kernel the plan depends on the shape and max_len, not on the rank
+        if dt == 1 or r == 0:
+            assert lk.lrkv_decode_num_splits(lk.make_dims(B, H, d_h, 0, L, dt), L) == (G, chunk)
+    # one resident round of workgroups on the 256 CUs for the long-context shape
+    assert lk.lrkv_decode_num_splits(lk.make_dims(4, 32, 128, 64, 33024, 1), 32818) == (256, 64)
+    # short contexts: never more workgroups than tiles
+    assert lk.lrkv_decode_num_splits(lk.make_dims(4, 32, 128, 64, 256, 1), 64) == (4, 64)
     d = lk.make_dims(2, 8, 64, 8, 256, 1)
     assert lk.lrkv_decode_num_splits(d, 0) == (0, 0)
     assert lk.lrkv_decode_workspace_bytes(d, 0) == 0

@@ -252,3 +252,28 @@ def test_rows_past_the_end_are_never_used(dtype, shape):
     dirty = gpu_decode(w, dev, 300, L_cap=320)
     assert bool(torch.isfinite(dirty).all())
     assert torch.equal(clean, dirty)
+
+
+@pytest.mark.parametrize("dtype,H,d_h,r", [("bf16", 32, 128, 64), ("f32", 32, 128, 0), ("f32", 8, 64, 16)])
+@pytest.mark.parametrize("mix", ["one_long", "skewed", "all_empty"])
+def test_length_proportional_splits(dtype, H, d_h, r, mix):
+    """Splits are dealt to sequences by length on the device: one long sequence among empty ones, a skewed
+    mix, and an all-empty batch (bf16 and fp32 matrix-core kernels, general kernel)."""
+    lens = {"one_long": [0] * 15 + [5000],
+            "skewed": [1, 2, 3000, 33, 0, 700, 64, 65, 4999, 31, 32, 5000, 128, 0, 1, 96],
+            "all_empty": [0] * 16}[mix]
+    lens = np.array(lens, dtype=np.int32)
+    w = synth.WORKLOADS["ragged"].with_(name=f"lp_{mix}_{dtype}_{H}_{d_h}_{r}", batch=16, H=H, d_h=d_h, r=r,
+                                        dtype=dtype, L=5000, L_cap=5024, ragged_lo=None)
+    G, chunk = lk.lrkv_decode_num_splits(dims_of(w, 5024), 5000)
+    say(f"[case] length-proportional splits {mix} {dtype} H={H} d_h={d_h} r={r}: G={G} granule={chunk}")
+    dev = sdev.fill_layer(w, 0, L_cap=5024, lengths=lens)
+    got = gpu_decode(w, dev, 5000, L_cap=5024)
+    live = [b for b in range(16) if lens[b] > 0]
+    for b in range(16):
+        if lens[b] == 0:
+            assert torch.equal(got[b], torch.zeros_like(got[b]))
+    if live:
+        pairs = [(b, h) for b in live for h in sorted({0, H - 1})]
+        ref = oracle_pairs(w, 0, lens, pairs, mqa=(r == 0))
+        compare(w, got, ref, pairs, f"lp_{mix}")
