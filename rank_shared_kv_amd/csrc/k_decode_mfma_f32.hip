@@ -11,10 +11,11 @@
 // fp32 accumulation).  The kernel writes the same per-split online-softmax
 // records as the bf16 kernel; the merge kernel combines them.
 //
-// Work decomposition (as in the bf16 kernel): a workgroup of 4 waves owns one
-// (b, split), splits dealt to sequences by length; a wave owns 16 heads (MFMA
-// N) on one row lane of 32-row blocks, blocks dealt round-robin over the
-// sequence's (split, row lane) slots.  Per block:
+// Work decomposition: a workgroup of 4 waves owns one (b, split), splits dealt
+// to sequences by length; each wave is one row lane of 32-row blocks (blocks
+// dealt round-robin over the sequence's (split, row lane) slots) and handles
+// every head, in groups of 16 (MFMA N), so each key/value row is loaded by
+// exactly one wave.  Per block and head group:
 //   S^T[32 rows x 16 heads] = K[32 x d_h] Q^T         (two 16-row halves)
 //   online softmax on S^T in the MFMA result layout (lane = head, 8 rows)
 //   O^T[d_h x 16 heads]    += V^T[d_h x 32 rows] P^T
@@ -43,17 +44,19 @@ constexpr int kWaves = 4;
 
 template <int D, int H, int OCC>
 struct CfgF32 {
-    static constexpr int NHG = (H + 15) / 16;        // head groups of 16 (MFMA N)
-    static constexpr int NTL = kWaves / NHG;          // row lanes per workgroup
+    static constexpr int NHG = (H + 15) / 16;        // head groups of 16 (MFMA N), all handled by every wave
+    static constexpr int NTL = kWaves;                // row lanes per workgroup: one per wave
     static constexpr int KLD = D / 16;                // 16-byte loads per lane per key half
     static constexpr int VP = D / 64;                 // 64-column blocks of a value row
-    static constexpr int UDW = D / 4;                 // dwords per unit (key half or value half)
-    static constexpr int NU = 4;                      // units per block: K half 0, K half 1, V half 0, V half 1
-    static constexpr int NSLOT = (OCC == 1) ? 4 : 2;  // ring depth (divides NU)
+    static constexpr int UDW = D / 8;                 // dwords per unit (a quarter of the key or value rows)
+    static constexpr int NU = 8;                      // units per block: 4 key quarters, then 4 value quarters
+    static constexpr int NSLOT = 8;                   // ring depth (divides NU)
     static constexpr int CB = D / 16;                 // column blocks of the value product
+    static constexpr int QS = D + 4;                  // floats per q row in LDS
     static constexpr int REC = ((D + 2) + 3) & ~3;
-    static constexpr int MW_BYTES = kWaves * 16 * 4;
-    static constexpr int LDS_BYTES = MW_BYTES + H * REC * 4;
+    static constexpr int Q_BYTES = NHG * 16 * QS * 4;
+    static constexpr int MW_BYTES = kWaves * NHG * 16 * 4;
+    static constexpr int LDS_BYTES = Q_BYTES + MW_BYTES + H * REC * 4;
     static_assert(D % 64 == 0, "head width");
     static_assert(H % 8 == 0 && H <= 32, "head count");
 };
@@ -65,13 +68,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 template <int D, int H, int OCC>
 __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(DecodeArgs a) {
     using C = CfgF32<D, H, OCC>;
-    constexpr int NSLOT = C::NSLOT, NU = C::NU, UDW = C::UDW;
+    constexpr int NSLOT = C::NSLOT, NU = C::NU, UDW = C::UDW, NHG = C::NHG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    float* mw_lds = (float*)lds;               // [waves][16] running maxima
-    float* mg = (float*)(lds + C::MW_BYTES);   // [H][REC] merged records
+    float* q_lds = (float*)lds;                              // [NHG * 16][QS] query rows (zero rows pad)
+    float* mw_lds = (float*)(lds + C::Q_BYTES);              // [waves][NHG * 16] running maxima
+    float* mg = (float*)(lds + C::Q_BYTES + C::MW_BYTES);   // [H][REC] merged records
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hg = wave % C::NHG, tl = wave / C::NHG;
+    const int tid = threadIdx.x, lane = tid & 63, tl = __builtin_amdgcn_readfirstlane(tid >> 6);
     const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
     const int b = wslot.b, split = wslot.s;
     if (b < 0) return;
@@ -80,20 +83,16 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     const int nb = (Lb + kRows - 1) / kRows;
 
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int head = 16 * hg + n16;
     const float scale = kLog2e / sqrtf((float)D);
 
-    // query fragments, kept for the whole kernel: qf[4 m + j] = q[head][16 m + 4 g4 + j] (zero for padded heads)
-    float qf[4 * C::KLD];
     {
-        const float* qg = (const float*)a.q + ((size_t)b * H + (head < H ? head : 0)) * D;
-#pragma unroll
-        for (int m = 0; m < C::KLD; ++m) {
-            const f32x4_t v = *(const f32x4_t*)(qg + 16 * m + 4 * g4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) qf[4 * m + j] = (head < H) ? v[j] : 0.f;
+        const float* qg = (const float*)a.q + (size_t)b * H * D;
+        for (int i = tid; i < NHG * 16 * D; i += kWaves * 64) {
+            const int h = i / D, c = i - h * D;
+            q_lds[h * C::QS + c] = (h < H) ? qg[(size_t)h * D + c] : 0.f;
         }
     }
+    __syncthreads();
 
     const uint32_t row_bytes = D * 4;
     const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const float*)a.k_shared + (size_t)b * a.L_cap * D,
@@ -103,39 +102,53 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     const uint32_t vo_k = (uint32_t)n16 * row_bytes + 16 * g4;       // row n16 of the half, columns 4 g4 + 16 m
     const uint32_t vo_v = (uint32_t)(4 * g4) * row_bytes + 16 * n16;  // rows 4 g4 + tt, columns 64 p + 4 n16
 
+    // Units of a block (8, equal size):
+    //   u = 0..3  key half u/2, 16-column blocks m of part u%2 (m in [KLD/2 * (u%2), KLD/2 * (u%2 + 1)))
+    //   u = 4..7  value half (u-4)/2, rows 4 g4 + tt with tt in {2 ((u-4)%2), 2 ((u-4)%2) + 1}
+    constexpr int KH = C::KLD / 2;
     uint32_t ring[NSLOT][UDW];
     auto issue = [&](int u, int t0, int slot) {
-        const int so = (t0 + 16 * (u & 1)) * (int)row_bytes;
-        if (u < 2) {
+        if (u < 4) {
+            const int so = (t0 + 16 * (u >> 1)) * (int)row_bytes;
 #pragma unroll
-            for (int m = 0; m < C::KLD; ++m) {
+            for (int mm = 0; mm < KH; ++mm) {
+                const int m = KH * (u & 1) + mm;
                 const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, vo_k + 64 * m, so, 0);
-                ring[slot][4 * m] = v.x;
-                ring[slot][4 * m + 1] = v.y;
-                ring[slot][4 * m + 2] = v.z;
-                ring[slot][4 * m + 3] = v.w;
+                ring[slot][4 * mm] = v.x;
+                ring[slot][4 * mm + 1] = v.y;
+                ring[slot][4 * mm + 2] = v.z;
+                ring[slot][4 * mm + 3] = v.w;
             }
         } else {
+            const int so = (t0 + 16 * ((u - 4) >> 1)) * (int)row_bytes;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+            for (int k = 0; k < 2; ++k) {
+                const int tt = 2 * ((u - 4) & 1) + k;
 #pragma unroll
                 for (int p = 0; p < C::VP; ++p) {
                     const v4u_t v =
                         __builtin_amdgcn_raw_buffer_load_b128(rs_v, vo_v + tt * row_bytes + 256 * p, so, 0);
-                    const int o = 4 * (tt * C::VP + p);
+                    const int o = 4 * (k * C::VP + p);
                     ring[slot][o] = v.x;
                     ring[slot][o + 1] = v.y;
                     ring[slot][o + 2] = v.z;
                     ring[slot][o + 3] = v.w;
                 }
+            }
         }
     };
 
-    f32x4_t acc[C::CB];
+    f32x4_t acc[NHG][C::CB];
+    float m_run[NHG], l_run[NHG];
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int g = 0; g < NHG; ++g) {
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) acc[g][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
+    // row lane tl of split s takes blocks s*NTL + tl + k*S_b*NTL of the sequence
     const int first_blk = split * C::NTL + tl, step_blk = wslot.S_b * C::NTL, last_blk = nb;
     const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
     // sequence b walks its blocks starting b/batch of the way along (same blocks, rotated order)
@@ -152,8 +165,9 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
         const int nvalid = min(kRows, Lb - t0);
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
         const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
-        f32x4_t s_sh[2];
-        float ev[8];
+        constexpr int NCH = (NHG == 1) ? 2 : 1;
+        f32x4_t s_sh[NHG][2], s_acc[NHG][NCH];
+        float ev[NHG][8];
 
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -164,87 +178,130 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
             }
             __builtin_amdgcn_sched_barrier(0);
             uint32_t* cur = ring[u % NSLOT];
-            if (u < 2) {
-                // S^T half u on the matrix cores
-                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+            if (u < 4) {
+                // S^T of key half u/2 on the matrix cores, 16-column blocks of part u%2; q fragments from
+                // LDS.  Two independent accumulation chains are interleaved (the head groups, or with one
+                // group its even and odd column blocks) so consecutive MFMAs never wait on each other.
+                if ((u & 1) == 0) {
 #pragma unroll
-                for (int t = 0; t < 4 * C::KLD; ++t)
-                    s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(cur[t]), qf[t], s, 0, 0, 0);
-                s_sh[u] = s;
-                if (u == 1) {
-                    // online softmax: lane (head n16, g4) holds rows 4 g4 + i and 16 + 4 g4 + i
-                    float sc[8];
+                    for (int g = 0; g < NHG; ++g)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        sc[i] = (4 * g4 + i < nvalid) ? s_sh[0][i] * scale : -INFINITY;
-                        sc[4 + i] = (16 + 4 * g4 + i < nvalid) ? s_sh[1][i] * scale : -INFINITY;
+                        for (int c = 0; c < NCH; ++c) s_acc[g][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int mm = 0; mm < KH; ++mm) {
+                    const int m = KH * (u & 1) + mm;
+                    f32x4_t qv[NHG];
+#pragma unroll
+                    for (int g = 0; g < NHG; ++g)
+                        qv[g] = *(const f32x4_t*)(q_lds + (16 * g + n16) * C::QS + 4 * g4 + 16 * m);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int g = 0; g < NHG; ++g)
+                            s_acc[g][m % NCH] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                __uint_as_float(cur[4 * mm + j]), qv[g][j], s_acc[g][m % NCH], 0, 0, 0);
+                }
+                if (u & 1) {
+#pragma unroll
+                    for (int g = 0; g < NHG; ++g)
+                        s_sh[g][u >> 1] = (NCH == 2) ? s_acc[g][0] + s_acc[g][NCH - 1] : s_acc[g][0];
+                }
+                if (u == 3) {
+                    // online softmax: lane (head n16 of group g, g4) holds rows 4 g4 + i and 16 + 4 g4 + i
+#pragma unroll
+                    for (int g = 0; g < NHG; ++g) {
+                        float sc[8];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            sc[i] = (4 * g4 + i < nvalid) ? s_sh[g][0][i] * scale : -INFINITY;
+                            sc[4 + i] = (16 + 4 * g4 + i < nvalid) ? s_sh[g][1][i] * scale : -INFINITY;
+                        }
+                        float tmax = sc[0];
+#pragma unroll
+                        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+                        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                        const float m_new = fmaxf(m_run[g], tmax);
+                        const float alpha = fast_exp2(m_run[g] - m_new);
+                        m_run[g] = m_new;
+                        float esum = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            ev[g][i] = fast_exp2(sc[i] - m_new);
+                            esum += ev[g][i];
+                        }
+                        l_run[g] = fmaf(alpha, l_run[g], esum);
+#pragma unroll
+                        for (int cb = 0; cb < C::CB; ++cb) acc[g][cb] *= alpha;
                     }
-                    float tmax = sc[0];
-#pragma unroll
-                    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
-                    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                    const float m_new = fmaxf(m_run, tmax);
-                    const float alpha = fast_exp2(m_run - m_new);
-                    m_run = m_new;
-                    float esum = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        ev[i] = fast_exp2(sc[i] - m_new);
-                        esum += ev[i];
-                    }
-                    l_run = fmaf(alpha, l_run, esum);
-#pragma unroll
-                    for (int cb = 0; cb < C::CB; ++cb) acc[cb] *= alpha;
                 }
             } else {
-                const int h = u - 2;  // value half: rows 16 h + 4 g4 + tt
+                const int h = (u - 4) >> 1;      // value half: rows 16 h + 4 g4 + tt
+                const int tp = 2 * ((u - 4) & 1);  // this unit holds tt = tp, tp + 1
                 if (nvalid < kRows) {
                     // last block of the sequence: rows past the end hold arbitrary values; zero them
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
-                        if (16 * h + 4 * g4 + tt >= nvalid) {
+                    for (int k = 0; k < 2; ++k)
+                        if (16 * h + 4 * g4 + tp + k >= nvalid) {
 #pragma unroll
-                            for (int k = 0; k < 4 * C::VP; ++k) cur[4 * tt * C::VP + k] = 0u;
+                            for (int e = 0; e < 4 * C::VP; ++e) cur[4 * k * C::VP + e] = 0u;
                         }
                 }
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
+                for (int g = 0; g < NHG; ++g)
 #pragma unroll
-                    for (int p = 0; p < C::VP; ++p)
+                    for (int k = 0; k < 2; ++k)
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const int cb = 4 * p + s;
-                            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                __uint_as_float(cur[4 * (tt * C::VP + p) + s]), ev[4 * h + tt], acc[cb], 0, 0, 0);
-                        }
+                        for (int p = 0; p < C::VP; ++p)
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                const int cb = 4 * p + s;
+                                acc[g][cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    __uint_as_float(cur[4 * (k * C::VP + p) + s]), ev[g][4 * h + tp + k],
+                                    acc[g][cb], 0, 0, 0);
+                            }
             }
         }
     }
 
-    // ---- merge the row lanes of each head group (fixed order), one record per head ----
-    l_run += __shfl_xor(l_run, 16);  // every lane of a head holds the same partial sum of its rows
-    l_run += __shfl_xor(l_run, 32);
-    if (g4 == 0) mw_lds[wave * 16 + n16] = m_run;
+    // ---- merge the row lanes (fixed order), one record per head ----
+#pragma unroll
+    for (int g = 0; g < NHG; ++g) {
+        l_run[g] += __shfl_xor(l_run[g], 16);  // every lane of a head holds the same partial sum of its rows
+        l_run[g] += __shfl_xor(l_run[g], 32);
+        if (g4 == 0) mw_lds[(tl * NHG + g) * 16 + n16] = m_run[g];
+    }
     __syncthreads();
-    float M = -INFINITY;
-    for (int t = 0; t < C::NTL; ++t) M = fmaxf(M, mw_lds[(t * C::NHG + hg) * 16 + n16]);
-    const float f = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+    float f[NHG], M[NHG];
+#pragma unroll
+    for (int g = 0; g < NHG; ++g) {
+        M[g] = -INFINITY;
+        for (int t = 0; t < C::NTL; ++t) M[g] = fmaxf(M[g], mw_lds[(t * NHG + g) * 16 + n16]);
+        f[g] = (m_run[g] == -INFINITY) ? 0.f : fast_exp2(m_run[g] - M[g]);
+    }
     for (int t = 0; t < C::NTL; ++t) {
-        if (tl == t && head < H) {
-            float* row = mg + head * C::REC;
+        if (tl == t) {
 #pragma unroll
-            for (int p = 0; p < C::VP; ++p)
+            for (int g = 0; g < NHG; ++g) {
+                const int head = 16 * g + n16;
+                if (head < H) {
+                    float* row = mg + head * C::REC;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4_t v = f32x4_t{acc[4 * p][i], acc[4 * p + 1][i], acc[4 * p + 2][i], acc[4 * p + 3][i]} * f;
-                    f32x4_t* dst = (f32x4_t*)(row + 64 * p + 16 * g4 + 4 * i);
-                    *dst = (t == 0) ? v : (*dst + v);
+                    for (int p = 0; p < C::VP; ++p)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const f32x4_t v = f32x4_t{acc[g][4 * p][i], acc[g][4 * p + 1][i], acc[g][4 * p + 2][i],
+                                                      acc[g][4 * p + 3][i]} * f[g];
+                            f32x4_t* dst = (f32x4_t*)(row + 64 * p + 16 * g4 + 4 * i);
+                            *dst = (t == 0) ? v : (*dst + v);
+                        }
+                    if (g4 == 0) {
+                        const float lv = l_run[g] * f[g];
+                        row[D + 1] = (t == 0) ? lv : row[D + 1] + lv;
+                        if (t == 0) row[D] = M[g];
+                    }
                 }
-            if (g4 == 0) {
-                const float lv = l_run * f;
-                row[D + 1] = (t == 0) ? lv : row[D + 1] + lv;
-                if (t == 0) row[D] = M;
             }
         }
         __syncthreads();
@@ -266,12 +323,17 @@ hipError_t launch_h(const DecodeArgs& a, int occ, hipStream_t stream) {
     switch (a.H) {
         case 8: return occ == 1 ? launch_one<D, 8, 1>(a, stream) : launch_one<D, 8, 2>(a, stream);
         case 16: return occ == 1 ? launch_one<D, 16, 1>(a, stream) : launch_one<D, 16, 2>(a, stream);
-        case 32: return occ == 1 ? launch_one<D, 32, 1>(a, stream) : launch_one<D, 32, 2>(a, stream);
+        case 32:
+            // 32 heads of width 128 per wave need more registers than two waves per SIMD leave
+            if constexpr (D == 128) return launch_one<D, 32, 1>(a, stream);
+            else return occ == 1 ? launch_one<D, 32, 1>(a, stream) : launch_one<D, 32, 2>(a, stream);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+int mfma_f32_rows_per_tile() { return kRows * kWaves; }
 
 bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap) {
     if (dtype != 0 || r != 0) return false;

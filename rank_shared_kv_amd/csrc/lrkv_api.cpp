@@ -102,7 +102,9 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
         return false;
     }
     const bool mfma = p.path != SplitPath::kGeneral;
-    p.chunk = mfma ? mfma_rows_per_tile(d.H) : general_rows_per_tile();
+    p.chunk = (p.path == SplitPath::kMfmaBf16)  ? mfma_rows_per_tile(d.H)
+              : (p.path == SplitPath::kMfmaF32) ? mfma_f32_rows_per_tile()
+                                                 : general_rows_per_tile();
     if (max_len <= 0) {
         p.num_splits = 0;
         *out = p;
