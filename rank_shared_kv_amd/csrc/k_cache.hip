@@ -49,6 +49,56 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_kernel(int H, int d_h, 
     }
 }
 
+// Vector path (rows of B^K a multiple of 16 bytes): q staged in LDS; thread (row group rg, vector vi)
+// reads B^K[h][c][vi*VE .. vi*VE + VE) for rows c = rg, rg + rpp, ... as 16-byte vectors and keeps VE
+// partial sums; the row groups are added in a fixed order in LDS.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int H, int d_h, int r, const T* __restrict__ q,
+                                                                    const T* __restrict__ B_k,
+                                                                    float* __restrict__ p) {
+    constexpr int VE = 16 / (int)sizeof(T);
+    __shared__ float qs[256];
+    __shared__ float part[kAbsorbThreads * VE];  // [row group][r]: rpp * r <= kAbsorbThreads * VE
+    const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x;
+    for (int c = tid; c < d_h; c += kAbsorbThreads) qs[c] = elem<T>::load(q, (size_t)bh * d_h + c);
+    __syncthreads();
+    const int nv = r / VE, rpp = kAbsorbThreads / nv;
+    const int vi = tid % nv, rg = tid / nv;
+    const int groups = min(rpp, d_h);
+    if (rg < groups) {
+        float acc[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+        const T* basis = B_k + (size_t)h * d_h * r + vi * VE;
+#pragma unroll 4
+        for (int c = rg; c < d_h; c += rpp) {
+            const u32x4_t v = *(const u32x4_t*)(basis + (size_t)c * r);
+            const float qc = qs[c];
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                float x;
+                if constexpr (sizeof(T) == 4) {
+                    x = __uint_as_float(v[e]);
+                } else {
+                    const uint32_t w = v[e >> 1];
+                    x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
+                }
+                acc[e] = fmaf(qc, x, acc[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VE; ++e) part[rg * r + vi * VE + e] = acc[e];
+    }
+    __syncthreads();
+    for (int i = tid; i < r; i += kAbsorbThreads) {
+        float sum = 0.f;
+        for (int g = 0; g < groups; ++g) sum += part[g * r + i];  // fixed order
+        p[(size_t)bh * r + i] = sum;
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int L_cap, T* __restrict__ k_shared,
                                                      T* __restrict__ v_shared, T* __restrict__ z_k,
@@ -65,16 +115,29 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
     const int j = row;
     if (j < 0) return;  // full or invalid: nothing written, length unchanged
     const size_t srow = ((size_t)b * L_cap + j) * d_h;
-    for (int c = threadIdx.x; c < d_h; c += blockDim.x) {
-        k_shared[srow + c] = k_new[(size_t)b * d_h + c];
-        v_shared[srow + c] = v_new[(size_t)b * d_h + c];
-    }
-    for (int idx = threadIdx.x; idx < H * r; idx += blockDim.x) {
-        const int h = idx / r, i = idx - h * r;
-        const size_t dst = (((size_t)b * L_cap + j) * H + h) * r + i;  // token-major latents
-        const size_t src = ((size_t)b * H + h) * r + i;
-        z_k[dst] = zk_new[src];
-        z_v[dst] = zv_new[src];
+    // token-major latents: token j's H x r latents of every head form one contiguous row, and the
+    // new rows [b][H][r] are contiguous too, so both copies are plain row copies
+    const size_t zrow = ((size_t)b * L_cap + j) * H * r, zsrc = (size_t)b * H * r;
+    constexpr int VE = 16 / (int)sizeof(T);
+    if ((d_h % VE) == 0 && ((H * r) % VE) == 0) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        for (int c = threadIdx.x; c < d_h / VE; c += blockDim.x) {
+            ((u32x4_t*)(k_shared + srow))[c] = ((const u32x4_t*)(k_new + (size_t)b * d_h))[c];
+            ((u32x4_t*)(v_shared + srow))[c] = ((const u32x4_t*)(v_new + (size_t)b * d_h))[c];
+        }
+        for (int c = threadIdx.x; c < H * r / VE; c += blockDim.x) {
+            ((u32x4_t*)(z_k + zrow))[c] = ((const u32x4_t*)(zk_new + zsrc))[c];
+            ((u32x4_t*)(z_v + zrow))[c] = ((const u32x4_t*)(zv_new + zsrc))[c];
+        }
+    } else {
+        for (int c = threadIdx.x; c < d_h; c += blockDim.x) {
+            k_shared[srow + c] = k_new[(size_t)b * d_h + c];
+            v_shared[srow + c] = v_new[(size_t)b * d_h + c];
+        }
+        for (int idx = threadIdx.x; idx < H * r; idx += blockDim.x) {
+            z_k[zrow + idx] = zk_new[zsrc + idx];
+            z_v[zrow + idx] = zv_new[zsrc + idx];
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) seq_lens[b] = j + 1;
@@ -85,12 +148,23 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
                          hipStream_t stream) {
     dim3 grid(batch * H), block(kAbsorbThreads);
-    if (dtype == 0)
-        hipLaunchKernelGGL(absorb_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
-                           (const float*)B_k, p);
-    else
-        hipLaunchKernelGGL(absorb_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
-                           (const uint16_t*)B_k, p);
+    const int ve = dtype == 0 ? 4 : 8;
+    const bool vec = (r % ve) == 0 && d_h <= 256;  // 16-byte rows of B^K; q row fits the LDS stage
+    if (dtype == 0) {
+        if (vec)
+            hipLaunchKernelGGL(absorb_vec_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
+                               (const float*)B_k, p);
+        else
+            hipLaunchKernelGGL(absorb_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
+                               (const float*)B_k, p);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL(absorb_vec_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
+                               (const uint16_t*)B_k, p);
+        else
+            hipLaunchKernelGGL(absorb_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
+                               (const uint16_t*)B_k, p);
+    }
     return hipGetLastError();
 }
 

@@ -16,9 +16,13 @@
 // only splits with s * granule < L_b hold live rows.
 //
 // One workgroup of 1024 threads per (b, h): thread (column c, split group j)
-// sums splits s = j, j + 4, ... of column c with four independent partial sums
-// (memory-level parallelism), then the four groups are added in LDS in a fixed
-// order -- results are bitwise reproducible.
+// walks splits s = j, j + 4, ... of column c once, in batches of 16 whose
+// loads are issued together, keeping its own running maximum and rescaling
+// its sum once per batch (no separate pass for the maxima).  The four groups
+// are then combined in LDS in a fixed order, so results are bitwise
+// reproducible.  The B^V row
+// fragments the epilogue needs are loaded at kernel start, off the critical
+// path.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
 
@@ -28,32 +32,42 @@ namespace {
 constexpr int kMergeThreads = 1024;
 constexpr int kCols = 256;                       // columns handled per pass
 constexpr int kGroups = kMergeThreads / kCols;   // split groups
+constexpr int kMaxCols = 512;                    // d_h + r <= 512
+constexpr int kBatch = 16;                       // splits per thread loaded together
 
-__device__ __forceinline__ float block_max(float v, float* red) {
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float m = red[0];
-    for (int w = 1; w < kMergeThreads / 64; ++w) m = fmaxf(m, red[w]);
-    __syncthreads();
-    return m;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ float vec_elem(const u32x4_t& v, int e) {
+    if constexpr (sizeof(T) == 4) {
+        return __uint_as_float(v[e]);
+    } else {
+        const uint32_t w = v[e >> 1];
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
 }
 
 template <typename T>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, int D, int R, int max_len, int chunk,
-                                                              int S,
-                                                              const int32_t* __restrict__ seq_lens,
+                                                              int S, const int32_t* __restrict__ seq_lens,
                                                               const T* __restrict__ B_v, float* __restrict__ out,
                                                               const float* __restrict__ ws) {
-    extern __shared__ float sm[];
-    float* w = sm;                          // [S - batch + 1] split weights
-    float* part = w + (S - batch + 1);      // [kGroups][kCols] per-group column sums
-    float* sums = part + kGroups * kCols;   // [D + R] merged numerators
-    float* red = sums + D + R;              // [16] reduction scratch
+    constexpr int VE = 16 / (int)sizeof(T);  // B^V elements per 16-byte vector
+    __shared__ float gmax[kGroups][kCols];   // per-group running maxima
+    __shared__ float gsum[kGroups][kCols];   // per-group rescaled sums
+    __shared__ float sums[kMaxCols + 2];     // merged numerators, then l at [D + R]
+    __shared__ float epi[kMergeThreads];     // epilogue partial products
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int rec = partial_record_floats(D, R);
     float* o = out + ((size_t)b * H + h) * D;
+
+    // epilogue operand: thread (c, vi) holds B^V[h][c][vi*VE, vi*VE + VE) as one 16-byte vector
+    const int nvv = (R > 0 && (R % VE) == 0) ? R / VE : 0;
+    const bool vec_epi = nvv > 0 && D * nvv <= kMergeThreads;
+    u32x4_t bv = {0u, 0u, 0u, 0u};
+    const int ec = vec_epi ? tid / nvv : 0, evi = vec_epi ? tid % nvv : 0;
+    if (vec_epi && ec < D) bv = *(const u32x4_t*)(B_v + ((size_t)h * D + ec) * R + evi * VE);
+
     const int Lb = clamped_len(seq_lens, b, max_len);
     int W_b, S_b;
     sequence_splits(seq_lens, batch, max_len, S, b, &W_b, &S_b);  // every wave computes the same values
@@ -63,48 +77,82 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, 
         return;
     }
     const float* base = ws + ((size_t)W_b * H + h) * rec;  // split s at base + s * H * rec
-    const size_t sstride = (size_t)H * rec;
-
-    float mloc = -INFINITY;
-    for (int s = tid; s < Sb; s += kMergeThreads) mloc = fmaxf(mloc, base[s * sstride + D + R]);
-    const float M = block_max(mloc, red);
-    for (int s = tid; s < Sb; s += kMergeThreads) w[s] = fast_exp2(base[s * sstride + D + R] - M);
-    __syncthreads();
+    const int sstride = H * rec;  // the workspace is far below 2^31 floats
 
     // numerators (columns 0 .. D+R-1) and the denominator (column D+R+1) in passes of kCols columns
     const int ncols = D + R + 2;
-    float l = 0.f;
     for (int c0 = 0; c0 < ncols; c0 += kCols) {
-        const int c = c0 + (tid % kCols), j = tid / kCols;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        const int cl = tid % kCols, j = tid / kCols, c = c0 + cl;
+        float mj = -INFINITY, sj = 0.f;
         if (c < ncols && c != D + R) {
-            int s = j;
-            for (; s + 3 * kGroups < Sb; s += 4 * kGroups) {
-                a0 = fmaf(w[s], base[(size_t)s * sstride + c], a0);
-                a1 = fmaf(w[s + kGroups], base[(size_t)(s + kGroups) * sstride + c], a1);
-                a2 = fmaf(w[s + 2 * kGroups], base[(size_t)(s + 2 * kGroups) * sstride + c], a2);
-                a3 = fmaf(w[s + 3 * kGroups], base[(size_t)(s + 3 * kGroups) * sstride + c], a3);
+            // batches of kBatch splits: all loads of a batch are issued together, one rescale per batch
+            for (int s0 = j; s0 < Sb; s0 += kGroups * kBatch) {
+                float mr[kBatch], xr[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    // unconditional loads (splits past the end re-read split s0), all issued before any use
+                    const int s = s0 + kGroups * k;
+                    const int o = (s < Sb ? s : s0) * sstride;
+                    mr[k] = base[o + D + R];
+                    xr[k] = base[o + c];
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep every load of the batch ahead of the arithmetic
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    if (s0 + kGroups * k >= Sb) {
+                        mr[k] = -INFINITY;
+                        xr[k] = 0.f;
+                    }
+                }
+                float mc = mr[0];
+#pragma unroll
+                for (int k = 1; k < kBatch; ++k) mc = fmaxf(mc, mr[k]);
+                const float mn = fmaxf(mj, mc);  // finite: split s0 < Sb holds live rows
+                float t = 0.f;
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) t = fmaf(fast_exp2(mr[k] - mn), xr[k], t);  // absent: 0 * 0
+                sj = fmaf(sj, fast_exp2(mj - mn), t);  // mj = -inf at first: 0
+                mj = mn;
             }
-            for (; s < Sb; s += kGroups) a0 = fmaf(w[s], base[(size_t)s * sstride + c], a0);
         }
-        part[j * kCols + (tid % kCols)] = (a0 + a1) + (a2 + a3);
+        gmax[j][cl] = mj;
+        gsum[j][cl] = sj;
         __syncthreads();
-        if (j == 0 && c < ncols) {
-            float v = part[tid % kCols];
-            for (int g = 1; g < kGroups; ++g) v += part[g * kCols + (tid % kCols)];
-            if (c < D + R) sums[c] = v;
-            else if (c == D + R + 1) red[15] = v;
+        if (j == 0 && c < ncols && c != D + R) {
+            float M = gmax[0][cl];
+            for (int g = 1; g < kGroups; ++g) M = fmaxf(M, gmax[g][cl]);
+            float v = 0.f;
+            for (int g = 0; g < kGroups; ++g)  // fixed order; empty groups (max -inf) add nothing
+                v += (gmax[g][cl] == -INFINITY) ? 0.f : fast_exp2(gmax[g][cl] - M) * gsum[g][cl];
+            sums[c < D + R ? c : D + R] = v;
         }
         __syncthreads();
     }
-    l = red[15];
-    const float inv_l = 1.0f / l;
+    // Every column saw the same split maxima, so all of them are scaled by the same 2^-M.
+    const float inv_l = 1.0f / sums[D + R];
     const float* u = sums + D;
-    const T* Bh = B_v + (size_t)h * D * R;
-    for (int c = tid; c < D; c += kMergeThreads) {
+    if (R == 0) {
+        for (int c = tid; c < D; c += kMergeThreads) o[c] = sums[c] * inv_l;
+    } else if (vec_epi) {
         float pr = 0.f;
-        for (int i = 0; i < R; ++i) pr = fmaf(u[i], elem<T>::load(Bh, (size_t)c * R + i), pr);
-        o[c] = (sums[c] + pr) * inv_l;
+        if (ec < D) {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) pr = fmaf(u[evi * VE + e], vec_elem<T>(bv, e), pr);
+        }
+        epi[tid] = pr;
+        __syncthreads();
+        for (int c = tid; c < D; c += kMergeThreads) {
+            float t = 0.f;
+            for (int k = 0; k < nvv; ++k) t += epi[c * nvv + k];  // fixed order
+            o[c] = (sums[c] + t) * inv_l;
+        }
+    } else {
+        const T* Bh = B_v + (size_t)h * D * R;
+        for (int c = tid; c < D; c += kMergeThreads) {
+            float pr = 0.f;
+            for (int i = 0; i < R; ++i) pr = fmaf(u[i], elem<T>::load(Bh, (size_t)c * R + i), pr);
+            o[c] = (sums[c] + pr) * inv_l;
+        }
     }
 }
 
@@ -112,17 +160,14 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, 
 
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream) {
+    if (d_h + r > kMaxCols) return hipErrorInvalidValue;
     dim3 grid(H, batch), block(kMergeThreads);
-    // a sequence has at most num_splits - batch + 1 splits (every other sequence holds at least one)
-    const size_t max_sb = (size_t)(num_splits - batch + 1);
-    const size_t lds = sizeof(float) * (max_sb + kGroups * kCols + (size_t)d_h + r + 16);
     if (dtype == 0)
-        hipLaunchKernelGGL(merge_kernel<float>, grid, block, lds, stream, batch, H, d_h, r, max_len, chunk, num_splits,
+        hipLaunchKernelGGL(merge_kernel<float>, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits,
                            seq_lens, (const float*)B_v, out, ws);
     else
-        hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, block, lds, stream, batch, H, d_h, r, max_len, chunk,
-                           num_splits,
-                           seq_lens, (const uint16_t*)B_v, out, ws);
+        hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk,
+                           num_splits, seq_lens, (const uint16_t*)B_v, out, ws);
     return hipGetLastError();
 }
 

@@ -117,6 +117,8 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
     G = std::min<long>(G, (long)d.batch + kMaxExtraSplits);
     G = std::min<long>(G, (long)d.batch * tiles_per_seq);
     G = std::max<long>(G, d.batch);
+    // the merge kernel addresses the workspace with 32-bit offsets
+    if ((long long)G * d.H * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31)) return false;
     p.num_splits = (int)G;
     *out = p;
     return true;
