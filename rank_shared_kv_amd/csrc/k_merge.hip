@@ -15,7 +15,7 @@
 // split launch (splits dealt to sequences by length; see lrkv_device.hpp);
 // only splits with s * granule < L_b hold live rows.
 //
-// One workgroup of 1024 threads per (b, h): thread (column c, split group j)
+// One workgroup per (b, h) of 256 threads times 1 or 4 split groups: thread (column c, split group j)
 // walks splits s = j, j + 4, ... of column c once, in batches of 16 whose
 // loads are issued together, keeping its own running maximum and rescaling
 // its sum once per batch (no separate pass for the maxima).  The four groups
@@ -29,9 +29,7 @@
 namespace lrkv {
 namespace {
 
-constexpr int kMergeThreads = 1024;
 constexpr int kCols = 256;                       // columns handled per pass
-constexpr int kGroups = kMergeThreads / kCols;   // split groups
 constexpr int kMaxCols = 512;                    // d_h + r <= 512
 constexpr int kBatch = 16;                       // splits per thread loaded together
 
@@ -47,11 +45,14 @@ __device__ __forceinline__ float vec_elem(const u32x4_t& v, int e) {
     }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, int D, int R, int max_len, int chunk,
-                                                              int S, const int32_t* __restrict__ seq_lens,
-                                                              const T* __restrict__ B_v, float* __restrict__ out,
-                                                              const float* __restrict__ ws) {
+// kGroups split groups of kCols threads each: 4 groups when sequences hold many splits, 1 when they
+// hold few (then the extra threads would only wait).
+template <typename T, int kGroups>
+__global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H, int D, int R, int max_len, int chunk,
+                                                                int S, const int32_t* __restrict__ seq_lens,
+                                                                const T* __restrict__ B_v, float* __restrict__ out,
+                                                                const float* __restrict__ ws) {
+    constexpr int kMergeThreads = kGroups * kCols;
     constexpr int VE = 16 / (int)sizeof(T);  // B^V elements per 16-byte vector
     __shared__ float gmax[kGroups][kCols];   // per-group running maxima
     __shared__ float gsum[kGroups][kCols];   // per-group rescaled sums
@@ -146,6 +147,17 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, 
             for (int k = 0; k < nvv; ++k) t += epi[c * nvv + k];  // fixed order
             o[c] = (sums[c] + t) * inv_l;
         }
+    } else if (nvv > 0) {  // row c of B^V_h read as 16-byte vectors by thread c
+        for (int c = tid; c < D; c += kMergeThreads) {
+            const T* row = B_v + ((size_t)h * D + c) * R;
+            float pr = 0.f;
+            for (int vi = 0; vi < nvv; ++vi) {
+                const u32x4_t v = *(const u32x4_t*)(row + vi * VE);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) pr = fmaf(u[vi * VE + e], vec_elem<T>(v, e), pr);
+            }
+            o[c] = (sums[c] + pr) * inv_l;
+        }
     } else {
         const T* Bh = B_v + (size_t)h * D * R;
         for (int c = tid; c < D; c += kMergeThreads) {
@@ -161,13 +173,18 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(int batch, int H, 
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream) {
     if (d_h + r > kMaxCols) return hipErrorInvalidValue;
-    dim3 grid(H, batch), block(kMergeThreads);
-    if (dtype == 0)
-        hipLaunchKernelGGL(merge_kernel<float>, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits,
-                           seq_lens, (const float*)B_v, out, ws);
-    else
-        hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk,
-                           num_splits, seq_lens, (const uint16_t*)B_v, out, ws);
+    // one split group per column when sequences average at most 16 splits, four otherwise
+    const bool wide = num_splits > 16 * batch;
+    dim3 grid(H, batch), block(wide ? 4 * kCols : kCols);
+    if (dtype == 0) {
+        auto k = wide ? merge_kernel<float, 4> : merge_kernel<float, 1>;
+        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits, seq_lens,
+                           (const float*)B_v, out, ws);
+    } else {
+        auto k = wide ? merge_kernel<uint16_t, 4> : merge_kernel<uint16_t, 1>;
+        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits, seq_lens,
+                           (const uint16_t*)B_v, out, ws);
+    }
     return hipGetLastError();
 }
 
