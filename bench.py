@@ -49,12 +49,15 @@ def launch_config(w, steps: int, capacity: int = 0):
     return L_cap, L_max + steps
 
 
+# the sources that determine the bf16 split kernel's code and launch configuration
+SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hip", "lrkv_device.hpp", "lrkv_internal.hpp", "lrkv_api.cpp")
+
+
 def kernel_sources_digest() -> str:
-    import glob
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "rank_shared_kv_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode())
+    for name in SPLIT_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "rank_shared_kv_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
