@@ -311,3 +311,113 @@ def test_planted_mistake_is_caught(plant, tmp_path):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"planted mistake {plant} slipped through every pin"
+
+
+# ---------------------------------------------------------------------------------------------
+# layer step around the attention core: projections in, output projection out
+# ---------------------------------------------------------------------------------------------
+from oracle import layer as olayer  # noqa: E402
+
+
+def _layer_case(seed, B, H, d_h, r, dm, L_hist):
+    g = lambda s, shape, std=1.0: _rand(seed + s, shape, std)
+    n_in = H * d_h + 2 * d_h + 2 * H * r
+    return {"B": B, "H": H, "d_h": d_h, "r": r, "dm": dm,
+            "W_in": g(1, (n_in, dm), 1 / math.sqrt(dm)), "W_o": g(2, (dm, H * d_h), 1 / math.sqrt(H * d_h)),
+            "B_k": g(3, (H, d_h, r), 1 / math.sqrt(max(r, 1))), "B_v": g(4, (H, d_h, r), 1 / math.sqrt(max(r, 1))),
+            "X": g(5, (B, L_hist, dm)), "x": g(6, (B, dm))}
+
+
+def _layer_oracle(c, lens, plant=0, lib_path=None):
+    L_cap = c["X"].shape[1] + 2
+    cache = olayer.project_history("f64", c["X"], c["W_in"], c["H"], c["d_h"], c["r"], L_cap, lens)
+    return olayer.layer_step("f64", c["x"], c["W_in"], c["W_o"], c["B_k"], c["B_v"], cache, lens, c["H"], c["d_h"],
+                             c["r"], plant=plant, lib_path=lib_path)["y"]
+
+
+def pin_layer_materialized_weights(lib_path=None, plant=0):
+    """The factored step (project into the cache, LRKV decode, W_o) equals attention with every head's
+    weights materialised, W_h = W_S + U_h B_h^T (reading notes sec. 2.1 Eqs. (2)-(5)), computed by a
+    different route: torch fp64, keys and values of all tokens from the materialised weights."""
+    for i, (B, H, d_h, r, dm, L) in enumerate([(2, 3, 4, 2, 7, 6), (1, 2, 8, 3, 5, 9), (2, 4, 4, 4, 16, 5)]):
+        c = _layer_case(1100 + 10 * i, B, H, d_h, r, dm, L)
+        lens = np.array([L - b for b in range(B)], dtype=np.int32)
+        got = _layer_oracle(c, lens, plant, lib_path)
+        t = {k: torch.from_numpy(np.asarray(v)) for k, v in c.items() if isinstance(v, np.ndarray)}
+        o_rows = 0
+        Wq = t["W_in"][0:H * d_h]; o_rows = H * d_h
+        WSK = t["W_in"][o_rows:o_rows + d_h]; o_rows += d_h
+        WSV = t["W_in"][o_rows:o_rows + d_h]; o_rows += d_h
+        UK = t["W_in"][o_rows:o_rows + H * r]; o_rows += H * r
+        UV = t["W_in"][o_rows:o_rows + H * r]
+        ref = torch.zeros((B, dm), dtype=torch.float64)
+        for b in range(B):
+            n = int(lens[b])
+            X_all = torch.cat([t["X"][b, :n], t["x"][b:b + 1]], dim=0)  # history then the new token
+            heads = []
+            for h in range(H):
+                WK_h = WSK.T + UK[h * r:(h + 1) * r].T @ t["B_k"][h].T   # [dm][d_h]
+                WV_h = WSV.T + UV[h * r:(h + 1) * r].T @ t["B_v"][h].T
+                q_h = t["x"][b] @ Wq[h * d_h:(h + 1) * d_h].T
+                K_h, V_h = X_all @ WK_h, X_all @ WV_h
+                a = torch.softmax(K_h @ q_h / math.sqrt(d_h), dim=0)
+                heads.append(a @ V_h)
+            ref[b] = torch.cat(heads) @ t["W_o"].T
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_layer_mha_special_case(lib_path=None, plant=0):
+    """r = d_h, B_h = I, zero shared projections and d_model = H*d_h: the layer step is textbook multi-head
+    attention, checked against torch's own implementation (fp64)."""
+    B, H, d_h, L = 2, 3, 4, 6
+    dm, r = H * d_h, d_h
+    c = _layer_case(1200, B, H, d_h, r, dm, L)
+    c["W_in"][H * d_h:H * d_h + 2 * d_h] = 0.0
+    c["B_k"] = np.broadcast_to(np.eye(d_h), (H, d_h, d_h)).copy()
+    c["B_v"] = c["B_k"].copy()
+    lens = np.array([L, L - 2], dtype=np.int32)
+    got = _layer_oracle(c, lens, plant, lib_path)
+    W = torch.from_numpy(c["W_in"])
+    in_proj = torch.cat([W[:H * d_h], W[H * d_h + 2 * d_h:H * d_h + 2 * d_h + H * r],
+                         W[H * d_h + 2 * d_h + H * r:]], dim=0)
+    for b in range(B):
+        n = int(lens[b])
+        X_all = torch.cat([torch.from_numpy(c["X"][b, :n]), torch.from_numpy(c["x"][b:b + 1])], dim=0)
+        ref, _ = torch.nn.functional.multi_head_attention_forward(
+            torch.from_numpy(c["x"][b:b + 1])[:, None, :], X_all[:, None, :], X_all[:, None, :], dm, H,
+            in_proj, None, None, None, False, 0.0, torch.from_numpy(c["W_o"]), None, training=False,
+            need_weights=False)
+        np.testing.assert_allclose(got[b], ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_layer_rounding(lib_path=None, plant=0):
+    """Stored rows are the fp64 projections rounded to the cache dtype: fp32 values are the nearest fp32,
+    bf16 values the nearest bf16 of that (both round half to even); bf16 of an exact bf16 value is itself."""
+    # bf16 keeps 7 fraction bits: the spacing just above 1 is 2^-7
+    y = np.array([1.0, 1.0 + 2.0 ** -9, 1.0 + 3 * 2.0 ** -9, -2.5, 1.0 + 2.0 ** -30,
+                  1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8])  # the last two are exact ties
+    b = olayer.round_to("bf16", y)
+    np.testing.assert_array_equal(olayer.widen("bf16", b),
+                                  [1.0, 1.0, 1.0 + 2.0 ** -7, -2.5, 1.0, 1.0, 1.0 + 2.0 ** -6])
+    np.testing.assert_array_equal(olayer.widen("f32", olayer.round_to("f32", y)), y.astype(np.float32))
+
+
+LAYER_PINS = [pin_layer_materialized_weights, pin_layer_mha_special_case, pin_layer_rounding]
+
+
+@pytest.mark.parametrize("pin", LAYER_PINS, ids=lambda f: f.__name__)
+def test_layer_pin(pin):
+    pin()
+
+
+@pytest.mark.parametrize("plant", [1, 2, 3, 4])
+def test_layer_planted_mistake_is_caught(plant):
+    """The layer reference with one planted mistake (K/V projections swapped, W_o transposed, heads of the
+    value latents reversed, new token not appended) must fail at least one layer pin."""
+    failed = []
+    for pin in LAYER_PINS:
+        try:
+            pin(plant=plant)
+        except (AssertionError, ValueError, RuntimeError):
+            failed.append(pin.__name__)
+    assert failed, f"planted layer mistake {plant} slipped through every pin"
