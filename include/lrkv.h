@@ -156,6 +156,39 @@ lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, 
 lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
                               float* out, const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Project the new token of every sequence and append it to the cache, in one
+ * stacked product (review sec. 3, Algorithm 1; reading notes sec. 2.1
+ * Eqs. (2)-(5) and sec. 2.3):
+ *   y = x W_in^T, the rows of W_in ordered
+ *       [W_q (H*d_h rows) | W_S^K (d_h) | W_S^V (d_h) | U^K (H*r, head h at rows h*r) | U^V (H*r)]
+ *   q_out[b] = y[b][0 .. H*d_h); the shared key/value rows and every head's
+ *   latents are written to row seq_lens[b] of the cache, then seq_lens[b] is
+ *   incremented (a full sequence, seq_lens[b] >= L_cap, or a negative length
+ *   is left unchanged and nothing of its cache is written; its q_out is still
+ *   written).
+ *   x      device [batch][d_model]                       (dims->dtype)
+ *   W_in   device [H*d_h + 2*d_h + 2*H*r][d_model]       (dims->dtype; one output feature per row)
+ *   q_out  device [batch][H][d_h]                        (dims->dtype)
+ * Arithmetic: fp32 accumulation in a fixed order, results rounded to
+ * dims->dtype (nearest even).  bf16 weights with d_model a multiple of 1024 run
+ * on the matrix cores; other shapes on a plain fp32 kernel.  Enqueues two
+ * kernels (the product, then the length update).  Fails with
+ * LRKV_ERR_UNSUPPORTED when W_in has 2^31 elements or more. */
+lrkv_status lrkv_project_append(const lrkv_dims* dims, int32_t d_model, const lrkv_cache* cache, const void* x,
+                                const void* W_in, void* q_out, void* stream);
+
+/* Output projection of the decode result (review sec. 3, the last step of
+ * Algorithm 2; reading notes sec. 2.4, after Eq. (7)):
+ *   y[b] = concat_h(o[b][h]) W_o^T
+ *   o    device [batch][H][d_h] fp32 (the output of lrkv_decode)
+ *   W_o  device [d_model][H*d_h] (dims->dtype; one output feature per row)
+ *   y    device [batch][d_model] fp32
+ * Arithmetic: fp32 accumulation in a fixed order.  With bf16 weights (and
+ * H*d_h a multiple of 512) o enters the matrix cores as a bf16 high part plus a
+ * bf16 low part, about 16 significant bits; otherwise a plain fp32 kernel. */
+lrkv_status lrkv_output_project(const lrkv_dims* dims, int32_t d_model, const float* o, const void* W_o, float* y,
+                                void* stream);
+
 /* Cache payload in bytes, counted as the pages count it (numel x element size
  * of the live rows): 2 * s * sum_b L_b * (d_h + H * r), s = 4 (fp32) or 2 (bf16)
  * (reading notes sec. 2.5 Eqs. (8)-(9); review sec. 4).  host_seq_lens is a

@@ -26,8 +26,8 @@ LRKV_F32 = 0
 LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
-            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_cache_bytes", "lrkv_status_str",
-            "lrkv_last_error")
+            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_project_append", "lrkv_output_project",
+            "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
 
 class LrkvError(RuntimeError):
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode": ([D, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_partial": ([D, C, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_project_append": ([D, i32, C, vp, vp, vp, vp], ctypes.c_int),
+            "lrkv_output_project": ([D, i32, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_cache_bytes": ([D, vp], ctypes.c_uint64),
             "lrkv_status_str": ([ctypes.c_int], ctypes.c_char_p),
             "lrkv_last_error": ([], ctypes.c_char_p),
@@ -156,6 +158,16 @@ def lrkv_decode_merge(dims: Dims, seq_lens, max_len: int, B_v, out, workspace, w
                       stream=None) -> None:
     _check(lib().lrkv_decode_merge(ctypes.byref(dims), _ptr(seq_lens), max_len, _ptr(B_v), _ptr(out),
                                    _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_merge")
+
+
+def lrkv_project_append(dims: Dims, d_model: int, cache: Cache, x, W_in, q_out, stream=None) -> None:
+    _check(lib().lrkv_project_append(ctypes.byref(dims), d_model, ctypes.byref(cache), _ptr(x), _ptr(W_in),
+                                     _ptr(q_out), _stream(stream)), "lrkv_project_append")
+
+
+def lrkv_output_project(dims: Dims, d_model: int, o, W_o, y, stream=None) -> None:
+    _check(lib().lrkv_output_project(ctypes.byref(dims), d_model, _ptr(o), _ptr(W_o), _ptr(y), _stream(stream)),
+           "lrkv_output_project")
 
 
 def lrkv_cache_bytes(dims: Dims, host_seq_lens: Optional[Sequence[int]] = None) -> int:

@@ -309,4 +309,38 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
     return ok();
 }
 
+lrkv_status lrkv_project_append(const lrkv_dims* dims, int32_t d_model, const lrkv_cache* cache, const void* x,
+                                const void* W_in, void* q_out, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (d_model < 1) return fail(LRKV_ERR_INVALID_ARG, "d_model=%d must be >= 1", d_model);
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(x, "x"));
+    LRKV_TRY(need_ptr(W_in, "W_in"));
+    LRKV_TRY(need_ptr(q_out, "q_out"));
+    const long long n_in = (long long)dims->H * dims->d_h + 2LL * dims->d_h + 2LL * dims->H * dims->r;
+    if (n_in * d_model >= (1LL << 31) || (long long)dims->batch * n_in >= (1LL << 31))
+        return fail(LRKV_ERR_UNSUPPORTED, "projection of %lld features from d_model=%d is too large", n_in, d_model);
+    hipError_t e = lrkv::launch_project_append(dims->batch, dims->H, dims->d_h, dims->r, dims->L_cap, dims->dtype,
+                                               d_model, cache->k_shared, cache->v_shared, cache->z_k, cache->z_v,
+                                               cache->seq_lens, x, W_in, q_out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "projection kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_output_project(const lrkv_dims* dims, int32_t d_model, const float* o, const void* W_o, float* y,
+                                void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (d_model < 1) return fail(LRKV_ERR_INVALID_ARG, "d_model=%d must be >= 1", d_model);
+    LRKV_TRY(need_ptr(o, "o"));
+    LRKV_TRY(need_ptr(W_o, "W_o"));
+    LRKV_TRY(need_ptr(y, "y"));
+    const long long k = (long long)dims->H * dims->d_h;
+    if (k * d_model >= (1LL << 31) || (long long)dims->batch * d_model >= (1LL << 31))
+        return fail(LRKV_ERR_UNSUPPORTED, "output projection %lld x %d is too large", k, d_model);
+    hipError_t e = lrkv::launch_output_project(dims->batch, dims->H, dims->d_h, dims->dtype, d_model, o, W_o, y,
+                                               (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "output projection kernel launch");
+    return ok();
+}
+
 }  // extern "C"

@@ -54,5 +54,10 @@ hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t
 hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
                         const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream);
 int general_rows_per_tile();  // rows one general-kernel split advances per step
+hipError_t launch_project_append(int batch, int H, int d_h, int r, int L_cap, int dtype, int d_model, void* k_shared,
+                                 void* v_shared, void* z_k, void* z_v, int32_t* seq_lens, const void* x,
+                                 const void* W_in, void* q_out, hipStream_t stream);
+hipError_t launch_output_project(int batch, int H, int d_h, int dtype, int d_model, const float* o, const void* W_o,
+                                 float* y, hipStream_t stream);
 
 }  // namespace lrkv
