@@ -120,6 +120,9 @@ def main():
     ap.add_argument("--capacity", type=int, default=0,
                     help="cache rows allocated per sequence (default: the context plus the timed appends, "
                          "rounded up to 256)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the whole layer step: project + append (d_model = H*d_h), absorb, decode, output "
+                         "projection (random seeded weights)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -176,19 +179,46 @@ def main():
     zv_new = rows["zv_new"] if w.r else None
 
     ev_pairs = []
+    layer_ev = []  # (project start, project end, output projection start, output projection end)
+    d_model = w.H * w.d_h
+    if args.layer:
+        import math
+        n_in = w.H * w.d_h + 2 * w.d_h + 2 * w.H * w.r
+        W_in = sdev.to_device(synth.normal(8800, 1.0 / math.sqrt(d_model), n_in * d_model, w.dtype)
+                              .reshape(n_in, d_model))
+        W_o = sdev.to_device(synth.normal(8801, 1.0 / math.sqrt(d_model), d_model * d_model, w.dtype)
+                             .reshape(d_model, d_model))
+        x_new = sdev.to_device(synth.normal(8802, 1.0, w.batch * d_model, w.dtype).reshape(w.batch, d_model))
+        q_step = torch.empty((w.batch, w.H, w.d_h), dtype=sdev.torch_dtype(w), device="cuda")
+        y_step = torch.empty((w.batch, d_model), dtype=torch.float32, device="cuda")
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
 
     def step(timed: bool):
-        lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+        if args.layer:
+            e_p0 = ev() if timed else None
+            lk.lrkv_project_append(dims, d_model, cache, x_new, W_in, q_step, stream)
+            e_p1 = ev() if timed else None
+            q_use = q_step
+        else:
+            lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+            q_use = dev["q"]
         if w.r:
-            lk.lrkv_absorb_query(dims, dev["q"], dev["B_k"], p, stream)
+            lk.lrkv_absorb_query(dims, q_use, dev["B_k"], p, stream)
         if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        lk.lrkv_decode_partial(dims, cache, max_len, dev["q"], pp, ws, nbytes, stream)
+            e0 = ev()
+        lk.lrkv_decode_partial(dims, cache, max_len, q_use, pp, ws, nbytes, stream)
         if timed:
-            e1.record(stream)
-            ev_pairs.append((e0, e1))
+            ev_pairs.append((e0, ev()))
         lk.lrkv_decode_merge(dims, dev["seq_lens"], max_len, bv, out, ws, nbytes, stream)
+        if args.layer:
+            e_o0 = ev() if timed else None
+            lk.lrkv_output_project(dims, d_model, out, W_o, y_step, stream)
+            if timed:
+                layer_ev.append((e_p0, e_p1, e_o0, ev()))
 
     for _ in range(W):
         step(False)
@@ -223,7 +253,23 @@ def main():
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = read_traffic(w.name, split_bytes)
+    traffic = read_traffic(w.name, split_bytes) if not args.layer else None
+    layer = None
+    if args.layer:
+        assert bool(torch.isfinite(y_step).all())
+        proj_us = 1e3 * sum(a.elapsed_time(b) for a, b, _, _ in layer_ev) / len(layer_ev)
+        outp_us = 1e3 * sum(c.elapsed_time(d) for _, _, c, d in layer_ev) / len(layer_ev)
+        w_in_bytes = W_in.numel() * W_in.element_size()
+        w_o_bytes = W_o.numel() * W_o.element_size()
+        layer = {"d_model": d_model, "project_append_us": proj_us,
+                 "project_weight_gbps": w_in_bytes / (proj_us * 1e-6) / 1e9, "project_weight_bytes": w_in_bytes,
+                 "output_project_us": outp_us, "output_weight_gbps": w_o_bytes / (outp_us * 1e-6) / 1e9,
+                 "output_weight_bytes": w_o_bytes,
+                 "note": "project_append_us includes its length-update kernel; weights are random and seeded"}
+        step_bytes += w_in_bytes + w_o_bytes  # the weights are streamed once per step
+        step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
+        log(f"bench: layer step: project+append {proj_us:.1f} us ({layer['project_weight_gbps']:.0f} GB/s of "
+            f"weights), output projection {outp_us:.1f} us ({layer['output_weight_gbps']:.0f} GB/s)")
     log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); split pass {split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
@@ -246,7 +292,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+        "config": {"workload": w.name + ("+projections" if args.layer else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
                    "splits": S, "chunk_tokens": chunk},
@@ -257,6 +303,7 @@ def main():
                      "traffic": traffic, "kernel": "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
         "mfma_util_shared_score": mfma_util,
+        "layer_step": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

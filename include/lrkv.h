@@ -170,7 +170,7 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
  *   W_in   device [H*d_h + 2*d_h + 2*H*r][d_model]       (dims->dtype; one output feature per row)
  *   q_out  device [batch][H][d_h]                        (dims->dtype)
  * Arithmetic: fp32 accumulation in a fixed order, results rounded to
- * dims->dtype (nearest even).  bf16 weights with d_model a multiple of 1024 run
+ * dims->dtype (nearest even).  bf16 weights with d_model a multiple of 512 run
  * on the matrix cores; other shapes on a plain fp32 kernel.  Enqueues two
  * kernels (the product, then the length update).  Fails with
  * LRKV_ERR_UNSUPPORTED when W_in has 2^31 elements or more. */

@@ -13,13 +13,13 @@
 //
 // Both are skinny products (M = batch rows, K = d_model or H*d_h, N features)
 // bound by streaming the weights once.  Matrix-core path (bf16 weights): a
-// workgroup of 4 waves owns 16 output features; the waves split K into four
-// quarters and each runs v_mfma_f32_16x16x32_bf16 over its quarter for every
-// 16-row tile of the batch (weights read once, reused by all rows).  Operands
+// workgroup of 16 (or 8, 4) waves owns 16 output features; the waves split K
+// into equal slices and each runs v_mfma_f32_16x16x32_bf16 over its slice for
+// every 16-row tile of the batch (weights read once, reused by all rows).  Operands
 // are 16-byte global loads: weight row n, 8 consecutive k per lane; batch row
 // m likewise.  An fp32 left operand (the decode output o) enters as a bf16
 // high part plus a bf16 low part (two products), about 16 significant bits.
-// The four partial products are added in LDS in a fixed order.  Other shapes
+// The waves' partial products are added in LDS in a fixed order.  Other shapes
 // and fp32 weights use a plain fp32 kernel.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
@@ -31,12 +31,9 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = 256;  // plain kernel
 constexpr int kMaxMTiles = 4;  // at most 64 rows per workgroup pass
-
-// k-steps of 32 whose loads are issued together (fewer for fp32 left operands: twice the registers)
-template <typename AT>
-constexpr int unroll_for() { return sizeof(AT) == 2 ? 8 : 4; }
+constexpr int kUnroll = 4;     // k-steps of 32 whose loads are issued together
 
 // Where output feature n of row m goes.
 struct ProjectSink {
@@ -121,18 +118,18 @@ struct AFrag<float> {
     }
 };
 
-// MT row tiles of 16 per workgroup pass; K must be a multiple of 4 * 32 * unroll_for<AT>()
-template <typename AT, int MT, typename Sink>
-__global__ void __launch_bounds__(kThreads) linear_mfma_kernel(int M, int K, int N, const AT* __restrict__ A,
-                                                               const uint16_t* __restrict__ W, Sink sink) {
-    constexpr int kUnroll = unroll_for<AT>();
-    __shared__ float red[4][MT * 16][17];
+// MT row tiles of 16 per workgroup pass; KW waves split K into equal slices, so K must be a multiple of
+// KW * 32 * kUnroll.  Many waves per workgroup keep many weight loads in flight per CU.
+template <typename AT, int MT, int KW, typename Sink>
+__global__ void __launch_bounds__(KW * 64) linear_mfma_kernel(int M, int K, int N, const AT* __restrict__ A,
+                                                              const uint16_t* __restrict__ W, Sink sink) {
+    __shared__ float red[KW][MT * 16][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int m_base = blockIdx.y * (MT * 16);
     const int mt_count = min(MT, (M - m_base + 15) / 16);
-    const int kq = K / 4, k_begin = wave * kq;  // this wave's quarter of K
+    const int kq = K / KW, k_begin = wave * kq;  // this wave's slice of K
     const int n = min(n0 + n16, N - 1);           // features past N re-read the last row; results dropped
     const uint16_t* wrow = W + (size_t)n * K + 8 * g4;
 
@@ -172,11 +169,13 @@ __global__ void __launch_bounds__(kThreads) linear_mfma_kernel(int M, int K, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) red[wave][16 * t + 4 * g4 + i][n16] = acc[t][i];
     __syncthreads();
-    for (int idx = tid; idx < mt_count * 16 * 16; idx += kThreads) {
+    for (int idx = tid; idx < mt_count * 16 * 16; idx += KW * 64) {
         const int ml = idx / 16, nl = idx % 16;
         const int m = m_base + ml, nn = n0 + nl;
         if (m >= M || nn >= N) continue;
-        const float v = ((red[0][ml][nl] + red[1][ml][nl]) + red[2][ml][nl]) + red[3][ml][nl];  // fixed order
+        float v = red[0][ml][nl];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) v += red[w][ml][nl];  // fixed order
         sink.put(m, nn, v);
     }
 }
@@ -200,20 +199,34 @@ __global__ void commit_kernel(int batch, int L_cap, int32_t* __restrict__ seq_le
     if (L >= 0 && L < L_cap) seq_lens[b] = L + 1;
 }
 
-template <typename AT, int MT, typename Sink>
+template <typename AT, int MT, int KW, typename Sink>
 void launch_mfma(int M, int K, int N, const AT* A, const void* W, Sink sink, hipStream_t stream) {
     dim3 grid((N + 15) / 16, (M + MT * 16 - 1) / (MT * 16));
-    hipLaunchKernelGGL((linear_mfma_kernel<AT, MT, Sink>), grid, dim3(kThreads), 0, stream, M, K, N, A,
+    hipLaunchKernelGGL((linear_mfma_kernel<AT, MT, KW, Sink>), grid, dim3(KW * 64), 0, stream, M, K, N, A,
                        (const uint16_t*)W, sink);
+}
+
+// K slices per workgroup: as many waves as the shape allows (16, 8 or 4); four row tiles use at most 8
+// (the LDS of the final reduction)
+template <typename AT, int MT, typename Sink>
+bool launch_mfma_kw(int M, int K, int N, const AT* A, const void* W, Sink sink, hipStream_t stream) {
+    constexpr int step = 32 * kUnroll;
+    if (MT < 4 && K % (16 * step) == 0) launch_mfma<AT, MT, (MT < 4 ? 16 : 8)>(M, K, N, A, W, sink, stream);
+    else if (K % (8 * step) == 0) launch_mfma<AT, MT, 8>(M, K, N, A, W, sink, stream);
+    else if (K % (4 * step) == 0) launch_mfma<AT, MT, 4>(M, K, N, A, W, sink, stream);
+    else return false;
+    return true;
 }
 
 template <typename AT, typename Sink>
 hipError_t launch_linear(int dtype, int M, int K, int N, const AT* A, const void* W, Sink sink, hipStream_t stream) {
-    if (dtype == 1 && K % (4 * 32 * unroll_for<AT>()) == 0) {
-        if (M <= 16) launch_mfma<AT, 1>(M, K, N, A, W, sink, stream);
-        else if (M <= 32) launch_mfma<AT, 2>(M, K, N, A, W, sink, stream);
-        else launch_mfma<AT, kMaxMTiles>(M, K, N, A, W, sink, stream);
-    } else {
+    bool done = false;
+    if (dtype == 1) {
+        if (M <= 16) done = launch_mfma_kw<AT, 1>(M, K, N, A, W, sink, stream);
+        else if (M <= 32) done = launch_mfma_kw<AT, 2>(M, K, N, A, W, sink, stream);
+        else done = launch_mfma_kw<AT, kMaxMTiles>(M, K, N, A, W, sink, stream);
+    }
+    if (!done) {
         const long total = (long)M * N;
         dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
         if (dtype == 1)
