@@ -156,6 +156,24 @@ lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, 
 lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
                               float* out, const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode Q query tokens per sequence at once (speculative decode, chunked
+ * prefill): the last Q tokens of every sequence, already appended, each
+ * attend to the rows before and at their own position -- query i sits at
+ * position seq_lens[b] - Q + i and sees rows j <= seq_lens[b] - Q + i, the
+ * causal mask inside the chunk (reading notes sec. 2.4, Eqs. (6)-(7) under
+ * the causal softmax; review sec. 3).  Everything else is lrkv_decode's.
+ *   n_queries  Q, 1 <= Q <= 64
+ *   q          device [batch][Q][H][d_h] (dims->dtype)
+ *   p          device [batch][Q][H][r] fp32: lrkv_absorb_query with dims->batch = batch * Q
+ *   out        device [batch][Q][H][d_h] fp32 (0 for a query that sees no row)
+ *   workspace  >= lrkv_decode_multi_workspace_bytes(dims, Q, max_len) bytes, 256-byte aligned
+ * The rows are read once for all Q queries of a sequence.  Q = 1 gives exactly
+ * lrkv_decode's kernels and results. */
+size_t lrkv_decode_multi_workspace_bytes(const lrkv_dims* dims, int32_t n_queries, int32_t max_len);
+lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lrkv_cache* cache, int32_t max_len,
+                              const void* q, const float* p, const void* B_v, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Project the new token of every sequence and append it to the cache, in one
  * stacked product (review sec. 3, Algorithm 1; reading notes sec. 2.1
  * Eqs. (2)-(5) and sec. 2.3):

@@ -160,3 +160,21 @@ def relative_error(got: np.ndarray, ref: np.ndarray) -> float:
     den = np.max(np.abs(ref), axis=-1)
     den = np.where(den > 0, den, 1.0)
     return float(np.max(num / den)) if num.size else 0.0
+
+
+def lrkv_decode_multi(dtype: str, q, k_shared, v_shared, z_k, z_v, B_k, B_v, seq_lens, threads=None,
+                      lib_path=None) -> np.ndarray:
+    """Q query tokens per sequence, the last Q tokens of each sequence (already in the cache): query i sits
+    at position L_b - Q + i and attends to rows j <= L_b - Q + i, the causal mask inside the chunk
+    ("Low-Rank Key Value Attention: Chinese reading notes", sec. 2.4, the score of Eq. (6) under the causal
+    softmax; review sec. 3).  That is the single-query reference at length L_b - Q + i + 1 for every i.
+    q [batch][Q][H][d_h]; returns out [batch][Q][H][d_h] (0 where a query sees no row)."""
+    q = np.asarray(q)
+    B, Q, H, d_h = q.shape
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    out = np.zeros((B, Q, H, d_h), dtype=np.float64)
+    for i in range(Q):
+        li = np.clip(lens - Q + i + 1, 0, None).astype(np.int32)
+        out[:, i] = lrkv_decode(dtype, np.ascontiguousarray(q[:, i]), k_shared, v_shared, z_k, z_v, B_k, B_v, li,
+                                threads=threads, lib_path=lib_path).reshape(B, H, d_h)
+    return out

@@ -26,7 +26,8 @@ LRKV_F32 = 0
 LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
-            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_project_append", "lrkv_output_project",
+            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
+            "lrkv_decode_multi", "lrkv_project_append", "lrkv_output_project",
             "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
 
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode": ([D, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_partial": ([D, C, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_decode_multi_workspace_bytes": ([D, i32, i32], sz),
+            "lrkv_decode_multi": ([D, i32, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_project_append": ([D, i32, C, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_output_project": ([D, i32, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_cache_bytes": ([D, vp], ctypes.c_uint64),
@@ -158,6 +161,17 @@ def lrkv_decode_merge(dims: Dims, seq_lens, max_len: int, B_v, out, workspace, w
                       stream=None) -> None:
     _check(lib().lrkv_decode_merge(ctypes.byref(dims), _ptr(seq_lens), max_len, _ptr(B_v), _ptr(out),
                                    _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_merge")
+
+
+def lrkv_decode_multi_workspace_bytes(dims: Dims, n_queries: int, max_len: int) -> int:
+    return int(lib().lrkv_decode_multi_workspace_bytes(ctypes.byref(dims), n_queries, max_len))
+
+
+def lrkv_decode_multi(dims: Dims, n_queries: int, cache: Cache, max_len: int, q, p, B_v, out, workspace,
+                      workspace_bytes: int, stream=None) -> None:
+    _check(lib().lrkv_decode_multi(ctypes.byref(dims), n_queries, ctypes.byref(cache), max_len, _ptr(q), _ptr(p),
+                                   _ptr(B_v), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "lrkv_decode_multi")
 
 
 def lrkv_project_append(dims: Dims, d_model: int, cache: Cache, x, W_in, q_out, stream=None) -> None:

@@ -86,16 +86,18 @@ int env_int(const char* name, int dflt) {
 // per SIMD), LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch).
 constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
-bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
+// n_queries: query tokens per sequence (1 for single-token decode); they act as H * n_queries virtual heads.
+bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_queries = 1) {
     using namespace lrkv;
     SplitPlan p{};
-    if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+    p.n_queries = n_queries;
+    if (n_queries == 1 && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
         p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
-    } else if (mfma_f32_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+    } else if (n_queries == 1 && mfma_f32_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaF32;
         p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
-    } else if (general_path_supports(d.H, d.d_h, d.r)) {
+    } else if (general_path_supports(d.H * n_queries, d.d_h, d.r)) {
         p.path = SplitPath::kGeneral;
         p.occupancy = 1;
     } else {
@@ -118,21 +120,23 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out) {
     G = std::min<long>(G, (long)d.batch * tiles_per_seq);
     G = std::max<long>(G, d.batch);
     // the merge kernel addresses the workspace with 32-bit offsets
-    if ((long long)G * d.H * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31)) return false;
+    if ((long long)G * d.H * n_queries * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31)) return false;
     p.num_splits = (int)G;
     *out = p;
     return true;
 }
 
 size_t workspace_bytes(const lrkv_dims& d, const lrkv::SplitPlan& p) {
-    return sizeof(float) * (size_t)p.num_splits * (size_t)d.H * (size_t)lrkv::partial_record_floats(d.d_h, d.r);
+    return sizeof(float) * (size_t)p.num_splits * (size_t)d.H * (size_t)p.n_queries *
+           (size_t)lrkv::partial_record_floats(d.d_h, d.r);
 }
 
-lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan) {
+lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan, int n_queries = 1) {
     LRKV_TRY(check_dims(dims));
     if (max_len < 0 || max_len > dims->L_cap)
         return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
-    if (!plan_split(*dims, max_len, plan))
+    if (n_queries < 1 || n_queries > 64) return fail(LRKV_ERR_INVALID_ARG, "n_queries=%d outside [1, 64]", n_queries);
+    if (!plan_split(*dims, max_len, plan, n_queries))
         return fail(LRKV_ERR_UNSUPPORTED, "no kernel for H=%d d_h=%d r=%d dtype=%d", dims->H, dims->d_h, dims->r,
                     dims->dtype);
     return LRKV_OK;
@@ -161,6 +165,7 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.max_len = max_len;
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
+    a.n_queries = plan.n_queries;
     a.k_shared = c.k_shared;
     a.v_shared = c.v_shared;
     a.z_k = c.z_k;
@@ -281,7 +286,7 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
     LRKV_TRY(need_ptr(out, "out"));
     if (dims->r > 0) LRKV_TRY(need_ptr(B_v, "B_v"));
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -302,9 +307,37 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+size_t lrkv_decode_multi_workspace_bytes(const lrkv_dims* dims, int32_t n_queries, int32_t max_len) {
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap || n_queries < 1 || n_queries > 64) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p, n_queries)) return 0;
+    return workspace_bytes(*dims, p);
+}
+
+lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lrkv_cache* cache, int32_t max_len,
+                              const void* q, const float* p, const void* B_v, float* out, void* workspace,
+                              size_t workspace_bytes_, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, n_queries));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(p, "p"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, n_queries, dims->d_h, dims->r, dims->dtype, max_len,
+                                      plan.chunk, plan.num_splits, cache->seq_lens, B_v, out,
+                                      (const float*)workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ok();
 }

@@ -14,6 +14,7 @@ struct DecodeArgs {
     int max_len;         // host bound of seq_lens
     int chunk;           // split granule in rows: split s holds live rows iff s * chunk < L_b
     int num_splits;      // G: workgroups of the launch = partial records per head (shared by the batch)
+    int n_queries;       // Q query tokens per sequence (the last Q tokens; causal inside the chunk)
     const void* k_shared;
     const void* v_shared;
     const void* z_k;
@@ -21,7 +22,7 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const void* q;
     const float* p;
-    float* ws;           // [G][H][record]
+    float* ws;           // [G][H * Q][record]
 };
 
 // Which split kernel a problem uses.
@@ -34,6 +35,7 @@ struct SplitPlan {
     int chunk;       // split granule in rows (the kernel's tile: rows a split advances per step)
     int num_splits;  // G: workgroups for the whole batch, dealt to sequences by length on the device
     int occupancy;   // MFMA kernels: waves per SIMD they are compiled for (1 or 2)
+    int n_queries;   // Q query tokens per sequence
 };
 
 bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);      // bf16 MFMA kernel
@@ -51,8 +53,9 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
-hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk, int num_splits,
-                        const int32_t* seq_lens, const void* B_v, float* out, const float* ws, hipStream_t stream);
+hipError_t launch_merge(int batch, int H, int n_queries, int d_h, int r, int dtype, int max_len, int chunk,
+                        int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
+                        hipStream_t stream);
 int general_rows_per_tile();  // rows one general-kernel split advances per step
 hipError_t launch_project_append(int batch, int H, int d_h, int r, int L_cap, int dtype, int d_model, void* k_shared,
                                  void* v_shared, void* z_k, void* z_v, int32_t* seq_lens, const void* x,

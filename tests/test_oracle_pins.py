@@ -421,3 +421,33 @@ def test_layer_planted_mistake_is_caught(plant):
         except (AssertionError, ValueError, RuntimeError):
             failed.append(pin.__name__)
     assert failed, f"planted layer mistake {plant} slipped through every pin"
+
+
+# ---------------------------------------------------------------------------------------------
+# several query tokens per sequence with a causal mask inside the chunk
+# ---------------------------------------------------------------------------------------------
+def pin_multi_query_causal(lib_path=None):
+    """Q trailing query tokens with the causal mask inside the chunk, checked against torch's
+    scaled_dot_product_attention (fp64) on materialised per-head keys and values with an explicit mask."""
+    for i, (B, Q, H, d_h, r, L) in enumerate([(2, 3, 2, 8, 3, 9), (1, 4, 3, 4, 2, 4), (3, 2, 1, 6, 6, 7)]):
+        c = _random_case(1300 + 10 * i, B, H, d_h, r, L, [L - b for b in range(B)])
+        q = _rand(1305 + 10 * i, (B, Q, H, d_h))
+        lens = np.array([L - b for b in range(B)], dtype=np.int32)
+        got = oracle.lrkv_decode_multi("f64", q, c["k"], c["v"], c["zk"], c["zv"], c["Bk"], c["Bv"], lens,
+                                       lib_path=lib_path)
+        for b in range(B):
+            n = int(lens[b])
+            for h in range(H):
+                K = torch.from_numpy(c["k"][b, :n] + c["zk"][b, h, :n] @ c["Bk"][h].T)
+                V = torch.from_numpy(c["v"][b, :n] + c["zv"][b, h, :n] @ c["Bv"][h].T)
+                pos = torch.arange(n - Q, n)[:, None]           # query positions (may be negative)
+                mask = torch.arange(n)[None, :] <= pos           # [Q][n]
+                qq = torch.from_numpy(q[b, :, h])
+                ref = torch.nn.functional.scaled_dot_product_attention(qq[None], K[None], V[None],
+                                                                       attn_mask=mask[None])[0]
+                seen = mask.any(dim=1)
+                ref = torch.where(seen[:, None], ref, torch.zeros_like(ref))  # a query that sees nothing: 0
+                np.testing.assert_allclose(got[b, :, h], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+ALL_PINS.append(pin_multi_query_causal)
