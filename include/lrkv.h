@@ -174,6 +174,18 @@ lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lr
                               const void* q, const float* p, const void* B_v, float* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Rebuild every head's keys and values from the factored cache (reading notes
+ * sec. 2.1 Eqs. (2)-(5); review sec. 3, the materialised form training and
+ * prefill use):
+ *   K_out[b][h][j] = k_shared[b][j] + z_k[b][j][h] (B_k[h])^T
+ *   V_out[b][h][j] = v_shared[b][j] + z_v[b][j][h] (B_v[h])^T,  j < seq_lens[b]
+ *   K_out, V_out  device [batch][H][L_cap][d_h] (dims->dtype); rows j >= seq_lens[b] are not written
+ *   max_len       host bound of seq_lens, 0 <= max_len <= L_cap
+ * Arithmetic: fp32 sums rounded once to dims->dtype.  bf16 with d_h a multiple
+ * of 16 and r a multiple of 8 up to 64 runs on the matrix cores. */
+lrkv_status lrkv_materialize(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* B_k,
+                             const void* B_v, void* K_out, void* V_out, void* stream);
+
 /* Project the new token of every sequence and append it to the cache, in one
  * stacked product (review sec. 3, Algorithm 1; reading notes sec. 2.1
  * Eqs. (2)-(5) and sec. 2.3):

@@ -122,3 +122,23 @@ def layer_step(dtype: str, x, W_in, W_o, B_k, B_v, cache: Dict[str, np.ndarray],
     Wo = widen(dtype, W_o)
     y = o.reshape(B, H * d_h) @ (Wo if plant == 2 else Wo.T)
     return {"y": y, "o": o, "lens": lens, **stored}
+
+
+def materialize(dtype: str, k_shared, v_shared, z_k, z_v, B_k, B_v, seq_lens):
+    """Per-head keys and values of every live row, rebuilt from the factored cache and stored in dtype:
+    K_h = K_S + Z^K_h (B^K_h)^T, V_h = V_S + Z^V_h (B^V_h)^T (reading notes sec. 2.1 Eqs. (2)-(5); review
+    sec. 3, the materialised path used for training and prefill).  Inputs in the per-head layout; returns
+    (K, V) as [batch][H][L_cap][d_h] in dtype, rows at or past seq_lens[b] zero."""
+    ks, vs = widen(dtype, k_shared), widen(dtype, v_shared)
+    zk, zv = widen(dtype, z_k), widen(dtype, z_v)
+    bk, bv = widen(dtype, B_k), widen(dtype, B_v)
+    B, H, L_cap, r = zk.shape
+    d_h = ks.shape[-1]
+    K = np.zeros((B, H, L_cap, d_h))
+    V = np.zeros((B, H, L_cap, d_h))
+    for b in range(B):
+        n = int(seq_lens[b])
+        for h in range(H):
+            K[b, h, :n] = ks[b, :n] + zk[b, h, :n] @ bk[h].T
+            V[b, h, :n] = vs[b, :n] + zv[b, h, :n] @ bv[h].T
+    return round_to(dtype, K), round_to(dtype, V)

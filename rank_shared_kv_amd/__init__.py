@@ -27,7 +27,7 @@ LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
-            "lrkv_decode_multi", "lrkv_project_append", "lrkv_output_project",
+            "lrkv_decode_multi", "lrkv_materialize", "lrkv_project_append", "lrkv_output_project",
             "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_multi_workspace_bytes": ([D, i32, i32], sz),
             "lrkv_decode_multi": ([D, i32, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_materialize": ([D, C, i32, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_project_append": ([D, i32, C, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_output_project": ([D, i32, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_cache_bytes": ([D, vp], ctypes.c_uint64),
@@ -172,6 +173,11 @@ def lrkv_decode_multi(dims: Dims, n_queries: int, cache: Cache, max_len: int, q,
     _check(lib().lrkv_decode_multi(ctypes.byref(dims), n_queries, ctypes.byref(cache), max_len, _ptr(q), _ptr(p),
                                    _ptr(B_v), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
            "lrkv_decode_multi")
+
+
+def lrkv_materialize(dims: Dims, cache: Cache, max_len: int, B_k, B_v, K_out, V_out, stream=None) -> None:
+    _check(lib().lrkv_materialize(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(B_k), _ptr(B_v), _ptr(K_out),
+                                  _ptr(V_out), _stream(stream)), "lrkv_materialize")
 
 
 def lrkv_project_append(dims: Dims, d_model: int, cache: Cache, x, W_in, q_out, stream=None) -> None:

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(HERE, "liblrkv.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["lrkv_api.cpp", "k_cache.hip", "k_decode_general.hip", "k_decode_mfma.hip", "k_decode_mfma_f32.hip",
-           "k_merge.hip", "k_linear.hip"]
+           "k_merge.hip", "k_linear.hip", "k_materialize.hip"]
 
 # Packed fp32 instructions are disabled in device code: ordinary float code
 # only, scheduled by the compiler without v_pk_*_f32.

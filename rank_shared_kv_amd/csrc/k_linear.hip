@@ -163,6 +163,7 @@ __global__ void __launch_bounds__(KW * 64) linear_mfma_kernel(int M, int K, int 
                                                                      0, 0);
             }
     }
+    mfma_result_fence();  // the K loop ends with products; their results are read next
     // D layout: lane (n16, g4) holds rows 4 g4 + i of the tile, feature n0 + n16
 #pragma unroll
     for (int t = 0; t < MT; ++t)

@@ -1,0 +1,132 @@
+// Materialised per-head keys and values from the factored cache:
+//   K_h[j] = k_shared[j] + z^K_{h,j} (B^K_h)^T,   V_h[j] = v_shared[j] + z^V_{h,j} (B^V_h)^T
+// for every live row j < seq_lens[b] ("Low-Rank Key Value Attention: Chinese
+// reading notes", sec. 2.1 Eqs. (2)-(5); "Low-Rank Key Value Attention | What
+// a shared cache can preserve", sec. 3: the rebuilt form training and prefill
+// use).  Output [batch][H][L_cap][d_h] in the cache dtype.
+//
+// bf16 path (r <= 64): a wave owns 16 rows of one head and computes, per 16-column block
+// of d_h, Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16] on
+// v_mfma_f32_16x16x32_bf16 (k-steps of 32 rank coordinates; coordinates past r
+// enter as zeros).  In that layout each lane holds four consecutive columns of
+// one row, so the shared row is added and the result stored 8 bytes at a time.
+// fp32 (or shapes off the grid): one thread per output element.
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;  // 64 rows of one head per workgroup
+
+// NKS k-steps of 32 rank coordinates (1 for r <= 32, 2 for r <= 64), a compile-time count: the products
+// and the reads of their results then sit in one straight-line block, where the compiler places the wait
+// states between a matrix-core result and its first read (with a run-time loop count those waits were
+// missing at the loop exit and three of the four result registers were read too early).
+template <int NKS>
+__global__ void __launch_bounds__(kWaves * 64) materialize_mfma_kernel(int H, int D, int R, int L_cap, int max_len,
+                                                                       const int32_t* __restrict__ seq_lens,
+                                                                       const uint16_t* __restrict__ shared,
+                                                                       const uint16_t* __restrict__ z,
+                                                                       const uint16_t* __restrict__ basis,
+                                                                       uint16_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int Lb = clamped_len(seq_lens, b, max_len);
+    const int t0 = (blockIdx.x * kWaves + wave) * 16;
+    if (t0 >= Lb) return;
+    const int row = t0 + n16;                       // this lane's row (B operand column, result column)
+    const int row_c = min(row, L_cap - 1);          // clamped: loads stay inside the allocation
+    const uint16_t* zrow = z + (((size_t)b * L_cap + row_c) * H + h) * R;  // token-major latents
+    const uint16_t* bh = basis + (size_t)h * D * R;
+    for (int cb = 0; cb < D / 16; ++cb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k = 32 * ks + 8 * g4;
+            const bool in = k < R;                   // R is a multiple of 8: whole 8-coordinate groups
+            const int kc = in ? k : 0;
+            u32x4_t zv = *(const u32x4_t*)(zrow + kc);
+            u32x4_t bv = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + kc);
+            if (!in) zv = bv = u32x4_t{0u, 0u, 0u, 0u};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bv),
+                                                          __builtin_bit_cast(bf16x8_t, zv), acc, 0, 0, 0);
+        }
+        mfma_result_fence();
+        // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row
+        if (row < Lb) {
+            const int c0 = 16 * cb + 4 * g4;
+            const u32x2_t s = *(const u32x2_t*)(shared + ((size_t)b * L_cap + row) * D + c0);
+            const float v0 = acc[0] + bf16_lo(s[0]), v1 = acc[1] + bf16_hi(s[0]);
+            const float v2 = acc[2] + bf16_lo(s[1]), v3 = acc[3] + bf16_hi(s[1]);
+            u32x2_t o;
+            o[0] = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+            o[1] = f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16);
+            *(u32x2_t*)(out + (((size_t)b * H + h) * L_cap + row) * D + c0) = o;
+        }
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) materialize_simple_kernel(int batch, int H, int D, int R, int L_cap,
+                                                                 int max_len, const int32_t* __restrict__ seq_lens,
+                                                                 const T* __restrict__ shared,
+                                                                 const T* __restrict__ z, const T* __restrict__ basis,
+                                                                 T* __restrict__ out) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t total = (size_t)batch * H * max_len * D;
+    if (idx >= total) return;
+    const int c = (int)(idx % D);
+    const int row = (int)((idx / D) % max_len);
+    const int h = (int)((idx / ((size_t)D * max_len)) % H);
+    const int b = (int)(idx / ((size_t)D * max_len * H));
+    if (row >= clamped_len(seq_lens, b, max_len)) return;
+    float s = elem<T>::load(shared, ((size_t)b * L_cap + row) * D + c);
+    const size_t zr = (((size_t)b * L_cap + row) * H + h) * R;
+    for (int i = 0; i < R; ++i) s = fmaf(elem<T>::load(z, zr + i), elem<T>::load(basis, ((size_t)h * D + c) * R + i), s);
+    const size_t o = (((size_t)b * H + h) * L_cap + row) * D + c;
+    if constexpr (sizeof(T) == 4) out[o] = s;
+    else out[o] = (T)f32_to_bf16_bits(s);
+}
+
+hipError_t launch_one(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, const int32_t* seq_lens,
+                      const void* shared, const void* z, const void* basis, void* out, hipStream_t stream) {
+    if (max_len == 0) return hipSuccess;
+    if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
+        dim3 grid((max_len + 16 * kWaves - 1) / (16 * kWaves), H, batch);
+        auto kern = (r <= 32) ? materialize_mfma_kernel<1> : materialize_mfma_kernel<2>;
+        hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, d_h, r, L_cap, max_len, seq_lens,
+                           (const uint16_t*)shared, (const uint16_t*)z, (const uint16_t*)basis, (uint16_t*)out);
+    } else {
+        const size_t total = (size_t)batch * H * max_len * d_h;
+        dim3 grid((unsigned)((total + 255) / 256));
+        if (dtype == 0)
+            hipLaunchKernelGGL(materialize_simple_kernel<float>, grid, dim3(256), 0, stream, batch, H, d_h, r, L_cap,
+                               max_len, seq_lens, (const float*)shared, (const float*)z, (const float*)basis,
+                               (float*)out);
+        else
+            hipLaunchKernelGGL(materialize_simple_kernel<uint16_t>, grid, dim3(256), 0, stream, batch, H, d_h, r,
+                               L_cap, max_len, seq_lens, (const uint16_t*)shared, (const uint16_t*)z,
+                               (const uint16_t*)basis, (uint16_t*)out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len,
+                              const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
+                              const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
+                              hipStream_t stream) {
+    hipError_t e = launch_one(batch, H, d_h, r, L_cap, dtype, max_len, seq_lens, k_shared, z_k, B_k, K_out, stream);
+    if (e != hipSuccess) return e;
+    return launch_one(batch, H, d_h, r, L_cap, dtype, max_len, seq_lens, v_shared, z_v, B_v, V_out, stream);
+}
+
+}  // namespace lrkv

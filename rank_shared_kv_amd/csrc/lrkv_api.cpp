@@ -342,6 +342,25 @@ lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lr
     return ok();
 }
 
+lrkv_status lrkv_materialize(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* B_k,
+                             const void* B_v, void* K_out, void* V_out, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (max_len < 0 || max_len > dims->L_cap)
+        return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(K_out, "K_out"));
+    LRKV_TRY(need_ptr(V_out, "V_out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(B_k, "B_k"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    hipError_t e = lrkv::launch_materialize(dims->batch, dims->H, dims->d_h, dims->r, dims->L_cap, dims->dtype, max_len,
+                                            cache->seq_lens, cache->k_shared, cache->v_shared, cache->z_k, cache->z_v,
+                                            B_k, B_v, K_out, V_out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "materialize kernel launch");
+    return ok();
+}
+
 lrkv_status lrkv_project_append(const lrkv_dims* dims, int32_t d_model, const lrkv_cache* cache, const void* x,
                                 const void* W_in, void* q_out, void* stream) {
     LRKV_TRY(check_dims(dims));

@@ -48,6 +48,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait states between matrix-core products and the first read of their results, for code where the
+// products end a loop with a run-time trip count and the results are read after it: at such a loop exit
+// the compiler was seen to read accumulators too early.  24 wait states cover the longest result latency
+// of the 16x16 products used here.  Costs a few dozen cycles per use.
+__device__ __forceinline__ void mfma_result_fence() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // log2(e): scores are carried in log2 units so that exp2 (v_exp_f32) applies.
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -60,6 +60,10 @@ int general_rows_per_tile();  // rows one general-kernel split advances per step
 hipError_t launch_project_append(int batch, int H, int d_h, int r, int L_cap, int dtype, int d_model, void* k_shared,
                                  void* v_shared, void* z_k, void* z_v, int32_t* seq_lens, const void* x,
                                  const void* W_in, void* q_out, hipStream_t stream);
+hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len,
+                              const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
+                              const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
+                              hipStream_t stream);
 hipError_t launch_output_project(int batch, int H, int d_h, int dtype, int d_model, const float* o, const void* W_o,
                                  float* y, hipStream_t stream);
 

@@ -206,3 +206,49 @@ def test_project_append_long_context_full_size():
     ref = olayer.linear("f32", o, "bf16", W_o)
     err = np.abs(y_o.cpu().numpy().astype(np.float64) - ref) - _bound("f32", o, "bf16", W_o)
     assert np.all(err <= 0)
+
+
+MAT_CASES = [  # (dtype, batch, H, d_h, r, lengths)
+    ("bf16", 3, 8, 64, 8, [100, 17, 0]),
+    ("bf16", 2, 32, 128, 64, [300, 65]),
+    ("bf16", 2, 16, 128, 48, [129, 1]),
+    ("f32", 2, 4, 16, 4, [40, 9]),
+    ("bf16", 2, 8, 64, 0, [50, 3]),
+]
+
+
+@pytest.mark.parametrize("case", MAT_CASES, ids=lambda c: f"{c[0]}_B{c[1]}_H{c[2]}_d{c[3]}_r{c[4]}")
+def test_materialize(case):
+    """Rebuilt per-head keys and values against the reference: |g - y| <= half an ulp of the storage type
+    plus 1e-5 * (|k_s| + sum_i |z_i b_i|) (at most 65 fp32 terms); rows past each length untouched."""
+    dtype, B, H, d_h, r, lens = case
+    L = max(lens)
+    w = synth.WORKLOADS["small_bf16"].with_(name="mat", batch=B, H=H, d_h=d_h, r=r, dtype=dtype, L=L,
+                                            L_cap=L + 16, ragged_lo=None)
+    lens = np.array(lens, dtype=np.int32)
+    say(f"[case] materialize {case}")
+    dev = sdev.fill_layer(w, 0, lengths=lens)
+    # sentinels exactly representable in bf16 and fp32
+    K = torch.full((B, H, w.cap, d_h), 1024.0, dtype=sdev.torch_dtype(w), device="cuda")
+    V = torch.full_like(K, -512.0)
+    lk.lrkv_materialize(dims_of(w), cache_of(dev, r), L, dev["B_k"] if r else None, dev["B_v"] if r else None, K, V)
+    torch.cuda.synchronize()
+    host = _host_cache(w, lens)
+    npdt = host["k_shared"].dtype
+    Bk = synth.gen_small(w, 0, "B_k") if r else np.zeros((H, d_h, 0), npdt)
+    Bv = synth.gen_small(w, 0, "B_v") if r else np.zeros((H, d_h, 0), npdt)
+    for out, shared, z, basis, fill, name in ((K, "k_shared", "z_k", Bk, 1024.0, "K"),
+                                              (V, "v_shared", "z_v", Bv, -512.0, "V")):
+        ks = olayer.widen(dtype, host[shared])
+        zz = olayer.widen(dtype, host[z])
+        bb = olayer.widen(dtype, basis)
+        got = _dev_array(out, dtype)
+        for b in range(B):
+            n = int(lens[b])
+            for h in range(H):
+                ref = ks[b, :n] + zz[b, h, :n] @ bb[h].T
+                bound = 1e-5 * (np.abs(ks[b, :n]) + np.abs(zz[b, h, :n]) @ np.abs(bb[h]).T)
+                _check_stored(dtype, got[b, h, :n], ref, bound, f"{name}[{b},{h}]") if (b, h) == (0, 0) else None
+                half_ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
+                assert np.all(np.abs(olayer.widen(dtype, got[b, h, :n]) - ref) <= half_ulp * np.abs(ref) + bound)
+            assert np.all(olayer.widen(dtype, got[b, :, n:]) == fill), f"{name}: rows past the length written"

@@ -451,3 +451,39 @@ def pin_multi_query_causal(lib_path=None):
 
 
 ALL_PINS.append(pin_multi_query_causal)
+
+
+def pin_materialize_weight_space(lib_path=None, plant=0):
+    """Keys and values rebuilt from the factored cache equal the projections through materialised weights
+    W_h = W_S + U_h B_h^T (torch fp64 route), and attending over them reproduces the decode reference."""
+    B, H, d_h, r, dm, L = 2, 3, 4, 2, 7, 6
+    c = _layer_case(1400, B, H, d_h, r, dm, L)
+    lens = np.array([L, L - 2], dtype=np.int32)
+    cache = olayer.project_history("f64", c["X"], c["W_in"], H, d_h, r, L, lens)
+    K, V = olayer.materialize("f64", cache["k_shared"], cache["v_shared"], cache["z_k"], cache["z_v"], c["B_k"],
+                              c["B_v"], lens)
+    W = torch.from_numpy(c["W_in"])
+    o = H * d_h
+    WSK, WSV = W[o:o + d_h], W[o + d_h:o + 2 * d_h]
+    UK, UV = W[o + 2 * d_h:o + 2 * d_h + H * r], W[o + 2 * d_h + H * r:]
+    for b in range(B):
+        n = int(lens[b])
+        X = torch.from_numpy(c["X"][b, :n])
+        for h in range(H):
+            WK_h = WSK.T + UK[h * r:(h + 1) * r].T @ torch.from_numpy(c["B_k"][h]).T
+            WV_h = WSV.T + UV[h * r:(h + 1) * r].T @ torch.from_numpy(c["B_v"][h]).T
+            np.testing.assert_allclose(K[b, h, :n], (X @ WK_h).numpy(), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(V[b, h, :n], (X @ WV_h).numpy(), rtol=1e-12, atol=1e-12)
+        assert not K[b, :, n:].any() and not V[b, :, n:].any()
+    q = _rand(1410, (B, H, d_h))
+    ref = oracle.lrkv_decode("f64", q, cache["k_shared"], cache["v_shared"], cache["z_k"], cache["z_v"], c["B_k"],
+                             c["B_v"], lens, lib_path=lib_path).reshape(B, H, d_h)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(H):
+            a = torch.softmax(torch.from_numpy(K[b, h, :n] @ q[b, h]) / math.sqrt(d_h), dim=0)
+            np.testing.assert_allclose(ref[b, h], (a @ torch.from_numpy(V[b, h, :n])).numpy(), rtol=1e-12,
+                                       atol=1e-13)
+
+
+LAYER_PINS.append(pin_materialize_weight_space)
