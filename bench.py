@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--layer", action="store_true",
                     help="time the whole layer step: project + append (d_model = H*d_h), absorb, decode, output "
                          "projection (random seeded weights)")
+    ap.add_argument("--queries", type=int, default=1, metavar="Q",
+                    help="multi-token decode: Q new query tokens per sequence and step, causal inside the chunk "
+                         "(each step appends Q rows, absorbs B*Q queries and runs lrkv_decode_multi)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -141,6 +144,10 @@ def main():
               f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
         sys.exit(2)
 
+    if args.queries > 1 and args.layer:
+        print("bench.py: --queries and --layer do not combine", file=sys.stderr)
+        sys.exit(2)
+
     import numpy as np
     import torch
 
@@ -149,13 +156,13 @@ def main():
     from synth import device as sdev
 
     w = synth.WORKLOADS[args.workload]
-    K, W = args.steps, args.warmup
+    K, W, Q = args.steps, args.warmup, max(1, args.queries)
     lens_full = synth.seq_lengths(w)
-    L_cap, max_len = launch_config(w, K, args.capacity)
-    start_lens = lens_full - 1 - W
+    L_cap, max_len = launch_config(w, K * Q, args.capacity)
+    start_lens = lens_full - Q - W * Q
     assert int(start_lens.min()) >= 0
     log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
-        f"steps={K} warmup={W}")
+        f"steps={K} warmup={W} queries={Q}")
     t0 = time.time()
     dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens_full)
     dev["seq_lens"].copy_(torch.from_numpy(start_lens.astype(np.int32)).cuda())
@@ -172,6 +179,15 @@ def main():
     p = torch.empty((w.batch, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")
     out = torch.empty((w.batch, w.H, w.d_h), dtype=torch.float32, device="cuda")
     S, chunk = lk.lrkv_decode_num_splits(dims, max_len)
+    if Q > 1:
+        nbytes = lk.lrkv_decode_multi_workspace_bytes(dims, Q, max_len)
+        ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+        dims_q = lk.make_dims(w.batch * Q, w.H, w.d_h, w.r, L_cap, dtype_code)
+        q_multi = sdev.to_device(synth.normal(8803, 1.0, w.batch * Q * w.H * w.d_h, w.dtype)
+                                 .reshape(w.batch, Q, w.H, w.d_h))
+        p = torch.empty((w.batch, Q, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")
+        out = torch.empty((w.batch, Q, w.H, w.d_h), dtype=torch.float32, device="cuda")
+        S, chunk = None, None
     stream = torch.cuda.current_stream()
     pp = p if w.r else None
     bv = dev["B_v"] if w.r else None
@@ -197,7 +213,20 @@ def main():
         e.record(stream)
         return e
 
+    def step_multi(timed: bool):
+        for _ in range(Q):
+            lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+        if w.r:
+            lk.lrkv_absorb_query(dims_q, q_multi, dev["B_k"], p, stream)
+        if timed:
+            e0 = ev()
+        lk.lrkv_decode_multi(dims, Q, cache, max_len, q_multi, p if w.r else None, bv, out, ws, nbytes, stream)
+        if timed:
+            ev_pairs.append((e0, ev()))
+
     def step(timed: bool):
+        if Q > 1:
+            return step_multi(timed)
         if args.layer:
             e_p0 = ev() if timed else None
             lk.lrkv_project_append(dims, d_model, cache, x_new, W_in, q_step, stream)
@@ -223,7 +252,7 @@ def main():
     for _ in range(W):
         step(False)
     torch.cuda.synchronize()
-    assert dev["seq_lens"].cpu().numpy().tolist() == (lens_full - 1).tolist()
+    assert dev["seq_lens"].cpu().numpy().tolist() == (lens_full - Q).tolist()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -234,26 +263,30 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     split_ms = [a.elapsed_time(b) for a, b in ev_pairs]
     final_lens = dev["seq_lens"].cpu().numpy()
-    assert final_lens.tolist() == (lens_full - 1 + K).tolist()
+    assert final_lens.tolist() == (lens_full - Q + K * Q).tolist()
     assert bool(torch.isfinite(out).all())
 
-    # work per timed step k: every sequence decodes over lens_full + k rows
-    token_heads = sum(int(np.sum(lens_full + k, dtype=np.int64)) * w.H for k in range(K))
+    # work per timed step k: sequence b holds lens_full + k*Q rows, and its query i (0-based among the Q new
+    # tokens) sees the rows up to and including its own, lens_full + k*Q - Q + i + 1 of them
+    token_heads = sum(int(np.sum(Q * (lens_full + k * Q) - Q * (Q - 1) // 2, dtype=np.int64)) * w.H
+                      for k in range(K))
     value = token_heads / (total_ms / 1e3)
     s_bytes = w.elem_bytes
-    cache_bytes_per_step = [lk.lrkv_cache_bytes(dims, (lens_full + k).tolist()) for k in range(K)]
-    q_bytes = w.batch * w.H * w.d_h * s_bytes
-    p_bytes = w.batch * w.H * w.r * 4
+    cache_bytes_per_step = [lk.lrkv_cache_bytes(dims, (lens_full + k * Q).tolist()) for k in range(K)]
+    q_bytes = Q * w.batch * w.H * w.d_h * s_bytes
+    p_bytes = Q * w.batch * w.H * w.r * 4
     basis_bytes = 2 * w.H * w.d_h * w.r * s_bytes
-    out_bytes = w.batch * w.H * w.d_h * 4
+    out_bytes = Q * w.batch * w.H * w.d_h * 4
     step_bytes = sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes
     split_bytes = sum(cache_bytes_per_step) / K + q_bytes + p_bytes
+    if Q > 1:  # the timed call is the whole multi-query decode: split pass, merge and epilogue
+        split_bytes += out_bytes + w.H * w.d_h * w.r * s_bytes
     split_avg_ms = sum(split_ms) / len(split_ms)
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = read_traffic(w.name, split_bytes) if not args.layer else None
+    traffic = read_traffic(w.name, split_bytes) if not args.layer and Q == 1 else None
     layer = None
     if args.layer:
         assert bool(torch.isfinite(y_step).all())
@@ -270,7 +303,8 @@ def main():
         step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
         log(f"bench: layer step: project+append {proj_us:.1f} us ({layer['project_weight_gbps']:.0f} GB/s of "
             f"weights), output projection {outp_us:.1f} us ({layer['output_weight_gbps']:.0f} GB/s)")
-    log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); split pass {split_avg_ms * 1e3:.1f} us "
+    log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); "
+        f"{'split pass' if Q == 1 else 'multi-query decode'} {split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
     cpu = None
@@ -292,15 +326,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name + ("+projections" if args.layer else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+        "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
-                   "splits": S, "chunk_tokens": chunk},
+                   "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q},
         "hbm_gbps_step": step_gbps,
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": split_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "kernel": "split pass (lrkv_decode_partial)",
+                     "traffic": traffic, "kernel": "split pass (lrkv_decode_partial)" if Q == 1 else
+                     "lrkv_decode_multi (split pass + merge)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
         "mfma_util_shared_score": mfma_util,
         "layer_step": layer,
