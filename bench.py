@@ -50,7 +50,8 @@ def launch_config(w, steps: int, capacity: int = 0):
 
 
 # the sources that determine the bf16 split kernel's code and launch configuration
-SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hip", "lrkv_device.hpp", "lrkv_internal.hpp", "lrkv_api.cpp")
+SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hpp", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma.hip", "lrkv_device.hpp",
+                        "lrkv_internal.hpp", "lrkv_api.cpp")
 
 
 def kernel_sources_digest() -> str:
@@ -126,6 +127,9 @@ def main():
     ap.add_argument("--queries", type=int, default=1, metavar="Q",
                     help="multi-token decode: Q new query tokens per sequence and step, causal inside the chunk "
                          "(each step appends Q rows, absorbs B*Q queries and runs lrkv_decode_multi)")
+    ap.add_argument("--norm", action="store_true",
+                    help="normalised variant: each step appends a row, computes its key scales, normalises the "
+                         "query (gain folded in), absorbs it and runs lrkv_decode_normed")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -144,8 +148,8 @@ def main():
               f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
         sys.exit(2)
 
-    if args.queries > 1 and args.layer:
-        print("bench.py: --queries and --layer do not combine", file=sys.stderr)
+    if sum([args.queries > 1, args.layer, args.norm]) > 1:
+        print("bench.py: --queries, --layer and --norm do not combine", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -188,6 +192,13 @@ def main():
         p = torch.empty((w.batch, Q, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")
         out = torch.empty((w.batch, Q, w.H, w.d_h), dtype=torch.float32, device="cuda")
         S, chunk = None, None
+    if args.norm:
+        eps = 1e-6
+        rho = torch.empty((w.batch, L_cap, w.H), dtype=sdev.torch_dtype(w), device="cuda")
+        lk.lrkv_key_scales(dims, cache, max_len, max_len, dev["B_k"] if w.r else None, eps, rho)
+        g_q = sdev.to_device(synth.gain(8804, (w.H, w.d_h), w.dtype))
+        g_k = sdev.to_device(synth.gain(8805, (w.H, w.d_h), w.dtype))
+        q_eff = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
     pp = p if w.r else None
     bv = dev["B_v"] if w.r else None
@@ -224,9 +235,23 @@ def main():
         if timed:
             ev_pairs.append((e0, ev()))
 
+    def step_norm(timed: bool):
+        lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+        lk.lrkv_key_scales(dims, cache, max_len, 1, dev["B_k"] if w.r else None, eps, rho, stream)
+        lk.lrkv_norm_query(dims, dev["q"], g_q, g_k, eps, q_eff, stream)
+        if w.r:
+            lk.lrkv_absorb_query(dims, q_eff, dev["B_k"], p, stream)
+        if timed:
+            e0 = ev()
+        lk.lrkv_decode_normed(dims, cache, rho, max_len, q_eff, pp, bv, out, ws, nbytes, stream)
+        if timed:
+            ev_pairs.append((e0, ev()))
+
     def step(timed: bool):
         if Q > 1:
             return step_multi(timed)
+        if args.norm:
+            return step_norm(timed)
         if args.layer:
             e_p0 = ev() if timed else None
             lk.lrkv_project_append(dims, d_model, cache, x_new, W_in, q_step, stream)
@@ -279,14 +304,18 @@ def main():
     out_bytes = Q * w.batch * w.H * w.d_h * 4
     step_bytes = sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes
     split_bytes = sum(cache_bytes_per_step) / K + q_bytes + p_bytes
-    if Q > 1:  # the timed call is the whole multi-query decode: split pass, merge and epilogue
+    if args.norm:  # the scales are read once per step, one per (row, head)
+        rho_bytes = [sum(int(x) for x in (lens_full + k)) * w.H * s_bytes for k in range(K)]
+        split_bytes += sum(rho_bytes) / K
+        step_bytes += sum(rho_bytes) / K
+    if Q > 1 or args.norm:  # the timed call is the whole decode: split pass, merge and epilogue
         split_bytes += out_bytes + w.H * w.d_h * w.r * s_bytes
     split_avg_ms = sum(split_ms) / len(split_ms)
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = read_traffic(w.name, split_bytes) if not args.layer and Q == 1 else None
+    traffic = read_traffic(w.name, split_bytes) if not (args.layer or args.norm) and Q == 1 else None
     layer = None
     if args.layer:
         assert bool(torch.isfinite(y_step).all())
@@ -304,7 +333,7 @@ def main():
         log(f"bench: layer step: project+append {proj_us:.1f} us ({layer['project_weight_gbps']:.0f} GB/s of "
             f"weights), output projection {outp_us:.1f} us ({layer['output_weight_gbps']:.0f} GB/s)")
     log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); "
-        f"{'split pass' if Q == 1 else 'multi-query decode'} {split_avg_ms * 1e3:.1f} us "
+        f"{'split pass' if Q == 1 and not args.norm else 'whole decode call'} {split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
     cpu = None
@@ -326,7 +355,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+        "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else "") + ("+normalised" if args.norm else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
                    "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q},
@@ -334,8 +363,8 @@ def main():
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": split_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic, "kernel": "split pass (lrkv_decode_partial)" if Q == 1 else
-                     "lrkv_decode_multi (split pass + merge)",
+                     "traffic": traffic, "kernel": "lrkv_decode_multi (split pass + merge)" if Q > 1 else
+                     "lrkv_decode_normed (split pass + merge)" if args.norm else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
         "mfma_util_shared_score": mfma_util,
         "layer_step": layer,

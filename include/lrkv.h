@@ -174,6 +174,51 @@ lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lr
                               const void* q, const float* p, const void* B_v, float* out, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Normalised variant: post-projection RMS normalisation of the keys and
+ * queries, evaluated exactly on the factored cache (review sec. 8, the
+ * paragraphs on post-projection normalisation and its cache cost; reading
+ * notes sec. 2.7, last paragraph).  The key of head h at token j is the summed
+ * key k_{h,j} = k_shared[j] + z_k[j][h] (B_k[h])^T; it is normalised as a whole
+ * (the shared and private parts together), with a per-head gain g_k[h], and the
+ * query with g_q[h]:
+ *   rho_{h,j} = 1 / sqrt(|k_{h,j}|^2 / d_h + eps)       one scalar per (token, head), cached
+ *   q_eff[b][h] = g_k[h] * g_q[h] * q[b][h] / sqrt(|q[b][h]|^2 / d_h + eps)   (the key gain folded in)
+ *   s_j = rho_{h,j} * (q_eff . k_shared[j] + p . z_k[j][h]) / sqrt(d_h),  p = q_eff B_k[h]
+ * Values are not normalised.  The scales are kept beside the cache:
+ *   rho  device [batch][L_cap][H] (dims->dtype), token-major like the latents:
+ *        2 bytes per (token, head) in bf16, 1/(2 d_h) of a per-head K/V payload.
+ * A step: lrkv_cache_append (or lrkv_project_append), lrkv_key_scales with
+ * n_last = 1, lrkv_norm_query, lrkv_absorb_query on q_eff, lrkv_decode_normed. */
+
+/* Scales of the last n_last live rows of every sequence, rows
+ * max(0, L_b - n_last) .. L_b - 1 (n_last = 1 after an append; n_last >= max_len
+ * for the whole history, e.g. after a prefill).  Other rows of rho are not
+ * written.  The key is rebuilt in fp32 from the stored factors (never stored)
+ * and the scale rounded once to dims->dtype (nearest even).
+ *   max_len  host bound of seq_lens, 0 <= max_len <= L_cap
+ *   n_last   >= 0; B_k device [H][d_h][r] (may be NULL iff r == 0); eps finite, >= 0
+ *            (with eps = 0 an all-zero key gets an infinite scale)
+ * bf16 with d_h a multiple of 16 and r a multiple of 8 up to 64 runs on the
+ * matrix cores; other shapes on a plain kernel. */
+lrkv_status lrkv_key_scales(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, int32_t n_last,
+                            const void* B_k, float eps, void* rho, void* stream);
+
+/* The normalised query with the key gain folded in, q_eff as above, rounded
+ * once to dims->dtype (nearest even):
+ *   q, q_eff  device [batch][H][d_h];  g_q, g_k  device [H][d_h]  (all dims->dtype)
+ * Arithmetic: fp32, the sum of squares reduced in a fixed order. */
+lrkv_status lrkv_norm_query(const lrkv_dims* dims, const void* q, const void* g_q, const void* g_k, float eps,
+                            void* q_eff, void* stream);
+
+/* lrkv_decode with every logit multiplied by its cached scale (above).
+ * Arguments as lrkv_decode with q = q_eff (and p from lrkv_absorb_query on
+ * q_eff), plus rho as written by lrkv_key_scales; the workspace is
+ * lrkv_decode_workspace_bytes(dims, max_len).  Rows j < seq_lens[b] need their
+ * scale in rho. */
+lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, const void* rho, int32_t max_len,
+                               const void* q_eff, const float* p, const void* B_v, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Rebuild every head's keys and values from the factored cache (reading notes
  * sec. 2.1 Eqs. (2)-(5); review sec. 3, the materialised form training and
  * prefill use):

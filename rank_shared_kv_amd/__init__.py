@@ -27,8 +27,8 @@ LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
-            "lrkv_decode_multi", "lrkv_materialize", "lrkv_project_append", "lrkv_output_project",
-            "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
+            "lrkv_decode_multi", "lrkv_key_scales", "lrkv_norm_query", "lrkv_decode_normed", "lrkv_materialize",
+            "lrkv_project_append", "lrkv_output_project", "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
 
 class LrkvError(RuntimeError):
@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_multi_workspace_bytes": ([D, i32, i32], sz),
             "lrkv_decode_multi": ([D, i32, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_key_scales": ([D, C, i32, i32, vp, ctypes.c_float, vp, vp], ctypes.c_int),
+            "lrkv_norm_query": ([D, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int),
+            "lrkv_decode_normed": ([D, C, vp, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_materialize": ([D, C, i32, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_project_append": ([D, i32, C, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_output_project": ([D, i32, vp, vp, vp, vp], ctypes.c_int),
@@ -173,6 +176,23 @@ def lrkv_decode_multi(dims: Dims, n_queries: int, cache: Cache, max_len: int, q,
     _check(lib().lrkv_decode_multi(ctypes.byref(dims), n_queries, ctypes.byref(cache), max_len, _ptr(q), _ptr(p),
                                    _ptr(B_v), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
            "lrkv_decode_multi")
+
+
+def lrkv_key_scales(dims: Dims, cache: Cache, max_len: int, n_last: int, B_k, eps: float, rho, stream=None) -> None:
+    _check(lib().lrkv_key_scales(ctypes.byref(dims), ctypes.byref(cache), max_len, n_last, _ptr(B_k), float(eps),
+                                 _ptr(rho), _stream(stream)), "lrkv_key_scales")
+
+
+def lrkv_norm_query(dims: Dims, q, g_q, g_k, eps: float, q_eff, stream=None) -> None:
+    _check(lib().lrkv_norm_query(ctypes.byref(dims), _ptr(q), _ptr(g_q), _ptr(g_k), float(eps), _ptr(q_eff),
+                                 _stream(stream)), "lrkv_norm_query")
+
+
+def lrkv_decode_normed(dims: Dims, cache: Cache, rho, max_len: int, q_eff, p, B_v, out, workspace,
+                       workspace_bytes: int, stream=None) -> None:
+    _check(lib().lrkv_decode_normed(ctypes.byref(dims), ctypes.byref(cache), _ptr(rho), max_len, _ptr(q_eff),
+                                    _ptr(p), _ptr(B_v), _ptr(out), _ptr(workspace), workspace_bytes,
+                                    _stream(stream)), "lrkv_decode_normed")
 
 
 def lrkv_materialize(dims: Dims, cache: Cache, max_len: int, B_k, B_v, K_out, V_out, stream=None) -> None:

@@ -13,8 +13,11 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblrkv.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["lrkv_api.cpp", "k_cache.hip", "k_decode_general.hip", "k_decode_mfma.hip", "k_decode_mfma_f32.hip",
-           "k_merge.hip", "k_linear.hip", "k_materialize.hip"]
+# the bf16 decode kernel's instances are spread over four translation units so they compile in parallel
+SOURCES = ["lrkv_api.cpp", "k_cache.hip", "k_decode_general.hip", "k_decode_mfma.hip",
+           "k_decode_mfma_part_d64_n0.hip", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma_part_d64_n1.hip",
+           "k_decode_mfma_part_d128_n1.hip", "k_decode_mfma_f32.hip", "k_merge.hip", "k_linear.hip",
+           "k_materialize.hip", "k_norm.hip"]
 
 # Packed fp32 instructions are disabled in device code: ordinary float code
 # only, scheduled by the compiler without v_pk_*_f32.
@@ -44,7 +47,7 @@ def _run(cmd, verbose: bool) -> None:
 
 def build(verbose: bool = False, out_path: str = LIB_PATH, defines=(), jobs: int = 0) -> str:
     """Compile every source to an object in parallel (one hipcc per file), then link the shared library."""
-    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1, 8))
+    jobs = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1, 16))
     with tempfile.TemporaryDirectory(prefix="lrkv_build_") as tmpdir:
         cmds, objs = [], []
         for s in SOURCES:

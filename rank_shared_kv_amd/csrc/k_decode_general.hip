@@ -13,6 +13,9 @@
 // summed-logit score in "Low-Rank Key Value Attention: Chinese reading notes",
 // sec. 2.4 Eqs. (6)-(7).  The running state of all heads lives in LDS; the
 // split's final state is written to the workspace for the merge kernel.
+// Normalised variant (rho set): each logit is also multiplied by the cached
+// reciprocal RMS of its (head, token) key ("Low-Rank Key Value Attention |
+// What a shared cache can preserve", sec. 8, post-projection normalisation).
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
 
@@ -56,6 +59,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     const T* zk = (const T*)a.z_k;
     const T* zv = (const T*)a.z_v;
     const T* q = (const T*)a.q;
+    const T* rho = (const T*)a.rho;  // [batch][L_cap][H] or NULL
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float scale = kLog2e / sqrtf((float)D);
 
@@ -91,7 +95,10 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
             for (int c = c_lo; c < c_hi; ++c) sc = fmaf(elem<T>::load(q, bh * D + c), Kt[t * (D + 1) + c], sc);
             for (int i = i_lo; i < i_hi; ++i) sc = fmaf(a.p[bh * R + i], elem<T>::load(zk, zrow + i), sc);
             sc += __shfl_xor(sc, 32);
-            const float s2 = seen ? sc * scale : -INFINITY;
+            // normalised variant: the cached scale of (row, head) multiplies the summed logit
+            float f = scale;
+            if (rho) f *= elem<T>::load(rho, ((size_t)b * a.L_cap + (size_t)(t0 + (live ? t : 0))) * H + h);
+            const float s2 = seen ? sc * f : -INFINITY;
             float tmax = s2;
             for (int o = 16; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
             const float m_old = mrow[v];

@@ -1,0 +1,648 @@
+// MFMA split kernel for bf16 LRKV decode on gfx950 (CDNA4, wave64).
+//
+// What one step computes, per sequence b and head h (fp32 arithmetic):
+//   s_j = (q_h . k_j + p_h . z^K_{h,j}) / sqrt(d_h)    p_h = q_h B^K_h (absorbed)
+//   a   = softmax(s) over the live rows j < L_b          (one softmax, summed logits)
+//   o_h = sum_j a_j v_j + (sum_j a_j z^V_{h,j}) (B^V_h)^T
+// ("Low-Rank Key Value Attention: Chinese reading notes", sec. 2.4,
+// Eqs. (6)-(7); "Low-Rank Key Value Attention | What a shared cache can
+// preserve", sec. 3, Algorithm 2 and the fused online-softmax paragraph after
+// it).  This kernel produces, for every (b, split of `chunk` rows, h), the
+// online-softmax state of that split: running max m (log2 units), denominator
+// l, shared numerator sum_j e_j v_j (d_h) and private numerator
+// sum_j e_j z^V_{h,j} (r).  The merge kernel combines splits and applies B^V.
+//
+// Work decomposition.  A workgroup of 4 waves owns one (b, split).  Each wave
+// handles one group of 16 heads (the MFMA N dimension) on one "row lane": the
+// 32-row blocks tl, tl + NTL, ... of the split, where NTL = 4 / head groups.
+// Shared key/value rows of a block are read from HBM once per block and serve
+// every head of the group; with two head groups the second wave of the same
+// row lane re-reads them from the L2 of the same CU.  At the end the waves of
+// a head group merge their states in LDS in a fixed order and the workgroup
+// writes one record per head.
+//
+// Per 32-row block (one wave, 16 heads):
+//   * shared scores S^T[row][head] = K_s[32 x d_h] Q^T[d_h x 16] on MFMA
+//     (v_mfma_f32_16x16x32_bf16, exact bf16 products, fp32 accumulation); the
+//     key fragments are loaded from HBM straight into the MFMA A layout;
+//   * the value tile is transposed into LDS (V^T[d_h][32 rows]);
+//   * private scores p_h . z^K_{h,j} on the VALU: latent rows are read from HBM
+//     into registers, 8 lanes per head (each lane owns r/8 coordinates); the
+//     latents are stored token-major, so one load instruction reads one token's
+//     latents of 8 consecutive heads, 8*r*2 contiguous bytes; the 8 partial dots
+//     of 8 rows are combined by a 3-stage transpose-reduce over lanes (DPP half
+//     mirror, xor 2, xor 1) that leaves each lane with one finished score;
+//   * scores meet in the MFMA result layout (lane = one head, 8 rows) through a
+//     small LDS exchange; online softmax there (max across lanes xor 16, 32);
+//   * shared values O^T[d_h x 16] += V^T[d_h x 32] P^T[32 x 16] on MFMA, with P
+//     split into bf16 hi + lo parts (two MFMAs) so the weights keep ~16 bits;
+//   * private values acc_pr[h] += e_j z^V_{h,j} on the VALU in the latent layout,
+//     the weights read back from the LDS exchange.
+// All global loads of a block -- key fragments, value tile, latent units --
+// form one sequence of equal-sized "units" that runs through a ring of NSLOT
+// register slots, NSLOT - 1 units ahead of the arithmetic (across blocks too).
+// Loads are buffer loads: the lane-dependent part of an address is a 32-bit
+// VGPR offset fixed for the whole kernel, the block/octet part is a scalar
+// offset and the row within the block an immediate, so no vector arithmetic is
+// spent on addresses.  Rows are kept inside the allocation by construction
+// (L_cap is a multiple of 32 and blocks start on multiples of 32); rows past a
+// sequence's length inside its last block are masked (scores) or zeroed
+// (values), never used.
+//
+// Normalised variant (NORM): the key of every (head, token) is RMS-normalised
+// as a whole, and its cached reciprocal scale multiplies the summed logit
+// ("Low-Rank Key Value Attention | What a shared cache can preserve", sec. 8,
+// post-projection normalisation; the gain is already folded into q).  Each
+// lane reads the 8 scales of its scores (2 bytes each) at the top of a block;
+// they are used at the combine step, half a block of loads later.
+//
+// The template is instantiated in k_decode_mfma_part*.hip, one (d_h, NORM)
+// set per translation unit so they compile in parallel.
+#pragma once
+
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+constexpr int kRows = 32;   // rows per block
+constexpr int kWaves = 4;   // waves per workgroup
+// cache-policy bits of the streamed loads: 2 = non-temporal.  Latent rows are read exactly once;
+// shared key/value rows are re-read through L2 (split key lines, second head group).
+#ifndef LRKV_NT_LATENT
+#define LRKV_NT_LATENT 0
+#endif
+#ifndef LRKV_NT_SHARED
+#define LRKV_NT_SHARED 0
+#endif
+constexpr int kNTLat = LRKV_NT_LATENT ? 2 : 0;
+constexpr int kNTSh = LRKV_NT_SHARED ? 2 : 0;
+
+template <int D, int R, int H, int OCC>
+struct Cfg {
+    static constexpr int EPL = R / 8;                   // latent coordinates per lane
+    static constexpr int LDW = (EPL + 1) / 2;           // dwords per latent load (EPL = 1 uses one dword)
+    static constexpr int NOCT = H / 8;                  // head octets
+    static constexpr int NHG = (H + 15) / 16;           // head groups (16 heads: MFMA N)
+    static constexpr int NTL = kWaves / NHG;            // row lanes per workgroup
+    static constexpr int OCTS = (H >= 16) ? 2 : 1;      // octets per head group
+    static constexpr int KSTEPS = D / 32;               // k-steps of the score MFMA
+    static constexpr int CB = D / 16;                   // 16-column blocks of the value MFMA
+    static constexpr int LPR = D / 8;                   // lanes per shared row (16 B each)
+    static constexpr int RPI = 64 / LPR;                // shared rows per load instruction
+    static constexpr int NINS = kRows / RPI;            // load instructions per value tile
+    static constexpr int NLU = (R > 0) ? 8 * OCTS : 0;  // latent units per block (K then V)
+    static constexpr int NU = 2 + NLU;                  // + key-fragment unit + value-tile unit
+    static constexpr int KDW = 8 * KSTEPS;              // dwords of the key unit
+    static constexpr int VDW = 4 * NINS;                // dwords of the value unit
+    static constexpr int LUDW = 8 * LDW;                // dwords of a latent unit
+    static constexpr int SLOT_DW = (KDW > VDW ? (KDW > LUDW ? KDW : LUDW) : (VDW > LUDW ? VDW : LUDW));
+    // ring depth: as deep as the register budget allows.  OCC = waves per SIMD (2: 256 registers per
+    // wave, 1: 512).  The depth must divide the per-block unit count so slots repeat every block.
+    static constexpr int pick_slots() {
+        const int budget = (OCC == 1) ? 200 : 96;  // registers for the ring
+        const int cand[6] = {9, 6, 5, 4, 3, 2};
+        for (int i = 0; i < 6; ++i)
+            if (NU % cand[i] == 0 && cand[i] * SLOT_DW <= budget) return cand[i];
+        return (NU % 2 == 0) ? 2 : 1;
+    }
+    static constexpr int NSLOT = pick_slots();
+    static constexpr int QROW = D + 8;                  // bf16 per q row in LDS (16 B pad)
+    static constexpr int PROW = R + 4;                  // floats per p row in LDS
+    static constexpr int VTS = kRows + 4;               // bf16 per V^T row in LDS (72 B: conflict-free reads)
+    static constexpr int XS = 36;                       // floats per exchange row (32 rows + alpha + pad)
+    static constexpr int REC = ((D + R + 2) + 3) & ~3;
+    static constexpr int Q_BYTES = NHG * 16 * QROW * 2;
+    static constexpr int P_BYTES = ((H * PROW * 4) + 15) & ~15;
+    static constexpr int MW_BYTES = kWaves * 16 * 4;
+    static constexpr int VT_BYTES = ((D * VTS * 2) + 15) & ~15;
+    static constexpr int X_BYTES = 16 * XS * 4;
+    static constexpr int WAVE_BYTES = VT_BYTES + X_BYTES;
+    static constexpr int LDS_BYTES = Q_BYTES + P_BYTES + MW_BYTES + kWaves * WAVE_BYTES;
+    static constexpr int MERGE_BYTES = H * REC * 4;
+    static_assert(MERGE_BYTES <= kWaves * WAVE_BYTES, "merge area must fit in the per-wave tiles");
+    static_assert(NU % NSLOT == 0, "ring must divide the unit sequence");
+    static_assert(H % 8 == 0 && H <= 32, "head count");
+};
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // (a.lo16, b.lo16)
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // (a.hi16, b.hi16)
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+__device__ __forceinline__ float lat_at(const uint32_t* w, int e) {
+    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v3u_t __attribute__((ext_vector_type(3)));
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+
+// DPP lane exchanges within rows of 16 lanes (no LDS traffic)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// dot of two bf16 pairs accumulated into fp32 (v_dot2_f32_bf16); operands are plain
+// scalars, never vector subscripts, before the bit casts
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// raw buffer descriptor over [base, base + bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int D, int R, int H, int OCC, bool NORM>
+__global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs a) {
+    using C = Cfg<D, R, H, OCC>;
+    constexpr int EPL = C::EPL, LDW = C::LDW, OCTS = C::OCTS, NU = C::NU, NSLOT = C::NSLOT, SDW = C::SLOT_DW;
+    constexpr bool kDot2 = (EPL % 2 == 0) && EPL > 0;  // private score on v_dot2 (p split into bf16 hi + lo)
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    uint16_t* q_lds = (uint16_t*)lds;
+    uint32_t* p_lds = (uint32_t*)(lds + C::Q_BYTES);
+    float* mw_lds = (float*)(lds + C::Q_BYTES + C::P_BYTES);
+    unsigned char* wave_base = lds + C::Q_BYTES + C::P_BYTES + C::MW_BYTES;
+
+    // the wave index is uniform across a wave; saying so keeps every block offset in SGPRs
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hg = wave % C::NHG, tl = wave / C::NHG;  // head group, row lane
+    unsigned char* my = wave_base + wave * C::WAVE_BYTES;
+    uint16_t* vt = (uint16_t*)my;
+    float* xb = (float*)(my + C::VT_BYTES);
+
+    // Which sequence and split this workgroup handles (splits dealt to sequences by length), and
+    // which 32-row blocks its row lanes take: blocks are dealt round-robin over the (split, row lane)
+    // slots of the sequence, slot (split, tl) takes blocks split*NTL + tl + k*S_b*NTL.
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const int b = wslot.b, split = wslot.s;
+    if (b < 0) return;
+    const int Lb = clamped_len(a.seq_lens, b, a.max_len);
+    if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
+    const int nb = (Lb + kRows - 1) / kRows;  // blocks of this sequence
+
+    const uint16_t* qg = (const uint16_t*)a.q + (size_t)b * H * D;
+
+    // ---- q (zero rows pad a partial head group) and p into LDS ----
+    for (int i = tid; i < C::NHG * 16 * D; i += kWaves * 64) {
+        const int h = i / D, c = i - h * D;
+        q_lds[h * C::QROW + c] = (h < H) ? qg[h * D + c] : (uint16_t)0;
+    }
+    if constexpr (R > 0) {
+        const float* pg = a.p + (size_t)b * H * R;
+        if constexpr (kDot2) {
+            // per head and r-slice of EPL coordinates: EPL/2 pairs of high parts, then EPL/2 of low parts
+            for (int i = tid; i < H * (R / 2); i += kWaves * 64) {
+                const int h = i / (R / 2), pr = i - h * (R / 2);  // pair index within the head
+                const int slice = pr / (EPL / 2), j = pr - slice * (EPL / 2);
+                const float x0 = pg[h * R + 2 * pr], x1 = pg[h * R + 2 * pr + 1];
+                const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                const uint32_t l0 = f32_to_bf16_bits(x0 - __uint_as_float(h0 << 16));
+                const uint32_t l1 = f32_to_bf16_bits(x1 - __uint_as_float(h1 << 16));
+                uint32_t* row = p_lds + h * C::PROW + slice * EPL;
+                row[j] = h0 | (h1 << 16);
+                row[EPL / 2 + j] = l0 | (l1 << 16);
+            }
+        } else {
+            for (int i = tid; i < H * R; i += kWaves * 64) {
+                const int h = i / R, k = i - h * R;
+                p_lds[h * C::PROW + k] = __float_as_uint(pg[i]);
+            }
+        }
+    }
+    for (int i = lane; i < 16 * C::XS; i += 64) xb[i] = 0.f;
+    __syncthreads();
+
+    const int n16 = lane & 15, g4 = lane >> 4;  // MFMA layout: column (head or value column), row group
+    const int hh = lane >> 3, sl = lane & 7;    // latent layout: head within octet, coordinate slice
+    const bool sb0 = sl & 1, sb1 = (sl >> 1) & 1, sb2 = (sl >> 2) & 1;
+    const int srow = lane / C::LPR, schunk = lane % C::LPR;  // value-tile load layout
+    const float scale = kLog2e / sqrtf((float)D);
+
+    f32x4_t acc_sh[C::CB];
+    float acc_pr[OCTS][EPL > 0 ? EPL : 1];
+    float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb) acc_sh[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int o = 0; o < OCTS; ++o)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc_pr[o][e] = 0.f;
+
+    // ---- buffer descriptors of this sequence and fixed per-lane byte offsets ----
+    // latents are token-major ([L_cap][H][r] per sequence): one latent row holds every head
+    const uint32_t row_bytes_sh = D * 2, row_bytes_lat = H * R * 2;
+    const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + (size_t)b * a.L_cap * D,
+                                                 (uint32_t)a.L_cap * row_bytes_sh);
+    const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const uint16_t*)a.v_shared + (size_t)b * a.L_cap * D,
+                                                 (uint32_t)a.L_cap * row_bytes_sh);
+    __amdgpu_buffer_rsrc_t rs_zk = rs_k, rs_zv = rs_v;
+    uint32_t vo_zv = 0;  // lane offset of (head 16*hg + hh, coordinate slice sl) in the latent tensors
+    if constexpr (R > 0) {
+        const uint32_t lat_bytes = (uint32_t)H * a.L_cap * (R * 2);
+        rs_zk = buf_rsrc((const uint16_t*)a.z_k + (size_t)b * H * a.L_cap * R, lat_bytes);
+        rs_zv = buf_rsrc((const uint16_t*)a.z_v + (size_t)b * H * a.L_cap * R, lat_bytes);
+        vo_zv = (uint32_t)(16 * hg + hh) * R * 2 + sl * EPL * 2;
+    }
+    const uint32_t vo_kf = (uint32_t)n16 * row_bytes_sh + 16 * g4;              // key fragment rows n16, 16 + n16
+    const uint32_t vo_vt = (uint32_t)(4 * srow) * row_bytes_sh + 16 * schunk;  // value tile rows 4*srow + 0..3
+    const uint32_t oct_bytes = 8u * R * 2;  // next head octet within a latent row
+    // normalised variant: the cached scale of (row, head) multiplies the summed logit; this lane's scores are
+    // head 16*hg + n16 at rows 4*g4 + i and 16 + 4*g4 + i of a block (scales token-major: [L_cap][H])
+    __amdgpu_buffer_rsrc_t rs_rho = rs_k;
+    uint32_t vo_rho = 0;
+    if constexpr (NORM) {
+        rs_rho = buf_rsrc((const uint16_t*)a.rho + (size_t)b * a.L_cap * H, (uint32_t)a.L_cap * H * 2);
+        vo_rho = (uint32_t)(4 * g4 * H + 16 * hg + n16) * 2;
+    }
+
+    // ---- the load ring ----
+    uint32_t ring[NSLOT][SDW];
+
+    // unit u of the block starting at row t0 -> slot
+    auto issue = [&](int u, int t0, int slot) {
+        if (u == 0) {  // key fragments in the MFMA A layout: rows 16*half + n16, chunk 4*kk + g4
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int so = (t0 + 16 * half) * (int)row_bytes_sh;
+#pragma unroll
+                for (int kk = 0; kk < C::KSTEPS; ++kk) {
+                    const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, vo_kf + 64 * kk, so, kNTSh);
+                    const int o = 4 * (half * C::KSTEPS + kk);
+                    ring[slot][o] = v.x;
+                    ring[slot][o + 1] = v.y;
+                    ring[slot][o + 2] = v.z;
+                    ring[slot][o + 3] = v.w;
+                }
+            }
+        } else if (u == 1) {  // value tile, rows 4*srow + (ins & 3) + 4*RPI*(ins >> 2)
+#pragma unroll
+            for (int grp = 0; grp < C::NINS / 4; ++grp) {
+                const int so = (t0 + 4 * C::RPI * grp) * (int)row_bytes_sh;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int ins = 4 * grp + jj;
+                    const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(rs_v, vo_vt + jj * row_bytes_sh, so, kNTSh);
+                    ring[slot][4 * ins] = v.x;
+                    ring[slot][4 * ins + 1] = v.y;
+                    ring[slot][4 * ins + 2] = v.z;
+                    ring[slot][4 * ins + 3] = v.w;
+                }
+            }
+        } else if constexpr (R > 0) {  // latent unit: phase (K, V), octet, 8-row sub-block
+            const int v = u - 2;
+            const int phase = v / (4 * OCTS);
+            const int oi = (v % (4 * OCTS)) / 4, sub = v % 4;
+            const int so = t0 * (int)row_bytes_lat + oi * (int)oct_bytes;
+            const __amdgpu_buffer_rsrc_t rs = (phase == 0) ? rs_zk : rs_zv;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                // one instruction reads row 8*sub + k of 8 consecutive heads: 8*r*2 contiguous bytes
+                const uint32_t vo = vo_zv + (k + 8 * sub) * row_bytes_lat;
+                if constexpr (EPL == 8) {
+                    const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat);
+                    ring[slot][4 * k] = w.x;
+                    ring[slot][4 * k + 1] = w.y;
+                    ring[slot][4 * k + 2] = w.z;
+                    ring[slot][4 * k + 3] = w.w;
+                } else if constexpr (EPL == 6) {
+                    const v3u_t w = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, kNTLat);
+                    ring[slot][3 * k] = w.x;
+                    ring[slot][3 * k + 1] = w.y;
+                    ring[slot][3 * k + 2] = w.z;
+                } else if constexpr (EPL == 4) {
+                    const v2u_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNTLat);
+                    ring[slot][2 * k] = w.x;
+                    ring[slot][2 * k + 1] = w.y;
+                } else if constexpr (EPL == 2) {
+                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, kNTLat);
+                } else {  // EPL == 1
+                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, kNTLat);
+                }
+            }
+        }
+    };
+
+    const int first_blk = split * C::NTL + tl, step_blk = wslot.S_b * C::NTL, last_blk = nb;
+    const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
+    // Sequence b walks its blocks starting b/batch of the way along (the same blocks, rotated order).
+    // Otherwise every sequence reads the same relative position of its cache region at the same time,
+    // and with some region strides those concurrent streams crowd the same HBM channels.
+    const int rot = (int)(((long)nmine * b) / a.batch);
+    if (nmine > 0) {
+#pragma unroll
+        for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * (first_blk + rot * step_blk), u);
+    }
+
+    for (int it = 0; it < nmine; ++it) {
+        int itr = it + rot;
+        if (itr >= nmine) itr -= nmine;
+        const int blk = first_blk + itr * step_blk;
+        const int t0 = kRows * blk;
+        const int nvalid = min(kRows, Lb - t0);
+        // next block of this row lane; on the last block the prefetch re-reads this block (always in bounds)
+        const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
+        const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
+        f32x4_t s_sh[2];
+        float ev[8];
+        uint32_t rho_w[8];  // scales of this lane's 8 scores (bf16 bits), read at the top of the block
+        if constexpr (NORM) {
+            const int so = t0 * H * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                rho_w[i] = __builtin_amdgcn_raw_buffer_load_b16(rs_rho, vo_rho + i * H * 2, so, 0);
+                rho_w[4 + i] = __builtin_amdgcn_raw_buffer_load_b16(rs_rho, vo_rho + (16 + i) * H * 2, so, 0);
+            }
+        }
+
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            // keep NSLOT - 1 units in flight ahead of this one
+            {
+                const int un = u + NSLOT - 1;
+                if (un < NU) issue(un, t0, un % NSLOT);
+                else issue(un - NU, t0_pf, un % NSLOT);
+            }
+            // fence the scheduler at unit boundaries: loads stay NSLOT - 1 units ahead, no further
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t* cur = ring[u % NSLOT];
+            if (u == 0) {
+                // shared scores on MFMA (both 16-row halves)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+                        const int o = 4 * (half * C::KSTEPS + kk);
+                        const u32x4_t av = {cur[o], cur[o + 1], cur[o + 2], cur[o + 3]};
+                        const u32x4_t bv =
+                            *(const u32x4_t*)(q_lds + (16 * hg + n16) * C::QROW + 32 * kk + 8 * g4);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                     __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+                    }
+                    s_sh[half] = acc;
+                }
+            } else if (u == 1) {
+                // value tile -> V^T in LDS: vt[c][row], 4 consecutive rows per 8-byte store;
+                // rows past the sequence end are zeroed (their weight is 0, their content arbitrary)
+#pragma unroll
+                for (int grp = 0; grp < C::NINS / 4; ++grp) {
+                    const int t4 = 4 * srow + 4 * C::RPI * grp;
+                    const bool ok0 = t4 < nvalid, ok1 = t4 + 1 < nvalid, ok2 = t4 + 2 < nvalid, ok3 = t4 + 3 < nvalid;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int c = 8 * schunk + j;
+                        const uint32_t w0 = ok0 ? cur[4 * (4 * grp + 0) + (j >> 1)] : 0u;
+                        const uint32_t w1 = ok1 ? cur[4 * (4 * grp + 1) + (j >> 1)] : 0u;
+                        const uint32_t w2 = ok2 ? cur[4 * (4 * grp + 2) + (j >> 1)] : 0u;
+                        const uint32_t w3 = ok3 ? cur[4 * (4 * grp + 3) + (j >> 1)] : 0u;
+                        u32x2_t pk;
+                        pk[0] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
+                        pk[1] = (j & 1) ? pack_hi(w2, w3) : pack_lo(w2, w3);
+                        *(u32x2_t*)(vt + c * C::VTS + t4) = pk;
+                    }
+                }
+                if constexpr (R == 0) {
+                    // no private branch: zero private scores
+#pragma unroll
+                    for (int oi = 0; oi < OCTS; ++oi)
+#pragma unroll
+                        for (int sub = 0; sub < 4; ++sub) xb[(8 * oi + hh) * C::XS + 8 * sub + sl] = 0.f;
+                }
+            } else if constexpr (R > 0) {
+                const int v = u - 2;
+                const int phase = v / (4 * OCTS);
+                const int oi = (v % (4 * OCTS)) / 4, sub = v % 4;
+                if (phase == 0) {
+                    uint32_t pw[EPL];
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) pw[e] = p_lds[(16 * hg + 8 * oi + hh) * C::PROW + sl * EPL + e];
+                    float part[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        float acc = 0.f;
+                        if constexpr (kDot2) {
+#pragma unroll
+                            for (int pr = 0; pr < EPL / 2; ++pr) {
+                                const uint32_t z = cur[LDW * k + pr];
+                                acc = dot2_bf16(z, pw[EPL / 2 + pr], acc);  // low parts of p
+                                acc = dot2_bf16(z, pw[pr], acc);            // high parts of p
+                            }
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e) acc = fmaf(__uint_as_float(pw[e]), lat_at(cur + LDW * k, e), acc);
+                        }
+                        part[k] = acc;
+                    }
+                    // transpose-reduce across the 8 lanes of a head: part[k] is this lane's slice of
+                    // row k.  Stage 1 pairs lanes sl, 7-sl (half mirror) and each keeps the rows whose
+                    // bit 2 equals its own; stages 2 and 3 do the same on bits 1 and 0 with lanes
+                    // sl^2 and sl^1.  Lane sl ends with the whole score of row 8*sub + sl.
+                    float q4[4], q2[2];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float keep = sb2 ? part[k + 4] : part[k];
+                        const float send = sb2 ? part[k] : part[k + 4];
+                        q4[k] = keep + dpp<kDppHalfMirror>(send);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const float keep = sb1 ? q4[k + 2] : q4[k];
+                        const float send = sb1 ? q4[k] : q4[k + 2];
+                        q2[k] = keep + dpp<kDppXor2>(send);
+                    }
+                    const float keep = sb0 ? q2[1] : q2[0];
+                    const float send = sb0 ? q2[0] : q2[1];
+                    xb[(8 * oi + hh) * C::XS + 8 * sub + sl] = keep + dpp<kDppXor1>(send);
+                } else {
+                    if (sub == 0) {
+                        const float al = xb[(8 * oi + hh) * C::XS + 32];
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc_pr[oi][e] *= al;
+                    }
+                    const f32x4_t e0 = *(const f32x4_t*)(xb + (8 * oi + hh) * C::XS + 8 * sub);
+                    const f32x4_t e1 = *(const f32x4_t*)(xb + (8 * oi + hh) * C::XS + 8 * sub + 4);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        if (8 * sub + k < nvalid) {  // rows past the end: weight 0, content arbitrary
+                            const float w = (k < 4) ? e0[k] : e1[k - 4];
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e)
+                                acc_pr[oi][e] = fmaf(w, lat_at(cur + LDW * k, e), acc_pr[oi][e]);
+                        }
+                    }
+                }
+            }
+
+            // after the last key unit: combine, online softmax, shared values
+            if (u == 1 + C::NLU / 2) {
+                wave_lds_sync();
+                float sc[8];
+                const f32x4_t pa = *(const f32x4_t*)(xb + n16 * C::XS + 4 * g4);
+                const f32x4_t pb = *(const f32x4_t*)(xb + n16 * C::XS + 16 + 4 * g4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r0 = 4 * g4 + i, r1 = 16 + 4 * g4 + i;
+                    float f0 = scale, f1 = scale;
+                    if constexpr (NORM) {
+                        f0 = scale * __uint_as_float(rho_w[i] << 16);
+                        f1 = scale * __uint_as_float(rho_w[4 + i] << 16);
+                    }
+                    sc[i] = (r0 < nvalid) ? (s_sh[0][i] + pa[i]) * f0 : -INFINITY;
+                    sc[4 + i] = (r1 < nvalid) ? (s_sh[1][i] + pb[i]) * f1 : -INFINITY;
+                }
+                float tmax = sc[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                const float m_new = fmaxf(m_run, tmax);
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                float esum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ev[i] = fast_exp2(sc[i] - m_new);
+                    esum += ev[i];
+                }
+                l_run = fmaf(alpha, l_run, esum);
+                wave_lds_sync();  // every lane has read its private scores
+                *(f32x4_t*)(xb + n16 * C::XS + 4 * g4) = f32x4_t{ev[0], ev[1], ev[2], ev[3]};
+                *(f32x4_t*)(xb + n16 * C::XS + 16 + 4 * g4) = f32x4_t{ev[4], ev[5], ev[6], ev[7]};
+                if (g4 == 0) xb[n16 * C::XS + 32] = alpha;
+                wave_lds_sync();
+
+                // shared values on MFMA: O^T += V^T P^T with P = hi + lo (bf16)
+                u32x4_t phi, plo;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t h0 = f32_to_bf16_bits(ev[2 * i]), h1 = f32_to_bf16_bits(ev[2 * i + 1]);
+                    const float r0 = ev[2 * i] - __uint_as_float(h0 << 16);
+                    const float r1 = ev[2 * i + 1] - __uint_as_float(h1 << 16);
+                    phi[i] = h0 | (h1 << 16);
+                    plo[i] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+                }
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb) {
+                    acc_sh[cb] *= alpha;
+                    const int c = 16 * cb + n16;
+                    const u32x2_t v0 = *(const u32x2_t*)(vt + c * C::VTS + 4 * g4);
+                    const u32x2_t v1 = *(const u32x2_t*)(vt + c * C::VTS + 16 + 4 * g4);
+                    const uint32_t a0 = v0[0], a1 = v0[1], a2 = v1[0], a3 = v1[1];
+                    const u32x4_t av = {a0, a1, a2, a3};
+                    acc_sh[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, phi), acc_sh[cb], 0, 0, 0);
+                    acc_sh[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, plo), acc_sh[cb], 0, 0, 0);
+                }
+            }
+        }
+        wave_lds_sync();  // V^T and weights consumed before the next block rewrites them
+    }
+
+    // ---- merge the row lanes of each head group (fixed order), one record per head ----
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (g4 == 0) mw_lds[wave * 16 + n16] = m_run;
+    __syncthreads();  // all waves done with their tiles; running maxima visible
+    float* mg = (float*)wave_base;  // [H][REC], aliases the per-wave areas
+    float M = -INFINITY;
+    for (int t = 0; t < C::NTL; ++t) M = fmaxf(M, mw_lds[(t * C::NHG + hg) * 16 + n16]);
+    const float fsh = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+    float fpr[OCTS];
+#pragma unroll
+    for (int oi = 0; oi < OCTS; ++oi) {
+        const int n = 8 * oi + hh;
+        float Mo = -INFINITY;
+        for (int t = 0; t < C::NTL; ++t) Mo = fmaxf(Mo, mw_lds[(t * C::NHG + hg) * 16 + n]);
+        const float mine = mw_lds[wave * 16 + n];
+        fpr[oi] = (mine == -INFINITY) ? 0.f : fast_exp2(mine - Mo);
+    }
+    const int head = 16 * hg + n16;
+    for (int t = 0; t < C::NTL; ++t) {
+        if (tl == t && head < H) {
+            float* row = mg + head * C::REC;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) {
+                const f32x4_t v = acc_sh[cb] * fsh;
+                f32x4_t* dst = (f32x4_t*)(row + 16 * cb + 4 * g4);
+                *dst = (t == 0) ? v : (*dst + v);
+            }
+            if (g4 == 0) {
+                const float lv = l_run * fsh;
+                row[D + R + 1] = (t == 0) ? lv : row[D + R + 1] + lv;
+                if (t == 0) row[D + R] = M;
+            }
+        }
+        if (tl == t) {
+#pragma unroll
+            for (int oi = 0; oi < OCTS; ++oi) {
+                float* row = mg + (16 * hg + 8 * oi + hh) * C::REC + D + sl * EPL;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const float v = acc_pr[oi][e] * fpr[oi];
+                    row[e] = (t == 0) ? v : row[e] + v;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* out = a.ws + (size_t)blockIdx.x * H * C::REC;  // record of workgroup w = W_b + split
+    for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
+}
+
+template <int D, int R, int H, int OCC, bool NORM>
+hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
+    using C = Cfg<D, R, H, OCC>;
+    auto kern = split_mfma_kernel<D, R, H, OCC, NORM>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
+// the normalised variant is built for one wave per SIMD only
+template <int D, int R, int H, bool NORM>
+hipError_t launch_dhr(const DecodeArgs& a, int occ, hipStream_t stream) {
+    if constexpr (NORM) return launch_one<D, R, H, 1, true>(a, stream);
+    else return occ == 1 ? launch_one<D, R, H, 1, false>(a, stream) : launch_one<D, R, H, 2, false>(a, stream);
+}
+
+template <int D, int H, bool NORM>
+hipError_t launch_r(const DecodeArgs& a, int occ, hipStream_t stream) {
+    switch (a.r) {
+        case 0: return launch_dhr<D, 0, H, NORM>(a, occ, stream);
+        case 8: return launch_dhr<D, 8, H, NORM>(a, occ, stream);
+        case 16: return launch_dhr<D, 16, H, NORM>(a, occ, stream);
+        case 32: return launch_dhr<D, 32, H, NORM>(a, occ, stream);
+        case 48: return launch_dhr<D, 48, H, NORM>(a, occ, stream);
+        case 64: return launch_dhr<D, 64, H, NORM>(a, occ, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D, bool NORM>
+hipError_t launch_h(const DecodeArgs& a, int occ, hipStream_t stream) {
+    switch (a.H) {
+        case 8: return launch_r<D, 8, NORM>(a, occ, stream);
+        case 16: return launch_r<D, 16, NORM>(a, occ, stream);
+        case 32: return launch_r<D, 32, NORM>(a, occ, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace lrkv

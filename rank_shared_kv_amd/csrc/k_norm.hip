@@ -1,0 +1,176 @@
+// Kernels of the normalised variant ("Low-Rank Key Value Attention | What a
+// shared cache can preserve", sec. 8, post-projection normalisation and its
+// cache cost; "Low-Rank Key Value Attention: Chinese reading notes", sec. 2.7,
+// last paragraph).  The key of head h at token j is the summed key
+//   k_{h,j} = k_s[j] + z^K_{h,j} (B^K_h)^T,
+// RMS-normalised as a whole; what the cache keeps besides the factors is its
+// reciprocal RMS, one scalar per (token, head):
+//   rho_{h,j} = 1 / sqrt(|k_{h,j}|^2 / d_h + eps)         [batch][L_cap][H], cache dtype
+// The per-head key gain moves to the query side, so the decode only multiplies
+// the summed logit of (h, j) by rho_{h,j}:
+//   q_eff_h = g^K_h * g^Q_h * q_h / sqrt(|q_h|^2 / d_h + eps)
+//
+// key_scales_mfma_kernel: bf16, d_h a multiple of 16, r a multiple of 8 up to
+// 64.  A wave owns 16 rows of one head and rebuilds their keys 16 columns at a
+// time on v_mfma_f32_16x16x32_bf16 (Out^T = B_h Z^T, as the materialise
+// kernel does), adds the shared row and accumulates squares; the four lanes
+// that hold one row's columns then sum in a fixed order.  The keys themselves
+// are never written.  Other shapes: one thread per (row, head).
+#include <algorithm>
+
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;  // 64 rows of one head per workgroup
+
+__device__ __forceinline__ float rms_scale(float sum_sq, int D, float eps) { return 1.f / sqrtf(sum_sq / (float)D + eps); }
+
+// rows max(0, L_b - n_last) .. L_b - 1 of sequence b; NKS k-steps of 32 rank coordinates, a compile-time
+// count so the matrix-core results are read after their wait states (see materialize_mfma_kernel)
+template <int NKS>
+__global__ void __launch_bounds__(kWaves * 64) key_scales_mfma_kernel(int H, int D, int R, int L_cap, int max_len,
+                                                                      int n_last, float eps,
+                                                                      const int32_t* __restrict__ seq_lens,
+                                                                      const uint16_t* __restrict__ shared,
+                                                                      const uint16_t* __restrict__ z,
+                                                                      const uint16_t* __restrict__ basis,
+                                                                      uint16_t* __restrict__ rho) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int Lb = clamped_len(seq_lens, b, max_len);
+    const int start = max(0, Lb - n_last);
+    const int t0 = start + (blockIdx.x * kWaves + wave) * 16;
+    if (t0 >= Lb) return;
+    const int row = t0 + n16;                       // this lane's row (B operand column, result column)
+    const int row_c = min(row, Lb - 1);             // rows past the end re-read the last live row
+    const uint16_t* zrow = z + (((size_t)b * L_cap + row_c) * H + h) * R;  // token-major latents
+    const uint16_t* srow = shared + ((size_t)b * L_cap + row_c) * D;
+    const uint16_t* bh = basis + (size_t)h * D * R;
+    float ss = 0.f;
+    for (int cb = 0; cb < D / 16; ++cb) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k = 32 * ks + 8 * g4;
+            const bool in = k < R;                   // R is a multiple of 8: whole 8-coordinate groups
+            const int kc = in ? k : 0;
+            u32x4_t zv = *(const u32x4_t*)(zrow + kc);
+            u32x4_t bv = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + kc);
+            if (!in) zv = bv = u32x4_t{0u, 0u, 0u, 0u};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bv),
+                                                          __builtin_bit_cast(bf16x8_t, zv), acc, 0, 0, 0);
+        }
+        mfma_result_fence();
+        // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row's key
+        const u32x2_t s = *(const u32x2_t*)(srow + 16 * cb + 4 * g4);
+        const float v0 = acc[0] + bf16_lo(s[0]), v1 = acc[1] + bf16_hi(s[0]);
+        const float v2 = acc[2] + bf16_lo(s[1]), v3 = acc[3] + bf16_hi(s[1]);
+        ss = fmaf(v0, v0, ss);
+        ss = fmaf(v1, v1, ss);
+        ss = fmaf(v2, v2, ss);
+        ss = fmaf(v3, v3, ss);
+    }
+    ss += __shfl_xor(ss, 16);  // the four column groups of a row: (g4 0 + 1) + (2 + 3)
+    ss += __shfl_xor(ss, 32);
+    if (g4 == 0 && row < Lb) rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) key_scales_simple_kernel(int batch, int H, int D, int R, int L_cap, int max_len,
+                                                                int n_last, int n_rows, float eps,
+                                                                const int32_t* __restrict__ seq_lens,
+                                                                const T* __restrict__ shared, const T* __restrict__ z,
+                                                                const T* __restrict__ basis, T* __restrict__ rho) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)batch * n_rows * H) return;
+    const int h = (int)(idx % H);
+    const int k = (int)((idx / H) % n_rows);
+    const int b = (int)(idx / ((size_t)H * n_rows));
+    const int Lb = clamped_len(seq_lens, b, max_len);
+    const int row = max(0, Lb - n_last) + k;
+    if (row >= Lb) return;
+    const size_t zr = (((size_t)b * L_cap + row) * H + h) * R;
+    float ss = 0.f;
+    for (int c = 0; c < D; ++c) {
+        float v = elem<T>::load(shared, ((size_t)b * L_cap + row) * D + c);
+        for (int i = 0; i < R; ++i) v = fmaf(elem<T>::load(z, zr + i), elem<T>::load(basis, ((size_t)h * D + c) * R + i), v);
+        ss = fmaf(v, v, ss);
+    }
+    const float s = rms_scale(ss, D, eps);
+    const size_t o = ((size_t)b * L_cap + row) * H + h;
+    if constexpr (sizeof(T) == 4) rho[o] = s;
+    else rho[o] = (T)f32_to_bf16_bits(s);
+}
+
+// one wave per (b, h): q_eff = g_k * ((g_q * q) * inv_rms(q)), rounded once to the storage dtype
+template <typename T>
+__global__ void __launch_bounds__(64) norm_query_kernel(int H, int D, float eps, const T* __restrict__ q,
+                                                        const T* __restrict__ g_q, const T* __restrict__ g_k,
+                                                        T* __restrict__ q_eff) {
+    const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+    const size_t row = ((size_t)b * H + h) * D;
+    float ss = 0.f;
+    for (int c = lane; c < D; c += 64) {
+        const float x = elem<T>::load(q, row + c);
+        ss = fmaf(x, x, ss);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float inv = rms_scale(ss, D, eps);
+    for (int c = lane; c < D; c += 64) {
+        const float x = elem<T>::load(q, row + c);
+        const float v = elem<T>::load(g_k, (size_t)h * D + c) * ((elem<T>::load(g_q, (size_t)h * D + c) * x) * inv);
+        if constexpr (sizeof(T) == 4) q_eff[row + c] = v;
+        else q_eff[row + c] = (T)f32_to_bf16_bits(v);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, int n_last,
+                             float eps, const int32_t* seq_lens, const void* k_shared, const void* z_k,
+                             const void* B_k, void* rho, hipStream_t stream) {
+    const int n_rows = std::min(n_last, max_len);
+    if (n_rows <= 0) return hipSuccess;
+    if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
+        dim3 grid((n_rows + 16 * kWaves - 1) / (16 * kWaves), H, batch);
+        auto kern = (r <= 32) ? key_scales_mfma_kernel<1> : key_scales_mfma_kernel<2>;
+        hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, d_h, r, L_cap, max_len, n_last, eps, seq_lens,
+                           (const uint16_t*)k_shared, (const uint16_t*)z_k, (const uint16_t*)B_k, (uint16_t*)rho);
+    } else {
+        const size_t total = (size_t)batch * n_rows * H;
+        dim3 grid((unsigned)((total + 255) / 256));
+        if (dtype == 0)
+            hipLaunchKernelGGL(key_scales_simple_kernel<float>, grid, dim3(256), 0, stream, batch, H, d_h, r, L_cap,
+                               max_len, n_last, n_rows, eps, seq_lens, (const float*)k_shared, (const float*)z_k,
+                               (const float*)B_k, (float*)rho);
+        else
+            hipLaunchKernelGGL(key_scales_simple_kernel<uint16_t>, grid, dim3(256), 0, stream, batch, H, d_h, r, L_cap,
+                               max_len, n_last, n_rows, eps, seq_lens, (const uint16_t*)k_shared,
+                               (const uint16_t*)z_k, (const uint16_t*)B_k, (uint16_t*)rho);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_query(int batch, int H, int d_h, int dtype, float eps, const void* q, const void* g_q,
+                             const void* g_k, void* q_eff, hipStream_t stream) {
+    dim3 grid(H, batch);
+    if (dtype == 0)
+        hipLaunchKernelGGL(norm_query_kernel<float>, grid, dim3(64), 0, stream, H, d_h, eps, (const float*)q,
+                           (const float*)g_q, (const float*)g_k, (float*)q_eff);
+    else
+        hipLaunchKernelGGL(norm_query_kernel<uint16_t>, grid, dim3(64), 0, stream, H, d_h, eps, (const uint16_t*)q,
+                           (const uint16_t*)g_q, (const uint16_t*)g_k, (uint16_t*)q_eff);
+    return hipGetLastError();
+}
+
+}  // namespace lrkv

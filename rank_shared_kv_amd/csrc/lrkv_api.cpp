@@ -87,10 +87,33 @@ int env_int(const char* name, int dflt) {
 constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
 // n_queries: query tokens per sequence (1 for single-token decode); they act as H * n_queries virtual heads.
-bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_queries = 1) {
+// normed: the normalised variant (scaled logits).  Its bf16 matrix-core kernel is built for one wave per SIMD
+// and the fp32 one has no such variant (the general kernel serves it); its G never exceeds the plain plan's,
+// so the plain workspace size serves both.
+bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_queries = 1, bool normed = false) {
     using namespace lrkv;
     SplitPlan p{};
     p.n_queries = n_queries;
+    if (normed) {
+        SplitPlan plain;
+        if (n_queries != 1 || !plan_split(d, max_len, &plain)) return false;
+        if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+            p.path = SplitPath::kMfmaBf16;
+            p.chunk = mfma_rows_per_tile(d.H);
+        } else if (general_path_supports(d.H, d.d_h, d.r)) {
+            p.path = SplitPath::kGeneral;
+            p.chunk = general_rows_per_tile();
+        } else {
+            return false;
+        }
+        p.occupancy = 1;
+        const long tiles_per_seq = max_len > 0 ? (max_len + p.chunk - 1) / p.chunk : 0;
+        long G = std::min<long>(plain.num_splits, p.path == SplitPath::kGeneral ? 1024 : 256);
+        G = std::min<long>(G, (long)d.batch * tiles_per_seq);
+        p.num_splits = max_len > 0 ? (int)std::max<long>(G, d.batch) : 0;
+        *out = p;
+        return true;
+    }
     if (n_queries == 1 && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
         p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
@@ -131,12 +154,13 @@ size_t workspace_bytes(const lrkv_dims& d, const lrkv::SplitPlan& p) {
            (size_t)lrkv::partial_record_floats(d.d_h, d.r);
 }
 
-lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan, int n_queries = 1) {
+lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan, int n_queries = 1,
+                                bool normed = false) {
     LRKV_TRY(check_dims(dims));
     if (max_len < 0 || max_len > dims->L_cap)
         return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
     if (n_queries < 1 || n_queries > 64) return fail(LRKV_ERR_INVALID_ARG, "n_queries=%d outside [1, 64]", n_queries);
-    if (!plan_split(*dims, max_len, plan, n_queries))
+    if (!plan_split(*dims, max_len, plan, n_queries, normed))
         return fail(LRKV_ERR_UNSUPPORTED, "no kernel for H=%d d_h=%d r=%d dtype=%d", dims->H, dims->d_h, dims->r,
                     dims->dtype);
     return LRKV_OK;
@@ -152,7 +176,7 @@ lrkv_status check_workspace(const lrkv_dims& d, const lrkv::SplitPlan& p, const 
 }
 
 lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, const void* q, const float* p,
-                        void* ws, const lrkv::SplitPlan& plan, hipStream_t stream) {
+                        void* ws, const lrkv::SplitPlan& plan, hipStream_t stream, const void* rho = nullptr) {
     using namespace lrkv;
     if (plan.num_splits == 0) return LRKV_OK;
     DecodeArgs a{};
@@ -173,6 +197,7 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.seq_lens = c.seq_lens;
     a.q = q;
     a.p = p;
+    a.rho = rho;
     a.ws = (float*)ws;
     hipError_t e = (plan.path == SplitPath::kMfmaBf16)  ? launch_split_mfma(a, plan.occupancy, stream)
                    : (plan.path == SplitPath::kMfmaF32) ? launch_split_mfma_f32(a, plan.occupancy, stream)
@@ -338,6 +363,64 @@ lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lr
     hipError_t e = lrkv::launch_merge(dims->batch, dims->H, n_queries, dims->d_h, dims->r, dims->dtype, max_len,
                                       plan.chunk, plan.num_splits, cache->seq_lens, B_v, out,
                                       (const float*)workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_key_scales(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, int32_t n_last,
+                            const void* B_k, float eps, void* rho, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (max_len < 0 || max_len > dims->L_cap)
+        return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
+    if (n_last < 0) return fail(LRKV_ERR_INVALID_ARG, "n_last=%d is negative", n_last);
+    if (!(eps >= 0.f) || eps > 3.0e38f) return fail(LRKV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!cache) return fail(LRKV_ERR_INVALID_ARG, "cache is NULL");
+    LRKV_TRY(need_ptr(cache->k_shared, "cache.k_shared"));
+    LRKV_TRY(need_ptr(cache->seq_lens, "cache.seq_lens"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(cache->z_k, "cache.z_k"));
+        LRKV_TRY(need_ptr(B_k, "B_k"));
+    }
+    LRKV_TRY(need_ptr(rho, "rho"));
+    hipError_t e = lrkv::launch_key_scales(dims->batch, dims->H, dims->d_h, dims->r, dims->L_cap, dims->dtype, max_len,
+                                           n_last, eps, cache->seq_lens, cache->k_shared, cache->z_k, B_k, rho,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "key scale kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_norm_query(const lrkv_dims* dims, const void* q, const void* g_q, const void* g_k, float eps,
+                            void* q_eff, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (!(eps >= 0.f) || eps > 3.0e38f) return fail(LRKV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(g_q, "g_q"));
+    LRKV_TRY(need_ptr(g_k, "g_k"));
+    LRKV_TRY(need_ptr(q_eff, "q_eff"));
+    hipError_t e = lrkv::launch_norm_query(dims->batch, dims->H, dims->d_h, dims->dtype, eps, q, g_q, g_k, q_eff,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "query normalisation kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, const void* rho, int32_t max_len,
+                               const void* q_eff, const float* p, const void* B_v, float* out, void* workspace,
+                               size_t workspace_bytes_, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, 1, true));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(rho, "rho"));
+    LRKV_TRY(need_ptr(q_eff, "q_eff"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(p, "p"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    LRKV_TRY(run_partial(*dims, *cache, max_len, q_eff, p, workspace, plan, (hipStream_t)stream, rho));
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                                      plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
+                                      (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ok();
 }

@@ -22,6 +22,7 @@ struct DecodeArgs {
     const int32_t* seq_lens;
     const void* q;
     const float* p;
+    const void* rho;     // normalised variant: scales [batch][L_cap][H] (cache dtype) multiplying the logits; else NULL
     float* ws;           // [G][H * Q][record]
 };
 
@@ -64,6 +65,11 @@ hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int d
                               const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
                               const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
                               hipStream_t stream);
+hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, int n_last,
+                             float eps, const int32_t* seq_lens, const void* k_shared, const void* z_k,
+                             const void* B_k, void* rho, hipStream_t stream);
+hipError_t launch_norm_query(int batch, int H, int d_h, int dtype, float eps, const void* q, const void* g_q,
+                             const void* g_k, void* q_eff, hipStream_t stream);
 hipError_t launch_output_project(int batch, int H, int d_h, int dtype, int d_model, const float* o, const void* W_o,
                                  float* y, hipStream_t stream);
 

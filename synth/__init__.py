@@ -104,6 +104,19 @@ def uniform_int(seed: int, lo: int, hi: int, n: int, offset: int = 0) -> np.ndar
     return out
 
 
+def gain(seed: int, shape, dtype: str, spread: float = 0.25) -> np.ndarray:
+    """Per-coordinate gains 1 + spread*N(0,1) (normalisation weights), stored in dtype: fp64 -> fp32 round to
+    nearest even -> (bf16) round to nearest even, as the other generated tensors."""
+    n = int(np.prod(shape))
+    f = (1.0 + normal(seed, spread, n, "f64")).astype(np.float32)
+    if dtype == "f64":
+        return f.astype(np.float64).reshape(shape)
+    if dtype == "f32":
+        return f.reshape(shape)
+    u = f.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16).reshape(shape)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to float32."""
     return (bits.astype(np.uint32) << 16).view(np.float32)
