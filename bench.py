@@ -130,6 +130,10 @@ def main():
     ap.add_argument("--norm", action="store_true",
                     help="normalised variant: each step appends a row, computes its key scales, normalises the "
                          "query (gain folded in), absorbs it and runs lrkv_decode_normed")
+    ap.add_argument("--paged", type=int, default=0, metavar="PAGE_ROWS",
+                    help="paged cache: the rows in PAGE_ROWS-row pages of a shuffled pool (power of two >= 32; the "
+                         "capacity is rounded up to whole pages); each step appends through the block table and "
+                         "runs lrkv_decode_paged")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -148,8 +152,8 @@ def main():
               f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
         sys.exit(2)
 
-    if sum([args.queries > 1, args.layer, args.norm]) > 1:
-        print("bench.py: --queries, --layer and --norm do not combine", file=sys.stderr)
+    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0]) > 1:
+        print("bench.py: --queries, --layer, --norm and --paged do not combine", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -163,6 +167,8 @@ def main():
     K, W, Q = args.steps, args.warmup, max(1, args.queries)
     lens_full = synth.seq_lengths(w)
     L_cap, max_len = launch_config(w, K * Q, args.capacity)
+    if args.paged:
+        L_cap = (L_cap + args.paged - 1) // args.paged * args.paged
     start_lens = lens_full - Q - W * Q
     assert int(start_lens.min()) >= 0
     log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
@@ -199,6 +205,20 @@ def main():
         g_q = sdev.to_device(synth.gain(8804, (w.H, w.d_h), w.dtype))
         g_k = sdev.to_device(synth.gain(8805, (w.H, w.d_h), w.dtype))
         q_eff = torch.empty_like(dev["q"])
+    if args.paged:  # the same rows in a shuffled pool of pages (pages past each sequence's need are spare)
+        P = args.paged
+        maxp = L_cap // P
+        n_pages = w.batch * maxp
+        perm = torch.from_numpy(np.random.default_rng(12345).permutation(n_pages).astype(np.int32))
+        table = perm.reshape(w.batch, maxp).cuda()
+        pools = {}
+        for name in ("k_shared", "v_shared") + (("z_k", "z_v") if w.r else ()):
+            src = dev[name]
+            pool = torch.empty((n_pages, P) + tuple(src.shape[2:]), dtype=src.dtype, device="cuda")
+            pool[table.reshape(-1).long()] = src.reshape((w.batch * maxp, P) + tuple(src.shape[2:]))
+            pools[name] = pool
+        pcache = lk.make_paged_cache(pools["k_shared"], pools["v_shared"], pools.get("z_k"), pools.get("z_v"), table,
+                                     dev["seq_lens"], P, maxp, n_pages)
     stream = torch.cuda.current_stream()
     pp = p if w.r else None
     bv = dev["B_v"] if w.r else None
@@ -247,9 +267,21 @@ def main():
         if timed:
             ev_pairs.append((e0, ev()))
 
+    def step_paged(timed: bool):
+        lk.lrkv_paged_append(dims, pcache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+        if w.r:
+            lk.lrkv_absorb_query(dims, dev["q"], dev["B_k"], p, stream)
+        if timed:
+            e0 = ev()
+        lk.lrkv_decode_paged(dims, pcache, max_len, dev["q"], pp, bv, out, ws, nbytes, stream)
+        if timed:
+            ev_pairs.append((e0, ev()))
+
     def step(timed: bool):
         if Q > 1:
             return step_multi(timed)
+        if args.paged:
+            return step_paged(timed)
         if args.norm:
             return step_norm(timed)
         if args.layer:
@@ -308,14 +340,16 @@ def main():
         rho_bytes = [sum(int(x) for x in (lens_full + k)) * w.H * s_bytes for k in range(K)]
         split_bytes += sum(rho_bytes) / K
         step_bytes += sum(rho_bytes) / K
-    if Q > 1 or args.norm:  # the timed call is the whole decode: split pass, merge and epilogue
+    if args.paged:  # the block table entries of the live pages
+        split_bytes += w.batch * ((int(lens_full.max()) + K + args.paged - 1) // args.paged) * 4
+    if Q > 1 or args.norm or args.paged:  # the timed call is the whole decode: split pass, merge and epilogue
         split_bytes += out_bytes + w.H * w.d_h * w.r * s_bytes
     split_avg_ms = sum(split_ms) / len(split_ms)
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = read_traffic(w.name, split_bytes) if not (args.layer or args.norm) and Q == 1 else None
+    traffic = read_traffic(w.name, split_bytes) if not (args.layer or args.norm or args.paged) and Q == 1 else None
     layer = None
     if args.layer:
         assert bool(torch.isfinite(y_step).all())
@@ -333,7 +367,7 @@ def main():
         log(f"bench: layer step: project+append {proj_us:.1f} us ({layer['project_weight_gbps']:.0f} GB/s of "
             f"weights), output projection {outp_us:.1f} us ({layer['output_weight_gbps']:.0f} GB/s)")
     log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); "
-        f"{'split pass' if Q == 1 and not args.norm else 'whole decode call'} {split_avg_ms * 1e3:.1f} us "
+        f"{'split pass' if Q == 1 and not (args.norm or args.paged) else 'whole decode call'} {split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
     cpu = None
@@ -355,7 +389,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else "") + ("+normalised" if args.norm else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+        "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else "") + ("+normalised" if args.norm else "")
+                   + (f"+paged{args.paged}" if args.paged else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
                    "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q},
@@ -364,7 +399,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": split_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "kernel": "lrkv_decode_multi (split pass + merge)" if Q > 1 else
-                     "lrkv_decode_normed (split pass + merge)" if args.norm else "split pass (lrkv_decode_partial)",
+                     "lrkv_decode_normed (split pass + merge)" if args.norm else
+                     "lrkv_decode_paged (split pass + merge)" if args.paged else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
         "mfma_util_shared_score": mfma_util,
         "layer_step": layer,

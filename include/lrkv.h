@@ -84,6 +84,33 @@ typedef struct {
     int32_t* seq_lens;
 } lrkv_cache;
 
+/* A paged factored cache (review sec. 4, the paged allocation a serving system
+ * uses; sec. 9, append after prefill across page boundaries): the same rows as
+ * lrkv_cache, stored in fixed-size pages drawn from one pool per tensor.
+ *   k_pages, v_pages    [n_pages][page_rows][d_h]     (dims->dtype)
+ *   zk_pages, zv_pages  [n_pages][page_rows][H][r]    token-major as in lrkv_cache; may be NULL iff r == 0
+ *   block_table         device [batch][max_pages] int32: logical page m of sequence b (rows
+ *                       m*page_rows .. (m+1)*page_rows - 1) is pool page block_table[b][m]
+ *   seq_lens            device [batch] int32, as in lrkv_cache
+ *   page_rows           rows per page: a power of two, >= 32
+ *   max_pages           entries per sequence in block_table; dims->L_cap must equal max_pages * page_rows
+ *   n_pages             pages in each pool
+ * Every table entry that covers a live row (or the row an append writes) must
+ * be a valid page index in [0, n_pages); the library does not check device
+ * contents.  Pages may be shared between sequences only if their live rows
+ * are identical (e.g. a common prefix) and no append writes into them. */
+typedef struct {
+    void* k_pages;
+    void* v_pages;
+    void* zk_pages;
+    void* zv_pages;
+    int32_t* block_table;
+    int32_t* seq_lens;
+    int32_t page_rows;
+    int32_t max_pages;
+    int32_t n_pages;
+} lrkv_paged_cache;
+
 /* Absorb the key basis into the query: p[b][h][i] = sum_c q[b][h][c] * B_k[h][c][i]
  * (reading notes sec. 2.4 Eq. (6); review sec. 3, Algorithm 2: one small
  * product per head per step).
@@ -218,6 +245,21 @@ lrkv_status lrkv_norm_query(const lrkv_dims* dims, const void* q, const void* g_
 lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, const void* rho, int32_t max_len,
                                const void* q_eff, const float* p, const void* B_v, float* out, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* lrkv_cache_append on a paged cache: row seq_lens[b] of sequence b goes to
+ * pool page block_table[b][seq_lens[b] / page_rows], row seq_lens[b] %
+ * page_rows, then seq_lens[b] is incremented; a sequence at L_cap or with a
+ * negative length is left unchanged. */
+lrkv_status lrkv_paged_append(const lrkv_dims* dims, const lrkv_paged_cache* cache, const void* k_new,
+                              const void* v_new, const void* zk_new, const void* zv_new, void* stream);
+
+/* lrkv_decode on a paged cache: the same arithmetic, plan and workspace
+ * (lrkv_decode_workspace_bytes(dims, max_len)) as lrkv_decode on the
+ * contiguous cache holding the same rows, and for the matrix-core bf16 shapes
+ * bitwise the same result.  Each pool must hold fewer than 2^31 bytes. */
+lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cache, int32_t max_len, const void* q,
+                              const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Rebuild every head's keys and values from the factored cache (reading notes
  * sec. 2.1 Eqs. (2)-(5); review sec. 3, the materialised form training and

@@ -27,7 +27,7 @@ LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
-            "lrkv_decode_multi", "lrkv_key_scales", "lrkv_norm_query", "lrkv_decode_normed", "lrkv_materialize",
+            "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_key_scales", "lrkv_norm_query", "lrkv_decode_normed", "lrkv_materialize",
             "lrkv_project_append", "lrkv_output_project", "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
 
@@ -49,6 +49,14 @@ class Cache(ctypes.Structure):
                 ("z_v", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p)]
 
 
+class PagedCache(ctypes.Structure):
+    """lrkv_paged_cache: page pools k/v/zk/zv, block_table, seq_lens (device pointers), page_rows, max_pages,
+    n_pages."""
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p), ("zk_pages", ctypes.c_void_p),
+                ("zv_pages", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("page_rows", ctypes.c_int32), ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -61,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
         D, C = ctypes.POINTER(Dims), ctypes.POINTER(Cache)
+        PC = ctypes.POINTER(PagedCache)
         sig = {
             "lrkv_absorb_query": ([D, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_cache_append": ([D, C, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -71,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_multi_workspace_bytes": ([D, i32, i32], sz),
             "lrkv_decode_multi": ([D, i32, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_paged_append": ([D, PC, vp, vp, vp, vp, vp], ctypes.c_int),
+            "lrkv_decode_paged": ([D, PC, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_key_scales": ([D, C, i32, i32, vp, ctypes.c_float, vp, vp], ctypes.c_int),
             "lrkv_norm_query": ([D, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int),
             "lrkv_decode_normed": ([D, C, vp, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -126,7 +137,9 @@ def make_dims(batch: int, H: int, d_h: int, r: int, L_cap: int, dtype: int) -> D
 
 
 def make_cache(k_shared, v_shared, z_k, z_v, seq_lens) -> Cache:
-    return Cache(_ptr(k_shared), _ptr(v_shared), _ptr(z_k), _ptr(z_v), _ptr(seq_lens))
+    c = Cache(_ptr(k_shared), _ptr(v_shared), _ptr(z_k), _ptr(z_v), _ptr(seq_lens))
+    c._tensors = (k_shared, v_shared, z_k, z_v, seq_lens)  # keep the pointed-to tensors alive with the structure
+    return c
 
 
 def lrkv_absorb_query(dims: Dims, q, B_k, p, stream=None) -> None:
@@ -176,6 +189,26 @@ def lrkv_decode_multi(dims: Dims, n_queries: int, cache: Cache, max_len: int, q,
     _check(lib().lrkv_decode_multi(ctypes.byref(dims), n_queries, ctypes.byref(cache), max_len, _ptr(q), _ptr(p),
                                    _ptr(B_v), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)),
            "lrkv_decode_multi")
+
+
+def make_paged_cache(k_pages, v_pages, zk_pages, zv_pages, block_table, seq_lens, page_rows: int, max_pages: int,
+                     n_pages: int) -> PagedCache:
+    pc = PagedCache(_ptr(k_pages), _ptr(v_pages), _ptr(zk_pages), _ptr(zv_pages), _ptr(block_table),
+                    _ptr(seq_lens), page_rows, max_pages, n_pages)
+    # the structure holds raw device pointers: keep the tensors alive as long as it is
+    pc._tensors = (k_pages, v_pages, zk_pages, zv_pages, block_table, seq_lens)
+    return pc
+
+
+def lrkv_paged_append(dims: Dims, cache: PagedCache, k_new, v_new, zk_new, zv_new, stream=None) -> None:
+    _check(lib().lrkv_paged_append(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(zk_new),
+                                   _ptr(zv_new), _stream(stream)), "lrkv_paged_append")
+
+
+def lrkv_decode_paged(dims: Dims, cache: PagedCache, max_len: int, q, p, B_v, out, workspace, workspace_bytes: int,
+                      stream=None) -> None:
+    _check(lib().lrkv_decode_paged(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(q), _ptr(p), _ptr(B_v),
+                                   _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_paged")
 
 
 def lrkv_key_scales(dims: Dims, cache: Cache, max_len: int, n_last: int, B_k, eps: float, rho, stream=None) -> None:

@@ -100,11 +100,15 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int H, int d
 }
 
 template <typename T>
+// block_table NULL: contiguous cache [batch][L_cap][...]; else page pools [n_pages][1 << page_shift][...]
+// with logical page m of sequence b at pool page block_table[b * max_pages + m] (L_cap = max_pages pages)
 __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int L_cap, T* __restrict__ k_shared,
                                                      T* __restrict__ v_shared, T* __restrict__ z_k,
                                                      T* __restrict__ z_v, int32_t* __restrict__ seq_lens,
                                                      const T* __restrict__ k_new, const T* __restrict__ v_new,
-                                                     const T* __restrict__ zk_new, const T* __restrict__ zv_new) {
+                                                     const T* __restrict__ zk_new, const T* __restrict__ zv_new,
+                                                     const int32_t* __restrict__ block_table, int page_shift,
+                                                     int max_pages) {
     __shared__ int row;
     const int b = blockIdx.x;
     if (threadIdx.x == 0) {
@@ -114,10 +118,14 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
     __syncthreads();
     const int j = row;
     if (j < 0) return;  // full or invalid: nothing written, length unchanged
-    const size_t srow = ((size_t)b * L_cap + j) * d_h;
+    // the row's index in the cache tensors (contiguous) or page pools (paged)
+    const size_t grow = block_table ? ((size_t)block_table[(size_t)b * max_pages + (j >> page_shift)] << page_shift) +
+                                          (size_t)(j & ((1 << page_shift) - 1))
+                                    : (size_t)b * L_cap + j;
+    const size_t srow = grow * d_h;
     // token-major latents: token j's H x r latents of every head form one contiguous row, and the
     // new rows [b][H][r] are contiguous too, so both copies are plain row copies
-    const size_t zrow = ((size_t)b * L_cap + j) * H * r, zsrc = (size_t)b * H * r;
+    const size_t zrow = grow * H * r, zsrc = (size_t)b * H * r;
     constexpr int VE = 16 / (int)sizeof(T);
     if ((d_h % VE) == 0 && ((H * r) % VE) == 0) {
         typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -168,18 +176,41 @@ hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void
     return hipGetLastError();
 }
 
+namespace {
+template <typename T>
+void launch_append_t(int batch, int H, int d_h, int r, int L_cap, void* k_shared, void* v_shared, void* z_k,
+                     void* z_v, int32_t* seq_lens, const void* k_new, const void* v_new, const void* zk_new,
+                     const void* zv_new, const int32_t* block_table, int page_shift, int max_pages,
+                     hipStream_t stream) {
+    hipLaunchKernelGGL(append_kernel<T>, dim3(batch), dim3(256), 0, stream, H, d_h, r, L_cap, (T*)k_shared,
+                       (T*)v_shared, (T*)z_k, (T*)z_v, seq_lens, (const T*)k_new, (const T*)v_new, (const T*)zk_new,
+                       (const T*)zv_new, block_table, page_shift, max_pages);
+}
+}  // namespace
+
 hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype, void* k_shared, void* v_shared,
                          void* z_k, void* z_v, int32_t* seq_lens, const void* k_new, const void* v_new,
                          const void* zk_new, const void* zv_new, hipStream_t stream) {
-    dim3 grid(batch), block(256);
     if (dtype == 0)
-        hipLaunchKernelGGL(append_kernel<float>, grid, block, 0, stream, H, d_h, r, L_cap, (float*)k_shared,
-                           (float*)v_shared, (float*)z_k, (float*)z_v, seq_lens, (const float*)k_new,
-                           (const float*)v_new, (const float*)zk_new, (const float*)zv_new);
+        launch_append_t<float>(batch, H, d_h, r, L_cap, k_shared, v_shared, z_k, z_v, seq_lens, k_new, v_new, zk_new,
+                               zv_new, nullptr, 0, 0, stream);
     else
-        hipLaunchKernelGGL(append_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, L_cap, (uint16_t*)k_shared,
-                           (uint16_t*)v_shared, (uint16_t*)z_k, (uint16_t*)z_v, seq_lens, (const uint16_t*)k_new,
-                           (const uint16_t*)v_new, (const uint16_t*)zk_new, (const uint16_t*)zv_new);
+        launch_append_t<uint16_t>(batch, H, d_h, r, L_cap, k_shared, v_shared, z_k, z_v, seq_lens, k_new, v_new,
+                                  zk_new, zv_new, nullptr, 0, 0, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int page_shift, int max_pages,
+                              void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
+                              const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,
+                              const void* zk_new, const void* zv_new, hipStream_t stream) {
+    const int L_cap = max_pages << page_shift;
+    if (dtype == 0)
+        launch_append_t<float>(batch, H, d_h, r, L_cap, k_pages, v_pages, zk_pages, zv_pages, seq_lens, k_new, v_new,
+                               zk_new, zv_new, block_table, page_shift, max_pages, stream);
+    else
+        launch_append_t<uint16_t>(batch, H, d_h, r, L_cap, k_pages, v_pages, zk_pages, zv_pages, seq_lens, k_new,
+                                  v_new, zk_new, zv_new, block_table, page_shift, max_pages, stream);
     return hipGetLastError();
 }
 

@@ -54,8 +54,8 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     const int Lb = clamped_len(a.seq_lens, b, a.max_len);
     if (split * kTile >= Lb) return;  // no live rows in this split; the merge skips it
 
-    const T* ks = (const T*)a.k_shared + (size_t)b * a.L_cap * D;
-    const T* vs = (const T*)a.v_shared + (size_t)b * a.L_cap * D;
+    const T* ks = (const T*)a.k_shared;  // rows addressed by their row in the tensor (or page pool)
+    const T* vs = (const T*)a.v_shared;
     const T* zk = (const T*)a.z_k;
     const T* zv = (const T*)a.z_v;
     const T* q = (const T*)a.q;
@@ -71,12 +71,15 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
 
     for (int t0 = split * kTile; t0 < Lb; t0 += wslot.S_b * kTile) {
         const int nvalid = min(kTile, Lb - t0);
+        // first row of the tile in the cache tensors: contiguous, or the pool row of its page (a page holds
+        // whole tiles)
+        const size_t r0 = a.block_table ? (size_t)paged_row(a, b, t0) : (size_t)b * a.L_cap + t0;
         __syncthreads();  // previous tile fully consumed (and state initialised)
         for (int idx = tid; idx < kTile * D; idx += kThreads) {
             const int t = idx / D, c = idx - t * D;
-            const int row = t0 + (t < nvalid ? t : nvalid - 1);  // stay on live rows
-            Kt[t * (D + 1) + c] = elem<T>::load(ks, (size_t)row * D + c);
-            Vt[t * D + c] = elem<T>::load(vs, (size_t)row * D + c);
+            const size_t row = r0 + (t < nvalid ? t : nvalid - 1);  // stay on live rows
+            Kt[t * (D + 1) + c] = elem<T>::load(ks, row * D + c);
+            Vt[t * D + c] = elem<T>::load(vs, row * D + c);
         }
         __syncthreads();
 
@@ -89,7 +92,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
             const size_t bh = (size_t)b * HV + v;           // q and p row of (sequence, query, head)
             const bool seen = live && t0 + t < Lb - Q + qi + 1;  // causal limit of query qi
             // latents are token-major: row t of sequence b holds every head's r coordinates
-            const size_t zrow = (((size_t)b * a.L_cap + (size_t)(t0 + (live ? t : 0))) * H + h) * R;
+            const size_t zrow = ((r0 + (size_t)(live ? t : 0)) * H + h) * R;
             // score: shared part on the LDS tile, private part on the latent row
             float sc = 0.f;
             for (int c = c_lo; c < c_hi; ++c) sc = fmaf(elem<T>::load(q, bh * D + c), Kt[t * (D + 1) + c], sc);
@@ -121,7 +124,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
             }
             for (int i = lane; i < R; i += 64) {
                 float sum = 0.f;
-                const size_t z0 = (((size_t)b * a.L_cap + (size_t)t0) * H + h) * R + i;
+                const size_t z0 = (r0 * H + h) * R + i;
                 for (int u = 0; u < nvalid; ++u)
                     sum = fmaf(ebuf[wave * kTile + u], elem<T>::load(zv, z0 + (size_t)u * H * R), sum);
                 acc_h[D + i] = alpha * acc_h[D + i] + sum;

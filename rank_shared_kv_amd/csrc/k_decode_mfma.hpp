@@ -245,16 +245,19 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // ---- buffer descriptors of this sequence and fixed per-lane byte offsets ----
     // latents are token-major ([L_cap][H][r] per sequence): one latent row holds every head
     const uint32_t row_bytes_sh = D * 2, row_bytes_lat = H * R * 2;
-    const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + (size_t)b * a.L_cap * D,
-                                                 (uint32_t)a.L_cap * row_bytes_sh);
-    const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const uint16_t*)a.v_shared + (size_t)b * a.L_cap * D,
-                                                 (uint32_t)a.L_cap * row_bytes_sh);
+    // contiguous cache: descriptors over this sequence's rows, a block addressed by its row t0; paged cache:
+    // descriptors over the whole page pools, a block addressed by its pool row (pages hold whole blocks)
+    const bool paged = a.block_table != nullptr;
+    const size_t seq_rows = paged ? 0 : (size_t)b * a.L_cap;
+    const uint32_t n_rows = paged ? (uint32_t)a.n_pages << a.page_shift : (uint32_t)a.L_cap;
+    const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + seq_rows * D, n_rows * row_bytes_sh);
+    const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const uint16_t*)a.v_shared + seq_rows * D, n_rows * row_bytes_sh);
     __amdgpu_buffer_rsrc_t rs_zk = rs_k, rs_zv = rs_v;
     uint32_t vo_zv = 0;  // lane offset of (head 16*hg + hh, coordinate slice sl) in the latent tensors
     if constexpr (R > 0) {
-        const uint32_t lat_bytes = (uint32_t)H * a.L_cap * (R * 2);
-        rs_zk = buf_rsrc((const uint16_t*)a.z_k + (size_t)b * H * a.L_cap * R, lat_bytes);
-        rs_zv = buf_rsrc((const uint16_t*)a.z_v + (size_t)b * H * a.L_cap * R, lat_bytes);
+        const uint32_t lat_bytes = n_rows * row_bytes_lat;
+        rs_zk = buf_rsrc((const uint16_t*)a.z_k + seq_rows * H * R, lat_bytes);
+        rs_zv = buf_rsrc((const uint16_t*)a.z_v + seq_rows * H * R, lat_bytes);
         vo_zv = (uint32_t)(16 * hg + hh) * R * 2 + sl * EPL * 2;
     }
     const uint32_t vo_kf = (uint32_t)n16 * row_bytes_sh + 16 * g4;              // key fragment rows n16, 16 + n16
@@ -273,11 +276,12 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     uint32_t ring[NSLOT][SDW];
 
     // unit u of the block starting at row t0 -> slot
-    auto issue = [&](int u, int t0, int slot) {
+    // unit u of the block whose first row sits at (pool) row pr, into ring slot `slot`
+    auto issue = [&](int u, int pr, int slot) {
         if (u == 0) {  // key fragments in the MFMA A layout: rows 16*half + n16, chunk 4*kk + g4
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int so = (t0 + 16 * half) * (int)row_bytes_sh;
+                const int so = (pr + 16 * half) * (int)row_bytes_sh;
 #pragma unroll
                 for (int kk = 0; kk < C::KSTEPS; ++kk) {
                     const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, vo_kf + 64 * kk, so, kNTSh);
@@ -291,7 +295,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         } else if (u == 1) {  // value tile, rows 4*srow + (ins & 3) + 4*RPI*(ins >> 2)
 #pragma unroll
             for (int grp = 0; grp < C::NINS / 4; ++grp) {
-                const int so = (t0 + 4 * C::RPI * grp) * (int)row_bytes_sh;
+                const int so = (pr + 4 * C::RPI * grp) * (int)row_bytes_sh;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int ins = 4 * grp + jj;
@@ -306,7 +310,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             const int v = u - 2;
             const int phase = v / (4 * OCTS);
             const int oi = (v % (4 * OCTS)) / 4, sub = v % 4;
-            const int so = t0 * (int)row_bytes_lat + oi * (int)oct_bytes;
+            const int so = pr * (int)row_bytes_lat + oi * (int)oct_bytes;
             const __amdgpu_buffer_rsrc_t rs = (phase == 0) ? rs_zk : rs_zv;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -343,8 +347,9 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // and with some region strides those concurrent streams crowd the same HBM channels.
     const int rot = (int)(((long)nmine * b) / a.batch);
     if (nmine > 0) {
+        const int pr_first = paged_row(a, b, kRows * (first_blk + rot * step_blk));
 #pragma unroll
-        for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * (first_blk + rot * step_blk), u);
+        for (int u = 0; u < NSLOT - 1; ++u) issue(u, pr_first, u);
     }
 
     for (int it = 0; it < nmine; ++it) {
@@ -356,6 +361,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         // next block of this row lane; on the last block the prefetch re-reads this block (always in bounds)
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
         const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
+        const int pr = paged_row(a, b, t0), pr_pf = paged_row(a, b, t0_pf);  // pool rows (t0 when contiguous)
         f32x4_t s_sh[2];
         float ev[8];
         uint32_t rho_w[8];  // scales of this lane's 8 scores (bf16 bits), read at the top of the block
@@ -373,8 +379,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             // keep NSLOT - 1 units in flight ahead of this one
             {
                 const int un = u + NSLOT - 1;
-                if (un < NU) issue(un, t0, un % NSLOT);
-                else issue(un - NU, t0_pf, un % NSLOT);
+                if (un < NU) issue(un, pr, un % NSLOT);
+                else issue(un - NU, pr_pf, un % NSLOT);
             }
             // fence the scheduler at unit boundaries: loads stay NSLOT - 1 units ahead, no further
             __builtin_amdgcn_sched_barrier(0);

@@ -86,17 +86,25 @@ int env_int(const char* name, int dflt) {
 // per SIMD), LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch).
 constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
+// Which decode the plan is for.  The normalised variant's bf16 matrix-core kernel is built for one wave per
+// SIMD; neither it nor the paged cache has an fp32 matrix-core kernel (the general kernel serves them).  Their
+// G never exceeds the plain plan's, so the plain workspace size serves every variant, and a paged decode of a
+// bf16 matrix-core shape uses exactly the plain plan.
+enum class PlanVariant { kPlain, kNormed, kPaged };
+
 // n_queries: query tokens per sequence (1 for single-token decode); they act as H * n_queries virtual heads.
-// normed: the normalised variant (scaled logits).  Its bf16 matrix-core kernel is built for one wave per SIMD
-// and the fp32 one has no such variant (the general kernel serves it); its G never exceeds the plain plan's,
-// so the plain workspace size serves both.
-bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_queries = 1, bool normed = false) {
+bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_queries = 1,
+                PlanVariant variant = PlanVariant::kPlain) {
     using namespace lrkv;
     SplitPlan p{};
     p.n_queries = n_queries;
-    if (normed) {
+    if (variant != PlanVariant::kPlain) {
         SplitPlan plain;
         if (n_queries != 1 || !plan_split(d, max_len, &plain)) return false;
+        if (variant == PlanVariant::kPaged && plain.path != SplitPath::kMfmaF32) {
+            *out = plain;
+            return true;
+        }
         if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
             p.path = SplitPath::kMfmaBf16;
             p.chunk = mfma_rows_per_tile(d.H);
@@ -155,12 +163,12 @@ size_t workspace_bytes(const lrkv_dims& d, const lrkv::SplitPlan& p) {
 }
 
 lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan, int n_queries = 1,
-                                bool normed = false) {
+                                PlanVariant variant = PlanVariant::kPlain) {
     LRKV_TRY(check_dims(dims));
     if (max_len < 0 || max_len > dims->L_cap)
         return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
     if (n_queries < 1 || n_queries > 64) return fail(LRKV_ERR_INVALID_ARG, "n_queries=%d outside [1, 64]", n_queries);
-    if (!plan_split(*dims, max_len, plan, n_queries, normed))
+    if (!plan_split(*dims, max_len, plan, n_queries, variant))
         return fail(LRKV_ERR_UNSUPPORTED, "no kernel for H=%d d_h=%d r=%d dtype=%d", dims->H, dims->d_h, dims->r,
                     dims->dtype);
     return LRKV_OK;
@@ -175,8 +183,14 @@ lrkv_status check_workspace(const lrkv_dims& d, const lrkv::SplitPlan& p, const 
     return LRKV_OK;
 }
 
+struct PagedView {  // the paged layout of a cache handed to run_partial (block_table NULL: contiguous)
+    const int32_t* block_table = nullptr;
+    int page_shift = 0, max_pages = 0, n_pages = 0;
+};
+
 lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, const void* q, const float* p,
-                        void* ws, const lrkv::SplitPlan& plan, hipStream_t stream, const void* rho = nullptr) {
+                        void* ws, const lrkv::SplitPlan& plan, hipStream_t stream, const void* rho = nullptr,
+                        const PagedView& pv = PagedView()) {
     using namespace lrkv;
     if (plan.num_splits == 0) return LRKV_OK;
     DecodeArgs a{};
@@ -199,6 +213,10 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.p = p;
     a.rho = rho;
     a.ws = (float*)ws;
+    a.block_table = pv.block_table;
+    a.page_shift = pv.page_shift;
+    a.max_pages = pv.max_pages;
+    a.n_pages = pv.n_pages;
     hipError_t e = (plan.path == SplitPath::kMfmaBf16)  ? launch_split_mfma(a, plan.occupancy, stream)
                    : (plan.path == SplitPath::kMfmaF32) ? launch_split_mfma_f32(a, plan.occupancy, stream)
                                                          : launch_split_general(a, stream);
@@ -407,7 +425,7 @@ lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, c
                                const void* q_eff, const float* p, const void* B_v, float* out, void* workspace,
                                size_t workspace_bytes_, void* stream) {
     lrkv::SplitPlan plan;
-    LRKV_TRY(check_decode_common(dims, max_len, &plan, 1, true));
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, 1, PlanVariant::kNormed));
     LRKV_TRY(check_cache(*dims, cache, true));
     LRKV_TRY(need_ptr(rho, "rho"));
     LRKV_TRY(need_ptr(q_eff, "q_eff"));
@@ -418,6 +436,91 @@ lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, c
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q_eff, p, workspace, plan, (hipStream_t)stream, rho));
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                                      plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+int log2_exact(int x) {  // log2 of a power of two, -1 otherwise
+    if (x <= 0 || (x & (x - 1)) != 0) return -1;
+    int k = 0;
+    while ((1 << k) < x) ++k;
+    return k;
+}
+
+lrkv_status check_paged(const lrkv_dims& d, const lrkv_paged_cache* c, PagedView* pv) {
+    if (!c) return fail(LRKV_ERR_INVALID_ARG, "cache is NULL");
+    LRKV_TRY(need_ptr(c->k_pages, "cache.k_pages"));
+    LRKV_TRY(need_ptr(c->v_pages, "cache.v_pages"));
+    LRKV_TRY(need_ptr(c->block_table, "cache.block_table"));
+    LRKV_TRY(need_ptr(c->seq_lens, "cache.seq_lens"));
+    if (d.r > 0) {
+        LRKV_TRY(need_ptr(c->zk_pages, "cache.zk_pages"));
+        LRKV_TRY(need_ptr(c->zv_pages, "cache.zv_pages"));
+    }
+    const int shift = log2_exact(c->page_rows);
+    if (shift < 5) return fail(LRKV_ERR_INVALID_ARG, "page_rows=%d is not a power of two >= 32", c->page_rows);
+    if (c->max_pages < 1 || c->n_pages < 1)
+        return fail(LRKV_ERR_INVALID_ARG, "max_pages=%d and n_pages=%d must be >= 1", c->max_pages, c->n_pages);
+    if ((long long)c->max_pages * c->page_rows != d.L_cap)
+        return fail(LRKV_ERR_INVALID_ARG, "L_cap=%d differs from max_pages * page_rows = %lld", d.L_cap,
+                    (long long)c->max_pages * c->page_rows);
+    const long long s = d.dtype == LRKV_F32 ? 4 : 2;
+    const long long pool_rows = (long long)c->n_pages * c->page_rows;
+    if (pool_rows * d.d_h * s >= (1LL << 31) || pool_rows * d.H * d.r * s >= (1LL << 31))
+        return fail(LRKV_ERR_UNSUPPORTED, "a page pool of %lld rows reaches 2^31 bytes", pool_rows);
+    pv->block_table = c->block_table;
+    pv->page_shift = shift;
+    pv->max_pages = c->max_pages;
+    pv->n_pages = c->n_pages;
+    return LRKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lrkv_status lrkv_paged_append(const lrkv_dims* dims, const lrkv_paged_cache* cache, const void* k_new,
+                              const void* v_new, const void* zk_new, const void* zv_new, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    PagedView pv;
+    LRKV_TRY(check_paged(*dims, cache, &pv));
+    LRKV_TRY(need_ptr(k_new, "k_new"));
+    LRKV_TRY(need_ptr(v_new, "v_new"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(zk_new, "zk_new"));
+        LRKV_TRY(need_ptr(zv_new, "zv_new"));
+    }
+    hipError_t e = lrkv::launch_paged_append(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, pv.page_shift,
+                                             pv.max_pages, cache->k_pages, cache->v_pages, cache->zk_pages,
+                                             cache->zv_pages, cache->block_table, cache->seq_lens, k_new, v_new,
+                                             zk_new, zv_new, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "paged append kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cache, int32_t max_len, const void* q,
+                              const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes_,
+                              void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, 1, PlanVariant::kPaged));
+    PagedView pv;
+    LRKV_TRY(check_paged(*dims, cache, &pv));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(p, "p"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    const lrkv_cache pools{cache->k_pages, cache->v_pages, cache->zk_pages, cache->zv_pages, cache->seq_lens};
+    LRKV_TRY(run_partial(*dims, pools, max_len, q, p, workspace, plan, (hipStream_t)stream, nullptr, pv));
     hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);

@@ -24,7 +24,18 @@ struct DecodeArgs {
     const float* p;
     const void* rho;     // normalised variant: scales [batch][L_cap][H] (cache dtype) multiplying the logits; else NULL
     float* ws;           // [G][H * Q][record]
+    // paged cache (block_table set): the four cache pointers are page pools [n_pages][page_rows][...] and
+    // logical row t of sequence b is pool row block_table[b * max_pages + (t >> page_shift)] * page_rows
+    // + (t & (page_rows - 1)); block_table NULL: contiguous [batch][L_cap][...]
+    const int32_t* block_table;
+    int page_shift, max_pages, n_pages;
 };
+
+// pool row of logical row t of sequence b (t uniform across the caller's wave)
+__device__ __forceinline__ int paged_row(const DecodeArgs& a, int b, int t) {
+    if (!a.block_table) return t;
+    return (a.block_table[(size_t)b * a.max_pages + (t >> a.page_shift)] << a.page_shift) + (t & ((1 << a.page_shift) - 1));
+}
 
 // Which split kernel a problem uses.
 enum class SplitPath { kGeneral, kMfmaBf16, kMfmaF32 };
@@ -65,6 +76,10 @@ hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int d
                               const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
                               const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
                               hipStream_t stream);
+hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int page_shift, int max_pages,
+                              void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
+                              const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,
+                              const void* zk_new, const void* zv_new, hipStream_t stream);
 hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, int n_last,
                              float eps, const int32_t* seq_lens, const void* k_shared, const void* z_k,
                              const void* B_k, void* rho, hipStream_t stream);
