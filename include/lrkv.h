@@ -189,12 +189,17 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
  * position seq_lens[b] - Q + i and sees rows j <= seq_lens[b] - Q + i, the
  * causal mask inside the chunk (reading notes sec. 2.4, Eqs. (6)-(7) under
  * the causal softmax; review sec. 3).  Everything else is lrkv_decode's.
- *   n_queries  Q, 1 <= Q <= 64
+ *   n_queries  Q, 1 <= Q <= 64, batch * Q <= 65535
  *   q          device [batch][Q][H][d_h] (dims->dtype)
  *   p          device [batch][Q][H][r] fp32: lrkv_absorb_query with dims->batch = batch * Q
  *   out        device [batch][Q][H][d_h] fp32 (0 for a query that sees no row)
  *   workspace  >= lrkv_decode_multi_workspace_bytes(dims, Q, max_len) bytes, 256-byte aligned
- * The rows are read once for all Q queries of a sequence.  Q = 1 gives exactly
+ * It runs lrkv_decode's kernels on batch * Q virtual sequences (query i of
+ * sequence b is virtual sequence b * Q + i, with the causal length above).
+ * The Q virtual sequences of one sequence share its block order, so their
+ * workgroups read the same rows at about the same time and the repeats are
+ * served by the GPU's caches.  The workspace holds lrkv_decode's records for
+ * batch * Q sequences, then the virtual lengths.  Q = 1 gives exactly
  * lrkv_decode's kernels and results. */
 size_t lrkv_decode_multi_workspace_bytes(const lrkv_dims* dims, int32_t n_queries, int32_t max_len);
 lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lrkv_cache* cache, int32_t max_len,

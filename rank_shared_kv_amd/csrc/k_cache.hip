@@ -200,6 +200,22 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
     return hipGetLastError();
 }
 
+namespace {
+__global__ void __launch_bounds__(256) multi_lengths_kernel(int n, int Q, const int32_t* __restrict__ seq_lens,
+                                                            int32_t* __restrict__ lens_out) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= n) return;
+    const int b = v / Q, i = v - b * Q;
+    lens_out[v] = max(0, seq_lens[b] - Q + 1 + i);
+}
+}  // namespace
+
+hipError_t launch_multi_lengths(int batch, int Q, const int32_t* seq_lens, int32_t* lens_out, hipStream_t stream) {
+    const int n = batch * Q;
+    hipLaunchKernelGGL(multi_lengths_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, Q, seq_lens, lens_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int page_shift, int max_pages,
                               void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
                               const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,

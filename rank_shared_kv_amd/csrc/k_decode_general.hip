@@ -36,15 +36,13 @@ __host__ __device__ inline size_t general_lds_floats(int H, int d_h, int r) {
 template <typename T>
 __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     extern __shared__ float smem[];
-    // Q query tokens per sequence make H * Q virtual heads v = i * H + h (query i, head h); query i
-    // sits at position L_b - Q + i and sees the rows before and at it (causal inside the chunk)
-    const int H = a.H, Q = a.n_queries, HV = H * Q, D = a.d_h, R = a.r, rec = partial_record_floats(D, R);
+    const int H = a.H, D = a.d_h, R = a.r, rec = partial_record_floats(D, R);
     float* Kt = smem;                          // [kTile][D + 1]
     float* Vt = Kt + kTile * (D + 1);          // [kTile][D]
-    float* acc = Vt + kTile * D;               // [HV][D + R]
-    float* mrow = acc + (size_t)HV * (D + R);  // [HV]
-    float* lrow = mrow + HV;                   // [HV]
-    float* ebuf = lrow + HV;                   // [4][kTile]
+    float* acc = Vt + kTile * D;               // [H][D + R]
+    float* mrow = acc + (size_t)H * (D + R);   // [H]
+    float* lrow = mrow + H;                    // [H]
+    float* ebuf = lrow + H;                    // [4][kTile]
 
     // which sequence and split (splits dealt to sequences by length); split s of sequence b takes the
     // tiles s, s + S_b, s + 2 S_b, ... of the sequence
@@ -53,6 +51,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     if (b < 0) return;
     const int Lb = clamped_len(a.seq_lens, b, a.max_len);
     if (split * kTile >= Lb) return;  // no live rows in this split; the merge skips it
+    const int bc = b / a.qgroup;      // the cached sequence this (virtual) sequence reads
 
     const T* ks = (const T*)a.k_shared;  // rows addressed by their row in the tensor (or page pool)
     const T* vs = (const T*)a.v_shared;
@@ -63,8 +62,8 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float scale = kLog2e / sqrtf((float)D);
 
-    for (int i = tid; i < HV * (D + R); i += kThreads) acc[i] = 0.f;
-    for (int i = tid; i < HV; i += kThreads) {
+    for (int i = tid; i < H * (D + R); i += kThreads) acc[i] = 0.f;
+    for (int i = tid; i < H; i += kThreads) {
         mrow[i] = -INFINITY;
         lrow[i] = 0.f;
     }
@@ -73,7 +72,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
         const int nvalid = min(kTile, Lb - t0);
         // first row of the tile in the cache tensors: contiguous, or the pool row of its page (a page holds
         // whole tiles)
-        const size_t r0 = a.block_table ? (size_t)paged_row(a, b, t0) : (size_t)b * a.L_cap + t0;
+        const size_t r0 = a.block_table ? (size_t)paged_row(a, bc, t0) : (size_t)bc * a.L_cap + t0;
         __syncthreads();  // previous tile fully consumed (and state initialised)
         for (int idx = tid; idx < kTile * D; idx += kThreads) {
             const int t = idx / D, c = idx - t * D;
@@ -87,10 +86,8 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
         const bool live = t < nvalid;
         const int c_lo = half * ((D + 1) / 2), c_hi = min(D, (half + 1) * ((D + 1) / 2));
         const int i_lo = half * ((R + 1) / 2), i_hi = min(R, (half + 1) * ((R + 1) / 2));
-        for (int v = wave; v < HV; v += kThreads / 64) {
-            const int h = v % H, qi = v / H;
-            const size_t bh = (size_t)b * HV + v;           // q and p row of (sequence, query, head)
-            const bool seen = live && t0 + t < Lb - Q + qi + 1;  // causal limit of query qi
+        for (int h = wave; h < H; h += kThreads / 64) {
+            const size_t bh = (size_t)b * H + h;  // q and p row of (sequence, head)
             // latents are token-major: row t of sequence b holds every head's r coordinates
             const size_t zrow = ((r0 + (size_t)(live ? t : 0)) * H + h) * R;
             // score: shared part on the LDS tile, private part on the latent row
@@ -100,23 +97,23 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
             sc += __shfl_xor(sc, 32);
             // normalised variant: the cached scale of (row, head) multiplies the summed logit
             float f = scale;
-            if (rho) f *= elem<T>::load(rho, ((size_t)b * a.L_cap + (size_t)(t0 + (live ? t : 0))) * H + h);
-            const float s2 = seen ? sc * f : -INFINITY;
+            if (rho) f *= elem<T>::load(rho, ((size_t)bc * a.L_cap + (size_t)(t0 + (live ? t : 0))) * H + h);
+            const float s2 = live ? sc * f : -INFINITY;
             float tmax = s2;
             for (int o = 16; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
-            const float m_old = mrow[v];
+            const float m_old = mrow[h];
             const float m_new = fmaxf(m_old, tmax);
             const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_old - m_new);  // nothing seen yet
-            const float e = seen ? fast_exp2(s2 - m_new) : 0.f;
+            const float e = live ? fast_exp2(s2 - m_new) : 0.f;
             float esum = e;
             for (int o = 16; o >= 1; o >>= 1) esum += __shfl_xor(esum, o);
             if (lane < kTile) ebuf[wave * kTile + lane] = e;
             wave_lds_sync();
             if (lane == 0) {
-                mrow[v] = m_new;
-                lrow[v] = alpha * lrow[v] + esum;
+                mrow[h] = m_new;
+                lrow[h] = alpha * lrow[h] + esum;
             }
-            float* acc_h = acc + (size_t)v * (D + R);
+            float* acc_h = acc + (size_t)h * (D + R);
             for (int c = lane; c < D; c += 64) {
                 float sum = 0.f;
                 for (int u = 0; u < nvalid; ++u) sum = fmaf(ebuf[wave * kTile + u], Vt[u * D + c], sum);
@@ -129,12 +126,12 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
                     sum = fmaf(ebuf[wave * kTile + u], elem<T>::load(zv, z0 + (size_t)u * H * R), sum);
                 acc_h[D + i] = alpha * acc_h[D + i] + sum;
             }
-            wave_lds_sync();  // ebuf reused by this wave's next virtual head
+            wave_lds_sync();  // ebuf reused by this wave's next head
         }
     }
     __syncthreads();
-    float* out = a.ws + (size_t)blockIdx.x * HV * rec;  // record of workgroup w = W_b + split
-    for (int idx = tid; idx < HV * rec; idx += kThreads) {
+    float* out = a.ws + (size_t)blockIdx.x * H * rec;  // record of workgroup w = W_b + split
+    for (int idx = tid; idx < H * rec; idx += kThreads) {
         const int v = idx / rec, k = idx - v * rec;
         float x = 0.f;
         if (k < D + R) x = acc[(size_t)v * (D + R) + k];
@@ -150,14 +147,14 @@ int general_rows_per_tile() { return kTile; }
 
 size_t general_lds_bytes(int H, int d_h, int r) { return general_lds_floats(H, d_h, r) * sizeof(float); }
 
-// H here counts virtual heads (heads x query tokens); gfx950 gives a workgroup up to 160 KiB of LDS
+// gfx950 gives a workgroup up to 160 KiB of LDS
 bool general_path_supports(int H, int d_h, int r) {
     return d_h >= 1 && d_h <= 256 && r >= 0 && r <= 256 && H >= 1 && general_lds_bytes(H, d_h, r) <= 160 * 1024;
 }
 
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid(a.num_splits), block(kThreads);
-    const size_t lds = general_lds_bytes(a.H * a.n_queries, a.d_h, a.r);
+    const size_t lds = general_lds_bytes(a.H, a.d_h, a.r);
     const void* kern = (a.dtype == 0) ? (const void*)split_general_kernel<float> : (const void*)split_general_kernel<uint16_t>;
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

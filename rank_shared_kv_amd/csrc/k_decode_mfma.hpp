@@ -248,7 +248,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // contiguous cache: descriptors over this sequence's rows, a block addressed by its row t0; paged cache:
     // descriptors over the whole page pools, a block addressed by its pool row (pages hold whole blocks)
     const bool paged = a.block_table != nullptr;
-    const size_t seq_rows = paged ? 0 : (size_t)b * a.L_cap;
+    const int bc = b / a.qgroup;  // the cached sequence this (virtual) sequence reads
+    const size_t seq_rows = paged ? 0 : (size_t)bc * a.L_cap;
     const uint32_t n_rows = paged ? (uint32_t)a.n_pages << a.page_shift : (uint32_t)a.L_cap;
     const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + seq_rows * D, n_rows * row_bytes_sh);
     const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const uint16_t*)a.v_shared + seq_rows * D, n_rows * row_bytes_sh);
@@ -268,7 +269,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     __amdgpu_buffer_rsrc_t rs_rho = rs_k;
     uint32_t vo_rho = 0;
     if constexpr (NORM) {
-        rs_rho = buf_rsrc((const uint16_t*)a.rho + (size_t)b * a.L_cap * H, (uint32_t)a.L_cap * H * 2);
+        rs_rho = buf_rsrc((const uint16_t*)a.rho + (size_t)bc * a.L_cap * H, (uint32_t)a.L_cap * H * 2);
         vo_rho = (uint32_t)(4 * g4 * H + 16 * hg + n16) * 2;
     }
 
@@ -345,9 +346,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // Sequence b walks its blocks starting b/batch of the way along (the same blocks, rotated order).
     // Otherwise every sequence reads the same relative position of its cache region at the same time,
     // and with some region strides those concurrent streams crowd the same HBM channels.
-    const int rot = (int)(((long)nmine * b) / a.batch);
+    // (the virtual sequences of one cached sequence share its rotation, so they read the same rows together)
+    const int rot = (int)(((long)nmine * bc) / (a.batch / a.qgroup));
     if (nmine > 0) {
-        const int pr_first = paged_row(a, b, kRows * (first_blk + rot * step_blk));
+        const int pr_first = paged_row(a, bc, kRows * (first_blk + rot * step_blk));
 #pragma unroll
         for (int u = 0; u < NSLOT - 1; ++u) issue(u, pr_first, u);
     }
@@ -361,7 +363,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         // next block of this row lane; on the last block the prefetch re-reads this block (always in bounds)
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
         const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
-        const int pr = paged_row(a, b, t0), pr_pf = paged_row(a, b, t0_pf);  // pool rows (t0 when contiguous)
+        const int pr = paged_row(a, bc, t0), pr_pf = paged_row(a, bc, t0_pf);  // pool rows (t0 when contiguous)
         f32x4_t s_sh[2];
         float ev[8];
         uint32_t rho_w[8];  // scales of this lane's 8 scores (bf16 bits), read at the top of the block

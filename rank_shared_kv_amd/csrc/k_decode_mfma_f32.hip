@@ -95,9 +95,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     __syncthreads();
 
     const uint32_t row_bytes = D * 4;
-    const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const float*)a.k_shared + (size_t)b * a.L_cap * D,
+    const int bc = b / a.qgroup;  // the cached sequence this (virtual) sequence reads
+    const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const float*)a.k_shared + (size_t)bc * a.L_cap * D,
                                                  (uint32_t)a.L_cap * row_bytes);
-    const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const float*)a.v_shared + (size_t)b * a.L_cap * D,
+    const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const float*)a.v_shared + (size_t)bc * a.L_cap * D,
                                                  (uint32_t)a.L_cap * row_bytes);
     const uint32_t vo_k = (uint32_t)n16 * row_bytes + 16 * g4;       // row n16 of the half, columns 4 g4 + 16 m
     const uint32_t vo_v = (uint32_t)(4 * g4) * row_bytes + 16 * n16;  // rows 4 g4 + tt, columns 64 p + 4 n16
@@ -151,8 +152,9 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     // row lane tl of split s takes blocks s*NTL + tl + k*S_b*NTL of the sequence
     const int first_blk = split * C::NTL + tl, step_blk = wslot.S_b * C::NTL, last_blk = nb;
     const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
-    // sequence b walks its blocks starting b/batch of the way along (same blocks, rotated order)
-    const int rot = (int)(((long)nmine * b) / a.batch);
+    // sequence b walks its blocks starting b/batch of the way along (same blocks, rotated order; the
+    // virtual sequences of one cached sequence share its rotation)
+    const int rot = (int)(((long)nmine * bc) / (a.batch / a.qgroup));
     if (nmine > 0) {
 #pragma unroll
         for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * (first_blk + rot * step_blk), u);

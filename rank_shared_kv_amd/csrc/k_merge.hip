@@ -48,7 +48,7 @@ __device__ __forceinline__ float vec_elem(const u32x4_t& v, int e) {
 // kGroups split groups of kCols threads each: 4 groups when sequences hold many splits, 1 when they
 // hold few (then the extra threads would only wait).
 template <typename T, int kGroups>
-__global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H, int Q, int D, int R, int max_len,
+__global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H, int D, int R, int max_len,
                                                                 int chunk, int S, const int32_t* __restrict__ seq_lens,
                                                                 const T* __restrict__ B_v, float* __restrict__ out,
                                                                 const float* __restrict__ ws) {
@@ -58,11 +58,9 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H
     __shared__ float gsum[kGroups][kCols];   // per-group rescaled sums
     __shared__ float sums[kMaxCols + 2];     // merged numerators, then l at [D + R]
     __shared__ float epi[kMergeThreads];     // epilogue partial products
-    // virtual head v = i * H + h: query token i (of Q) and head h
-    const int v = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, HV = H * Q;
-    const int h = v % H, qi = v / H;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int rec = partial_record_floats(D, R);
-    float* o = out + ((size_t)b * HV + v) * D;
+    float* o = out + ((size_t)b * H + h) * D;
 
     // epilogue operand: thread (c, vi) holds B^V[h][c][vi*VE, vi*VE + VE) as one 16-byte vector
     const int nvv = (R > 0 && (R % VE) == 0) ? R / VE : 0;
@@ -72,16 +70,15 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H
     if (vec_epi && ec < D) bv = *(const u32x4_t*)(B_v + ((size_t)h * D + ec) * R + evi * VE);
 
     const int Lb = clamped_len(seq_lens, b, max_len);
-    const int Lv = max(0, Lb - Q + qi + 1);  // rows query qi sees (causal inside the chunk)
     int W_b, S_b;
     sequence_splits(seq_lens, batch, max_len, S, b, &W_b, &S_b);  // every wave computes the same values
-    const int Sb = min(S_b, (Lv + chunk - 1) / chunk);  // splits s with s * granule < L_v hold rows it sees
+    const int Sb = min(S_b, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold rows
     if (Sb == 0) {
         for (int c = tid; c < D; c += kMergeThreads) o[c] = 0.f;
         return;
     }
-    const float* base = ws + ((size_t)W_b * HV + v) * rec;  // split s at base + s * HV * rec
-    const int sstride = HV * rec;  // the workspace is far below 2^31 floats
+    const float* base = ws + ((size_t)W_b * H + h) * rec;  // split s at base + s * H * rec
+    const int sstride = H * rec;  // the workspace is far below 2^31 floats
 
     // numerators (columns 0 .. D+R-1) and the denominator (column D+R+1) in passes of kCols columns
     const int ncols = D + R + 2;
@@ -173,21 +170,21 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H
 
 }  // namespace
 
-hipError_t launch_merge(int batch, int H, int n_queries, int d_h, int r, int dtype, int max_len, int chunk,
+hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk,
                         int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
                         hipStream_t stream) {
     if (d_h + r > kMaxCols) return hipErrorInvalidValue;
     // one split group per column when sequences average at most 16 splits, four otherwise
     const bool wide = num_splits > 16 * batch;
-    dim3 grid(H * n_queries, batch), block(wide ? 4 * kCols : kCols);
+    dim3 grid(H, batch), block(wide ? 4 * kCols : kCols);
     if (dtype == 0) {
         auto k = wide ? merge_kernel<float, 4> : merge_kernel<float, 1>;
-        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, n_queries, d_h, r, max_len, chunk, num_splits,
-                           seq_lens, (const float*)B_v, out, ws);
+        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits, seq_lens,
+                           (const float*)B_v, out, ws);
     } else {
         auto k = wide ? merge_kernel<uint16_t, 4> : merge_kernel<uint16_t, 1>;
-        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, n_queries, d_h, r, max_len, chunk, num_splits,
-                           seq_lens, (const uint16_t*)B_v, out, ws);
+        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits, seq_lens,
+                           (const uint16_t*)B_v, out, ws);
     }
     return hipGetLastError();
 }

@@ -92,15 +92,12 @@ constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's 
 // bf16 matrix-core shape uses exactly the plain plan.
 enum class PlanVariant { kPlain, kNormed, kPaged };
 
-// n_queries: query tokens per sequence (1 for single-token decode); they act as H * n_queries virtual heads.
-bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_queries = 1,
-                PlanVariant variant = PlanVariant::kPlain) {
+bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVariant variant = PlanVariant::kPlain) {
     using namespace lrkv;
     SplitPlan p{};
-    p.n_queries = n_queries;
     if (variant != PlanVariant::kPlain) {
         SplitPlan plain;
-        if (n_queries != 1 || !plan_split(d, max_len, &plain)) return false;
+        if (!plan_split(d, max_len, &plain)) return false;
         if (variant == PlanVariant::kPaged && plain.path != SplitPath::kMfmaF32) {
             *out = plain;
             return true;
@@ -122,13 +119,13 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_que
         *out = p;
         return true;
     }
-    if (n_queries == 1 && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+    if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
         p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
-    } else if (n_queries == 1 && mfma_f32_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+    } else if (mfma_f32_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaF32;
         p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
-    } else if (general_path_supports(d.H * n_queries, d.d_h, d.r)) {
+    } else if (general_path_supports(d.H, d.d_h, d.r)) {
         p.path = SplitPath::kGeneral;
         p.occupancy = 1;
     } else {
@@ -151,24 +148,23 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, int n_que
     G = std::min<long>(G, (long)d.batch * tiles_per_seq);
     G = std::max<long>(G, d.batch);
     // the merge kernel addresses the workspace with 32-bit offsets
-    if ((long long)G * d.H * n_queries * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31)) return false;
+    if ((long long)G * d.H * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31)) return false;
     p.num_splits = (int)G;
     *out = p;
     return true;
 }
 
 size_t workspace_bytes(const lrkv_dims& d, const lrkv::SplitPlan& p) {
-    return sizeof(float) * (size_t)p.num_splits * (size_t)d.H * (size_t)p.n_queries *
+    return sizeof(float) * (size_t)p.num_splits * (size_t)d.H *
            (size_t)lrkv::partial_record_floats(d.d_h, d.r);
 }
 
-lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan, int n_queries = 1,
+lrkv_status check_decode_common(const lrkv_dims* dims, int32_t max_len, lrkv::SplitPlan* plan,
                                 PlanVariant variant = PlanVariant::kPlain) {
     LRKV_TRY(check_dims(dims));
     if (max_len < 0 || max_len > dims->L_cap)
         return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
-    if (n_queries < 1 || n_queries > 64) return fail(LRKV_ERR_INVALID_ARG, "n_queries=%d outside [1, 64]", n_queries);
-    if (!plan_split(*dims, max_len, plan, n_queries, variant))
+    if (!plan_split(*dims, max_len, plan, variant))
         return fail(LRKV_ERR_UNSUPPORTED, "no kernel for H=%d d_h=%d r=%d dtype=%d", dims->H, dims->d_h, dims->r,
                     dims->dtype);
     return LRKV_OK;
@@ -190,7 +186,7 @@ struct PagedView {  // the paged layout of a cache handed to run_partial (block_
 
 lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, const void* q, const float* p,
                         void* ws, const lrkv::SplitPlan& plan, hipStream_t stream, const void* rho = nullptr,
-                        const PagedView& pv = PagedView()) {
+                        const PagedView& pv = PagedView(), int qgroup = 1) {
     using namespace lrkv;
     if (plan.num_splits == 0) return LRKV_OK;
     DecodeArgs a{};
@@ -203,7 +199,7 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.max_len = max_len;
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
-    a.n_queries = plan.n_queries;
+    a.qgroup = qgroup;
     a.k_shared = c.k_shared;
     a.v_shared = c.v_shared;
     a.z_k = c.z_k;
@@ -329,7 +325,7 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
     LRKV_TRY(need_ptr(out, "out"));
     if (dims->r > 0) LRKV_TRY(need_ptr(B_v, "B_v"));
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -350,25 +346,58 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Multi-token decode runs as single-token decode of batch * Q virtual sequences: query i of sequence b is
+// virtual sequence b * Q + i, which reads sequence b's cache up to its causal length seq_lens[b] - Q + 1 + i.
+// The workspace holds the plan's partial records, then the virtual lengths (256-byte aligned parts).
+struct MultiPlan {
+    lrkv_dims dq;         // dims of the virtual batch
+    lrkv::SplitPlan plan;
+    size_t records_bytes, total_bytes;
+};
+
+bool plan_multi(const lrkv_dims& d, int Q, int max_len, MultiPlan* mp) {
+    if (Q < 1 || Q > 64 || (long long)d.batch * Q > 65535) return false;
+    mp->dq = d;
+    mp->dq.batch = d.batch * Q;
+    if (!plan_split(mp->dq, max_len, &mp->plan)) return false;
+    mp->records_bytes = (workspace_bytes(mp->dq, mp->plan) + 255) & ~(size_t)255;
+    mp->total_bytes = mp->records_bytes + (((size_t)mp->dq.batch * sizeof(int32_t) + 255) & ~(size_t)255);
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t lrkv_decode_multi_workspace_bytes(const lrkv_dims* dims, int32_t n_queries, int32_t max_len) {
-    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap || n_queries < 1 || n_queries > 64) return 0;
-    lrkv::SplitPlan p;
-    if (!plan_split(*dims, max_len, &p, n_queries)) return 0;
-    return workspace_bytes(*dims, p);
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap) return 0;
+    MultiPlan mp;
+    if (!plan_multi(*dims, n_queries, max_len, &mp)) return 0;
+    return mp.total_bytes;
 }
 
 lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lrkv_cache* cache, int32_t max_len,
                               const void* q, const float* p, const void* B_v, float* out, void* workspace,
                               size_t workspace_bytes_, void* stream) {
-    lrkv::SplitPlan plan;
-    LRKV_TRY(check_decode_common(dims, max_len, &plan, n_queries));
+    LRKV_TRY(check_dims(dims));
+    if (max_len < 0 || max_len > dims->L_cap)
+        return fail(LRKV_ERR_INVALID_ARG, "max_len=%d outside [0, L_cap=%d]", max_len, dims->L_cap);
+    if (n_queries < 1 || n_queries > 64) return fail(LRKV_ERR_INVALID_ARG, "n_queries=%d outside [1, 64]", n_queries);
+    MultiPlan mp;
+    if (!plan_multi(*dims, n_queries, max_len, &mp))
+        return fail(LRKV_ERR_UNSUPPORTED, "no kernel for batch*Q=%lld H=%d d_h=%d r=%d dtype=%d",
+                    (long long)dims->batch * n_queries, dims->H, dims->d_h, dims->r, dims->dtype);
     LRKV_TRY(check_cache(*dims, cache, true));
     LRKV_TRY(need_ptr(q, "q"));
     LRKV_TRY(need_ptr(out, "out"));
@@ -376,11 +405,18 @@ lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lr
         LRKV_TRY(need_ptr(p, "p"));
         LRKV_TRY(need_ptr(B_v, "B_v"));
     }
-    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
-    LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, n_queries, dims->d_h, dims->r, dims->dtype, max_len,
-                                      plan.chunk, plan.num_splits, cache->seq_lens, B_v, out,
-                                      (const float*)workspace, (hipStream_t)stream);
+    if (!workspace) return fail(LRKV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", mp.total_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(LRKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (workspace_bytes_ < mp.total_bytes)
+        return fail(LRKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes_, mp.total_bytes);
+    int32_t* vlens = (int32_t*)((char*)workspace + mp.records_bytes);
+    hipError_t e = lrkv::launch_multi_lengths(dims->batch, n_queries, cache->seq_lens, vlens, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "length kernel launch");
+    const lrkv_cache vc{cache->k_shared, cache->v_shared, cache->z_k, cache->z_v, vlens};
+    LRKV_TRY(run_partial(mp.dq, vc, max_len, q, p, workspace, mp.plan, (hipStream_t)stream, nullptr, PagedView(),
+                         n_queries));
+    e = lrkv::launch_merge(mp.dq.batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, mp.plan.chunk,
+                           mp.plan.num_splits, vlens, B_v, out, (const float*)workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ok();
 }
@@ -425,7 +461,7 @@ lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, c
                                const void* q_eff, const float* p, const void* B_v, float* out, void* workspace,
                                size_t workspace_bytes_, void* stream) {
     lrkv::SplitPlan plan;
-    LRKV_TRY(check_decode_common(dims, max_len, &plan, 1, PlanVariant::kNormed));
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, PlanVariant::kNormed));
     LRKV_TRY(check_cache(*dims, cache, true));
     LRKV_TRY(need_ptr(rho, "rho"));
     LRKV_TRY(need_ptr(q_eff, "q_eff"));
@@ -436,7 +472,7 @@ lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, c
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q_eff, p, workspace, plan, (hipStream_t)stream, rho));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -509,7 +545,7 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
                               const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes_,
                               void* stream) {
     lrkv::SplitPlan plan;
-    LRKV_TRY(check_decode_common(dims, max_len, &plan, 1, PlanVariant::kPaged));
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, PlanVariant::kPaged));
     PagedView pv;
     LRKV_TRY(check_paged(*dims, cache, &pv));
     LRKV_TRY(need_ptr(q, "q"));
@@ -521,7 +557,7 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     const lrkv_cache pools{cache->k_pages, cache->v_pages, cache->zk_pages, cache->zv_pages, cache->seq_lens};
     LRKV_TRY(run_partial(*dims, pools, max_len, q, p, workspace, plan, (hipStream_t)stream, nullptr, pv));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, 1, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");

@@ -14,7 +14,8 @@ struct DecodeArgs {
     int max_len;         // host bound of seq_lens
     int chunk;           // split granule in rows: split s holds live rows iff s * chunk < L_b
     int num_splits;      // G: workgroups of the launch = partial records per head (shared by the batch)
-    int n_queries;       // Q query tokens per sequence (the last Q tokens; causal inside the chunk)
+    int qgroup;          // virtual sequences per cached sequence: sequence b reads cache sequence b / qgroup
+                         // (multi-token decode: one virtual sequence per query token, with its causal length)
     const void* k_shared;
     const void* v_shared;
     const void* z_k;
@@ -23,7 +24,7 @@ struct DecodeArgs {
     const void* q;
     const float* p;
     const void* rho;     // normalised variant: scales [batch][L_cap][H] (cache dtype) multiplying the logits; else NULL
-    float* ws;           // [G][H * Q][record]
+    float* ws;           // [G][H][record]
     // paged cache (block_table set): the four cache pointers are page pools [n_pages][page_rows][...] and
     // logical row t of sequence b is pool row block_table[b * max_pages + (t >> page_shift)] * page_rows
     // + (t & (page_rows - 1)); block_table NULL: contiguous [batch][L_cap][...]
@@ -47,7 +48,6 @@ struct SplitPlan {
     int chunk;       // split granule in rows (the kernel's tile: rows a split advances per step)
     int num_splits;  // G: workgroups for the whole batch, dealt to sequences by length on the device
     int occupancy;   // MFMA kernels: waves per SIMD they are compiled for (1 or 2)
-    int n_queries;   // Q query tokens per sequence
 };
 
 bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);      // bf16 MFMA kernel
@@ -65,7 +65,7 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
-hipError_t launch_merge(int batch, int H, int n_queries, int d_h, int r, int dtype, int max_len, int chunk,
+hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk,
                         int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
                         hipStream_t stream);
 int general_rows_per_tile();  // rows one general-kernel split advances per step
@@ -76,6 +76,8 @@ hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int d
                               const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
                               const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
                               hipStream_t stream);
+// lens_out[b * Q + i] = max(0, seq_lens[b] - Q + 1 + i): the rows query token i of sequence b sees
+hipError_t launch_multi_lengths(int batch, int Q, const int32_t* seq_lens, int32_t* lens_out, hipStream_t stream);
 hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int page_shift, int max_pages,
                               void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
                               const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,

@@ -207,3 +207,19 @@ def test_split_plan_arithmetic():
     d = lk.make_dims(2, 8, 64, 8, 256, 1)
     assert lk.lrkv_decode_num_splits(d, 0) == (0, 0)
     assert lk.lrkv_decode_workspace_bytes(d, 0) == 0
+
+
+def test_multi_query_plan_arithmetic():
+    """Multi-token decode plans batch * Q virtual sequences: the single-token plan of that batch, then the
+    virtual lengths, each part 256-byte aligned."""
+    al = lambda n: (n + 255) // 256 * 256
+    for (B, H, d_h, r, L, dt, Q) in [(4, 32, 128, 64, 33024, 1, 4), (4, 32, 128, 64, 33024, 1, 16),
+                                     (2, 4, 16, 4, 128, 0, 3), (3, 8, 64, 16, 512, 1, 1)]:
+        d = lk.make_dims(B, H, d_h, r, L, dt)
+        dq = lk.make_dims(B * Q, H, d_h, r, L, dt)
+        want = al(lk.lrkv_decode_workspace_bytes(dq, L)) + al(4 * B * Q)
+        assert lk.lrkv_decode_multi_workspace_bytes(d, Q, L) == want
+    d = lk.make_dims(4, 32, 128, 64, 33024, 1)
+    assert lk.lrkv_decode_multi_workspace_bytes(d, 0, 100) == 0
+    assert lk.lrkv_decode_multi_workspace_bytes(d, 65, 100) == 0
+    assert lk.lrkv_decode_multi_workspace_bytes(lk.make_dims(2048, 8, 64, 8, 256, 1), 64, 100) == 0  # > 65535

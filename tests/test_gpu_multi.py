@@ -60,6 +60,10 @@ CASES = [  # (dtype, batch, Q, H, d_h, r, lengths)
     ("bf16", 2, 3, 32, 128, 64, [700, 2]),
     ("f32", 2, 2, 32, 128, 0, [129, 31]),
     ("bf16", 4, 8, 8, 64, 8, [40, 8, 7, 100]),
+    ("bf16", 2, 16, 32, 128, 64, [1000, 5]),   # a sequence shorter than Q: its first queries see nothing
+    ("bf16", 4, 8, 32, 128, 64, [2100, 1500, 17, 8]),
+    ("bf16", 2, 64, 8, 64, 16, [200, 64]),
+    ("bf16", 3, 4, 16, 128, 0, [333, 40, 4]),
 ]
 
 
@@ -102,3 +106,29 @@ def test_single_query_through_multi_equals_decode():
     lk.lrkv_decode(dims, cache_of(dev, w.r), 500, qh, p, dev["B_v"], out, ws, nbytes)
     torch.cuda.synchronize()
     assert torch.equal(got, out)
+
+
+@pytest.mark.timeout(600)
+def test_multi_query_long_context_full_size():
+    """The long-context workload (batch 4, H 32, d_h 128, r 64, bf16) with Q = 4 query tokens per sequence in
+    the benchmark's launch configuration; the first and last sequence are checked in full against the
+    reference."""
+    import bench
+    Q = 4
+    w0 = synth.WORKLOADS["long_context"]
+    L_cap, max_len = bench.launch_config(w0, 50 * Q)
+    w = w0.with_(L_cap=L_cap)
+    lens = synth.seq_lengths(w)
+    say(f"[case] multi-query long context Q={Q} L_cap={L_cap}")
+    dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens)
+    qh = synth.normal(9200, 1.0, w.batch * Q * w.H * w.d_h, "bf16").reshape(w.batch, Q, w.H, w.d_h)
+    got = _multi_gpu(w, dev, Q, qh, max_len).cpu().numpy()
+    Bk, Bv = synth.gen_small(w, 0, "B_k"), synth.gen_small(w, 0, "B_v")
+    for b in (0, w.batch - 1):
+        n = int(lens[b])
+        sq = synth.gen_sequence(w, 0, b, n)
+        ref = oracle.lrkv_decode_multi("bf16", qh[b:b + 1], sq["k_shared"][None], sq["v_shared"][None],
+                                       sq["z_k"][None], sq["z_v"][None], Bk, Bv, np.array([n], dtype=np.int32))
+        err = oracle.relative_error(got[b].reshape(-1, w.d_h), ref[0].reshape(-1, w.d_h))
+        say(f"  seq {b}: max rel err {err:.3e} over {Q * w.H} (query, head) rows (tol {TOL['bf16']:.0e})")
+        assert err <= TOL["bf16"]
