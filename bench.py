@@ -134,6 +134,9 @@ def main():
                     help="paged cache: the rows in PAGE_ROWS-row pages of a shuffled pool (power of two >= 32; the "
                          "capacity is rounded up to whole pages); each step appends through the block table and "
                          "runs lrkv_decode_paged")
+    ap.add_argument("--rope", action="store_true",
+                    help="rotary variant: each step appends a row and runs lrkv_decode_rope (every head's key "
+                         "rebuilt and turned at its position)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -152,8 +155,8 @@ def main():
               f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
         sys.exit(2)
 
-    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0]) > 1:
-        print("bench.py: --queries, --layer, --norm and --paged do not combine", file=sys.stderr)
+    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0, args.rope]) > 1:
+        print("bench.py: --queries, --layer, --norm, --paged and --rope do not combine", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -219,6 +222,9 @@ def main():
             pools[name] = pool
         pcache = lk.make_paged_cache(pools["k_shared"], pools["v_shared"], pools.get("z_k"), pools.get("z_v"), table,
                                      dev["seq_lens"], P, maxp, n_pages)
+    if args.rope:
+        rope_cs = torch.empty((L_cap, w.d_h // 2, 2), dtype=torch.float32, device="cuda")
+        lk.lrkv_rope_table(w.d_h, L_cap, 10000.0, rope_cs)
     stream = torch.cuda.current_stream()
     pp = p if w.r else None
     bv = dev["B_v"] if w.r else None
@@ -277,9 +283,20 @@ def main():
         if timed:
             ev_pairs.append((e0, ev()))
 
+    def step_rope(timed: bool):
+        lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+        if timed:
+            e0 = ev()
+        lk.lrkv_decode_rope(dims, cache, max_len, dev["q"], dev["B_k"] if w.r else None, rope_cs, bv, out, ws,
+                            nbytes, stream)
+        if timed:
+            ev_pairs.append((e0, ev()))
+
     def step(timed: bool):
         if Q > 1:
             return step_multi(timed)
+        if args.rope:
+            return step_rope(timed)
         if args.paged:
             return step_paged(timed)
         if args.norm:
@@ -342,14 +359,17 @@ def main():
         step_bytes += sum(rho_bytes) / K
     if args.paged:  # the block table entries of the live pages
         split_bytes += w.batch * ((int(lens_full.max()) + K + args.paged - 1) // args.paged) * 4
-    if Q > 1 or args.norm or args.paged:  # the timed call is the whole decode: split pass, merge and epilogue
+    if args.rope:  # the rotation table rows of the live positions (no absorbed query is read)
+        split_bytes += int(lens_full.max() + K) * w.d_h * 4 - p_bytes
+    if Q > 1 or args.norm or args.paged or args.rope:  # the timed call is the whole decode (split + merge)
         split_bytes += out_bytes + w.H * w.d_h * w.r * s_bytes
     split_avg_ms = sum(split_ms) / len(split_ms)
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = read_traffic(w.name, split_bytes) if not (args.layer or args.norm or args.paged) and Q == 1 else None
+    traffic = (read_traffic(w.name, split_bytes)
+               if not (args.layer or args.norm or args.paged or args.rope) and Q == 1 else None)
     layer = None
     if args.layer:
         assert bool(torch.isfinite(y_step).all())
@@ -367,7 +387,8 @@ def main():
         log(f"bench: layer step: project+append {proj_us:.1f} us ({layer['project_weight_gbps']:.0f} GB/s of "
             f"weights), output projection {outp_us:.1f} us ({layer['output_weight_gbps']:.0f} GB/s)")
     log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step); "
-        f"{'split pass' if Q == 1 and not (args.norm or args.paged) else 'whole decode call'} {split_avg_ms * 1e3:.1f} us "
+        f"{'split pass' if Q == 1 and not (args.norm or args.paged or args.rope) else 'whole decode call'} "
+        f"{split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
     cpu = None
@@ -390,7 +411,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else "") + ("+normalised" if args.norm else "")
-                   + (f"+paged{args.paged}" if args.paged else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+                   + (f"+paged{args.paged}" if args.paged else "") + ("+rope" if args.rope else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
                    "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q},
@@ -400,7 +421,8 @@ def main():
                      "frac": split_gbps / HBM_PEAK_GBPS,
                      "traffic": traffic, "kernel": "lrkv_decode_multi (split pass + merge)" if Q > 1 else
                      "lrkv_decode_normed (split pass + merge)" if args.norm else
-                     "lrkv_decode_paged (split pass + merge)" if args.paged else "split pass (lrkv_decode_partial)",
+                     "lrkv_decode_paged (split pass + merge)" if args.paged else
+                     "lrkv_decode_rope (split pass + merge)" if args.rope else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
         "mfma_util_shared_score": mfma_util,
         "layer_step": layer,

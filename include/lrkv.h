@@ -266,6 +266,33 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
                               const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Rotary variant: rotary position embedding applied exactly on the factored
+ * cache (review sec. 8, "Full RoPE needs a stronger identity"; reading notes
+ * sec. 2.7).  A rotation cannot be moved into the rank-r latent for a generic
+ * B_k, so the cache keeps every factor unrotated and the decode turns each
+ * head's whole key at its own position:
+ *   ktilde_{h,j} = (k_shared[j] + z_k[j][h] (B_k[h])^T) D_j,   qtilde = q D_{L_b - 1}
+ *   s_j = qtilde . ktilde_{h,j} / sqrt(d_h),  a = softmax(s),  values as in lrkv_decode (not rotated)
+ * D_t turns coordinate pair k = (2k, 2k+1) by t * theta_k, theta_k = base^(-2k/d_h):
+ *   (x_2k, x_2k+1) -> (x_2k cos - x_2k+1 sin, x_2k sin + x_2k+1 cos).
+ * Row j of a sequence sits at position j; the query is its last row. */
+
+/* table[t][k] = (cos, sin)(t * theta_k), t < n_pos, k < d_h / 2: device
+ * [n_pos][d_h / 2][2] fp32, the angle and both values computed in fp64. */
+lrkv_status lrkv_rope_table(int32_t d_h, int32_t n_pos, float base, float* table, void* stream);
+
+/* Decode under the rotary variant.  Arguments as lrkv_decode, except:
+ *   q      device [batch][H][d_h], unrotated (the kernel turns it at position seq_lens[b] - 1)
+ *   B_k    device [H][d_h][r] (the keys are rebuilt; no absorbed query is used); NULL iff r == 0
+ *   table  lrkv_rope_table output with n_pos >= max_len
+ * Workspace: lrkv_decode_workspace_bytes(dims, max_len).  d_h must be a
+ * multiple of 4.  The key of every (row, head) is rebuilt, turned and dotted
+ * in fp32: d_h * r extra multiply-adds per row and head, the cost the review
+ * names for the exact contraction. */
+lrkv_status lrkv_decode_rope(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                             const void* B_k, const float* table, const void* B_v, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Rebuild every head's keys and values from the factored cache (reading notes
  * sec. 2.1 Eqs. (2)-(5); review sec. 3, the materialised form training and
  * prefill use):

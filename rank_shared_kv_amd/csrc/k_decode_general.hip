@@ -25,15 +25,16 @@ namespace {
 constexpr int kTile = 32;     // tokens per tile (lanes 0..31 and 32..63 split each dot product)
 constexpr int kThreads = 256;  // 4 waves
 
-__host__ __device__ inline size_t general_lds_floats(int H, int d_h, int r) {
+__host__ __device__ inline size_t general_lds_floats(int H, int d_h, int r, bool rope) {
     return (size_t)kTile * (d_h + 1)      // K tile, padded rows
            + (size_t)kTile * d_h          // V tile
            + (size_t)H * (d_h + r)        // numerators
            + 2 * (size_t)H                // running max, denominator
-           + 4 * (size_t)kTile;           // per-wave weights
+           + 4 * (size_t)kTile            // per-wave weights
+           + (rope ? (size_t)H * d_h : 0);  // rotated queries
 }
 
-template <typename T>
+template <typename T, bool ROPE>
 __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     extern __shared__ float smem[];
     const int H = a.H, D = a.d_h, R = a.r, rec = partial_record_floats(D, R);
@@ -43,6 +44,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     float* mrow = acc + (size_t)H * (D + R);   // [H]
     float* lrow = mrow + H;                    // [H]
     float* ebuf = lrow + H;                    // [4][kTile]
+    float* qrot = ebuf + 4 * kTile;            // [H][D] rotated queries (rotary variant)
 
     // which sequence and split (splits dealt to sequences by length); split s of sequence b takes the
     // tiles s, s + S_b, s + 2 S_b, ... of the sequence
@@ -62,6 +64,18 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float scale = kLog2e / sqrtf((float)D);
 
+    if constexpr (ROPE) {
+        // the query sits at position L_b - 1: q D_{L_b - 1}, pair by pair, in fp32
+        const float* cs = a.rope_cs + (size_t)(Lb - 1) * D;
+        for (int idx = tid; idx < H * (D / 2); idx += kThreads) {
+            const int h = idx / (D / 2), k = idx - h * (D / 2);
+            const float x0 = elem<T>::load(q, ((size_t)b * H + h) * D + 2 * k);
+            const float x1 = elem<T>::load(q, ((size_t)b * H + h) * D + 2 * k + 1);
+            const float co = cs[2 * k], si = cs[2 * k + 1];
+            qrot[h * D + 2 * k] = x0 * co - x1 * si;
+            qrot[h * D + 2 * k + 1] = x0 * si + x1 * co;
+        }
+    }
     for (int i = tid; i < H * (D + R); i += kThreads) acc[i] = 0.f;
     for (int i = tid; i < H; i += kThreads) {
         mrow[i] = -INFINITY;
@@ -92,8 +106,27 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
             const size_t zrow = ((r0 + (size_t)(live ? t : 0)) * H + h) * R;
             // score: shared part on the LDS tile, private part on the latent row
             float sc = 0.f;
-            for (int c = c_lo; c < c_hi; ++c) sc = fmaf(elem<T>::load(q, bh * D + c), Kt[t * (D + 1) + c], sc);
-            for (int i = i_lo; i < i_hi; ++i) sc = fmaf(a.p[bh * R + i], elem<T>::load(zk, zrow + i), sc);
+            if constexpr (ROPE) {
+                // rotary variant: rebuild the key's columns of this half (shared row + latent times B^K_h),
+                // turn each pair at the row's position, dot with the rotated query (the halves hold whole
+                // pairs: d_h is a multiple of 4)
+                const T* bkh = (const T*)a.rope_bk + (size_t)h * D * R;
+                const float* cs = a.rope_cs + (size_t)(t0 + (live ? t : 0)) * D;
+                for (int c = c_lo; c < c_hi; c += 2) {
+                    float u0 = Kt[t * (D + 1) + c], u1 = Kt[t * (D + 1) + c + 1];
+                    for (int i = 0; i < R; ++i) {
+                        const float z = elem<T>::load(zk, zrow + i);
+                        u0 = fmaf(z, elem<T>::load(bkh, (size_t)c * R + i), u0);
+                        u1 = fmaf(z, elem<T>::load(bkh, (size_t)(c + 1) * R + i), u1);
+                    }
+                    const float co = cs[c], si = cs[c + 1];
+                    sc = fmaf(qrot[h * D + c], u0 * co - u1 * si, sc);
+                    sc = fmaf(qrot[h * D + c + 1], u0 * si + u1 * co, sc);
+                }
+            } else {
+                for (int c = c_lo; c < c_hi; ++c) sc = fmaf(elem<T>::load(q, bh * D + c), Kt[t * (D + 1) + c], sc);
+                for (int i = i_lo; i < i_hi; ++i) sc = fmaf(a.p[bh * R + i], elem<T>::load(zk, zrow + i), sc);
+            }
             sc += __shfl_xor(sc, 32);
             // normalised variant: the cached scale of (row, head) multiplies the summed logit
             float f = scale;
@@ -145,24 +178,27 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
 
 int general_rows_per_tile() { return kTile; }
 
-size_t general_lds_bytes(int H, int d_h, int r) { return general_lds_floats(H, d_h, r) * sizeof(float); }
+size_t general_lds_bytes(int H, int d_h, int r, bool rope) { return general_lds_floats(H, d_h, r, rope) * sizeof(float); }
 
 // gfx950 gives a workgroup up to 160 KiB of LDS
 bool general_path_supports(int H, int d_h, int r) {
     return d_h >= 1 && d_h <= 256 && r >= 0 && r <= 256 && H >= 1 && general_lds_bytes(H, d_h, r) <= 160 * 1024;
 }
 
-hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream) {
-    dim3 grid(a.num_splits), block(kThreads);
-    const size_t lds = general_lds_bytes(a.H, a.d_h, a.r);
-    const void* kern = (a.dtype == 0) ? (const void*)split_general_kernel<float> : (const void*)split_general_kernel<uint16_t>;
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+template <typename T, bool ROPE>
+hipError_t launch_general_t(const DecodeArgs& a, hipStream_t stream) {
+    const size_t lds = general_lds_bytes(a.H, a.d_h, a.r, ROPE);
+    auto kern = split_general_kernel<T, ROPE>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (a.dtype == 0)
-        hipLaunchKernelGGL(split_general_kernel<float>, grid, block, lds, stream, a);
-    else
-        hipLaunchKernelGGL(split_general_kernel<uint16_t>, grid, block, lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
+}
+
+hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream) {
+    const bool rope = a.rope_cs != nullptr;
+    if (a.dtype == 0) return rope ? launch_general_t<float, true>(a, stream) : launch_general_t<float, false>(a, stream);
+    return rope ? launch_general_t<uint16_t, true>(a, stream) : launch_general_t<uint16_t, false>(a, stream);
 }
 
 }  // namespace lrkv

@@ -90,7 +90,7 @@ constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's 
 // SIMD; neither it nor the paged cache has an fp32 matrix-core kernel (the general kernel serves them).  Their
 // G never exceeds the plain plan's, so the plain workspace size serves every variant, and a paged decode of a
 // bf16 matrix-core shape uses exactly the plain plan.
-enum class PlanVariant { kPlain, kNormed, kPaged };
+enum class PlanVariant { kPlain, kNormed, kPaged, kRope };
 
 bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVariant variant = PlanVariant::kPlain) {
     using namespace lrkv;
@@ -102,10 +102,12 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
             *out = plain;
             return true;
         }
-        if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+        if (variant != PlanVariant::kRope && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
             p.path = SplitPath::kMfmaBf16;
             p.chunk = mfma_rows_per_tile(d.H);
-        } else if (general_path_supports(d.H, d.d_h, d.r)) {
+        } else if (variant == PlanVariant::kRope ? general_lds_bytes(d.H, d.d_h, d.r, true) <= 160 * 1024 &&
+                                                       general_path_supports(d.H, d.d_h, d.r)
+                                                 : general_path_supports(d.H, d.d_h, d.r)) {
             p.path = SplitPath::kGeneral;
             p.chunk = general_rows_per_tile();
         } else {
@@ -186,7 +188,8 @@ struct PagedView {  // the paged layout of a cache handed to run_partial (block_
 
 lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, const void* q, const float* p,
                         void* ws, const lrkv::SplitPlan& plan, hipStream_t stream, const void* rho = nullptr,
-                        const PagedView& pv = PagedView(), int qgroup = 1) {
+                        const PagedView& pv = PagedView(), int qgroup = 1, const float* rope_cs = nullptr,
+                        const void* rope_bk = nullptr) {
     using namespace lrkv;
     if (plan.num_splits == 0) return LRKV_OK;
     DecodeArgs a{};
@@ -209,6 +212,8 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.p = p;
     a.rho = rho;
     a.ws = (float*)ws;
+    a.rope_cs = rope_cs;
+    a.rope_bk = rope_bk;
     a.block_table = pv.block_table;
     a.page_shift = pv.page_shift;
     a.max_pages = pv.max_pages;
@@ -557,6 +562,41 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     const lrkv_cache pools{cache->k_pages, cache->v_pages, cache->zk_pages, cache->zv_pages, cache->seq_lens};
     LRKV_TRY(run_partial(*dims, pools, max_len, q, p, workspace, plan, (hipStream_t)stream, nullptr, pv));
+    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                                      plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
+                                      (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_rope_table(int32_t d_h, int32_t n_pos, float base, float* table, void* stream) {
+    if (d_h < 2 || d_h > 4096 || (d_h & 1)) return fail(LRKV_ERR_INVALID_ARG, "d_h=%d must be even, 2..4096", d_h);
+    if (n_pos < 0 || n_pos > (1 << 28)) return fail(LRKV_ERR_INVALID_ARG, "n_pos=%d outside [0, 2^28]", n_pos);
+    if (!(base > 1.f) || base > 3.0e38f) return fail(LRKV_ERR_INVALID_ARG, "base must be finite and > 1");
+    LRKV_TRY(need_ptr(table, "table"));
+    hipError_t e = lrkv::launch_rope_table(d_h, n_pos, base, table, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "rotary table kernel launch");
+    return ok();
+}
+
+lrkv_status lrkv_decode_rope(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                             const void* B_k, const float* table, const void* B_v, float* out, void* workspace,
+                             size_t workspace_bytes_, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (dims->d_h % 4 != 0) return fail(LRKV_ERR_UNSUPPORTED, "rotary decode needs d_h a multiple of 4 (d_h=%d)", dims->d_h);
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan, PlanVariant::kRope));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(table, "table"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(B_k, "B_k"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
+    LRKV_TRY(run_partial(*dims, *cache, max_len, q, nullptr, workspace, plan, (hipStream_t)stream, nullptr,
+                         PagedView(), 1, table, B_k));
     hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);

@@ -30,6 +30,11 @@ struct DecodeArgs {
     // + (t & (page_rows - 1)); block_table NULL: contiguous [batch][L_cap][...]
     const int32_t* block_table;
     int page_shift, max_pages, n_pages;
+    // rotary variant (rope_cs set): every key k_s + z^K_h (B^K_h)^T is turned at its row position and the query
+    // at position L_b - 1; rope_cs holds (cos, sin) per position and coordinate pair [L_cap][d_h / 2][2], rope_bk
+    // is B^K [H][d_h][r]; p is not used
+    const float* rope_cs;
+    const void* rope_bk;
 };
 
 // pool row of logical row t of sequence b (t uniform across the caller's wave)
@@ -55,7 +60,7 @@ bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap);  // fp
 int mfma_f32_rows_per_tile();  // rows one fp32 MFMA-kernel split advances per step
 int mfma_rows_per_tile(int H);  // rows one MFMA-kernel workgroup advances per step
 bool general_path_supports(int H, int d_h, int r);
-size_t general_lds_bytes(int H, int d_h, int r);
+size_t general_lds_bytes(int H, int d_h, int r, bool rope = false);
 
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
                          hipStream_t stream);
@@ -82,6 +87,7 @@ hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int 
                               void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
                               const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,
                               const void* zk_new, const void* zv_new, hipStream_t stream);
+hipError_t launch_rope_table(int d_h, int n_pos, float base, float* table, hipStream_t stream);
 hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, int n_last,
                              float eps, const int32_t* seq_lens, const void* k_shared, const void* z_k,
                              const void* B_k, void* rho, hipStream_t stream);
