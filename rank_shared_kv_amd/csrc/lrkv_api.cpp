@@ -102,7 +102,10 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
             *out = plain;
             return true;
         }
-        if (variant != PlanVariant::kRope && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+        if (variant == PlanVariant::kRope && rope_mfma_path_supports(d.H, d.d_h, d.r, d.dtype)) {
+            p.path = SplitPath::kRopeMfma;
+            p.chunk = rope_mfma_rows_per_tile();
+        } else if (variant != PlanVariant::kRope && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
             p.path = SplitPath::kMfmaBf16;
             p.chunk = mfma_rows_per_tile(d.H);
         } else if (variant == PlanVariant::kRope ? general_lds_bytes(d.H, d.d_h, d.r, true) <= 160 * 1024 &&
@@ -115,7 +118,7 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
         }
         p.occupancy = 1;
         const long tiles_per_seq = max_len > 0 ? (max_len + p.chunk - 1) / p.chunk : 0;
-        long G = std::min<long>(plain.num_splits, p.path == SplitPath::kGeneral ? 1024 : 256);
+        long G = std::min<long>(plain.num_splits, p.path == SplitPath::kGeneral ? 1024 : 256);  // one resident round
         G = std::min<long>(G, (long)d.batch * tiles_per_seq);
         p.num_splits = max_len > 0 ? (int)std::max<long>(G, d.batch) : 0;
         *out = p;
@@ -218,9 +221,10 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.page_shift = pv.page_shift;
     a.max_pages = pv.max_pages;
     a.n_pages = pv.n_pages;
-    hipError_t e = (plan.path == SplitPath::kMfmaBf16)  ? launch_split_mfma(a, plan.occupancy, stream)
-                   : (plan.path == SplitPath::kMfmaF32) ? launch_split_mfma_f32(a, plan.occupancy, stream)
-                                                         : launch_split_general(a, stream);
+    hipError_t e = (plan.path == SplitPath::kMfmaBf16)   ? launch_split_mfma(a, plan.occupancy, stream)
+                   : (plan.path == SplitPath::kMfmaF32)  ? launch_split_mfma_f32(a, plan.occupancy, stream)
+                   : (plan.path == SplitPath::kRopeMfma) ? launch_split_rope_mfma(a, stream)
+                                                          : launch_split_general(a, stream);
     if (e != hipSuccess) return hip_fail(e, "split kernel launch");
     return LRKV_OK;
 }

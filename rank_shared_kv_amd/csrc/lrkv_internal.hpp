@@ -44,7 +44,7 @@ __device__ __forceinline__ int paged_row(const DecodeArgs& a, int b, int t) {
 }
 
 // Which split kernel a problem uses.
-enum class SplitPath { kGeneral, kMfmaBf16, kMfmaF32 };
+enum class SplitPath { kGeneral, kMfmaBf16, kMfmaF32, kRopeMfma };
 
 // Decode split plan: pure host arithmetic (no device query), so workspace
 // sizes are known without a GPU.
@@ -60,6 +60,9 @@ bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap);  // fp
 int mfma_f32_rows_per_tile();  // rows one fp32 MFMA-kernel split advances per step
 int mfma_rows_per_tile(int H);  // rows one MFMA-kernel workgroup advances per step
 bool general_path_supports(int H, int d_h, int r);
+bool rope_mfma_path_supports(int H, int d_h, int r, int dtype);  // rotary variant, bf16 matrix-core kernel
+int rope_mfma_rows_per_tile();
+hipError_t launch_split_rope_mfma(const DecodeArgs& a, hipStream_t stream);
 size_t general_lds_bytes(int H, int d_h, int r, bool rope = false);
 
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
