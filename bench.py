@@ -225,6 +225,8 @@ def main():
     if args.rope:
         rope_cs = torch.empty((L_cap, w.d_h // 2, 2), dtype=torch.float32, device="cuda")
         lk.lrkv_rope_table(w.d_h, L_cap, 10000.0, rope_cs)
+        nbytes = lk.lrkv_decode_rope_workspace_bytes(dims, max_len)
+        ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     pp = p if w.r else None
     bv = dev["B_v"] if w.r else None

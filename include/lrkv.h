@@ -281,11 +281,16 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
  * [n_pos][d_h / 2][2] fp32, the angle and both values computed in fp64. */
 lrkv_status lrkv_rope_table(int32_t d_h, int32_t n_pos, float base, float* table, void* stream);
 
+/* Bytes of device workspace lrkv_decode_rope needs (its own plan: the
+ * matrix-core rotary kernel keeps two workgroups per CU).  Returns 0 for
+ * invalid dims or d_h not a multiple of 4.  Host arithmetic only. */
+size_t lrkv_decode_rope_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
+
 /* Decode under the rotary variant.  Arguments as lrkv_decode, except:
  *   q      device [batch][H][d_h], unrotated (the kernel turns it at position seq_lens[b] - 1)
  *   B_k    device [H][d_h][r] (the keys are rebuilt; no absorbed query is used); NULL iff r == 0
  *   table  lrkv_rope_table output with n_pos >= max_len
- * Workspace: lrkv_decode_workspace_bytes(dims, max_len).  d_h must be a
+ * Workspace: lrkv_decode_rope_workspace_bytes(dims, max_len).  d_h must be a
  * multiple of 4.  The key of every (row, head) is rebuilt, turned and dotted
  * in fp32: d_h * r extra multiply-adds per row and head, the cost the review
  * names for the exact contraction. */

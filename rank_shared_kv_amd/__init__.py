@@ -27,7 +27,8 @@ LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
-            "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table", "lrkv_decode_rope",
+            "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table", "lrkv_decode_rope_workspace_bytes",
+            "lrkv_decode_rope",
             "lrkv_key_scales", "lrkv_norm_query", "lrkv_decode_normed", "lrkv_materialize",
             "lrkv_project_append", "lrkv_output_project", "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "lrkv_paged_append": ([D, PC, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_paged": ([D, PC, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_rope_table": ([i32, i32, ctypes.c_float, vp, vp], ctypes.c_int),
+            "lrkv_decode_rope_workspace_bytes": ([D, i32], sz),
             "lrkv_decode_rope": ([D, C, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_key_scales": ([D, C, i32, i32, vp, ctypes.c_float, vp, vp], ctypes.c_int),
             "lrkv_norm_query": ([D, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int),
@@ -216,6 +218,10 @@ def lrkv_decode_paged(dims: Dims, cache: PagedCache, max_len: int, q, p, B_v, ou
 
 def lrkv_rope_table(d_h: int, n_pos: int, base: float, table, stream=None) -> None:
     _check(lib().lrkv_rope_table(d_h, n_pos, float(base), _ptr(table), _stream(stream)), "lrkv_rope_table")
+
+
+def lrkv_decode_rope_workspace_bytes(dims: Dims, max_len: int) -> int:
+    return int(lib().lrkv_decode_rope_workspace_bytes(ctypes.byref(dims), max_len))
 
 
 def lrkv_decode_rope(dims: Dims, cache: Cache, max_len: int, q, B_k, table, B_v, out, workspace, workspace_bytes: int,

@@ -10,8 +10,7 @@
 //
 // A workgroup of 4 waves owns one (sequence, split) and walks its 64-row
 // tiles (tile s, s + S_b, ... of the sequence).  Per tile:
-//   1. stage: shared key rows (bf16), their (cos, sin) rows (fp32) and the
-//      shared value rows (bf16) in LDS;
+//   1. stage: shared key rows (bf16) and their (cos, sin) rows (fp32) in LDS;
 //   2. scores: wave w takes heads w*HPW .. w*HPW + HPW - 1.  Per head it loads
 //      the B^K_h fragments once (the next head's are loaded while this one
 //      computes) and, per 16-row group, rebuilds the key 16 columns at a time,
@@ -23,8 +22,11 @@
 //   3. softmax: one wave per head, lanes = the tile's rows, online max and
 //      denominator in LDS;
 //   4. values: thread (head, g) of 8 groups accumulates the shared sum over
-//      columns g*d_h/8 .. and the private sum over latent coordinates g*r/8 ..
-//      from the LDS value tile and the latent rows.
+//      columns g*d_h/8 .. and the private sum over latent coordinates g*r/8 ..,
+//      reading value and latent rows 8 at a time (the lanes of a wave that
+//      read the same value columns share one access).
+// Two workgroups are resident per CU (LDS 75 KB, at most 256 registers per
+// lane), so one workgroup's barriers and load latency overlap the other's work.
 // The workgroup writes the usual partial record per head (running max in
 // log2 units, denominator, shared sum, private sum); the merge kernel combines
 // splits and applies B^V.
@@ -52,19 +54,24 @@ struct RopeCfg {
     static constexpr int SHC = D / 8;              // shared-value columns per thread
     static constexpr int PRC = R / 8;              // latent coordinates per thread
     static constexpr size_t lds_bytes(int H) {
-        return (size_t)kTileRows * KS_STRIDE * 2 + (size_t)kTileRows * CS_STRIDE * 4 + (size_t)kTileRows * D * 2 +
-               (size_t)H * D * 4 + (size_t)H * E_STRIDE * 4 + 3 * (size_t)H * 4;
+        return (size_t)kTileRows * KS_STRIDE * 2 + (size_t)kTileRows * CS_STRIDE * 4 + (size_t)H * D * 4 +
+               (size_t)H * E_STRIDE * 4 + 3 * (size_t)H * 4;
     }
 };
 
-constexpr int kBatchRows = 16;  // value-phase rows whose latent loads are issued together
+constexpr int kBatchRows = 8;  // value-phase rows whose value and latent loads are issued together
 
-// N consecutive bf16 latent coordinates (N = r / 8: 0, 1, 2, 4, 6 or 8), loaded with one instruction
+// N consecutive bf16 values (latent coordinates: N = r / 8 in {0, 1, 2, 4, 6, 8}; value columns: N = d_h / 8
+// in {8, 16}), loaded with as few instructions as their alignment allows
 template <int N>
 struct LatVec {
     uint32_t w[N > 1 ? (N + 1) / 2 : 1];
     __device__ __forceinline__ void load(const uint16_t* p) {
-        if constexpr (N == 8) {
+        if constexpr (N == 16) {
+            const u32x4_t v0 = *(const u32x4_t*)p, v1 = *(const u32x4_t*)(p + 8);
+            w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
+            w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2]; w[7] = v1[3];
+        } else if constexpr (N == 8) {
             const u32x4_t v = *(const u32x4_t*)p;
             w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
         } else if constexpr (N == 6) {
@@ -91,15 +98,14 @@ struct Frags {  // one head's B^K fragments and the latent fragments of the tile
 };
 
 template <int D, int R>
-__global__ void __launch_bounds__(kWaves * 64, 1) split_rope_mfma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kWaves * 64, 2) split_rope_mfma_kernel(DecodeArgs a) {
     using C = RopeCfg<D, R>;
     constexpr int CB = C::CB, NKS = C::NKS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int H = a.H;
     uint16_t* ks_l = (uint16_t*)lds;                                           // [64][D + 8]
     float* cs_l = (float*)(lds + (size_t)kTileRows * C::KS_STRIDE * 2);        // [64][D + 4]
-    uint16_t* v_l = (uint16_t*)((unsigned char*)cs_l + (size_t)kTileRows * C::CS_STRIDE * 4);  // [64][D]
-    float* qr_l = (float*)((unsigned char*)v_l + (size_t)kTileRows * D * 2);  // [H][D]
+    float* qr_l = (float*)((unsigned char*)cs_l + (size_t)kTileRows * C::CS_STRIDE * 4);  // [H][D]
     float* e_l = qr_l + (size_t)H * D;                                         // [H][64 + 4]
     float* m_l = e_l + (size_t)H * C::E_STRIDE;                                // [H] running max (log2 units)
     float* l_l = m_l + H;                                                      // [H] denominator
@@ -158,7 +164,6 @@ __global__ void __launch_bounds__(kWaves * 64, 1) split_rope_mfma_kernel(DecodeA
             const int r = idx / (D / 8), c8 = idx - r * (D / 8);
             const size_t row = (size_t)(t0 + min(r, nvalid - 1));
             *(u32x4_t*)(ks_l + r * C::KS_STRIDE + 8 * c8) = *(const u32x4_t*)(ksg + row * D + 8 * c8);
-            *(u32x4_t*)(v_l + r * D + 8 * c8) = *(const u32x4_t*)(vsg + row * D + 8 * c8);
         }
         for (int idx = tid; idx < kTileRows * (D / 4); idx += kWaves * 64) {
             const int r = idx / (D / 4), c4 = idx - r * (D / 4);
@@ -224,16 +229,10 @@ __global__ void __launch_bounds__(kWaves * 64, 1) split_rope_mfma_kernel(DecodeA
                 if (g4 == 0) e_l[(size_t)h * C::E_STRIDE + rl] = part;
             }
         };
-        if (h_first < h_end) {
-            Frags<D, R> fa, fb;
-            load_frags(fa, h_first);
-            for (int h = h_first; h < h_end; h += 2) {
-                if (h + 1 < h_end) load_frags(fb, h + 1);
-                score_head(fa, h);
-                if (h + 1 >= h_end) break;
-                if (h + 2 < h_end) load_frags(fa, h + 2);
-                score_head(fb, h + 1);
-            }
+        for (int h = h_first; h < h_end; ++h) {  // the other resident workgroup covers these loads' latency
+            Frags<D, R> f;
+            load_frags(f, h);
+            score_head(f, h);
         }
         __syncthreads();
 
@@ -273,22 +272,22 @@ __global__ void __launch_bounds__(kWaves * 64, 1) split_rope_mfma_kernel(DecodeA
             for (int j = 0; j < C::PRC; ++j) acc_pr[j] *= al;
             const float* eh = e_l + (size_t)hv * C::E_STRIDE;
             const uint16_t* zbase = zvg + ((size_t)t0 * H + hv) * R + gv * C::PRC;
+            const uint16_t* vbase = vsg + (size_t)t0 * D + gv * C::SHC;
             for (int r0 = 0; r0 < nvalid; r0 += kBatchRows) {
+                LatVec<C::SHC> vb[kBatchRows];
                 LatVec<C::PRC> zb[kBatchRows];
 #pragma unroll
-                for (int k = 0; k < kBatchRows; ++k) zb[k].load(zbase + (size_t)min(r0 + k, nvalid - 1) * H * R);
+                for (int k = 0; k < kBatchRows; ++k) {
+                    const size_t r = (size_t)min(r0 + k, nvalid - 1);
+                    vb[k].load(vbase + r * D);
+                    zb[k].load(zbase + r * H * R);
+                }
 #pragma unroll
                 for (int k = 0; k < kBatchRows; ++k) {
-                    const int r = r0 + k;
-                    if (r < nvalid) {
-                        const float e = eh[r];
-                        const uint16_t* vr = v_l + r * D + gv * C::SHC;
+                    if (r0 + k < nvalid) {
+                        const float e = eh[r0 + k];
 #pragma unroll
-                        for (int j = 0; j < C::SHC; j += 2) {
-                            const uint32_t w = *(const uint32_t*)(vr + j);
-                            acc_sh[j] = fmaf(e, bf16_lo(w), acc_sh[j]);
-                            acc_sh[j + 1] = fmaf(e, bf16_hi(w), acc_sh[j + 1]);
-                        }
+                        for (int j = 0; j < C::SHC; ++j) acc_sh[j] = fmaf(e, vb[k].at(j), acc_sh[j]);
 #pragma unroll
                         for (int j = 0; j < C::PRC; ++j) acc_pr[j] = fmaf(e, zb[k].at(j), acc_pr[j]);
                     }

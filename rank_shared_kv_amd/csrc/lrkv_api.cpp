@@ -88,8 +88,9 @@ constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's 
 
 // Which decode the plan is for.  The normalised variant's bf16 matrix-core kernel is built for one wave per
 // SIMD; neither it nor the paged cache has an fp32 matrix-core kernel (the general kernel serves them).  Their
-// G never exceeds the plain plan's, so the plain workspace size serves every variant, and a paged decode of a
-// bf16 matrix-core shape uses exactly the plain plan.
+// G never exceeds the plain plan's, so the plain workspace size serves them, and a paged decode of a bf16
+// matrix-core shape uses exactly the plain plan.  The rotary variant has kernels of its own (two resident
+// workgroups per CU for the bf16 one) and its own workspace query.
 enum class PlanVariant { kPlain, kNormed, kPaged, kRope };
 
 bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVariant variant = PlanVariant::kPlain) {
@@ -118,9 +119,13 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
         }
         p.occupancy = 1;
         const long tiles_per_seq = max_len > 0 ? (max_len + p.chunk - 1) / p.chunk : 0;
-        long G = std::min<long>(plain.num_splits, p.path == SplitPath::kGeneral ? 1024 : 256);  // one resident round
+        // one resident round of workgroups; capped by the plain plan except for the rotary variant
+        long G = p.path == SplitPath::kGeneral ? 1024 : p.path == SplitPath::kRopeMfma ? 512 : 256;
+        if (variant != PlanVariant::kRope) G = std::min<long>(plain.num_splits, G);
+        G = std::min<long>(G, (long)d.batch + kMaxExtraSplits);
         G = std::min<long>(G, (long)d.batch * tiles_per_seq);
         p.num_splits = max_len > 0 ? (int)std::max<long>(G, d.batch) : 0;
+        if ((long long)p.num_splits * d.H * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31)) return false;
         *out = p;
         return true;
     }
@@ -581,6 +586,13 @@ lrkv_status lrkv_rope_table(int32_t d_h, int32_t n_pos, float base, float* table
     hipError_t e = lrkv::launch_rope_table(d_h, n_pos, base, table, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "rotary table kernel launch");
     return ok();
+}
+
+size_t lrkv_decode_rope_workspace_bytes(const lrkv_dims* dims, int32_t max_len) {
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap || dims->d_h % 4 != 0) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p, PlanVariant::kRope)) return 0;
+    return workspace_bytes(*dims, p);
 }
 
 lrkv_status lrkv_decode_rope(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,

@@ -47,7 +47,7 @@ def test_rope_table(d_h, n_pos, base):
 def _run(w, dev, max_len, table):
     dims = dims_of(w)
     out = torch.full((w.batch, w.H, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
-    nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
+    nbytes = lk.lrkv_decode_rope_workspace_bytes(dims, max_len)
     ws = torch.empty(max(nbytes, 256) // 4 + 64, dtype=torch.float32, device="cuda")
     lk.lrkv_decode_rope(dims, cache_of(dev, w.r), max_len, dev["q"], dev["B_k"] if w.r else None, table,
                         dev["B_v"] if w.r else None, out, ws, nbytes)
