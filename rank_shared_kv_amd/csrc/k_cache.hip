@@ -8,7 +8,11 @@
 // append:  write one token's shared rows and per-head latents at index
 //          seq_lens[b] and advance seq_lens[b] (review sec. 3, Algorithm 1;
 //          reading notes sec. 2.3).  Latents are token-major, so one token's
-//          H x r latents land in one contiguous row.
+//          H x r latents land in one contiguous row.  With a block table the
+//          row goes to its pool page instead (paged cache).
+// multi-token lengths: query i of Q at the end of sequence b sees
+//          max(0, L_b - Q + 1 + i) rows (the causal mask inside the chunk);
+//          the multi-token decode runs one virtual sequence per query token.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
 
