@@ -50,7 +50,7 @@ struct CfgF32 {
     static constexpr int VP = D / 64;                 // 64-column blocks of a value row
     static constexpr int UDW = D / 8;                 // dwords per unit (a quarter of the key or value rows)
     static constexpr int NU = 8;                      // units per block: 4 key quarters, then 4 value quarters
-    static constexpr int NSLOT = 8;                   // ring depth (divides NU)
+    static constexpr int NSLOT = OCC == 2 ? 4 : 8;    // ring depth (divides NU); two waves per SIMD hide latency too
     static constexpr int CB = D / 16;                 // column blocks of the value product
     static constexpr int QS = D + 4;                  // floats per q row in LDS
     static constexpr int REC = ((D + 2) + 3) & ~3;
@@ -325,10 +325,7 @@ hipError_t launch_h(const DecodeArgs& a, int occ, hipStream_t stream) {
     switch (a.H) {
         case 8: return occ == 1 ? launch_one<D, 8, 1>(a, stream) : launch_one<D, 8, 2>(a, stream);
         case 16: return occ == 1 ? launch_one<D, 16, 1>(a, stream) : launch_one<D, 16, 2>(a, stream);
-        case 32:
-            // 32 heads of width 128 per wave need more registers than two waves per SIMD leave
-            if constexpr (D == 128) return launch_one<D, 32, 1>(a, stream);
-            else return occ == 1 ? launch_one<D, 32, 1>(a, stream) : launch_one<D, 32, 2>(a, stream);
+        case 32: return occ == 1 ? launch_one<D, 32, 1>(a, stream) : launch_one<D, 32, 2>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -83,7 +83,9 @@ int env_int(const char* name, int dflt) {
 // within a kernel, so problems differing only in rank reduce in the same order.
 // Tuning overrides (read at every call, so they must not change between a
 // workspace query and the decode that uses it): LRKV_OCCUPANCY (1 or 2 waves
-// per SIMD), LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch).
+// per SIMD; defaults: 2 for the fp32 matrix-core kernel, 2 for the bf16 one at
+// batch >= 32 and 1 below),
+// LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch).
 constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
 // Which decode the plan is for.  The normalised variant's bf16 matrix-core kernel is built for one wave per
@@ -131,10 +133,13 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
     }
     if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
-        p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
+        // two waves per SIMD pay off for large batches (many sequences, splits of few blocks each: the
+        // 64-sequence ragged batch runs 4% faster) and cost 1-3% for a few long sequences; the choice
+        // depends on the batch only, never on r, so problems differing only in rank share a plan
+        p.occupancy = env_int("LRKV_OCCUPANCY", d.batch >= 32 ? 2 : 1) == 2 ? 2 : 1;
     } else if (mfma_f32_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaF32;
-        p.occupancy = env_int("LRKV_OCCUPANCY", 1) == 2 ? 2 : 1;
+        p.occupancy = env_int("LRKV_OCCUPANCY", 2) == 1 ? 1 : 2;  // two waves per SIMD hide its MFMA chains
     } else if (general_path_supports(d.H, d.d_h, d.r)) {
         p.path = SplitPath::kGeneral;
         p.occupancy = 1;
