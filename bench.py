@@ -137,6 +137,8 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="rotary variant: each step appends a row and runs lrkv_decode_rope (every head's key "
                          "rebuilt and turned at its position)")
+    ap.add_argument("--no-stream-probe", action="store_true",
+                    help="skip the streaming-read probe (the measured read bandwidth the split pass is compared with)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (for scaling HBM counters)")
     args = ap.parse_args()
@@ -393,6 +395,26 @@ def main():
         f"{split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
+    # the measured streaming-read bandwidth on this GPU: lrkv_read_probe over a 1 GiB buffer, HIP events on the
+    # same stream, best of 10 reads
+    stream_gbps = None
+    if not args.no_stream_probe:
+        probe_bytes = 1 << 30
+        src = torch.ones(probe_bytes // 4, dtype=torch.int32, device="cuda")
+        sink = torch.empty(lk.READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        best = None
+        for i in range(12):
+            e_a, e_b = ev(), None
+            lk.lrkv_read_probe(src, probe_bytes, sink, stream)
+            e_b = ev()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms = e_a.elapsed_time(e_b)
+                best = ms if best is None else min(best, ms)
+        stream_gbps = probe_bytes / (best / 1e3) / 1e9
+        del src
+        log(f"bench: streaming-read probe {stream_gbps:.0f} GB/s ({100 * stream_gbps / HBM_PEAK_GBPS:.1f}% of the peak)")
+
     cpu = None
     if args.cpu_budget > 0:
         log(f"bench: timing the CPU reference (~{args.cpu_budget:.0f} s)")
@@ -425,7 +447,9 @@ def main():
                      "lrkv_decode_normed (split pass + merge)" if args.norm else
                      "lrkv_decode_paged (split pass + merge)" if args.paged else
                      "lrkv_decode_rope (split pass + merge)" if args.rope else "split pass (lrkv_decode_partial)",
-                     "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3},
+                     "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3,
+                     "stream_read_gbps": stream_gbps,
+                     "frac_of_stream_read": (split_gbps / stream_gbps) if stream_gbps else None},
         "mfma_util_shared_score": mfma_util,
         "layer_step": layer,
         "cpu_baseline": cpu,

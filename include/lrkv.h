@@ -343,6 +343,13 @@ lrkv_status lrkv_project_append(const lrkv_dims* dims, int32_t d_model, const lr
 lrkv_status lrkv_output_project(const lrkv_dims* dims, int32_t d_model, const float* o, const void* W_o, float* y,
                                 void* stream);
 
+/* Measurement helper, not part of the method: read every byte of src once
+ * with 16-byte loads (the streaming-read bandwidth the decode is compared
+ * with) and write one XOR checksum per workgroup to sink.
+ *   src   device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink  device uint32 [2048] */
+lrkv_status lrkv_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Cache payload in bytes, counted as the pages count it (numel x element size
  * of the live rows): 2 * s * sum_b L_b * (d_h + H * r), s = 4 (fp32) or 2 (bf16)
  * (reading notes sec. 2.5 Eqs. (8)-(9); review sec. 4).  host_seq_lens is a

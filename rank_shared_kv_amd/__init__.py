@@ -27,10 +27,10 @@ LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
-            "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table", "lrkv_decode_rope_workspace_bytes",
-            "lrkv_decode_rope",
-            "lrkv_key_scales", "lrkv_norm_query", "lrkv_decode_normed", "lrkv_materialize",
-            "lrkv_project_append", "lrkv_output_project", "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
+            "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table",
+            "lrkv_decode_rope_workspace_bytes", "lrkv_decode_rope", "lrkv_key_scales", "lrkv_norm_query",
+            "lrkv_decode_normed", "lrkv_materialize", "lrkv_project_append", "lrkv_output_project", "lrkv_read_probe",
+            "lrkv_cache_bytes", "lrkv_status_str", "lrkv_last_error")
 
 
 class LrkvError(RuntimeError):
@@ -85,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "lrkv_paged_append": ([D, PC, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_paged": ([D, PC, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_rope_table": ([i32, i32, ctypes.c_float, vp, vp], ctypes.c_int),
+            "lrkv_read_probe": ([vp, sz, vp, vp], ctypes.c_int),
             "lrkv_decode_rope_workspace_bytes": ([D, i32], sz),
             "lrkv_decode_rope": ([D, C, i32, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_key_scales": ([D, C, i32, i32, vp, ctypes.c_float, vp, vp], ctypes.c_int),
@@ -214,6 +215,13 @@ def lrkv_decode_paged(dims: Dims, cache: PagedCache, max_len: int, q, p, B_v, ou
                       stream=None) -> None:
     _check(lib().lrkv_decode_paged(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(q), _ptr(p), _ptr(B_v),
                                    _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_paged")
+
+
+READ_PROBE_SINK_WORDS = 2048
+
+
+def lrkv_read_probe(src, nbytes: int, sink, stream=None) -> None:
+    _check(lib().lrkv_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "lrkv_read_probe")
 
 
 def lrkv_rope_table(d_h: int, n_pos: int, base: float, table, stream=None) -> None:

@@ -1,0 +1,50 @@
+// Streaming-read probe: the measured read bandwidth that the decode's achieved
+// bandwidth is also compared with (besides the published HBM peak).  Every
+// 16-byte chunk of a buffer is read once by a grid-stride loop with 8 loads in
+// flight per lane; each workgroup folds what it read into one XOR checksum so
+// the loads cannot be dropped.  Not part of the attention method.
+#include "lrkv_device.hpp"
+#include "lrkv_internal.hpp"
+
+namespace lrkv {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;
+
+__global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const u32x4_t* __restrict__ p, size_t n16,
+                                                                   uint32_t* __restrict__ sink) {
+    __shared__ uint32_t part[kProbeThreads / 64];
+    const size_t stride = (size_t)gridDim.x * kProbeThreads;
+    size_t i = (size_t)blockIdx.x * kProbeThreads + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+        u32x4_t v[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4_t v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+}  // namespace
+
+int read_probe_workgroups() { return 2048; }  // 8 per CU on 256 CUs
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(read_probe_workgroups()), dim3(kProbeThreads), 0, stream,
+                       (const u32x4_t*)src, bytes / 16, sink);
+    return hipGetLastError();
+}
+
+}  // namespace lrkv

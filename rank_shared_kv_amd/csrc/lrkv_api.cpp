@@ -583,6 +583,15 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
     return ok();
 }
 
+lrkv_status lrkv_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    LRKV_TRY(need_ptr(src, "src"));
+    LRKV_TRY(need_ptr(sink, "sink"));
+    if (bytes == 0 || bytes % 16 != 0) return fail(LRKV_ERR_INVALID_ARG, "bytes=%zu must be a positive multiple of 16", bytes);
+    hipError_t e = lrkv::launch_read_probe(src, bytes, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
+    return ok();
+}
+
 lrkv_status lrkv_rope_table(int32_t d_h, int32_t n_pos, float base, float* table, void* stream) {
     if (d_h < 2 || d_h > 4096 || (d_h & 1)) return fail(LRKV_ERR_INVALID_ARG, "d_h=%d must be even, 2..4096", d_h);
     if (n_pos < 0 || n_pos > (1 << 28)) return fail(LRKV_ERR_INVALID_ARG, "n_pos=%d outside [0, 2^28]", n_pos);
