@@ -217,7 +217,7 @@ def lrkv_decode_paged(dims: Dims, cache: PagedCache, max_len: int, q, p, B_v, ou
                                    _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_paged")
 
 
-READ_PROBE_SINK_WORDS = 2048
+READ_PROBE_SINK_WORDS = 1024
 
 
 def lrkv_read_probe(src, nbytes: int, sink, stream=None) -> None:
