@@ -75,9 +75,9 @@ constexpr int kRows = 32;   // rows per block
 constexpr int kWaves = 4;   // waves per workgroup
 // cache-policy bits of the streamed loads: 2 = non-temporal.  Latent rows are read exactly once;
 // shared key/value rows are re-read through L2 (split key lines, second head group).
-// waves of a workgroup advance block by block together (one barrier per block): the second head-group
-// wave's shared-row loads then hit more often in L2 (long context: HBM read 1.176 GB per launch instead of
-// 1.188 GB, split pass 1.3% faster)
+// waves of a workgroup advance block by block together (one barrier per block) in single-token decode: the
+// second head-group wave's shared-row loads then hit more often in L2 (long context: HBM read 1.176 GB per
+// launch instead of 1.188 GB, split pass 1.3% faster)
 #ifndef LRKV_LOCKSTEP
 #define LRKV_LOCKSTEP 1
 #endif
@@ -365,9 +365,12 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // across the workgroup: the barrier at the top of an iteration is reached equally often by every wave
     // (a wave past its own blocks only takes the barrier).  The waves then move block by block together,
     // and the two head-group waves of a row lane read the same shared rows at nearly the same time.
-    const int n_all = (last_blk > split * C::NTL) ? (last_blk - split * C::NTL + step_blk - 1) / step_blk : 0;
+    // Multi-token decode (virtual sequences) runs without it: there the barrier cost 7-11%.
+    const bool lockstep = a.qgroup == 1;  // a kernel argument: the same for every wave
+    const int n_all = !lockstep ? nmine
+                      : (last_blk > split * C::NTL) ? (last_blk - split * C::NTL + step_blk - 1) / step_blk : 0;
     for (int it = 0; it < n_all; ++it) {
-        __syncthreads();
+        if (lockstep) __syncthreads();
         if (it >= nmine) continue;
 #else
     for (int it = 0; it < nmine; ++it) {
