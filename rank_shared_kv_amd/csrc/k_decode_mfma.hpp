@@ -365,8 +365,9 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // across the workgroup: the barrier at the top of an iteration is reached equally often by every wave
     // (a wave past its own blocks only takes the barrier).  The waves then move block by block together,
     // and the two head-group waves of a row lane read the same shared rows at nearly the same time.
-    // Multi-token decode (virtual sequences) runs without it: there the barrier cost 7-11%.
-    const bool lockstep = a.qgroup == 1;  // a kernel argument: the same for every wave
+    // Only with two head groups (no duplicate fetch to save otherwise: one group measured 0.5-4% slower
+    // with it) and without virtual sequences (multi-token decode: the barrier cost 7-11%).
+    const bool lockstep = C::NHG > 1 && a.qgroup == 1;  // compile-time and a kernel argument: the same for every wave
     const int n_all = !lockstep ? nmine
                       : (last_blk > split * C::NTL) ? (last_blk - split * C::NTL + step_blk - 1) / step_blk : 0;
     for (int it = 0; it < n_all; ++it) {
