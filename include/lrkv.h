@@ -194,13 +194,18 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
  *   p          device [batch][Q][H][r] fp32: lrkv_absorb_query with dims->batch = batch * Q
  *   out        device [batch][Q][H][d_h] fp32 (0 for a query that sees no row)
  *   workspace  >= lrkv_decode_multi_workspace_bytes(dims, Q, max_len) bytes, 256-byte aligned
- * It runs lrkv_decode's kernels on batch * Q virtual sequences (query i of
- * sequence b is virtual sequence b * Q + i, with the causal length above).
- * The Q virtual sequences of one sequence share its block order, so their
- * workgroups read the same rows at about the same time and the repeats are
- * served by the GPU's caches.  The workspace holds lrkv_decode's records for
- * batch * Q sequences, then the virtual lengths.  Q = 1 gives exactly
- * lrkv_decode's kernels and results. */
+ * It runs lrkv_decode's split-and-merge scheme on virtual sequences, each a
+ * set of qw consecutive query tokens of one sequence with the causal length
+ * of its last token.  On the bf16 matrix-core shapes qw = 2 (Q = 2) or 4
+ * (Q >= 3; at most 2 for d_h = 128 and r = 64): one workgroup serves all qw
+ * tokens from a single read of the rows.  Elsewhere qw = 1, one virtual
+ * sequence per token.  The sets of one sequence share its block order, so
+ * their workgroups read the same rows at about the same time and the repeats
+ * are served by the GPU's caches.  The workspace holds qw records per split
+ * workgroup and head, then the virtual lengths.  Q = 1 gives exactly
+ * lrkv_decode's kernels and results.  LRKV_MULTI_QW (1, 2 or 4) overrides
+ * qw; it is read at every call and must not change between the workspace
+ * query and the decode. */
 size_t lrkv_decode_multi_workspace_bytes(const lrkv_dims* dims, int32_t n_queries, int32_t max_len);
 lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lrkv_cache* cache, int32_t max_len,
                               const void* q, const float* p, const void* B_v, float* out, void* workspace,

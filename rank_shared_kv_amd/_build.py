@@ -13,11 +13,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "liblrkv.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-# the bf16 decode kernel's instances are spread over four translation units so they compile in parallel
+# the bf16 decode kernel's instances are spread over eight translation units so they compile in parallel
 SOURCES = ["lrkv_api.cpp", "k_cache.hip", "k_decode_general.hip", "k_decode_mfma.hip",
            "k_decode_mfma_part_d64_n0.hip", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma_part_d64_n1.hip",
-           "k_decode_mfma_part_d128_n1.hip", "k_decode_mfma_f32.hip", "k_merge.hip", "k_linear.hip",
-           "k_materialize.hip", "k_norm.hip", "k_rope.hip", "k_decode_rope_mfma.hip", "k_probe.hip"]
+           "k_decode_mfma_part_d128_n1.hip", "k_decode_mfma_part_d64_q2.hip", "k_decode_mfma_part_d64_q4.hip",
+           "k_decode_mfma_part_d128_q2.hip", "k_decode_mfma_part_d128_q4.hip", "k_decode_mfma_f32.hip",
+           "k_merge.hip", "k_linear.hip", "k_materialize.hip", "k_norm.hip", "k_rope.hip", "k_decode_rope_mfma.hip",
+           "k_probe.hip"]
 
 # Packed fp32 instructions are disabled in device code: ordinary float code
 # only, scheduled by the compiler without v_pk_*_f32.

@@ -205,18 +205,22 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
 }
 
 namespace {
-__global__ void __launch_bounds__(256) multi_lengths_kernel(int n, int Q, const int32_t* __restrict__ seq_lens,
+__global__ void __launch_bounds__(256) multi_lengths_kernel(int n, int Q, int qw, const int32_t* __restrict__ seq_lens,
                                                             int32_t* __restrict__ lens_out) {
     const int v = blockIdx.x * 256 + threadIdx.x;
     if (v >= n) return;
-    const int b = v / Q, i = v - b * Q;
-    lens_out[v] = max(0, seq_lens[b] - Q + 1 + i);
+    const int nc = (Q + qw - 1) / qw;
+    const int b = v / nc, c = v - b * nc;
+    const int last = min((c + 1) * qw, Q) - 1;  // the set's last token
+    lens_out[v] = max(0, seq_lens[b] - Q + 1 + last);
 }
 }  // namespace
 
-hipError_t launch_multi_lengths(int batch, int Q, const int32_t* seq_lens, int32_t* lens_out, hipStream_t stream) {
-    const int n = batch * Q;
-    hipLaunchKernelGGL(multi_lengths_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, Q, seq_lens, lens_out);
+hipError_t launch_multi_lengths(int batch, int Q, int qw, const int32_t* seq_lens, int32_t* lens_out,
+                                hipStream_t stream) {
+    const int n = batch * ((Q + qw - 1) / qw);
+    hipLaunchKernelGGL(multi_lengths_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, Q, qw, seq_lens,
+                       lens_out);
     return hipGetLastError();
 }
 

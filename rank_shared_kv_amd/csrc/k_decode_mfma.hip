@@ -8,6 +8,10 @@ hipError_t launch_split_mfma_d64_n0(const DecodeArgs& a, int occupancy, hipStrea
 hipError_t launch_split_mfma_d64_n1(const DecodeArgs& a, int occupancy, hipStream_t stream);
 hipError_t launch_split_mfma_d128_n0(const DecodeArgs& a, int occupancy, hipStream_t stream);
 hipError_t launch_split_mfma_d128_n1(const DecodeArgs& a, int occupancy, hipStream_t stream);
+hipError_t launch_split_mfma_d64_q2(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_split_mfma_d64_q4(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_split_mfma_d128_q2(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_split_mfma_d128_q4(const DecodeArgs& a, hipStream_t stream);
 
 namespace {
 constexpr int kRows = 32;   // rows per block (k_decode_mfma.hpp)
@@ -26,7 +30,18 @@ bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap) {
 
 int mfma_rows_per_tile(int H) { return kRows * (kWaves / ((H + 15) / 16)); }
 
+// query tokens one workgroup can serve in multi-token decode: 4, except at d_h = 128 and r = 64, where four
+// queries' accumulators do not fit the register file next to the load ring (k_decode_mfma.hpp)
+int mfma_max_query_width(int H, int d_h, int r) { return (d_h == 128 && r == 64) ? 2 : 4; }
+
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream) {
+    if (a.qw == 2 || a.qw == 4) {  // several query tokens per workgroup (plain decode only, one wave per SIMD)
+        if (a.rho != nullptr || a.block_table != nullptr) return hipErrorInvalidValue;
+        if (a.d_h == 64) return a.qw == 2 ? launch_split_mfma_d64_q2(a, stream) : launch_split_mfma_d64_q4(a, stream);
+        if (a.d_h == 128) return a.qw == 2 ? launch_split_mfma_d128_q2(a, stream) : launch_split_mfma_d128_q4(a, stream);
+        return hipErrorInvalidValue;
+    }
+    if (a.qw != 1) return hipErrorInvalidValue;
     const bool norm = a.rho != nullptr;
     if (a.d_h == 64) return norm ? launch_split_mfma_d64_n1(a, occupancy, stream) : launch_split_mfma_d64_n0(a, occupancy, stream);
     if (a.d_h == 128) return norm ? launch_split_mfma_d128_n1(a, occupancy, stream) : launch_split_mfma_d128_n0(a, occupancy, stream);

@@ -49,6 +49,14 @@
 // sequence's length inside its last block are masked (scores) or zeroed
 // (values), never used.
 //
+// Several query tokens (QW = 2 or 4, multi-token decode): a workgroup serves
+// QW consecutive query tokens of one sequence from a single pass over its rows.
+// Every loaded unit feeds all of them: the key fragments go into QW score
+// products, the V^T tile into QW value products, and each latent register
+// into QW private dots and QW private-value updates.  Each token keeps its own
+// softmax state and is causally masked at its own length; the padding slots of
+// a last, partial set see no row.  Records are [workgroup][QW][H].
+//
 // Normalised variant (NORM): the key of every (head, token) is RMS-normalised
 // as a whole, and its cached reciprocal scale multiplies the summed logit
 // ("Low-Rank Key Value Attention | What a shared cache can preserve", sec. 8,
@@ -90,7 +98,7 @@ constexpr int kWaves = 4;   // waves per workgroup
 constexpr int kNTLat = LRKV_NT_LATENT ? 2 : 0;
 constexpr int kNTSh = LRKV_NT_SHARED ? 2 : 0;
 
-template <int D, int R, int H, int OCC>
+template <int D, int R, int H, int OCC, int QW = 1>
 struct Cfg {
     static constexpr int EPL = R / 8;                   // latent coordinates per lane
     static constexpr int LDW = (EPL + 1) / 2;           // dwords per latent load (EPL = 1 uses one dword)
@@ -110,9 +118,10 @@ struct Cfg {
     static constexpr int LUDW = 8 * LDW;                // dwords of a latent unit
     static constexpr int SLOT_DW = (KDW > VDW ? (KDW > LUDW ? KDW : LUDW) : (VDW > LUDW ? VDW : LUDW));
     // ring depth: as deep as the register budget allows.  OCC = waves per SIMD (2: 256 registers per
-    // wave, 1: 512).  The depth must divide the per-block unit count so slots repeat every block.
+    // wave, 1: 512); each query a wave serves takes (d_h + r) / 2 + 16 accumulator registers from it.
+    // The depth must divide the per-block unit count so slots repeat every block.
     static constexpr int pick_slots() {
-        const int budget = (OCC == 1) ? 200 : 96;  // registers for the ring
+        const int budget = (OCC == 2) ? 96 : (QW == 1) ? 200 : (QW == 2) ? 160 : (H <= 16) ? 96 : 64;  // ring registers
         const int cand[6] = {9, 6, 5, 4, 3, 2};
         for (int i = 0; i < 6; ++i)
             if (NU % cand[i] == 0 && cand[i] * SLOT_DW <= budget) return cand[i];
@@ -124,17 +133,19 @@ struct Cfg {
     static constexpr int VTS = kRows + 4;               // bf16 per V^T row in LDS (72 B: conflict-free reads)
     static constexpr int XS = 36;                       // floats per exchange row (32 rows + alpha + pad)
     static constexpr int REC = ((D + R + 2) + 3) & ~3;
-    static constexpr int Q_BYTES = NHG * 16 * QROW * 2;
-    static constexpr int P_BYTES = ((H * PROW * 4) + 15) & ~15;
+    static constexpr int Q_BYTES = QW * NHG * 16 * QROW * 2;        // q rows of each query, head-group padded
+    static constexpr int P_BYTES = ((QW * H * PROW * 4) + 15) & ~15;
     static constexpr int MW_BYTES = kWaves * 16 * 4;
     static constexpr int VT_BYTES = ((D * VTS * 2) + 15) & ~15;
-    static constexpr int X_BYTES = 16 * XS * 4;
+    static constexpr int X_BYTES = QW * 16 * XS * 4;                   // one exchange area per query
     static constexpr int WAVE_BYTES = VT_BYTES + X_BYTES;
     static constexpr int LDS_BYTES = Q_BYTES + P_BYTES + MW_BYTES + kWaves * WAVE_BYTES;
     static constexpr int MERGE_BYTES = H * REC * 4;
     static_assert(MERGE_BYTES <= kWaves * WAVE_BYTES, "merge area must fit in the per-wave tiles");
     static_assert(NU % NSLOT == 0, "ring must divide the unit sequence");
     static_assert(H % 8 == 0 && H <= 32, "head count");
+    static_assert(QW == 1 || QW == 2 || QW == 4, "queries per wave");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // (a.lo16, b.lo16)
@@ -172,9 +183,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int D, int R, int H, int OCC, bool NORM>
+template <int D, int R, int H, int OCC, bool NORM, int QW>
 __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs a) {
-    using C = Cfg<D, R, H, OCC>;
+    using C = Cfg<D, R, H, OCC, QW>;
+    static_assert(!(NORM && QW > 1), "the normalised variant serves one query per sequence");
     constexpr int EPL = C::EPL, LDW = C::LDW, OCTS = C::OCTS, NU = C::NU, NSLOT = C::NSLOT, SDW = C::SLOT_DW;
     constexpr bool kDot2 = (EPL % 2 == 0) && EPL > 0;  // private score on v_dot2 (p split into bf16 hi + lo)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -199,22 +211,41 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     const int Lb = clamped_len(a.seq_lens, b, a.max_len);
     if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
     const int nb = (Lb + kRows - 1) / kRows;  // blocks of this sequence
+    const int bc = b / a.qgroup;  // the cached sequence this (virtual) sequence reads
 
-    const uint16_t* qg = (const uint16_t*)a.q + (size_t)b * H * D;
+    // Query rows served by this workgroup.  QW == 1: the row of sequence b (virtual sequence b of a
+    // multi-token decode).  QW > 1 (multi-token decode of n_queries tokens per sequence): virtual sequence b
+    // is token set c = b % qgroup of cached sequence bc, tokens c*QW .. c*QW + nreal - 1; token qi of the set
+    // sees Lq[qi] rows, the set's last token Lb of them (the virtual length), each earlier token one row
+    // fewer.  Padding slots qi >= nreal see no row and their records are never read.
+    int q_row0 = b, nreal = 1;
+    int Lq[QW];
+    Lq[0] = Lb;
+    if constexpr (QW > 1) {
+        const int c = b - bc * a.qgroup;
+        nreal = min(QW, a.n_queries - c * QW);
+        q_row0 = bc * a.n_queries + c * QW;
+#pragma unroll
+        for (int qi = 0; qi < QW; ++qi) Lq[qi] = (qi < nreal) ? max(0, Lb - (nreal - 1 - qi)) : 0;
+    }
+    const uint16_t* qg = (const uint16_t*)a.q + (size_t)q_row0 * H * D;
 
-    // ---- q (zero rows pad a partial head group) and p into LDS ----
-    for (int i = tid; i < C::NHG * 16 * D; i += kWaves * 64) {
-        const int h = i / D, c = i - h * D;
-        q_lds[h * C::QROW + c] = (h < H) ? qg[h * D + c] : (uint16_t)0;
+    // ---- q (zero rows pad a partial head group and the padding query slots) and p into LDS ----
+    // LDS q row (qi, head) sits at qi * 16 * NHG + head; p row (qi, head) at qi * H + head
+    for (int i = tid; i < QW * C::NHG * 16 * D; i += kWaves * 64) {
+        const int hq = i / D, c = i - hq * D;
+        const int qi = (QW == 1) ? 0 : hq / (C::NHG * 16), h = hq - qi * (C::NHG * 16);
+        q_lds[hq * C::QROW + c] = (h < H && qi < nreal) ? qg[(qi * H + h) * D + c] : (uint16_t)0;
     }
     if constexpr (R > 0) {
-        const float* pg = a.p + (size_t)b * H * R;
+        const float* pg = a.p + (size_t)q_row0 * H * R;
         if constexpr (kDot2) {
             // per head and r-slice of EPL coordinates: EPL/2 pairs of high parts, then EPL/2 of low parts
-            for (int i = tid; i < H * (R / 2); i += kWaves * 64) {
-                const int h = i / (R / 2), pr = i - h * (R / 2);  // pair index within the head
+            for (int i = tid; i < QW * H * (R / 2); i += kWaves * 64) {
+                const int h = i / (R / 2), pr = i - h * (R / 2);  // pair index within the (query, head) row
                 const int slice = pr / (EPL / 2), j = pr - slice * (EPL / 2);
-                const float x0 = pg[h * R + 2 * pr], x1 = pg[h * R + 2 * pr + 1];
+                const bool live = QW == 1 || h < nreal * H;
+                const float x0 = live ? pg[h * R + 2 * pr] : 0.f, x1 = live ? pg[h * R + 2 * pr + 1] : 0.f;
                 const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
                 const uint32_t l0 = f32_to_bf16_bits(x0 - __uint_as_float(h0 << 16));
                 const uint32_t l1 = f32_to_bf16_bits(x1 - __uint_as_float(h1 << 16));
@@ -223,13 +254,13 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 row[EPL / 2 + j] = l0 | (l1 << 16);
             }
         } else {
-            for (int i = tid; i < H * R; i += kWaves * 64) {
+            for (int i = tid; i < QW * H * R; i += kWaves * 64) {
                 const int h = i / R, k = i - h * R;
-                p_lds[h * C::PROW + k] = __float_as_uint(pg[i]);
+                p_lds[h * C::PROW + k] = (QW == 1 || h < nreal * H) ? __float_as_uint(pg[i]) : 0u;
             }
         }
     }
-    for (int i = lane; i < 16 * C::XS; i += 64) xb[i] = 0.f;
+    for (int i = lane; i < QW * 16 * C::XS; i += 64) xb[i] = 0.f;
     __syncthreads();
 
     const int n16 = lane & 15, g4 = lane >> 4;  // MFMA layout: column (head or value column), row group
@@ -238,15 +269,20 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     const int srow = lane / C::LPR, schunk = lane % C::LPR;  // value-tile load layout
     const float scale = kLog2e / sqrtf((float)D);
 
-    f32x4_t acc_sh[C::CB];
-    float acc_pr[OCTS][EPL > 0 ? EPL : 1];
-    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t acc_sh[QW][C::CB];
+    float acc_pr[QW][OCTS][EPL > 0 ? EPL : 1];
+    float m_run[QW], l_run[QW];
 #pragma unroll
-    for (int cb = 0; cb < C::CB; ++cb) acc_sh[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int qi = 0; qi < QW; ++qi) {
+        m_run[qi] = -INFINITY;
+        l_run[qi] = 0.f;
 #pragma unroll
-    for (int o = 0; o < OCTS; ++o)
+        for (int cb = 0; cb < C::CB; ++cb) acc_sh[qi][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc_pr[o][e] = 0.f;
+        for (int o = 0; o < OCTS; ++o)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc_pr[qi][o][e] = 0.f;
+    }
 
     // ---- buffer descriptors of this sequence and fixed per-lane byte offsets ----
     // latents are token-major ([L_cap][H][r] per sequence): one latent row holds every head
@@ -254,7 +290,6 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // contiguous cache: descriptors over this sequence's rows, a block addressed by its row t0; paged cache:
     // descriptors over the whole page pools, a block addressed by its pool row (pages hold whole blocks)
     const bool paged = a.block_table != nullptr;
-    const int bc = b / a.qgroup;  // the cached sequence this (virtual) sequence reads
     const size_t seq_rows = paged ? 0 : (size_t)bc * a.L_cap;
     const uint32_t n_rows = paged ? (uint32_t)a.n_pages << a.page_shift : (uint32_t)a.L_cap;
     const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + seq_rows * D, n_rows * row_bytes_sh);
@@ -385,8 +420,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
         const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
         const int pr = paged_row(a, bc, t0), pr_pf = paged_row(a, bc, t0_pf);  // pool rows (t0 when contiguous)
-        f32x4_t s_sh[2];
-        float ev[8];
+        f32x4_t s_sh[QW][2];
         uint32_t rho_w[8];  // scales of this lane's 8 scores (bf16 bits), read at the top of the block
         if constexpr (NORM) {
             const int so = t0 * H * 2;
@@ -412,17 +446,20 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 // shared scores on MFMA (both 16-row halves)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-                        const int o = 4 * (half * C::KSTEPS + kk);
-                        const u32x4_t av = {cur[o], cur[o + 1], cur[o + 2], cur[o + 3]};
-                        const u32x4_t bv =
-                            *(const u32x4_t*)(q_lds + (16 * hg + n16) * C::QROW + 32 * kk + 8 * g4);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                                     __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+                    for (int qi = 0; qi < QW; ++qi) {  // every query against the same key fragments
+                        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kk = 0; kk < C::KSTEPS; ++kk) {
+                            const int o = 4 * (half * C::KSTEPS + kk);
+                            const u32x4_t av = {cur[o], cur[o + 1], cur[o + 2], cur[o + 3]};
+                            const u32x4_t bv = *(const u32x4_t*)(q_lds + (qi * C::NHG * 16 + 16 * hg + n16) * C::QROW +
+                                                                 32 * kk + 8 * g4);
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
+                        }
+                        s_sh[qi][half] = acc;
                     }
-                    s_sh[half] = acc;
                 }
             } else if (u == 1) {
                 // value tile -> V^T in LDS: vt[c][row], 4 consecutive rows per 8-byte store;
@@ -447,70 +484,90 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 if constexpr (R == 0) {
                     // no private branch: zero private scores
 #pragma unroll
-                    for (int oi = 0; oi < OCTS; ++oi)
+                    for (int qi = 0; qi < QW; ++qi)
 #pragma unroll
-                        for (int sub = 0; sub < 4; ++sub) xb[(8 * oi + hh) * C::XS + 8 * sub + sl] = 0.f;
+                        for (int oi = 0; oi < OCTS; ++oi)
+#pragma unroll
+                            for (int sub = 0; sub < 4; ++sub)
+                                xb[(qi * 16 + 8 * oi + hh) * C::XS + 8 * sub + sl] = 0.f;
                 }
             } else if constexpr (R > 0) {
                 const int v = u - 2;
                 const int phase = v / (4 * OCTS);
                 const int oi = (v % (4 * OCTS)) / 4, sub = v % 4;
                 if (phase == 0) {
-                    uint32_t pw[EPL];
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) pw[e] = p_lds[(16 * hg + 8 * oi + hh) * C::PROW + sl * EPL + e];
-                    float part[8];
+                    for (int qi = 0; qi < QW; ++qi) {  // every query against the same latent registers
+                        uint32_t pw[EPL];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        float acc = 0.f;
-                        if constexpr (kDot2) {
+                        for (int e = 0; e < EPL; ++e)
+                            pw[e] = p_lds[(qi * H + 16 * hg + 8 * oi + hh) * C::PROW + sl * EPL + e];
+                        float part[8];
 #pragma unroll
-                            for (int pr = 0; pr < EPL / 2; ++pr) {
-                                const uint32_t z = cur[LDW * k + pr];
-                                acc = dot2_bf16(z, pw[EPL / 2 + pr], acc);  // low parts of p
-                                acc = dot2_bf16(z, pw[pr], acc);            // high parts of p
+                        for (int k = 0; k < 8; ++k) {
+                            float acc = 0.f;
+                            if constexpr (kDot2) {
+#pragma unroll
+                                for (int pr = 0; pr < EPL / 2; ++pr) {
+                                    const uint32_t z = cur[LDW * k + pr];
+                                    acc = dot2_bf16(z, pw[EPL / 2 + pr], acc);  // low parts of p
+                                    acc = dot2_bf16(z, pw[pr], acc);            // high parts of p
+                                }
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < EPL; ++e)
+                                    acc = fmaf(__uint_as_float(pw[e]), lat_at(cur + LDW * k, e), acc);
                             }
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < EPL; ++e) acc = fmaf(__uint_as_float(pw[e]), lat_at(cur + LDW * k, e), acc);
+                            part[k] = acc;
                         }
-                        part[k] = acc;
-                    }
-                    // transpose-reduce across the 8 lanes of a head: part[k] is this lane's slice of
-                    // row k.  Stage 1 pairs lanes sl, 7-sl (half mirror) and each keeps the rows whose
-                    // bit 2 equals its own; stages 2 and 3 do the same on bits 1 and 0 with lanes
-                    // sl^2 and sl^1.  Lane sl ends with the whole score of row 8*sub + sl.
-                    float q4[4], q2[2];
+                        // transpose-reduce across the 8 lanes of a head: part[k] is this lane's slice of
+                        // row k.  Stage 1 pairs lanes sl, 7-sl (half mirror) and each keeps the rows whose
+                        // bit 2 equals its own; stages 2 and 3 do the same on bits 1 and 0 with lanes
+                        // sl^2 and sl^1.  Lane sl ends with the whole score of row 8*sub + sl.
+                        float q4[4], q2[2];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float keep = sb2 ? part[k + 4] : part[k];
-                        const float send = sb2 ? part[k] : part[k + 4];
-                        q4[k] = keep + dpp<kDppHalfMirror>(send);
-                    }
+                        for (int k = 0; k < 4; ++k) {
+                            const float keep = sb2 ? part[k + 4] : part[k];
+                            const float send = sb2 ? part[k] : part[k + 4];
+                            q4[k] = keep + dpp<kDppHalfMirror>(send);
+                        }
 #pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        const float keep = sb1 ? q4[k + 2] : q4[k];
-                        const float send = sb1 ? q4[k] : q4[k + 2];
-                        q2[k] = keep + dpp<kDppXor2>(send);
+                        for (int k = 0; k < 2; ++k) {
+                            const float keep = sb1 ? q4[k + 2] : q4[k];
+                            const float send = sb1 ? q4[k] : q4[k + 2];
+                            q2[k] = keep + dpp<kDppXor2>(send);
+                        }
+                        const float keep = sb0 ? q2[1] : q2[0];
+                        const float send = sb0 ? q2[0] : q2[1];
+                        xb[(qi * 16 + 8 * oi + hh) * C::XS + 8 * sub + sl] = keep + dpp<kDppXor1>(send);
                     }
-                    const float keep = sb0 ? q2[1] : q2[0];
-                    const float send = sb0 ? q2[0] : q2[1];
-                    xb[(8 * oi + hh) * C::XS + 8 * sub + sl] = keep + dpp<kDppXor1>(send);
                 } else {
                     if (sub == 0) {
-                        const float al = xb[(8 * oi + hh) * C::XS + 32];
 #pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc_pr[oi][e] *= al;
+                        for (int qi = 0; qi < QW; ++qi) {
+                            const float al = xb[(qi * 16 + 8 * oi + hh) * C::XS + 32];
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e) acc_pr[qi][oi][e] *= al;
+                        }
                     }
-                    const f32x4_t e0 = *(const f32x4_t*)(xb + (8 * oi + hh) * C::XS + 8 * sub);
-                    const f32x4_t e1 = *(const f32x4_t*)(xb + (8 * oi + hh) * C::XS + 8 * sub + 4);
+                    f32x4_t e0[QW], e1[QW];
+#pragma unroll
+                    for (int qi = 0; qi < QW; ++qi) {
+                        e0[qi] = *(const f32x4_t*)(xb + (qi * 16 + 8 * oi + hh) * C::XS + 8 * sub);
+                        e1[qi] = *(const f32x4_t*)(xb + (qi * 16 + 8 * oi + hh) * C::XS + 8 * sub + 4);
+                    }
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
-                        if (8 * sub + k < nvalid) {  // rows past the end: weight 0, content arbitrary
-                            const float w = (k < 4) ? e0[k] : e1[k - 4];
+                        // rows past the sequence end: weight 0, content arbitrary (rows a query token does not
+                        // see are live rows of the sequence with weight 0)
+                        if (8 * sub + k < nvalid) {
 #pragma unroll
-                            for (int e = 0; e < EPL; ++e)
-                                acc_pr[oi][e] = fmaf(w, lat_at(cur + LDW * k, e), acc_pr[oi][e]);
+                            for (int e = 0; e < EPL; ++e) {
+                                const float z = lat_at(cur + LDW * k, e);
+#pragma unroll
+                                for (int qi = 0; qi < QW; ++qi)
+                                    acc_pr[qi][oi][e] = fmaf((k < 4) ? e0[qi][k] : e1[qi][k - 4], z, acc_pr[qi][oi][e]);
+                            }
                         }
                     }
                 }
@@ -519,156 +576,184 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             // after the last key unit: combine, online softmax, shared values
             if (u == 1 + C::NLU / 2) {
                 wave_lds_sync();
-                float sc[8];
-                const f32x4_t pa = *(const f32x4_t*)(xb + n16 * C::XS + 4 * g4);
-                const f32x4_t pb = *(const f32x4_t*)(xb + n16 * C::XS + 16 + 4 * g4);
+                // one query at a time: softmax of its scores, its weights and alpha into its exchange area (for
+                // the private values), then its shared-value products; each lane reads and rewrites only its
+                // own score slots, so no exchange between the queries' passes is needed
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r0 = 4 * g4 + i, r1 = 16 + 4 * g4 + i;
-                    float f0 = scale, f1 = scale;
-                    if constexpr (NORM) {
-                        f0 = scale * __uint_as_float(rho_w[i] << 16);
-                        f1 = scale * __uint_as_float(rho_w[4 + i] << 16);
+                for (int qi = 0; qi < QW; ++qi) {
+                    // rows of this block that query qi sees (the sequence's rows when QW == 1)
+                    const int nvq = (QW == 1) ? nvalid : Lq[qi] - t0;
+                    float* xq = xb + qi * 16 * C::XS;
+                    float sc[8];
+                    const f32x4_t pa = *(const f32x4_t*)(xq + n16 * C::XS + 4 * g4);
+                    const f32x4_t pb = *(const f32x4_t*)(xq + n16 * C::XS + 16 + 4 * g4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r0 = 4 * g4 + i, r1 = 16 + 4 * g4 + i;
+                        float f0 = scale, f1 = scale;
+                        if constexpr (NORM) {
+                            f0 = scale * __uint_as_float(rho_w[i] << 16);
+                            f1 = scale * __uint_as_float(rho_w[4 + i] << 16);
+                        }
+                        sc[i] = (r0 < nvq) ? (s_sh[qi][0][i] + pa[i]) * f0 : -INFINITY;
+                        sc[4 + i] = (r1 < nvq) ? (s_sh[qi][1][i] + pb[i]) * f1 : -INFINITY;
                     }
-                    sc[i] = (r0 < nvalid) ? (s_sh[0][i] + pa[i]) * f0 : -INFINITY;
-                    sc[4 + i] = (r1 < nvalid) ? (s_sh[1][i] + pb[i]) * f1 : -INFINITY;
-                }
-                float tmax = sc[0];
+                    float tmax = sc[0];
 #pragma unroll
-                for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-                const float m_new = fmaxf(m_run, tmax);
-                const float alpha = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                float esum = 0.f;
+                    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                    const float m_new = fmaxf(m_run[qi], tmax);
+                    // with several queries a block can hold no row for an earlier token (m_new = -inf while
+                    // nothing was seen yet): subtract 0 instead so that alpha and the weights are 0, not NaN
+                    const float m_sub = (QW > 1 && m_new == -INFINITY) ? 0.f : m_new;
+                    const float alpha = fast_exp2(m_run[qi] - m_sub);
+                    m_run[qi] = m_new;
+                    float ev[8];
+                    float esum = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    ev[i] = fast_exp2(sc[i] - m_new);
-                    esum += ev[i];
-                }
-                l_run = fmaf(alpha, l_run, esum);
-                wave_lds_sync();  // every lane has read its private scores
-                *(f32x4_t*)(xb + n16 * C::XS + 4 * g4) = f32x4_t{ev[0], ev[1], ev[2], ev[3]};
-                *(f32x4_t*)(xb + n16 * C::XS + 16 + 4 * g4) = f32x4_t{ev[4], ev[5], ev[6], ev[7]};
-                if (g4 == 0) xb[n16 * C::XS + 32] = alpha;
-                wave_lds_sync();
+                    for (int i = 0; i < 8; ++i) {
+                        ev[i] = fast_exp2(sc[i] - m_sub);
+                        esum += ev[i];
+                    }
+                    l_run[qi] = fmaf(alpha, l_run[qi], esum);
+                    wave_lds_sync();  // every lane has read its private scores
+                    *(f32x4_t*)(xq + n16 * C::XS + 4 * g4) = f32x4_t{ev[0], ev[1], ev[2], ev[3]};
+                    *(f32x4_t*)(xq + n16 * C::XS + 16 + 4 * g4) = f32x4_t{ev[4], ev[5], ev[6], ev[7]};
+                    if (g4 == 0) xq[n16 * C::XS + 32] = alpha;
 
-                // shared values on MFMA: O^T += V^T P^T with P = hi + lo (bf16)
-                u32x4_t phi, plo;
+                    // shared values on MFMA: O^T += V^T P^T with P = hi + lo (bf16)
+                    u32x4_t phi, plo;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t h0 = f32_to_bf16_bits(ev[2 * i]), h1 = f32_to_bf16_bits(ev[2 * i + 1]);
-                    const float r0 = ev[2 * i] - __uint_as_float(h0 << 16);
-                    const float r1 = ev[2 * i + 1] - __uint_as_float(h1 << 16);
-                    phi[i] = h0 | (h1 << 16);
-                    plo[i] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t h0 = f32_to_bf16_bits(ev[2 * i]), h1 = f32_to_bf16_bits(ev[2 * i + 1]);
+                        const float r0 = ev[2 * i] - __uint_as_float(h0 << 16);
+                        const float r1 = ev[2 * i + 1] - __uint_as_float(h1 << 16);
+                        phi[i] = h0 | (h1 << 16);
+                        plo[i] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+                    }
 #pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb) {
-                    acc_sh[cb] *= alpha;
-                    const int c = 16 * cb + n16;
-                    const u32x2_t v0 = *(const u32x2_t*)(vt + c * C::VTS + 4 * g4);
-                    const u32x2_t v1 = *(const u32x2_t*)(vt + c * C::VTS + 16 + 4 * g4);
-                    const uint32_t a0 = v0[0], a1 = v0[1], a2 = v1[0], a3 = v1[1];
-                    const u32x4_t av = {a0, a1, a2, a3};
-                    acc_sh[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, phi), acc_sh[cb], 0, 0, 0);
-                    acc_sh[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, plo), acc_sh[cb], 0, 0, 0);
+                    for (int cb = 0; cb < C::CB; ++cb) {
+                        acc_sh[qi][cb] *= alpha;
+                        const int c = 16 * cb + n16;
+                        const u32x2_t v0 = *(const u32x2_t*)(vt + c * C::VTS + 4 * g4);
+                        const u32x2_t v1 = *(const u32x2_t*)(vt + c * C::VTS + 16 + 4 * g4);
+                        const uint32_t a0 = v0[0], a1 = v0[1], a2 = v1[0], a3 = v1[1];
+                        const u32x4_t av = {a0, a1, a2, a3};
+                        const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
+                        acc_sh[qi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, phi),
+                                                                                acc_sh[qi][cb], 0, 0, 0);
+                        acc_sh[qi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, plo),
+                                                                                acc_sh[qi][cb], 0, 0, 0);
+                    }
                 }
+                wave_lds_sync();  // weights and alphas visible to the private-value units
             }
         }
         wave_lds_sync();  // V^T and weights consumed before the next block rewrites them
     }
 
-    // ---- merge the row lanes of each head group (fixed order), one record per head ----
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (g4 == 0) mw_lds[wave * 16 + n16] = m_run;
-    __syncthreads();  // all waves done with their tiles; running maxima visible
-    float* mg = (float*)wave_base;  // [H][REC], aliases the per-wave areas
-    float M = -INFINITY;
-    for (int t = 0; t < C::NTL; ++t) M = fmaxf(M, mw_lds[(t * C::NHG + hg) * 16 + n16]);
-    const float fsh = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-    float fpr[OCTS];
+    // ---- merge the row lanes of each head group (fixed order), one record per (query, head) ----
+    // (records of workgroup w = W_b + split: [QW][H] at (w * QW + qi) * H; the next query's pass starts
+    // with a barrier after every wave has copied this one's records out)
 #pragma unroll
-    for (int oi = 0; oi < OCTS; ++oi) {
-        const int n = 8 * oi + hh;
-        float Mo = -INFINITY;
-        for (int t = 0; t < C::NTL; ++t) Mo = fmaxf(Mo, mw_lds[(t * C::NHG + hg) * 16 + n]);
-        const float mine = mw_lds[wave * 16 + n];
-        fpr[oi] = (mine == -INFINITY) ? 0.f : fast_exp2(mine - Mo);
-    }
-    const int head = 16 * hg + n16;
-    for (int t = 0; t < C::NTL; ++t) {
-        if (tl == t && head < H) {
-            float* row = mg + head * C::REC;
+    for (int qi = 0; qi < QW; ++qi) {
+        float l_q = l_run[qi];
+        l_q += __shfl_xor(l_q, 16);
+        l_q += __shfl_xor(l_q, 32);
+        if (g4 == 0) mw_lds[wave * 16 + n16] = m_run[qi];
+        __syncthreads();  // all waves done with their tiles (or the previous query's copy); maxima visible
+        float* mg = (float*)wave_base;  // [H][REC], aliases the per-wave areas
+        float M = -INFINITY;
+        for (int t = 0; t < C::NTL; ++t) M = fmaxf(M, mw_lds[(t * C::NHG + hg) * 16 + n16]);
+        const float fsh = (m_run[qi] == -INFINITY) ? 0.f : fast_exp2(m_run[qi] - M);
+        float fpr[OCTS];
 #pragma unroll
-            for (int cb = 0; cb < C::CB; ++cb) {
-                const f32x4_t v = acc_sh[cb] * fsh;
-                f32x4_t* dst = (f32x4_t*)(row + 16 * cb + 4 * g4);
-                *dst = (t == 0) ? v : (*dst + v);
-            }
-            if (g4 == 0) {
-                const float lv = l_run * fsh;
-                row[D + R + 1] = (t == 0) ? lv : row[D + R + 1] + lv;
-                if (t == 0) row[D + R] = M;
-            }
+        for (int oi = 0; oi < OCTS; ++oi) {
+            const int n = 8 * oi + hh;
+            float Mo = -INFINITY;
+            for (int t = 0; t < C::NTL; ++t) Mo = fmaxf(Mo, mw_lds[(t * C::NHG + hg) * 16 + n]);
+            const float mine = mw_lds[wave * 16 + n];
+            fpr[oi] = (mine == -INFINITY) ? 0.f : fast_exp2(mine - Mo);
         }
-        if (tl == t) {
+        const int head = 16 * hg + n16;
+        for (int t = 0; t < C::NTL; ++t) {
+            if (tl == t && head < H) {
+                float* row = mg + head * C::REC;
 #pragma unroll
-            for (int oi = 0; oi < OCTS; ++oi) {
-                float* row = mg + (16 * hg + 8 * oi + hh) * C::REC + D + sl * EPL;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const float v = acc_pr[oi][e] * fpr[oi];
-                    row[e] = (t == 0) ? v : row[e] + v;
+                for (int cb = 0; cb < C::CB; ++cb) {
+                    const f32x4_t v = acc_sh[qi][cb] * fsh;
+                    f32x4_t* dst = (f32x4_t*)(row + 16 * cb + 4 * g4);
+                    *dst = (t == 0) ? v : (*dst + v);
+                }
+                if (g4 == 0) {
+                    const float lv = l_q * fsh;
+                    row[D + R + 1] = (t == 0) ? lv : row[D + R + 1] + lv;
+                    if (t == 0) row[D + R] = M;
                 }
             }
+            if (tl == t) {
+#pragma unroll
+                for (int oi = 0; oi < OCTS; ++oi) {
+                    float* row = mg + (16 * hg + 8 * oi + hh) * C::REC + D + sl * EPL;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) {
+                        const float v = acc_pr[qi][oi][e] * fpr[oi];
+                        row[e] = (t == 0) ? v : row[e] + v;
+                    }
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
+        float* out = a.ws + ((size_t)blockIdx.x * QW + qi) * H * C::REC;
+        for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
     }
-    float* out = a.ws + (size_t)blockIdx.x * H * C::REC;  // record of workgroup w = W_b + split
-    for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
 }
 
-template <int D, int R, int H, int OCC, bool NORM>
+template <int D, int R, int H, int OCC, bool NORM, int QW>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-    using C = Cfg<D, R, H, OCC>;
-    auto kern = split_mfma_kernel<D, R, H, OCC, NORM>;
+    using C = Cfg<D, R, H, OCC, QW>;
+    auto kern = split_mfma_kernel<D, R, H, OCC, NORM, QW>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
-// the normalised variant is built for one wave per SIMD only
-template <int D, int R, int H, bool NORM>
-hipError_t launch_dhr(const DecodeArgs& a, int occ, hipStream_t stream) {
-    if constexpr (NORM) return launch_one<D, R, H, 1, true>(a, stream);
-    else return occ == 1 ? launch_one<D, R, H, 1, false>(a, stream) : launch_one<D, R, H, 2, false>(a, stream);
+// Four queries per wave do not fit the register file at d_h = 128, r = 64 (the compiled kernel spills in its
+// main loop); those shapes serve at most two (mfma_max_query_width, k_decode_mfma.hip).
+template <int D, int R, int H>
+constexpr bool query_width_fits(int qw) {
+    return qw <= 2 || !(D == 128 && R == 64);
 }
 
-template <int D, int H, bool NORM>
+// the normalised variant and the several-query instances are built for one wave per SIMD only
+template <int D, int R, int H, bool NORM, int QW>
+hipError_t launch_dhr(const DecodeArgs& a, int occ, hipStream_t stream) {
+    if constexpr (!query_width_fits<D, R, H>(QW)) return hipErrorInvalidValue;
+    else if constexpr (NORM || QW > 1) return launch_one<D, R, H, 1, NORM, QW>(a, stream);
+    else return occ == 1 ? launch_one<D, R, H, 1, false, 1>(a, stream) : launch_one<D, R, H, 2, false, 1>(a, stream);
+}
+
+template <int D, int H, bool NORM, int QW>
 hipError_t launch_r(const DecodeArgs& a, int occ, hipStream_t stream) {
     switch (a.r) {
-        case 0: return launch_dhr<D, 0, H, NORM>(a, occ, stream);
-        case 8: return launch_dhr<D, 8, H, NORM>(a, occ, stream);
-        case 16: return launch_dhr<D, 16, H, NORM>(a, occ, stream);
-        case 32: return launch_dhr<D, 32, H, NORM>(a, occ, stream);
-        case 48: return launch_dhr<D, 48, H, NORM>(a, occ, stream);
-        case 64: return launch_dhr<D, 64, H, NORM>(a, occ, stream);
+        case 0: return launch_dhr<D, 0, H, NORM, QW>(a, occ, stream);
+        case 8: return launch_dhr<D, 8, H, NORM, QW>(a, occ, stream);
+        case 16: return launch_dhr<D, 16, H, NORM, QW>(a, occ, stream);
+        case 32: return launch_dhr<D, 32, H, NORM, QW>(a, occ, stream);
+        case 48: return launch_dhr<D, 48, H, NORM, QW>(a, occ, stream);
+        case 64: return launch_dhr<D, 64, H, NORM, QW>(a, occ, stream);
     }
     return hipErrorInvalidValue;
 }
 
-template <int D, bool NORM>
+template <int D, bool NORM, int QW = 1>
 hipError_t launch_h(const DecodeArgs& a, int occ, hipStream_t stream) {
     switch (a.H) {
-        case 8: return launch_r<D, 8, NORM>(a, occ, stream);
-        case 16: return launch_r<D, 16, NORM>(a, occ, stream);
-        case 32: return launch_r<D, 32, NORM>(a, occ, stream);
+        case 8: return launch_r<D, 8, NORM, QW>(a, occ, stream);
+        case 16: return launch_r<D, 16, NORM, QW>(a, occ, stream);
+        case 32: return launch_r<D, 32, NORM, QW>(a, occ, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -13,7 +13,11 @@
 //
 // Split s of sequence b is the partial record of workgroup W_b + s of the
 // split launch (splits dealt to sequences by length; see lrkv_device.hpp);
-// only splits with s * granule < L_b hold live rows.
+// only splits with s * granule < L_b hold live rows.  Multi-token decode with
+// Q query tokens per sequence runs virtual sequences of qw tokens each
+// (ceil(Q / qw) per sequence); a workgroup then holds qw records per head, and
+// token i of sequence b reads record i % qw of the splits of its virtual
+// sequence, live up to its own causal length.
 //
 // One workgroup per (b, h) of 256 threads times 1 or 4 split groups: thread (column c, split group j)
 // walks splits s = j, j + 4, ... of column c once, in batches of 16 whose
@@ -48,8 +52,9 @@ __device__ __forceinline__ float vec_elem(const u32x4_t& v, int e) {
 // kGroups split groups of kCols threads each: 4 groups when sequences hold many splits, 1 when they
 // hold few (then the extra threads would only wait).
 template <typename T, int kGroups>
-__global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H, int D, int R, int max_len,
-                                                                int chunk, int S, const int32_t* __restrict__ seq_lens,
+__global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int nv, int Q, int qw, int H, int D, int R,
+                                                                int max_len, int chunk, int S,
+                                                                const int32_t* __restrict__ seq_lens,
                                                                 const T* __restrict__ B_v, float* __restrict__ out,
                                                                 const float* __restrict__ ws) {
     constexpr int kMergeThreads = kGroups * kCols;
@@ -58,9 +63,15 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H
     __shared__ float gsum[kGroups][kCols];   // per-group rescaled sums
     __shared__ float sums[kMaxCols + 2];     // merged numerators, then l at [D + R]
     __shared__ float epi[kMergeThreads];     // epilogue partial products
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;  // output row = sequence * Q + token
     const int rec = partial_record_floats(D, R);
-    float* o = out + ((size_t)b * H + h) * D;
+    float* o = out + ((size_t)row * H + h) * D;
+    // the virtual sequence v holding token i of sequence b, the token's slot qi in it and its causal length
+    const int nc = (Q + qw - 1) / qw;
+    const int b = row / Q, i = row - b * Q;
+    const int c = i / qw, qi = i - c * qw;
+    const int v = b * nc + c;
+    const int nreal = min(qw, Q - c * qw);
 
     // epilogue operand: thread (c, vi) holds B^V[h][c][vi*VE, vi*VE + VE) as one 16-byte vector
     const int nvv = (R > 0 && (R % VE) == 0) ? R / VE : 0;
@@ -69,16 +80,16 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H
     const int ec = vec_epi ? tid / nvv : 0, evi = vec_epi ? tid % nvv : 0;
     if (vec_epi && ec < D) bv = *(const u32x4_t*)(B_v + ((size_t)h * D + ec) * R + evi * VE);
 
-    const int Lb = clamped_len(seq_lens, b, max_len);
+    const int Lb = max(0, clamped_len(seq_lens, v, max_len) - (nreal - 1 - qi));
     int W_b, S_b;
-    sequence_splits(seq_lens, batch, max_len, S, b, &W_b, &S_b);  // every wave computes the same values
+    sequence_splits(seq_lens, nv, max_len, S, v, &W_b, &S_b);  // every wave computes the same values
     const int Sb = min(S_b, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold rows
     if (Sb == 0) {
         for (int c = tid; c < D; c += kMergeThreads) o[c] = 0.f;
         return;
     }
-    const float* base = ws + ((size_t)W_b * H + h) * rec;  // split s at base + s * H * rec
-    const int sstride = H * rec;  // the workspace is far below 2^31 floats
+    const float* base = ws + (((size_t)W_b * qw + qi) * H + h) * rec;  // split s at base + s * qw * H * rec
+    const int sstride = qw * H * rec;  // the workspace is below 2^31 floats
 
     // numerators (columns 0 .. D+R-1) and the denominator (column D+R+1) in passes of kCols columns
     const int ncols = D + R + 2;
@@ -170,20 +181,21 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int batch, int H
 
 }  // namespace
 
-hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk,
+hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dtype, int max_len, int chunk,
                         int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
                         hipStream_t stream) {
-    if (d_h + r > kMaxCols) return hipErrorInvalidValue;
+    if (d_h + r > kMaxCols || Q < 1 || qw < 1) return hipErrorInvalidValue;
+    const int nv = batch * ((Q + qw - 1) / qw);  // sequences of the split launch
     // one split group per column when sequences average at most 16 splits, four otherwise
-    const bool wide = num_splits > 16 * batch;
-    dim3 grid(H, batch), block(wide ? 4 * kCols : kCols);
+    const bool wide = num_splits > 16 * nv;
+    dim3 grid(H, batch * Q), block(wide ? 4 * kCols : kCols);
     if (dtype == 0) {
         auto k = wide ? merge_kernel<float, 4> : merge_kernel<float, 1>;
-        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits, seq_lens,
+        hipLaunchKernelGGL(k, grid, block, 0, stream, nv, Q, qw, H, d_h, r, max_len, chunk, num_splits, seq_lens,
                            (const float*)B_v, out, ws);
     } else {
         auto k = wide ? merge_kernel<uint16_t, 4> : merge_kernel<uint16_t, 1>;
-        hipLaunchKernelGGL(k, grid, block, 0, stream, batch, H, d_h, r, max_len, chunk, num_splits, seq_lens,
+        hipLaunchKernelGGL(k, grid, block, 0, stream, nv, Q, qw, H, d_h, r, max_len, chunk, num_splits, seq_lens,
                            (const uint16_t*)B_v, out, ws);
     }
     return hipGetLastError();

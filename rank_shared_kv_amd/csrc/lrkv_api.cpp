@@ -92,8 +92,9 @@ constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's 
 // SIMD; neither it nor the paged cache has an fp32 matrix-core kernel (the general kernel serves them).  Their
 // G never exceeds the plain plan's, so the plain workspace size serves them, and a paged decode of a bf16
 // matrix-core shape uses exactly the plain plan.  The rotary variant has kernels of its own (two resident
-// workgroups per CU for the bf16 one) and its own workspace query.
-enum class PlanVariant { kPlain, kNormed, kPaged, kRope };
+// workgroups per CU for the bf16 one) and its own workspace query.  Query sets (multi-token decode with
+// several tokens per workgroup) run the bf16 matrix-core kernel at one wave per SIMD.
+enum class PlanVariant { kPlain, kNormed, kPaged, kRope, kQuerySets };
 
 bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVariant variant = PlanVariant::kPlain) {
     using namespace lrkv;
@@ -199,10 +200,14 @@ struct PagedView {  // the paged layout of a cache handed to run_partial (block_
     int page_shift = 0, max_pages = 0, n_pages = 0;
 };
 
+struct QuerySets {  // multi-token decode: virtual sequences of qw query tokens, qgroup per cached sequence
+    int qgroup = 1, n_queries = 1, qw = 1;
+};
+
 lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, const void* q, const float* p,
                         void* ws, const lrkv::SplitPlan& plan, hipStream_t stream, const void* rho = nullptr,
-                        const PagedView& pv = PagedView(), int qgroup = 1, const float* rope_cs = nullptr,
-                        const void* rope_bk = nullptr) {
+                        const PagedView& pv = PagedView(), const QuerySets& qs = QuerySets(),
+                        const float* rope_cs = nullptr, const void* rope_bk = nullptr) {
     using namespace lrkv;
     if (plan.num_splits == 0) return LRKV_OK;
     DecodeArgs a{};
@@ -215,7 +220,9 @@ lrkv_status run_partial(const lrkv_dims& d, const lrkv_cache& c, int max_len, co
     a.max_len = max_len;
     a.chunk = plan.chunk;
     a.num_splits = plan.num_splits;
-    a.qgroup = qgroup;
+    a.qgroup = qs.qgroup;
+    a.n_queries = qs.n_queries;
+    a.qw = qs.qw;
     a.k_shared = c.k_shared;
     a.v_shared = c.v_shared;
     a.z_k = c.z_k;
@@ -344,7 +351,7 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
     LRKV_TRY(need_ptr(out, "out"));
     if (dims->r > 0) LRKV_TRY(need_ptr(B_v, "B_v"));
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -365,7 +372,7 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, workspace, plan, (hipStream_t)stream));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -376,21 +383,38 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
 
 namespace {
 
-// Multi-token decode runs as single-token decode of batch * Q virtual sequences: query i of sequence b is
-// virtual sequence b * Q + i, which reads sequence b's cache up to its causal length seq_lens[b] - Q + 1 + i.
-// The workspace holds the plan's partial records, then the virtual lengths (256-byte aligned parts).
+// Multi-token decode runs as single-token decode of virtual sequences, each a set of qw consecutive query
+// tokens of one cached sequence: set c of sequence b is virtual sequence b * nc + c (nc = ceil(Q / qw)) and
+// reads sequence b's cache up to the causal length of its last token (token i sees seq_lens[b] - Q + 1 + i
+// rows).  Shapes of the bf16 matrix-core kernel take qw = 2 (Q = 2) or 4 (Q >= 3): one workgroup serves the
+// whole set from one read of the rows (qw = 2 at most for d_h = 128, r = 64, where four queries' state does
+// not fit the registers).  Other shapes take qw = 1, one virtual sequence per token.  Tuning
+// override (read at every call, so it must not change between a workspace query and the decode that uses it):
+// LRKV_MULTI_QW (1, 2 or 4).  The workspace holds the plan's partial records ([G][qw][H][record]), then the
+// virtual lengths (256-byte aligned parts).
 struct MultiPlan {
     lrkv_dims dq;         // dims of the virtual batch
     lrkv::SplitPlan plan;
+    int qw;               // query tokens per virtual sequence
     size_t records_bytes, total_bytes;
 };
 
 bool plan_multi(const lrkv_dims& d, int Q, int max_len, MultiPlan* mp) {
     if (Q < 1 || Q > 64 || (long long)d.batch * Q > 65535) return false;
+    int qw = 1;
+    if (Q > 1 && lrkv::mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+        const int qmax = lrkv::mfma_max_query_width(d.H, d.d_h, d.r);
+        qw = env_int("LRKV_MULTI_QW", Q == 2 ? 2 : qmax);
+        if (qw != 1 && qw != 2 && qw != 4) qw = qmax;
+        qw = std::min(qw, qmax);
+    }
+    mp->qw = qw;
     mp->dq = d;
-    mp->dq.batch = d.batch * Q;
-    if (!plan_split(mp->dq, max_len, &mp->plan)) return false;
-    mp->records_bytes = (workspace_bytes(mp->dq, mp->plan) + 255) & ~(size_t)255;
+    mp->dq.batch = d.batch * ((Q + qw - 1) / qw);
+    if (!plan_split(mp->dq, max_len, &mp->plan, qw > 1 ? PlanVariant::kQuerySets : PlanVariant::kPlain)) return false;
+    if ((long long)mp->plan.num_splits * qw * d.H * lrkv::partial_record_floats(d.d_h, d.r) >= (1LL << 31))
+        return false;  // the merge kernel addresses the records with 32-bit offsets
+    mp->records_bytes = (qw * workspace_bytes(mp->dq, mp->plan) + 255) & ~(size_t)255;
     mp->total_bytes = mp->records_bytes + (((size_t)mp->dq.batch * sizeof(int32_t) + 255) & ~(size_t)255);
     return true;
 }
@@ -429,12 +453,17 @@ lrkv_status lrkv_decode_multi(const lrkv_dims* dims, int32_t n_queries, const lr
     if (workspace_bytes_ < mp.total_bytes)
         return fail(LRKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes_, mp.total_bytes);
     int32_t* vlens = (int32_t*)((char*)workspace + mp.records_bytes);
-    hipError_t e = lrkv::launch_multi_lengths(dims->batch, n_queries, cache->seq_lens, vlens, (hipStream_t)stream);
+    hipError_t e =
+        lrkv::launch_multi_lengths(dims->batch, n_queries, mp.qw, cache->seq_lens, vlens, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "length kernel launch");
     const lrkv_cache vc{cache->k_shared, cache->v_shared, cache->z_k, cache->z_v, vlens};
-    LRKV_TRY(run_partial(mp.dq, vc, max_len, q, p, workspace, mp.plan, (hipStream_t)stream, nullptr, PagedView(),
-                         n_queries));
-    e = lrkv::launch_merge(mp.dq.batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, mp.plan.chunk,
+    QuerySets qs;
+    qs.qgroup = (n_queries + mp.qw - 1) / mp.qw;
+    qs.n_queries = n_queries;
+    qs.qw = mp.qw;
+    LRKV_TRY(run_partial(mp.dq, vc, max_len, q, p, workspace, mp.plan, (hipStream_t)stream, nullptr, PagedView(), qs));
+    e = lrkv::launch_merge(dims->batch, n_queries, mp.qw, dims->H, dims->d_h, dims->r, dims->dtype, max_len,
+                           mp.plan.chunk,
                            mp.plan.num_splits, vlens, B_v, out, (const float*)workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ok();
@@ -491,7 +520,7 @@ lrkv_status lrkv_decode_normed(const lrkv_dims* dims, const lrkv_cache* cache, c
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q_eff, p, workspace, plan, (hipStream_t)stream, rho));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -576,7 +605,7 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     const lrkv_cache pools{cache->k_pages, cache->v_pages, cache->zk_pages, cache->zv_pages, cache->seq_lens};
     LRKV_TRY(run_partial(*dims, pools, max_len, q, p, workspace, plan, (hipStream_t)stream, nullptr, pv));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+    hipError_t e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -626,8 +655,8 @@ lrkv_status lrkv_decode_rope(const lrkv_dims* dims, const lrkv_cache* cache, int
     }
     LRKV_TRY(check_workspace(*dims, plan, workspace, workspace_bytes_));
     LRKV_TRY(run_partial(*dims, *cache, max_len, q, nullptr, workspace, plan, (hipStream_t)stream, nullptr,
-                         PagedView(), 1, table, B_k));
-    hipError_t e = lrkv::launch_merge(dims->batch, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                         PagedView(), QuerySets(), table, B_k));
+    hipError_t e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");

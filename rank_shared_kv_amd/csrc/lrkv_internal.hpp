@@ -15,7 +15,11 @@ struct DecodeArgs {
     int chunk;           // split granule in rows: split s holds live rows iff s * chunk < L_b
     int num_splits;      // G: workgroups of the launch = partial records per head (shared by the batch)
     int qgroup;          // virtual sequences per cached sequence: sequence b reads cache sequence b / qgroup
-                         // (multi-token decode: one virtual sequence per query token, with its causal length)
+                         // (multi-token decode: one virtual sequence per set of qw query tokens, with the causal
+                         // length of the set's last token)
+    int n_queries;       // multi-token decode: query tokens per cached sequence (q and p rows [batch][n_queries][H])
+    int qw;              // query tokens per virtual sequence: 1, or 2 / 4 for the bf16 matrix-core kernel, which
+                         // then writes qw records per workgroup and head ([G][qw][H][record])
     const void* k_shared;
     const void* v_shared;
     const void* z_k;
@@ -59,6 +63,7 @@ bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);      // bf
 bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap);  // fp32 MFMA kernel (r = 0)
 int mfma_f32_rows_per_tile();  // rows one fp32 MFMA-kernel split advances per step
 int mfma_rows_per_tile(int H);  // rows one MFMA-kernel workgroup advances per step
+int mfma_max_query_width(int H, int d_h, int r);  // multi-token decode: query tokens per bf16 MFMA workgroup (2 or 4)
 bool general_path_supports(int H, int d_h, int r);
 bool rope_mfma_path_supports(int H, int d_h, int r, int dtype);  // rotary variant, bf16 matrix-core kernel
 int rope_mfma_rows_per_tile();
@@ -73,7 +78,10 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
-hipError_t launch_merge(int batch, int H, int d_h, int r, int dtype, int max_len, int chunk,
+// Merge of a decode of `batch` cached sequences with Q query tokens each, split as virtual sequences of qw
+// tokens (ceil(Q / qw) per cached sequence; seq_lens are their lengths, num_splits the split launch's G);
+// out [batch][Q][H][d_h].  Single-token decode: Q = qw = 1.
+hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dtype, int max_len, int chunk,
                         int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
                         hipStream_t stream);
 int general_rows_per_tile();  // rows one general-kernel split advances per step
@@ -84,8 +92,11 @@ hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int d
                               const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
                               const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
                               hipStream_t stream);
-// lens_out[b * Q + i] = max(0, seq_lens[b] - Q + 1 + i): the rows query token i of sequence b sees
-hipError_t launch_multi_lengths(int batch, int Q, const int32_t* seq_lens, int32_t* lens_out, hipStream_t stream);
+// Virtual lengths of a multi-token decode split into sets of qw tokens: lens_out[b * nc + c] (nc = ceil(Q / qw))
+// is the number of rows the last token of set c of sequence b sees, max(0, seq_lens[b] - Q + 1 + last) with
+// last = min((c + 1) * qw, Q) - 1 (token i sees seq_lens[b] - Q + 1 + i rows)
+hipError_t launch_multi_lengths(int batch, int Q, int qw, const int32_t* seq_lens, int32_t* lens_out,
+                                hipStream_t stream);
 hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int page_shift, int max_pages,
                               void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
                               const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,

@@ -209,17 +209,37 @@ def test_split_plan_arithmetic():
     assert lk.lrkv_decode_workspace_bytes(d, 0) == 0
 
 
-def test_multi_query_plan_arithmetic():
-    """Multi-token decode plans batch * Q virtual sequences: the single-token plan of that batch, then the
-    virtual lengths, each part 256-byte aligned."""
+def test_multi_query_plan_arithmetic(monkeypatch):
+    """Multi-token decode plans virtual sequences of qw query tokens each (ceil(Q / qw) per sequence): qw = 2
+    (Q = 2) or 4 (Q >= 3, but 2 at d_h = 128 and r = 64) on the bf16 matrix-core shapes, one workgroup per SIMD,
+    so G is the single-token plan's G of the virtual batch capped at 256; qw = 1 elsewhere (the single-token
+    plan of batch * Q virtual sequences).  Workspace: G * qw * H records, then the virtual lengths, each part
+    256-byte aligned."""
     al = lambda n: (n + 255) // 256 * 256
-    for (B, H, d_h, r, L, dt, Q) in [(4, 32, 128, 64, 33024, 1, 4), (4, 32, 128, 64, 33024, 1, 16),
-                                     (2, 4, 16, 4, 128, 0, 3), (3, 8, 64, 16, 512, 1, 1)]:
+    rec = lambda d_h, r: 4 * ((d_h + r + 2 + 3) // 4 * 4)
+    monkeypatch.delenv("LRKV_MULTI_QW", raising=False)
+    for (B, H, d_h, r, L, dt, Q, qw) in [(4, 32, 128, 64, 33024, 1, 4, 2), (4, 32, 128, 64, 33024, 1, 16, 2),
+                                         (4, 16, 128, 48, 8192, 1, 4, 4), (4, 32, 64, 64, 4096, 1, 7, 4),
+                                         (2, 16, 128, 32, 4096, 1, 2, 2), (64, 32, 128, 32, 33024, 1, 3, 4),
+                                         (2, 8, 64, 16, 256, 1, 5, 4), (2, 4, 16, 4, 128, 0, 3, 1),
+                                         (3, 8, 64, 16, 512, 1, 1, 1)]:
         d = lk.make_dims(B, H, d_h, r, L, dt)
-        dq = lk.make_dims(B * Q, H, d_h, r, L, dt)
-        want = al(lk.lrkv_decode_workspace_bytes(dq, L)) + al(4 * B * Q)
-        assert lk.lrkv_decode_multi_workspace_bytes(d, Q, L) == want
-    d = lk.make_dims(4, 32, 128, 64, 33024, 1)
+        nv = B * -(-Q // qw)
+        dq = lk.make_dims(nv, H, d_h, r, L, dt)
+        if qw == 1:
+            want = al(lk.lrkv_decode_workspace_bytes(dq, L)) + al(4 * nv)
+        else:
+            G = min(lk.lrkv_decode_num_splits(dq, L)[0], 256)
+            want = al(G * qw * H * rec(d_h, r)) + al(4 * nv)
+        assert lk.lrkv_decode_multi_workspace_bytes(d, Q, L) == want, (B, H, d_h, r, Q)
+    # the override selects one token per workgroup (the single-token plan of batch * Q sequences); four tokens
+    # are capped at two where they do not fit
+    monkeypatch.setenv("LRKV_MULTI_QW", "1")
+    d, dq = lk.make_dims(4, 32, 128, 64, 33024, 1), lk.make_dims(16, 32, 128, 64, 33024, 1)
+    assert lk.lrkv_decode_multi_workspace_bytes(d, 4, 33024) == al(lk.lrkv_decode_workspace_bytes(dq, 33024)) + 256
+    monkeypatch.setenv("LRKV_MULTI_QW", "4")
+    assert lk.lrkv_decode_multi_workspace_bytes(d, 4, 33024) == al(256 * 2 * 32 * rec(128, 64)) + 256
+    monkeypatch.delenv("LRKV_MULTI_QW")
     assert lk.lrkv_decode_multi_workspace_bytes(d, 0, 100) == 0
     assert lk.lrkv_decode_multi_workspace_bytes(d, 65, 100) == 0
     assert lk.lrkv_decode_multi_workspace_bytes(lk.make_dims(2048, 8, 64, 8, 256, 1), 64, 100) == 0  # > 65535

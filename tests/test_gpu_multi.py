@@ -1,5 +1,9 @@
 """GPU parity of multi-token decode (Q query tokens per sequence, causal inside the chunk) against the fp64
-reference, through the C ABI.  Metric and tolerances as in test_gpu_decode.py."""
+reference, through the C ABI.  Metric and tolerances as in test_gpu_decode.py.  On the bf16 matrix-core shapes
+every case also runs with each number of query tokens per workgroup (LRKV_MULTI_QW = 1, 2, 4) besides the
+default choice."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -64,17 +68,32 @@ CASES = [  # (dtype, batch, Q, H, d_h, r, lengths)
     ("bf16", 4, 8, 32, 128, 64, [2100, 1500, 17, 8]),
     ("bf16", 2, 64, 8, 64, 16, [200, 64]),
     ("bf16", 3, 4, 16, 128, 0, [333, 40, 4]),
+    ("bf16", 2, 5, 16, 128, 32, [96, 40]),     # Q = 5: the last set of four holds one token
+    ("bf16", 2, 4, 32, 128, 64, [33, 65]),     # last block: one row, seen by the last token only
+    ("bf16", 3, 3, 8, 64, 48, [97, 129, 2]),   # four row lanes; last block of one row
 ]
 
 
+@pytest.fixture(params=[None, "1", "2", "4"], ids=["qw_auto", "qw1", "qw2", "qw4"])
+def query_width(request, monkeypatch):
+    """LRKV_MULTI_QW for the call (None: the library's choice)."""
+    if request.param is None:
+        monkeypatch.delenv("LRKV_MULTI_QW", raising=False)
+    else:
+        monkeypatch.setenv("LRKV_MULTI_QW", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}_B{c[1]}_Q{c[2]}_H{c[3]}_d{c[4]}_r{c[5]}")
-def test_multi_query_matches_reference(case):
+def test_multi_query_matches_reference(case, query_width):
     dtype, B, Q, H, d_h, r, lens = case
+    if query_width is not None and dtype != "bf16":
+        pytest.skip("the query-set width applies to the bf16 matrix-core kernel only")
     L = max(lens)
     w = synth.WORKLOADS["small_bf16"].with_(name="multi", batch=B, H=H, d_h=d_h, r=r, dtype=dtype, L=L,
                                             L_cap=(L + 31) // 32 * 32 + 32, ragged_lo=None)
     lens = np.array(lens, dtype=np.int32)
-    say(f"[case] multi-query {case}")
+    say(f"[case] multi-query {case} LRKV_MULTI_QW={os.environ.get('LRKV_MULTI_QW')}")
     dev = sdev.fill_layer(w, 0, lengths=lens)
     qh = synth.normal(9100 + B, 1.0, B * Q * H * d_h, dtype).reshape(B, Q, H, d_h)
     got = _multi_gpu(w, dev, Q, qh, L).cpu().numpy()
