@@ -186,8 +186,10 @@ hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dty
                         hipStream_t stream) {
     if (d_h + r > kMaxCols || Q < 1 || qw < 1) return hipErrorInvalidValue;
     const int nv = batch * ((Q + qw - 1) / qw);  // sequences of the split launch
-    // one split group per column when sequences average at most 16 splits, four otherwise
-    const bool wide = num_splits > 16 * nv;
+    // one split group per column when sequences average at most 32 splits (two batches per thread), four
+    // otherwise (4-token decode at long context, 32 splits per token set: 8.0 us with one group, 11.1 us
+    // with four)
+    const bool wide = num_splits > 32 * nv;
     dim3 grid(H, batch * Q), block(wide ? 4 * kCols : kCols);
     if (dtype == 0) {
         auto k = wide ? merge_kernel<float, 4> : merge_kernel<float, 1>;
