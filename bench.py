@@ -2,8 +2,8 @@
 """Benchmark of LRKV factored decode on one MI355X.
 
 One step is one decode step of the whole path on a batch of sequences:
-  append the new token's projected rows -> absorb the query (p = q B^K) ->
-  split-L partial pass -> split merge + B^V epilogue,
+  append the new token's projected rows + absorb the query (p = q B^K), one
+  launch -> split-L partial pass -> split merge + B^V epilogue,
 all through the C ABI on one HIP stream, with the inputs resident in HBM.
 Before the timed region the caches hold L - 1 - warmup rows per sequence, so
 the first timed step decodes over exactly L rows; every step appends one row,
@@ -315,11 +315,12 @@ def main():
             lk.lrkv_project_append(dims, d_model, cache, x_new, W_in, q_step, stream)
             e_p1 = ev() if timed else None
             q_use = q_step
-        else:
-            lk.lrkv_cache_append(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, stream)
+            if w.r:
+                lk.lrkv_absorb_query(dims, q_use, dev["B_k"], p, stream)
+        else:  # the append and the query absorption in one launch
             q_use = dev["q"]
-        if w.r:
-            lk.lrkv_absorb_query(dims, q_use, dev["B_k"], p, stream)
+            lk.lrkv_append_absorb(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, q_use,
+                                  dev["B_k"] if w.r else None, pp, stream)
         if timed:
             e0 = ev()
         lk.lrkv_decode_partial(dims, cache, max_len, q_use, pp, ws, nbytes, stream)

@@ -132,6 +132,19 @@ lrkv_status lrkv_absorb_query(const lrkv_dims* dims, const void* q, const void* 
 lrkv_status lrkv_cache_append(const lrkv_dims* dims, const lrkv_cache* cache, const void* k_new, const void* v_new,
                               const void* zk_new, const void* zv_new, void* stream);
 
+/* The two per-token operations of a decode step in one launch: lrkv_cache_append
+ * of (k_new, v_new, zk_new, zv_new) and lrkv_absorb_query of (q, B_k) into p,
+ * with the same arguments, layouts and results (bit for bit) as the two calls
+ * (review sec. 3, Algorithms 1 and 2; reading notes secs. 2.3-2.4).  They
+ * touch disjoint memory, so their workgroups run side by side and the step
+ * pays one kernel launch instead of two.  r == 0: the append alone (q, B_k, p
+ * may be NULL).  Shapes outside the absorb's vector path (r not a multiple of
+ * 8 in bf16 or 4 in fp32, or d_h > 256) run the two kernels one after the
+ * other. */
+lrkv_status lrkv_append_absorb(const lrkv_dims* dims, const lrkv_cache* cache, const void* k_new, const void* v_new,
+                               const void* zk_new, const void* zv_new, const void* q, const void* B_k, float* p,
+                               void* stream);
+
 /* Bytes of device workspace lrkv_decode / lrkv_decode_partial need for these
  * dims and this max_len: G x H x align4(d_h + r + 2) floats, G as returned by
  * lrkv_decode_num_splits.  Host arithmetic only.  Returns 0 for invalid dims. */

@@ -25,7 +25,7 @@ LRKV_ERR_HIP = 4
 LRKV_F32 = 0
 LRKV_BF16 = 1
 
-EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
+EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_append_absorb", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_multi_workspace_bytes",
             "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table",
             "lrkv_decode_rope_workspace_bytes", "lrkv_decode_rope", "lrkv_key_scales", "lrkv_norm_query",
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "lrkv_absorb_query": ([D, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_cache_append": ([D, C, vp, vp, vp, vp, vp], ctypes.c_int),
+            "lrkv_append_absorb": ([D, C, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_workspace_bytes": ([D, i32], sz),
             "lrkv_decode_num_splits": ([D, i32, ctypes.POINTER(i32)], i32),
             "lrkv_decode": ([D, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -156,6 +157,11 @@ def lrkv_absorb_query(dims: Dims, q, B_k, p, stream=None) -> None:
 def lrkv_cache_append(dims: Dims, cache: Cache, k_new, v_new, zk_new, zv_new, stream=None) -> None:
     _check(lib().lrkv_cache_append(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(zk_new),
                                    _ptr(zv_new), _stream(stream)), "lrkv_cache_append")
+
+
+def lrkv_append_absorb(dims: Dims, cache: Cache, k_new, v_new, zk_new, zv_new, q, B_k, p, stream=None) -> None:
+    _check(lib().lrkv_append_absorb(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(zk_new),
+                                    _ptr(zv_new), _ptr(q), _ptr(B_k), _ptr(p), _stream(stream)), "lrkv_append_absorb")
 
 
 def lrkv_decode_workspace_bytes(dims: Dims, max_len: int) -> int:

@@ -10,6 +10,7 @@
 //          reading notes sec. 2.3).  Latents are token-major, so one token's
 //          H x r latents land in one contiguous row.  With a block table the
 //          row goes to its pool page instead (paged cache).
+// append + absorb: both in one launch (a decode step's per-token work).
 // multi-token lengths: query i of Q at the end of sequence b sees
 //          max(0, L_b - Q + 1 + i) rows (the causal mask inside the chunk);
 //          the multi-token decode runs one virtual sequence per query token.
@@ -59,13 +60,12 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_kernel(int H, int d_h, 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
-__global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int H, int d_h, int r, const T* __restrict__ q,
-                                                                    const T* __restrict__ B_k,
-                                                                    float* __restrict__ p) {
+__device__ __forceinline__ void absorb_vec_body(int bh, int H, int d_h, int r, const T* __restrict__ q,
+                                                const T* __restrict__ B_k, float* __restrict__ p) {
     constexpr int VE = 16 / (int)sizeof(T);
     __shared__ float qs[256];
     __shared__ float part[kAbsorbThreads * VE];  // [row group][r]: rpp * r <= kAbsorbThreads * VE
-    const int bh = blockIdx.x, h = bh % H, tid = threadIdx.x;
+    const int h = bh % H, tid = threadIdx.x;
     for (int c = tid; c < d_h; c += kAbsorbThreads) qs[c] = elem<T>::load(q, (size_t)bh * d_h + c);
     __syncthreads();
     const int nv = r / VE, rpp = kAbsorbThreads / nv;
@@ -104,17 +104,22 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int H, int d
 }
 
 template <typename T>
+__global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int H, int d_h, int r, const T* __restrict__ q,
+                                                                    const T* __restrict__ B_k,
+                                                                    float* __restrict__ p) {
+    absorb_vec_body<T>(blockIdx.x, H, d_h, r, q, B_k, p);
+}
+
 // block_table NULL: contiguous cache [batch][L_cap][...]; else page pools [n_pages][1 << page_shift][...]
 // with logical page m of sequence b at pool page block_table[b * max_pages + m] (L_cap = max_pages pages)
-__global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int L_cap, T* __restrict__ k_shared,
-                                                     T* __restrict__ v_shared, T* __restrict__ z_k,
-                                                     T* __restrict__ z_v, int32_t* __restrict__ seq_lens,
-                                                     const T* __restrict__ k_new, const T* __restrict__ v_new,
-                                                     const T* __restrict__ zk_new, const T* __restrict__ zv_new,
-                                                     const int32_t* __restrict__ block_table, int page_shift,
-                                                     int max_pages) {
+template <typename T>
+__device__ __forceinline__ void append_body(int b, int H, int d_h, int r, int L_cap, T* __restrict__ k_shared,
+                                            T* __restrict__ v_shared, T* __restrict__ z_k, T* __restrict__ z_v,
+                                            int32_t* __restrict__ seq_lens, const T* __restrict__ k_new,
+                                            const T* __restrict__ v_new, const T* __restrict__ zk_new,
+                                            const T* __restrict__ zv_new, const int32_t* __restrict__ block_table,
+                                            int page_shift, int max_pages) {
     __shared__ int row;
-    const int b = blockIdx.x;
     if (threadIdx.x == 0) {
         const int L = seq_lens[b];
         row = (L >= 0 && L < L_cap) ? L : -1;
@@ -155,6 +160,39 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
     if (threadIdx.x == 0) seq_lens[b] = j + 1;
 }
 
+template <typename T>
+__global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int L_cap, T* __restrict__ k_shared,
+                                                     T* __restrict__ v_shared, T* __restrict__ z_k,
+                                                     T* __restrict__ z_v, int32_t* __restrict__ seq_lens,
+                                                     const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                                     const T* __restrict__ zk_new, const T* __restrict__ zv_new,
+                                                     const int32_t* __restrict__ block_table, int page_shift,
+                                                     int max_pages) {
+    append_body<T>(blockIdx.x, H, d_h, r, L_cap, k_shared, v_shared, z_k, z_v, seq_lens, k_new, v_new, zk_new,
+                   zv_new, block_table, page_shift, max_pages);
+}
+
+// One launch for the two per-token operations of a decode step: workgroups 0 .. batch-1 append (as
+// append_kernel), workgroups batch .. batch + batch*H - 1 absorb (as absorb_vec_kernel).  The two touch
+// disjoint memory, so they run side by side; each workgroup's arithmetic is the separate kernels', so the
+// results are bitwise the same.
+template <typename T>
+__global__ void __launch_bounds__(256) append_absorb_kernel(int batch, int H, int d_h, int r, int L_cap,
+                                                            T* __restrict__ k_shared, T* __restrict__ v_shared,
+                                                            T* __restrict__ z_k, T* __restrict__ z_v,
+                                                            int32_t* __restrict__ seq_lens,
+                                                            const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                                            const T* __restrict__ zk_new,
+                                                            const T* __restrict__ zv_new, const T* __restrict__ q,
+                                                            const T* __restrict__ B_k, float* __restrict__ p) {
+    const int w = blockIdx.x;
+    if (w < batch)
+        append_body<T>(w, H, d_h, r, L_cap, k_shared, v_shared, z_k, z_v, seq_lens, k_new, v_new, zk_new, zv_new,
+                       nullptr, 0, 0);
+    else
+        absorb_vec_body<T>(w - batch, H, d_h, r, q, B_k, p);
+}
+
 }  // namespace
 
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
@@ -177,6 +215,30 @@ hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void
             hipLaunchKernelGGL(absorb_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
                                (const uint16_t*)B_k, p);
     }
+    return hipGetLastError();
+}
+
+bool append_absorb_supported(int H, int d_h, int r, int dtype) {
+    const int ve = dtype == 0 ? 4 : 8;
+    return kAbsorbThreads == 256 && r > 0 && (r % ve) == 0 && d_h <= 256;  // the absorb's vector path
+}
+
+hipError_t launch_append_absorb(int batch, int H, int d_h, int r, int L_cap, int dtype, void* k_shared,
+                                void* v_shared, void* z_k, void* z_v, int32_t* seq_lens, const void* k_new,
+                                const void* v_new, const void* zk_new, const void* zv_new, const void* q,
+                                const void* B_k, float* p, hipStream_t stream) {
+    if (!append_absorb_supported(H, d_h, r, dtype)) return hipErrorInvalidValue;
+    dim3 grid(batch + batch * H), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(append_absorb_kernel<float>, grid, block, 0, stream, batch, H, d_h, r, L_cap,
+                           (float*)k_shared, (float*)v_shared, (float*)z_k, (float*)z_v, seq_lens,
+                           (const float*)k_new, (const float*)v_new, (const float*)zk_new, (const float*)zv_new,
+                           (const float*)q, (const float*)B_k, p);
+    else
+        hipLaunchKernelGGL(append_absorb_kernel<uint16_t>, grid, block, 0, stream, batch, H, d_h, r, L_cap,
+                           (uint16_t*)k_shared, (uint16_t*)v_shared, (uint16_t*)z_k, (uint16_t*)z_v, seq_lens,
+                           (const uint16_t*)k_new, (const uint16_t*)v_new, (const uint16_t*)zk_new,
+                           (const uint16_t*)zv_new, (const uint16_t*)q, (const uint16_t*)B_k, p);
     return hipGetLastError();
 }
 

@@ -331,6 +331,31 @@ lrkv_status lrkv_cache_append(const lrkv_dims* dims, const lrkv_cache* cache, co
     return ok();
 }
 
+lrkv_status lrkv_append_absorb(const lrkv_dims* dims, const lrkv_cache* cache, const void* k_new, const void* v_new,
+                               const void* zk_new, const void* zv_new, const void* q, const void* B_k, float* p,
+                               void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (dims->r == 0) return lrkv_cache_append(dims, cache, k_new, v_new, zk_new, zv_new, stream);
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(k_new, "k_new"));
+    LRKV_TRY(need_ptr(v_new, "v_new"));
+    LRKV_TRY(need_ptr(zk_new, "zk_new"));
+    LRKV_TRY(need_ptr(zv_new, "zv_new"));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(B_k, "B_k"));
+    LRKV_TRY(need_ptr(p, "p"));
+    if (!lrkv::append_absorb_supported(dims->H, dims->d_h, dims->r, dims->dtype)) {  // two launches
+        LRKV_TRY(lrkv_cache_append(dims, cache, k_new, v_new, zk_new, zv_new, stream));
+        return lrkv_absorb_query(dims, q, B_k, p, stream);
+    }
+    hipError_t e = lrkv::launch_append_absorb(dims->batch, dims->H, dims->d_h, dims->r, dims->L_cap, dims->dtype,
+                                              cache->k_shared, cache->v_shared, cache->z_k, cache->z_v,
+                                              cache->seq_lens, k_new, v_new, zk_new, zv_new, q, B_k, p,
+                                              (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "append/absorb kernel launch");
+    return ok();
+}
+
 lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
                                 const float* p, void* workspace, size_t workspace_bytes_, void* stream) {
     lrkv::SplitPlan plan;

@@ -76,6 +76,13 @@ hipError_t launch_append(int batch, int H, int d_h, int r, int L_cap, int dtype,
                          void* z_k, void* z_v, int32_t* seq_lens, const void* k_new, const void* v_new,
                          const void* zk_new, const void* zv_new, hipStream_t stream);
 hipError_t launch_split_general(const DecodeArgs& a, hipStream_t stream);
+// append and absorb in one launch (the absorb's 16-byte vector path: r > 0, r a multiple of 16 / element bytes,
+// d_h <= 256); contiguous cache
+bool append_absorb_supported(int H, int d_h, int r, int dtype);
+hipError_t launch_append_absorb(int batch, int H, int d_h, int r, int L_cap, int dtype, void* k_shared,
+                                void* v_shared, void* z_k, void* z_v, int32_t* seq_lens, const void* k_new,
+                                const void* v_new, const void* zk_new, const void* zv_new, const void* q,
+                                const void* B_k, float* p, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
 // Merge of a decode of `batch` cached sequences with Q query tokens each, split as virtual sequences of qw

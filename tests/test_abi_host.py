@@ -160,6 +160,10 @@ def test_null_and_misaligned_pointers_rejected():
     assert _status(lk.lrkv_absorb_query, d, A, A, A + 4, 0) == lk.LRKV_ERR_INVALID_ARG
     assert _status(lk.lrkv_cache_append, d, good, A, None, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
     assert _status(lk.lrkv_decode_merge, d, None, 256, A, A, 1 << 12, ws, 0) == lk.LRKV_ERR_INVALID_ARG
+    for i in range(7):  # k_new, v_new, zk_new, zv_new, q, B_k, p of the fused append + absorb
+        args = [A] * 7
+        args[i] = None
+        assert _status(lk.lrkv_append_absorb, d, good, *args, 0) == lk.LRKV_ERR_INVALID_ARG, i
 
 
 def test_max_len_and_workspace_rejected():
