@@ -3,30 +3,36 @@
 // stronger identity"; "Low-Rank Key Value Attention: Chinese reading notes",
 // sec. 2.7).  Every head's whole key is turned at its own position,
 //   ktilde_{h,j} = (k_s[j] + z^K_{h,j} (B^K_h)^T) D_j,   qtilde = q D_{L_b - 1},
-// which no rank-space rotation reproduces for a generic B_h, so the key of
-// every (row, head) is rebuilt: d_h * r multiply-adds per row and head, the
-// cost the review names for the exact contraction.  They run on the matrix
-// cores, the rest on the VALU.
+// which no rank-space rotation reproduces for a generic B_h, so the private
+// part of every (row, head) key is rebuilt: d_h * r multiply-adds per row and
+// head, the cost the review names for the exact contraction.  The rotation is
+// linear, so the score splits into a shared part, qtilde_h . (k_s[j] D_j), and
+// a private part, qtilde_h . ((z^K_{h,j} (B^K_h)^T) D_j).
 //
-// A workgroup of 4 waves owns one (sequence, split) and walks its 64-row
-// tiles (tile s, s + S_b, ... of the sequence).  Per tile:
-//   1. stage: shared key rows (bf16) and their (cos, sin) rows (fp32) in LDS;
-//   2. scores: wave w takes heads w*HPW .. w*HPW + HPW - 1.  Per head it loads
-//      the B^K_h fragments once (the next head's are loaded while this one
-//      computes) and, per 16-row group, rebuilds the key 16 columns at a time,
-//      Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16], on
-//      v_mfma_f32_16x16x32_bf16 (exact bf16 products, fp32 sums).  Lane
-//      (row n16, g4) then holds columns 16 cb + 4 g4 + i of its row: it adds
-//      the shared row, turns the two coordinate pairs, dots them with the
-//      rotated query (fp32) and the four lanes of a row sum in a fixed order;
+// A workgroup of 8 waves owns one (sequence, split) and walks its 64-row tiles
+// (tile s, s + S_b, ... of the sequence); one workgroup per CU.  Per tile:
+//   1. stage: each shared key row is turned once (fp32) and kept as a bf16
+//      high part and a bf16 remainder; the (cos, sin) rows go to LDS as fp32,
+//      the value rows as V^T (bf16);
+//   2a. shared scores of all heads on the matrix cores (v_mfma_f32_16x16x32_bf16):
+//      S[16 rows x 16 heads] = Ktilde Qtilde^T with both operands split into
+//      high + low bf16 parts (hi*hi + hi*lo + lo*hi; about 16 significant bits
+//      of each operand), one (row group, head group) block per wave;
+//   2b. private scores: wave w takes heads w, w + 8, ...; per head it loads
+//      the B^K_h fragments once and, per 16-row group, rebuilds the private key
+//      16 columns at a time, Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16]
+//      (exact bf16 products, fp32 sums).  Lane (row n16, g4) then holds
+//      columns 16 cb + 4 g4 + i of its row: it turns the two coordinate pairs
+//      (fp32) and dots them with the rotated query; the four lanes of a row sum
+//      in a fixed order;
 //   3. softmax: one wave per head, lanes = the tile's rows, online max and
 //      denominator in LDS;
-//   4. values: thread (head, g) of 8 groups accumulates the shared sum over
-//      columns g*d_h/8 .. and the private sum over latent coordinates g*r/8 ..,
-//      reading value and latent rows 8 at a time (the lanes of a wave that
-//      read the same value columns share one access).
-// Two workgroups are resident per CU (LDS 75 KB, at most 256 registers per
-// lane), so one workgroup's barriers and load latency overlap the other's work.
+//   4. values: the shared sum O^T[d_h x 16 heads] += V^T[d_h x 64] P^T on the
+//      matrix cores (P split into bf16 high + low parts), one or two
+//      (column block, head group) blocks per wave; the private sum on the VALU:
+//      a thread owns one 16-byte chunk (8 coordinates of one head) of the
+//      latent rows in one part of the tile, reads 16 rows at a time, and the
+//      parts' sums are added in a fixed order at the end.
 // The workgroup writes the usual partial record per head (running max in
 // log2 units, denominator, shared sum, private sum); the merge kernel combines
 // splits and applies B^V.
@@ -41,75 +47,55 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr int kTileRows = 64;  // 4 groups of 16 rows
+constexpr int kMaxHeads = 32;
 
 template <int D, int R>
 struct RopeCfg {
-    static constexpr int CB = D / 16;              // 16-column blocks of a key
-    static constexpr int NKS = (R + 31) / 32;      // k-steps of 32 latent coordinates
-    static constexpr int KS_STRIDE = D + 8;        // bf16 per staged shared-key row
-    static constexpr int CS_STRIDE = D + 4;        // floats per staged (cos, sin) row
-    static constexpr int E_STRIDE = kTileRows + 4; // floats per head of the score / weight rows
-    static constexpr int SHC = D / 8;              // shared-value columns per thread
-    static constexpr int PRC = R / 8;              // latent coordinates per thread
+    static constexpr int CB = D / 16;                 // 16-column blocks of a key or value row
+    static constexpr int KSD = D / 32;                // k-steps of the shared-score product
+    static constexpr int NKS = (R + 31) / 32;         // k-steps of 32 latent coordinates
+    static constexpr int KR_STRIDE = D + 8;           // bf16 per turned shared-key row (hi and lo arrays)
+    static constexpr int CS_STRIDE = D + 4;           // floats per staged (cos, sin) row
+    static constexpr int VT_STRIDE = kTileRows + 8;   // bf16 per V^T row (one value column, 64 rows)
+    static constexpr int E_STRIDE = kTileRows + 4;    // floats per head of the score / weight rows
+    static constexpr int NCH = R / 8;                 // 16-byte chunks (8 coordinates) of a head's latent row
+    static constexpr int SVB = (CB * 2 + kWaves - 1) / kWaves;  // shared-value blocks per wave (H <= 32)
+    static constexpr size_t KR_BYTES = (size_t)2 * kTileRows * KR_STRIDE * 2;
+    static constexpr size_t CS_BYTES = (size_t)kTileRows * CS_STRIDE * 4;
+    static constexpr size_t VT_BYTES = (size_t)D * VT_STRIDE * 2;
     static constexpr size_t lds_bytes(int H) {
-        return (size_t)kTileRows * KS_STRIDE * 2 + (size_t)kTileRows * CS_STRIDE * 4 + (size_t)H * D * 4 +
-               (size_t)H * E_STRIDE * 4 + 3 * (size_t)H * 4;
+        return KR_BYTES + CS_BYTES + VT_BYTES + (size_t)H * D * 4 + 2 * (size_t)kMaxHeads * E_STRIDE * 4 +
+               3 * (size_t)kMaxHeads * 4;
     }
 };
 
-constexpr int kBatchRows = 8;  // value-phase rows whose value and latent loads are issued together
+constexpr int kBatchRows = 16;  // private-value rows whose latent loads are issued together
 
-// N consecutive bf16 values (latent coordinates: N = r / 8 in {0, 1, 2, 4, 6, 8}; value columns: N = d_h / 8
-// in {8, 16}), loaded with as few instructions as their alignment allows
-template <int N>
-struct LatVec {
-    uint32_t w[N > 1 ? (N + 1) / 2 : 1];
-    __device__ __forceinline__ void load(const uint16_t* p) {
-        if constexpr (N == 16) {
-            const u32x4_t v0 = *(const u32x4_t*)p, v1 = *(const u32x4_t*)(p + 8);
-            w[0] = v0[0]; w[1] = v0[1]; w[2] = v0[2]; w[3] = v0[3];
-            w[4] = v1[0]; w[5] = v1[1]; w[6] = v1[2]; w[7] = v1[3];
-        } else if constexpr (N == 8) {
-            const u32x4_t v = *(const u32x4_t*)p;
-            w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-        } else if constexpr (N == 6) {
-            const uint32_t* d = (const uint32_t*)p;  // 12 bytes at 4-byte alignment
-            w[0] = d[0]; w[1] = d[1]; w[2] = d[2];
-        } else if constexpr (N == 4) {
-            const u32x2_t v = *(const u32x2_t*)p;
-            w[0] = v[0]; w[1] = v[1];
-        } else if constexpr (N == 2) {
-            w[0] = *(const uint32_t*)p;
-        } else if constexpr (N == 1) {
-            w[0] = *p;
-        }
-    }
-    __device__ __forceinline__ float at(int j) const {  // j < N, a compile-time index after unrolling
-        return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
-    }
-};
+// (hi, lo) bf16 parts of x: hi = bf16(x), lo = bf16(x - hi); hi + lo carries about 16 significant bits
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+    hi = f32_to_bf16_bits(x);
+    lo = f32_to_bf16_bits(x - __uint_as_float(hi << 16));
+}
 
 template <int D, int R>
-struct Frags {  // one head's B^K fragments and the latent fragments of the tile's 4 row groups
-    u32x4_t b[RopeCfg<D, R>::CB][RopeCfg<D, R>::NKS > 0 ? RopeCfg<D, R>::NKS : 1];
-    u32x4_t z[4][RopeCfg<D, R>::NKS > 0 ? RopeCfg<D, R>::NKS : 1];
-};
-
-template <int D, int R>
-__global__ void __launch_bounds__(kWaves * 64, 2) split_rope_mfma_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs a) {
     using C = RopeCfg<D, R>;
-    constexpr int CB = C::CB, NKS = C::NKS;
+    constexpr int CB = C::CB, NKS = C::NKS, KSD = C::KSD;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int H = a.H;
-    uint16_t* ks_l = (uint16_t*)lds;                                           // [64][D + 8]
-    float* cs_l = (float*)(lds + (size_t)kTileRows * C::KS_STRIDE * 2);        // [64][D + 4]
-    float* qr_l = (float*)((unsigned char*)cs_l + (size_t)kTileRows * C::CS_STRIDE * 4);  // [H][D]
-    float* e_l = qr_l + (size_t)H * D;                                         // [H][64 + 4]
-    float* m_l = e_l + (size_t)H * C::E_STRIDE;                                // [H] running max (log2 units)
-    float* l_l = m_l + H;                                                      // [H] denominator
-    float* al_l = l_l + H;                                                     // [H] this tile's rescale
+    uint16_t* kr_hi = (uint16_t*)lds;                                       // [64][D + 8]
+    uint16_t* kr_lo = kr_hi + (size_t)kTileRows * C::KR_STRIDE;             // [64][D + 8]
+    float* cs_l = (float*)(lds + C::KR_BYTES);                              // [64][D + 4]
+    uint16_t* vt = (uint16_t*)(lds + C::KR_BYTES + C::CS_BYTES);            // [D][64 + 8]
+    float* qr_l = (float*)(lds + C::KR_BYTES + C::CS_BYTES + C::VT_BYTES);  // [H][D]
+    float* es_l = qr_l + (size_t)H * D;                                     // [32][64 + 4] shared scores
+    float* ep_l = es_l + (size_t)kMaxHeads * C::E_STRIDE;                   // [32][64 + 4] private, then weights
+    float* m_l = ep_l + (size_t)kMaxHeads * C::E_STRIDE;                    // [32] running max (log2 units)
+    float* l_l = m_l + kMaxHeads;                                           // [32] denominator
+    float* al_l = l_l + kMaxHeads;                                          // [32] this tile's rescale
 
     const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
     const int b = wslot.b, split = wslot.s;
@@ -119,7 +105,7 @@ __global__ void __launch_bounds__(kWaves * 64, 2) split_rope_mfma_kernel(DecodeA
     const int bc = b / a.qgroup;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int HPW = (H + kWaves - 1) / kWaves;  // heads per wave (scores) and per wave in the value phase
+    const int NHG = (H + 15) / 16;  // head groups of the matrix-core products
     const float scale = kLog2e / sqrtf((float)D);
 
     const uint16_t* ksg = (const uint16_t*)a.k_shared + (size_t)bc * a.L_cap * D;
@@ -128,119 +114,208 @@ __global__ void __launch_bounds__(kWaves * 64, 2) split_rope_mfma_kernel(DecodeA
     const uint16_t* zvg = (const uint16_t*)a.z_v + (size_t)bc * a.L_cap * H * R;
     const uint16_t* bkg = (const uint16_t*)a.rope_bk;
 
-    // the rotated query (position L_b - 1) of every head, fp32
+    // the rotated query (position L_b - 1) of every head, fp32; score and weight rows of absent heads stay
+    // zero, so the shared-value product reads finite weights for them
     {
         const float* cs = a.rope_cs + (size_t)(Lb - 1) * D;
         const uint16_t* qg = (const uint16_t*)a.q + (size_t)b * H * D;
-        for (int idx = tid; idx < H * (D / 2); idx += kWaves * 64) {
+        for (int idx = tid; idx < H * (D / 2); idx += kThreads) {
             const int h = idx / (D / 2), k = idx - h * (D / 2);
             const float x0 = bf16_to_f32(qg[h * D + 2 * k]), x1 = bf16_to_f32(qg[h * D + 2 * k + 1]);
             const float co = cs[2 * k], si = cs[2 * k + 1];
             qr_l[h * D + 2 * k] = x0 * co - x1 * si;
             qr_l[h * D + 2 * k + 1] = x0 * si + x1 * co;
         }
-        for (int h = tid; h < H; h += kWaves * 64) {
+        for (int i = tid; i < 2 * kMaxHeads * C::E_STRIDE; i += kThreads) es_l[i] = 0.f;
+        for (int h = tid; h < kMaxHeads; h += kThreads) {
             m_l[h] = -INFINITY;
             l_l[h] = 0.f;
+            al_l[h] = 0.f;
         }
     }
+    __syncthreads();
 
-    // value-phase ownership: thread (head hv, group g)
-    const int hv = wave * HPW + (lane >> 3), gv = lane & 7;
-    const bool own = (lane >> 3) < HPW && hv < H;
-    float acc_sh[C::SHC], acc_pr[C::PRC > 0 ? C::PRC : 1];
-#pragma unroll
-    for (int j = 0; j < C::SHC; ++j) acc_sh[j] = 0.f;
-#pragma unroll
-    for (int j = 0; j < C::PRC; ++j) acc_pr[j] = 0.f;
+    // shared-score block of this wave: row group rg2, head group hg2 (waves past the head groups idle there)
+    const int rg2 = wave & 3, hg2 = wave >> 2;
+    const bool do_sh = hg2 < NHG;
 
-    const int h_first = wave * HPW, h_end = min(H, h_first + HPW);
+    // shared-value blocks of this wave: block blk = wave + 8 k is (column block blk % CB, head group blk / CB)
+    f32x4_t acc_sv[C::SVB];
+#pragma unroll
+    for (int k = 0; k < C::SVB; ++k) acc_sv[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // private-value ownership: a latent row holds H * NCH chunks of 16 bytes (cells); thread t takes cell
+    // t % cells over the rows of tile part t / cells (parts * cells <= 512, parts a power of two, at most 16),
+    // so consecutive threads read consecutive chunks of a row; the parts' sums are added at the end
+    const int cells = H * C::NCH;
+    int parts = 1;
+    while (cells > 0 && parts < 16 && 2 * parts * cells <= kThreads) parts *= 2;
+    const int rpp = kTileRows / parts;  // rows per part
+    const int cell = cells > 0 ? tid % cells : 0, part = cells > 0 ? tid / cells : 0;
+    const bool own_pr = R > 0 && part < parts;
+    const int hv = cell / (C::NCH > 0 ? C::NCH : 1);  // the cell's head
+    float acc_pr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc_pr[j] = 0.f;
 
     for (int t0 = split * kTileRows; t0 < Lb; t0 += wslot.S_b * kTileRows) {
         const int nvalid = min(kTileRows, Lb - t0);
-        __syncthreads();  // the previous tile's weights and value rows are consumed
-        // ---- 1. stage the tile (rows past the end re-read the last live row) ----
-        for (int idx = tid; idx < kTileRows * (D / 8); idx += kWaves * 64) {
+        __syncthreads();  // the previous tile's staged rows and weights are consumed
+        // ---- 1. stage the tile.  Key and (cos, sin) rows past the end re-read the last live row (their
+        //         scores are masked); value rows past the end are zero (weight 0 must not meet arbitrary
+        //         contents) ----
+        for (int idx = tid; idx < kTileRows * (D / 8); idx += kThreads) {
             const int r = idx / (D / 8), c8 = idx - r * (D / 8);
             const size_t row = (size_t)(t0 + min(r, nvalid - 1));
-            *(u32x4_t*)(ks_l + r * C::KS_STRIDE + 8 * c8) = *(const u32x4_t*)(ksg + row * D + 8 * c8);
+            const u32x4_t kv = *(const u32x4_t*)(ksg + row * D + 8 * c8);
+            const f32x4_t c0 = *(const f32x4_t*)(a.rope_cs + row * D + 8 * c8);      // pairs 4 c8, 4 c8 + 1
+            const f32x4_t c1 = *(const f32x4_t*)(a.rope_cs + row * D + 8 * c8 + 4);  // pairs 4 c8 + 2, + 3
+            *(f32x4_t*)(cs_l + r * C::CS_STRIDE + 8 * c8) = c0;
+            *(f32x4_t*)(cs_l + r * C::CS_STRIDE + 8 * c8 + 4) = c1;
+            u32x4_t hi4, lo4;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {  // pair p of the 8 columns: (x0, x1) turned by (cos, sin)
+                const float x0 = bf16_lo(kv[p]), x1 = bf16_hi(kv[p]);
+                const float co = p < 2 ? c0[2 * p] : c1[2 * p - 4], si = p < 2 ? c0[2 * p + 1] : c1[2 * p - 3];
+                uint32_t h0, l0, h1, l1;
+                split_bf16(x0 * co - x1 * si, h0, l0);
+                split_bf16(x0 * si + x1 * co, h1, l1);
+                hi4[p] = h0 | (h1 << 16);
+                lo4[p] = l0 | (l1 << 16);
+            }
+            *(u32x4_t*)(kr_hi + r * C::KR_STRIDE + 8 * c8) = hi4;
+            *(u32x4_t*)(kr_lo + r * C::KR_STRIDE + 8 * c8) = lo4;
         }
-        for (int idx = tid; idx < kTileRows * (D / 4); idx += kWaves * 64) {
-            const int r = idx / (D / 4), c4 = idx - r * (D / 4);
-            const size_t pos = (size_t)(t0 + min(r, nvalid - 1));
-            *(f32x4_t*)(cs_l + r * C::CS_STRIDE + 4 * c4) = *(const f32x4_t*)(a.rope_cs + pos * D + 4 * c4);
+        for (int idx = tid; idx < (kTileRows / 4) * (D / 8); idx += kThreads) {
+            // V^T: 4 consecutive rows x 8 columns per thread, one 8-byte store per column
+            const int r4 = idx / (D / 8), c8 = idx - r4 * (D / 8);
+            uint32_t w[4][4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = 4 * r4 + k;
+                const u32x4_t v = (r < nvalid) ? *(const u32x4_t*)(vsg + (size_t)(t0 + r) * D + 8 * c8)
+                                               : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[k][e] = v[e];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+                u32x2_t pk;
+                pk[0] = __builtin_amdgcn_perm(w[1][j >> 1], w[0][j >> 1], sel);  // (row 4 r4, row 4 r4 + 1)
+                pk[1] = __builtin_amdgcn_perm(w[3][j >> 1], w[2][j >> 1], sel);
+                *(u32x2_t*)(vt + (8 * c8 + j) * C::VT_STRIDE + 4 * r4) = pk;
+            }
         }
         __syncthreads();
 
-        // ---- 2. scores of this wave's heads ----
-        auto load_frags = [&](Frags<D, R>& f, int h) {
-            if constexpr (NKS > 0) {
+        // ---- 2a. shared scores: rows 16 rg2 .., heads 16 hg2 .. ----
+        if (do_sh) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            const int rl = 16 * rg2 + n16;
+            const int hq = 16 * hg2 + n16;  // the query row of the B operand (zero past H)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
+            for (int ks = 0; ks < KSD; ++ks) {
+                const int c = 32 * ks + 8 * g4;
+                const bf16x8_t khi = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr_hi + rl * C::KR_STRIDE + c));
+                const bf16x8_t klo = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr_lo + rl * C::KR_STRIDE + c));
+                // the rotated query's 8 values split into (hi, lo) bf16 parts
+                f32x4_t q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
+                if (hq < H) {
+                    q0 = *(const f32x4_t*)(qr_l + hq * D + c);
+                    q1 = *(const f32x4_t*)(qr_l + hq * D + c + 4);
+                }
+                u32x4_t qh4, ql4;
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        const int k = 32 * ks + 8 * g4;
-                        const int kc = k < R ? k : 0;
-                        f.b[cb][ks] = *(const u32x4_t*)(bkg + ((size_t)h * D + 16 * cb + n16) * R + kc);
-                        if (k >= R) f.b[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t h0, l0, h1, l1;
+                    split_bf16(i < 2 ? q0[2 * i] : q1[2 * i - 4], h0, l0);
+                    split_bf16(i < 2 ? q0[2 * i + 1] : q1[2 * i - 3], h1, l1);
+                    qh4[i] = h0 | (h1 << 16);
+                    ql4[i] = l0 | (l1 << 16);
+                }
+                const bf16x8_t qhi = __builtin_bit_cast(bf16x8_t, qh4);
+                const bf16x8_t qlo = __builtin_bit_cast(bf16x8_t, ql4);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, qhi, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, qlo, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, qhi, acc, 0, 0, 0);
+            }
+            // lane (head n16, g4) holds rows 16 rg2 + 4 g4 + i
+            const int h = 16 * hg2 + n16;
+            if (h < H) *(f32x4_t*)(es_l + h * C::E_STRIDE + 16 * rg2 + 4 * g4) = acc;
+        }
+
+        // ---- 2b. private scores of this wave's heads.  The next head's latent fragments (from HBM) are loaded
+        //          while this head computes: two register sets, used in turn; the B^K_h fragments (from L2)
+        //          are loaded per head. ----
+        if constexpr (NKS > 0) {
+            typedef u32x4_t ZFrag[4][NKS];
+            auto load_z = [&](ZFrag& zf, int h) {
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const size_t row = (size_t)(t0 + min(16 * rg + n16, nvalid - 1));
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
                         const int k = 32 * ks + 8 * g4;
-                        const int kc = k < R ? k : 0;
-                        f.z[rg][ks] = *(const u32x4_t*)(zkg + (row * H + h) * R + kc);
-                        if (k >= R) f.z[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
+                        zf[rg][ks] = (k < R) ? *(const u32x4_t*)(zkg + (row * H + h) * R + k) : u32x4_t{0u, 0u, 0u, 0u};
                     }
                 }
-            }
-        };
-        auto score_head = [&](const Frags<D, R>& f, int h) {
-            const float* qh = qr_l + (size_t)h * D;
+            };
+            auto score_head = [&](const ZFrag& zf, int h) {
+                u32x4_t bf[CB][NKS];
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int rl = 16 * rg + n16;  // this lane's row in the tile
-                float part = 0.f;
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                    if constexpr (NKS > 0) {
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int k = 32 * ks + 8 * g4;
+                        bf[cb][ks] = (k < R) ? *(const u32x4_t*)(bkg + ((size_t)h * D + 16 * cb + n16) * R + k)
+                                             : u32x4_t{0u, 0u, 0u, 0u};
+                    }
+                const float* qh = qr_l + (size_t)h * D;
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int rl = 16 * rg + n16;  // this lane's row in the tile
+                    float part = 0.f;
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int ks = 0; ks < NKS; ++ks)
-                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, f.b[cb][ks]),
-                                                                          __builtin_bit_cast(bf16x8_t, f.z[rg][ks]),
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
+                                                                          __builtin_bit_cast(bf16x8_t, zf[rg][ks]),
                                                                           acc, 0, 0, 0);
+                        const int c0 = 16 * cb + 4 * g4;
+                        const f32x4_t cs = *(const f32x4_t*)(cs_l + rl * C::CS_STRIDE + c0);
+                        const f32x4_t qv = *(const f32x4_t*)(qh + c0);
+                        part = fmaf(qv[0], acc[0] * cs[0] - acc[1] * cs[1], part);
+                        part = fmaf(qv[1], acc[0] * cs[1] + acc[1] * cs[0], part);
+                        part = fmaf(qv[2], acc[2] * cs[2] - acc[3] * cs[3], part);
+                        part = fmaf(qv[3], acc[2] * cs[3] + acc[3] * cs[2], part);
                     }
-                    const int c0 = 16 * cb + 4 * g4;
-                    const u32x2_t kv = *(const u32x2_t*)(ks_l + rl * C::KS_STRIDE + c0);
-                    const f32x4_t cs = *(const f32x4_t*)(cs_l + rl * C::CS_STRIDE + c0);
-                    const f32x4_t qv = *(const f32x4_t*)(qh + c0);
-                    const float u0 = acc[0] + bf16_lo(kv[0]), u1 = acc[1] + bf16_hi(kv[0]);
-                    const float u2 = acc[2] + bf16_lo(kv[1]), u3 = acc[3] + bf16_hi(kv[1]);
-                    part = fmaf(qv[0], u0 * cs[0] - u1 * cs[1], part);
-                    part = fmaf(qv[1], u0 * cs[1] + u1 * cs[0], part);
-                    part = fmaf(qv[2], u2 * cs[2] - u3 * cs[3], part);
-                    part = fmaf(qv[3], u2 * cs[3] + u3 * cs[2], part);
+                    part += __shfl_xor(part, 16);  // the row's four column groups: (0 + 1) + (2 + 3)
+                    part += __shfl_xor(part, 32);
+                    if (g4 == 0) ep_l[(size_t)h * C::E_STRIDE + rl] = part;
                 }
-                part += __shfl_xor(part, 16);  // the row's four column groups: (0 + 1) + (2 + 3)
-                part += __shfl_xor(part, 32);
-                if (g4 == 0) e_l[(size_t)h * C::E_STRIDE + rl] = part;
+            };
+            ZFrag za, zb;
+            if (wave < H) load_z(za, wave);
+            for (int h = wave; h < H; h += 2 * kWaves) {  // heads h (in za) and h + 8 (in zb)
+                const int h1 = h + kWaves, h2 = h + 2 * kWaves;
+                if (h1 < H) load_z(zb, h1);
+                score_head(za, h);
+                if (h1 >= H) break;
+                if (h2 < H) load_z(za, h2);
+                score_head(zb, h1);
             }
-        };
-        for (int h = h_first; h < h_end; ++h) {  // the other resident workgroup covers these loads' latency
-            Frags<D, R> f;
-            load_frags(f, h);
-            score_head(f, h);
         }
         __syncthreads();
 
         // ---- 3. online softmax, one wave per head, lanes = rows ----
         for (int h = wave; h < H; h += kWaves) {
-            float* eh = e_l + (size_t)h * C::E_STRIDE;
+            float* eh = ep_l + (size_t)h * C::E_STRIDE;
             const bool live = lane < nvalid;
-            const float s = live ? eh[lane] * scale : -INFINITY;
+            const float raw = es_l[(size_t)h * C::E_STRIDE + lane] + (NKS > 0 ? eh[lane] : 0.f);
+            const float s = live ? raw * scale : -INFINITY;
             float tmax = s;
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
@@ -261,35 +336,60 @@ __global__ void __launch_bounds__(kWaves * 64, 2) split_rope_mfma_kernel(DecodeA
         }
         __syncthreads();
 
-        // ---- 4. values: shared columns gv*SHC.., latent coordinates gv*PRC.. of head hv ----
-        // Rows go in batches of 16: the batch's latent loads are all issued before any of its arithmetic, so
-        // their latency is paid once per batch (rows past the tile's end re-read the last live row, unused).
-        if (own) {
+        // ---- 4a. shared values on the matrix cores: O^T[16 cols x 16 heads] += V^T[16 x 64] P^T[64 x 16] ----
+#pragma unroll
+        for (int k = 0; k < C::SVB; ++k) {
+            const int blk = wave + kWaves * k;
+            const int cb = blk % CB, hg = blk / CB;
+            if (hg < NHG) {
+                const int h = 16 * hg + n16;
+                acc_sv[k] *= al_l[h];  // absent heads: alpha 0 on zero sums
+#pragma unroll
+                for (int ks = 0; ks < kTileRows / 32; ++ks) {
+                    const int r0 = 32 * ks + 8 * g4;
+                    const bf16x8_t av =
+                        __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(vt + (16 * cb + n16) * C::VT_STRIDE + r0));
+                    const f32x4_t e0 = *(const f32x4_t*)(ep_l + h * C::E_STRIDE + r0);
+                    const f32x4_t e1 = *(const f32x4_t*)(ep_l + h * C::E_STRIDE + r0 + 4);
+                    u32x4_t phi, plo;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t h0, l0, h1, l1;
+                        split_bf16(i < 2 ? e0[2 * i] : e1[2 * i - 4], h0, l0);
+                        split_bf16(i < 2 ? e0[2 * i + 1] : e1[2 * i - 3], h1, l1);
+                        phi[i] = h0 | (h1 << 16);
+                        plo[i] = l0 | (l1 << 16);
+                    }
+                    acc_sv[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, phi),
+                                                                        acc_sv[k], 0, 0, 0);
+                    acc_sv[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, plo),
+                                                                        acc_sv[k], 0, 0, 0);
+                }
+            }
+        }
+
+        // ---- 4b. private values: chunk `cell` of the latent rows of this thread's part, 16 rows at a time whose
+        //          loads are issued before any of their arithmetic (rows past the tile's end re-read the last
+        //          live row and are skipped) ----
+        if (own_pr) {
             const float al = al_l[hv];
 #pragma unroll
-            for (int j = 0; j < C::SHC; ++j) acc_sh[j] *= al;
+            for (int j = 0; j < 8; ++j) acc_pr[j] *= al;
+            const float* eh = ep_l + (size_t)hv * C::E_STRIDE;
+            const int rbeg = part * rpp, rend = min(rbeg + rpp, nvalid);
+            const uint16_t* zbase = zvg + (size_t)t0 * H * R + 8 * cell;
+            for (int r0 = rbeg; r0 < rend; r0 += kBatchRows) {
+                u32x4_t zb[kBatchRows];
 #pragma unroll
-            for (int j = 0; j < C::PRC; ++j) acc_pr[j] *= al;
-            const float* eh = e_l + (size_t)hv * C::E_STRIDE;
-            const uint16_t* zbase = zvg + ((size_t)t0 * H + hv) * R + gv * C::PRC;
-            const uint16_t* vbase = vsg + (size_t)t0 * D + gv * C::SHC;
-            for (int r0 = 0; r0 < nvalid; r0 += kBatchRows) {
-                LatVec<C::SHC> vb[kBatchRows];
-                LatVec<C::PRC> zb[kBatchRows];
-#pragma unroll
-                for (int k = 0; k < kBatchRows; ++k) {
-                    const size_t r = (size_t)min(r0 + k, nvalid - 1);
-                    vb[k].load(vbase + r * D);
-                    zb[k].load(zbase + r * H * R);
-                }
+                for (int k = 0; k < kBatchRows; ++k)
+                    zb[k] = *(const u32x4_t*)(zbase + (size_t)min(r0 + k, rend - 1) * H * R);
 #pragma unroll
                 for (int k = 0; k < kBatchRows; ++k) {
-                    if (r0 + k < nvalid) {
+                    if (r0 + k < rend) {
                         const float e = eh[r0 + k];
 #pragma unroll
-                        for (int j = 0; j < C::SHC; ++j) acc_sh[j] = fmaf(e, vb[k].at(j), acc_sh[j]);
-#pragma unroll
-                        for (int j = 0; j < C::PRC; ++j) acc_pr[j] = fmaf(e, zb[k].at(j), acc_pr[j]);
+                        for (int j = 0; j < 8; ++j)
+                            acc_pr[j] = fmaf(e, (j & 1) ? bf16_hi(zb[k][j >> 1]) : bf16_lo(zb[k][j >> 1]), acc_pr[j]);
                     }
                 }
             }
@@ -297,18 +397,35 @@ __global__ void __launch_bounds__(kWaves * 64, 2) split_rope_mfma_kernel(DecodeA
     }
 
     // ---- the split's record of every head ----
+    mfma_result_fence();  // the shared-value products end a loop with a run-time trip count
     __syncthreads();
-    if (own) {
-        const int rec = partial_record_floats(D, R);
-        float* out = a.ws + ((size_t)blockIdx.x * H + hv) * rec;
+    const int rec = partial_record_floats(D, R);
+    float* out = a.ws + (size_t)blockIdx.x * H * rec;
 #pragma unroll
-        for (int j = 0; j < C::SHC; ++j) out[gv * C::SHC + j] = acc_sh[j];
+    for (int k = 0; k < C::SVB; ++k) {
+        const int blk = wave + kWaves * k;
+        const int cb = blk % CB, hg = blk / CB;
+        const int h = 16 * hg + n16;
+        if (hg < NHG && h < H) *(f32x4_t*)(out + (size_t)h * rec + 16 * cb + 4 * g4) = acc_sv[k];
+    }
+    if constexpr (R > 0) {  // the parts' private sums, added in part order (the staged-key area is free now)
+        float* pr_l = (float*)lds;  // [512][8]
+        if (own_pr) {
 #pragma unroll
-        for (int j = 0; j < C::PRC; ++j) out[D + gv * C::PRC + j] = acc_pr[j];
-        if (gv == 0) {
-            out[D + R] = m_l[hv];
-            out[D + R + 1] = l_l[hv];
+            for (int j = 0; j < 8; ++j) pr_l[tid * 8 + j] = acc_pr[j];
         }
+        __syncthreads();
+        for (int i = tid; i < cells * 8; i += kThreads) {
+            const int c = i >> 3, j = i & 7;
+            float sum = 0.f;
+            for (int p = 0; p < parts; ++p) sum += pr_l[(p * cells + c) * 8 + j];
+            const int h = c / C::NCH, ch = c - h * C::NCH;
+            out[(size_t)h * rec + D + 8 * ch + j] = sum;
+        }
+    }
+    for (int h = tid; h < H; h += kThreads) {
+        out[(size_t)h * rec + D + R] = m_l[h];
+        out[(size_t)h * rec + D + R + 1] = l_l[h];
     }
 }
 
@@ -318,7 +435,7 @@ hipError_t launch_dr(const DecodeArgs& a, hipStream_t stream) {
     auto kern = split_rope_mfma_kernel<D, R>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), lds, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -338,15 +455,16 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool rope_mfma_path_supports(int H, int d_h, int r, int dtype) {
-    if (dtype != 1 || H < 1 || H > 32) return false;
+    if (dtype != 1 || H < 1 || H > kMaxHeads) return false;
     if (d_h != 64 && d_h != 128) return false;
-    if (!(r == 0 || r == 8 || r == 16 || r == 32 || r == 48 || r == 64)) return false;
-    return RopeCfg<128, 64>::lds_bytes(H) <= 160 * 1024;
+    return r == 0 || r == 8 || r == 16 || r == 32 || r == 48 || r == 64;
 }
 
 int rope_mfma_rows_per_tile() { return kTileRows; }
+int rope_mfma_workgroups() { return 256; }  // one per CU
 
 hipError_t launch_split_rope_mfma(const DecodeArgs& a, hipStream_t stream) {
+    static_assert(RopeCfg<128, 64>::lds_bytes(kMaxHeads) <= 160 * 1024, "LDS");
     if (a.d_h == 64) return launch_d<64>(a, stream);
     if (a.d_h == 128) return launch_d<128>(a, stream);
     return hipErrorInvalidValue;

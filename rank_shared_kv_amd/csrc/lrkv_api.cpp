@@ -91,8 +91,8 @@ constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's 
 // Which decode the plan is for.  The normalised variant's bf16 matrix-core kernel is built for one wave per
 // SIMD; neither it nor the paged cache has an fp32 matrix-core kernel (the general kernel serves them).  Their
 // G never exceeds the plain plan's, so the plain workspace size serves them, and a paged decode of a bf16
-// matrix-core shape uses exactly the plain plan.  The rotary variant has kernels of its own (two resident
-// workgroups per CU for the bf16 one) and its own workspace query.  Query sets (multi-token decode with
+// matrix-core shape uses exactly the plain plan.  The rotary variant has kernels of its own (one
+// eight-wave workgroup per CU for the bf16 one) and its own workspace query.  Query sets (multi-token decode with
 // several tokens per workgroup) run the bf16 matrix-core kernel at one wave per SIMD.
 enum class PlanVariant { kPlain, kNormed, kPaged, kRope, kQuerySets };
 
@@ -123,7 +123,7 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
         p.occupancy = 1;
         const long tiles_per_seq = max_len > 0 ? (max_len + p.chunk - 1) / p.chunk : 0;
         // one resident round of workgroups; capped by the plain plan except for the rotary variant
-        long G = p.path == SplitPath::kGeneral ? 1024 : p.path == SplitPath::kRopeMfma ? 512 : 256;
+        long G = p.path == SplitPath::kGeneral ? 1024 : p.path == SplitPath::kRopeMfma ? rope_mfma_workgroups() : 256;
         if (variant != PlanVariant::kRope) G = std::min<long>(plain.num_splits, G);
         G = std::min<long>(G, (long)d.batch + kMaxExtraSplits);
         G = std::min<long>(G, (long)d.batch * tiles_per_seq);

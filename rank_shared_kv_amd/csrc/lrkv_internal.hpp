@@ -67,6 +67,7 @@ int mfma_max_query_width(int H, int d_h, int r);  // multi-token decode: query t
 bool general_path_supports(int H, int d_h, int r);
 bool rope_mfma_path_supports(int H, int d_h, int r, int dtype);  // rotary variant, bf16 matrix-core kernel
 int rope_mfma_rows_per_tile();
+int rope_mfma_workgroups();  // G of the rotary bf16 matrix-core kernel (one workgroup per CU)
 hipError_t launch_split_rope_mfma(const DecodeArgs& a, hipStream_t stream);
 size_t general_lds_bytes(int H, int d_h, int r, bool rope = false);
 

@@ -250,11 +250,13 @@ def test_multi_query_plan_arithmetic(monkeypatch):
 
 
 def test_rope_plan_arithmetic():
-    """The rotary decode plans on its own: up to 512 workgroups (two per CU) on the bf16 matrix-core shapes,
-    the general kernel's 1024 elsewhere; workspace = G * H * record floats."""
+    """The rotary decode plans on its own: up to 256 workgroups (one eight-wave workgroup per CU) on the bf16
+    matrix-core shapes, the general kernel's 1024 elsewhere; workspace = G * H * record floats."""
     d = lk.make_dims(4, 32, 128, 64, 33024, 1)
     rec = (128 + 64 + 2 + 3) // 4 * 4
-    assert lk.lrkv_decode_rope_workspace_bytes(d, 32818) == 4 * 512 * 32 * rec
+    assert lk.lrkv_decode_rope_workspace_bytes(d, 32818) == 4 * 256 * 32 * rec
+    # a short batch: at most one workgroup per 64-row tile of each sequence
+    assert lk.lrkv_decode_rope_workspace_bytes(lk.make_dims(3, 8, 64, 16, 256, 1), 100) == 4 * 3 * 2 * 8 * 84
     small = lk.make_dims(2, 4, 16, 4, 128, 0)
     G = lk.lrkv_decode_rope_workspace_bytes(small, 100) // (4 * 4 * ((16 + 4 + 2 + 3) // 4 * 4))
     assert G == 2 * math.ceil(100 / 32)  # one workgroup per 32-row tile of each sequence, the general kernel
