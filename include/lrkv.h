@@ -300,7 +300,7 @@ lrkv_status lrkv_decode_paged(const lrkv_dims* dims, const lrkv_paged_cache* cac
 lrkv_status lrkv_rope_table(int32_t d_h, int32_t n_pos, float base, float* table, void* stream);
 
 /* Bytes of device workspace lrkv_decode_rope needs (its own plan: the
- * matrix-core rotary kernel keeps two workgroups per CU).  Returns 0 for
+ * matrix-core rotary kernel runs one eight-wave workgroup per CU).  Returns 0 for
  * invalid dims or d_h not a multiple of 4.  Host arithmetic only. */
 size_t lrkv_decode_rope_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
 

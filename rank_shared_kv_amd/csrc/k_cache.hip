@@ -13,7 +13,8 @@
 // append + absorb: both in one launch (a decode step's per-token work).
 // multi-token lengths: query i of Q at the end of sequence b sees
 //          max(0, L_b - Q + 1 + i) rows (the causal mask inside the chunk);
-//          the multi-token decode runs one virtual sequence per query token.
+//          the multi-token decode runs one virtual sequence per set of qw
+//          consecutive query tokens, with the length of the set's last token.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
 
