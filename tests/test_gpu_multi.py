@@ -127,18 +127,20 @@ def test_single_query_through_multi_equals_decode():
     assert torch.equal(got, out)
 
 
-@pytest.mark.timeout(600)
-def test_multi_query_long_context_full_size():
-    """The long-context workload (batch 4, H 32, d_h 128, r 64, bf16) with Q = 4 query tokens per sequence in
-    the benchmark's launch configuration; the first and last sequence are checked in full against the
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("workload", ["long_context", "ragged"])
+def test_multi_query_full_size(workload):
+    """The long-context workload (batch 4, H 32, d_h 128, r 64: two query tokens per workgroup) and the
+    64-sequence ragged batch (r 32: four per workgroup), bf16, with Q = 4 query tokens per sequence in the
+    benchmark's launch configuration; the first and last sequence are checked in full against the
     reference."""
     import bench
     Q = 4
-    w0 = synth.WORKLOADS["long_context"]
+    w0 = synth.WORKLOADS[workload]
     L_cap, max_len = bench.launch_config(w0, 50 * Q)
     w = w0.with_(L_cap=L_cap)
     lens = synth.seq_lengths(w)
-    say(f"[case] multi-query long context Q={Q} L_cap={L_cap}")
+    say(f"[case] multi-query {workload} Q={Q} L_cap={L_cap}")
     dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens)
     qh = synth.normal(9200, 1.0, w.batch * Q * w.H * w.d_h, "bf16").reshape(w.batch, Q, w.H, w.d_h)
     got = _multi_gpu(w, dev, Q, qh, max_len).cpu().numpy()
