@@ -158,8 +158,8 @@ def main():
         log(f"bench: copied {n * 4} bytes 5 times")
         return
     if args.gpus != 1:
-        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(sequence, head and L sharding across GPUs are described in DESIGN.md, not run)", file=sys.stderr)
+        print(f"bench.py: the decode path runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     if sum([args.queries > 1, args.layer, args.norm, args.paged > 0, args.rope]) > 1:
