@@ -9,25 +9,27 @@
 // linear, so the score splits into a shared part, qtilde_h . (k_s[j] D_j), and
 // a private part, qtilde_h . ((z^K_{h,j} (B^K_h)^T) D_j).
 //
-// A workgroup of 8 waves owns one (sequence, split) and walks its 64-row tiles
+// A workgroup of 8 waves owns one (sequence, split) and walks its 128-row tiles
 // (tile s, s + S_b, ... of the sequence); one workgroup per CU.  Per tile:
-//   1. stage: each shared key row is turned once (fp32) and kept as a bf16
-//      high part and a bf16 remainder; the (cos, sin) rows go to LDS as fp32,
-//      the value rows as V^T (bf16);
+//   1. stage: the (cos, sin) rows go to LDS as fp32, the value rows as V^T
+//      (bf16); each wave also loads the shared-key fragments of its 16-row
+//      group for step 2a into registers;
 //   2a. shared scores of all heads on the matrix cores (v_mfma_f32_16x16x32_bf16):
-//      S[16 rows x 16 heads] = Ktilde Qtilde^T with both operands split into
-//      high + low bf16 parts (hi*hi + hi*lo + lo*hi; about 16 significant bits
-//      of each operand), one (row group, head group) block per wave;
+//      wave w turns the key rows of row group w (fp32) and splits them into
+//      bf16 high and low parts, and computes S[16 rows x 16 heads] = Ktilde
+//      Qtilde^T for every head group with both operands split (hi*hi + hi*lo
+//      + lo*hi; about 16 significant bits of each operand);
 //   2b. private scores: wave w takes heads w, w + 8, ...; per head it loads
-//      the B^K_h fragments once and, per 16-row group, rebuilds the private key
-//      16 columns at a time, Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16]
-//      (exact bf16 products, fp32 sums).  Lane (row n16, g4) then holds
-//      columns 16 cb + 4 g4 + i of its row: it turns the two coordinate pairs
-//      (fp32) and dots them with the rotated query; the four lanes of a row sum
-//      in a fixed order;
-//   3. softmax: one wave per head, lanes = the tile's rows, online max and
+//      the B^K_h fragments once for the tile's two 64-row halves and, per
+//      16-row group, rebuilds the private key 16 columns at a time,
+//      Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16] (exact bf16
+//      products, fp32 sums).  Lane (row n16, g4) then holds columns
+//      16 cb + 4 g4 + i of its row: it turns the two coordinate pairs (fp32)
+//      and dots them with the rotated query; the four lanes of a row sum in a
+//      fixed order;
+//   3. softmax: one wave per head, two rows per lane, online max and
 //      denominator in LDS;
-//   4. values: the shared sum O^T[d_h x 16 heads] += V^T[d_h x 64] P^T on the
+//   4. values: the shared sum O^T[d_h x 16 heads] += V^T[d_h x 128] P^T on the
 //      matrix cores (P split into bf16 high + low parts), one or two
 //      (column block, head group) blocks per wave; the private sum on the VALU:
 //      a thread owns one 16-byte chunk (8 coordinates of one head) of the
@@ -49,30 +51,30 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kTileRows = 64;  // 4 groups of 16 rows
+constexpr int kTileRows = 128;  // 8 groups of 16 rows
+constexpr int kHalfRows = 64;   // rows of one private-score pass (4 groups of 16)
 constexpr int kMaxHeads = 32;
+constexpr int kBatchRows = 16;  // private-value rows whose latent loads are issued together
 
 template <int D, int R>
 struct RopeCfg {
     static constexpr int CB = D / 16;                 // 16-column blocks of a key or value row
     static constexpr int KSD = D / 32;                // k-steps of the shared-score product
     static constexpr int NKS = (R + 31) / 32;         // k-steps of 32 latent coordinates
-    static constexpr int KR_STRIDE = D + 8;           // bf16 per turned shared-key row (hi and lo arrays)
     static constexpr int CS_STRIDE = D + 4;           // floats per staged (cos, sin) row
-    static constexpr int VT_STRIDE = kTileRows + 8;   // bf16 per V^T row (one value column, 64 rows)
+    static constexpr int VT_STRIDE = kTileRows + 8;   // bf16 per V^T row (one value column, 128 rows)
     static constexpr int E_STRIDE = kTileRows + 4;    // floats per head of the score / weight rows
     static constexpr int NCH = R / 8;                 // 16-byte chunks (8 coordinates) of a head's latent row
     static constexpr int SVB = (CB * 2 + kWaves - 1) / kWaves;  // shared-value blocks per wave (H <= 32)
-    static constexpr size_t KR_BYTES = (size_t)2 * kTileRows * KR_STRIDE * 2;
     static constexpr size_t CS_BYTES = (size_t)kTileRows * CS_STRIDE * 4;
     static constexpr size_t VT_BYTES = (size_t)D * VT_STRIDE * 2;
+    // the weight rows come last but for the 96 floats of running state, which a masked read past the last
+    // head's row (private values, at most 31 floats) may touch
     static constexpr size_t lds_bytes(int H) {
-        return KR_BYTES + CS_BYTES + VT_BYTES + (size_t)H * D * 4 + 2 * (size_t)kMaxHeads * E_STRIDE * 4 +
+        return CS_BYTES + VT_BYTES + (size_t)H * D * 4 + 2 * (size_t)kMaxHeads * E_STRIDE * 4 +
                3 * (size_t)kMaxHeads * 4;
     }
 };
-
-constexpr int kBatchRows = 16;  // private-value rows whose latent loads are issued together
 
 // (hi, lo) bf16 parts of x: hi = bf16(x), lo = bf16(x - hi); hi + lo carries about 16 significant bits
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
@@ -84,18 +86,17 @@ template <int D, int R>
 __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs a) {
     using C = RopeCfg<D, R>;
     constexpr int CB = C::CB, NKS = C::NKS, KSD = C::KSD;
+    static_assert(R <= 64, "a head's latent row is at most 8 chunks, so a tile part holds at most 64 rows");
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     const int H = a.H;
-    uint16_t* kr_hi = (uint16_t*)lds;                                       // [64][D + 8]
-    uint16_t* kr_lo = kr_hi + (size_t)kTileRows * C::KR_STRIDE;             // [64][D + 8]
-    float* cs_l = (float*)(lds + C::KR_BYTES);                              // [64][D + 4]
-    uint16_t* vt = (uint16_t*)(lds + C::KR_BYTES + C::CS_BYTES);            // [D][64 + 8]
-    float* qr_l = (float*)(lds + C::KR_BYTES + C::CS_BYTES + C::VT_BYTES);  // [H][D]
-    float* es_l = qr_l + (size_t)H * D;                                     // [32][64 + 4] shared scores
-    float* ep_l = es_l + (size_t)kMaxHeads * C::E_STRIDE;                   // [32][64 + 4] private, then weights
-    float* m_l = ep_l + (size_t)kMaxHeads * C::E_STRIDE;                    // [32] running max (log2 units)
-    float* l_l = m_l + kMaxHeads;                                           // [32] denominator
-    float* al_l = l_l + kMaxHeads;                                          // [32] this tile's rescale
+    float* cs_l = (float*)lds;                                // [128][D + 4]
+    uint16_t* vt = (uint16_t*)(lds + C::CS_BYTES);            // [D][128 + 8]
+    float* qr_l = (float*)(lds + C::CS_BYTES + C::VT_BYTES);  // [H][D]
+    float* es_l = qr_l + (size_t)H * D;                       // [32][128 + 4] shared scores
+    float* ep_l = es_l + (size_t)kMaxHeads * C::E_STRIDE;     // [32][128 + 4] private, then weights
+    float* m_l = ep_l + (size_t)kMaxHeads * C::E_STRIDE;      // [32] running max (log2 units)
+    float* l_l = m_l + kMaxHeads;                             // [32] denominator
+    float* al_l = l_l + kMaxHeads;                            // [32] this tile's rescale
 
     const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
     const int b = wslot.b, split = wslot.s;
@@ -135,10 +136,6 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
     }
     __syncthreads();
 
-    // shared-score block of this wave: row group rg2, head group hg2 (waves past the head groups idle there)
-    const int rg2 = wave & 3, hg2 = wave >> 2;
-    const bool do_sh = hg2 < NHG;
-
     // shared-value blocks of this wave: block blk = wave + 8 k is (column block blk % CB, head group blk / CB)
     f32x4_t acc_sv[C::SVB];
 #pragma unroll
@@ -150,7 +147,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
     const int cells = H * C::NCH;
     int parts = 1;
     while (cells > 0 && parts < 16 && 2 * parts * cells <= kThreads) parts *= 2;
-    const int rpp = kTileRows / parts;  // rows per part
+    const int rpp = kTileRows / parts;  // rows per part: 8 .. 64
     const int cell = cells > 0 ? tid % cells : 0, part = cells > 0 ? tid / cells : 0;
     const bool own_pr = R > 0 && part < parts;
     const int hv = cell / (C::NCH > 0 ? C::NCH : 1);  // the cell's head
@@ -158,33 +155,60 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc_pr[j] = 0.f;
 
+    // Latent fragments of one head over 64 rows (four 16-row groups) of a tile; rows past the tile's end
+    // re-read its last live row.  Two register sets are used in turn, so that the next 64 rows load while
+    // the current ones compute; the first half of the next tile's first head is loaded at the end of a
+    // tile's private-score phase.  Vector loads retire in order, so every load here is issued
+    // unconditionally (a stand-in head or row where there is none): a load issued on one branch only would
+    // make the compiler wait for it wherever an older load is waited for after the branches join.
+    constexpr int NKS1 = NKS > 0 ? NKS : 1;
+    typedef u32x4_t ZFrag[4][NKS1];
+    typedef u32x4_t BFrag[CB][NKS1];
+    auto load_z = [&](ZFrag& zf, int h, int tb, int nv, int half) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const size_t row = (size_t)(tb + min(kHalfRows * half + 16 * rg + n16, nv - 1));
+#pragma unroll
+            for (int ks = 0; ks < NKS1; ++ks) {
+                const int k = 32 * ks + 8 * g4;
+                zf[rg][ks] = (k < R) ? *(const u32x4_t*)(zkg + (row * H + h) * R + k) : u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    const int hw0 = min(wave, H - 1);  // this wave's first head (a stand-in for a wave without heads)
+    ZFrag za, zb;
+    if constexpr (NKS > 0) load_z(za, hw0, split * kTileRows, min(kTileRows, Lb - split * kTileRows), 0);
+
+    // private-value latent rows of this thread's part, 16 at a time in two register sets; the first set is
+    // loaded before the softmax (rows past the part's end re-read its last live row)
+    const int rbeg = own_pr ? part * rpp : 0;
+    u32x4_t va[kBatchRows], vb[kBatchRows];
+    auto load_v = [&](u32x4_t (&zv)[kBatchRows], int tb, int r0, int rend) {
+        const uint16_t* zbase = zvg + (size_t)tb * H * R + 8 * cell;
+#pragma unroll
+        for (int k = 0; k < kBatchRows; ++k)
+            zv[k] = *(const u32x4_t*)(zbase + (size_t)max(min(r0 + k, rend - 1), 0) * H * R);
+    };
+
     for (int t0 = split * kTileRows; t0 < Lb; t0 += wslot.S_b * kTileRows) {
         const int nvalid = min(kTileRows, Lb - t0);
         __syncthreads();  // the previous tile's staged rows and weights are consumed
-        // ---- 1. stage the tile.  Key and (cos, sin) rows past the end re-read the last live row (their
-        //         scores are masked); value rows past the end are zero (weight 0 must not meet arbitrary
-        //         contents) ----
-        for (int idx = tid; idx < kTileRows * (D / 8); idx += kThreads) {
-            const int r = idx / (D / 8), c8 = idx - r * (D / 8);
-            const size_t row = (size_t)(t0 + min(r, nvalid - 1));
-            const u32x4_t kv = *(const u32x4_t*)(ksg + row * D + 8 * c8);
-            const f32x4_t c0 = *(const f32x4_t*)(a.rope_cs + row * D + 8 * c8);      // pairs 4 c8, 4 c8 + 1
-            const f32x4_t c1 = *(const f32x4_t*)(a.rope_cs + row * D + 8 * c8 + 4);  // pairs 4 c8 + 2, + 3
-            *(f32x4_t*)(cs_l + r * C::CS_STRIDE + 8 * c8) = c0;
-            *(f32x4_t*)(cs_l + r * C::CS_STRIDE + 8 * c8 + 4) = c1;
-            u32x4_t hi4, lo4;
+        // ---- 1. stage the tile.  This wave's shared-key fragments (row group `wave`, for step 2a) go to
+        //         registers.  Key and (cos, sin) rows past the end re-read the last live row (their scores are
+        //         masked); value rows past the end are zero (weight 0 must not meet arbitrary contents) ----
+        const int rk = 16 * wave + n16;  // this lane's key row in the tile (step 2a)
+        u32x4_t kf[KSD];
+        {
+            const size_t row = (size_t)(t0 + min(rk, nvalid - 1));
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {  // pair p of the 8 columns: (x0, x1) turned by (cos, sin)
-                const float x0 = bf16_lo(kv[p]), x1 = bf16_hi(kv[p]);
-                const float co = p < 2 ? c0[2 * p] : c1[2 * p - 4], si = p < 2 ? c0[2 * p + 1] : c1[2 * p - 3];
-                uint32_t h0, l0, h1, l1;
-                split_bf16(x0 * co - x1 * si, h0, l0);
-                split_bf16(x0 * si + x1 * co, h1, l1);
-                hi4[p] = h0 | (h1 << 16);
-                lo4[p] = l0 | (l1 << 16);
-            }
-            *(u32x4_t*)(kr_hi + r * C::KR_STRIDE + 8 * c8) = hi4;
-            *(u32x4_t*)(kr_lo + r * C::KR_STRIDE + 8 * c8) = lo4;
+            for (int ks = 0; ks < KSD; ++ks) kf[ks] = *(const u32x4_t*)(ksg + row * D + 32 * ks + 8 * g4);
+        }
+#pragma unroll
+        for (int it = 0; it < kTileRows * (D / 4) / kThreads; ++it) {
+            const int idx = tid + it * kThreads;
+            const int r = idx / (D / 4), c4 = idx - r * (D / 4);
+            const size_t row = (size_t)(t0 + min(r, nvalid - 1));
+            *(f32x4_t*)(cs_l + r * C::CS_STRIDE + 4 * c4) = *(const f32x4_t*)(a.rope_cs + row * D + 4 * c4);
         }
         for (int idx = tid; idx < (kTileRows / 4) * (D / 8); idx += kThreads) {
             // V^T: 4 consecutive rows x 8 columns per thread, one 8-byte store per column
@@ -193,10 +217,9 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int r = 4 * r4 + k;
-                const u32x4_t v = (r < nvalid) ? *(const u32x4_t*)(vsg + (size_t)(t0 + r) * D + 8 * c8)
-                                               : u32x4_t{0u, 0u, 0u, 0u};
+                const u32x4_t v = *(const u32x4_t*)(vsg + (size_t)(t0 + min(r, nvalid - 1)) * D + 8 * c8);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[k][e] = v[e];
+                for (int e = 0; e < 4; ++e) w[k][e] = (r < nvalid) ? v[e] : 0u;  // loaded anyway: no branch
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -209,72 +232,70 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
         }
         __syncthreads();
 
-        // ---- 2a. shared scores: rows 16 rg2 .., heads 16 hg2 .. ----
-        if (do_sh) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            const int rl = 16 * rg2 + n16;
-            const int hq = 16 * hg2 + n16;  // the query row of the B operand (zero past H)
+        // ---- 2a. shared scores: rows 16 wave .., every head group.  The key fragment is turned by its row's
+        //          (cos, sin) pairs once and split into (hi, lo) bf16 parts ----
+        {
+            u32x4_t khi[KSD], klo[KSD];
 #pragma unroll
             for (int ks = 0; ks < KSD; ++ks) {
                 const int c = 32 * ks + 8 * g4;
-                const bf16x8_t khi = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr_hi + rl * C::KR_STRIDE + c));
-                const bf16x8_t klo = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(kr_lo + rl * C::KR_STRIDE + c));
-                // the rotated query's 8 values split into (hi, lo) bf16 parts
-                f32x4_t q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
-                if (hq < H) {
-                    q0 = *(const f32x4_t*)(qr_l + hq * D + c);
-                    q1 = *(const f32x4_t*)(qr_l + hq * D + c + 4);
-                }
-                u32x4_t qh4, ql4;
+                const f32x4_t c0 = *(const f32x4_t*)(cs_l + rk * C::CS_STRIDE + c);      // pairs c/2, c/2 + 1
+                const f32x4_t c1 = *(const f32x4_t*)(cs_l + rk * C::CS_STRIDE + c + 4);  // pairs c/2 + 2, + 3
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int p = 0; p < 4; ++p) {  // pair p of the 8 columns: (x0, x1) turned by (cos, sin)
+                    const float x0 = bf16_lo(kf[ks][p]), x1 = bf16_hi(kf[ks][p]);
+                    const float co = p < 2 ? c0[2 * p] : c1[2 * p - 4], si = p < 2 ? c0[2 * p + 1] : c1[2 * p - 3];
                     uint32_t h0, l0, h1, l1;
-                    split_bf16(i < 2 ? q0[2 * i] : q1[2 * i - 4], h0, l0);
-                    split_bf16(i < 2 ? q0[2 * i + 1] : q1[2 * i - 3], h1, l1);
-                    qh4[i] = h0 | (h1 << 16);
-                    ql4[i] = l0 | (l1 << 16);
+                    split_bf16(x0 * co - x1 * si, h0, l0);
+                    split_bf16(x0 * si + x1 * co, h1, l1);
+                    khi[ks][p] = h0 | (h1 << 16);
+                    klo[ks][p] = l0 | (l1 << 16);
                 }
-                const bf16x8_t qhi = __builtin_bit_cast(bf16x8_t, qh4);
-                const bf16x8_t qlo = __builtin_bit_cast(bf16x8_t, ql4);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, qhi, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, qlo, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, qhi, acc, 0, 0, 0);
             }
-            // lane (head n16, g4) holds rows 16 rg2 + 4 g4 + i
-            const int h = 16 * hg2 + n16;
-            if (h < H) *(f32x4_t*)(es_l + h * C::E_STRIDE + 16 * rg2 + 4 * g4) = acc;
+            for (int hg = 0; hg < NHG; ++hg) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                const int hq = 16 * hg + n16;  // the query row of the B operand (zero past H)
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks) {
+                    const int c = 32 * ks + 8 * g4;
+                    // the rotated query's 8 values split into (hi, lo) bf16 parts
+                    f32x4_t q0 = {0.f, 0.f, 0.f, 0.f}, q1 = {0.f, 0.f, 0.f, 0.f};
+                    if (hq < H) {
+                        q0 = *(const f32x4_t*)(qr_l + hq * D + c);
+                        q1 = *(const f32x4_t*)(qr_l + hq * D + c + 4);
+                    }
+                    u32x4_t qh4, ql4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t h0, l0, h1, l1;
+                        split_bf16(i < 2 ? q0[2 * i] : q1[2 * i - 4], h0, l0);
+                        split_bf16(i < 2 ? q0[2 * i + 1] : q1[2 * i - 3], h1, l1);
+                        qh4[i] = h0 | (h1 << 16);
+                        ql4[i] = l0 | (l1 << 16);
+                    }
+                    const bf16x8_t khv = __builtin_bit_cast(bf16x8_t, khi[ks]);
+                    const bf16x8_t klv = __builtin_bit_cast(bf16x8_t, klo[ks]);
+                    const bf16x8_t qhi = __builtin_bit_cast(bf16x8_t, qh4);
+                    const bf16x8_t qlo = __builtin_bit_cast(bf16x8_t, ql4);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khv, qhi, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khv, qlo, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klv, qhi, acc, 0, 0, 0);
+                }
+                // lane (head n16, g4) holds rows 16 wave + 4 g4 + i
+                if (hq < H) *(f32x4_t*)(es_l + hq * C::E_STRIDE + 16 * wave + 4 * g4) = acc;
+            }
         }
 
-        // ---- 2b. private scores of this wave's heads.  The next head's latent fragments (from HBM) are loaded
-        //          while this head computes: two register sets, used in turn; the B^K_h fragments (from L2)
-        //          are loaded per head. ----
+        // ---- 2b. private scores of this wave's heads: per head, the B^K_h fragments (from L2) once, then the
+        //          tile's two 64-row halves (h, 0) in za and (h, 1) in zb.  The B^K_h loads are issued before
+        //          the next half's latent loads (from HBM), so the first product waits for the former only ----
+        const int rbeg_end = min(rbeg + rpp, nvalid);  // end of this thread's private-value rows
         if constexpr (NKS > 0) {
-            typedef u32x4_t ZFrag[4][NKS];
-            auto load_z = [&](ZFrag& zf, int h) {
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const size_t row = (size_t)(t0 + min(16 * rg + n16, nvalid - 1));
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        const int k = 32 * ks + 8 * g4;
-                        zf[rg][ks] = (k < R) ? *(const u32x4_t*)(zkg + (row * H + h) * R + k) : u32x4_t{0u, 0u, 0u, 0u};
-                    }
-                }
-            };
-            auto score_head = [&](const ZFrag& zf, int h) {
-                u32x4_t bf[CB][NKS];
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        const int k = 32 * ks + 8 * g4;
-                        bf[cb][ks] = (k < R) ? *(const u32x4_t*)(bkg + ((size_t)h * D + 16 * cb + n16) * R + k)
-                                             : u32x4_t{0u, 0u, 0u, 0u};
-                    }
+            auto score_half = [&](const ZFrag& zf, const u32x4_t (&bf)[CB][NKS1], int h, int half) {
                 const float* qh = qr_l + (size_t)h * D;
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    const int rl = 16 * rg + n16;  // this lane's row in the tile
+                    const int rl = kHalfRows * half + 16 * rg + n16;  // this lane's row in the tile
                     float part = 0.f;
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
@@ -297,36 +318,52 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
                     if (g4 == 0) ep_l[(size_t)h * C::E_STRIDE + rl] = part;
                 }
             };
-            ZFrag za, zb;
-            if (wave < H) load_z(za, wave);
-            for (int h = wave; h < H; h += 2 * kWaves) {  // heads h (in za) and h + 8 (in zb)
-                const int h1 = h + kWaves, h2 = h + 2 * kWaves;
-                if (h1 < H) load_z(zb, h1);
-                score_head(za, h);
-                if (h1 >= H) break;
-                if (h2 < H) load_z(za, h2);
-                score_head(zb, h1);
+            auto load_bk = [&](BFrag& bf, int h) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int k = 32 * ks + 8 * g4;
+                        bf[cb][ks] = (k < R) ? *(const u32x4_t*)(bkg + ((size_t)h * D + 16 * cb + n16) * R + k)
+                                             : u32x4_t{0u, 0u, 0u, 0u};
+                    }
+            };
+            // the next tile of this split (this tile again when there is none: the loads are then stand-ins)
+            const int t0n = t0 + wslot.S_b * kTileRows;
+            const int tbn = t0n < Lb ? t0n : t0, nvn = t0n < Lb ? min(kTileRows, Lb - t0n) : nvalid;
+            BFrag bf;
+            for (int h = wave; h < H; h += kWaves) {
+                const bool last = h + kWaves >= H;  // the next unit is the next tile's first head
+                load_bk(bf, h);
+                load_z(zb, h, t0, nvalid, 1);
+                score_half(za, bf, h, 0);
+                load_z(za, last ? hw0 : h + kWaves, last ? tbn : t0, last ? nvn : nvalid, 0);
+                score_half(zb, bf, h, 1);
             }
         }
+        if constexpr (R > 0) load_v(va, t0, rbeg, rbeg_end);  // the first private-value batch
         __syncthreads();
 
-        // ---- 3. online softmax, one wave per head, lanes = rows ----
+        // ---- 3. online softmax, one wave per head, rows lane and lane + 64 ----
         for (int h = wave; h < H; h += kWaves) {
             float* eh = ep_l + (size_t)h * C::E_STRIDE;
-            const bool live = lane < nvalid;
-            const float raw = es_l[(size_t)h * C::E_STRIDE + lane] + (NKS > 0 ? eh[lane] : 0.f);
-            const float s = live ? raw * scale : -INFINITY;
-            float tmax = s;
+            const float* sh = es_l + (size_t)h * C::E_STRIDE;
+            const bool live0 = lane < nvalid, live1 = lane + 64 < nvalid;
+            const float s0 = live0 ? (sh[lane] + (NKS > 0 ? eh[lane] : 0.f)) * scale : -INFINITY;
+            const float s1 = live1 ? (sh[lane + 64] + (NKS > 0 ? eh[lane + 64] : 0.f)) * scale : -INFINITY;
+            float tmax = fmaxf(s0, s1);
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
             const float m_old = m_l[h];
             const float m_new = fmaxf(m_old, tmax);  // finite: the tile holds a live row
             const float alpha = fast_exp2(m_old - m_new);
-            const float e = live ? fast_exp2(s - m_new) : 0.f;
-            float esum = e;
+            const float e0 = live0 ? fast_exp2(s0 - m_new) : 0.f;
+            const float e1 = live1 ? fast_exp2(s1 - m_new) : 0.f;
+            float esum = e0 + e1;
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) esum += __shfl_xor(esum, o);
-            eh[lane] = e;
+            eh[lane] = e0;
+            eh[lane + 64] = e1;
             wave_lds_sync();
             if (lane == 0) {
                 m_l[h] = m_new;
@@ -336,7 +373,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
         }
         __syncthreads();
 
-        // ---- 4a. shared values on the matrix cores: O^T[16 cols x 16 heads] += V^T[16 x 64] P^T[64 x 16] ----
+        // ---- 4a. shared values on the matrix cores: O^T[16 cols x 16 heads] += V^T[16 x 128] P^T[128 x 16] ----
 #pragma unroll
         for (int k = 0; k < C::SVB; ++k) {
             const int blk = wave + kWaves * k;
@@ -368,30 +405,33 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
             }
         }
 
-        // ---- 4b. private values: chunk `cell` of the latent rows of this thread's part, 16 rows at a time whose
-        //          loads are issued before any of their arithmetic (rows past the tile's end re-read the last
-        //          live row and are skipped) ----
-        if (own_pr) {
+        // ---- 4b. private values: chunk `cell` of the latent rows of this thread's part, in batches of 16
+        //          rows, two register sets used in turn; the first batch was loaded before the softmax ----
+        if constexpr (R > 0) {
             const float al = al_l[hv];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc_pr[j] *= al;
-            const float* eh = ep_l + (size_t)hv * C::E_STRIDE;
-            const int rbeg = part * rpp, rend = min(rbeg + rpp, nvalid);
-            const uint16_t* zbase = zvg + (size_t)t0 * H * R + 8 * cell;
-            for (int r0 = rbeg; r0 < rend; r0 += kBatchRows) {
-                u32x4_t zb[kBatchRows];
-#pragma unroll
-                for (int k = 0; k < kBatchRows; ++k)
-                    zb[k] = *(const u32x4_t*)(zbase + (size_t)min(r0 + k, rend - 1) * H * R);
+            for (int j = 0; j < 8; ++j) acc_pr[j] *= al;  // threads without a part: sums never stored
+            // Branch-free.  Rows past the tile's end have weight 0 in LDS; rows past the part are masked by a
+            // uniform test.  Their latents are re-read live rows, so finite.  The weight read for such a row
+            // can lie up to 31 floats past this head's row, inside the workgroup's LDS, and is discarded.  A
+            // thread without a part reads part 0 and never stores its sums.
+            const float* ep = ep_l + (size_t)hv * C::E_STRIDE + rbeg;
+            auto consume = [&](const u32x4_t (&zv)[kBatchRows], int kb) {
 #pragma unroll
                 for (int k = 0; k < kBatchRows; ++k) {
-                    if (r0 + k < rend) {
-                        const float e = eh[r0 + k];
+                    const float ek = ep[kb + k];
+                    const float e = (kb + k < rpp) ? ek : 0.f;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            acc_pr[j] = fmaf(e, (j & 1) ? bf16_hi(zb[k][j >> 1]) : bf16_lo(zb[k][j >> 1]), acc_pr[j]);
-                    }
+                    for (int j = 0; j < 8; ++j)
+                        acc_pr[j] = fmaf(e, (j & 1) ? bf16_hi(zv[k][j >> 1]) : bf16_lo(zv[k][j >> 1]), acc_pr[j]);
                 }
+            };
+            // batches 2 i (in va) and 2 i + 1 (in vb); the load after the last pair is a stand-in
+            for (int kb = 0; kb < rpp; kb += 2 * kBatchRows) {
+                load_v(vb, t0, rbeg + kb + kBatchRows, rbeg_end);
+                consume(va, kb);
+                load_v(va, t0, rbeg + kb + 2 * kBatchRows, rbeg_end);
+                consume(vb, kb + kBatchRows);
             }
         }
     }
@@ -408,7 +448,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
         const int h = 16 * hg + n16;
         if (hg < NHG && h < H) *(f32x4_t*)(out + (size_t)h * rec + 16 * cb + 4 * g4) = acc_sv[k];
     }
-    if constexpr (R > 0) {  // the parts' private sums, added in part order (the staged-key area is free now)
+    if constexpr (R > 0) {  // the parts' private sums, added in part order (the staged (cos, sin) area is free now)
         float* pr_l = (float*)lds;  // [512][8]
         if (own_pr) {
 #pragma unroll

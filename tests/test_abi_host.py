@@ -255,8 +255,9 @@ def test_rope_plan_arithmetic():
     d = lk.make_dims(4, 32, 128, 64, 33024, 1)
     rec = (128 + 64 + 2 + 3) // 4 * 4
     assert lk.lrkv_decode_rope_workspace_bytes(d, 32818) == 4 * 256 * 32 * rec
-    # a short batch: at most one workgroup per 64-row tile of each sequence
-    assert lk.lrkv_decode_rope_workspace_bytes(lk.make_dims(3, 8, 64, 16, 256, 1), 100) == 4 * 3 * 2 * 8 * 84
+    # a short batch: at most one workgroup per 128-row tile of each sequence
+    assert lk.lrkv_decode_rope_workspace_bytes(lk.make_dims(3, 8, 64, 16, 256, 1), 100) == 4 * 3 * 1 * 8 * 84
+    assert lk.lrkv_decode_rope_workspace_bytes(lk.make_dims(3, 8, 64, 16, 256, 1), 129) == 4 * 3 * 2 * 8 * 84
     small = lk.make_dims(2, 4, 16, 4, 128, 0)
     G = lk.lrkv_decode_rope_workspace_bytes(small, 100) // (4 * 4 * ((16 + 4 + 2 + 3) // 4 * 4))
     assert G == 2 * math.ceil(100 / 32)  # one workgroup per 32-row tile of each sequence, the general kernel
