@@ -234,6 +234,9 @@ def main():
         lk.lrkv_rope_table(w.d_h, L_cap, 10000.0, rope_cs)
         nbytes = lk.lrkv_decode_rope_workspace_bytes(dims, max_len)
         ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+        # the rotary plan is its own: its split count from its workspace (one record of every head per
+        # split); its row granule is not exported
+        S, chunk = nbytes // (4 * w.H * ((w.d_h + w.r + 2 + 3) // 4 * 4)), None
     stream = torch.cuda.current_stream()
     pp = p if w.r else None
     bv = dev["B_v"] if w.r else None
