@@ -62,6 +62,8 @@ CASES = [  # (dtype, batch, H, d_h, r, lengths)
     ("bf16", 2, 8, 64, 0, [100, 31]),
     ("bf16", 2, 20, 128, 48, [300, 65]),    # a partial second head group; six latent chunks per head
     ("bf16", 3, 12, 64, 8, [130, 64, 1]),   # a partial head group; one latent chunk per head
+    ("bf16", 3, 32, 128, 64, [128, 129, 192]),  # a whole 128-row tile; one row past it; one and a half tiles
+    ("bf16", 2, 4, 64, 16, [200, 129]),       # fewer heads than waves: four waves without a head
     ("bf16", 2, 4, 48, 12, [90, 7]),
     ("f32", 2, 4, 16, 4, [64, 3]),
     ("f32", 2, 8, 128, 0, [129, 31]),
