@@ -116,6 +116,67 @@ def cpu_baseline(w, lens, budget_s: float):
                       f"OpenMP over pairs)"}
 
 
+def materialize_bench(args):
+    """Time lrkv_materialize over the workload's whole live cache: per step, K_h and V_h of every live
+    (row, head) are rebuilt and written.  Bytes: the factored rows read once plus both bases, and the
+    rebuilt rows written once."""
+    import numpy as np
+    import torch
+
+    import rank_shared_kv_amd as lk
+    import synth
+    from synth import device as sdev
+
+    w = synth.WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    lens = synth.seq_lengths(w)
+    L_cap, max_len = launch_config(w, 0, args.capacity)
+    log(f"bench: materialise, workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} "
+        f"L_max={int(lens.max())} steps={K} warmup={W}")
+    dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens)
+    dims = lk.make_dims(w.batch, w.H, w.d_h, w.r, L_cap, lk.LRKV_F32 if w.dtype == "f32" else lk.LRKV_BF16)
+    cache = lk.make_cache(dev["k_shared"], dev["v_shared"], dev["z_k"] if w.r else None,
+                          dev["z_v"] if w.r else None, dev["seq_lens"])
+    K_out = torch.empty((w.batch, w.H, L_cap, w.d_h), dtype=sdev.torch_dtype(w), device="cuda")
+    V_out = torch.empty_like(K_out)
+    stream = torch.cuda.current_stream()
+    bk, bv = (dev["B_k"], dev["B_v"]) if w.r else (None, None)
+    for _ in range(W):
+        lk.lrkv_materialize(dims, cache, max_len, bk, bv, K_out, V_out, stream)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(K):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        lk.lrkv_materialize(dims, cache, max_len, bk, bv, K_out, V_out, stream)
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(K_out[0, :, : int(lens[0])].float()).all())
+    us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / K
+    rows = int(np.sum(lens, dtype=np.int64))
+    s = w.elem_bytes
+    read_bytes = lk.lrkv_cache_bytes(dims, lens.tolist()) + 2 * w.H * w.d_h * w.r * s
+    write_bytes = 2 * rows * w.H * w.d_h * s
+    gbps = (read_bytes + write_bytes) / (us * 1e-6) / 1e9
+    log(f"bench: materialise {us:.1f} us per call = {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of peak)")
+    rec = {
+        "metric": "LRKV materialised keys and values, rebuilt row-heads/s (the training / prefill form), 1 GPU",
+        "value": rows * w.H / (us * 1e-6), "unit": "row·heads/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name + "+materialise", "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+                   "L": int(lens.max()), "L_cap": L_cap},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "lrkv_materialize",
+                     "algorithmic_bytes_per_launch": read_bytes + write_bytes, "read_bytes": read_bytes,
+                     "write_bytes": write_bytes, "avg_launch_us": us,
+                     "timing": f"HIP events around each of {K} launches"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +203,9 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="rotary variant: each step appends a row and runs lrkv_decode_rope (every head's key "
                          "rebuilt and turned at its position)")
+    ap.add_argument("--materialize", action="store_true",
+                    help="materialised path: each step rebuilds K_h and V_h of every live row and head "
+                         "(lrkv_materialize, the training / prefill form)")
     ap.add_argument("--no-stream-probe", action="store_true",
                     help="skip the streaming-read probe (the measured read bandwidth the split pass is compared with)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -162,9 +226,12 @@ def main():
               f"(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
-    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0, args.rope]) > 1:
-        print("bench.py: --queries, --layer, --norm, --paged and --rope do not combine", file=sys.stderr)
+    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0, args.rope, args.materialize]) > 1:
+        print("bench.py: --queries, --layer, --norm, --paged, --rope and --materialize do not combine",
+              file=sys.stderr)
         sys.exit(2)
+    if args.materialize:
+        return materialize_bench(args)
 
     import numpy as np
     import torch

@@ -5,11 +5,17 @@
 // a shared cache can preserve", sec. 3: the rebuilt form training and prefill
 // use).  Output [batch][H][L_cap][d_h] in the cache dtype.
 //
-// bf16 path (r <= 64): a wave owns 16 rows of one head and computes, per 16-column block
-// of d_h, Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16] on
-// v_mfma_f32_16x16x32_bf16 (k-steps of 32 rank coordinates; coordinates past r
-// enter as zeros).  In that layout each lane holds four consecutive columns of
-// one row, so the shared row is added and the result stored 8 bytes at a time.
+// bf16 path (r <= 64): per 16-column block of d_h and 16 rows,
+// Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16] on v_mfma_f32_16x16x32_bf16
+// (k-steps of 32 rank coordinates; coordinates past r enter as zeros).  In that
+// layout each lane holds four consecutive columns of one row, so the shared row
+// is added and the result stored 8 bytes at a time.  With d_h = 64 or 128 a wave
+// owns 64 rows of one head and issues all its loads first: the B_h fragments once
+// (16 KB at d_h = 128, r = 64, from L2), the latents of its 64 rows and their
+// shared rows; every operand is then used from registers.  The products of 16
+// rows pass through LDS so that whole rows are written out (16 bytes per lane,
+// 256 contiguous bytes per row at d_h = 128), the shared row added before the
+// single rounding.  Other d_h: a wave per 16 rows, one column block at a time.
 // fp32 (or shapes off the grid): one thread per output element.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
@@ -73,6 +79,99 @@ __global__ void __launch_bounds__(kWaves * 64) materialize_mfma_kernel(int H, in
     }
 }
 
+constexpr int kWaveRows = 64;  // rows of one head per wave in the d_h = 64 / 128 kernel
+
+template <int D, int NKS>
+__global__ void __launch_bounds__(kWaves * 64) materialize_rows_kernel(int H, int R, int L_cap, int max_len,
+                                                                       const int32_t* __restrict__ seq_lens,
+                                                                       const uint16_t* __restrict__ shared,
+                                                                       const uint16_t* __restrict__ z,
+                                                                       const uint16_t* __restrict__ basis,
+                                                                       uint16_t* __restrict__ out) {
+    constexpr int CB = D / 16;
+    constexpr int XS = D + 4;          // floats per staged row
+    constexpr int LPR = D / 8;         // lanes per row in the write-out (8 columns each)
+    constexpr int RPI = 64 / LPR;      // rows per write-out instruction
+    __shared__ __attribute__((aligned(16))) float xs_all[kWaves][16 * XS];
+    float* xs = xs_all[threadIdx.x >> 6];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int Lb = clamped_len(seq_lens, b, max_len);
+    const int t0 = (blockIdx.x * kWaves + wave) * kWaveRows;
+    if (t0 >= Lb) return;
+    const uint16_t* bh = basis + (size_t)h * D * R;
+    // every load first: coordinates past r read coordinate 0 and are zeroed; rows past L_b re-read row L_b - 1
+    // and are not stored
+    u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16 (columns of the key), coordinates 32 ks + 8 g4
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k = 32 * ks + 8 * g4;
+            bf[cb][ks] = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + (k < R ? k : 0));
+        }
+    u32x4_t zf[4][NKS];        // latents of rows t0 + 16 rg + n16
+    u32x4_t sh[4][16 / RPI];   // shared rows of the write-out: row t0 + 16 rg + RPI it + lane / LPR, 8 columns
+    const int wr = lane / LPR, wc = 8 * (lane % LPR);  // write-out: row within RPI rows, first column
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+        const size_t row = (size_t)min(t0 + 16 * rg + n16, Lb - 1);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int k = 32 * ks + 8 * g4;
+            zf[rg][ks] = *(const u32x4_t*)(z + (((size_t)b * L_cap + row) * H + h) * R + (k < R ? k : 0));
+        }
+#pragma unroll
+        for (int it = 0; it < 16 / RPI; ++it) {
+            const size_t srow = (size_t)min(t0 + 16 * rg + RPI * it + wr, Lb - 1);
+            sh[rg][it] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + srow) * D + wc);
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (32 * ks + 8 * g4 >= R) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) bf[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) zf[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    uint16_t* outh = out + ((size_t)b * H + h) * L_cap * D;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+        // the products of 16 rows: lane (row n16, g4) holds columns 16 cb + 4 g4 .. + 3, staged in LDS as fp32
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
+                                                              __builtin_bit_cast(bf16x8_t, zf[rg][ks]), acc, 0, 0, 0);
+            *(f32x4_t*)(xs + n16 * XS + 16 * cb + 4 * g4) = acc;
+        }
+        wave_lds_sync();
+        // write-out: RPI whole rows per instruction, 8 columns per lane, the shared row added before rounding
+#pragma unroll
+        for (int it = 0; it < 16 / RPI; ++it) {
+            const int rl = RPI * it + wr;
+            const f32x4_t a0 = *(const f32x4_t*)(xs + rl * XS + wc);
+            const f32x4_t a1 = *(const f32x4_t*)(xs + rl * XS + wc + 4);
+            const u32x4_t s = sh[rg][it];
+            u32x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = (i < 2 ? a0[2 * i] : a1[2 * i - 4]) + bf16_lo(s[i]);
+                const float hi = (i < 2 ? a0[2 * i + 1] : a1[2 * i - 3]) + bf16_hi(s[i]);
+                o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+            }
+            const int row = t0 + 16 * rg + rl;
+            if (row < Lb) *(u32x4_t*)(outh + (size_t)row * D + wc) = o;
+        }
+        wave_lds_sync();  // the staging area is rewritten by the next row group
+    }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) materialize_simple_kernel(int batch, int H, int D, int R, int L_cap,
                                                                  int max_len, const int32_t* __restrict__ seq_lens,
@@ -98,7 +197,13 @@ __global__ void __launch_bounds__(256) materialize_simple_kernel(int batch, int 
 hipError_t launch_one(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, const int32_t* seq_lens,
                       const void* shared, const void* z, const void* basis, void* out, hipStream_t stream) {
     if (max_len == 0) return hipSuccess;
-    if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
+    if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64) {
+        dim3 grid((max_len + kWaveRows * kWaves - 1) / (kWaveRows * kWaves), H, batch);
+        auto kern = (d_h == 64) ? (r <= 32 ? materialize_rows_kernel<64, 1> : materialize_rows_kernel<64, 2>)
+                                : (r <= 32 ? materialize_rows_kernel<128, 1> : materialize_rows_kernel<128, 2>);
+        hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, r, L_cap, max_len, seq_lens,
+                           (const uint16_t*)shared, (const uint16_t*)z, (const uint16_t*)basis, (uint16_t*)out);
+    } else if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
         dim3 grid((max_len + 16 * kWaves - 1) / (16 * kWaves), H, batch);
         auto kern = (r <= 32) ? materialize_mfma_kernel<1> : materialize_mfma_kernel<2>;
         hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, d_h, r, L_cap, max_len, seq_lens,

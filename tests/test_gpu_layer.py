@@ -214,6 +214,8 @@ MAT_CASES = [  # (dtype, batch, H, d_h, r, lengths)
     ("bf16", 2, 16, 128, 48, [129, 1]),
     ("f32", 2, 4, 16, 4, [40, 9]),
     ("bf16", 2, 8, 64, 0, [50, 3]),
+    ("bf16", 2, 8, 128, 32, [700, 257]),  # several 256-row workgroups, one row past a 64-row wave
+    ("bf16", 2, 8, 96, 16, [70, 33]),     # d_h off the 64 / 128 kernels: a wave per 16 rows
 ]
 
 
