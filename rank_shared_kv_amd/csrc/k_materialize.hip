@@ -10,7 +10,8 @@
 // (k-steps of 32 rank coordinates; coordinates past r enter as zeros).  In that
 // layout each lane holds four consecutive columns of one row, so the shared row
 // is added and the result stored 8 bytes at a time.  With d_h = 64 or 128 a wave
-// owns 64 rows of one head and issues all its loads first: the B_h fragments once
+// owns 64 rows of one head (the four waves of a workgroup: four heads of the same
+// rows, whose shared rows then come from L1) and issues all its loads first: the B_h fragments once
 // (16 KB at d_h = 128, r = 64, from L2), the latents of its 64 rows and their
 // shared rows; every operand is then used from registers.  The products of 16
 // rows pass through LDS so that whole rows are written out (16 bytes per lane,
@@ -81,13 +82,20 @@ __global__ void __launch_bounds__(kWaves * 64) materialize_mfma_kernel(int H, in
 
 constexpr int kWaveRows = 64;  // rows of one head per wave in the d_h = 64 / 128 kernel
 
+// the operands of one rebuilt matrix (keys or values)
+struct MatOperands {
+    const uint16_t* shared;  // [batch][L_cap][d_h]
+    const uint16_t* z;       // [batch][L_cap][H][r]
+    const uint16_t* basis;   // [H][d_h][r]
+    uint16_t* out;           // [batch][H][L_cap][d_h]
+};
+
+// keys and values in one launch: blockIdx.z = batch * (0 for keys, 1 for values) + b
 template <int D, int NKS>
-__global__ void __launch_bounds__(kWaves * 64) materialize_rows_kernel(int H, int R, int L_cap, int max_len,
+__global__ void __launch_bounds__(kWaves * 64) materialize_rows_kernel(int batch, int H, int R, int L_cap,
+                                                                       int max_len,
                                                                        const int32_t* __restrict__ seq_lens,
-                                                                       const uint16_t* __restrict__ shared,
-                                                                       const uint16_t* __restrict__ z,
-                                                                       const uint16_t* __restrict__ basis,
-                                                                       uint16_t* __restrict__ out) {
+                                                                       MatOperands kop, MatOperands vop) {
     constexpr int CB = D / 16;
     constexpr int XS = D + 4;          // floats per staged row
     constexpr int LPR = D / 8;         // lanes per row in the write-out (8 columns each)
@@ -96,10 +104,18 @@ __global__ void __launch_bounds__(kWaves * 64) materialize_rows_kernel(int H, in
     float* xs = xs_all[threadIdx.x >> 6];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int h = blockIdx.y, b = blockIdx.z;
+    // the workgroup's waves take heads 4 y .. 4 y + 3 of the same 64 rows, so the shared rows come from L1
+    const int h = blockIdx.y * kWaves + wave;
+    const bool is_v = (int)blockIdx.z >= batch;
+    const int b = (int)blockIdx.z - (is_v ? batch : 0);
+    const MatOperands op = is_v ? vop : kop;
+    const uint16_t* __restrict__ shared = op.shared;
+    const uint16_t* __restrict__ z = op.z;
+    const uint16_t* __restrict__ basis = op.basis;
+    uint16_t* __restrict__ out = op.out;
     const int Lb = clamped_len(seq_lens, b, max_len);
-    const int t0 = (blockIdx.x * kWaves + wave) * kWaveRows;
-    if (t0 >= Lb) return;
+    const int t0 = blockIdx.x * kWaveRows;
+    if (t0 >= Lb || h >= H) return;
     const uint16_t* bh = basis + (size_t)h * D * R;
     // every load first: coordinates past r read coordinate 0 and are zeroed; rows past L_b re-read row L_b - 1
     // and are not stored
@@ -197,13 +213,7 @@ __global__ void __launch_bounds__(256) materialize_simple_kernel(int batch, int 
 hipError_t launch_one(int batch, int H, int d_h, int r, int L_cap, int dtype, int max_len, const int32_t* seq_lens,
                       const void* shared, const void* z, const void* basis, void* out, hipStream_t stream) {
     if (max_len == 0) return hipSuccess;
-    if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64) {
-        dim3 grid((max_len + kWaveRows * kWaves - 1) / (kWaveRows * kWaves), H, batch);
-        auto kern = (d_h == 64) ? (r <= 32 ? materialize_rows_kernel<64, 1> : materialize_rows_kernel<64, 2>)
-                                : (r <= 32 ? materialize_rows_kernel<128, 1> : materialize_rows_kernel<128, 2>);
-        hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, r, L_cap, max_len, seq_lens,
-                           (const uint16_t*)shared, (const uint16_t*)z, (const uint16_t*)basis, (uint16_t*)out);
-    } else if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
+    if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
         dim3 grid((max_len + 16 * kWaves - 1) / (16 * kWaves), H, batch);
         auto kern = (r <= 32) ? materialize_mfma_kernel<1> : materialize_mfma_kernel<2>;
         hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, d_h, r, L_cap, max_len, seq_lens,
@@ -229,6 +239,16 @@ hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int d
                               const int32_t* seq_lens, const void* k_shared, const void* v_shared, const void* z_k,
                               const void* z_v, const void* B_k, const void* B_v, void* K_out, void* V_out,
                               hipStream_t stream) {
+    if (max_len > 0 && dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64 &&
+        2 * (long)batch <= 65535) {  // grid z: keys and values of every sequence
+        dim3 grid((max_len + kWaveRows - 1) / kWaveRows, (H + kWaves - 1) / kWaves, 2 * batch);
+        auto kern = (d_h == 64) ? (r <= 32 ? materialize_rows_kernel<64, 1> : materialize_rows_kernel<64, 2>)
+                                : (r <= 32 ? materialize_rows_kernel<128, 1> : materialize_rows_kernel<128, 2>);
+        const MatOperands kop{(const uint16_t*)k_shared, (const uint16_t*)z_k, (const uint16_t*)B_k, (uint16_t*)K_out};
+        const MatOperands vop{(const uint16_t*)v_shared, (const uint16_t*)z_v, (const uint16_t*)B_v, (uint16_t*)V_out};
+        hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, batch, H, r, L_cap, max_len, seq_lens, kop, vop);
+        return hipGetLastError();
+    }
     hipError_t e = launch_one(batch, H, d_h, r, L_cap, dtype, max_len, seq_lens, k_shared, z_k, B_k, K_out, stream);
     if (e != hipSuccess) return e;
     return launch_one(batch, H, d_h, r, L_cap, dtype, max_len, seq_lens, v_shared, z_v, B_v, V_out, stream);
