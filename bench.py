@@ -119,7 +119,8 @@ def cpu_baseline(w, lens, budget_s: float):
 def materialize_bench(args):
     """Time lrkv_materialize over the workload's whole live cache: per step, K_h and V_h of every live
     (row, head) are rebuilt and written.  Bytes: the factored rows read once plus both bases, and the
-    rebuilt rows written once."""
+    rebuilt rows written once.  With --key-scales, lrkv_key_scales over the whole history instead: the key
+    factors read once plus B^K, one scale per (row, head) written."""
     import numpy as np
     import torch
 
@@ -131,44 +132,58 @@ def materialize_bench(args):
     K, W = args.steps, args.warmup
     lens = synth.seq_lengths(w)
     L_cap, max_len = launch_config(w, 0, args.capacity)
-    log(f"bench: materialise, workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} "
+    what = "key scales" if args.key_scales else "materialise"
+    log(f"bench: {what}, workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} "
         f"L_max={int(lens.max())} steps={K} warmup={W}")
     dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens)
     dims = lk.make_dims(w.batch, w.H, w.d_h, w.r, L_cap, lk.LRKV_F32 if w.dtype == "f32" else lk.LRKV_BF16)
     cache = lk.make_cache(dev["k_shared"], dev["v_shared"], dev["z_k"] if w.r else None,
                           dev["z_v"] if w.r else None, dev["seq_lens"])
-    K_out = torch.empty((w.batch, w.H, L_cap, w.d_h), dtype=sdev.torch_dtype(w), device="cuda")
-    V_out = torch.empty_like(K_out)
     stream = torch.cuda.current_stream()
     bk, bv = (dev["B_k"], dev["B_v"]) if w.r else (None, None)
+    if args.key_scales:
+        rho = torch.empty((w.batch, L_cap, w.H), dtype=sdev.torch_dtype(w), device="cuda")
+        call = lambda: lk.lrkv_key_scales(dims, cache, max_len, max_len, bk, 1e-6, rho, stream)  # noqa: E731
+    else:
+        K_out = torch.empty((w.batch, w.H, L_cap, w.d_h), dtype=sdev.torch_dtype(w), device="cuda")
+        V_out = torch.empty_like(K_out)
+        call = lambda: lk.lrkv_materialize(dims, cache, max_len, bk, bv, K_out, V_out, stream)  # noqa: E731
     for _ in range(W):
-        lk.lrkv_materialize(dims, cache, max_len, bk, bv, K_out, V_out, stream)
+        call()
     torch.cuda.synchronize()
     evs = []
     for _ in range(K):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        lk.lrkv_materialize(dims, cache, max_len, bk, bv, K_out, V_out, stream)
+        call()
         b.record(stream)
         evs.append((a, b))
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(K_out[0, :, : int(lens[0])].float()).all())
+    check = rho[0, : int(lens[0])] if args.key_scales else K_out[0, :, : int(lens[0])]
+    assert bool(torch.isfinite(check.float()).all())
     us = 1e3 * sum(a.elapsed_time(b) for a, b in evs) / K
     rows = int(np.sum(lens, dtype=np.int64))
     s = w.elem_bytes
-    read_bytes = lk.lrkv_cache_bytes(dims, lens.tolist()) + 2 * w.H * w.d_h * w.r * s
-    write_bytes = 2 * rows * w.H * w.d_h * s
+    if args.key_scales:  # the key half of the cache, B^K, and the scales
+        read_bytes = lk.lrkv_cache_bytes(dims, lens.tolist()) // 2 + w.H * w.d_h * w.r * s
+        write_bytes = rows * w.H * s
+    else:
+        read_bytes = lk.lrkv_cache_bytes(dims, lens.tolist()) + 2 * w.H * w.d_h * w.r * s
+        write_bytes = 2 * rows * w.H * w.d_h * s
     gbps = (read_bytes + write_bytes) / (us * 1e-6) / 1e9
-    log(f"bench: materialise {us:.1f} us per call = {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of peak)")
+    log(f"bench: {what} {us:.1f} us per call = {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of peak)")
     rec = {
-        "metric": "LRKV materialised keys and values, rebuilt row-heads/s (the training / prefill form), 1 GPU",
+        "metric": ("LRKV key scales of the whole history (normalised variant), row-heads/s, 1 GPU" if args.key_scales
+                   else "LRKV materialised keys and values, rebuilt row-heads/s (the training / prefill form), "
+                        "1 GPU"),
         "value": rows * w.H / (us * 1e-6), "unit": "row·heads/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": w.name + "+materialise", "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
+        "config": {"workload": w.name + ("+key_scales" if args.key_scales else "+materialise"), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens.max()), "L_cap": L_cap},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "lrkv_materialize",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "lrkv_key_scales" if args.key_scales else "lrkv_materialize",
                      "algorithmic_bytes_per_launch": read_bytes + write_bytes, "read_bytes": read_bytes,
                      "write_bytes": write_bytes, "avg_launch_us": us,
                      "timing": f"HIP events around each of {K} launches"},
@@ -206,6 +221,9 @@ def main():
     ap.add_argument("--materialize", action="store_true",
                     help="materialised path: each step rebuilds K_h and V_h of every live row and head "
                          "(lrkv_materialize, the training / prefill form)")
+    ap.add_argument("--key-scales", action="store_true",
+                    help="normalised variant's whole-history pass: each step computes the key scale of every live "
+                         "row and head (lrkv_key_scales with n_last = the whole history, as after a prefill)")
     ap.add_argument("--no-stream-probe", action="store_true",
                     help="skip the streaming-read probe (the measured read bandwidth the split pass is compared with)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -226,11 +244,12 @@ def main():
               f"(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
-    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0, args.rope, args.materialize]) > 1:
-        print("bench.py: --queries, --layer, --norm, --paged, --rope and --materialize do not combine",
-              file=sys.stderr)
+    if sum([args.queries > 1, args.layer, args.norm, args.paged > 0, args.rope, args.materialize,
+            args.key_scales]) > 1:
+        print("bench.py: --queries, --layer, --norm, --paged, --rope, --materialize and --key-scales do not "
+              "combine", file=sys.stderr)
         sys.exit(2)
-    if args.materialize:
+    if args.materialize or args.key_scales:
         return materialize_bench(args)
 
     import numpy as np

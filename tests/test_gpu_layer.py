@@ -216,6 +216,7 @@ MAT_CASES = [  # (dtype, batch, H, d_h, r, lengths)
     ("bf16", 2, 8, 64, 0, [50, 3]),
     ("bf16", 2, 8, 128, 32, [700, 257]),  # several 256-row workgroups, one row past a 64-row wave
     ("bf16", 2, 8, 96, 16, [70, 33]),     # d_h off the 64 / 128 kernels: a wave per 16 rows
+    ("bf16", 2, 6, 64, 16, [100, 70]),    # heads not a multiple of a workgroup's four
 ]
 
 

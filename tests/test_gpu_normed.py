@@ -104,6 +104,8 @@ SCALE_CASES = [  # (dtype, batch, H, d_h, r, lengths): matrix-core path (bf16, d
     ("bf16", 2, 16, 128, 48, [65, 130]),
     ("bf16", 2, 8, 64, 0, [50, 9]),
     ("bf16", 2, 4, 48, 12, [40, 3]),
+    ("bf16", 2, 6, 64, 8, [100, 70]),     # heads not a multiple of a workgroup's four
+    ("bf16", 2, 8, 96, 16, [70, 33]),     # d_h off the 64 / 128 kernel: a wave per 16 rows
     ("f32", 2, 4, 16, 4, [64, 3]),
     ("f32", 2, 32, 128, 0, [70, 1]),
 ]
