@@ -15,10 +15,11 @@
 // kernel does), the shared row is added and the squares accumulated; the four
 // lanes that hold one row's columns then sum in a fixed order.  The keys
 // themselves are never written.  With d_h = 64 or 128 (key_scales_rows_kernel)
-// a wave owns 64 rows of one head, the four waves of a workgroup four heads of
-// the same rows, and a wave issues all its loads first (the B_h fragments once,
-// its rows' latents and shared rows); other d_h (key_scales_mfma_kernel) take a
-// wave per 16 rows.  Other shapes: one thread per (row, head).
+// the four waves of a workgroup take four heads of the same 256 rows, in chunks
+// of 64 whose shared rows the workgroup stages in LDS; each wave fetches its
+// B_h fragments once, and the next chunk's loads are in flight while a chunk
+// computes.  Other d_h (key_scales_mfma_kernel) take a wave per 16 rows.  Other
+// shapes: one thread per (row, head).
 #include <algorithm>
 
 #include "lrkv_device.hpp"
@@ -87,9 +88,13 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_mfma_kernel(int H, int
     if (g4 == 0 && row < Lb) rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
 }
 
-constexpr int kWaveRows = 64;  // rows of one head per wave in the d_h = 64 / 128 kernel
+constexpr int kChunkRows = 64;  // rows per chunk in the d_h = 64 / 128 kernel
+constexpr int kChunks = 4;      // chunks per workgroup: 256 rows, one B^K_h fetch per wave
 
-// rows max(0, L_b - n_last) .. L_b - 1 of sequence b; heads 4 y .. 4 y + 3 in the workgroup's waves
+// rows max(0, L_b - n_last) .. L_b - 1 of sequence b; heads 4 y .. 4 y + 3 in the workgroup's waves.  The
+// workgroup walks 4 chunks of 64 rows (past L_b: stand-ins, computed, not stored); each wave loads its
+// head's B^K_h fragments once.  The chunk's shared rows are staged in LDS by the whole workgroup (two
+// buffers: the next chunk's rows and latents load while the current chunk computes).
 template <int D, int NKS>
 __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int R, int L_cap, int max_len, int n_last,
                                                                       float eps, const int32_t* __restrict__ seq_lens,
@@ -98,17 +103,58 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
                                                                       const uint16_t* __restrict__ basis,
                                                                       uint16_t* __restrict__ rho) {
     constexpr int CB = D / 16;
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    constexpr int SROW = D + 8;                               // bf16 per staged shared row
+    constexpr int PPT = kChunkRows * (D / 8) / (kWaves * 64);  // 16-byte pieces of a chunk per thread
+    __shared__ __attribute__((aligned(16))) uint16_t sh_l[2][kChunkRows * SROW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.y * kWaves + wave, b = blockIdx.z;
+    const int hc = min(h, H - 1);  // waves past the last head compute a stand-in and store nothing
     const int Lb = clamped_len(seq_lens, b, max_len);
     const int start = max(0, Lb - n_last);
-    const int t0 = start + blockIdx.x * kWaveRows;
-    if (t0 >= Lb || h >= H) return;
-    const uint16_t* bh = basis + (size_t)h * D * R;
-    // every load first: coordinates past r read coordinate 0 and are zeroed; rows past L_b re-read row L_b - 1
-    // and are not stored
-    u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16, coordinates 32 ks + 8 g4
+    const int r0 = start + blockIdx.x * kChunkRows * kChunks;
+    if (r0 >= Lb) return;  // the whole workgroup
+    const uint16_t* bh = basis + (size_t)hc * D * R;
+    typedef u32x4_t ZFrag[4][NKS];
+    auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + 16 rg + n16 (past L_b: row L_b - 1)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const size_t row = (size_t)min(r0 + kChunkRows * c + 16 * rg + n16, Lb - 1);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int k = 32 * ks + 8 * g4;
+                zf[rg][ks] = *(const u32x4_t*)(z + (((size_t)b * L_cap + row) * H + hc) * R + (k < R ? k : 0));
+            }
+        }
+    };
+    auto load_sh = [&](u32x4_t (&v)[PPT], int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + kWaves * 64 * i;
+            const size_t row = (size_t)min(r0 + kChunkRows * c + p / (D / 8), Lb - 1);
+            v[i] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + row) * D + 8 * (p % (D / 8)));
+        }
+    };
+    auto store_sh = [&](const u32x4_t (&v)[PPT], int buf) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + kWaves * 64 * i;
+            *(u32x4_t*)(sh_l[buf] + (p / (D / 8)) * SROW + 8 * (p % (D / 8))) = v[i];
+        }
+    };
+    auto zero_past_r = [&](ZFrag& zf) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            if (32 * ks + 8 * g4 >= R) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) zf[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+    };
+    u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16, coordinates 32 ks + 8 g4 (past r: zero)
+    u32x4_t sv[PPT];
+    ZFrag za, zb;
+    load_sh(sv, 0);
+    load_z(za, 0);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -116,53 +162,53 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
             const int k = 32 * ks + 8 * g4;
             bf[cb][ks] = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + (k < R ? k : 0));
         }
-    u32x4_t zf[4][NKS];  // latents of rows t0 + 16 rg + n16
-    u32x2_t sh[4][CB];   // their shared rows, columns 16 cb + 4 g4 .. + 3 (from L1 after the first head's wave)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        const size_t row = (size_t)min(t0 + 16 * rg + n16, Lb - 1);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int k = 32 * ks + 8 * g4;
-            zf[rg][ks] = *(const u32x4_t*)(z + (((size_t)b * L_cap + row) * H + h) * R + (k < R ? k : 0));
-        }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-            sh[rg][cb] = *(const u32x2_t*)(shared + ((size_t)b * L_cap + row) * D + 16 * cb + 4 * g4);
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks)
         if (32 * ks + 8 * g4 >= R) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) bf[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) zf[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
         }
-    }
+    store_sh(sv, 0);
+    __syncthreads();
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        float ss = 0.f;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
-                                                              __builtin_bit_cast(bf16x8_t, zf[rg][ks]), acc, 0, 0, 0);
-            // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row's key
-            const u32x2_t s = sh[rg][cb];
-            const float v0 = acc[0] + bf16_lo(s[0]), v1 = acc[1] + bf16_hi(s[0]);
-            const float v2 = acc[2] + bf16_lo(s[1]), v3 = acc[3] + bf16_hi(s[1]);
-            ss = fmaf(v0, v0, ss);
-            ss = fmaf(v1, v1, ss);
-            ss = fmaf(v2, v2, ss);
-            ss = fmaf(v3, v3, ss);
+    for (int c = 0; c < kChunks; ++c) {
+        ZFrag& zc = (c & 1) ? zb : za;
+        ZFrag& zn = (c & 1) ? za : zb;
+        if (c + 1 < kChunks) {  // the next chunk's loads first
+            load_sh(sv, c + 1);
+            load_z(zn, c + 1);
         }
-        ss += __shfl_xor(ss, 16);  // the four column groups of a row: (g4 0 + 1) + (2 + 3)
-        ss += __shfl_xor(ss, 32);
-        const int row = t0 + 16 * rg + n16;
-        if (g4 == 0 && row < Lb)
-            rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
+        zero_past_r(zc);
+        const uint16_t* shc = sh_l[c & 1];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            float ss = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
+                                                                  __builtin_bit_cast(bf16x8_t, zc[rg][ks]), acc, 0, 0, 0);
+                // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row's key
+                const u32x2_t s = *(const u32x2_t*)(shc + (16 * rg + n16) * SROW + 16 * cb + 4 * g4);
+                const float v0 = acc[0] + bf16_lo(s[0]), v1 = acc[1] + bf16_hi(s[0]);
+                const float v2 = acc[2] + bf16_lo(s[1]), v3 = acc[3] + bf16_hi(s[1]);
+                ss = fmaf(v0, v0, ss);
+                ss = fmaf(v1, v1, ss);
+                ss = fmaf(v2, v2, ss);
+                ss = fmaf(v3, v3, ss);
+            }
+            ss += __shfl_xor(ss, 16);  // the four column groups of a row: (g4 0 + 1) + (2 + 3)
+            ss += __shfl_xor(ss, 32);
+            const int row = r0 + kChunkRows * c + 16 * rg + n16;
+            if (g4 == 0 && h < H && row < Lb)
+                rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
+        }
+        if (c + 1 < kChunks) {
+            store_sh(sv, (c + 1) & 1);  // that buffer's chunk finished before the previous barrier
+            __syncthreads();
+        }
     }
 }
 
@@ -224,7 +270,7 @@ hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dt
     const int n_rows = std::min(n_last, max_len);
     if (n_rows <= 0) return hipSuccess;
     if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64) {
-        dim3 grid((n_rows + kWaveRows - 1) / kWaveRows, (H + kWaves - 1) / kWaves, batch);
+        dim3 grid((n_rows + kChunkRows * kChunks - 1) / (kChunkRows * kChunks), (H + kWaves - 1) / kWaves, batch);
         auto kern = (d_h == 64) ? (r <= 32 ? key_scales_rows_kernel<64, 1> : key_scales_rows_kernel<64, 2>)
                                 : (r <= 32 ? key_scales_rows_kernel<128, 1> : key_scales_rows_kernel<128, 2>);
         hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, r, L_cap, max_len, n_last, eps, seq_lens,
