@@ -9,13 +9,13 @@
 // Out^T[16 cols x 16 rows] = B_h[16 x r] Z^T[r x 16] on v_mfma_f32_16x16x32_bf16
 // (k-steps of 32 rank coordinates; coordinates past r enter as zeros).  In that
 // layout each lane holds four consecutive columns of one row, so the shared row
-// is added and the result stored 8 bytes at a time.  With d_h = 64 or 128 a wave
-// owns 64 rows of one head (the four waves of a workgroup: four heads of the same
-// rows, whose shared rows then come from L1) and issues all its loads first: the B_h fragments once
-// (16 KB at d_h = 128, r = 64, from L2), the latents of its 64 rows and their
-// shared rows; every operand is then used from registers.  The products of 16
-// rows pass through LDS so that whole rows are written out (16 bytes per lane,
-// 256 contiguous bytes per row at d_h = 128), the shared row added before the
+// is added and the result stored 8 bytes at a time.  With d_h = 64 or 128 the
+// four waves of a workgroup take four heads of the same 256 rows, in chunks of
+// 64 rows whose shared rows the workgroup stages in LDS; each wave fetches its
+// B_h fragments (16 KB at d_h = 128, r = 64, from L2) once, the next chunk's
+// loads are in flight while a chunk computes, and the products of 16 rows pass
+// through LDS so that whole rows are written out (16 bytes per lane, 256
+// contiguous bytes per row at d_h = 128), the shared row added before the
 // single rounding.  Other d_h: a wave per 16 rows, one column block at a time.
 // fp32 (or shapes off the grid): one thread per output element.
 #include "lrkv_device.hpp"
@@ -80,8 +80,6 @@ __global__ void __launch_bounds__(kWaves * 64) materialize_mfma_kernel(int H, in
     }
 }
 
-constexpr int kWaveRows = 64;  // rows of one head per wave in the d_h = 64 / 128 kernel
-
 // the operands of one rebuilt matrix (keys or values)
 struct MatOperands {
     const uint16_t* shared;  // [batch][L_cap][d_h]
@@ -90,36 +88,75 @@ struct MatOperands {
     uint16_t* out;           // [batch][H][L_cap][d_h]
 };
 
-// keys and values in one launch: blockIdx.z = batch * (0 for keys, 1 for values) + b
+constexpr int kChunkRows = 64;  // rows per chunk in the d_h = 64 / 128 kernel
+constexpr int kChunks = 4;      // chunks per workgroup: 256 rows, one B_h fetch per wave
+
+// Keys and values in one launch: blockIdx.z = batch * (0 for keys, 1 for values) + b.  The workgroup's
+// waves take heads 4 y .. 4 y + 3 of the same 256 rows, in 4 chunks of 64 (rows past L_b: stand-ins,
+// computed, not stored).  Each wave loads its head's B_h fragments once.  The chunk's shared rows are staged
+// in LDS by the whole workgroup (two buffers: the next chunk's rows and latents load while the current chunk
+// computes), and the products of 16 rows pass through a per-wave LDS tile so that whole rows are written.
 template <int D, int NKS>
 __global__ void __launch_bounds__(kWaves * 64) materialize_rows_kernel(int batch, int H, int R, int L_cap,
                                                                        int max_len,
                                                                        const int32_t* __restrict__ seq_lens,
                                                                        MatOperands kop, MatOperands vop) {
     constexpr int CB = D / 16;
-    constexpr int XS = D + 4;          // floats per staged row
-    constexpr int LPR = D / 8;         // lanes per row in the write-out (8 columns each)
-    constexpr int RPI = 64 / LPR;      // rows per write-out instruction
+    constexpr int SROW = D + 8;                               // bf16 per staged shared row
+    constexpr int PPT = kChunkRows * (D / 8) / (kWaves * 64);  // 16-byte pieces of a chunk per thread
+    constexpr int XS = D + 4;                                 // floats per staged product row
+    constexpr int LPR = D / 8;                                // lanes per row in the write-out (8 columns each)
+    constexpr int RPI = 64 / LPR;                             // rows per write-out instruction
+    __shared__ __attribute__((aligned(16))) uint16_t sh_l[2][kChunkRows * SROW];
     __shared__ __attribute__((aligned(16))) float xs_all[kWaves][16 * XS];
-    float* xs = xs_all[threadIdx.x >> 6];
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float* xs = xs_all[wave];
     const int n16 = lane & 15, g4 = lane >> 4;
-    // the workgroup's waves take heads 4 y .. 4 y + 3 of the same 64 rows, so the shared rows come from L1
     const int h = blockIdx.y * kWaves + wave;
+    const int hc = min(h, H - 1);  // waves past the last head compute a stand-in and store nothing
     const bool is_v = (int)blockIdx.z >= batch;
     const int b = (int)blockIdx.z - (is_v ? batch : 0);
     const MatOperands op = is_v ? vop : kop;
     const uint16_t* __restrict__ shared = op.shared;
     const uint16_t* __restrict__ z = op.z;
     const uint16_t* __restrict__ basis = op.basis;
-    uint16_t* __restrict__ out = op.out;
     const int Lb = clamped_len(seq_lens, b, max_len);
-    const int t0 = blockIdx.x * kWaveRows;
-    if (t0 >= Lb || h >= H) return;
-    const uint16_t* bh = basis + (size_t)h * D * R;
-    // every load first: coordinates past r read coordinate 0 and are zeroed; rows past L_b re-read row L_b - 1
-    // and are not stored
-    u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16 (columns of the key), coordinates 32 ks + 8 g4
+    const int r0 = blockIdx.x * kChunkRows * kChunks;
+    if (r0 >= Lb) return;  // the whole workgroup
+    uint16_t* outh = op.out + ((size_t)b * H + hc) * L_cap * D;
+    const uint16_t* bh = basis + (size_t)hc * D * R;
+    typedef u32x4_t ZFrag[4][NKS];
+    auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + 16 rg + n16 (past L_b: row L_b - 1)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const size_t row = (size_t)min(r0 + kChunkRows * c + 16 * rg + n16, Lb - 1);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int k = 32 * ks + 8 * g4;
+                zf[rg][ks] = *(const u32x4_t*)(z + (((size_t)b * L_cap + row) * H + hc) * R + (k < R ? k : 0));
+            }
+        }
+    };
+    auto load_sh = [&](u32x4_t (&v)[PPT], int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + kWaves * 64 * i;
+            const size_t row = (size_t)min(r0 + kChunkRows * c + p / (D / 8), Lb - 1);
+            v[i] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + row) * D + 8 * (p % (D / 8)));
+        }
+    };
+    auto store_sh = [&](const u32x4_t (&v)[PPT], int buf) {
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int p = tid + kWaves * 64 * i;
+            *(u32x4_t*)(sh_l[buf] + (p / (D / 8)) * SROW + 8 * (p % (D / 8))) = v[i];
+        }
+    };
+    u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16 (columns of the key), coordinates 32 ks + 8 g4 (past r: zero)
+    u32x4_t sv[PPT];
+    ZFrag za, zb;
+    load_sh(sv, 0);
+    load_z(za, 0);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -127,64 +164,66 @@ __global__ void __launch_bounds__(kWaves * 64) materialize_rows_kernel(int batch
             const int k = 32 * ks + 8 * g4;
             bf[cb][ks] = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + (k < R ? k : 0));
         }
-    u32x4_t zf[4][NKS];        // latents of rows t0 + 16 rg + n16
-    u32x4_t sh[4][16 / RPI];   // shared rows of the write-out: row t0 + 16 rg + RPI it + lane / LPR, 8 columns
-    const int wr = lane / LPR, wc = 8 * (lane % LPR);  // write-out: row within RPI rows, first column
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        const size_t row = (size_t)min(t0 + 16 * rg + n16, Lb - 1);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int k = 32 * ks + 8 * g4;
-            zf[rg][ks] = *(const u32x4_t*)(z + (((size_t)b * L_cap + row) * H + h) * R + (k < R ? k : 0));
-        }
-#pragma unroll
-        for (int it = 0; it < 16 / RPI; ++it) {
-            const size_t srow = (size_t)min(t0 + 16 * rg + RPI * it + wr, Lb - 1);
-            sh[rg][it] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + srow) * D + wc);
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks)
         if (32 * ks + 8 * g4 >= R) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) bf[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) zf[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
         }
-    }
-    uint16_t* outh = out + ((size_t)b * H + h) * L_cap * D;
+    store_sh(sv, 0);
+    __syncthreads();
+    const int wr = lane / LPR, wc = 8 * (lane % LPR);  // write-out: row within RPI rows, first column
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-        // the products of 16 rows: lane (row n16, g4) holds columns 16 cb + 4 g4 .. + 3, staged in LDS as fp32
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
-                                                              __builtin_bit_cast(bf16x8_t, zf[rg][ks]), acc, 0, 0, 0);
-            *(f32x4_t*)(xs + n16 * XS + 16 * cb + 4 * g4) = acc;
+    for (int c = 0; c < kChunks; ++c) {
+        ZFrag& zc = (c & 1) ? zb : za;
+        ZFrag& zn = (c & 1) ? za : zb;
+        if (c + 1 < kChunks) {  // the next chunk's loads first
+            load_sh(sv, c + 1);
+            load_z(zn, c + 1);
         }
-        wave_lds_sync();
-        // write-out: RPI whole rows per instruction, 8 columns per lane, the shared row added before rounding
 #pragma unroll
-        for (int it = 0; it < 16 / RPI; ++it) {
-            const int rl = RPI * it + wr;
-            const f32x4_t a0 = *(const f32x4_t*)(xs + rl * XS + wc);
-            const f32x4_t a1 = *(const f32x4_t*)(xs + rl * XS + wc + 4);
-            const u32x4_t s = sh[rg][it];
-            u32x4_t o;
+        for (int ks = 0; ks < NKS; ++ks)
+            if (32 * ks + 8 * g4 >= R) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = (i < 2 ? a0[2 * i] : a1[2 * i - 4]) + bf16_lo(s[i]);
-                const float hi = (i < 2 ? a0[2 * i + 1] : a1[2 * i - 3]) + bf16_hi(s[i]);
-                o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+                for (int rg = 0; rg < 4; ++rg) zc[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
             }
-            const int row = t0 + 16 * rg + rl;
-            if (row < Lb) *(u32x4_t*)(outh + (size_t)row * D + wc) = o;
+        const uint16_t* shc = sh_l[c & 1];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            // the products of 16 rows: lane (row n16, g4) holds columns 16 cb + 4 g4 .. + 3, staged as fp32
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
+                                                                  __builtin_bit_cast(bf16x8_t, zc[rg][ks]), acc, 0, 0, 0);
+                *(f32x4_t*)(xs + n16 * XS + 16 * cb + 4 * g4) = acc;
+            }
+            wave_lds_sync();
+            // write-out: RPI whole rows per instruction, 8 columns per lane, the shared row added before rounding
+#pragma unroll
+            for (int it = 0; it < 16 / RPI; ++it) {
+                const int rl = RPI * it + wr;  // row within the 16
+                const f32x4_t a0 = *(const f32x4_t*)(xs + rl * XS + wc);
+                const f32x4_t a1 = *(const f32x4_t*)(xs + rl * XS + wc + 4);
+                const u32x4_t sr = *(const u32x4_t*)(shc + (16 * rg + rl) * SROW + wc);
+                u32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = (i < 2 ? a0[2 * i] : a1[2 * i - 4]) + bf16_lo(sr[i]);
+                    const float hi = (i < 2 ? a0[2 * i + 1] : a1[2 * i - 3]) + bf16_hi(sr[i]);
+                    o[i] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+                }
+                const int row = r0 + kChunkRows * c + 16 * rg + rl;
+                if (h < H && row < Lb) *(u32x4_t*)(outh + (size_t)row * D + wc) = o;
+            }
+            wave_lds_sync();  // the product tile is rewritten by the next row group
         }
-        wave_lds_sync();  // the staging area is rewritten by the next row group
+        if (c + 1 < kChunks) {
+            store_sh(sv, (c + 1) & 1);  // that buffer's chunk finished before the previous barrier
+            __syncthreads();
+        }
     }
 }
 
@@ -241,7 +280,8 @@ hipError_t launch_materialize(int batch, int H, int d_h, int r, int L_cap, int d
                               hipStream_t stream) {
     if (max_len > 0 && dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64 &&
         2 * (long)batch <= 65535) {  // grid z: keys and values of every sequence
-        dim3 grid((max_len + kWaveRows - 1) / kWaveRows, (H + kWaves - 1) / kWaves, 2 * batch);
+        dim3 grid((max_len + kChunkRows * kChunks - 1) / (kChunkRows * kChunks), (H + kWaves - 1) / kWaves,
+                  2 * batch);
         auto kern = (d_h == 64) ? (r <= 32 ? materialize_rows_kernel<64, 1> : materialize_rows_kernel<64, 2>)
                                 : (r <= 32 ? materialize_rows_kernel<128, 1> : materialize_rows_kernel<128, 2>);
         const MatOperands kop{(const uint16_t*)k_shared, (const uint16_t*)z_k, (const uint16_t*)B_k, (uint16_t*)K_out};
