@@ -362,8 +362,8 @@ lrkv_status lrkv_output_project(const lrkv_dims* dims, int32_t d_model, const fl
                                 void* stream);
 
 /* Measurement helper, not part of the method: read every byte of src once
- * with 16-byte loads (the streaming-read bandwidth the decode is compared
- * with) and write one XOR checksum per workgroup to sink.
+ * with 16-byte non-temporal loads (the streaming-read bandwidth the decode is
+ * compared with) and write one XOR checksum per workgroup to sink.
  *   src   device, 16-byte aligned; bytes a positive multiple of 16
  *   sink  device uint32 [1024] */
 lrkv_status lrkv_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);

@@ -81,21 +81,26 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
 constexpr int kRows = 32;   // rows per block
 constexpr int kWaves = 4;   // waves per workgroup
-// cache-policy bits of the streamed loads: 2 = non-temporal.  Latent rows are read exactly once;
-// shared key/value rows are re-read through L2 (split key lines, second head group).
-// waves of a workgroup advance block by block together (one barrier per block) in single-token decode: the
+// Cache-policy bits of the streamed loads: 2 = non-temporal.  With one query token per workgroup (QW = 1)
+// every latent row is read exactly once, and marking those loads non-temporal raises the stream rate (long
+// context: split pass 177 us against 195 us; a plain streaming read of 1 GiB goes from 6.3 to 7.0 TB/s the
+// same way).  With several query tokens per workgroup the sets of one sequence re-read the same rows
+// through L2, so those instances keep ordinary loads.  Shared key/value rows are re-read through L2 (split
+// key lines, second head group) and keep ordinary loads.
+// Waves of a workgroup advance block by block together (one barrier per block) in single-token decode: the
 // second head-group wave's shared-row loads then hit more often in L2 (long context: HBM read 1.176 GB per
 // launch instead of 1.188 GB, split pass 1.3% faster)
 #ifndef LRKV_LOCKSTEP
 #define LRKV_LOCKSTEP 1
 #endif
 #ifndef LRKV_NT_LATENT
-#define LRKV_NT_LATENT 0
+#define LRKV_NT_LATENT 1
 #endif
 #ifndef LRKV_NT_SHARED
 #define LRKV_NT_SHARED 0
 #endif
-constexpr int kNTLat = LRKV_NT_LATENT ? 2 : 0;
+template <int QW>
+constexpr int kNTLat = (LRKV_NT_LATENT && QW == 1) ? 2 : 0;
 constexpr int kNTSh = LRKV_NT_SHARED ? 2 : 0;
 
 template <int D, int R, int H, int OCC, int QW = 1>
@@ -359,24 +364,24 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 // one instruction reads row 8*sub + k of 8 consecutive heads: 8*r*2 contiguous bytes
                 const uint32_t vo = vo_zv + (k + 8 * sub) * row_bytes_lat;
                 if constexpr (EPL == 8) {
-                    const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat);
+                    const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat<QW>);
                     ring[slot][4 * k] = w.x;
                     ring[slot][4 * k + 1] = w.y;
                     ring[slot][4 * k + 2] = w.z;
                     ring[slot][4 * k + 3] = w.w;
                 } else if constexpr (EPL == 6) {
-                    const v3u_t w = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, kNTLat);
+                    const v3u_t w = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, kNTLat<QW>);
                     ring[slot][3 * k] = w.x;
                     ring[slot][3 * k + 1] = w.y;
                     ring[slot][3 * k + 2] = w.z;
                 } else if constexpr (EPL == 4) {
-                    const v2u_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNTLat);
+                    const v2u_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNTLat<QW>);
                     ring[slot][2 * k] = w.x;
                     ring[slot][2 * k + 1] = w.y;
                 } else if constexpr (EPL == 2) {
-                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, kNTLat);
+                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, kNTLat<QW>);
                 } else {  // EPL == 1
-                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, kNTLat);
+                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, kNTLat<QW>);
                 }
             }
         }

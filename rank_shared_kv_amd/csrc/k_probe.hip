@@ -1,10 +1,10 @@
 // Streaming-read probe: the measured read bandwidth that the decode's achieved
 // bandwidth is also compared with (besides the published HBM peak).  Every
-// 16-byte chunk of a buffer is read once: each workgroup sweeps a contiguous
-// slice, 16 loads in flight per lane (the best of 4, 8 and 16 measured);
-// each workgroup folds what it read into one
-// XOR checksum so the loads cannot be dropped.  Not part of the attention
-// method.
+// 16-byte chunk of a buffer is read once with non-temporal loads: each
+// workgroup sweeps a contiguous slice, 16 loads in flight per lane (the best of
+// 4, 8 and 16 measured; non-temporal loads read 7.0 TB/s where ordinary ones
+// read 6.3); each workgroup folds what it read into one XOR checksum so the
+// loads cannot be dropped.  Not part of the attention method.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
 
@@ -26,12 +26,12 @@ __global__ void __launch_bounds__(kProbeThreads) read_probe_kernel(const u32x4_t
     for (; i + (kProbeUnroll - 1) * kProbeThreads < end; i += kProbeUnroll * kProbeThreads) {
         u32x4_t v[kProbeUnroll];
 #pragma unroll
-        for (int u = 0; u < kProbeUnroll; ++u) v[u] = p[i + u * kProbeThreads];
+        for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kProbeThreads);
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     for (; i < end; i += kProbeThreads) {
-        const u32x4_t v = p[i];
+        const u32x4_t v = __builtin_nontemporal_load(p + i);
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
 #pragma unroll
