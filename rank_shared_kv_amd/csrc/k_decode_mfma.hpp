@@ -81,12 +81,13 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
 constexpr int kRows = 32;   // rows per block
 constexpr int kWaves = 4;   // waves per workgroup
-// Cache-policy bits of the streamed loads: 2 = non-temporal.  With one query token per workgroup (QW = 1)
-// every latent row is read exactly once, and marking those loads non-temporal raises the stream rate (long
-// context: split pass 177 us against 195 us; a plain streaming read of 1 GiB goes from 6.3 to 7.0 TB/s the
-// same way).  With several query tokens per workgroup the sets of one sequence re-read the same rows
-// through L2, so those instances keep ordinary loads.  Shared key/value rows are re-read through L2 (split
-// key lines, second head group) and keep ordinary loads.
+// Cache-policy bits of the streamed loads: 2 = non-temporal.  When a launch reads every latent row once
+// (one query set per cached sequence: single-token decode, or multi-token decode with Q <= qw), marking
+// those loads non-temporal raises the stream rate (long context: split pass 177 us against 195 us; a plain
+// streaming read of 1 GiB goes from 6.3 to 7.0 TB/s the same way).  With several query sets per sequence
+// the sets re-read the same rows through L2, so those launches keep ordinary loads (the NTL template flag
+// of the kernel, chosen per launch).  Shared key/value rows are re-read through L2 (split key lines,
+// second head group) and keep ordinary loads.
 // Waves of a workgroup advance block by block together (one barrier per block) in single-token decode: the
 // second head-group wave's shared-row loads then hit more often in L2 (long context: HBM read 1.176 GB per
 // launch instead of 1.188 GB, split pass 1.3% faster)
@@ -99,8 +100,8 @@ constexpr int kWaves = 4;   // waves per workgroup
 #ifndef LRKV_NT_SHARED
 #define LRKV_NT_SHARED 0
 #endif
-template <int QW>
-constexpr int kNTLat = (LRKV_NT_LATENT && QW == 1) ? 2 : 0;
+template <bool NTL>
+constexpr int kNTLat = (LRKV_NT_LATENT && NTL) ? 2 : 0;
 constexpr int kNTSh = LRKV_NT_SHARED ? 2 : 0;
 
 template <int D, int R, int H, int OCC, int QW = 1>
@@ -188,7 +189,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int D, int R, int H, int OCC, bool NORM, int QW>
+template <int D, int R, int H, int OCC, bool NORM, int QW, bool NTL>
 __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs a) {
     using C = Cfg<D, R, H, OCC, QW>;
     static_assert(!(NORM && QW > 1), "the normalised variant serves one query per sequence");
@@ -364,24 +365,24 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 // one instruction reads row 8*sub + k of 8 consecutive heads: 8*r*2 contiguous bytes
                 const uint32_t vo = vo_zv + (k + 8 * sub) * row_bytes_lat;
                 if constexpr (EPL == 8) {
-                    const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat<QW>);
+                    const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat<NTL>);
                     ring[slot][4 * k] = w.x;
                     ring[slot][4 * k + 1] = w.y;
                     ring[slot][4 * k + 2] = w.z;
                     ring[slot][4 * k + 3] = w.w;
                 } else if constexpr (EPL == 6) {
-                    const v3u_t w = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, kNTLat<QW>);
+                    const v3u_t w = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, kNTLat<NTL>);
                     ring[slot][3 * k] = w.x;
                     ring[slot][3 * k + 1] = w.y;
                     ring[slot][3 * k + 2] = w.z;
                 } else if constexpr (EPL == 4) {
-                    const v2u_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNTLat<QW>);
+                    const v2u_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNTLat<NTL>);
                     ring[slot][2 * k] = w.x;
                     ring[slot][2 * k + 1] = w.y;
                 } else if constexpr (EPL == 2) {
-                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, kNTLat<QW>);
+                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, kNTLat<NTL>);
                 } else {  // EPL == 1
-                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, kNTLat<QW>);
+                    ring[slot][k] = __builtin_amdgcn_raw_buffer_load_b16(rs, vo, so, kNTLat<NTL>);
                 }
             }
         }
@@ -715,10 +716,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     }
 }
 
-template <int D, int R, int H, int OCC, bool NORM, int QW>
+template <int D, int R, int H, int OCC, bool NORM, int QW, bool NTL = true>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     using C = Cfg<D, R, H, OCC, QW>;
-    auto kern = split_mfma_kernel<D, R, H, OCC, NORM, QW>;
+    auto kern = split_mfma_kernel<D, R, H, OCC, NORM, QW, NTL>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
@@ -736,7 +737,10 @@ constexpr bool query_width_fits(int qw) {
 template <int D, int R, int H, bool NORM, int QW>
 hipError_t launch_dhr(const DecodeArgs& a, int occ, hipStream_t stream) {
     if constexpr (!query_width_fits<D, R, H>(QW)) return hipErrorInvalidValue;
-    else if constexpr (NORM || QW > 1) return launch_one<D, R, H, 1, NORM, QW>(a, stream);
+    else if constexpr (QW > 1)  // non-temporal latent loads only with one query set per cached sequence
+        return a.qgroup == 1 ? launch_one<D, R, H, 1, false, QW, true>(a, stream)
+                             : launch_one<D, R, H, 1, false, QW, false>(a, stream);
+    else if constexpr (NORM) return launch_one<D, R, H, 1, NORM, 1>(a, stream);
     else return occ == 1 ? launch_one<D, R, H, 1, false, 1>(a, stream) : launch_one<D, R, H, 2, false, 1>(a, stream);
 }
 
