@@ -153,6 +153,26 @@ def factored_decode(dtype: str, q, k_shared, v_shared, z_k, z_v, B_k, B_v, seq_l
     return out
 
 
+def _widen(dtype: str, a) -> np.ndarray:
+    a = np.asarray(a)
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def absorb_query(dtype: str, q, B_k) -> np.ndarray:
+    """The projected query p[b][h][i] = sum_c q[b][h][c] B_k[h][c][i] in fp64 from the exactly widened stored
+    inputs ("Low-Rank Key Value Attention: Chinese reading notes", sec. 2.4 Eq. (6): the key basis moves onto
+    the query; "Low-Rank Key Value Attention | What a shared cache can preserve", sec. 3, one small product
+    per head per step).  q [batch][H][d_h], B_k [H][d_h][r]; returns [batch][H][r] fp64."""
+    qf, bf = _widen(dtype, q), _widen(dtype, B_k)
+    B, H, d_h = qf.shape
+    p = np.zeros((B, H, bf.shape[-1]))
+    for h in range(H):
+        p[:, h] = qf[:, h] @ bf[h]
+    return p
+
+
 def relative_error(got: np.ndarray, ref: np.ndarray) -> float:
     """max over rows of ||got - ref||_inf / ||ref||_inf (rows are (sequence, head) outputs)."""
     got = np.asarray(got, dtype=np.float64).reshape(ref.shape)

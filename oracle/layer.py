@@ -124,11 +124,12 @@ def layer_step(dtype: str, x, W_in, W_o, B_k, B_v, cache: Dict[str, np.ndarray],
     return {"y": y, "o": o, "lens": lens, **stored}
 
 
-def materialize(dtype: str, k_shared, v_shared, z_k, z_v, B_k, B_v, seq_lens):
+def materialize(dtype: str, k_shared, v_shared, z_k, z_v, B_k, B_v, seq_lens, rounded: bool = True):
     """Per-head keys and values of every live row, rebuilt from the factored cache and stored in dtype:
     K_h = K_S + Z^K_h (B^K_h)^T, V_h = V_S + Z^V_h (B^V_h)^T (reading notes sec. 2.1 Eqs. (2)-(5); review
     sec. 3, the materialised path used for training and prefill).  Inputs in the per-head layout; returns
-    (K, V) as [batch][H][L_cap][d_h] in dtype, rows at or past seq_lens[b] zero."""
+    (K, V) as [batch][H][L_cap][d_h] in dtype, rows at or past seq_lens[b] zero.  rounded=False returns the
+    exact fp64 values before the one rounding to dtype."""
     ks, vs = widen(dtype, k_shared), widen(dtype, v_shared)
     zk, zv = widen(dtype, z_k), widen(dtype, z_v)
     bk, bv = widen(dtype, B_k), widen(dtype, B_v)
@@ -141,4 +142,6 @@ def materialize(dtype: str, k_shared, v_shared, z_k, z_v, B_k, B_v, seq_lens):
         for h in range(H):
             K[b, h, :n] = ks[b, :n] + zk[b, h, :n] @ bk[h].T
             V[b, h, :n] = vs[b, :n] + zv[b, h, :n] @ bv[h].T
+    if not rounded:
+        return K, V
     return round_to(dtype, K), round_to(dtype, V)

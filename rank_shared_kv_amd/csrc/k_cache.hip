@@ -196,11 +196,19 @@ __global__ void __launch_bounds__(256) append_absorb_kernel(int batch, int H, in
 
 }  // namespace
 
+// The vector path needs 16-byte rows of B^K (r a multiple of 16 / element bytes), a q row that fits its LDS
+// stage (d_h <= 256) and at least one row group: each of its threads owns one 16-byte vector of a row, so
+// r / (16 / element bytes) must not exceed the workgroup width (r <= 2048 for bf16, 1024 for fp32).  Other
+// shapes take the scalar kernel.
+static bool absorb_vec_ok(int d_h, int r, int dtype) {
+    const int ve = dtype == 0 ? 4 : 8;
+    return r > 0 && (r % ve) == 0 && r / ve <= kAbsorbThreads && d_h <= 256;
+}
+
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
                          hipStream_t stream) {
     dim3 grid(batch * H), block(kAbsorbThreads);
-    const int ve = dtype == 0 ? 4 : 8;
-    const bool vec = (r % ve) == 0 && d_h <= 256;  // 16-byte rows of B^K; q row fits the LDS stage
+    const bool vec = absorb_vec_ok(d_h, r, dtype);
     if (dtype == 0) {
         if (vec)
             hipLaunchKernelGGL(absorb_vec_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
@@ -220,8 +228,7 @@ hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void
 }
 
 bool append_absorb_supported(int H, int d_h, int r, int dtype) {
-    const int ve = dtype == 0 ? 4 : 8;
-    return kAbsorbThreads == 256 && r > 0 && (r % ve) == 0 && d_h <= 256;  // the absorb's vector path
+    return kAbsorbThreads == 256 && absorb_vec_ok(d_h, r, dtype);  // the absorb's vector path
 }
 
 hipError_t launch_append_absorb(int batch, int H, int d_h, int r, int L_cap, int dtype, void* k_shared,

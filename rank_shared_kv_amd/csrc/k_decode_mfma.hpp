@@ -658,6 +658,9 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         }
         wave_lds_sync();  // V^T and weights consumed before the next block rewrites them
     }
+    // the block loop has a run-time trip count and can end on a value product: wait for the matrix cores
+    // before the accumulators are read below
+    mfma_result_fence();
 
     // ---- merge the row lanes of each head group (fixed order), one record per (query, head) ----
     // (records of workgroup w = W_b + split: [QW][H] at (w * QW + qi) * H; the next query's pass starts

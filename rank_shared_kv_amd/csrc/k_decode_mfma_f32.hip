@@ -273,6 +273,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
         }
     }
 
+    // the block loop has a run-time trip count and ends on value products: wait for the matrix cores before
+    // the accumulators are read below
+    mfma_result_fence();
+
     // ---- merge the row lanes (fixed order), one record per head ----
 #pragma unroll
     for (int g = 0; g < NHG; ++g) {

@@ -85,7 +85,8 @@ int env_int(const char* name, int dflt) {
 // workspace query and the decode that uses it): LRKV_OCCUPANCY (1 or 2 waves
 // per SIMD; defaults: 2 for the fp32 matrix-core kernel, 2 for the bf16 one at
 // batch >= 32 and 1 below),
-// LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch).
+// LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch), LRKV_FORCE_GENERAL (1: the general
+// kernel for the plain decode).
 constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
 // Which decode the plan is for.  The normalised variant's bf16 matrix-core kernel is built for one wave per
@@ -132,7 +133,13 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
         *out = p;
         return true;
     }
-    if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+    // LRKV_FORCE_GENERAL=1 runs the general kernel wherever it applies (comparisons of problems that would
+    // otherwise take different kernels, e.g. fp32 rank 0 against fp32 rank r with zero latents)
+    const bool force_general = env_int("LRKV_FORCE_GENERAL", 0) == 1 && general_path_supports(d.H, d.d_h, d.r);
+    if (force_general) {
+        p.path = SplitPath::kGeneral;
+        p.occupancy = 1;
+    } else if (mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
         p.path = SplitPath::kMfmaBf16;
         // two waves per SIMD pay off for large batches (many sequences, splits of few blocks each: the
         // 64-sequence ragged batch runs 4% faster) and cost 1-3% for a few long sequences; the choice

@@ -53,14 +53,21 @@ def test_small_bf16_all_pairs():
     _run_and_check(synth.WORKLOADS["small_bf16"])
 
 
+@pytest.mark.parametrize("splits", [None, 3])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(8, 64, 16), (16, 128, 48), (32, 128, 64), (8, 64, 8), (32, 128, 32)])
-def test_ragged_edges(dtype, shape):
-    """Lengths 0, 1, tile boundaries +-1 and a few tiles, with the split plan forced to several splits."""
+def test_ragged_edges(dtype, shape, splits, monkeypatch):
+    """Lengths 0, 1, tile boundaries +-1 and a few tiles, with the default split plan and with the plan forced
+    to three splits per sequence (LRKV_SPLITS, read at every call)."""
     H, d_h, r = shape
-    w = synth.WORKLOADS["ragged"].with_(name=f"edges_{dtype}_{H}_{d_h}_{r}", batch=8, H=H, d_h=d_h, r=r,
+    if splits:
+        monkeypatch.setenv("LRKV_SPLITS", str(splits))
+    w = synth.WORKLOADS["ragged"].with_(name=f"edges_{dtype}_{H}_{d_h}_{r}_s{splits}", batch=8, H=H, d_h=d_h, r=r,
                                         dtype=dtype, L=700, L_cap=704, ragged_lo=None)
     lens = [0, 1, 31, 32, 33, 127, 129, 700]
+    G, _ = lk.lrkv_decode_num_splits(dims_of(w, 704), 700)
+    if splits:
+        assert G == splits * 8
     pairs = [(b, h) for b in range(8) for h in sorted({0, H // 2, H - 1})]
     _run_and_check(w, lengths=lens, L_cap=704, pairs=pairs)
 
@@ -154,17 +161,26 @@ def test_batch_independence():
     assert not torch.equal(a[1], b[1])
 
 
-def test_absorb_matches_float64_product():
-    w = synth.WORKLOADS["long_context"].with_(batch=2)
+@pytest.mark.parametrize("dtype,H,d_h,r", [("bf16", 32, 128, 64), ("bf16", 2, 64, 2048), ("bf16", 2, 64, 2056),
+                                           ("f32", 2, 32, 1024), ("f32", 2, 32, 1028), ("bf16", 3, 24, 55)])
+def test_absorb_matches_reference(dtype, H, d_h, r):
+    """p = q B^K against the reference's fp64 product (oracle.absorb_query), on the vector path and on ranks past
+    it (r > 2048 for bf16, r > 1024 for fp32, r not a multiple of a 16-byte vector), where the scalar kernel
+    runs: every rank gets a complete p."""
+    w = synth.WORKLOADS["long_context"].with_(name=f"absorb_{dtype}_{H}_{d_h}_{r}", batch=2, H=H, d_h=d_h, r=r,
+                                              dtype=dtype)
+    say(f"[case] absorb {dtype} H={H} d_h={d_h} r={r}")
     q = synth.gen_small(w, 0, "q")
     Bk = synth.gen_small(w, 0, "B_k")
     dims = dims_of(w)
-    p = torch.empty((2, w.H, w.r), dtype=torch.float32, device="cuda")
+    p = torch.full((2, w.H, w.r), float("nan"), dtype=torch.float32, device="cuda")
     lk.lrkv_absorb_query(dims, sdev.to_device(q), sdev.to_device(Bk), p)
     torch.cuda.synchronize()
-    qf, Bf = synth.bf16_bits_to_f32(q).astype(np.float64), synth.bf16_bits_to_f32(Bk).astype(np.float64)
-    ref = np.einsum("bhc,hcr->bhr", qf, Bf)
-    err = np.max(np.abs(p.cpu().numpy() - ref)) / np.max(np.abs(ref))
+    ref = oracle.absorb_query(dtype, q, Bk)
+    got = p.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+    say(f"  max rel err {err:.3e}")
     assert err < 1e-6, err
 
 

@@ -272,6 +272,28 @@ def test_pin(pin):
     pin()
 
 
+def test_absorb_query_pins():
+    """The projected query: the review's hand calculation (q = (2, 1), reconstruction column (1, -1) give the
+    projected coordinate 1), a one-hot query picks one row of the basis exactly, and the associativity step of
+    Eq. (6): (q B^K) . z equals q . (z B^K^T) for random inputs."""
+    g = _golden("hand_calc_score.json")
+    p = oracle.absorb_query("f64", _f64(g["q"]).reshape(1, 1, 2), _f64(g["B_k"]).reshape(1, 2, 1))
+    assert p.reshape(-1).tolist() == g["projected_query"]
+    Bk = _rand(71, (3, 8, 5), 0.5)
+    q = np.zeros((1, 3, 8))
+    q[0, 1, 6] = 1.0
+    np.testing.assert_array_equal(oracle.absorb_query("f64", q, Bk)[0, 1], Bk[1, 6])
+    q = _rand(72, (2, 3, 8))
+    z = _rand(73, (2, 3, 5))
+    lhs = np.einsum("bhi,bhi->bh", oracle.absorb_query("f64", q, Bk), z)
+    rhs = np.einsum("bhc,bhc->bh", q, np.einsum("bhi,hci->bhc", z, Bk))
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-13, atol=1e-13)
+    # bf16 inputs are widened exactly: a power-of-two basis times an integer query is exact
+    qb = np.array([[[0x4000, 0x3F80]]], dtype=np.uint16)          # (2, 1) in bf16
+    bb = np.array([[[0x3F80], [0xBF80]]], dtype=np.uint16)        # (1, -1) in bf16
+    assert oracle.absorb_query("bf16", qb, bb).reshape(-1).tolist() == [1.0]
+
+
 def test_r0_lrkv_equals_mqa_bitwise():
     """r = 0 reduces the rebuilt keys and values to the shared ones exactly (empty private sums)."""
     for dtype in ("f32", "bf16", "f64"):
