@@ -196,6 +196,24 @@ lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, 
 lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
                               float* out, const void* workspace, size_t workspace_bytes, void* stream);
 
+/* lrkv_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, kernels, split plan and results (bit for bit) as lrkv_decode,
+ * without the workspace: the split records go to a static device array of
+ * lrkv_decode_noalloc_max_bytes() bytes (32 MiB) inside the library.  Each GPU
+ * holds its own copy of that array from the first call on it until the process
+ * ends; the call itself allocates nothing and calls no allocating routine.
+ * The array is looked up once per device (the device of `stream`, or the
+ * current device for the NULL stream) and is never read before this call's
+ * split pass has written the records it needs, so nothing needs clearing.
+ * Calls that overlap in time on one GPU share the array and race: run them on
+ * one stream, or order them.  A problem whose split records need more than
+ * the array (lrkv_decode_workspace_bytes(dims, max_len) > the maximum) is
+ * rejected with LRKV_ERR_WORKSPACE before anything is enqueued. */
+size_t lrkv_decode_noalloc_max_bytes(void);
+lrkv_status lrkv_decode_noalloc(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                                const float* p, const void* B_v, float* out, void* stream);
+
 /* Decode Q query tokens per sequence at once (speculative decode, chunked
  * prefill): the last Q tokens of every sequence, already appended, each
  * attend to the rows before and at their own position -- query i sits at

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -62,6 +63,46 @@ lrkv_status need_ptr(const void* p, const char* name) {
         lrkv_status _s = (expr);        \
         if (_s != LRKV_OK) return _s;   \
     } while (0)
+
+// Device scratch of lrkv_decode_noalloc: the split records of one decode, in a static device array instead of
+// a caller's workspace.  Each GPU the library runs on holds its own copy from the first call on it until the
+// process ends.  Host code never uses the array's name as an address: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept in scratch_ptr[].
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev` (NULL with *err set on failure).
+void* scratch_on(int dev, hipError_t* err) {
+    *err = hipSuccess;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+    int cur = -1;
+    if ((*err = hipGetDevice(&cur)) != hipSuccess) return nullptr;
+    if (cur != dev && (*err = hipSetDevice(dev)) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess && e2 != hipSuccess) {
+            *err = e2;
+            return nullptr;
+        }
+    }
+    if (e != hipSuccess || !ptr) {
+        *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+    return ptr;
+}
 
 int env_int(const char* name, int dflt) {
     const char* v = getenv(name);
@@ -407,6 +448,42 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
     hipError_t e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
                                       plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace,
                                       (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    return ok();
+}
+
+size_t lrkv_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+lrkv_status lrkv_decode_noalloc(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
+                                const float* p, const void* B_v, float* out, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(p, "p"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+    }
+    const size_t need = workspace_bytes(*dims, plan);
+    if (need > kScratchBytes)
+        return fail(LRKV_ERR_WORKSPACE,
+                    "lrkv_decode_noalloc: the split records need %zu bytes, more than its %zu-byte device scratch; "
+                    "use lrkv_decode with a workspace",
+                    need, kScratchBytes);
+    void* ws = nullptr;  // no live rows anywhere (need == 0): the merge alone writes zeros, as in lrkv_decode
+    hipError_t e = hipSuccess;
+    if (need > 0) {
+        // the device the stream belongs to (the current device for the null stream)
+        int dev = -1;
+        e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess) return hip_fail(e, "lrkv_decode_noalloc: device of the stream");
+        ws = scratch_on(dev, &e);
+        if (!ws) return hip_fail(e, "lrkv_decode_noalloc: address of the device scratch");
+    }
+    LRKV_TRY(run_partial(*dims, *cache, max_len, q, p, ws, plan, (hipStream_t)stream));
+    e = lrkv::launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                           plan.num_splits, cache->seq_lens, B_v, out, (const float*)ws, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     return ok();
 }

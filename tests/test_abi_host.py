@@ -179,6 +179,25 @@ def test_max_len_and_workspace_rejected():
     assert _status(lk.lrkv_decode_partial, d, c, 256, A, A, 1 << 12, need - 4, 0) == lk.LRKV_ERR_WORKSPACE
 
 
+def test_noalloc_checks_before_any_launch():
+    """lrkv_decode_noalloc: the same argument checks as lrkv_decode, and a problem whose split records exceed
+    its device scratch is rejected with LRKV_ERR_WORKSPACE before anything is enqueued."""
+    cap = lk.lrkv_decode_noalloc_max_bytes()
+    assert cap == 32 << 20
+    d = _dims()
+    c = lk.Cache(A, A, A, A, A)
+    assert _status(lk.lrkv_decode_noalloc, d, c, 257, A, A, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    for i in range(4):  # q, p, B_v, out
+        args = [A, A, A, A]
+        args[i] = None
+        assert _status(lk.lrkv_decode_noalloc, d, c, 256, *args, 0) == lk.LRKV_ERR_INVALID_ARG, i
+    big = lk.make_dims(8, 32, 128, 128, 65536, lk.LRKV_F32)  # general kernel, 1024 splits of 260-float records
+    need = lk.lrkv_decode_workspace_bytes(big, 65536)
+    assert need > cap
+    assert _status(lk.lrkv_decode_noalloc, big, c, 65536, A, A, A, A, 0) == lk.LRKV_ERR_WORKSPACE
+    assert "scratch" in lk.lib().lrkv_last_error().decode()
+
+
 def test_unsupported_shape_rejected():
     d = lk.make_dims(1, 4, 300, 4, 64, lk.LRKV_F32)  # d_h beyond every kernel
     c = lk.Cache(A, A, A, A, A)
