@@ -4,7 +4,9 @@
 One step is one decode step of the whole path on a batch of sequences:
   append the new token's projected rows + absorb the query (p = q B^K), one
   launch -> split-L partial pass -> split merge + B^V epilogue,
-all through the C ABI on one HIP stream, with the inputs resident in HBM.
+all through the C ABI on one HIP stream, with the inputs resident in HBM.  A
+workload with several independent layers (the 24-layer one) runs every layer
+in turn in each step, each with its own cache, query and bases.
 Before the timed region the caches hold L - 1 - warmup rows per sequence, so
 the first timed step decodes over exactly L rows; every step appends one row,
 so step k decodes over L + k rows.
@@ -81,13 +83,22 @@ def read_traffic(workload: str, launch_bytes: float):
     return float(m_bytes.group(1))
 
 
-def cpu_baseline(w, lens, budget_s: float):
+def host_cores():
+    """CPU cores this process may use: the affinity mask, further limited by OMP_NUM_THREADS when that is set
+    (the share of the host a GPU job is granted)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(w, lens, budget_s: float, threads: int):
     """The fp64 CPU reference, as it stands, on (b, h) pairs of this workload until ~budget_s of wall time."""
     import numpy as np
     import oracle
     import synth
 
-    threads = oracle._threads(None)
     done_tokens, elapsed, npairs = 0, 0.0, 0
     seqs = list(range(w.batch))
     for b in seqs:
@@ -114,6 +125,14 @@ def cpu_baseline(w, lens, budget_s: float):
             "sample": f"{npairs} of {w.batch * w.H} (sequence, head) pairs of this workload at its full lengths "
                       f"({done_tokens} cached-token·heads, {elapsed:.1f} s wall, fp64 rebuild-then-attend, "
                       f"OpenMP over pairs)"}
+
+
+def quantiles(xs):
+    """p10 / median / p90 (linear interpolation) of a list of durations."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    p10, p50, p90 = np.percentile(a, [10, 50, 90])
+    return {"p10": float(p10), "p50": float(p50), "p90": float(p90), "mean": float(a.mean()), "n": int(a.size)}
 
 
 def materialize_bench(args):
@@ -224,6 +243,9 @@ def main():
     ap.add_argument("--key-scales", action="store_true",
                     help="normalised variant's whole-history pass: each step computes the key scale of every live "
                          "row and head (lrkv_key_scales with n_last = the whole history, as after a prefill)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="independent layers decoded back to back per step, each with its own cache, query and "
+                         "bases (default: the workload's layer count, 24 for mid_24layer; plain decode only)")
     ap.add_argument("--no-stream-probe", action="store_true",
                     help="skip the streaming-read probe (the measured read bandwidth the split pass is compared with)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -261,29 +283,42 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     K, W, Q = args.steps, args.warmup, max(1, args.queries)
+    plain = not (Q > 1 or args.layer or args.norm or args.paged or args.rope)
+    n_layers = args.layers or (w.layers if plain else 1)
+    if n_layers > 1 and not plain:
+        print("bench.py: several layers per step are timed for the plain decode only", file=sys.stderr)
+        sys.exit(2)
     lens_full = synth.seq_lengths(w)
+    for layer in range(1, n_layers):  # the layers' caches share one capacity and length bound
+        assert synth.seq_lengths(w, layer).tolist() == lens_full.tolist()
     L_cap, max_len = launch_config(w, K * Q, args.capacity)
     if args.paged:
         L_cap = (L_cap + args.paged - 1) // args.paged * args.paged
     start_lens = lens_full - Q - W * Q
     assert int(start_lens.min()) >= 0
     log(f"bench: workload {w.name} B={w.batch} H={w.H} d_h={w.d_h} r={w.r} {w.dtype} L_max={int(lens_full.max())} "
-        f"steps={K} warmup={W} queries={Q}")
+        f"steps={K} warmup={W} queries={Q} layers={n_layers}")
     t0 = time.time()
-    dev = sdev.fill_layer(w, 0, L_cap=L_cap, lengths=lens_full)
-    dev["seq_lens"].copy_(torch.from_numpy(start_lens.astype(np.int32)).cuda())
+    devs = []
+    for layer in range(n_layers):  # every layer its own seeded cache, query and bases
+        d_l = sdev.fill_layer(w, layer, L_cap=L_cap, lengths=lens_full)
+        d_l["seq_lens"].copy_(torch.from_numpy(start_lens.astype(np.int32)).cuda())
+        devs.append(d_l)
+    dev = devs[0]
     rows = sdev.new_rows(w)
     torch.cuda.synchronize()
     log(f"bench: inputs resident in HBM ({time.time() - t0:.1f} s to generate and copy)")
 
     dtype_code = lk.LRKV_F32 if w.dtype == "f32" else lk.LRKV_BF16
     dims = lk.make_dims(w.batch, w.H, w.d_h, w.r, L_cap, dtype_code)
-    cache = lk.make_cache(dev["k_shared"], dev["v_shared"], dev["z_k"] if w.r else None,
-                          dev["z_v"] if w.r else None, dev["seq_lens"])
+    caches = [lk.make_cache(d_l["k_shared"], d_l["v_shared"], d_l["z_k"] if w.r else None,
+                            d_l["z_v"] if w.r else None, d_l["seq_lens"]) for d_l in devs]
+    cache = caches[0]
     nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
     ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
-    p = torch.empty((w.batch, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda")
-    out = torch.empty((w.batch, w.H, w.d_h), dtype=torch.float32, device="cuda")
+    ps = [torch.empty((w.batch, w.H, max(w.r, 1)), dtype=torch.float32, device="cuda") for _ in devs]
+    outs = [torch.empty((w.batch, w.H, w.d_h), dtype=torch.float32, device="cuda") for _ in devs]
+    p, out = ps[0], outs[0]
     S, chunk = lk.lrkv_decode_num_splits(dims, max_len)
     if Q > 1:
         nbytes = lk.lrkv_decode_multi_workspace_bytes(dims, Q, max_len)
@@ -406,10 +441,21 @@ def main():
             q_use = q_step
             if w.r:
                 lk.lrkv_absorb_query(dims, q_use, dev["B_k"], p, stream)
-        else:  # the append and the query absorption in one launch
-            q_use = dev["q"]
-            lk.lrkv_append_absorb(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, q_use,
-                                  dev["B_k"] if w.r else None, pp, stream)
+        else:
+            # every layer in turn: the append and the query absorption in one launch, the split pass, the merge
+            # (the layers share the workspace: each merge has read it before the next split pass writes it)
+            for d_l, c_l, p_l, o_l in zip(devs, caches, ps, outs):
+                pp_l = p_l if w.r else None
+                lk.lrkv_append_absorb(dims, c_l, rows["k_new"], rows["v_new"], zk_new, zv_new, d_l["q"],
+                                      d_l["B_k"] if w.r else None, pp_l, stream)
+                if timed:
+                    e0 = ev()
+                lk.lrkv_decode_partial(dims, c_l, max_len, d_l["q"], pp_l, ws, nbytes, stream)
+                if timed:
+                    ev_pairs.append((e0, ev()))
+                lk.lrkv_decode_merge(dims, d_l["seq_lens"], max_len, d_l["B_v"] if w.r else None, o_l, ws, nbytes,
+                                     stream)
+            return
         if timed:
             e0 = ev()
         lk.lrkv_decode_partial(dims, cache, max_len, q_use, pp, ws, nbytes, stream)
@@ -422,32 +468,43 @@ def main():
             if timed:
                 layer_ev.append((e_p0, e_p1, e_o0, ev()))
 
-    def timed_pass(instrumented: bool) -> float:
+    def timed_pass(instrumented: bool, marks=None) -> float:
         # the same work each time: lengths back to the start, W warm-up steps, then K timed steps
-        dev["seq_lens"].copy_(torch.from_numpy(start_lens.astype(np.int32)).cuda())
+        for d_l in devs:
+            d_l["seq_lens"].copy_(torch.from_numpy(start_lens.astype(np.int32)).cuda())
         for _ in range(W):
             step(False)
         torch.cuda.synchronize()
-        assert dev["seq_lens"].cpu().numpy().tolist() == (lens_full - Q).tolist()
+        for d_l in devs:
+            assert d_l["seq_lens"].cpu().numpy().tolist() == (lens_full - Q).tolist()
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t_start.record(stream)
         for _ in range(K):
+            if marks is not None:
+                marks.append(ev())
             step(instrumented)
         t_end.record(stream)
+        if marks is not None:
+            marks.append(t_end)
         torch.cuda.synchronize()
-        assert dev["seq_lens"].cpu().numpy().tolist() == (lens_full - Q + K * Q).tolist()
-        assert bool(torch.isfinite(out).all())
+        for d_l, o_l in zip(devs, outs):
+            assert d_l["seq_lens"].cpu().numpy().tolist() == (lens_full - Q + K * Q).tolist()
+            assert bool(torch.isfinite(o_l).all())
         return t_start.elapsed_time(t_end)
 
     total_ms = timed_pass(False)         # the step time: nothing but the step's own launches
     total_ms_events = timed_pass(True)   # the decode launches' durations
     split_ms = [a.elapsed_time(b) for a, b in ev_pairs]
+    # per-step latency: a third pass with one event at every step boundary (about 1 us each)
+    marks = []
+    timed_pass(False, marks)
+    step_us = [1e3 * marks[k].elapsed_time(marks[k + 1]) for k in range(K)]
 
     # work per timed step k: sequence b holds lens_full + k*Q rows, and its query i (0-based among the Q new
     # tokens) sees the rows up to and including its own, lens_full + k*Q - Q + i + 1 of them
-    token_heads = sum(int(np.sum(Q * (lens_full + k * Q) - Q * (Q - 1) // 2, dtype=np.int64)) * w.H
-                      for k in range(K))
+    token_heads = n_layers * sum(int(np.sum(Q * (lens_full + k * Q) - Q * (Q - 1) // 2, dtype=np.int64)) * w.H
+                                 for k in range(K))
     value = token_heads / (total_ms / 1e3)
     s_bytes = w.elem_bytes
     cache_bytes_per_step = [lk.lrkv_cache_bytes(dims, (lens_full + k * Q).tolist()) for k in range(K)]
@@ -455,8 +512,8 @@ def main():
     p_bytes = Q * w.batch * w.H * w.r * 4
     basis_bytes = 2 * w.H * w.d_h * w.r * s_bytes
     out_bytes = Q * w.batch * w.H * w.d_h * 4
-    step_bytes = sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes
-    split_bytes = sum(cache_bytes_per_step) / K + q_bytes + p_bytes
+    step_bytes = n_layers * (sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes)
+    split_bytes = sum(cache_bytes_per_step) / K + q_bytes + p_bytes  # per split launch (one layer)
     if args.norm:  # the scales are read once per step, one per (row, head)
         rho_bytes = [sum(int(x) for x in (lens_full + k)) * w.H * s_bytes for k in range(K)]
         split_bytes += sum(rho_bytes) / K
@@ -470,7 +527,7 @@ def main():
     split_avg_ms = sum(split_ms) / len(split_ms)
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
-    flops_mfma = 2 * w.d_h * (token_heads / K)  # shared-key score tile per step
+    flops_mfma = 2 * w.d_h * (token_heads / K / n_layers)  # shared-key score tile per split launch
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
     traffic = (read_traffic(w.name, split_bytes)
                if not (args.layer or args.norm or args.paged or args.rope) and Q == 1 else None)
@@ -517,9 +574,18 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        log(f"bench: timing the CPU reference (~{args.cpu_budget:.0f} s)")
-        cpu = cpu_baseline(w, lens_full, args.cpu_budget)
-        log(f"bench: CPU reference {cpu['value']:.3e} token·heads/s on {cpu['cores']} threads")
+        cores = host_cores()
+        log(f"bench: timing the CPU reference on {cores} cores (~{args.cpu_budget:.0f} s), then on one core")
+        cpu = cpu_baseline(w, lens_full, args.cpu_budget, cores)
+        one = cpu_baseline(w, lens_full, max(2.0, args.cpu_budget / 2), 1)
+        cpu.update({"nproc": os.cpu_count(),
+                    "affinity_cores": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+                    "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+                    "cores_note": "every core this process may use (its affinity mask, limited by OMP_NUM_THREADS "
+                                  "when set: the host share granted to a one-GPU job)",
+                    "single_core": {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}})
+        log(f"bench: CPU reference {cpu['value']:.3e} token·heads/s on {cpu['cores']} threads "
+            f"(nproc {cpu['nproc']}), {one['value']:.3e} on one core")
 
     rec = {
         "metric": METRIC,
@@ -535,11 +601,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "step_us_quantiles": dict(quantiles(step_us), timing="a third pass over the same steps with one HIP "
+                                  "event at every step boundary (each event adds about 1 us)"),
+        "split_launch_us_quantiles": quantiles([1e3 * x for x in split_ms]),
+        "per_layer_us": (total_ms / K / n_layers * 1e3) if n_layers > 1 else None,
         "config": {"workload": w.name + ("+projections" if args.layer else "") + (f"+{Q}queries" if Q > 1 else "") + ("+normalised" if args.norm else "")
                    + (f"+paged{args.paged}" if args.paged else "") + ("+rope" if args.rope else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
-                   "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q},
+                   "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q, "layers": n_layers},
         "hbm_gbps_step": step_gbps,
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -549,8 +619,8 @@ def main():
                      "lrkv_decode_paged (split pass + merge)" if args.paged else
                      "lrkv_decode_rope (split pass + merge)" if args.rope else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3,
-                     "timing": f"HIP events around each of the {K} decode launches of a second pass over the same "
-                               "steps (the step time comes from a pass without them)",
+                     "timing": f"HIP events around each of the {K * n_layers} decode launches of a second pass "
+                               "over the same steps (the step time comes from a pass without them)",
                      "stream_read_gbps": stream_gbps,
                      "frac_of_stream_read": (split_gbps / stream_gbps) if stream_gbps else None},
         "mfma_util_shared_score": mfma_util,

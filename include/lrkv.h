@@ -72,8 +72,14 @@ typedef struct {
  * The latents are stored token-major: element z[b][j][h][i] is head h's
  * coordinate i for token j, so one token's H x r latents form one contiguous
  * row (the logical per-head tensor z_h[b][j][i] of the pages, transposed).
- * A decode step then streams every cache tensor linearly, and per-head latent
- * regions never sit at a common large stride, whatever L_cap is.
+ * This replaces the per-head layout [batch][H][L_cap][r] in which the pages'
+ * notation (reading notes sec. 2.1) and a per-head cache would hold them:
+ * latents in that layout are NOT accepted here -- the library cannot tell the
+ * two apart, and per-head latents give wrong results.  Convert them once with
+ * lrkv_latents_to_token_major.  The reason for the change: a decode step then
+ * streams every cache tensor linearly, and per-head latent regions never sit at
+ * a common large stride, whatever L_cap is (split pass 208 against 227 us at
+ * the long-context shape with L_cap = 33024).
  * For decode the current query's own token must already be appended, so
  * seq_lens[b] counts it; every live row is visible to the query. */
 typedef struct {
@@ -110,6 +116,15 @@ typedef struct {
     int32_t max_pages;
     int32_t n_pages;
 } lrkv_paged_cache;
+
+/* Latents from the per-head layout to the token-major layout lrkv_cache and
+ * lrkv_paged_cache expect (see lrkv_cache):
+ *   src  device [batch][H][L_cap][r]   (dims->dtype), per head
+ *   dst  device [batch][L_cap][H][r]   (dims->dtype), token-major
+ * dst[b][j][h][i] = src[b][h][j][i] for every row j < L_cap, copied bit for
+ * bit; src and dst must not overlap.  r == 0: nothing to do (src, dst may be
+ * NULL).  Apply it to z_k and z_v separately. */
+lrkv_status lrkv_latents_to_token_major(const lrkv_dims* dims, const void* src, void* dst, void* stream);
 
 /* Absorb the key basis into the query: p[b][h][i] = sum_c q[b][h][c] * B_k[h][c][i]
  * (reading notes sec. 2.4 Eq. (6); review sec. 3, Algorithm 2: one small

@@ -27,7 +27,7 @@ LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_append_absorb", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_noalloc_max_bytes",
-            "lrkv_decode_noalloc", "lrkv_decode_multi_workspace_bytes",
+            "lrkv_decode_noalloc", "lrkv_latents_to_token_major", "lrkv_decode_multi_workspace_bytes",
             "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table",
             "lrkv_decode_rope_workspace_bytes", "lrkv_decode_rope", "lrkv_key_scales", "lrkv_norm_query",
             "lrkv_decode_normed", "lrkv_materialize", "lrkv_project_append", "lrkv_output_project", "lrkv_read_probe",
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode_partial": ([D, C, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_noalloc_max_bytes": ([], sz),
+            "lrkv_latents_to_token_major": ([D, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_noalloc": ([D, C, i32, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_multi_workspace_bytes": ([D, i32, i32], sz),
             "lrkv_decode_multi": ([D, i32, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -181,6 +182,11 @@ def lrkv_decode(dims: Dims, cache: Cache, max_len: int, q, p, B_v, out, workspac
                 stream=None) -> None:
     _check(lib().lrkv_decode(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(q), _ptr(p), _ptr(B_v), _ptr(out),
                              _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode")
+
+
+def lrkv_latents_to_token_major(dims: Dims, src, dst, stream=None) -> None:
+    _check(lib().lrkv_latents_to_token_major(ctypes.byref(dims), _ptr(src), _ptr(dst), _stream(stream)),
+           "lrkv_latents_to_token_major")
 
 
 def lrkv_decode_noalloc_max_bytes() -> int:

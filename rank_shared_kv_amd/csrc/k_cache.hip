@@ -294,6 +294,40 @@ hipError_t launch_multi_lengths(int batch, int Q, int qw, const int32_t* seq_len
     return hipGetLastError();
 }
 
+namespace {
+// dst[b][j][h][i] = src[b][h][j][i]: one workgroup per (sequence, 8-row tile); thread t of a tile walks the
+// tile's destination elements (8 rows x H x r, contiguous in dst) with stride 256, so the writes are
+// coalesced and the reads come in runs of r elements of one head's rows.
+template <typename T>
+__global__ void __launch_bounds__(256) latents_token_major_kernel(int H, int L_cap, int r, const T* __restrict__ src,
+                                                                  T* __restrict__ dst) {
+    constexpr int kTile = 8;
+    const int b = blockIdx.y, j0 = blockIdx.x * kTile;
+    const int rows = min(kTile, L_cap - j0);
+    const size_t hr = (size_t)H * r;
+    const T* s = src + (size_t)b * H * L_cap * r;
+    T* d = dst + ((size_t)b * L_cap + j0) * hr;
+    const size_t n = (size_t)rows * hr;
+    for (size_t e = threadIdx.x; e < n; e += 256) {
+        const size_t jj = e / hr, rem = e - jj * hr;
+        const size_t h = rem / r, i = rem - h * r;
+        d[e] = s[(h * L_cap + j0 + jj) * r + i];
+    }
+}
+}  // namespace
+
+hipError_t launch_latents_token_major(int batch, int H, int L_cap, int r, int dtype, const void* src, void* dst,
+                                      hipStream_t stream) {
+    dim3 grid((L_cap + 7) / 8, batch), block(256);
+    if (dtype == 0)
+        hipLaunchKernelGGL(latents_token_major_kernel<float>, grid, block, 0, stream, H, L_cap, r, (const float*)src,
+                           (float*)dst);
+    else
+        hipLaunchKernelGGL(latents_token_major_kernel<uint16_t>, grid, block, 0, stream, H, L_cap, r,
+                           (const uint16_t*)src, (uint16_t*)dst);
+    return hipGetLastError();
+}
+
 hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int page_shift, int max_pages,
                               void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
                               const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,

@@ -452,6 +452,20 @@ lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t 
     return ok();
 }
 
+lrkv_status lrkv_latents_to_token_major(const lrkv_dims* dims, const void* src, void* dst, void* stream) {
+    LRKV_TRY(check_dims(dims));
+    if (dims->r == 0) return ok();
+    LRKV_TRY(need_ptr(src, "src"));
+    LRKV_TRY(need_ptr(dst, "dst"));
+    const size_t bytes = (size_t)dims->batch * dims->H * dims->L_cap * dims->r * (dims->dtype == LRKV_F32 ? 4 : 2);
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(LRKV_ERR_INVALID_ARG, "src and dst overlap");
+    hipError_t e = lrkv::launch_latents_token_major(dims->batch, dims->H, dims->L_cap, dims->r, dims->dtype, src, dst,
+                                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "latent layout kernel launch");
+    return ok();
+}
+
 size_t lrkv_decode_noalloc_max_bytes(void) { return kScratchBytes; }
 
 lrkv_status lrkv_decode_noalloc(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,

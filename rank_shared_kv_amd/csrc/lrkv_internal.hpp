@@ -109,6 +109,9 @@ hipError_t launch_paged_append(int batch, int H, int d_h, int r, int dtype, int 
                               void* k_pages, void* v_pages, void* zk_pages, void* zv_pages,
                               const int32_t* block_table, int32_t* seq_lens, const void* k_new, const void* v_new,
                               const void* zk_new, const void* zv_new, hipStream_t stream);
+// latents from the per-head layout [batch][H][L_cap][r] to the token-major one [batch][L_cap][H][r]
+hipError_t launch_latents_token_major(int batch, int H, int L_cap, int r, int dtype, const void* src, void* dst,
+                                      hipStream_t stream);
 int read_probe_workgroups();
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_rope_table(int d_h, int n_pos, float base, float* table, hipStream_t stream);

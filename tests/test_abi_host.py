@@ -198,6 +198,15 @@ def test_noalloc_checks_before_any_launch():
     assert "scratch" in lk.lib().lrkv_last_error().decode()
 
 
+def test_latent_layout_conversion_checks():
+    d = _dims()
+    n = 2 * 8 * 256 * 8 * 2  # bytes of one latent tensor
+    assert _status(lk.lrkv_latents_to_token_major, d, None, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_latents_to_token_major, d, A, A + n - 16, 0) == lk.LRKV_ERR_INVALID_ARG  # overlap
+    assert _status(lk.lrkv_latents_to_token_major, d, A, A + 8, 0) == lk.LRKV_ERR_INVALID_ARG       # misaligned
+    lk.lrkv_latents_to_token_major(lk.make_dims(2, 8, 64, 0, 256, lk.LRKV_BF16), None, None, 0)   # r = 0: no-op
+
+
 def test_unsupported_shape_rejected():
     d = lk.make_dims(1, 4, 300, 4, 64, lk.LRKV_F32)  # d_h beyond every kernel
     c = lk.Cache(A, A, A, A, A)

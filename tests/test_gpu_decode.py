@@ -293,3 +293,26 @@ def test_length_proportional_splits(dtype, H, d_h, r, mix):
         pairs = [(b, h) for b in live for h in sorted({0, H - 1})]
         ref = oracle_pairs(w, 0, lens, pairs, mqa=(r == 0))
         compare(w, got, ref, pairs, f"lp_{mix}")
+
+
+@pytest.mark.parametrize("dtype,H,r", [("bf16", 32, 64), ("f32", 6, 5), ("bf16", 18, 55)])
+def test_latents_from_head_major(dtype, H, r):
+    """lrkv_latents_to_token_major: per-head latents [batch][H][L_cap][r] become the token-major layout bit
+    for bit, and a decode on the converted cache equals the decode of the same cache filled token-major."""
+    w = synth.WORKLOADS["ragged"].with_(name=f"layout_{dtype}_{H}_{r}", batch=3, H=H, d_h=64, r=r, dtype=dtype,
+                                        L=300, L_cap=320, ragged_lo=None)
+    lens = np.array([300, 1, 129], dtype=np.int32)
+    say(f"[case] latents from the per-head layout {dtype} H={H} r={r}")
+    dev = sdev.fill_layer(w, 0, L_cap=320, lengths=lens)
+    want = gpu_decode(w, dev, 300, L_cap=320)
+    conv = dict(dev)
+    dims = dims_of(w, 320)
+    for name in ("z_k", "z_v"):
+        head_major = dev[name].permute(0, 2, 1, 3).contiguous()   # [batch][H][L_cap][r]
+        dst = torch.full_like(dev[name], float("nan"))
+        lk.lrkv_latents_to_token_major(dims, head_major, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(dst.view(torch.int16 if dtype == "bf16" else torch.int32),
+                           dev[name].view(torch.int16 if dtype == "bf16" else torch.int32))
+        conv[name] = dst
+    assert torch.equal(gpu_decode(w, conv, 300, L_cap=320), want)
