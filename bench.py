@@ -57,8 +57,8 @@ def launch_config(w, steps: int, capacity: int = 0):
 
 
 # the sources that determine the bf16 split kernel's code and launch configuration
-SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hpp", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma.hip", "lrkv_device.hpp",
-                        "lrkv_internal.hpp", "lrkv_api.cpp")
+SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hpp", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma.hip",
+                        "k_decode_mfma_f32.hip", "lrkv_device.hpp", "lrkv_internal.hpp", "lrkv_api.cpp")
 
 
 def kernel_sources_digest() -> str:
@@ -91,6 +91,31 @@ def host_cores():
     if env and env.isdigit() and int(env) > 0:
         n = min(n, int(env))
     return max(1, n)
+
+
+def read_sq_counters(workload: str):
+    """Matrix-core and VALU activity of the split kernel from the committed rocprofv3 counter summary, if it
+    matches these sources: the counted bf16 MFMA FLOP, the matrix cores' busy fraction, and the fractions of
+    wave time spent issuing VALU instructions and waiting."""
+    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_sq_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_digest = re.search(r"kernel sources digest:\s*`?([0-9a-f]{16})", text)
+    if not m_digest or m_digest.group(1) != kernel_sources_digest():
+        return None
+    fields = {"mfma_flop_per_launch": r"bf16 MFMA FLOP per split launch \(counter\):\s*([0-9.eE+]+)",
+              "mfma_busy_frac": r"MFMA busy fraction of the split launch \(counter\):\s*([0-9.eE+-]+)",
+              "valu_issue_frac": r"VALU issue fraction of wave time:\s*([0-9.eE+-]+)",
+              "wait_frac": r"Wait fraction of wave time:\s*([0-9.eE+-]+)"}
+    out = {}
+    for k, pat in fields.items():
+        m = re.search(pat, text)
+        if not m:
+            return None
+        out[k] = float(m.group(1))
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
 
 
 def cpu_baseline(w, lens, budget_s: float, threads: int):
@@ -624,6 +649,10 @@ def main():
                      "stream_read_gbps": stream_gbps,
                      "frac_of_stream_read": (split_gbps / stream_gbps) if stream_gbps else None},
         "mfma_util_shared_score": mfma_util,
+        "mfma_counters": (dict(read_sq_counters(w.name), note="rocprofv3 counters of the split kernel on this "
+                               "workload; the shared-score figure above is 2 d_h FLOP per cached token-head over "
+                               "the live launch time, the counted FLOP include the value products (3x)")
+                          if plain and read_sq_counters(w.name) else None),
         "layer_step": layer,
         "cpu_baseline": cpu,
     }
