@@ -322,10 +322,15 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
 
     // ---- the load ring ----
     uint32_t ring[NSLOT][SDW];
+    // a descriptor of no bytes: every load through it is out of range, returns zeros and touches no memory.
+    // During a row lane's last block there is no next block to prefetch; its latent units (non-temporal, so a
+    // re-read would go back to memory) then go through this descriptor, while the key and value units re-read
+    // the current block from L2.
+    const __amdgpu_buffer_rsrc_t rs_none = buf_rsrc(a.k_shared, 0);
 
-    // unit u of the block starting at row t0 -> slot
-    // unit u of the block whose first row sits at (pool) row pr, into ring slot `slot`
-    auto issue = [&](int u, int pr, int slot) {
+    // unit u of the block whose first row sits at (pool) row pr, into ring slot `slot`; live = false sends
+    // the latent loads through the empty descriptor
+    auto issue = [&](int u, int pr, int slot, bool live) {
         if (u == 0) {  // key fragments in the MFMA A layout: rows 16*half + n16, chunk 4*kk + g4
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -359,7 +364,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             const int phase = v / (4 * OCTS);
             const int oi = (v % (4 * OCTS)) / 4, sub = v % 4;
             const int so = pr * (int)row_bytes_lat + oi * (int)oct_bytes;
-            const __amdgpu_buffer_rsrc_t rs = (phase == 0) ? rs_zk : rs_zv;
+            const __amdgpu_buffer_rsrc_t rs = !live ? rs_none : (phase == 0) ? rs_zk : rs_zv;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 // one instruction reads row 8*sub + k of 8 consecutive heads: 8*r*2 contiguous bytes
@@ -398,7 +403,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     if (nmine > 0) {
         const int pr_first = paged_row(a, bc, kRows * (first_blk + rot * step_blk));
 #pragma unroll
-        for (int u = 0; u < NSLOT - 1; ++u) issue(u, pr_first, u);
+        for (int u = 0; u < NSLOT - 1; ++u) issue(u, pr_first, u, true);
     }
 
 #if LRKV_LOCKSTEP
@@ -422,9 +427,11 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         const int blk = first_blk + itr * step_blk;
         const int t0 = kRows * blk;
         const int nvalid = min(kRows, Lb - t0);
-        // next block of this row lane; on the last block the prefetch re-reads this block (always in bounds)
+        // next block of this row lane; on the last block there is none, and the prefetch goes through the
+        // empty descriptor (same addresses as this block, no memory traffic)
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
-        const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
+        const bool pf_live = it + 1 < nmine;
+        const int t0_pf = pf_live ? kRows * (first_blk + itn * step_blk) : t0;
         const int pr = paged_row(a, bc, t0), pr_pf = paged_row(a, bc, t0_pf);  // pool rows (t0 when contiguous)
         f32x4_t s_sh[QW][2];
         uint32_t rho_w[8];  // scales of this lane's 8 scores (bf16 bits), read at the top of the block
@@ -442,8 +449,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             // keep NSLOT - 1 units in flight ahead of this one
             {
                 const int un = u + NSLOT - 1;
-                if (un < NU) issue(un, pr, un % NSLOT);
-                else issue(un - NU, pr_pf, un % NSLOT);
+                if (un < NU) issue(un, pr, un % NSLOT, true);
+                else issue(un - NU, pr_pf, un % NSLOT, pf_live);
             }
             // fence the scheduler at unit boundaries: loads stay NSLOT - 1 units ahead, no further
             __builtin_amdgcn_sched_barrier(0);
