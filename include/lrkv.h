@@ -195,8 +195,10 @@ int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* 
  * dims, max_len and seq_lens contents.
  * Supported: d_h <= 256, r <= 256, H * (d_h + r + 2) * 4 <= 64 KiB.  Matrix-core
  * kernels cover bf16 with d_h in {64, 128}, r in {0, 8, 16, 32, 48, 64} and fp32
- * with r = 0, d_h in {64, 128}, both for H in {8, 16, 32} and L_cap a multiple
- * of 32; other valid shapes use the general kernels. */
+ * with r = 0, d_h in {64, 128}, both for H in {8, 16, 32}, and bf16 with d_h = 128
+ * at the reading notes' model-table shapes (H, r) = (6, 46), (12, 51), (18, 55),
+ * (32, 54) (sec. 2.5, Table 7 ranks), all with L_cap a multiple of 32; other
+ * valid shapes use the general kernels. */
 lrkv_status lrkv_decode(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* q,
                         const float* p, const void* B_v, float* out, void* workspace, size_t workspace_bytes,
                         void* stream);

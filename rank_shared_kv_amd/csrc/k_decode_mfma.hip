@@ -12,6 +12,8 @@ hipError_t launch_split_mfma_d64_q2(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma_d64_q4(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma_d128_q2(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma_d128_q4(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_split_mfma_d128_t7(const DecodeArgs& a, int occupancy, hipStream_t stream);
+bool mfma_table_shape(int H, int d_h, int r);
 
 namespace {
 constexpr int kRows = 32;   // rows per block (k_decode_mfma.hpp)
@@ -23,10 +25,15 @@ bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap) {
     // rows of a block never leave the allocation when L_cap is a multiple of 32; buffer offsets are 32-bit
     if (L_cap % kRows != 0) return false;
     if ((long long)L_cap * d_h * 2 >= (1LL << 31) || (long long)H * L_cap * r * 2 >= (1LL << 31)) return false;
+    if (mfma_table_shape(H, d_h, r)) return true;
     if (d_h != 64 && d_h != 128) return false;
     if (!(r == 0 || r == 8 || r == 16 || r == 32 || r == 48 || r == 64)) return false;
     return H == 8 || H == 16 || H == 32;
 }
+
+// the normalised-variant and several-query instances exist for the regular shapes only (the model table's
+// shapes have plain and paged single-token decode)
+bool mfma_all_variants(int H, int d_h, int r) { return !mfma_table_shape(H, d_h, r); }
 
 int mfma_rows_per_tile(int H) { return kRows * (kWaves / ((H + 15) / 16)); }
 
@@ -43,6 +50,7 @@ hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t str
     }
     if (a.qw != 1) return hipErrorInvalidValue;
     const bool norm = a.rho != nullptr;
+    if (mfma_table_shape(a.H, a.d_h, a.r)) return norm ? hipErrorInvalidValue : launch_split_mfma_d128_t7(a, occupancy, stream);
     if (a.d_h == 64) return norm ? launch_split_mfma_d64_n1(a, occupancy, stream) : launch_split_mfma_d64_n0(a, occupancy, stream);
     if (a.d_h == 128) return norm ? launch_split_mfma_d128_n1(a, occupancy, stream) : launch_split_mfma_d128_n0(a, occupancy, stream);
     return hipErrorInvalidValue;

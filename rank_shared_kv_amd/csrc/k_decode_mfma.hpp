@@ -106,12 +106,26 @@ constexpr int kNTSh = LRKV_NT_SHARED ? 2 : 0;
 
 template <int D, int R, int H, int OCC, int QW = 1>
 struct Cfg {
-    static constexpr int EPL = R / 8;                   // latent coordinates per lane
-    static constexpr int LDW = (EPL + 1) / 2;           // dwords per latent load (EPL = 1 uses one dword)
-    static constexpr int NOCT = H / 8;                  // head octets
+    // Latent slices: 8 lanes per head, lane sl owns the EPL coordinates from sl*EPL (the last lane: the rest,
+    // TAIL of them).  In the plain form (R a multiple of 8, H a multiple of 8) a lane's coordinates start on a
+    // dword and fill LDW dwords.  In the general form (GEN) every lane loads a window of LDL dwords from a
+    // token's latent row that holds its coordinates and lies inside the row: lanes 0..6 from the even element
+    // at or below their first coordinate, the last lane ending at its head's end (rounded up to an even
+    // element); a lane's coordinates then sit at window positions off .. off + own - 1, and the positions
+    // around them (neighbouring lanes' or heads' values) are masked out of the private score.
+    static constexpr int EPL = (R + 7) / 8;             // latent coordinates per lane
+    static constexpr bool REAL = EPL > 1 && !(R % 2 == 0 && EPL % 2 == 0);  // lanes may start on an odd element
+    static constexpr int LDW = (EPL + 1) / 2;           // dwords per lane and row (EPL = 1 uses one dword)
+    static constexpr int LDL = REAL ? (EPL + 2) / 2 : LDW;  // dwords per latent load
     static constexpr int NHG = (H + 15) / 16;           // head groups (16 heads: MFMA N)
     static constexpr int NTL = kWaves / NHG;            // row lanes per workgroup
-    static constexpr int OCTS = (H >= 16) ? 2 : 1;      // octets per head group
+    static constexpr int OCTS = (H >= 16) ? 2 : (H + 7) / 8;  // octets (8 head slots) per head group
+    static constexpr int HS = 16 * (NHG - 1) + 8 * OCTS;     // head slots the octets cover (padding slots: >= H)
+    // GEN: head slots past H or a partial last slice -- the general form of the addressing and masks
+    // (shapes with H a multiple of 8 and R a multiple of 8 compile to the plain form)
+    static constexpr bool GEN = (HS != H) || (8 * EPL != R);
+    static constexpr int TAIL = (R - 7 * EPL > 0) ? R - 7 * EPL : 0;  // coordinates of a head's last lane
+    static constexpr int NPOS = GEN ? 2 * LDL : EPL;   // latent values a lane accumulates per row (window positions)
     static constexpr int KSTEPS = D / 32;               // k-steps of the score MFMA
     static constexpr int CB = D / 16;                   // 16-column blocks of the value MFMA
     static constexpr int LPR = D / 8;                   // lanes per shared row (16 B each)
@@ -121,7 +135,7 @@ struct Cfg {
     static constexpr int NU = 2 + NLU;                  // + key-fragment unit + value-tile unit
     static constexpr int KDW = 8 * KSTEPS;              // dwords of the key unit
     static constexpr int VDW = 4 * NINS;                // dwords of the value unit
-    static constexpr int LUDW = 8 * LDW;                // dwords of a latent unit
+    static constexpr int LUDW = 8 * LDL;                // dwords of a latent unit
     static constexpr int SLOT_DW = (KDW > VDW ? (KDW > LUDW ? KDW : LUDW) : (VDW > LUDW ? VDW : LUDW));
     // ring depth: as deep as the register budget allows.  OCC = waves per SIMD (2: 256 registers per
     // wave, 1: 512); each query a wave serves takes (d_h + r) / 2 + 16 accumulator registers from it.
@@ -135,12 +149,13 @@ struct Cfg {
     }
     static constexpr int NSLOT = pick_slots();
     static constexpr int QROW = D + 8;                  // bf16 per q row in LDS (16 B pad)
-    static constexpr int PROW = R + 4;                  // floats per p row in LDS
+    // floats per p row in LDS: 8 slices of LDL high and LDL low pairs (matrix-core dot path), or R floats
+    static constexpr int PROW = (EPL >= 2 ? 16 * LDL : R) + 4;
     static constexpr int VTS = kRows + 4;               // bf16 per V^T row in LDS (72 B: conflict-free reads)
     static constexpr int XS = 36;                       // floats per exchange row (32 rows + alpha + pad)
     static constexpr int REC = ((D + R + 2) + 3) & ~3;
     static constexpr int Q_BYTES = QW * NHG * 16 * QROW * 2;        // q rows of each query, head-group padded
-    static constexpr int P_BYTES = ((QW * H * PROW * 4) + 15) & ~15;
+    static constexpr int P_BYTES = ((QW * HS * PROW * 4) + 15) & ~15;
     static constexpr int MW_BYTES = kWaves * 16 * 4;
     static constexpr int VT_BYTES = ((D * VTS * 2) + 15) & ~15;
     static constexpr int X_BYTES = QW * 16 * XS * 4;                   // one exchange area per query
@@ -149,7 +164,11 @@ struct Cfg {
     static constexpr int MERGE_BYTES = H * REC * 4;
     static_assert(MERGE_BYTES <= kWaves * WAVE_BYTES, "merge area must fit in the per-wave tiles");
     static_assert(NU % NSLOT == 0, "ring must divide the unit sequence");
-    static_assert(H % 8 == 0 && H <= 32, "head count");
+    static_assert(H % 2 == 0 && H <= 32 && (H % 8 == 0 || GEN), "head count");
+    // general form: the windows of lanes 0..6 end inside their head's coordinates or the next head's, never past
+    // the row (the last lane's window ends at its head's end), and the last lane has coordinates of its own
+    static_assert(!GEN || (EPL >= 2 && 6 * EPL + 2 * LDL <= R && TAIL >= 1 && 2 * LDL >= TAIL + (R % 2)),
+                  "latent windows");
     static_assert(QW == 1 || QW == 2 || QW == 4, "queries per wave");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
@@ -189,12 +208,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// General form: the latent window of lane sl of a real head h (its first coordinate, its element offset in the
+// row, the window position of that coordinate, the number of its coordinates); see Cfg.
+struct LatWindow {
+    int first, start, off, own;
+};
+template <int R, int EPL, int LDL>
+__device__ __forceinline__ LatWindow lat_window(int h, int sl) {
+    LatWindow w;
+    if (sl < 7) {
+        w.first = sl * EPL;
+        w.own = EPL;
+        const int e0 = h * R + w.first;
+        w.start = e0 & ~1;
+        w.off = e0 & 1;
+    } else {
+        w.first = 7 * EPL;
+        w.own = R - 7 * EPL;
+        int end = (h + 1) * R;
+        end += end & 1;
+        w.start = end - 2 * LDL;
+        w.off = h * R + w.first - w.start;
+    }
+    return w;
+}
+
 template <int D, int R, int H, int OCC, bool NORM, int QW, bool NTL>
 __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs a) {
     using C = Cfg<D, R, H, OCC, QW>;
     static_assert(!(NORM && QW > 1), "the normalised variant serves one query per sequence");
-    constexpr int EPL = C::EPL, LDW = C::LDW, OCTS = C::OCTS, NU = C::NU, NSLOT = C::NSLOT, SDW = C::SLOT_DW;
-    constexpr bool kDot2 = (EPL % 2 == 0) && EPL > 0;  // private score on v_dot2 (p split into bf16 hi + lo)
+    constexpr int EPL = C::EPL, LDW = C::LDW, LDL = C::LDL, OCTS = C::OCTS, NU = C::NU, NSLOT = C::NSLOT,
+                  SDW = C::SLOT_DW, HS = C::HS, NPOS = C::NPOS;
+    constexpr bool kDot2 = EPL >= 2;  // private score on v_dot2 (p split into bf16 hi + lo)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     uint16_t* q_lds = (uint16_t*)lds;
     uint32_t* p_lds = (uint32_t*)(lds + C::Q_BYTES);
@@ -245,7 +290,28 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     }
     if constexpr (R > 0) {
         const float* pg = a.p + (size_t)q_row0 * H * R;
-        if constexpr (kDot2) {
+        if constexpr (C::GEN) {
+            // per (query, head slot) and lane: LDL pairs of high parts, then LDL of low parts, in the order of the
+            // lane's latent window (position j holds p of coordinate first + j - off, or 0 where the position is
+            // not one of the lane's coordinates, or the slot is a padding head or query)
+            for (int i = tid; i < QW * HS * 8 * LDL; i += kWaves * 64) {
+                const int h = i / (8 * LDL), rem = i - h * (8 * LDL);
+                const int slice = rem / LDL, t = rem - slice * LDL;
+                const int qi = h / HS, hl = h - qi * HS;
+                const bool live = hl < H && (QW == 1 || qi < nreal);
+                const LatWindow lw = lat_window<R, EPL, LDL>(live ? hl : 0, slice);
+                const int j0 = 2 * t - lw.off, j1 = j0 + 1;  // the positions' coordinates within the lane's own
+                const bool ok0 = live && j0 >= 0 && j0 < lw.own, ok1 = live && j1 >= 0 && j1 < lw.own;
+                const float* prow = pg + (size_t)(qi * H + (live ? hl : 0)) * R + lw.first;
+                const float x0 = ok0 ? prow[j0] : 0.f, x1 = ok1 ? prow[j1] : 0.f;
+                const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                const uint32_t l0 = f32_to_bf16_bits(x0 - __uint_as_float(h0 << 16));
+                const uint32_t l1 = f32_to_bf16_bits(x1 - __uint_as_float(h1 << 16));
+                uint32_t* row = p_lds + h * C::PROW + slice * 2 * LDL;
+                row[t] = h0 | (h1 << 16);
+                row[LDL + t] = l0 | (l1 << 16);
+            }
+        } else if constexpr (kDot2) {
             // per head and r-slice of EPL coordinates: EPL/2 pairs of high parts, then EPL/2 of low parts
             for (int i = tid; i < QW * H * (R / 2); i += kWaves * 64) {
                 const int h = i / (R / 2), pr = i - h * (R / 2);  // pair index within the (query, head) row
@@ -276,7 +342,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     const float scale = kLog2e / sqrtf((float)D);
 
     f32x4_t acc_sh[QW][C::CB];
-    float acc_pr[QW][OCTS][EPL > 0 ? EPL : 1];
+    float acc_pr[QW][OCTS][NPOS > 0 ? NPOS : 1];
     float m_run[QW], l_run[QW];
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
@@ -287,7 +353,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
 #pragma unroll
         for (int o = 0; o < OCTS; ++o)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc_pr[qi][o][e] = 0.f;
+            for (int e = 0; e < NPOS; ++e) acc_pr[qi][o][e] = 0.f;
     }
 
     // ---- buffer descriptors of this sequence and fixed per-lane byte offsets ----
@@ -302,11 +368,31 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc((const uint16_t*)a.v_shared + seq_rows * D, n_rows * row_bytes_sh);
     __amdgpu_buffer_rsrc_t rs_zk = rs_k, rs_zv = rs_v;
     uint32_t vo_zv = 0;  // lane offset of (head 16*hg + hh, coordinate slice sl) in the latent tensors
+    // general form: the lane's window offset in a latent row per octet (a padding head slot gets an offset out
+    // of every descriptor's range, so its loads return zeros and touch no memory), and per-pair masks that keep
+    // the lane's own coordinates of the window
+    uint32_t vo_oct[OCTS];
+    uint32_t lat_mask[LDL > 0 ? LDL : 1];
     if constexpr (R > 0) {
         const uint32_t lat_bytes = n_rows * row_bytes_lat;
         rs_zk = buf_rsrc((const uint16_t*)a.z_k + seq_rows * H * R, lat_bytes);
         rs_zv = buf_rsrc((const uint16_t*)a.z_v + seq_rows * H * R, lat_bytes);
-        vo_zv = (uint32_t)(16 * hg + hh) * R * 2 + sl * EPL * 2;
+        if constexpr (C::GEN) {
+#pragma unroll
+            for (int oi = 0; oi < OCTS; ++oi) {
+                const int h = 16 * hg + 8 * oi + hh;
+                vo_oct[oi] = (h < H) ? (uint32_t)lat_window<R, EPL, LDL>(h, sl).start * 2 : 0x80000000u;
+            }
+            // a lane's window positions depend on its head only through the parity of head * R
+            const LatWindow lw = lat_window<R, EPL, LDL>(hh & 1, sl);
+#pragma unroll
+            for (int t = 0; t < LDL; ++t) {
+                const int j0 = 2 * t - lw.off, j1 = j0 + 1;
+                lat_mask[t] = ((j0 >= 0 && j0 < lw.own) ? 0x0000ffffu : 0u) | ((j1 >= 0 && j1 < lw.own) ? 0xffff0000u : 0u);
+            }
+        } else {
+            vo_zv = (uint32_t)(16 * hg + hh) * R * 2 + sl * EPL * 2;
+        }
     }
     const uint32_t vo_kf = (uint32_t)n16 * row_bytes_sh + 16 * g4;              // key fragment rows n16, 16 + n16
     const uint32_t vo_vt = (uint32_t)(4 * srow) * row_bytes_sh + 16 * schunk;  // value tile rows 4*srow + 0..3
@@ -363,24 +449,25 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             const int v = u - 2;
             const int phase = v / (4 * OCTS);
             const int oi = (v % (4 * OCTS)) / 4, sub = v % 4;
-            const int so = pr * (int)row_bytes_lat + oi * (int)oct_bytes;
+            // general form: the octet is in the lane's window offset; plain form: in the scalar offset
+            const int so = pr * (int)row_bytes_lat + (C::GEN ? 0 : oi * (int)oct_bytes);
             const __amdgpu_buffer_rsrc_t rs = !live ? rs_none : (phase == 0) ? rs_zk : rs_zv;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 // one instruction reads row 8*sub + k of 8 consecutive heads: 8*r*2 contiguous bytes
-                const uint32_t vo = vo_zv + (k + 8 * sub) * row_bytes_lat;
-                if constexpr (EPL == 8) {
+                const uint32_t vo = (C::GEN ? vo_oct[oi] : vo_zv) + (k + 8 * sub) * row_bytes_lat;
+                if constexpr (LDL == 4) {
                     const v4u_t w = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNTLat<NTL>);
                     ring[slot][4 * k] = w.x;
                     ring[slot][4 * k + 1] = w.y;
                     ring[slot][4 * k + 2] = w.z;
                     ring[slot][4 * k + 3] = w.w;
-                } else if constexpr (EPL == 6) {
+                } else if constexpr (LDL == 3) {
                     const v3u_t w = __builtin_amdgcn_raw_buffer_load_b96(rs, vo, so, kNTLat<NTL>);
                     ring[slot][3 * k] = w.x;
                     ring[slot][3 * k + 1] = w.y;
                     ring[slot][3 * k + 2] = w.z;
-                } else if constexpr (EPL == 4) {
+                } else if constexpr (LDL == 2) {
                     const v2u_t w = __builtin_amdgcn_raw_buffer_load_b64(rs, vo, so, kNTLat<NTL>);
                     ring[slot][2 * k] = w.x;
                     ring[slot][2 * k + 1] = w.y;
@@ -511,20 +598,24 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 if (phase == 0) {
 #pragma unroll
                     for (int qi = 0; qi < QW; ++qi) {  // every query against the same latent registers
-                        uint32_t pw[EPL];
+                        constexpr int NPW = kDot2 ? 2 * LDL : EPL;  // p dwords of a lane slice
+                        uint32_t pw[NPW];
 #pragma unroll
-                        for (int e = 0; e < EPL; ++e)
-                            pw[e] = p_lds[(qi * H + 16 * hg + 8 * oi + hh) * C::PROW + sl * EPL + e];
+                        for (int e = 0; e < NPW; ++e)
+                            pw[e] = p_lds[(qi * HS + 16 * hg + 8 * oi + hh) * C::PROW + sl * NPW + e];
                         float part[8];
 #pragma unroll
                         for (int k = 0; k < 8; ++k) {
                             float acc = 0.f;
                             if constexpr (kDot2) {
 #pragma unroll
-                                for (int pr = 0; pr < EPL / 2; ++pr) {
-                                    const uint32_t z = cur[LDW * k + pr];
-                                    acc = dot2_bf16(z, pw[EPL / 2 + pr], acc);  // low parts of p
-                                    acc = dot2_bf16(z, pw[pr], acc);            // high parts of p
+                                for (int pr = 0; pr < LDL; ++pr) {
+                                    uint32_t z = cur[LDL * k + pr];
+                                    // window positions that are not the lane's coordinates (a neighbouring lane's
+                                    // or head's values) have p = 0 but are zeroed too: nothing there is assumed
+                                    if constexpr (C::GEN) z &= lat_mask[pr];
+                                    acc = dot2_bf16(z, pw[LDL + pr], acc);  // low parts of p
+                                    acc = dot2_bf16(z, pw[pr], acc);        // high parts of p
                                 }
                             } else {
 #pragma unroll
@@ -560,7 +651,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                         for (int qi = 0; qi < QW; ++qi) {
                             const float al = xb[(qi * 16 + 8 * oi + hh) * C::XS + 32];
 #pragma unroll
-                            for (int e = 0; e < EPL; ++e) acc_pr[qi][oi][e] *= al;
+                            for (int e = 0; e < NPOS; ++e) acc_pr[qi][oi][e] *= al;
                         }
                     }
                     f32x4_t e0[QW], e1[QW];
@@ -575,8 +666,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                         // see are live rows of the sequence with weight 0)
                         if (8 * sub + k < nvalid) {
 #pragma unroll
-                            for (int e = 0; e < EPL; ++e) {
-                                const float z = lat_at(cur + LDW * k, e);
+                            for (int e = 0; e < NPOS; ++e) {
+                                const float z = lat_at(cur + LDL * k, e);
 #pragma unroll
                                 for (int qi = 0; qi < QW; ++qi)
                                     acc_pr[qi][oi][e] = fmaf((k < 4) ? e0[qi][k] : e1[qi][k - 4], z, acc_pr[qi][oi][e]);
@@ -709,13 +800,20 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 }
             }
             if (tl == t) {
+                // general form: window position j holds coordinate first + j - off of the lane's own
+                LatWindow lw{sl * EPL, 0, 0, EPL};
+                if constexpr (C::GEN) lw = lat_window<R, EPL, LDL>(hh & 1, sl);
 #pragma unroll
                 for (int oi = 0; oi < OCTS; ++oi) {
-                    float* row = mg + (16 * hg + 8 * oi + hh) * C::REC + D + sl * EPL;
+                    const int hs = 16 * hg + 8 * oi + hh;
+                    if (C::GEN && hs >= H) continue;  // padding head slot
+                    float* row = mg + hs * C::REC + D + lw.first;
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) {
+                    for (int e = 0; e < NPOS; ++e) {
+                        if (C::GEN && (e < lw.off || e >= lw.off + lw.own)) continue;  // not the lane's coordinate
                         const float v = acc_pr[qi][oi][e] * fpr[oi];
-                        row[e] = (t == 0) ? v : row[e] + v;
+                        const int c = e - lw.off;
+                        row[c] = (t == 0) ? v : row[c] + v;
                     }
                 }
             }

@@ -151,7 +151,8 @@ bool plan_split(const lrkv_dims& d, int max_len, lrkv::SplitPlan* out, PlanVaria
         if (variant == PlanVariant::kRope && rope_mfma_path_supports(d.H, d.d_h, d.r, d.dtype)) {
             p.path = SplitPath::kRopeMfma;
             p.chunk = rope_mfma_rows_per_tile();
-        } else if (variant != PlanVariant::kRope && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+        } else if (variant != PlanVariant::kRope && mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap) &&
+                   mfma_all_variants(d.H, d.d_h, d.r)) {
             p.path = SplitPath::kMfmaBf16;
             p.chunk = mfma_rows_per_tile(d.H);
         } else if (variant == PlanVariant::kRope ? general_lds_bytes(d.H, d.d_h, d.r, true) <= 160 * 1024 &&
@@ -525,7 +526,8 @@ struct MultiPlan {
 bool plan_multi(const lrkv_dims& d, int Q, int max_len, MultiPlan* mp) {
     if (Q < 1 || Q > 64 || (long long)d.batch * Q > 65535) return false;
     int qw = 1;
-    if (Q > 1 && lrkv::mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap)) {
+    if (Q > 1 && lrkv::mfma_path_supports(d.H, d.d_h, d.r, d.dtype, d.L_cap) &&
+        lrkv::mfma_all_variants(d.H, d.d_h, d.r)) {
         const int qmax = lrkv::mfma_max_query_width(d.H, d.d_h, d.r);
         qw = env_int("LRKV_MULTI_QW", Q == 2 ? 2 : qmax);
         if (qw != 1 && qw != 2 && qw != 4) qw = qmax;

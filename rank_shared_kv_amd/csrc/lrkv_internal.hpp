@@ -60,6 +60,7 @@ struct SplitPlan {
 };
 
 bool mfma_path_supports(int H, int d_h, int r, int dtype, int L_cap);      // bf16 MFMA kernel
+bool mfma_all_variants(int H, int d_h, int r);  // its normalised and several-query instances exist for the shape
 bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap);  // fp32 MFMA kernel (r = 0)
 int mfma_f32_rows_per_tile();  // rows one fp32 MFMA-kernel split advances per step
 int mfma_rows_per_tile(int H);  // rows one MFMA-kernel workgroup advances per step

@@ -174,6 +174,12 @@ WORKLOADS: Dict[str, Workload] = {
     # the same length draw with r = 0 (MQA-style sharing), fp32 values
     "ragged_mqa_fp32": Workload("ragged_mqa_fp32", 5, batch=64, H=32, d_h=128, r=0, L=32768, dtype="f32",
                                 ragged_lo=512, length_wid=4),
+    # the layer shapes of the reading notes' model table (d_h 128 with the ranks of its Table 7), at the
+    # pages' longer training context of 8192 tokens, 16 sequences
+    "model_128m": Workload("model_128m", 6, batch=16, H=6, d_h=128, r=46, L=8192, dtype="bf16"),
+    "model_1p2b": Workload("model_1p2b", 7, batch=16, H=12, d_h=128, r=51, L=8192, dtype="bf16"),
+    "model_2p5b": Workload("model_2p5b", 8, batch=16, H=18, d_h=128, r=55, L=8192, dtype="bf16"),
+    "model_6p3b": Workload("model_6p3b", 9, batch=16, H=32, d_h=128, r=54, L=8192, dtype="bf16"),
 }
 
 
