@@ -490,7 +490,12 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     if (nmine > 0) {
         const int pr_first = paged_row(a, bc, kRows * (first_blk + rot * step_blk));
 #pragma unroll
-        for (int u = 0; u < NSLOT - 1; ++u) issue(u, pr_first, u, true);
+        for (int u = 0; u < NSLOT - 1; ++u) {
+            issue(u, pr_first, u, true);
+            // in unit order, as the loop issues them: the wait counts at the loop head then hold for both ways
+            // into it (scheduled freely, the loads forced waits that left less than half the ring in flight)
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
 #if LRKV_LOCKSTEP

@@ -114,13 +114,16 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     //   u = 4..7  value half (u-4)/2, rows 4 g4 + tt with tt in {2 ((u-4)%2), 2 ((u-4)%2) + 1}
     constexpr int KH = C::KLD / 2;
     uint32_t ring[NSLOT][UDW];
-    auto issue = [&](int u, int t0, int slot) {
+    // a descriptor of no bytes: loads through it are out of range, return zeros and touch no memory (the
+    // prefetch issued during a row lane's last block, which has no next block)
+    const __amdgpu_buffer_rsrc_t rs_none = buf_rsrc(a.k_shared, 0);
+    auto issue = [&](int u, int t0, int slot, bool live) {
         if (u < 4) {
             const int so = (t0 + 16 * (u >> 1)) * (int)row_bytes;
 #pragma unroll
             for (int mm = 0; mm < KH; ++mm) {
                 const int m = KH * (u & 1) + mm;
-                const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(rs_k, vo_k + 64 * m, so, 0);
+                const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(live ? rs_k : rs_none, vo_k + 64 * m, so, 0);
                 ring[slot][4 * mm] = v.x;
                 ring[slot][4 * mm + 1] = v.y;
                 ring[slot][4 * mm + 2] = v.z;
@@ -133,8 +136,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
                 const int tt = 2 * ((u - 4) & 1) + k;
 #pragma unroll
                 for (int p = 0; p < C::VP; ++p) {
-                    const v4u_t v =
-                        __builtin_amdgcn_raw_buffer_load_b128(rs_v, vo_v + tt * row_bytes + 256 * p, so, kNTValue);
+                    const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(live ? rs_v : rs_none,
+                                                                          vo_v + tt * row_bytes + 256 * p, so, kNTValue);
                     const int o = 4 * (k * C::VP + p);
                     ring[slot][o] = v.x;
                     ring[slot][o + 1] = v.y;
@@ -163,7 +166,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     const int rot = (int)(((long)nmine * bc) / (a.batch / a.qgroup));
     if (nmine > 0) {
 #pragma unroll
-        for (int u = 0; u < NSLOT - 1; ++u) issue(u, kRows * (first_blk + rot * step_blk), u);
+        for (int u = 0; u < NSLOT - 1; ++u) {
+            issue(u, kRows * (first_blk + rot * step_blk), u, true);
+            __builtin_amdgcn_sched_barrier(0);  // in unit order, as the loop issues them
+        }
     }
 
     for (int it = 0; it < nmine; ++it) {
@@ -172,7 +178,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
         const int t0 = kRows * (first_blk + itr * step_blk);
         const int nvalid = min(kRows, Lb - t0);
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
-        const int t0_pf = (it + 1 < nmine) ? kRows * (first_blk + itn * step_blk) : t0;
+        const bool pf_live = it + 1 < nmine;  // the last block prefetches nothing (the empty descriptor)
+        const int t0_pf = pf_live ? kRows * (first_blk + itn * step_blk) : t0;
         constexpr int NCH = (NHG == 1) ? 2 : 1;
         f32x4_t s_sh[NHG][2], s_acc[NHG][NCH];
         float ev[NHG][8];
@@ -181,8 +188,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
         for (int u = 0; u < NU; ++u) {
             {
                 const int un = u + NSLOT - 1;
-                if (un < NU) issue(un, t0, un % NSLOT);
-                else issue(un - NU, t0_pf, un % NSLOT);
+                if (un < NU) issue(un, t0, un % NSLOT, true);
+                else issue(un - NU, t0_pf, un % NSLOT, pf_live);
             }
             __builtin_amdgcn_sched_barrier(0);
             uint32_t* cur = ring[u % NSLOT];
