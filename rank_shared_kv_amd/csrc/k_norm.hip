@@ -15,12 +15,14 @@
 // kernel does), the shared row is added and the squares accumulated; the four
 // lanes that hold one row's columns then sum in a fixed order.  The keys
 // themselves are never written.  With d_h = 64 or 128 (key_scales_rows_kernel)
-// the four waves of a workgroup take four heads of the same 256 rows, in chunks
-// of 64 whose shared rows the workgroup stages in LDS; each wave fetches its
-// B_h fragments once, and the next chunk's loads are in flight while a chunk
+// the eight waves of a workgroup take eight heads of the same rows (up to 1024), in
+// chunks of 64 whose shared rows the workgroup stages in LDS; each wave fetches
+// its B_h fragments once, and the next chunk's loads are in flight while a chunk
 // computes.  Other d_h (key_scales_mfma_kernel) take a wave per 16 rows.  Other
 // shapes: one thread per (row, head).
 #include <algorithm>
+#include <cstdlib>
+#include <type_traits>
 
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
@@ -89,14 +91,17 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_mfma_kernel(int H, int
 }
 
 constexpr int kChunkRows = 64;  // rows per chunk in the d_h = 64 / 128 kernel
-constexpr int kChunks = 4;      // chunks per workgroup: 256 rows, one B^K_h fetch per wave
+constexpr int kRowWaves = 8;    // waves (heads) per workgroup in the d_h = 64 / 128 kernel
 
-// rows max(0, L_b - n_last) .. L_b - 1 of sequence b; heads 4 y .. 4 y + 3 in the workgroup's waves.  The
-// workgroup walks 4 chunks of 64 rows (past L_b: stand-ins, computed, not stored); each wave loads its
+// rows max(0, L_b - n_last) .. L_b - 1 of sequence b; heads 8 y .. 8 y + 7 in the workgroup's waves.  The
+// workgroup walks CH chunks of 64 rows (past L_b: stand-ins, computed, not stored); each wave loads its
 // head's B^K_h fragments once.  The chunk's shared rows are staged in LDS by the whole workgroup (two
-// buffers: the next chunk's rows and latents load while the current chunk computes).
-template <int D, int NKS>
-__global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int R, int L_cap, int max_len, int n_last,
+// buffers: the next chunk's rows and latents load while the current chunk computes).  Every byte read
+// through the L1 caches costs about as much as one from memory here (measured: the kernel moved 1.08 GB
+// through them for 579 MB of data when 4 heads shared a chunk and B^K_h was fetched per 256 rows), so
+// eight heads share each staged chunk and B^K_h serves CH * 64 rows.
+template <int D, int NKS, int CH>
+__global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, int R, int L_cap, int max_len, int n_last,
                                                                       float eps, const int32_t* __restrict__ seq_lens,
                                                                       const uint16_t* __restrict__ shared,
                                                                       const uint16_t* __restrict__ z,
@@ -104,15 +109,15 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
                                                                       uint16_t* __restrict__ rho) {
     constexpr int CB = D / 16;
     constexpr int SROW = D + 8;                               // bf16 per staged shared row
-    constexpr int PPT = kChunkRows * (D / 8) / (kWaves * 64);  // 16-byte pieces of a chunk per thread
+    constexpr int PPT = kChunkRows * (D / 8) / (kRowWaves * 64);  // 16-byte pieces of a chunk per thread
     __shared__ __attribute__((aligned(16))) uint16_t sh_l[2][kChunkRows * SROW];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
-    const int h = blockIdx.y * kWaves + wave, b = blockIdx.z;
+    const int h = blockIdx.y * kRowWaves + wave, b = blockIdx.z;
     const int hc = min(h, H - 1);  // waves past the last head compute a stand-in and store nothing
     const int Lb = clamped_len(seq_lens, b, max_len);
     const int start = max(0, Lb - n_last);
-    const int r0 = start + blockIdx.x * kChunkRows * kChunks;
+    const int r0 = start + blockIdx.x * kChunkRows * CH;
     if (r0 >= Lb) return;  // the whole workgroup
     const uint16_t* bh = basis + (size_t)hc * D * R;
     typedef u32x4_t ZFrag[4][NKS];
@@ -130,7 +135,7 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
     auto load_sh = [&](u32x4_t (&v)[PPT], int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int p = tid + kWaves * 64 * i;
+            const int p = tid + kRowWaves * 64 * i;
             const size_t row = (size_t)min(r0 + kChunkRows * c + p / (D / 8), Lb - 1);
             v[i] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + row) * D + 8 * (p % (D / 8)));
         }
@@ -138,7 +143,7 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
     auto store_sh = [&](const u32x4_t (&v)[PPT], int buf) {
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
-            const int p = tid + kWaves * 64 * i;
+            const int p = tid + kRowWaves * 64 * i;
             *(u32x4_t*)(sh_l[buf] + (p / (D / 8)) * SROW + 8 * (p % (D / 8))) = v[i];
         }
     };
@@ -170,11 +175,9 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
         }
     store_sh(sv, 0);
     __syncthreads();
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        ZFrag& zc = (c & 1) ? zb : za;
-        ZFrag& zn = (c & 1) ? za : zb;
-        if (c + 1 < kChunks) {  // the next chunk's loads first
+    // one chunk: the next chunk's loads first, then this one's keys; false once no later chunk holds a live row
+    auto chunk = [&](ZFrag& zc, ZFrag& zn, int c) -> bool {
+        if (c + 1 < CH) {
             load_sh(sv, c + 1);
             load_z(zn, c + 1);
         }
@@ -205,10 +208,15 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_rows_kernel(int H, int
             if (g4 == 0 && h < H && row < Lb)
                 rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
         }
-        if (c + 1 < kChunks) {
-            store_sh(sv, (c + 1) & 1);  // that buffer's chunk finished before the previous barrier
-            __syncthreads();
-        }
+        if (c + 1 >= CH) return false;
+        store_sh(sv, (c + 1) & 1);  // that buffer's chunk finished before the previous barrier
+        __syncthreads();
+        return r0 + kChunkRows * (c + 1) < Lb;  // (workgroup-uniform)
+    };
+    // chunks in pairs, so the two latent fragment sets keep fixed roles
+    for (int c = 0; c < CH; c += 2) {
+        if (!chunk(za, zb, c)) break;
+        if (!chunk(zb, za, c + 1)) break;
     }
 }
 
@@ -270,10 +278,26 @@ hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dt
     const int n_rows = std::min(n_last, max_len);
     if (n_rows <= 0) return hipSuccess;
     if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64) {
-        dim3 grid((n_rows + kChunkRows * kChunks - 1) / (kChunkRows * kChunks), (H + kWaves - 1) / kWaves, batch);
-        auto kern = (d_h == 64) ? (r <= 32 ? key_scales_rows_kernel<64, 1> : key_scales_rows_kernel<64, 2>)
-                                : (r <= 32 ? key_scales_rows_kernel<128, 1> : key_scales_rows_kernel<128, 2>);
-        hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, stream, H, r, L_cap, max_len, n_last, eps, seq_lens,
+        // chunks of 64 rows per workgroup: B^K_h serves that many rows; a long history takes 16 (1024 rows;
+        // long context, whole history: 177 us, against 182 with 8, 202 with 4), a short pass (an append's
+        // single row) 1; LRKV_KS_CHUNKS overrides (tuning, read at every call)
+        int ch = n_rows >= 8192 ? 16 : n_rows >= 4096 ? 8 : n_rows >= 1024 ? 4 : 1;
+        if (const char* e = getenv("LRKV_KS_CHUNKS")) ch = atoi(e);
+        ch = (ch >= 16) ? 16 : (ch >= 8) ? 8 : (ch >= 4) ? 4 : 1;
+        dim3 grid((n_rows + kChunkRows * ch - 1) / (kChunkRows * ch), (H + kRowWaves - 1) / kRowWaves, batch);
+        auto pick = [&](auto d_tag, auto k_tag) {
+            constexpr int DD = decltype(d_tag)::value, KK = decltype(k_tag)::value;
+            return ch == 16 ? key_scales_rows_kernel<DD, KK, 16>
+                   : ch == 8 ? key_scales_rows_kernel<DD, KK, 8>
+                   : ch == 4 ? key_scales_rows_kernel<DD, KK, 4> : key_scales_rows_kernel<DD, KK, 1>;
+        };
+        using I64 = std::integral_constant<int, 64>;
+        using I128 = std::integral_constant<int, 128>;
+        using K1 = std::integral_constant<int, 1>;
+        using K2 = std::integral_constant<int, 2>;
+        auto kern = (d_h == 64) ? (r <= 32 ? pick(I64{}, K1{}) : pick(I64{}, K2{}))
+                                : (r <= 32 ? pick(I128{}, K1{}) : pick(I128{}, K2{}));
+        hipLaunchKernelGGL(kern, grid, dim3(kRowWaves * 64), 0, stream, H, r, L_cap, max_len, n_last, eps, seq_lens,
                            (const uint16_t*)k_shared, (const uint16_t*)z_k, (const uint16_t*)B_k, (uint16_t*)rho);
     } else if (dtype == 1 && d_h % 16 == 0 && r % 8 == 0 && r > 0 && r <= 64) {
         dim3 grid((n_rows + 16 * kWaves - 1) / (16 * kWaves), H, batch);
