@@ -57,8 +57,9 @@ def launch_config(w, steps: int, capacity: int = 0):
 
 
 # the sources that determine the bf16 split kernel's code and launch configuration
-SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hpp", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma.hip",
-                        "k_decode_mfma_f32.hip", "lrkv_device.hpp", "lrkv_internal.hpp", "lrkv_api.cpp")
+SPLIT_KERNEL_SOURCES = ("k_decode_mfma.hpp", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma_part_d128_s.hip",
+                        "k_decode_mfma.hip", "k_decode_mfma_f32.hip", "lrkv_device.hpp", "lrkv_internal.hpp",
+                        "lrkv_step.hpp", "k_cache.hip", "k_merge.hip", "lrkv_api.cpp")
 
 
 def kernel_sources_digest() -> str:
@@ -70,14 +71,15 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, launch_bytes: float):
-    """HBM traffic per split launch from the committed rocprofv3 counter summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_hbm_counters.md")
+def read_traffic(workload: str, launch_bytes: float, kind: str = "split"):
+    """HBM traffic per launch of the dominant kernel (kind "split": the split pass; "step": the fused decode
+    step) from the committed rocprofv3 counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_kernel_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_digest = re.search(r"kernel sources digest:\s*`?([0-9a-f]{16})", text)
-    m_bytes = re.search(r"HBM bytes per split launch \(scaled\):\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(r"HBM bytes per " + kind + r" launch \(scaled\):\s*([0-9.eE+]+)", text)
     if not m_digest or not m_bytes or m_digest.group(1) != kernel_sources_digest():
         return None
     return float(m_bytes.group(1))
@@ -93,19 +95,19 @@ def host_cores():
     return max(1, n)
 
 
-def read_sq_counters(workload: str):
+def read_sq_counters(workload: str, kind: str = "split"):
     """Matrix-core and VALU activity of the split kernel from the committed rocprofv3 counter summary, if it
     matches these sources: the counted bf16 MFMA FLOP, the matrix cores' busy fraction, and the fractions of
     wave time spent issuing VALU instructions and waiting."""
-    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_sq_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kind}_kernel_{workload}_sq_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_digest = re.search(r"kernel sources digest:\s*`?([0-9a-f]{16})", text)
     if not m_digest or m_digest.group(1) != kernel_sources_digest():
         return None
-    fields = {"mfma_flop_per_launch": r"bf16 MFMA FLOP per split launch \(counter\):\s*([0-9.eE+]+)",
-              "mfma_busy_frac": r"MFMA busy fraction of the split launch \(counter\):\s*([0-9.eE+-]+)",
+    fields = {"mfma_flop_per_launch": r"bf16 MFMA FLOP per " + kind + r" launch \(counter\):\s*([0-9.eE+]+)",
+              "mfma_busy_frac": r"MFMA busy fraction of the " + kind + r" launch \(counter\):\s*([0-9.eE+-]+)",
               "valu_issue_frac": r"VALU issue fraction of wave time:\s*([0-9.eE+-]+)",
               "wait_frac": r"Wait fraction of wave time:\s*([0-9.eE+-]+)"}
     out = {}
@@ -303,6 +305,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="independent layers decoded back to back per step, each with its own cache, query and "
                          "bases (default: the workload's layer count, 24 for mid_24layer; plain decode only)")
+    ap.add_argument("--separate", action="store_true",
+                    help="plain decode: time the step as three launches (append + absorb, split pass, merge) instead "
+                         "of the fused decode step")
     ap.add_argument("--no-stream-probe", action="store_true",
                     help="do not report the streaming-read probe (it still runs untimed before the timed steps, to "
                          "bring the GPU to its streaming state)")
@@ -378,6 +383,11 @@ def main():
     outs = [torch.empty((w.batch, w.H, w.d_h), dtype=torch.float32, device="cuda") for _ in devs]
     p, out = ps[0], outs[0]
     S, chunk = lk.lrkv_decode_num_splits(dims, max_len)
+    # plain decode: the whole step (append, absorb, split pass, merge) in one launch where the library fuses it
+    fused = plain and not args.separate and lk.lrkv_decode_step_fused(dims, max_len)
+    if fused:
+        nbytes_step = lk.lrkv_decode_step_workspace_bytes(dims, max_len)
+        ws_step = torch.zeros(nbytes_step // 4, dtype=torch.float32, device="cuda")  # counter words start at zero
     if Q > 1:
         nbytes = lk.lrkv_decode_multi_workspace_bytes(dims, Q, max_len)
         ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
@@ -500,10 +510,20 @@ def main():
             if w.r:
                 lk.lrkv_absorb_query(dims, q_use, dev["B_k"], p, stream)
         else:
-            # every layer in turn: the append and the query absorption in one launch, the split pass, the merge
-            # (the layers share the workspace: each merge has read it before the next split pass writes it)
+            # every layer in turn: the fused step (one launch), or the append and the query absorption in one
+            # launch, the split pass, the merge (the layers share the workspace: each layer's merge has read it
+            # before the next layer's split pass writes it)
             for d_l, c_l, p_l, o_l in zip(devs, caches, ps, outs):
                 pp_l = p_l if w.r else None
+                if fused:
+                    if timed:
+                        e0 = ev()
+                    lk.lrkv_decode_step(dims, c_l, max_len, rows["k_new"], rows["v_new"], zk_new, zv_new, d_l["q"],
+                                        d_l["B_k"] if w.r else None, d_l["B_v"] if w.r else None, pp_l, o_l, ws_step,
+                                        nbytes_step, stream)
+                    if timed:
+                        ev_pairs.append((e0, ev()))
+                    continue
                 lk.lrkv_append_absorb(dims, c_l, rows["k_new"], rows["v_new"], zk_new, zv_new, d_l["q"],
                                       d_l["B_k"] if w.r else None, pp_l, stream)
                 if timed:
@@ -583,12 +603,17 @@ def main():
         split_bytes += int(lens_full.max() + K) * w.d_h * 4 - p_bytes
     if Q > 1 or args.norm or args.paged or args.rope:  # the timed call is the whole decode (split + merge)
         split_bytes += out_bytes + w.H * w.d_h * w.r * s_bytes
+    if fused:  # the fused launch reads the cache, q and both bases, appends the new rows and writes out
+        new_row_bytes = w.batch * 2 * (w.d_h + w.H * w.r) * s_bytes
+        split_bytes = (sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes + 2 * new_row_bytes
+                       + 2 * p_bytes)
     split_avg_ms = sum(split_ms) / len(split_ms)
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K / n_layers)  # shared-key score tile per split launch
     mfma_util = flops_mfma / (split_avg_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
-    traffic = (read_traffic(w.name, split_bytes)
+    kind = "step" if fused else "split"
+    traffic = (read_traffic(w.name, split_bytes, kind)
                if not (args.layer or args.norm or args.paged or args.rope) and Q == 1 else None)
     layer = None
     if args.layer:
@@ -607,7 +632,7 @@ def main():
         log(f"bench: layer step: project+append {proj_us:.1f} us ({layer['project_weight_gbps']:.0f} GB/s of "
             f"weights), output projection {outp_us:.1f} us ({layer['output_weight_gbps']:.0f} GB/s)")
     log(f"bench: {K} steps in {total_ms:.3f} ms ({total_ms / K:.4f} ms/step; {total_ms_events / K:.4f} with events); "
-        f"{'split pass' if Q == 1 and not (args.norm or args.paged or args.rope) else 'whole decode call'} "
+        f"{'fused step' if fused else 'split pass' if Q == 1 and not (args.norm or args.paged or args.rope) else 'whole decode call'} "
         f"{split_avg_ms * 1e3:.1f} us "
         f"avg = {split_gbps:.0f} GB/s ({100 * split_gbps / HBM_PEAK_GBPS:.1f}% of peak); splits={S} chunk={chunk}")
 
@@ -653,7 +678,8 @@ def main():
                    + (f"+paged{args.paged}" if args.paged else "") + ("+rope" if args.rope else ""), "batch": w.batch, "H": w.H, "d_h": w.d_h, "r": w.r,
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
-                   "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q, "layers": n_layers},
+                   "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q, "layers": n_layers,
+                   "step_launches": 1 if fused else None},
         "hbm_gbps_step": step_gbps,
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -661,17 +687,19 @@ def main():
                      "traffic": traffic, "kernel": "lrkv_decode_multi (split pass + merge)" if Q > 1 else
                      "lrkv_decode_normed (split pass + merge)" if args.norm else
                      "lrkv_decode_paged (split pass + merge)" if args.paged else
-                     "lrkv_decode_rope (split pass + merge)" if args.rope else "split pass (lrkv_decode_partial)",
+                     "lrkv_decode_rope (split pass + merge)" if args.rope else
+                     "fused decode step (lrkv_decode_step: append, absorb, split pass and merge in one launch)"
+                     if fused else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3,
                      "timing": f"HIP events around each of the {K * n_layers} decode launches of a second pass "
                                "over the same steps (the step time comes from a pass without them)",
                      "stream_read_gbps": stream_gbps,
                      "frac_of_stream_read": (split_gbps / stream_gbps) if stream_gbps else None},
         "mfma_util_shared_score": mfma_util,
-        "mfma_counters": (dict(read_sq_counters(w.name), note="rocprofv3 counters of the split kernel on this "
-                               "workload; the shared-score figure above is 2 d_h FLOP per cached token-head over "
-                               "the live launch time, the counted FLOP include the value products (3x)")
-                          if plain and read_sq_counters(w.name) else None),
+        "mfma_counters": (dict(read_sq_counters(w.name, kind), note=f"rocprofv3 counters of the {kind} kernel on "
+                               "this workload; the shared-score figure above is 2 d_h FLOP per cached token-head "
+                               "over the live launch time, the counted FLOP include the value products (3x)")
+                          if plain and read_sq_counters(w.name, kind) else None),
         "layer_step": layer,
         "cpu_baseline": cpu,
     }

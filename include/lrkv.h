@@ -213,6 +213,42 @@ lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, 
 lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
                               float* out, const void* workspace, size_t workspace_bytes, void* stream);
 
+/* A whole decode step in one launch: lrkv_append_absorb(dims, cache, k_new,
+ * v_new, zk_new, zv_new, q, B_k, p) followed by lrkv_decode(dims, cache,
+ * max_len, q, p, B_v, out), with the same arguments, layouts and results, bit
+ * for bit (p and out written, the token appended, seq_lens advanced) -- the
+ * per-token work of Algorithms 1 and 2 and the fused online-softmax decode of
+ * the review's sec. 3 (reading notes secs. 2.3-2.4, Eqs. (6)-(7)).  On the bf16
+ * matrix-core shapes the launch holds three kinds of workgroups: absorb
+ * workgroups (p = q B^K), the decode's split workgroups (each sequence seen
+ * with the appended token; the workgroup that reads the token's rows writes
+ * them into the cache first) and merge workgroups, which start as soon as
+ * every split of their sequence is done.  They hand work on through counters
+ * in the workspace, each waiting only for workgroups placed before it in the
+ * launch, so the absorb and the merge run beside the splits instead of in
+ * launches of their own.  Other shapes run the two calls one after the other.
+ *   max_len    bound of the lengths after the append (as for lrkv_decode)
+ *   workspace  device, >= lrkv_decode_step_workspace_bytes(dims, max_len) bytes,
+ *              256-byte aligned; the split records, then the step's counter
+ *              words from byte offset lrkv_decode_step_sync_offset(dims,
+ *              max_len).  The counter words must be zero before the first
+ *              call (zero the whole workspace once after allocating it); every
+ *              call leaves them zero, so one workspace serves any number of
+ *              calls, including replays of a captured graph.  The word at
+ *              sync offset + 4 counts waits that ran out of their bound (never
+ *              in correct operation; the results of such a call are not
+ *              valid); it is not cleared by the library.
+ * Calls that overlap in time on one workspace race. */
+size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
+size_t lrkv_decode_step_sync_offset(const lrkv_dims* dims, int32_t max_len);
+/* 1 if lrkv_decode_step runs these dims and max_len as one launch, 0 if as the
+ * two calls (or the arguments are invalid).  Host arithmetic only. */
+int32_t lrkv_decode_step_fused(const lrkv_dims* dims, int32_t max_len);
+lrkv_status lrkv_decode_step(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* k_new,
+                             const void* v_new, const void* zk_new, const void* zv_new, const void* q,
+                             const void* B_k, const void* B_v, float* p, float* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* lrkv_decode for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.  Same
  * arguments, kernels, split plan and results (bit for bit) as lrkv_decode,

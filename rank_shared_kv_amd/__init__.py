@@ -26,7 +26,8 @@ LRKV_F32 = 0
 LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_append_absorb", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
-            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_noalloc_max_bytes",
+            "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_step_workspace_bytes",
+            "lrkv_decode_step_sync_offset", "lrkv_decode_step_fused", "lrkv_decode_step", "lrkv_decode_noalloc_max_bytes",
             "lrkv_decode_noalloc", "lrkv_latents_to_token_major", "lrkv_decode_multi_workspace_bytes",
             "lrkv_decode_multi", "lrkv_paged_append", "lrkv_decode_paged", "lrkv_rope_table",
             "lrkv_decode_rope_workspace_bytes", "lrkv_decode_rope", "lrkv_key_scales", "lrkv_norm_query",
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
             "lrkv_decode": ([D, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_partial": ([D, C, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+            "lrkv_decode_step_workspace_bytes": ([D, i32], sz),
+            "lrkv_decode_step_sync_offset": ([D, i32], sz),
+            "lrkv_decode_step_fused": ([D, i32], i32),
+            "lrkv_decode_step": ([D, C, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_noalloc_max_bytes": ([], sz),
             "lrkv_latents_to_token_major": ([D, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_noalloc": ([D, C, i32, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -182,6 +187,25 @@ def lrkv_decode(dims: Dims, cache: Cache, max_len: int, q, p, B_v, out, workspac
                 stream=None) -> None:
     _check(lib().lrkv_decode(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(q), _ptr(p), _ptr(B_v), _ptr(out),
                              _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode")
+
+
+def lrkv_decode_step_workspace_bytes(dims: Dims, max_len: int) -> int:
+    return int(lib().lrkv_decode_step_workspace_bytes(ctypes.byref(dims), max_len))
+
+
+def lrkv_decode_step_sync_offset(dims: Dims, max_len: int) -> int:
+    return int(lib().lrkv_decode_step_sync_offset(ctypes.byref(dims), max_len))
+
+
+def lrkv_decode_step_fused(dims: Dims, max_len: int) -> bool:
+    return bool(lib().lrkv_decode_step_fused(ctypes.byref(dims), max_len))
+
+
+def lrkv_decode_step(dims: Dims, cache: Cache, max_len: int, k_new, v_new, zk_new, zv_new, q, B_k, B_v, p, out,
+                     workspace, workspace_bytes: int, stream=None) -> None:
+    _check(lib().lrkv_decode_step(ctypes.byref(dims), ctypes.byref(cache), max_len, _ptr(k_new), _ptr(v_new),
+                                  _ptr(zk_new), _ptr(zv_new), _ptr(q), _ptr(B_k), _ptr(B_v), _ptr(p), _ptr(out),
+                                  _ptr(workspace), workspace_bytes, _stream(stream)), "lrkv_decode_step")
 
 
 def lrkv_latents_to_token_major(dims: Dims, src, dst, stream=None) -> None:

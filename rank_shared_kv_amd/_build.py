@@ -17,7 +17,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = ["lrkv_api.cpp", "k_cache.hip", "k_decode_general.hip", "k_decode_mfma.hip",
            "k_decode_mfma_part_d64_n0.hip", "k_decode_mfma_part_d128_n0.hip", "k_decode_mfma_part_d64_n1.hip",
            "k_decode_mfma_part_d128_n1.hip", "k_decode_mfma_part_d64_q2.hip", "k_decode_mfma_part_d64_q4.hip",
-           "k_decode_mfma_part_d128_q2.hip", "k_decode_mfma_part_d128_q4.hip", "k_decode_mfma_part_d128_t7.hip", "k_decode_mfma_f32.hip",
+           "k_decode_mfma_part_d128_q2.hip", "k_decode_mfma_part_d128_q4.hip", "k_decode_mfma_part_d128_t7.hip", "k_decode_mfma_part_d64_s.hip",
+           "k_decode_mfma_part_d128_s.hip", "k_decode_mfma_f32.hip",
            "k_merge.hip", "k_linear.hip", "k_materialize.hip", "k_norm.hip", "k_rope.hip", "k_decode_rope_mfma.hip",
            "k_probe.hip"]
 

@@ -17,6 +17,7 @@
 //          consecutive query tokens, with the length of the set's last token.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
+#include "lrkv_step.hpp"
 
 namespace lrkv {
 namespace {
@@ -55,60 +56,27 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_kernel(int H, int d_h, 
     }
 }
 
-// Vector path (rows of B^K a multiple of 16 bytes): q staged in LDS; thread (row group rg, vector vi)
-// reads B^K[h][c][vi*VE .. vi*VE + VE) for rows c = rg, rg + rpp, ... as 16-byte vectors and keeps VE
-// partial sums; the row groups are added in a fixed order in LDS.
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Vector path (rows of B^K a multiple of 16 bytes, r / VE <= 64): one wave per (b, h) unit, four units per
+// workgroup (absorb_wave, lrkv_step.hpp; the fused decode step runs the same body).
+constexpr int kAbsorbUnitsPerWg = kAbsorbThreads / 64;
+constexpr int kAbsorbPartFloats = 64 * 8;  // 64 * VE floats per wave (VE <= 8)
 
 template <typename T>
-__device__ __forceinline__ void absorb_vec_body(int bh, int H, int d_h, int r, const T* __restrict__ q,
+__device__ __forceinline__ void absorb_wg_units(int wg, int n_units, int H, int d_h, int r, const T* __restrict__ q,
                                                 const T* __restrict__ B_k, float* __restrict__ p) {
-    constexpr int VE = 16 / (int)sizeof(T);
-    __shared__ float qs[256];
-    __shared__ float part[kAbsorbThreads * VE];  // [row group][r]: rpp * r <= kAbsorbThreads * VE
-    const int h = bh % H, tid = threadIdx.x;
-    for (int c = tid; c < d_h; c += kAbsorbThreads) qs[c] = elem<T>::load(q, (size_t)bh * d_h + c);
-    __syncthreads();
-    const int nv = r / VE, rpp = kAbsorbThreads / nv;
-    const int vi = tid % nv, rg = tid / nv;
-    const int groups = min(rpp, d_h);
-    if (rg < groups) {
-        float acc[VE];
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[e] = 0.f;
-        const T* basis = B_k + (size_t)h * d_h * r + vi * VE;
-#pragma unroll 4
-        for (int c = rg; c < d_h; c += rpp) {
-            const u32x4_t v = *(const u32x4_t*)(basis + (size_t)c * r);
-            const float qc = qs[c];
-#pragma unroll
-            for (int e = 0; e < VE; ++e) {
-                float x;
-                if constexpr (sizeof(T) == 4) {
-                    x = __uint_as_float(v[e]);
-                } else {
-                    const uint32_t w = v[e >> 1];
-                    x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
-                }
-                acc[e] = fmaf(qc, x, acc[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < VE; ++e) part[rg * r + vi * VE + e] = acc[e];
-    }
-    __syncthreads();
-    for (int i = tid; i < r; i += kAbsorbThreads) {
-        float sum = 0.f;
-        for (int g = 0; g < groups; ++g) sum += part[g * r + i];  // fixed order
-        p[(size_t)bh * r + i] = sum;
-    }
+    __shared__ float qs[kAbsorbUnitsPerWg][256];
+    __shared__ float part[kAbsorbUnitsPerWg][kAbsorbPartFloats];
+    const int wave = threadIdx.x >> 6;
+    const int u = wg * kAbsorbUnitsPerWg + wave;
+    if (u < n_units) absorb_wave<T>(u, H, d_h, r, q, B_k, p, qs[wave], part[wave]);
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int H, int d_h, int r, const T* __restrict__ q,
+__global__ void __launch_bounds__(kAbsorbThreads) absorb_vec_kernel(int n_units, int H, int d_h, int r,
+                                                                    const T* __restrict__ q,
                                                                     const T* __restrict__ B_k,
                                                                     float* __restrict__ p) {
-    absorb_vec_body<T>(blockIdx.x, H, d_h, r, q, B_k, p);
+    absorb_wg_units<T>(blockIdx.x, n_units, H, d_h, r, q, B_k, p);
 }
 
 // block_table NULL: contiguous cache [batch][L_cap][...]; else page pools [n_pages][1 << page_shift][...]
@@ -128,35 +96,8 @@ __device__ __forceinline__ void append_body(int b, int H, int d_h, int r, int L_
     __syncthreads();
     const int j = row;
     if (j < 0) return;  // full or invalid: nothing written, length unchanged
-    // the row's index in the cache tensors (contiguous) or page pools (paged)
-    const size_t grow = block_table ? ((size_t)block_table[(size_t)b * max_pages + (j >> page_shift)] << page_shift) +
-                                          (size_t)(j & ((1 << page_shift) - 1))
-                                    : (size_t)b * L_cap + j;
-    const size_t srow = grow * d_h;
-    // token-major latents: token j's H x r latents of every head form one contiguous row, and the
-    // new rows [b][H][r] are contiguous too, so both copies are plain row copies
-    const size_t zrow = grow * H * r, zsrc = (size_t)b * H * r;
-    constexpr int VE = 16 / (int)sizeof(T);
-    if ((d_h % VE) == 0 && ((H * r) % VE) == 0) {
-        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-        for (int c = threadIdx.x; c < d_h / VE; c += blockDim.x) {
-            ((u32x4_t*)(k_shared + srow))[c] = ((const u32x4_t*)(k_new + (size_t)b * d_h))[c];
-            ((u32x4_t*)(v_shared + srow))[c] = ((const u32x4_t*)(v_new + (size_t)b * d_h))[c];
-        }
-        for (int c = threadIdx.x; c < H * r / VE; c += blockDim.x) {
-            ((u32x4_t*)(z_k + zrow))[c] = ((const u32x4_t*)(zk_new + zsrc))[c];
-            ((u32x4_t*)(z_v + zrow))[c] = ((const u32x4_t*)(zv_new + zsrc))[c];
-        }
-    } else {
-        for (int c = threadIdx.x; c < d_h; c += blockDim.x) {
-            k_shared[srow + c] = k_new[(size_t)b * d_h + c];
-            v_shared[srow + c] = v_new[(size_t)b * d_h + c];
-        }
-        for (int idx = threadIdx.x; idx < H * r; idx += blockDim.x) {
-            z_k[zrow + idx] = zk_new[zsrc + idx];
-            z_v[zrow + idx] = zv_new[zsrc + idx];
-        }
-    }
+    append_row_copy<T>(b, j, H, d_h, r, L_cap, k_shared, v_shared, z_k, z_v, k_new, v_new, zk_new, zv_new,
+                       block_table, page_shift, max_pages);
     __syncthreads();
     if (threadIdx.x == 0) seq_lens[b] = j + 1;
 }
@@ -174,7 +115,7 @@ __global__ void __launch_bounds__(256) append_kernel(int H, int d_h, int r, int 
 }
 
 // One launch for the two per-token operations of a decode step: workgroups 0 .. batch-1 append (as
-// append_kernel), workgroups batch .. batch + batch*H - 1 absorb (as absorb_vec_kernel).  The two touch
+// append_kernel), the rest absorb four (b, h) units each (as absorb_vec_kernel).  The two touch
 // disjoint memory, so they run side by side; each workgroup's arithmetic is the separate kernels', so the
 // results are bitwise the same.
 template <typename T>
@@ -191,35 +132,34 @@ __global__ void __launch_bounds__(256) append_absorb_kernel(int batch, int H, in
         append_body<T>(w, H, d_h, r, L_cap, k_shared, v_shared, z_k, z_v, seq_lens, k_new, v_new, zk_new, zv_new,
                        nullptr, 0, 0);
     else
-        absorb_vec_body<T>(w - batch, H, d_h, r, q, B_k, p);
+        absorb_wg_units<T>(w - batch, batch * H, H, d_h, r, q, B_k, p);
 }
 
 }  // namespace
 
 // The vector path needs 16-byte rows of B^K (r a multiple of 16 / element bytes), a q row that fits its LDS
-// stage (d_h <= 256) and at least one row group: each of its threads owns one 16-byte vector of a row, so
-// r / (16 / element bytes) must not exceed the workgroup width (r <= 2048 for bf16, 1024 for fp32).  Other
-// shapes take the scalar kernel.
-static bool absorb_vec_ok(int d_h, int r, int dtype) {
-    const int ve = dtype == 0 ? 4 : 8;
-    return r > 0 && (r % ve) == 0 && r / ve <= kAbsorbThreads && d_h <= 256;
-}
+// stage (d_h <= 256) and at least one row group: each lane of a unit's wave owns one 16-byte vector of a row,
+// so r / (16 / element bytes) must not exceed 64 (r <= 512 for bf16, 256 for fp32).  Other shapes take the
+// scalar kernel.
+static bool absorb_vec_ok(int d_h, int r, int dtype) { return absorb_wave_ok(d_h, r, dtype == 0 ? 4 : 2); }
+
+static int absorb_workgroups(int n_units) { return (n_units + kAbsorbUnitsPerWg - 1) / kAbsorbUnitsPerWg; }
 
 hipError_t launch_absorb(int batch, int H, int d_h, int r, int dtype, const void* q, const void* B_k, float* p,
                          hipStream_t stream) {
-    dim3 grid(batch * H), block(kAbsorbThreads);
     const bool vec = absorb_vec_ok(d_h, r, dtype);
+    dim3 grid(vec ? absorb_workgroups(batch * H) : batch * H), block(kAbsorbThreads);
     if (dtype == 0) {
         if (vec)
-            hipLaunchKernelGGL(absorb_vec_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
+            hipLaunchKernelGGL(absorb_vec_kernel<float>, grid, block, 0, stream, batch * H, H, d_h, r, (const float*)q,
                                (const float*)B_k, p);
         else
             hipLaunchKernelGGL(absorb_kernel<float>, grid, block, 0, stream, H, d_h, r, (const float*)q,
                                (const float*)B_k, p);
     } else {
         if (vec)
-            hipLaunchKernelGGL(absorb_vec_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
-                               (const uint16_t*)B_k, p);
+            hipLaunchKernelGGL(absorb_vec_kernel<uint16_t>, grid, block, 0, stream, batch * H, H, d_h, r,
+                               (const uint16_t*)q, (const uint16_t*)B_k, p);
         else
             hipLaunchKernelGGL(absorb_kernel<uint16_t>, grid, block, 0, stream, H, d_h, r, (const uint16_t*)q,
                                (const uint16_t*)B_k, p);
@@ -236,7 +176,7 @@ hipError_t launch_append_absorb(int batch, int H, int d_h, int r, int L_cap, int
                                 const void* v_new, const void* zk_new, const void* zv_new, const void* q,
                                 const void* B_k, float* p, hipStream_t stream) {
     if (!append_absorb_supported(H, d_h, r, dtype)) return hipErrorInvalidValue;
-    dim3 grid(batch + batch * H), block(256);
+    dim3 grid(batch + absorb_workgroups(batch * H)), block(256);
     if (dtype == 0)
         hipLaunchKernelGGL(append_absorb_kernel<float>, grid, block, 0, stream, batch, H, d_h, r, L_cap,
                            (float*)k_shared, (float*)v_shared, (float*)z_k, (float*)z_v, seq_lens,

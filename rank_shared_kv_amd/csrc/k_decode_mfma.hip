@@ -13,6 +13,8 @@ hipError_t launch_split_mfma_d64_q4(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma_d128_q2(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma_d128_q4(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_split_mfma_d128_t7(const DecodeArgs& a, int occupancy, hipStream_t stream);
+hipError_t launch_step_mfma_d64(const DecodeArgs& a, int occupancy, hipStream_t stream);
+hipError_t launch_step_mfma_d128(const DecodeArgs& a, int occupancy, hipStream_t stream);
 bool mfma_table_shape(int H, int d_h, int r);
 
 namespace {
@@ -53,6 +55,17 @@ hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t str
     if (mfma_table_shape(a.H, a.d_h, a.r)) return norm ? hipErrorInvalidValue : launch_split_mfma_d128_t7(a, occupancy, stream);
     if (a.d_h == 64) return norm ? launch_split_mfma_d64_n1(a, occupancy, stream) : launch_split_mfma_d64_n0(a, occupancy, stream);
     if (a.d_h == 128) return norm ? launch_split_mfma_d128_n1(a, occupancy, stream) : launch_split_mfma_d128_n0(a, occupancy, stream);
+    return hipErrorInvalidValue;
+}
+
+// Fused decode step: single query, plain contiguous cache, the regular shapes (the model-table ranks are outside
+// the absorb's one-wave vector path, so their steps run as separate launches).
+hipError_t launch_step_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream) {
+    if (a.qw != 1 || a.qgroup != 1 || a.rho != nullptr || a.block_table != nullptr || a.sync == nullptr ||
+        mfma_table_shape(a.H, a.d_h, a.r))
+        return hipErrorInvalidValue;
+    if (a.d_h == 64) return launch_step_mfma_d64(a, occupancy, stream);
+    if (a.d_h == 128) return launch_step_mfma_d128(a, occupancy, stream);
     return hipErrorInvalidValue;
 }
 

@@ -70,6 +70,7 @@
 
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
+#include "lrkv_step.hpp"
 
 namespace lrkv {
 namespace {
@@ -233,10 +234,53 @@ __device__ __forceinline__ LatWindow lat_window(int h, int sl) {
     return w;
 }
 
-template <int D, int R, int H, int OCC, bool NORM, int QW, bool NTL>
+// Fused decode step (STEP): LDS of the absorb workgroups (per wave: q staged as floats, then the row-group
+// partial sums) and the byte offset of the finish flag, past them.
+constexpr int kStepAbsorbWaveFloats = 256 + 64 * 8;
+constexpr int kStepFlagByte = kWaves * kStepAbsorbWaveFloats * 4;
+constexpr int kStepLdsMin = kStepFlagByte + 16;
+
+// Absorb and merge roles of the fused step.
+template <int D, int R, int H>
+__device__ __forceinline__ void step_absorb_role(const DecodeArgs& a, unsigned char* lds, int wave, int lane) {
+    if constexpr (R > 0) {
+        // four (sequence, head) units per workgroup, one per wave; each wave releases its p row, then counts it in
+        // ready[b]
+        const int u = (int)blockIdx.x * kWaves + wave;
+        if (u < a.batch * H) {
+            float* qs = (float*)lds + wave * kStepAbsorbWaveFloats;
+            absorb_wave<uint16_t, true>(u, H, D, R, (const uint16_t*)a.q, (const uint16_t*)a.B_k, a.p_out, qs,
+                                        qs + 256);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's p stores are done before the count
+            if (lane == 0)
+                __hip_atomic_fetch_add(a.sync + kStepHeader + u / H, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int D, int R, int H>
+__device__ __forceinline__ void step_merge_role(const DecodeArgs& a, unsigned char* lds) {
+    // one (sequence, head) per workgroup, once every split workgroup of the sequence is done
+    const int m = (int)blockIdx.x - a.n_absorb - a.num_splits;
+    const int mb = m / H, mh = m - mb * H;
+    uint32_t* done = a.sync + kStepHeader + a.batch + mb;
+    uint32_t* sync = a.sync;
+    auto wait = [=](int S_b) { step_wait(done, (uint32_t)S_b, sync); };
+    float* sums = (float*)lds;
+    if (a.merge_wide)
+        merge_body<uint16_t, 4, true>(mh, mb, a.batch, 1, 1, H, D, R, a.max_len, a.append_cap, a.chunk, a.num_splits,
+                                      a.seq_lens, (const uint16_t*)a.B_v, a.out, a.ws, sums, wait);
+    else
+        merge_body<uint16_t, 1, true>(mh, mb, a.batch, 1, 1, H, D, R, a.max_len, a.append_cap, a.chunk, a.num_splits,
+                                      a.seq_lens, (const uint16_t*)a.B_v, a.out, a.ws, sums, wait);
+    step_finish(a.sync, a.n_merge, a.batch, a.L_cap, a.seq_lens_rw, (int*)(lds + kStepFlagByte));
+}
+
+template <int D, int R, int H, int OCC, bool NORM, int QW, bool NTL, bool STEP = false>
 __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs a) {
     using C = Cfg<D, R, H, OCC, QW>;
     static_assert(!(NORM && QW > 1), "the normalised variant serves one query per sequence");
+    static_assert(!STEP || (QW == 1 && !NORM), "the fused step serves one query per sequence, plain decode");
     constexpr int EPL = C::EPL, LDW = C::LDW, LDL = C::LDL, OCTS = C::OCTS, NU = C::NU, NSLOT = C::NSLOT,
                   SDW = C::SLOT_DW, HS = C::HS, NPOS = C::NPOS;
     constexpr bool kDot2 = EPL >= 2;  // private score on v_dot2 (p split into bf16 hi + lo)
@@ -253,14 +297,59 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     uint16_t* vt = (uint16_t*)my;
     float* xb = (float*)(my + C::VT_BYTES);
 
+    // Fused decode step: workgroups [0, n_absorb) absorb, the next num_splits split, the rest merge.  The
+    // absorb and merge workgroups run their bodies (lrkv_step.hpp) here and leave.  Only the merge workgroups
+    // count themselves finished: the last of them finishes after every split workgroup has read the lengths
+    // (each merge waited for every split of its sequence) and after every absorb count was seen (by the splits).
+    int wid = blockIdx.x;  // this workgroup's index among the split workgroups
+    if constexpr (STEP) {
+        if ((int)blockIdx.x < a.n_absorb) {
+            step_absorb_role<D, R, H>(a, lds, wave, lane);
+            return;
+        }
+        if ((int)blockIdx.x >= a.n_absorb + a.num_splits) {
+            step_merge_role<D, R, H>(a, lds);
+            return;
+        }
+        wid = (int)blockIdx.x - a.n_absorb;
+    }
+
     // Which sequence and split this workgroup handles (splits dealt to sequences by length), and
     // which 32-row blocks its row lanes take: blocks are dealt round-robin over the (split, row lane)
     // slots of the sequence, slot (split, tl) takes blocks split*NTL + tl + k*S_b*NTL.
-    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, wid, a.append_cap);
     const int b = wslot.b, split = wslot.s;
-    if (b < 0) return;
-    const int Lb = clamped_len(a.seq_lens, b, a.max_len);
-    if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
+    // fused step: after the records are out (stores done), count this workgroup in done[b]
+    auto step_end = [&]() {
+        if constexpr (STEP) step_publish(b >= 0 ? a.sync + kStepHeader + a.batch + b : nullptr);
+    };
+    if (b < 0) {
+        step_end();
+        return;
+    }
+    // uniform: readfirstlane keeps it (and every loop bound and block offset derived from it) in SGPRs also where
+    // the compiler cannot prove the lengths unwritten (the fused step writes global memory before the loop)
+    const int Lb = __builtin_amdgcn_readfirstlane(clamped_len(a.seq_lens, b, a.max_len, a.append_cap));
+    if constexpr (STEP) {
+        // The appended token's rows (row L0 = stored length, when below L_cap), written before anything reads
+        // them: by the workgroup whose slot owns their block when the decode sees them, else by split 0.
+        const int L0 = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+        if (L0 >= 0 && L0 < a.L_cap) {
+            const int owner = (L0 < Lb) ? ((L0 / kRows) % (wslot.S_b * C::NTL)) / C::NTL : 0;
+            if (split == owner) {
+                append_row_copy<uint16_t>(b, L0, H, D, R, a.L_cap, (uint16_t*)a.k_shared, (uint16_t*)a.v_shared,
+                                          (uint16_t*)a.z_k, (uint16_t*)a.z_v, (const uint16_t*)a.k_new,
+                                          (const uint16_t*)a.v_new, (const uint16_t*)a.zk_new,
+                                          (const uint16_t*)a.zv_new, nullptr, 0, 0);
+                __builtin_amdgcn_s_waitcnt(0);  // the rows are in this XCD's L2 before any wave loads them
+                __syncthreads();
+            }
+        }
+    }
+    if (split * a.chunk >= Lb) {  // whole workgroup: no live rows in this split
+        step_end();
+        return;
+    }
     const int nb = (Lb + kRows - 1) / kRows;  // blocks of this sequence
     const int bc = b / a.qgroup;  // the cached sequence this (virtual) sequence reads
 
@@ -288,6 +377,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         const int qi = (QW == 1) ? 0 : hq / (C::NHG * 16), h = hq - qi * (C::NHG * 16);
         q_lds[hq * C::QROW + c] = (h < H && qi < nreal) ? qg[(qi * H + h) * D + c] : (uint16_t)0;
     }
+    auto stage_p = [&]() {
     if constexpr (R > 0) {
         const float* pg = a.p + (size_t)q_row0 * H * R;
         if constexpr (C::GEN) {
@@ -303,7 +393,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 const int j0 = 2 * t - lw.off, j1 = j0 + 1;  // the positions' coordinates within the lane's own
                 const bool ok0 = live && j0 >= 0 && j0 < lw.own, ok1 = live && j1 >= 0 && j1 < lw.own;
                 const float* prow = pg + (size_t)(qi * H + (live ? hl : 0)) * R + lw.first;
-                const float x0 = ok0 ? prow[j0] : 0.f, x1 = ok1 ? prow[j1] : 0.f;
+                const float x0 = ok0 ? ld_f32<STEP>(prow + j0) : 0.f, x1 = ok1 ? ld_f32<STEP>(prow + j1) : 0.f;
                 const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
                 const uint32_t l0 = f32_to_bf16_bits(x0 - __uint_as_float(h0 << 16));
                 const uint32_t l1 = f32_to_bf16_bits(x1 - __uint_as_float(h1 << 16));
@@ -317,7 +407,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
                 const int h = i / (R / 2), pr = i - h * (R / 2);  // pair index within the (query, head) row
                 const int slice = pr / (EPL / 2), j = pr - slice * (EPL / 2);
                 const bool live = QW == 1 || h < nreal * H;
-                const float x0 = live ? pg[h * R + 2 * pr] : 0.f, x1 = live ? pg[h * R + 2 * pr + 1] : 0.f;
+                const float x0 = live ? ld_f32<STEP>(pg + h * R + 2 * pr) : 0.f;
+                const float x1 = live ? ld_f32<STEP>(pg + h * R + 2 * pr + 1) : 0.f;
                 const uint32_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
                 const uint32_t l0 = f32_to_bf16_bits(x0 - __uint_as_float(h0 << 16));
                 const uint32_t l1 = f32_to_bf16_bits(x1 - __uint_as_float(h1 << 16));
@@ -328,12 +419,16 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         } else {
             for (int i = tid; i < QW * H * R; i += kWaves * 64) {
                 const int h = i / R, k = i - h * R;
-                p_lds[h * C::PROW + k] = (QW == 1 || h < nreal * H) ? __float_as_uint(pg[i]) : 0u;
+                p_lds[h * C::PROW + k] = (QW == 1 || h < nreal * H) ? __float_as_uint(ld_f32<STEP>(pg + i)) : 0u;
             }
         }
     }
+    };
+    // fused step: p is staged after the first cache loads are on their way and the absorb of this sequence
+    // is done (below)
+    if constexpr (!STEP) stage_p();
     for (int i = lane; i < QW * 16 * C::XS; i += 64) xb[i] = 0.f;
-    __syncthreads();
+    if constexpr (!STEP) __syncthreads();
 
     const int n16 = lane & 15, g4 = lane >> 4;  // MFMA layout: column (head or value column), row group
     const int hh = lane >> 3, sl = lane & 7;    // latent layout: head within octet, coordinate slice
@@ -361,7 +456,12 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     const uint32_t row_bytes_sh = D * 2, row_bytes_lat = H * R * 2;
     // contiguous cache: descriptors over this sequence's rows, a block addressed by its row t0; paged cache:
     // descriptors over the whole page pools, a block addressed by its pool row (pages hold whole blocks)
-    const bool paged = a.block_table != nullptr;
+    const bool paged = a.block_table != nullptr;  // never in the fused step (its launches pass no block table)
+    // pool row of logical row t of this sequence (t when contiguous), uniform
+    // pool row of logical row t of this sequence (t when contiguous).  readfirstlane: the row is uniform, and
+    // where the kernel writes global memory before the loop (the fused step) the compiler cannot tell that the
+    // block table is unchanged and would otherwise keep the row, and every block offset, in VGPRs
+    auto prow = [&](int t) { return __builtin_amdgcn_readfirstlane(paged_row(a, bc, t)); };
     const size_t seq_rows = paged ? 0 : (size_t)bc * a.L_cap;
     const uint32_t n_rows = paged ? (uint32_t)a.n_pages << a.page_shift : (uint32_t)a.L_cap;
     const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc((const uint16_t*)a.k_shared + seq_rows * D, n_rows * row_bytes_sh);
@@ -488,7 +588,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // (the virtual sequences of one cached sequence share its rotation, so they read the same rows together)
     const int rot = (int)(((long)nmine * bc) / (a.batch / a.qgroup));
     if (nmine > 0) {
-        const int pr_first = paged_row(a, bc, kRows * (first_blk + rot * step_blk));
+        const int pr_first = prow(kRows * (first_blk + rot * step_blk));
 #pragma unroll
         for (int u = 0; u < NSLOT - 1; ++u) {
             issue(u, pr_first, u, true);
@@ -496,6 +596,13 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             // into it (scheduled freely, the loads forced waits that left less than half the ring in flight)
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    if constexpr (STEP) {
+        // the absorb workgroups' p rows of this sequence (H units), then p into LDS; the barrier inside the
+        // wait also orders the q rows staged above
+        if constexpr (R > 0) step_wait(a.sync + kStepHeader + b, (uint32_t)H, a.sync);
+        stage_p();
+        __syncthreads();
     }
 
 #if LRKV_LOCKSTEP
@@ -524,7 +631,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
         const int itn = (itr + 1 < nmine) ? itr + 1 : 0;
         const bool pf_live = it + 1 < nmine;
         const int t0_pf = pf_live ? kRows * (first_blk + itn * step_blk) : t0;
-        const int pr = paged_row(a, bc, t0), pr_pf = paged_row(a, bc, t0_pf);  // pool rows (t0 when contiguous)
+        const int pr = prow(t0), pr_pf = prow(t0_pf);  // pool rows (t0 when contiguous)
         f32x4_t s_sh[QW][2];
         uint32_t rho_w[8];  // scales of this lane's 8 scores (bf16 bits), read at the top of the block
         if constexpr (NORM) {
@@ -824,9 +931,11 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
             }
             __syncthreads();
         }
-        float* out = a.ws + ((size_t)blockIdx.x * QW + qi) * H * C::REC;
-        for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
+        float* out = a.ws + ((size_t)wid * QW + qi) * H * C::REC;
+        // fused step: agent-coherent stores, for the merge workgroups of the same launch
+        for (int i = tid; i < H * C::REC; i += kWaves * 64) st_f32<STEP>(out + i, mg[i]);
     }
+    step_end();
 }
 
 template <int D, int R, int H, int OCC, bool NORM, int QW, bool NTL = true>
@@ -837,6 +946,46 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
     return hipGetLastError();
+}
+
+// Fused decode step: absorb workgroups, split workgroups and merge workgroups in one launch.
+template <int D, int R, int H, int OCC>
+hipError_t launch_step_one(const DecodeArgs& a, hipStream_t stream) {
+    using C = Cfg<D, R, H, OCC, 1>;
+    auto kern = split_mfma_kernel<D, R, H, OCC, false, 1, true, true>;
+    constexpr int kLds = C::LDS_BYTES > kStepLdsMin ? C::LDS_BYTES : kStepLdsMin;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(a.n_absorb + a.num_splits + a.n_merge), dim3(kWaves * 64), kLds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int R, int H>
+hipError_t launch_step_dhr(const DecodeArgs& a, int occ, hipStream_t stream) {
+    return occ == 1 ? launch_step_one<D, R, H, 1>(a, stream) : launch_step_one<D, R, H, 2>(a, stream);
+}
+
+template <int D, int H>
+hipError_t launch_step_r(const DecodeArgs& a, int occ, hipStream_t stream) {
+    switch (a.r) {
+        case 0: return launch_step_dhr<D, 0, H>(a, occ, stream);
+        case 8: return launch_step_dhr<D, 8, H>(a, occ, stream);
+        case 16: return launch_step_dhr<D, 16, H>(a, occ, stream);
+        case 32: return launch_step_dhr<D, 32, H>(a, occ, stream);
+        case 48: return launch_step_dhr<D, 48, H>(a, occ, stream);
+        case 64: return launch_step_dhr<D, 64, H>(a, occ, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_step_h(const DecodeArgs& a, int occ, hipStream_t stream) {
+    switch (a.H) {
+        case 8: return launch_step_r<D, 8>(a, occ, stream);
+        case 16: return launch_step_r<D, 16>(a, occ, stream);
+        case 32: return launch_step_r<D, 32>(a, occ, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 // Four queries per wave do not fit the register file at d_h = 128, r = 64 (the compiled kernel spills in its

@@ -26,9 +26,11 @@
 // are then combined in LDS in a fixed order, so results are bitwise
 // reproducible.  The B^V row
 // fragments the epilogue needs are loaded at kernel start, off the critical
-// path.
+// path.  The fused decode step merges with merge_body (lrkv_step.hpp), whose
+// arithmetic per column is this kernel's, so both give the same bits.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
+#include "lrkv_step.hpp"
 
 namespace lrkv {
 namespace {
@@ -37,17 +39,7 @@ constexpr int kCols = 256;                       // columns handled per pass
 constexpr int kMaxCols = 512;                    // d_h + r <= 512
 constexpr int kBatch = 16;                       // splits per thread loaded together
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-template <typename T>
-__device__ __forceinline__ float vec_elem(const u32x4_t& v, int e) {
-    if constexpr (sizeof(T) == 4) {
-        return __uint_as_float(v[e]);
-    } else {
-        const uint32_t w = v[e >> 1];
-        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-    }
-}
+typedef step_u32x4_t u32x4_t;
 
 // kGroups split groups of kCols threads each: 4 groups when sequences hold many splits, 1 when they
 // hold few (then the extra threads would only wait).
@@ -75,7 +67,7 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int nv, int Q, i
 
     // epilogue operand: thread (c, vi) holds B^V[h][c][vi*VE, vi*VE + VE) as one 16-byte vector
     const int nvv = (R > 0 && (R % VE) == 0) ? R / VE : 0;
-    const bool vec_epi = nvv > 0 && D * nvv <= kMergeThreads;
+    const bool vec_epi = merge_epilogue_in_parts(D, nvv, kMergeThreads);
     u32x4_t bv = {0u, 0u, 0u, 0u};
     const int ec = vec_epi ? tid / nvv : 0, evi = vec_epi ? tid % nvv : 0;
     if (vec_epi && ec < D) bv = *(const u32x4_t*)(B_v + ((size_t)h * D + ec) * R + evi * VE);
@@ -181,6 +173,9 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int nv, int Q, i
 
 }  // namespace
 
+// KG = 4 when sequences average more than 32 splits (two batches per group otherwise)
+bool merge_wide(int num_splits, int n_virtual) { return num_splits > 32 * n_virtual; }
+
 hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dtype, int max_len, int chunk,
                         int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
                         hipStream_t stream) {
@@ -189,7 +184,7 @@ hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dty
     // one split group per column when sequences average at most 32 splits (two batches per thread), four
     // otherwise (4-token decode at long context, 32 splits per token set: 8.0 us with one group, 11.1 us
     // with four)
-    const bool wide = num_splits > 32 * nv;
+    const bool wide = merge_wide(num_splits, nv);
     dim3 grid(H, batch * Q), block(wide ? 4 * kCols : kCols);
     if (dtype == 0) {
         auto k = wide ? merge_kernel<float, 4> : merge_kernel<float, 1>;

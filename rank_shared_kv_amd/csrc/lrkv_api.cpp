@@ -14,6 +14,7 @@
 
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
+#include "lrkv_step.hpp"
 
 namespace {
 
@@ -464,6 +465,106 @@ lrkv_status lrkv_latents_to_token_major(const lrkv_dims* dims, const void* src, 
     hipError_t e = lrkv::launch_latents_token_major(dims->batch, dims->H, dims->L_cap, dims->r, dims->dtype, src, dst,
                                                     (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "latent layout kernel launch");
+    return ok();
+}
+
+namespace {
+// The fused step runs where the plain plan takes the bf16 matrix-core kernel, the absorb has its one-wave
+// vector path (r == 0: no absorb) and the merge workgroups (one per (sequence, head), with the split kernel's
+// registers) fit in one resident round: the 64-sequence ragged batch (2048 of them, four rounds at two per CU)
+// ran 3% slower fused than as three launches.
+bool step_fused(const lrkv_dims& d, const lrkv::SplitPlan& plan) {
+    return plan.path == lrkv::SplitPath::kMfmaBf16 && plan.num_splits > 0 &&
+           (d.r == 0 || lrkv::absorb_wave_ok(d.d_h, d.r, 2)) && (long)d.batch * d.H <= 256L * plan.occupancy;
+}
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+size_t lrkv_decode_step_sync_offset(const lrkv_dims* dims, int32_t max_len) {
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p)) return 0;
+    return round256(workspace_bytes(*dims, p));
+}
+
+int32_t lrkv_decode_step_fused(const lrkv_dims* dims, int32_t max_len) {
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p)) return 0;
+    return step_fused(*dims, p) ? 1 : 0;
+}
+
+size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int32_t max_len) {
+    if (!dims_valid(dims) || max_len < 0 || max_len > dims->L_cap) return 0;
+    lrkv::SplitPlan p;
+    if (!plan_split(*dims, max_len, &p)) return 0;
+    return round256(workspace_bytes(*dims, p)) + round256(sizeof(uint32_t) * lrkv::step_sync_words(dims->batch));
+}
+
+lrkv_status lrkv_decode_step(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* k_new,
+                             const void* v_new, const void* zk_new, const void* zv_new, const void* q,
+                             const void* B_k, const void* B_v, float* p, float* out, void* workspace,
+                             size_t workspace_bytes_, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan));
+    LRKV_TRY(check_cache(*dims, cache, true));
+    LRKV_TRY(need_ptr(k_new, "k_new"));
+    LRKV_TRY(need_ptr(v_new, "v_new"));
+    LRKV_TRY(need_ptr(q, "q"));
+    LRKV_TRY(need_ptr(out, "out"));
+    if (dims->r > 0) {
+        LRKV_TRY(need_ptr(zk_new, "zk_new"));
+        LRKV_TRY(need_ptr(zv_new, "zv_new"));
+        LRKV_TRY(need_ptr(B_k, "B_k"));
+        LRKV_TRY(need_ptr(B_v, "B_v"));
+        LRKV_TRY(need_ptr(p, "p"));
+    }
+    const size_t need = lrkv_decode_step_workspace_bytes(dims, max_len);
+    if (!workspace) return fail(LRKV_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(LRKV_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if (workspace_bytes_ < need) return fail(LRKV_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", workspace_bytes_, need);
+    if (!step_fused(*dims, plan)) {  // the two calls
+        LRKV_TRY(lrkv_append_absorb(dims, cache, k_new, v_new, zk_new, zv_new, q, B_k, p, stream));
+        return lrkv_decode(dims, cache, max_len, q, p, B_v, out, workspace, workspace_bytes_, stream);
+    }
+    using namespace lrkv;
+    DecodeArgs a{};
+    a.batch = dims->batch;
+    a.H = dims->H;
+    a.d_h = dims->d_h;
+    a.r = dims->r;
+    a.L_cap = dims->L_cap;
+    a.dtype = dims->dtype;
+    a.max_len = max_len;
+    a.chunk = plan.chunk;
+    a.num_splits = plan.num_splits;
+    a.qgroup = 1;
+    a.n_queries = 1;
+    a.qw = 1;
+    a.k_shared = cache->k_shared;
+    a.v_shared = cache->v_shared;
+    a.z_k = cache->z_k;
+    a.z_v = cache->z_v;
+    a.seq_lens = cache->seq_lens;
+    a.seq_lens_rw = cache->seq_lens;
+    a.q = q;
+    a.p = p;
+    a.p_out = p;
+    a.ws = (float*)workspace;
+    a.append_cap = dims->L_cap;
+    a.n_absorb = dims->r > 0 ? (dims->batch * dims->H + 3) / 4 : 0;
+    a.n_merge = dims->batch * dims->H;
+    a.merge_wide = merge_wide(plan.num_splits, dims->batch) ? 1 : 0;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.zk_new = zk_new;
+    a.zv_new = zv_new;
+    a.B_k = B_k;
+    a.B_v = B_v;
+    a.out = out;
+    a.sync = (uint32_t*)((char*)workspace + lrkv_decode_step_sync_offset(dims, max_len));
+    const hipError_t e = launch_step_mfma(a, plan.occupancy, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode step kernel launch");
     return ok();
 }
 

@@ -76,9 +76,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // kernels and the merge kernel evaluate the same integer formulas, so they
 // agree on every W_b and S_b.  All helpers below are wave-level: every lane
 // of the calling wave must call them, and they return wave-uniform values.
+//
+// append_cap: 0 for a plain decode; L_cap for the fused decode step, which
+// appends one token per sequence in the same launch and so sees a sequence
+// of stored length L with 0 <= L < L_cap at length L + 1 (a full sequence,
+// or a negative length, does not grow), as lrkv_cache_append followed by a
+// decode would.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int max_len) {
-    const int L = seq_lens[b];
+__device__ __forceinline__ int grown_len(int L, int append_cap) { return (L >= 0 && L < append_cap) ? L + 1 : L; }
+__device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int max_len, int append_cap = 0) {
+    const int L = grown_len(seq_lens[b], append_cap);
     return L < 0 ? 0 : (L > max_len ? max_len : L);
 }
 __device__ __forceinline__ int len_blocks(int L) { return (L + 31) >> 5; }
@@ -89,9 +96,10 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 }
 
 // total blocks T of the batch
-__device__ inline int batch_blocks(const int32_t* seq_lens, int batch, int max_len) {
+__device__ inline int batch_blocks(const int32_t* seq_lens, int batch, int max_len, int append_cap = 0) {
     int t = 0;
-    for (int i = (int)(threadIdx.x & 63); i < batch; i += 64) t += len_blocks(clamped_len(seq_lens, i, max_len));
+    for (int i = (int)(threadIdx.x & 63); i < batch; i += 64)
+        t += len_blocks(clamped_len(seq_lens, i, max_len, append_cap));
     return wave_sum_i32(t);
 }
 
@@ -106,14 +114,15 @@ struct SplitSlot {
 };
 
 // The (sequence, split) that workgroup w of a G-workgroup launch handles.
-__device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int max_len, int G, int w) {
+__device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int max_len, int G, int w,
+                                      int append_cap = 0) {
     const int lane = threadIdx.x & 63;
-    const int T = batch_blocks(seq_lens, batch, max_len);
+    const int T = batch_blocks(seq_lens, batch, max_len, append_cap);
     const int extra = G - batch;
     int carry = 0;
     for (int c0 = 0; c0 < batch; c0 += 64) {
         const int b = c0 + lane;
-        const int nbk = (b < batch) ? len_blocks(clamped_len(seq_lens, b, max_len)) : 0;
+        const int nbk = (b < batch) ? len_blocks(clamped_len(seq_lens, b, max_len, append_cap)) : 0;
         int incl = nbk;  // inclusive scan over the lanes of this chunk of 64 sequences
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(incl, o);
@@ -138,12 +147,13 @@ __device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int m
 
 // First workgroup W_b and split count S_b of sequence b.
 __device__ inline void sequence_splits(const int32_t* seq_lens, int batch, int max_len, int G, int b, int* W_b,
-                                       int* S_b) {
-    const int T = batch_blocks(seq_lens, batch, max_len);
+                                       int* S_b, int append_cap = 0) {
+    const int T = batch_blocks(seq_lens, batch, max_len, append_cap);
     int before = 0;
-    for (int i = (int)(threadIdx.x & 63); i < b; i += 64) before += len_blocks(clamped_len(seq_lens, i, max_len));
+    for (int i = (int)(threadIdx.x & 63); i < b; i += 64)
+        before += len_blocks(clamped_len(seq_lens, i, max_len, append_cap));
     before = wave_sum_i32(before);
-    const int nbk = len_blocks(clamped_len(seq_lens, b, max_len));
+    const int nbk = len_blocks(clamped_len(seq_lens, b, max_len, append_cap));
     const int W0 = first_workgroup(b, before, G - batch, T);
     *W_b = __builtin_amdgcn_readfirstlane(W0);
     *S_b = __builtin_amdgcn_readfirstlane(first_workgroup(b + 1, before + nbk, G - batch, T) - W0);

@@ -39,6 +39,23 @@ struct DecodeArgs {
     // is B^K [H][d_h][r]; p is not used
     const float* rope_cs;
     const void* rope_bk;
+    // fused decode step (lrkv_decode_step): one launch of n_absorb absorb workgroups (p = q B^K, four (b, h) units
+    // each, written to p_out, which p also points at), the num_splits split workgroups and n_merge merge
+    // workgroups (one per (b, h), writing out), handing work on through the counters at sync; every sequence is
+    // seen at its appended length (append_cap = L_cap: the new token's rows k_new, v_new, zk_new, zv_new are
+    // written at row seq_lens[b] when it is below L_cap, and the lengths grow at the end).  append_cap = 0 and
+    // n_absorb = n_merge = 0 otherwise.
+    int append_cap, n_absorb, n_merge, merge_wide;
+    const void* k_new;
+    const void* v_new;
+    const void* zk_new;
+    const void* zv_new;
+    const void* B_k;
+    const void* B_v;
+    float* p_out;
+    float* out;
+    uint32_t* sync;
+    int32_t* seq_lens_rw;  // the same lengths as seq_lens, grown by the last workgroup
 };
 
 // pool row of logical row t of sequence b (t uniform across the caller's wave)
@@ -86,6 +103,9 @@ hipError_t launch_append_absorb(int batch, int H, int d_h, int r, int L_cap, int
                                 const void* v_new, const void* zk_new, const void* zv_new, const void* q,
                                 const void* B_k, float* p, hipStream_t stream);
 hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);  // occupancy: waves per SIMD (1 or 2)
+// fused decode step on the bf16 matrix-core kernel (single query, contiguous cache); a carries the step fields
+hipError_t launch_step_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);
+bool merge_wide(int num_splits, int n_virtual);  // the merge's split grouping (4 groups when true)
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
 // Merge of a decode of `batch` cached sequences with Q query tokens each, split as virtual sequences of qw
 // tokens (ceil(Q / qw) per cached sequence; seq_lens are their lengths, num_splits the split launch's G);

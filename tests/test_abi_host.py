@@ -198,6 +198,37 @@ def test_noalloc_checks_before_any_launch():
     assert "scratch" in lk.lib().lrkv_last_error().decode()
 
 
+def test_decode_step_layout_and_fusion():
+    """lrkv_decode_step: the workspace holds the split records (lrkv_decode_workspace_bytes, rounded up to 256
+    bytes), then the counter words (4 header words and two per sequence); the step runs as one launch on the bf16
+    matrix-core shapes whose merge workgroups fit one resident round, as the two calls elsewhere; its argument
+    checks run before any launch."""
+    for (B, H, d_h, r, L, dt, fused) in [(4, 32, 128, 64, 32768, 1, True), (16, 16, 128, 48, 8192, 1, True),
+                                         (4, 18, 128, 55, 8192, 1, False),   # r = 55: the absorb's scalar path
+                                         (64, 32, 128, 32, 32768, 1, False),  # 2048 merge workgroups
+                                         (32, 16, 128, 32, 2528, 1, True), (2, 8, 64, 0, 64, 1, True),
+                                         (64, 32, 128, 0, 32768, 0, False), (2, 8, 64, 12, 64, 1, False)]:
+        d = lk.make_dims(B, H, d_h, r, L, dt)
+        rec = lk.lrkv_decode_workspace_bytes(d, L)
+        off = lk.lrkv_decode_step_sync_offset(d, L)
+        total = lk.lrkv_decode_step_workspace_bytes(d, L)
+        assert off == (rec + 255) // 256 * 256
+        assert total == off + ((4 + 2 * B) * 4 + 255) // 256 * 256
+        assert lk.lrkv_decode_step_fused(d, L) == fused, (B, H, d_h, r, dt)
+    d = _dims()
+    c = lk.Cache(A, A, A, A, A)
+    need = lk.lrkv_decode_step_workspace_bytes(d, 256)
+    good = [A] * 10
+    assert _status(lk.lrkv_decode_step, d, c, 257, *good, need, 0) == lk.LRKV_ERR_INVALID_ARG  # max_len > L_cap
+    for i in range(9):  # k_new, v_new, zk_new, zv_new, q, B_k, B_v, p, out
+        args = list(good)
+        args[i] = None
+        assert _status(lk.lrkv_decode_step, d, c, 256, *args, need, 0) == lk.LRKV_ERR_INVALID_ARG, i
+    assert _status(lk.lrkv_decode_step, d, c, 256, *good[:9], None, need, 0) == lk.LRKV_ERR_WORKSPACE
+    assert _status(lk.lrkv_decode_step, d, c, 256, *good[:9], A + 64, need, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode_step, d, c, 256, *good, need - 4, 0) == lk.LRKV_ERR_WORKSPACE
+
+
 def test_latent_layout_conversion_checks():
     d = _dims()
     n = 2 * 8 * 256 * 8 * 2  # bytes of one latent tensor
