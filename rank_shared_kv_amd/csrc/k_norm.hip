@@ -91,15 +91,28 @@ __global__ void __launch_bounds__(kWaves * 64) key_scales_mfma_kernel(int H, int
 }
 
 constexpr int kChunkRows = 64;  // rows per chunk in the d_h = 64 / 128 kernel
+
+// f(integral_constant<int, 0>), f(..1), ... in order while f returns true
+template <class F, int... Cs>
+__device__ __forceinline__ void for_each_while(F&& f, std::integer_sequence<int, Cs...>) {
+    (void)((f(std::integral_constant<int, Cs>{})) && ...);
+}
 constexpr int kRowWaves = 8;    // waves (heads) per workgroup in the d_h = 64 / 128 kernel
 
 // rows max(0, L_b - n_last) .. L_b - 1 of sequence b; heads 8 y .. 8 y + 7 in the workgroup's waves.  The
 // workgroup walks CH chunks of 64 rows (past L_b: stand-ins, computed, not stored); each wave loads its
-// head's B^K_h fragments once.  The chunk's shared rows are staged in LDS by the whole workgroup (two
-// buffers: the next chunk's rows and latents load while the current chunk computes).  Every byte read
-// through the L1 caches costs about as much as one from memory here (measured: the kernel moved 1.08 GB
-// through them for 579 MB of data when 4 heads shared a chunk and B^K_h was fetched per 256 rows), so
-// eight heads share each staged chunk and B^K_h serves CH * 64 rows.
+// head's B^K_h fragments once.  The chunk's shared rows are staged in LDS by the whole workgroup.  Every byte
+// read through the L1 caches costs about as much as one from memory here (measured: the kernel moved 1.08 GB
+// through them for 579 MB of data when 4 heads shared a chunk and B^K_h was fetched per 256 rows), so eight
+// heads share each staged chunk and B^K_h serves CH * 64 rows.  The shared rows are widened to fp32 when they
+// are staged (once per workgroup instead of once per head) and enter each product as its accumulator, so the
+// key k_s + z B^T comes out of the matrix cores whole and the VALU only squares it (three VALU operations per
+// key element before, and the VALU was the busiest unit).  The loads run two chunks ahead: chunk c + 2's
+// latents and shared rows are issued before chunk c is computed (three latent register sets, two staging sets
+// for the shared rows, three LDS buffers).  The chunks are unrolled at compile time, so that whether a chunk
+// has a successor to load is known to the compiler: with those loads under a run-time condition (and a loop
+// back edge), the wait counts it derived were conservative, and most chunks waited for nearly every load in
+// flight.
 template <int D, int NKS, int CH>
 __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, int R, int L_cap, int max_len, int n_last,
                                                                       float eps, const int32_t* __restrict__ seq_lens,
@@ -108,9 +121,9 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
                                                                       const uint16_t* __restrict__ basis,
                                                                       uint16_t* __restrict__ rho) {
     constexpr int CB = D / 16;
-    constexpr int SROW = D + 8;                               // bf16 per staged shared row
+    constexpr int SROW = D + 4;                               // floats per staged shared row
     constexpr int PPT = kChunkRows * (D / 8) / (kRowWaves * 64);  // 16-byte pieces of a chunk per thread
-    __shared__ __attribute__((aligned(16))) uint16_t sh_l[2][kChunkRows * SROW];
+    __shared__ __attribute__((aligned(16))) float sh_l[3][kChunkRows * SROW];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.y * kRowWaves + wave, b = blockIdx.z;
@@ -121,6 +134,7 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
     if (r0 >= Lb) return;  // the whole workgroup
     const uint16_t* bh = basis + (size_t)hc * D * R;
     typedef u32x4_t ZFrag[4][NKS];
+    typedef u32x4_t SFrag[PPT];
     auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + 16 rg + n16 (past L_b: row L_b - 1)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
@@ -132,7 +146,7 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             }
         }
     };
-    auto load_sh = [&](u32x4_t (&v)[PPT], int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
+    auto load_sh = [&](SFrag& v, int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + kRowWaves * 64 * i;
@@ -140,11 +154,13 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             v[i] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + row) * D + 8 * (p % (D / 8)));
         }
     };
-    auto store_sh = [&](const u32x4_t (&v)[PPT], int buf) {
+    auto store_sh = [&](const SFrag& v, int buf) {  // widened to fp32 (exact)
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + kRowWaves * 64 * i;
-            *(u32x4_t*)(sh_l[buf] + (p / (D / 8)) * SROW + 8 * (p % (D / 8))) = v[i];
+            float* dst = sh_l[buf] + (p / (D / 8)) * SROW + 8 * (p % (D / 8));
+            *(f32x4_t*)dst = f32x4_t{bf16_lo(v[i][0]), bf16_hi(v[i][0]), bf16_lo(v[i][1]), bf16_hi(v[i][1])};
+            *(f32x4_t*)(dst + 4) = f32x4_t{bf16_lo(v[i][2]), bf16_hi(v[i][2]), bf16_lo(v[i][3]), bf16_hi(v[i][3])};
         }
     };
     auto zero_past_r = [&](ZFrag& zf) {
@@ -156,10 +172,9 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             }
     };
     u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16, coordinates 32 ks + 8 g4 (past r: zero)
-    u32x4_t sv[PPT];
-    ZFrag za, zb;
-    load_sh(sv, 0);
-    load_z(za, 0);
+    SFrag sv[2];          // shared rows of chunk k in sv[k & 1] until staged
+    ZFrag zr[3];          // latents of chunk k in zr[k % 3]
+    // prologue: B^K_h, then chunks 0 and 1 (shared rows and latents), in the order they are needed
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -167,40 +182,48 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             const int k = 32 * ks + 8 * g4;
             bf[cb][ks] = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + (k < R ? k : 0));
         }
+    load_sh(sv[0], 0);
+    load_z(zr[0], 0);
+    if constexpr (CH > 1) {
+        load_sh(sv[1], 1);
+        load_z(zr[1], 1);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
         if (32 * ks + 8 * g4 >= R) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) bf[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
         }
-    store_sh(sv, 0);
+    store_sh(sv[0], 0);
     __syncthreads();
-    // one chunk: the next chunk's loads first, then this one's keys; false once no later chunk holds a live row
-    auto chunk = [&](ZFrag& zc, ZFrag& zn, int c) -> bool {
-        if (c + 1 < CH) {
-            load_sh(sv, c + 1);
-            load_z(zn, c + 1);
+    // chunk C (compile time): chunk C + 2's loads first, then this chunk's keys, then chunk C + 1's shared rows
+    // into LDS; false once no later chunk holds a live row
+    auto chunk = [&](auto c_tag) -> bool {
+        constexpr int C = decltype(c_tag)::value, K = C;
+        constexpr int c = C;
+        if constexpr (C + 2 < CH) {
+            load_sh(sv[K & 1], c + 2);
+            load_z(zr[(K + 2) % 3], c + 2);
         }
+        ZFrag& zc = zr[K % 3];
         zero_past_r(zc);
-        const uint16_t* shc = sh_l[c & 1];
+        const float* shc = sh_l[c % 3];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             float ss = 0.f;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row's key: the shared row's values
+                // there are the accumulator the latent part is added to
+                f32x4_t acc = *(const f32x4_t*)(shc + (16 * rg + n16) * SROW + 16 * cb + 4 * g4);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
                                                                   __builtin_bit_cast(bf16x8_t, zc[rg][ks]), acc, 0, 0, 0);
-                // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row's key
-                const u32x2_t s = *(const u32x2_t*)(shc + (16 * rg + n16) * SROW + 16 * cb + 4 * g4);
-                const float v0 = acc[0] + bf16_lo(s[0]), v1 = acc[1] + bf16_hi(s[0]);
-                const float v2 = acc[2] + bf16_lo(s[1]), v3 = acc[3] + bf16_hi(s[1]);
-                ss = fmaf(v0, v0, ss);
-                ss = fmaf(v1, v1, ss);
-                ss = fmaf(v2, v2, ss);
-                ss = fmaf(v3, v3, ss);
+                ss = fmaf(acc[0], acc[0], ss);
+                ss = fmaf(acc[1], acc[1], ss);
+                ss = fmaf(acc[2], acc[2], ss);
+                ss = fmaf(acc[3], acc[3], ss);
             }
             ss += __shfl_xor(ss, 16);  // the four column groups of a row: (g4 0 + 1) + (2 + 3)
             ss += __shfl_xor(ss, 32);
@@ -208,16 +231,16 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             if (g4 == 0 && h < H && row < Lb)
                 rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
         }
-        if (c + 1 >= CH) return false;
-        store_sh(sv, (c + 1) & 1);  // that buffer's chunk finished before the previous barrier
-        __syncthreads();
-        return r0 + kChunkRows * (c + 1) < Lb;  // (workgroup-uniform)
+        if constexpr (C + 1 >= CH) {
+            return false;
+        } else {
+            // chunk c + 1's buffer last held chunk c - 2, finished before an earlier barrier
+            store_sh(sv[(K + 1) & 1], (c + 1) % 3);
+            __syncthreads();
+            return r0 + kChunkRows * (c + 1) < Lb;  // (workgroup-uniform)
+        }
     };
-    // chunks in pairs, so the two latent fragment sets keep fixed roles
-    for (int c = 0; c < CH; c += 2) {
-        if (!chunk(za, zb, c)) break;
-        if (!chunk(zb, za, c + 1)) break;
-    }
+    for_each_while(chunk, std::make_integer_sequence<int, CH>{});
 }
 
 template <typename T>
@@ -278,17 +301,17 @@ hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dt
     const int n_rows = std::min(n_last, max_len);
     if (n_rows <= 0) return hipSuccess;
     if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64) {
-        // chunks of 64 rows per workgroup: B^K_h serves that many rows; a long history takes 16 (1024 rows;
-        // long context, whole history: 177 us, against 182 with 8, 202 with 4), a short pass (an append's
-        // single row) 1; LRKV_KS_CHUNKS overrides (tuning, read at every call)
-        int ch = n_rows >= 8192 ? 16 : n_rows >= 4096 ? 8 : n_rows >= 1024 ? 4 : 1;
+        // chunks of 64 rows per workgroup: B^K_h serves that many rows; a long history takes 32 (2048 rows: the
+        // long-context whole history runs as one resident round of 256 workgroups, 153 us against 158 with 16),
+        // a short pass (an append's single row) 1; LRKV_KS_CHUNKS overrides (tuning, read at every call).
+        // (Eight chunks spilled registers with two chunks ahead, so that count is not built.)
+        int ch = n_rows >= 16384 ? 32 : n_rows >= 4096 ? 16 : n_rows >= 1024 ? 4 : 1;
         if (const char* e = getenv("LRKV_KS_CHUNKS")) ch = atoi(e);
-        ch = (ch >= 16) ? 16 : (ch >= 8) ? 8 : (ch >= 4) ? 4 : 1;
+        ch = (ch >= 32) ? 32 : (ch >= 16) ? 16 : (ch >= 4) ? 4 : 1;
         dim3 grid((n_rows + kChunkRows * ch - 1) / (kChunkRows * ch), (H + kRowWaves - 1) / kRowWaves, batch);
         auto pick = [&](auto d_tag, auto k_tag) {
             constexpr int DD = decltype(d_tag)::value, KK = decltype(k_tag)::value;
-            return ch == 16 ? key_scales_rows_kernel<DD, KK, 16>
-                   : ch == 8 ? key_scales_rows_kernel<DD, KK, 8>
+            return ch == 32 ? key_scales_rows_kernel<DD, KK, 32> : ch == 16 ? key_scales_rows_kernel<DD, KK, 16>
                    : ch == 4 ? key_scales_rows_kernel<DD, KK, 4> : key_scales_rows_kernel<DD, KK, 1>;
         };
         using I64 = std::integral_constant<int, 64>;

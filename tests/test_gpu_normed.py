@@ -106,6 +106,8 @@ SCALE_CASES = [  # (dtype, batch, H, d_h, r, lengths): matrix-core path (bf16, d
     ("bf16", 2, 4, 48, 12, [40, 3]),
     ("bf16", 2, 6, 64, 8, [100, 70]),     # heads not a multiple of a workgroup's four
     ("bf16", 2, 8, 96, 16, [70, 33]),     # d_h off the 64 / 128 kernel: a wave per 16 rows
+    ("bf16", 2, 16, 128, 64, [2500, 1100]),  # whole history of 1024..4095 rows: four chunks per workgroup
+    ("bf16", 1, 8, 128, 32, [5000]),         # 4096 rows and more: sixteen chunks, the last workgroup partial
     ("f32", 2, 4, 16, 4, [64, 3]),
     ("f32", 2, 32, 128, 0, [70, 1]),
 ]
