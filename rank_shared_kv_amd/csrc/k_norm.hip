@@ -99,21 +99,34 @@ __device__ __forceinline__ void for_each_while(F&& f, std::integer_sequence<int,
 }
 constexpr int kRowWaves = 8;    // waves (heads) per workgroup in the d_h = 64 / 128 kernel
 
+// A buffer resource over `bytes` bytes at base (bytes >= 0): a load whose lane offset (the offset from
+// the vector register; the scalar offset is not range-checked) is past the end returns zeros and touches no
+// memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ks_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a lane offset past every resource of this kernel
+
 // rows max(0, L_b - n_last) .. L_b - 1 of sequence b; heads 8 y .. 8 y + 7 in the workgroup's waves.  The
-// workgroup walks CH chunks of 64 rows (past L_b: stand-ins, computed, not stored); each wave loads its
-// head's B^K_h fragments once.  The chunk's shared rows are staged in LDS by the whole workgroup.  Every byte
-// read through the L1 caches costs about as much as one from memory here (measured: the kernel moved 1.08 GB
-// through them for 579 MB of data when 4 heads shared a chunk and B^K_h was fetched per 256 rows), so eight
-// heads share each staged chunk and B^K_h serves CH * 64 rows.  The shared rows are widened to fp32 when they
-// are staged (once per workgroup instead of once per head) and enter each product as its accumulator, so the
-// key k_s + z B^T comes out of the matrix cores whole and the VALU only squares it (three VALU operations per
-// key element before, and the VALU was the busiest unit).  The loads run two chunks ahead: chunk c + 2's
-// latents and shared rows are issued before chunk c is computed (three latent register sets, two staging sets
-// for the shared rows, three LDS buffers).  The chunks are unrolled at compile time, so that whether a chunk
-// has a successor to load is known to the compiler: with those loads under a run-time condition (and a loop
-// back edge), the wait counts it derived were conservative, and most chunks waited for nearly every load in
-// flight.
-template <int D, int NKS, int CH>
+// workgroup walks CH chunks of 64 rows (past L_b: zeros, computed, not stored); each wave loads its head's B^K_h
+// fragments once.  The chunk's shared rows are staged in LDS by the whole workgroup.  Every byte read through
+// the L1 caches costs about as much as one from memory here (measured: the kernel moved 1.08 GB through them
+// for 579 MB of data when 4 heads shared a chunk and B^K_h was fetched per 256 rows), so eight heads share each
+// staged chunk and B^K_h serves CH * 64 rows.  The shared rows are widened to fp32 when they are staged (once
+// per workgroup instead of once per head) and enter each product as its accumulator, so the key k_s + z B^T
+// comes out of the matrix cores whole and the VALU only squares it.  The loads run two chunks ahead: chunk
+// c + 2's latents and shared rows are issued before chunk c is computed (three latent register sets, two
+// staging sets for the shared rows, three LDS buffers).  The chunks are unrolled at compile time, so that
+// whether a chunk has a successor to load is known to the compiler: with those loads under a run-time condition
+// (and a loop back edge), the wait counts it derived were conservative, and most chunks waited for nearly every
+// load in flight.  The cache is read through buffer resources that start at a 16-row group (latents) or a chunk
+// (shared rows) and end at row L_b, so that the row offsets are scalar and rows past L_b (and coordinates past
+// r, through an offset past every resource) read as zeros without per-lane clamps; the
+// four partial sums of a row are reduced so that lane (row n16, group g4) ends with the whole sum of row
+// 16 g4 + n16 of the chunk, and each lane computes and stores one scale per chunk.  (The VALU issued more
+// instructions than the matrix cores took cycles before: per 64-row chunk and wave about 480, 130 of them the
+// squares, the rest address arithmetic, clamps and four full-precision scales per lane.)  FULL: r = 32 NKS.
+template <int D, int NKS, int CH, bool FULL>
 __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, int R, int L_cap, int max_len, int n_last,
                                                                       float eps, const int32_t* __restrict__ seq_lens,
                                                                       const uint16_t* __restrict__ shared,
@@ -128,30 +141,39 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
     const int n16 = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.y * kRowWaves + wave, b = blockIdx.z;
     const int hc = min(h, H - 1);  // waves past the last head compute a stand-in and store nothing
-    const int Lb = clamped_len(seq_lens, b, max_len);
+    const int Lb = __builtin_amdgcn_readfirstlane(clamped_len(seq_lens, b, max_len));
     const int start = max(0, Lb - n_last);
     const int r0 = start + blockIdx.x * kChunkRows * CH;
     if (r0 >= Lb) return;  // the whole workgroup
+    const int zrow = H * R * 2, srow = D * 2;  // bytes per cache row (every head), per shared row
+    const uint16_t* zb = z + (size_t)b * L_cap * H * R;
+    const uint16_t* sb = shared + (size_t)b * L_cap * D;
+    // lane offsets: latents of row n16 of a 16-row group, head hc, coordinates 32 ks + 8 g4 (past r: out of range)
+    uint32_t vz[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+        vz[ks] = (FULL || 32 * ks + 8 * g4 < R) ? (uint32_t)(n16 * H + hc) * R * 2 + (32 * ks + 8 * g4) * 2 : kOutOfRange;
     const uint16_t* bh = basis + (size_t)hc * D * R;
     typedef u32x4_t ZFrag[4][NKS];
     typedef u32x4_t SFrag[PPT];
-    auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + 16 rg + n16 (past L_b: row L_b - 1)
+    auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + 16 rg + n16 (past L_b: zeros)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const size_t row = (size_t)min(r0 + kChunkRows * c + 16 * rg + n16, Lb - 1);
+            const int t = r0 + kChunkRows * c + 16 * rg;  // the group's first row
+            const __amdgpu_buffer_rsrc_t rs = ks_rsrc(zb + (size_t)t * H * R, Lb > t ? (Lb - t) * zrow : 0);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int k = 32 * ks + 8 * g4;
-                zf[rg][ks] = *(const u32x4_t*)(z + (((size_t)b * L_cap + row) * H + hc) * R + (k < R ? k : 0));
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+                zf[rg][ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vz[ks], 0, 0));
         }
     };
     auto load_sh = [&](SFrag& v, int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
+        const int t = r0 + kChunkRows * c;  // the chunk's first row
+        const __amdgpu_buffer_rsrc_t rs = ks_rsrc(sb + (size_t)t * D, Lb > t ? (Lb - t) * srow : 0);
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             const int p = tid + kRowWaves * 64 * i;
-            const size_t row = (size_t)min(r0 + kChunkRows * c + p / (D / 8), Lb - 1);
-            v[i] = *(const u32x4_t*)(shared + ((size_t)b * L_cap + row) * D + 8 * (p % (D / 8)));
+            const uint32_t vo = (uint32_t)((p / (D / 8)) * srow + 16 * (p % (D / 8)));
+            v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
         }
     };
     auto store_sh = [&](const SFrag& v, int buf) {  // widened to fp32 (exact)
@@ -163,14 +185,6 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             *(f32x4_t*)(dst + 4) = f32x4_t{bf16_lo(v[i][2]), bf16_hi(v[i][2]), bf16_lo(v[i][3]), bf16_hi(v[i][3])};
         }
     };
-    auto zero_past_r = [&](ZFrag& zf) {
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            if (32 * ks + 8 * g4 >= R) {
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) zf[rg][ks] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-    };
     u32x4_t bf[CB][NKS];  // B_h rows 16 cb + n16, coordinates 32 ks + 8 g4 (past r: zero)
     SFrag sv[2];          // shared rows of chunk k in sv[k & 1] until staged
     ZFrag zr[3];          // latents of chunk k in zr[k % 3]
@@ -180,7 +194,7 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int k = 32 * ks + 8 * g4;
-            bf[cb][ks] = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + (k < R ? k : 0));
+            bf[cb][ks] = *(const u32x4_t*)(bh + (size_t)(16 * cb + n16) * R + (FULL || k < R ? k : 0));
         }
     load_sh(sv[0], 0);
     load_z(zr[0], 0);
@@ -188,12 +202,14 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
         load_sh(sv[1], 1);
         load_z(zr[1], 1);
     }
+    if constexpr (!FULL) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        if (32 * ks + 8 * g4 >= R) {
+        for (int ks = 0; ks < NKS; ++ks)
+            if (32 * ks + 8 * g4 >= R) {
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) bf[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+                for (int cb = 0; cb < CB; ++cb) bf[cb][ks] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+    }
     store_sh(sv[0], 0);
     __syncthreads();
     // chunk C (compile time): chunk C + 2's loads first, then this chunk's keys, then chunk C + 1's shared rows
@@ -205,12 +221,12 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             load_sh(sv[K & 1], c + 2);
             load_z(zr[(K + 2) % 3], c + 2);
         }
-        ZFrag& zc = zr[K % 3];
-        zero_past_r(zc);
+        const ZFrag& zc = zr[K % 3];
         const float* shc = sh_l[c % 3];
+        float ss[4];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            float ss = 0.f;
+            ss[rg] = 0.f;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 // lane (row n16, g4) holds columns 16 cb + 4 g4 + i of its row's key: the shared row's values
@@ -220,17 +236,23 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
                 for (int ks = 0; ks < NKS; ++ks)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bf[cb][ks]),
                                                                   __builtin_bit_cast(bf16x8_t, zc[rg][ks]), acc, 0, 0, 0);
-                ss = fmaf(acc[0], acc[0], ss);
-                ss = fmaf(acc[1], acc[1], ss);
-                ss = fmaf(acc[2], acc[2], ss);
-                ss = fmaf(acc[3], acc[3], ss);
+                ss[rg] = fmaf(acc[0], acc[0], ss[rg]);
+                ss[rg] = fmaf(acc[1], acc[1], ss[rg]);
+                ss[rg] = fmaf(acc[2], acc[2], ss[rg]);
+                ss[rg] = fmaf(acc[3], acc[3], ss[rg]);
             }
-            ss += __shfl_xor(ss, 16);  // the four column groups of a row: (g4 0 + 1) + (2 + 3)
-            ss += __shfl_xor(ss, 32);
-            const int row = r0 + kChunkRows * c + 16 * rg + n16;
-            if (g4 == 0 && h < H && row < Lb)
-                rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(ss, D, eps));
         }
+        // the four column groups of a row (lanes g4 = 0..3 of its n16) into lane g4 = rg of the row's group rg:
+        // groups (0 + 2) and (1 + 3) of the rows of groups rg with bit 1 equal to g4's, then the two of them
+        const bool hi2 = (g4 & 2) != 0, hi1 = (g4 & 1) != 0;
+        const float k0 = hi2 ? ss[2] : ss[0], k1 = hi2 ? ss[3] : ss[1];  // kept
+        const float s0 = hi2 ? ss[0] : ss[2], s1 = hi2 ? ss[1] : ss[3];  // sent
+        const float t0 = k0 + __shfl_xor(s0, 32), t1 = k1 + __shfl_xor(s1, 32);
+        const float kt = hi1 ? t1 : t0, st = hi1 ? t0 : t1;
+        const float tot = kt + __shfl_xor(st, 16);
+        const int row = r0 + kChunkRows * c + 16 * g4 + n16;
+        if (h < H && row < Lb)
+            rho[((size_t)b * L_cap + row) * H + h] = (uint16_t)f32_to_bf16_bits(rms_scale(tot, D, eps));
         if constexpr (C + 1 >= CH) {
             return false;
         } else {
@@ -300,7 +322,9 @@ hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dt
                              const void* B_k, void* rho, hipStream_t stream) {
     const int n_rows = std::min(n_last, max_len);
     if (n_rows <= 0) return hipSuccess;
-    if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64) {
+    // (the rows kernel sizes its buffer resources in 31-bit byte counts)
+    const bool rows_fit = (size_t)L_cap * H * r * 2 < ((size_t)1 << 31);
+    if (dtype == 1 && (d_h == 64 || d_h == 128) && r % 8 == 0 && r > 0 && r <= 64 && rows_fit) {
         // chunks of 64 rows per workgroup: B^K_h serves that many rows; a long history takes 32 (2048 rows: the
         // long-context whole history runs as one resident round of 256 workgroups, 153 us against 158 with 16),
         // a short pass (an append's single row) 1; LRKV_KS_CHUNKS overrides (tuning, read at every call).
@@ -309,10 +333,15 @@ hipError_t launch_key_scales(int batch, int H, int d_h, int r, int L_cap, int dt
         if (const char* e = getenv("LRKV_KS_CHUNKS")) ch = atoi(e);
         ch = (ch >= 32) ? 32 : (ch >= 16) ? 16 : (ch >= 4) ? 4 : 1;
         dim3 grid((n_rows + kChunkRows * ch - 1) / (kChunkRows * ch), (H + kRowWaves - 1) / kRowWaves, batch);
-        auto pick = [&](auto d_tag, auto k_tag) {
+        const bool full = r == 32 || r == 64;
+        auto pick_f = [&](auto d_tag, auto k_tag, auto f_tag) {
             constexpr int DD = decltype(d_tag)::value, KK = decltype(k_tag)::value;
-            return ch == 32 ? key_scales_rows_kernel<DD, KK, 32> : ch == 16 ? key_scales_rows_kernel<DD, KK, 16>
-                   : ch == 4 ? key_scales_rows_kernel<DD, KK, 4> : key_scales_rows_kernel<DD, KK, 1>;
+            constexpr bool FF = decltype(f_tag)::value;
+            return ch == 32 ? key_scales_rows_kernel<DD, KK, 32, FF> : ch == 16 ? key_scales_rows_kernel<DD, KK, 16, FF>
+                   : ch == 4 ? key_scales_rows_kernel<DD, KK, 4, FF> : key_scales_rows_kernel<DD, KK, 1, FF>;
+        };
+        auto pick = [&](auto d_tag, auto k_tag) {
+            return full ? pick_f(d_tag, k_tag, std::true_type{}) : pick_f(d_tag, k_tag, std::false_type{});
         };
         using I64 = std::integral_constant<int, 64>;
         using I128 = std::integral_constant<int, 128>;
