@@ -116,11 +116,14 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // a lane offset past every resou
 // per workgroup instead of once per head) and enter each product as its accumulator, so the key k_s + z B^T
 // comes out of the matrix cores whole and the VALU only squares it.  The loads run two chunks ahead: chunk
 // c + 2's latents and shared rows are issued before chunk c is computed (three latent register sets, two
-// staging sets for the shared rows, three LDS buffers).  The chunks are unrolled at compile time, so that
+// staging sets for the shared rows, two LDS buffers).  The chunks are unrolled at compile time, so that
 // whether a chunk has a successor to load is known to the compiler: with those loads under a run-time condition
 // (and a loop back edge), the wait counts it derived were conservative, and most chunks waited for nearly every
-// load in flight.  The cache is read through buffer resources that start at a 16-row group (latents) or a chunk
-// (shared rows) and end at row L_b, so that the row offsets are scalar and rows past L_b (and coordinates past
+// load in flight.  Each latent load reads whole rows of the wave's head (a head's r coordinates are contiguous),
+// which the wave passes through its own LDS rows into the operand layout, where a row's coordinates are spread
+// over four lanes (loaded directly in that layout, every load instruction read 16 rows x 64 bytes, and the
+// kernel ran 8% slower).  The cache is read through buffer resources that start at a load's first row (latents)
+// or a chunk (shared rows) and end at row L_b, so that the row offsets are scalar and rows past L_b (and coordinates past
 // r, through an offset past every resource) read as zeros without per-lane clamps; the
 // four partial sums of a row are reduced so that lane (row n16, group g4) ends with the whole sum of row
 // 16 g4 + n16 of the chunk, and each lane computes and stores one scale per chunk.  (The VALU issued more
@@ -136,7 +139,13 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
     constexpr int CB = D / 16;
     constexpr int SROW = D + 4;                               // floats per staged shared row
     constexpr int PPT = kChunkRows * (D / 8) / (kRowWaves * 64);  // 16-byte pieces of a chunk per thread
-    __shared__ __attribute__((aligned(16))) float sh_l[3][kChunkRows * SROW];
+    constexpr int RB = 64 * NKS;           // bytes of a head's latent row that the loads cover (r <= 32 NKS)
+    constexpr int LR = RB / 16;            // lanes per latent row in a load
+    constexpr int RPI = 64 / LR;           // latent rows per load instruction
+    constexpr int NZI = kChunkRows / RPI;  // latent load instructions per chunk
+    constexpr int ZS = RB + 16;            // bytes per latent row staged in LDS (padded)
+    __shared__ __attribute__((aligned(16))) float sh_l[2][kChunkRows * SROW];
+    __shared__ __attribute__((aligned(16))) unsigned char zs_l[kRowWaves][kChunkRows * ZS];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n16 = lane & 15, g4 = lane >> 4;
     const int h = blockIdx.y * kRowWaves + wave, b = blockIdx.z;
@@ -148,22 +157,19 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
     const int zrow = H * R * 2, srow = D * 2;  // bytes per cache row (every head), per shared row
     const uint16_t* zb = z + (size_t)b * L_cap * H * R;
     const uint16_t* sb = shared + (size_t)b * L_cap * D;
-    // lane offsets: latents of row n16 of a 16-row group, head hc, coordinates 32 ks + 8 g4 (past r: out of range)
-    uint32_t vz[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-        vz[ks] = (FULL || 32 * ks + 8 * g4 < R) ? (uint32_t)(n16 * H + hc) * R * 2 + (32 * ks + 8 * g4) * 2 : kOutOfRange;
+    // latent loads: lane (zi, zj) reads 16-byte piece zj (coordinates 8 zj ..) of head hc in row zi of the
+    // instruction's RPI rows (past r: out of range), so that each instruction reads whole rows of the head
+    const int zi = lane / LR, zj = lane % LR;
+    const uint32_t vz = (FULL || 8 * zj < R) ? (uint32_t)(zi * zrow + (hc * R + 8 * zj) * 2) : kOutOfRange;
     const uint16_t* bh = basis + (size_t)hc * D * R;
-    typedef u32x4_t ZFrag[4][NKS];
+    typedef u32x4_t ZFrag[NZI];
     typedef u32x4_t SFrag[PPT];
-    auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + 16 rg + n16 (past L_b: zeros)
+    auto load_z = [&](ZFrag& zf, int c) {  // latents of rows r0 + 64 c + RPI m + zi (past L_b: zeros)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const int t = r0 + kChunkRows * c + 16 * rg;  // the group's first row
+        for (int m = 0; m < NZI; ++m) {
+            const int t = r0 + kChunkRows * c + RPI * m;  // the instruction's first row
             const __amdgpu_buffer_rsrc_t rs = ks_rsrc(zb + (size_t)t * H * R, Lb > t ? (Lb - t) * zrow : 0);
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                zf[rg][ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vz[ks], 0, 0));
+            zf[m] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, vz, 0, 0));
         }
     };
     auto load_sh = [&](SFrag& v, int c) {  // piece p: row p / (D / 8), 8 columns at 8 (p % (D / 8))
@@ -221,8 +227,17 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
             load_sh(sv[K & 1], c + 2);
             load_z(zr[(K + 2) % 3], c + 2);
         }
-        const ZFrag& zc = zr[K % 3];
-        const float* shc = sh_l[c % 3];
+        // the chunk's latents through this wave's LDS rows into the operand layout: lane (row n16, g4) takes
+        // coordinates 32 ks + 8 g4 .. of row 16 rg + n16 (a wave's LDS operations complete in order)
+        unsigned char* zw = zs_l[wave];
+#pragma unroll
+        for (int m = 0; m < NZI; ++m) *(u32x4_t*)(zw + (RPI * m + zi) * ZS + 16 * zj) = zr[K % 3][m];
+        u32x4_t zc[4][NKS];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) zc[rg][ks] = *(const u32x4_t*)(zw + (16 * rg + n16) * ZS + 16 * (g4 + 4 * ks));
+        const float* shc = sh_l[c % 2];
         float ss[4];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
@@ -256,8 +271,8 @@ __global__ void __launch_bounds__(kRowWaves * 64) key_scales_rows_kernel(int H, 
         if constexpr (C + 1 >= CH) {
             return false;
         } else {
-            // chunk c + 1's buffer last held chunk c - 2, finished before an earlier barrier
-            store_sh(sv[(K + 1) & 1], (c + 1) % 3);
+            // chunk c + 1's buffer last held chunk c - 1, which every wave finished before the last barrier
+            store_sh(sv[(K + 1) & 1], (c + 1) % 2);
             __syncthreads();
             return r0 + kChunkRows * (c + 1) < Lb;  // (workgroup-uniform)
         }
