@@ -372,11 +372,18 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
 
     // ---- q (zero rows pad a partial head group and the padding query slots) and p into LDS ----
     // LDS q row (qi, head) sits at qi * 16 * NHG + head; p row (qi, head) at qi * H + head
-    for (int i = tid; i < QW * C::NHG * 16 * D; i += kWaves * 64) {
-        const int hq = i / D, c = i - hq * D;
-        const int qi = (QW == 1) ? 0 : hq / (C::NHG * 16), h = hq - qi * (C::NHG * 16);
-        q_lds[hq * C::QROW + c] = (h < H && qi < nreal) ? qg[(qi * H + h) * D + c] : (uint16_t)0;
-    }
+    auto stage_q = [&]() {
+        for (int i = tid; i < QW * C::NHG * 16 * D; i += kWaves * 64) {
+            const int hq = i / D, c = i - hq * D;
+            const int qi = (QW == 1) ? 0 : hq / (C::NHG * 16), h = hq - qi * (C::NHG * 16);
+            q_lds[hq * C::QROW + c] = (h < H && qi < nreal) ? qg[(qi * H + h) * D + c] : (uint16_t)0;
+        }
+    };
+    // the fused step stages q after the first cache loads have been issued (their round trip then covers the q
+    // loads; 0.8 us per step at the long-context shape), except at two waves per SIMD, where q's registers
+    // would spill
+    constexpr bool kQLate = STEP && OCC == 1;
+    if constexpr (!kQLate) stage_q();
     auto stage_p = [&]() {
     if constexpr (R > 0) {
         const float* pg = a.p + (size_t)q_row0 * H * R;
@@ -600,6 +607,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     if constexpr (STEP) {
         // the absorb workgroups' p rows of this sequence (H units), then p into LDS; the barrier inside the
         // wait also orders the q rows staged above
+        if constexpr (kQLate) stage_q();
         if constexpr (R > 0) step_wait(a.sync + kStepHeader + b, (uint32_t)H, a.sync);
         stage_p();
         __syncthreads();

@@ -121,6 +121,71 @@ def test_long_context_full_size():
     assert torch.equal(got, got2)
 
 
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("name", ["long_context", "mid_24layer"])
+def test_fused_step_full_size(name):
+    """The decode step the benchmark times at these workloads (lrkv_decode_step: the new token appended, p, the
+    split pass and the merge in one launch) at full size: every (sequence, head) pair against the reference on
+    the cache with the appended token, and the same bits as lrkv_append_absorb + lrkv_decode on a copy of the
+    cache (outputs, p, lengths, the appended rows)."""
+    w = synth.WORKLOADS[name]
+    L_cap, max_len = bench.launch_config(w, BENCH_STEPS)
+    lens = synth.seq_lengths(w)
+    dims = dims_of(w, L_cap)
+    assert lk.lrkv_decode_step_fused(dims, max_len), "the benchmark times the fused step at this workload"
+    say(f"[case] {name} fused step full size B={w.batch} H={w.H} r={w.r} L={int(lens.max())} {_plan_line(w, L_cap, max_len)}")
+    dev, host = _fill_and_keep(w, 0, lens, L_cap, keep=set(range(w.batch)))
+    twin = {k: dev[k].clone() for k in ("k_shared", "v_shared", "z_k", "z_v", "seq_lens")}
+    rows = sdev.new_rows(w)
+    outs, ps = [], []
+    for fused, d in ((True, dev), (False, twin)):
+        cache = cache_of(d, w.r)
+        p = torch.full((w.batch, w.H, w.r), float("nan"), dtype=torch.float32, device="cuda")
+        out = torch.full((w.batch, w.H, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
+        if fused:
+            nbytes = lk.lrkv_decode_step_workspace_bytes(dims, max_len)
+            ws = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+            lk.lrkv_decode_step(dims, cache, max_len, rows["k_new"], rows["v_new"], rows["zk_new"], rows["zv_new"],
+                                dev["q"], dev["B_k"], dev["B_v"], p, out, ws, nbytes)
+            torch.cuda.synchronize()
+            words = ws[lk.lrkv_decode_step_sync_offset(dims, max_len) // 4:].view(torch.int32)
+            assert int(words[1]) == 0 and int(words.abs().sum()) == 0, "step counters not back at zero"
+        else:
+            nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
+            ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
+            lk.lrkv_append_absorb(dims, cache, rows["k_new"], rows["v_new"], rows["zk_new"], rows["zv_new"], dev["q"],
+                                  dev["B_k"], p)
+            lk.lrkv_decode(dims, cache, max_len, dev["q"], p, dev["B_v"], out, ws, nbytes)
+            torch.cuda.synchronize()
+        outs.append(out)
+        ps.append(p)
+    grown = np.minimum(lens + 1, L_cap)
+    assert dev["seq_lens"].cpu().numpy().tolist() == grown.tolist()
+    assert torch.equal(dev["seq_lens"], twin["seq_lens"])
+    assert torch.equal(_bits(outs[0]), _bits(outs[1])), "fused step and separate calls differ"
+    assert torch.equal(_bits(ps[0]), _bits(ps[1]))
+    for k in ("k_shared", "v_shared", "z_k", "z_v"):
+        for b in range(w.batch):
+            n = int(lens[b])
+            assert torch.equal(_bits(dev[k][b, n]), _bits(twin[k][b, n])), f"appended {k} row of sequence {b}"
+    new = synth.gen_new_rows(w, 0)
+    ext = {}
+    for b in range(w.batch):
+        s = host[b]
+        ext[b] = {"k_shared": np.concatenate([s["k_shared"], new["k_new"][b][None]]),
+                  "v_shared": np.concatenate([s["v_shared"], new["v_new"][b][None]]),
+                  "z_k": np.concatenate([s["z_k"], new["zk_new"][b][:, None]], axis=1),
+                  "z_v": np.concatenate([s["z_v"], new["zv_new"][b][:, None]], axis=1)}
+    if name == "long_context":
+        pairs = [(b, h) for b in range(w.batch) for h in range(w.H)]
+    else:
+        pairs = [(b, h) for b in range(w.batch) for h in sorted({0, (5 * b) % w.H, w.H - 1})]
+    _check(w, outs[0], _reference(w, 0, ext, grown, pairs), pairs, f"{name} fused step")
+
+
 @pytest.mark.parametrize("layer", list(range(24)))
 def test_mid_24layer_full_size(layer):
     w = synth.WORKLOADS["mid_24layer"]
