@@ -593,7 +593,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // Otherwise every sequence reads the same relative position of its cache region at the same time,
     // and with some region strides those concurrent streams crowd the same HBM channels.
     // (the virtual sequences of one cached sequence share its rotation, so they read the same rows together)
-    const int rot = (int)(((long)nmine * bc) / (a.batch / a.qgroup));
+    const int rot = mul_div_floor(nmine, bc, a.batch / a.qgroup);
     if (nmine > 0) {
         const int pr_first = prow(kRows * (first_blk + rot * step_blk));
 #pragma unroll

@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     const int nmine = (last_blk > first_blk) ? (last_blk - first_blk + step_blk - 1) / step_blk : 0;
     // sequence b walks its blocks starting b/batch of the way along (same blocks, rotated order; the
     // virtual sequences of one cached sequence share its rotation)
-    const int rot = (int)(((long)nmine * bc) / (a.batch / a.qgroup));
+    const int rot = mul_div_floor(nmine, bc, a.batch / a.qgroup);
     if (nmine > 0) {
 #pragma unroll
         for (int u = 0; u < NSLOT - 1; ++u) {

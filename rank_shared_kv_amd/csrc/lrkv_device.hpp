@@ -96,6 +96,12 @@ __device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int m
 }
 __device__ __forceinline__ int len_blocks(int L) { return (L + 31) >> 5; }
 
+// floor(n * k / d) for 0 <= k < d < 2^16, in 32-bit arithmetic (n * k may not fit 32 bits)
+__device__ __forceinline__ int mul_div_floor(int n, int k, int d) {
+    const uint32_t q = (uint32_t)n / (uint32_t)d, r = (uint32_t)n % (uint32_t)d;
+    return (int)(q * (uint32_t)k + (r * (uint32_t)k) / (uint32_t)d);
+}
+
 __device__ __forceinline__ int wave_sum_i32(int v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return __builtin_amdgcn_readfirstlane(v);  // equal in every lane
@@ -126,9 +132,9 @@ __device__ inline int plan_per(const int32_t* seq_lens, int batch, int max_len, 
         t += nb;
         bmax = max(bmax, nb);
     }
-    const long long T = wave_sum_i32(t);
+    const uint32_t T = (uint32_t)wave_sum_i32(t), gn = (uint32_t)G * ntl;  // (block counts fit 31 bits)
     bmax = wave_max_i32(bmax);
-    int lo = (int)max(1LL, (T + (long long)G * ntl - 1) / ((long long)G * ntl));
+    int lo = max(1, (int)((T + gn - 1) / gn));
     const int hi = max(lo, (bmax + ntl - 1) / ntl);
     if (plan_need(seq_lens, batch, max_len, append_cap, lo * ntl) <= G) return lo * ntl;
     int good = hi;  // lo does not fit, good does
