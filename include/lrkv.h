@@ -169,12 +169,9 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
  * of partial records per head the workspace holds (the split kernel launches
  * G workgroups for the whole batch), and the split granule in rows
  * (*chunk_tokens, may be NULL).  On the device the G workgroups are dealt to
- * the sequences by their live lengths, at least one each: sequence b gets
- * S_b = max(1, ceil(n_b / M)) of them, n_b its 32-row blocks and M the least
- * multiple of granule / 32 for which the S_b add up to at most G (workgroups
- * past the sum have no split); split s of sequence b takes the granule-row
- * tiles s, s + S_b, s + 2 S_b, ... of the sequence and holds live rows iff
- * s * granule < seq_lens[b].
+ * the sequences in proportion to their live lengths, at least one each;
+ * split s of sequence b takes the granule-row tiles s, s + S_b, s + 2 S_b, ...
+ * of the sequence and holds live rows iff s * granule < seq_lens[b].
  * Host arithmetic only.  Returns 0 for invalid dims or max_len == 0. */
 int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens);
 

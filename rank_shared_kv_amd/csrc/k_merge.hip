@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int nv, int Q, i
 
     const int Lb = max(0, clamped_len(seq_lens, v, max_len) - (nreal - 1 - qi));
     int W_b, S_b;
-    sequence_splits(seq_lens, nv, max_len, S, chunk, v, &W_b, &S_b);  // every wave computes the same values
+    sequence_splits(seq_lens, nv, max_len, S, v, &W_b, &S_b);  // every wave computes the same values
     const int Sb = min(S_b, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold rows
     if (Sb == 0) {
         for (int c = tid; c < D; c += kMergeThreads) o[c] = 0.f;

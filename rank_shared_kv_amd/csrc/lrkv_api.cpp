@@ -116,10 +116,9 @@ int env_int(const char* name, int dflt) {
 // Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes
 // are known on the host without a device.  A plan is (G workgroups for the
 // whole batch, granule g in rows).  On the device the G workgroups are dealt
-// to the sequences by their lengths, at least one each, so that the busiest
-// row lane of any split is as short as it can be (lrkv_device.hpp); split s of
-// sequence b takes the g-row tiles s, s + S_b, ... of the sequence and writes
-// partial record W_b + s.  G aims at one
+// to the sequences in proportion to their lengths, at least one each
+// (lrkv_device.hpp); split s of sequence b takes the g-row tiles s, s + S_b,
+// ... of the sequence and writes partial record W_b + s.  G aims at one
 // resident round of workgroups (MI355X has 256 CUs; the matrix-core kernels
 // hold `occupancy` workgroups per CU), never fewer than one per sequence nor
 // more than one per tile of every sequence.  The plan does not depend on r

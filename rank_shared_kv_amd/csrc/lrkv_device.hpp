@@ -62,26 +62,20 @@ __device__ __forceinline__ void mfma_result_fence() {
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Split plan, evaluated on the device from seq_lens.
+// Length-proportional split plan, evaluated on the device from seq_lens.
 //
-// A decode launches G workgroups for the whole batch (G >= batch).  Each
-// sequence b gets S_b >= 1 of them (its splits), and a split deals the
-// sequence's nb_b 32-row blocks round robin over its ntl row lanes (ntl =
-// granule / 32), so the busiest lane of any split of b reads
-// ceil(nb_b / (S_b * ntl)) blocks.  The plan gives every sequence the fewest
-// splits that keep its lanes at or below a common cap M,
-//   S_b = max(1, ceil(nb_b / (M * ntl))),
-// with M the least cap for which the S_b add up to at most G.  The launch then
-// takes as long as its busiest lane, which no other choice of S_b shortens.
-// (Splits in proportion to nb_b, the earlier plan, rounded S_b down for some
-// sequences: in a batch of lengths between 512 and 32768 the busiest lane read
-// 38 blocks where the mean was 33.5, the launch 13% longer than its work.)
-// Workgroups past sum S_b have no split and leave.  Workgroup w = W_b + s,
-// W_b = S_0 + ... + S_{b-1}, handles split s of sequence b and writes partial
-// record w.  Split s of sequence b holds live rows iff s * granule < L_b.  The
-// split kernels and the merge kernels evaluate the same integer formulas, so
-// they agree on every W_b and S_b.  All helpers below are wave-level: every
-// lane of the calling wave must call them, and they return wave-uniform values.
+// A decode launches G workgroups for the whole batch.  They are dealt to the
+// sequences in proportion to each sequence's number of 32-row blocks, at
+// least one each: with G' = G - batch, C_b = blocks of sequences 0..b and
+// T = C_{batch-1},
+//   W_b = b + floor(G' * C_{b-1} / T)      first workgroup of sequence b
+//   S_b = W_{b+1} - W_b                    its number of splits
+// (with T = 0 every sequence gets one workgroup, W_b = b).  Workgroup
+// w = W_b + s handles split s of sequence b and writes partial record w.
+// Split s of sequence b holds live rows iff s * granule < L_b.  The split
+// kernels and the merge kernel evaluate the same integer formulas, so they
+// agree on every W_b and S_b.  All helpers below are wave-level: every lane
+// of the calling wave must call them, and they return wave-uniform values.
 //
 // append_cap: 0 for a plain decode; L_cap for the fused decode step, which
 // appends one token per sequence in the same launch and so sees a sequence
@@ -106,51 +100,21 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     return __builtin_amdgcn_readfirstlane(v);  // equal in every lane
 }
-__device__ __forceinline__ int wave_max_i32(int v) {
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return __builtin_amdgcn_readfirstlane(v);
-}
 
-// splits a sequence of nb blocks needs at `per` blocks per split (per = M * ntl)
-__device__ __forceinline__ int plan_splits(int nb, int per) { return nb > per ? (nb + per - 1) / per : 1; }
-
-// sum over the batch of plan_splits at `per`
-__device__ inline int plan_need(const int32_t* seq_lens, int batch, int max_len, int append_cap, int per) {
+// total blocks T of the batch
+__device__ inline int batch_blocks(const int32_t* seq_lens, int batch, int max_len, int append_cap = 0) {
     int t = 0;
     for (int i = (int)(threadIdx.x & 63); i < batch; i += 64)
-        t += plan_splits(len_blocks(clamped_len(seq_lens, i, max_len, append_cap)), per);
+        t += len_blocks(clamped_len(seq_lens, i, max_len, append_cap));
     return wave_sum_i32(t);
 }
 
-// blocks per split, M * ntl, of the plan: the least cap M >= 1 whose splits number at most G.  M is at least
-// ceil(T / (G * ntl)) (T blocks in all), which is the answer when the lengths are even; and ceil(Bmax / ntl)
-// (one split each, batch <= G) always fits.  Exponential, then binary search between the two.
-__device__ inline int plan_per(const int32_t* seq_lens, int batch, int max_len, int G, int ntl, int append_cap) {
-    int t = 0, bmax = 0;
-    for (int i = (int)(threadIdx.x & 63); i < batch; i += 64) {
-        const int nb = len_blocks(clamped_len(seq_lens, i, max_len, append_cap));
-        t += nb;
-        bmax = max(bmax, nb);
-    }
-    const uint32_t T = (uint32_t)wave_sum_i32(t), gn = (uint32_t)G * ntl;  // (block counts fit 31 bits)
-    bmax = wave_max_i32(bmax);
-    int lo = max(1, (int)((T + gn - 1) / gn));
-    const int hi = max(lo, (bmax + ntl - 1) / ntl);
-    if (plan_need(seq_lens, batch, max_len, append_cap, lo * ntl) <= G) return lo * ntl;
-    int good = hi;  // lo does not fit, good does
-    for (int step = 1; lo + step < good; step *= 2) {
-        if (plan_need(seq_lens, batch, max_len, append_cap, (lo + step) * ntl) <= G) {
-            good = lo + step;
-            break;
-        }
-        lo += step;
-    }
-    while (good - lo > 1) {
-        const int mid = lo + (good - lo) / 2;
-        if (plan_need(seq_lens, batch, max_len, append_cap, mid * ntl) <= G) good = mid;
-        else lo = mid;
-    }
-    return __builtin_amdgcn_readfirstlane(good * ntl);
+// b + floor(extra * blocks_before / total), the quotient in double precision: exact here (the product is below
+// 2^53 and so exact; a quotient that is not an integer lies at least 1 / total > 2^-31 from one, and the
+// division, correctly rounded, errs by less than 2^-39 at these magnitudes), and much cheaper than the 64-bit
+// integer division it replaces (which every split and merge workgroup ran before its first load)
+__device__ __forceinline__ int first_workgroup(int b, int blocks_before, int extra, int total) {
+    return b + (total > 0 ? (int)floor((double)extra * (double)blocks_before / (double)total) : 0);
 }
 
 struct SplitSlot {
@@ -159,21 +123,24 @@ struct SplitSlot {
     int S_b;  // splits of the sequence
 };
 
-// The (sequence, split) that workgroup w of a G-workgroup launch handles; granule = ntl * 32 rows.
-__device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int max_len, int G, int granule, int w,
+// The (sequence, split) that workgroup w of a G-workgroup launch handles.
+__device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int max_len, int G, int w,
                                       int append_cap = 0) {
     const int lane = threadIdx.x & 63;
-    const int per = plan_per(seq_lens, batch, max_len, G, max(1, granule >> 5), append_cap);
+    const int T = batch_blocks(seq_lens, batch, max_len, append_cap);
+    const int extra = G - batch;
     int carry = 0;
     for (int c0 = 0; c0 < batch; c0 += 64) {
         const int b = c0 + lane;
-        const int sb = (b < batch) ? plan_splits(len_blocks(clamped_len(seq_lens, b, max_len, append_cap)), per) : 0;
-        int incl = sb;  // inclusive scan over the lanes of this chunk of 64 sequences
+        const int nbk = (b < batch) ? len_blocks(clamped_len(seq_lens, b, max_len, append_cap)) : 0;
+        int incl = nbk;  // inclusive scan over the lanes of this chunk of 64 sequences
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(incl, o);
             if (lane >= o) incl += y;
         }
-        const int W0 = carry + incl - sb, W1 = carry + incl;
+        const int before = carry + incl - nbk;
+        const int W0 = first_workgroup(b, before, extra, T);
+        const int W1 = first_workgroup(b + 1, before + nbk, extra, T);
         const unsigned long long hit = __ballot(b < batch && w >= W0 && w < W1);
         if (hit) {
             // the values are wave-uniform; readfirstlane lets the compiler keep them (and every block
@@ -181,7 +148,7 @@ __device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int m
             const int src = __builtin_ctzll(hit);
             return SplitSlot{__builtin_amdgcn_readfirstlane(__shfl(b, src)),
                              __builtin_amdgcn_readfirstlane(w - __shfl(W0, src)),
-                             __builtin_amdgcn_readfirstlane(__shfl(sb, src))};
+                             __builtin_amdgcn_readfirstlane(__shfl(W1 - W0, src))};
         }
         carry += __shfl(incl, 63);
     }
@@ -189,14 +156,17 @@ __device__ inline SplitSlot split_slot(const int32_t* seq_lens, int batch, int m
 }
 
 // First workgroup W_b and split count S_b of sequence b.
-__device__ inline void sequence_splits(const int32_t* seq_lens, int batch, int max_len, int G, int granule, int b,
-                                       int* W_b, int* S_b, int append_cap = 0) {
-    const int per = plan_per(seq_lens, batch, max_len, G, max(1, granule >> 5), append_cap);
+__device__ inline void sequence_splits(const int32_t* seq_lens, int batch, int max_len, int G, int b, int* W_b,
+                                       int* S_b, int append_cap = 0) {
+    const int T = batch_blocks(seq_lens, batch, max_len, append_cap);
     int before = 0;
     for (int i = (int)(threadIdx.x & 63); i < b; i += 64)
-        before += plan_splits(len_blocks(clamped_len(seq_lens, i, max_len, append_cap)), per);
-    *W_b = wave_sum_i32(before);
-    *S_b = __builtin_amdgcn_readfirstlane(plan_splits(len_blocks(clamped_len(seq_lens, b, max_len, append_cap)), per));
+        before += len_blocks(clamped_len(seq_lens, i, max_len, append_cap));
+    before = wave_sum_i32(before);
+    const int nbk = len_blocks(clamped_len(seq_lens, b, max_len, append_cap));
+    const int W0 = first_workgroup(b, before, G - batch, T);
+    *W_b = __builtin_amdgcn_readfirstlane(W0);
+    *S_b = __builtin_amdgcn_readfirstlane(first_workgroup(b + 1, before + nbk, G - batch, T) - W0);
 }
 
 }  // namespace lrkv
