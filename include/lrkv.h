@@ -169,11 +169,31 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
  * of partial records per head the workspace holds (the split kernel launches
  * G workgroups for the whole batch), and the split granule in rows
  * (*chunk_tokens, may be NULL).  On the device the G workgroups are dealt to
- * the sequences in proportion to their live lengths, at least one each;
- * split s of sequence b takes the granule-row tiles s, s + S_b, s + 2 S_b, ...
- * of the sequence and holds live rows iff s * granule < seq_lens[b].
+ * the sequences by their live lengths, at least one each.  With n_b the
+ * 32-row blocks of sequence b and M the least multiple of granule / 32 for
+ * which S_b = max(1, ceil(n_b / M)) add up to at most G: when M is at least
+ * 8 * granule / 32, each sequence has one query set and the batch holds at
+ * most 64 sequences, sequence b gets those
+ * S_b workgroups (workgroups past the sum have no split); otherwise they are
+ * dealt in proportion to the n_b.  Split s of sequence b takes the
+ * granule-row tiles s, s + S_b, s + 2 S_b, ... of the sequence and holds live
+ * rows iff s * granule < seq_lens[b].
  * Host arithmetic only.  Returns 0 for invalid dims or max_len == 0. */
 int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens);
+
+/* The plan above, evaluated for given lengths as the decode's kernels evaluate
+ * it: first_wg[b] = W_b, the first of sequence b's workgroups (the index of its
+ * first partial record), and splits[b] = S_b, for b < dims->batch.  seq_lens
+ * (device, [batch]) are the lengths the decode reads; append = 1 gives the plan
+ * of lrkv_decode_step, which decodes each length L with 0 <= L < L_cap as
+ * L + 1 (append = 0: lrkv_decode).  first_wg and splits are device int32
+ * arrays of batch entries, written by a kernel enqueued on `stream` (nothing
+ * is written when max_len == 0: the decode launches no split workgroups).
+ * For inspecting and testing how a batch is split; the decode needs no call.
+ * Errors: invalid dims or max_len, append other than 0 or 1, NULL pointers,
+ * shapes with no kernel. */
+lrkv_status lrkv_decode_split_plan(const lrkv_dims* dims, int32_t max_len, const int32_t* seq_lens, int32_t append,
+                                   int32_t* first_wg, int32_t* splits, void* stream);
 
 /* One decode step against the factored history (review sec. 3, Algorithm 2
  * and its fused online-softmax form; reading notes sec. 2.4 Eqs. (6)-(7)):

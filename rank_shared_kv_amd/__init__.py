@@ -26,6 +26,7 @@ LRKV_F32 = 0
 LRKV_BF16 = 1
 
 EXPORTED = ("lrkv_absorb_query", "lrkv_cache_append", "lrkv_append_absorb", "lrkv_decode_workspace_bytes", "lrkv_decode_num_splits",
+            "lrkv_decode_split_plan",
             "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_merge", "lrkv_decode_step_workspace_bytes",
             "lrkv_decode_step_sync_offset", "lrkv_decode_step_fused", "lrkv_decode_step", "lrkv_decode_noalloc_max_bytes",
             "lrkv_decode_noalloc", "lrkv_latents_to_token_major", "lrkv_decode_multi_workspace_bytes",
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "lrkv_append_absorb": ([D, C, vp, vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
             "lrkv_decode_workspace_bytes": ([D, i32], sz),
             "lrkv_decode_num_splits": ([D, i32, ctypes.POINTER(i32)], i32),
+            "lrkv_decode_split_plan": ([D, i32, vp, i32, vp, vp, vp], ctypes.c_int),
             "lrkv_decode": ([D, C, i32, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_partial": ([D, C, i32, vp, vp, vp, sz, vp], ctypes.c_int),
             "lrkv_decode_merge": ([D, vp, i32, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -181,6 +183,11 @@ def lrkv_decode_num_splits(dims: Dims, max_len: int) -> Tuple[int, int]:
     chunk = ctypes.c_int32(0)
     s = lib().lrkv_decode_num_splits(ctypes.byref(dims), max_len, ctypes.byref(chunk))
     return int(s), int(chunk.value)
+
+
+def lrkv_decode_split_plan(dims: Dims, max_len: int, seq_lens, append: int, first_wg, splits, stream=None) -> None:
+    _check(lib().lrkv_decode_split_plan(ctypes.byref(dims), max_len, _ptr(seq_lens), append, _ptr(first_wg),
+                                        _ptr(splits), _stream(stream)), "lrkv_decode_split_plan")
 
 
 def lrkv_decode(dims: Dims, cache: Cache, max_len: int, q, p, B_v, out, workspace, workspace_bytes: int,

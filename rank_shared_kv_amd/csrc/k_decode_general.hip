@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(kThreads) split_general_kernel(DecodeArgs a) {
 
     // which sequence and split (splits dealt to sequences by length); split s of sequence b takes the
     // tiles s, s + S_b, s + 2 S_b, ... of the sequence
-    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, a.chunk, a.qgroup, blockIdx.x);
     const int b = wslot.b, split = wslot.s;
     if (b < 0) return;
     const int Lb = clamped_len(a.seq_lens, b, a.max_len);

@@ -317,7 +317,8 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_kernel(DecodeArgs
     // Which sequence and split this workgroup handles (splits dealt to sequences by length), and
     // which 32-row blocks its row lanes take: blocks are dealt round-robin over the (split, row lane)
     // slots of the sequence, slot (split, tl) takes blocks split*NTL + tl + k*S_b*NTL.
-    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, wid, a.append_cap);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, a.chunk, a.qgroup, wid,
+                                         a.append_cap);
     const int b = wslot.b, split = wslot.s;
     // fused step: after the records are out (stores done), count this workgroup in done[b]
     auto step_end = [&]() {

@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     float* mg = (float*)(lds + C::Q_BYTES + C::MW_BYTES);   // [H][REC] merged records
 
     const int tid = threadIdx.x, lane = tid & 63, tl = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, a.chunk, a.qgroup, blockIdx.x);
     const int b = wslot.b, split = wslot.s;
     if (b < 0) return;
     const int Lb = clamped_len(a.seq_lens, b, a.max_len);

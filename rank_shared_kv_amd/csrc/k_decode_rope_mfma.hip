@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(kThreads, 1) split_rope_mfma_kernel(DecodeArgs
     float* l_l = m_l + kMaxHeads;                             // [32] denominator
     float* al_l = l_l + kMaxHeads;                            // [32] this tile's rescale
 
-    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, blockIdx.x);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, a.chunk, a.qgroup, blockIdx.x);
     const int b = wslot.b, split = wslot.s;
     if (b < 0) return;
     const int Lb = clamped_len(a.seq_lens, b, a.max_len);

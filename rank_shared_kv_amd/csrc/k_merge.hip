@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(kGroups * kCols) merge_kernel(int nv, int Q, i
 
     const int Lb = max(0, clamped_len(seq_lens, v, max_len) - (nreal - 1 - qi));
     int W_b, S_b;
-    sequence_splits(seq_lens, nv, max_len, S, v, &W_b, &S_b);  // every wave computes the same values
+    sequence_splits(seq_lens, nv, max_len, S, chunk, nc, v, &W_b, &S_b);  // every wave computes the same values
     const int Sb = min(S_b, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold rows
     if (Sb == 0) {
         for (int c = tid; c < D; c += kMergeThreads) o[c] = 0.f;
@@ -195,6 +195,27 @@ hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dty
         hipLaunchKernelGGL(k, grid, block, 0, stream, nv, Q, qw, H, d_h, r, max_len, chunk, num_splits, seq_lens,
                            (const uint16_t*)B_v, out, ws);
     }
+    return hipGetLastError();
+}
+
+// The split plan on its own: one wave per sequence b writes W_b (its first workgroup, the index of its first
+// partial record) and S_b (its split count), as the split and merge kernels of a launch with these arguments
+// compute them.
+__global__ void __launch_bounds__(64) split_plan_kernel(int batch, int max_len, int append_cap, int chunk, int S,
+                                                       const int32_t* __restrict__ seq_lens,
+                                                       int32_t* __restrict__ first_wg, int32_t* __restrict__ splits) {
+    int W_b, S_b;
+    sequence_splits(seq_lens, batch, max_len, S, chunk, 1, (int)blockIdx.x, &W_b, &S_b, append_cap);
+    if (threadIdx.x == 0) {
+        first_wg[blockIdx.x] = W_b;
+        splits[blockIdx.x] = S_b;
+    }
+}
+
+hipError_t launch_split_plan(int batch, int max_len, int append_cap, int chunk, int num_splits,
+                             const int32_t* seq_lens, int32_t* first_wg, int32_t* splits, hipStream_t stream) {
+    hipLaunchKernelGGL(split_plan_kernel, dim3(batch), dim3(64), 0, stream, batch, max_len, append_cap, chunk,
+                       num_splits, seq_lens, first_wg, splits);
     return hipGetLastError();
 }
 

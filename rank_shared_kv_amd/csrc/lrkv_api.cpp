@@ -116,8 +116,9 @@ int env_int(const char* name, int dflt) {
 // Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes
 // are known on the host without a device.  A plan is (G workgroups for the
 // whole batch, granule g in rows).  On the device the G workgroups are dealt
-// to the sequences in proportion to their lengths, at least one each
-// (lrkv_device.hpp); split s of sequence b takes the g-row tiles s, s + S_b,
+// to the sequences by their lengths, at least one each (lrkv_device.hpp:
+// the fewest splits under a common cap on a row lane's blocks when that cap
+// is long, else in proportion to the lengths); split s of sequence b takes the g-row tiles s, s + S_b,
 // ... of the sequence and writes partial record W_b + s.  G aims at one
 // resident round of workgroups (MI355X has 256 CUs; the matrix-core kernels
 // hold `occupancy` workgroups per CU), never fewer than one per sequence nor
@@ -350,6 +351,21 @@ int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* 
     if (!plan_split(*dims, max_len, &p)) return 0;
     if (chunk_tokens) *chunk_tokens = p.chunk;
     return p.num_splits;
+}
+
+lrkv_status lrkv_decode_split_plan(const lrkv_dims* dims, int32_t max_len, const int32_t* seq_lens, int32_t append,
+                                   int32_t* first_wg, int32_t* splits, void* stream) {
+    lrkv::SplitPlan plan;
+    LRKV_TRY(check_decode_common(dims, max_len, &plan));
+    if (append != 0 && append != 1) return fail(LRKV_ERR_INVALID_ARG, "append=%d is neither 0 nor 1", append);
+    LRKV_TRY(need_ptr(seq_lens, "seq_lens"));
+    LRKV_TRY(need_ptr(first_wg, "first_wg"));
+    LRKV_TRY(need_ptr(splits, "splits"));
+    if (plan.num_splits == 0) return ok();  // max_len 0: no split workgroups, nothing written
+    const hipError_t e = lrkv::launch_split_plan(dims->batch, max_len, append ? dims->L_cap : 0, plan.chunk,
+                                                 plan.num_splits, seq_lens, first_wg, splits, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "split plan kernel launch");
+    return ok();
 }
 
 lrkv_status lrkv_absorb_query(const lrkv_dims* dims, const void* q, const void* B_k, float* p, void* stream) {

@@ -113,6 +113,9 @@ hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t
 hipError_t launch_merge(int batch, int Q, int qw, int H, int d_h, int r, int dtype, int max_len, int chunk,
                         int num_splits, const int32_t* seq_lens, const void* B_v, float* out, const float* ws,
                         hipStream_t stream);
+// the split plan of a single-query launch (append_cap: 0, or L_cap for the fused step): W_b and S_b per sequence
+hipError_t launch_split_plan(int batch, int max_len, int append_cap, int chunk, int num_splits,
+                             const int32_t* seq_lens, int32_t* first_wg, int32_t* splits, hipStream_t stream);
 int general_rows_per_tile();  // rows one general-kernel split advances per step
 hipError_t launch_project_append(int batch, int H, int d_h, int r, int L_cap, int dtype, int d_model, void* k_shared,
                                  void* v_shared, void* z_k, void* z_v, int32_t* seq_lens, const void* x,

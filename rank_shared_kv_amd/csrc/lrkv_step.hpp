@@ -223,7 +223,7 @@ __device__ __forceinline__ void merge_body(int h, int row, int nv, int Q, int qw
 
     const int Lb = max(0, clamped_len(seq_lens, v, max_len, append_cap) - (nreal - 1 - qi));
     int W_b, S_b;
-    sequence_splits(seq_lens, nv, max_len, S, v, &W_b, &S_b, append_cap);  // every wave computes the same values
+    sequence_splits(seq_lens, nv, max_len, S, chunk, nc, v, &W_b, &S_b, append_cap);  // every wave: the same values
     const int Sb = min(S_b, (Lb + chunk - 1) / chunk);  // splits s with s * granule < L_b hold rows
     wait(S_b);
     if (Sb == 0) {

@@ -236,10 +236,18 @@ def test_near_cancelling_key_terms():
     say(f"  cancelling heads alone: max rel err {err:.3e}")
 
 
-def _splits_of(G, lens, b):
-    """Sequence b's split count under the length-proportional plan: sequence i starts at workgroup
-    i + floor((G - batch) * C_{i-1} / T), C the running count of 32-row blocks, T their total."""
+def _splits_of(G, lens, b, ntl):
+    """Sequence b's split count (one query set per sequence, at most 64 sequences).  With the least cap M whose
+    splits S_i = max(1, ceil(n_i / (M ntl))) add up to at most G (n_i the 32-row block counts): those S_i when
+    M >= 8, else the length-proportional plan, where sequence i starts at workgroup i + floor((G - batch) C_{i-1} / T),
+    C the running count of blocks and T their total."""
     nbs = [(int(n) + 31) // 32 for n in lens]
+    need = lambda per: sum(max(1, -(-n // per)) for n in nbs)
+    M = 1
+    while need(M * ntl) > G:
+        M += 1
+    if M >= 8:
+        return max(1, -(-nbs[b] // (M * ntl)))
     T, extra = sum(nbs), G - len(lens)
     W = lambda i: i + (extra * sum(nbs[:i])) // T if T else i
     return W(b + 1) - W(b)
@@ -250,7 +258,7 @@ def _last_row_of_last_split(G, lens, b, ntl):
     split kernels' block deal (block s*NTL + tl + k*S_b*NTL) and their per-sequence rotation."""
     L = int(lens[b])
     nb = (L + 31) // 32
-    S = _splits_of(G, lens, b)
+    S = _splits_of(G, lens, b, ntl)
     s, tl = S - 1, ntl - 1
     first, step = s * ntl + tl, S * ntl
     nmine = (nb - first + step - 1) // step if nb > first else 0
