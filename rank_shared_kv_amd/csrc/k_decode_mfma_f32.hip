@@ -7,9 +7,19 @@
 // sec. 3, where rank 0 removes the private branch).  Per sequence b and head h:
 //   s_j = q_h . k_j / sqrt(d_h),  a = softmax(s),  o_h = sum_j a_j v_j.
 // Both products are dense contractions over all heads of a group at once, so
-// both run on the fp32 matrix cores (v_mfma_f32_16x16x4f32: fp32 products,
-// fp32 accumulation).  The kernel writes the same per-split online-softmax
-// records as the bf16 kernel; the merge kernel combines them.
+// both run on the matrix cores with fp32 accumulation.  The value product uses
+// v_mfma_f32_16x16x4f32 (fp32 products).  The score product takes its fp32
+// operands to the bf16 matrix cores: every key and query value x is split
+// exactly into three bf16 parts, x = x1 + x2 + x3 (x1 is x with the low 16
+// bits of its pattern cleared, x2 the same of x - x1, x3 the rest, at most 8
+// significant bits), and k q is taken as the six terms k1q1 + k1q2 + k2q1 +
+// k1q3 + k2q2 + k3q1 on v_mfma_f32_16x16x32_bf16; the three left out are below
+// 2^-21 |k q| together, against the 2^-24 of an fp32 product's rounding and
+// the accumulation error of a 128-term dot product.  That is 16 matrix-core
+// cycles per 32-column chunk and term, 96 for what takes 256 on the fp32
+// matrix cores, at about five VALU operations per key value for the split.
+// The kernel writes the same per-split online-softmax records as the bf16
+// kernel; the merge kernel combines them.
 //
 // Work decomposition: a workgroup of 4 waves owns one (b, split), splits dealt
 // to sequences by length; each wave is one row lane of 32-row blocks (blocks
@@ -20,10 +30,11 @@
 //   online softmax on S^T in the MFMA result layout (lane = head, 8 rows)
 //   O^T[d_h x 16 heads]    += V^T[d_h x 32 rows] P^T
 // The contraction index of each product is permuted so that every lane loads
-// 16 contiguous bytes per global load and no operand goes through LDS:
-//   * score product, k-step t of a half: lane (row n, group g) supplies
-//     K[n][16 (t/4) + 4 g + t%4] and Q[head n][same column] -- four
-//     consecutive k-steps come from one 16-byte load;
+// 16 contiguous bytes per global load and no cache operand goes through LDS:
+//   * score product, 32-column chunk j of a half: lane (row n, group g)
+//     supplies the parts of K[n][32 j + 4 g + e] and K[n][32 j + 16 + 4 g + e]
+//     (e < 4; two 16-byte loads) and, from LDS where they are split once, of
+//     q[head n][the same columns];
 //   * value product, k-step t (rows of half t/4): lane (column slot n, group g)
 //     supplies V[16 (t/4) + 4 g + t%4][64 p + 4 n + s] for column block
 //     cb = 4 p + s, and P^T[that row][head] is exactly the softmax weight the
@@ -44,6 +55,32 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+
+// (a.hi16, b.hi16): the high halves of two fp32 bit patterns, packed as two bf16 values
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// Exact three-way bf16 split of 8 fp32 values x = x1 + x2 + x3: x1 is x with its low 16 bits cleared, x2 the same
+// of x - x1 (exact), x3 = x - x1 - x2 (exact, at most 8 significant bits); packed as three bf16x8 operands.
+__device__ __forceinline__ void split3(const float* x, v4u_t& p1, v4u_t& p2, v4u_t& p3) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t u0 = __float_as_uint(x[2 * j]), u1 = __float_as_uint(x[2 * j + 1]);
+        const float r0 = x[2 * j] - __uint_as_float(u0 & 0xffff0000u);
+        const float r1 = x[2 * j + 1] - __uint_as_float(u1 & 0xffff0000u);
+        const uint32_t w0 = __float_as_uint(r0), w1 = __float_as_uint(r1);
+        const float t0 = r0 - __uint_as_float(w0 & 0xffff0000u);
+        const float t1 = r1 - __uint_as_float(w1 & 0xffff0000u);
+        p1[j] = pack_hi(u0, u1);
+        p2[j] = pack_hi(w0, w1);
+        p3[j] = pack_hi(__float_as_uint(t0), __float_as_uint(t1));
+    }
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf(const v4u_t& a, const v4u_t& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+}
 
 constexpr int kRows = 32;
 constexpr int kWaves = 4;
@@ -58,9 +95,9 @@ struct CfgF32 {
     static constexpr int NU = 8;                      // units per block: 4 key quarters, then 4 value quarters
     static constexpr int NSLOT = OCC == 2 ? 4 : 8;    // ring depth (divides NU); two waves per SIMD hide latency too
     static constexpr int CB = D / 16;                 // column blocks of the value product
-    static constexpr int QS = D + 4;                  // floats per q row in LDS
+    static constexpr int KB = D / 32;                 // 32-column chunks of the score contraction
     static constexpr int REC = ((D + 2) + 3) & ~3;
-    static constexpr int Q_BYTES = NHG * 16 * QS * 4;
+    static constexpr int Q_BYTES = 3 * NHG * KB * 64 * 16;  // q's three bf16 parts in each lane's operand order
     static constexpr int MW_BYTES = kWaves * NHG * 16 * 4;
     static constexpr int LDS_BYTES = Q_BYTES + MW_BYTES + H * REC * 4;
     static_assert(D % 64 == 0, "head width");
@@ -76,7 +113,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     using C = CfgF32<D, H, OCC>;
     constexpr int NSLOT = C::NSLOT, NU = C::NU, UDW = C::UDW, NHG = C::NHG;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    float* q_lds = (float*)lds;                              // [NHG * 16][QS] query rows (zero rows pad)
+    v4u_t* qp_lds = (v4u_t*)lds;                             // [3][NHG][KB][64 lanes] q's bf16 parts
     float* mw_lds = (float*)(lds + C::Q_BYTES);              // [waves][NHG * 16] running maxima
     float* mg = (float*)(lds + C::Q_BYTES + C::MW_BYTES);   // [H][REC] merged records
 
@@ -92,10 +129,24 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     const float scale = kLog2e / sqrtf((float)D);
 
     {
+        // lane (head n, group g) of chunk j supplies q[head][32 j + 4 g + e] and q[head][32 j + 16 + 4 g + e], e < 4,
+        // the columns the key operand's lane (row n, g) holds
         const float* qg = (const float*)a.q + (size_t)b * H * D;
-        for (int i = tid; i < NHG * 16 * D; i += kWaves * 64) {
-            const int h = i / D, c = i - h * D;
-            q_lds[h * C::QS + c] = (h < H) ? qg[(size_t)h * D + c] : 0.f;
+        for (int i = tid; i < NHG * C::KB * 64; i += kWaves * 64) {
+            const int ln = i & 63, gk = i >> 6;
+            const int g = gk / C::KB, j = gk - g * C::KB;
+            const int head = 16 * g + (ln & 15), gg = ln >> 4;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = head < H ? qg[(size_t)head * D + 32 * j + 4 * gg + e] : 0.f;
+                x[4 + e] = head < H ? qg[(size_t)head * D + 32 * j + 16 + 4 * gg + e] : 0.f;
+            }
+            v4u_t p1, p2, p3;
+            split3(x, p1, p2, p3);
+            qp_lds[(0 * NHG * C::KB + gk) * 64 + ln] = p1;
+            qp_lds[(1 * NHG * C::KB + gk) * 64 + ln] = p2;
+            qp_lds[(2 * NHG * C::KB + gk) * 64 + ln] = p3;
         }
     }
     __syncthreads();
@@ -204,18 +255,31 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
                         for (int c = 0; c < NCH; ++c) s_acc[g][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
-                for (int mm = 0; mm < KH; ++mm) {
-                    const int m = KH * (u & 1) + mm;
-                    f32x4_t qv[NHG];
+                for (int pp = 0; pp < KH / 2; ++pp) {
+                    // loads 2 pp and 2 pp + 1 of the unit: columns 32 j + 4 g4 + e and 32 j + 16 + 4 g4 + e
+                    const int j = (KH / 2) * (u & 1) + pp;
+                    float x[8];
 #pragma unroll
-                    for (int g = 0; g < NHG; ++g)
-                        qv[g] = *(const f32x4_t*)(q_lds + (16 * g + n16) * C::QS + 4 * g4 + 16 * m);
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = __uint_as_float(cur[4 * (2 * pp) + e]);
+                        x[4 + e] = __uint_as_float(cur[4 * (2 * pp + 1) + e]);
+                    }
+                    v4u_t k1, k2, k3;
+                    split3(x, k1, k2, k3);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int g = 0; g < NHG; ++g)
-                            s_acc[g][m % NCH] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                __uint_as_float(cur[4 * mm + j]), qv[g][j], s_acc[g][m % NCH], 0, 0, 0);
+                    for (int g = 0; g < NHG; ++g) {
+                        const int gk = g * C::KB + j;
+                        const v4u_t q1 = qp_lds[(0 * NHG * C::KB + gk) * 64 + lane];
+                        const v4u_t q2 = qp_lds[(1 * NHG * C::KB + gk) * 64 + lane];
+                        const v4u_t q3 = qp_lds[(2 * NHG * C::KB + gk) * 64 + lane];
+                        f32x4_t c = s_acc[g][pp % NCH];
+                        c = mfma_bf(k3, q1, c);  // the six leading terms, smallest first
+                        c = mfma_bf(k2, q2, c);
+                        c = mfma_bf(k1, q3, c);
+                        c = mfma_bf(k2, q1, c);
+                        c = mfma_bf(k1, q2, c);
+                        s_acc[g][pp % NCH] = mfma_bf(k1, q1, c);
+                    }
                 }
                 if (u & 1) {
 #pragma unroll
