@@ -319,6 +319,27 @@ def test_dominant_row_mqa_fp32():
     _check_vs_reference(w, dev, got, pairs, "dominant mqa fp32", mqa=True)
 
 
+def test_mqa_fp32_keys_of_wide_range():
+    """fp32 with r = 0: the score product takes each key and query value as three bf16 parts; keys whose rows
+    span 2^-12 to 2^2 in magnitude (every element with a full 24-bit significand) and queries scaled per head
+    over 2^-4 to 2^2 exercise all three parts and leave some heads' softmax nearly flat and others peaked on
+    a few rows (logits up to about 40).  Against the reference within the fp32 tolerance."""
+    w = synth.WORKLOADS["ragged_mqa_fp32"].with_(name="wide_mqa", batch=3, L=3000, L_cap=3008, ragged_lo=None)
+    lens = np.array([3000, 1777, 129], dtype=np.int32)
+    dev = sdev.fill_layer(w, 0, L_cap=3008, lengths=lens)
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    row_scale = torch.pow(2.0, torch.empty((3, 3008, 1)).uniform_(-10.0, 3.0, generator=g))
+    mant = 1.0 + torch.rand((3, 3008, w.d_h), generator=g)  # significands in [1, 2): low bits set
+    sign = torch.where(torch.rand((3, 3008, w.d_h), generator=g) < 0.5, -1.0, 1.0)
+    dev["k_shared"].copy_((sign * mant * row_scale / 4.0).float().cuda())
+    head_scale = torch.pow(2.0, torch.linspace(-4.0, 2.0, w.H)).view(1, w.H, 1)
+    dev["q"].copy_((dev["q"].cpu() * head_scale).float().cuda())
+    say("[case] fp32 r = 0, keys over 2^-12..2^2, queries over 2^-4..2^2 per head")
+    got = gpu_decode(w, dev, 3000, L_cap=3008)
+    pairs = [(b, h) for b in range(3) for h in range(0, w.H, 3)]
+    _check_vs_reference(w, dev, got, pairs, "wide-range keys, mqa fp32", mqa=True)
+
+
 # ---------------------------------------------------------------------------------------------------------
 # rank 0 at the ragged fp32 shape on one kernel
 # ---------------------------------------------------------------------------------------------------------
