@@ -91,9 +91,17 @@ struct CfgF32 {
     static constexpr int NTL = kWaves;                // row lanes per workgroup: one per wave
     static constexpr int KLD = D / 16;                // 16-byte loads per lane per key half
     static constexpr int VP = D / 64;                 // 64-column blocks of a value row
-    static constexpr int UDW = D / 8;                 // dwords per unit (a quarter of the key or value rows)
-    static constexpr int NU = 8;                      // units per block: 4 key quarters, then 4 value quarters
-    static constexpr int NSLOT = OCC == 2 ? 4 : 8;    // ring depth (divides NU); two waves per SIMD hide latency too
+    static constexpr int KPH = D == 128 ? 4 : 2;      // key units per 16-row half
+    static constexpr int LK = KLD / KPH;              // 16-byte key loads per lane and unit (even: whole chunks)
+    static constexpr int VPU = D == 128 ? 4 : 2;      // value units per half
+    static constexpr int TTU = 4 / VPU;               // row offsets tt per value unit
+    static constexpr int UDW = 4 * LK;                // dwords per unit
+    static constexpr int NU = 2 * KPH + 2 * VPU;      // units per block: the key units, then the value units
+    // ring depth (divides NU), 64 dwords at two waves per SIMD, 128 at one: at d_h = 128 the ring holds 8 or 16
+    // units of two loads, 14 or 30 loads ahead (units of four loads in 4 slots kept 12 ahead: 196.8 against
+    // 193.4 us on the ragged fp32 pass); a 16-unit ring at two waves per SIMD spills
+    static constexpr int NSLOT = D == 128 ? (OCC == 2 ? 8 : 16) : (OCC == 2 ? 4 : 8);
+    static_assert(UDW == 4 * TTU * (D / 64) && LK % 2 == 0 && NU % NSLOT == 0, "unit shape");
     static constexpr int CB = D / 16;                 // column blocks of the value product
     static constexpr int KB = D / 32;                 // 32-column chunks of the score contraction
     static constexpr int REC = ((D + 2) + 3) & ~3;
@@ -160,20 +168,20 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     const uint32_t vo_k = (uint32_t)n16 * row_bytes + 16 * g4;       // row n16 of the half, columns 4 g4 + 16 m
     const uint32_t vo_v = (uint32_t)(4 * g4) * row_bytes + 16 * n16;  // rows 4 g4 + tt, columns 64 p + 4 n16
 
-    // Units of a block (8, equal size):
-    //   u = 0..3  key half u/2, 16-column blocks m of part u%2 (m in [KLD/2 * (u%2), KLD/2 * (u%2 + 1)))
-    //   u = 4..7  value half (u-4)/2, rows 4 g4 + tt with tt in {2 ((u-4)%2), 2 ((u-4)%2) + 1}
-    constexpr int KH = C::KLD / 2;
+    // Units of a block (NU, equal size, LK 16-byte loads per lane):
+    //   u < 2 KPH        key half u / KPH, 16-column blocks m = LK (u % KPH) .. LK (u % KPH) + LK - 1
+    //   u = 2 KPH + w    value half w / VPU, rows 4 g4 + tt with tt = TTU (w % VPU) .. TTU (w % VPU) + TTU - 1
+    constexpr int KPH = C::KPH, LK = C::LK, VPU = C::VPU, TTU = C::TTU, NKU = 2 * KPH;
     uint32_t ring[NSLOT][UDW];
     // a descriptor of no bytes: loads through it are out of range, return zeros and touch no memory (the
     // prefetch issued during a row lane's last block, which has no next block)
     const __amdgpu_buffer_rsrc_t rs_none = buf_rsrc(a.k_shared, 0);
     auto issue = [&](int u, int t0, int slot, bool live) {
-        if (u < 4) {
-            const int so = (t0 + 16 * (u >> 1)) * (int)row_bytes;
+        if (u < NKU) {
+            const int so = (t0 + 16 * (u / KPH)) * (int)row_bytes;
 #pragma unroll
-            for (int mm = 0; mm < KH; ++mm) {
-                const int m = KH * (u & 1) + mm;
+            for (int mm = 0; mm < LK; ++mm) {
+                const int m = LK * (u % KPH) + mm;
                 const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(live ? rs_k : rs_none, vo_k + 64 * m, so, 0);
                 ring[slot][4 * mm] = v.x;
                 ring[slot][4 * mm + 1] = v.y;
@@ -181,10 +189,10 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
                 ring[slot][4 * mm + 3] = v.w;
             }
         } else {
-            const int so = (t0 + 16 * ((u - 4) >> 1)) * (int)row_bytes;
+            const int so = (t0 + 16 * ((u - NKU) / VPU)) * (int)row_bytes;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int tt = 2 * ((u - 4) & 1) + k;
+            for (int k = 0; k < TTU; ++k) {
+                const int tt = TTU * ((u - NKU) % VPU) + k;
 #pragma unroll
                 for (int p = 0; p < C::VP; ++p) {
                     const v4u_t v = __builtin_amdgcn_raw_buffer_load_b128(live ? rs_v : rs_none,
@@ -244,20 +252,20 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
             }
             __builtin_amdgcn_sched_barrier(0);
             uint32_t* cur = ring[u % NSLOT];
-            if (u < 4) {
+            if (u < NKU) {
                 // S^T of key half u/2 on the matrix cores, 16-column blocks of part u%2; q fragments from
                 // LDS.  Two independent accumulation chains are interleaved (the head groups, or with one
                 // group its even and odd column blocks) so consecutive MFMAs never wait on each other.
-                if ((u & 1) == 0) {
+                if (u % KPH == 0) {
 #pragma unroll
                     for (int g = 0; g < NHG; ++g)
 #pragma unroll
                         for (int c = 0; c < NCH; ++c) s_acc[g][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
-                for (int pp = 0; pp < KH / 2; ++pp) {
+                for (int pp = 0; pp < LK / 2; ++pp) {
                     // loads 2 pp and 2 pp + 1 of the unit: columns 32 j + 4 g4 + e and 32 j + 16 + 4 g4 + e
-                    const int j = (KH / 2) * (u & 1) + pp;
+                    const int j = (LK / 2) * (u % KPH) + pp;
                     float x[8];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -281,12 +289,12 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
                         s_acc[g][pp % NCH] = mfma_bf(k1, q1, c);
                     }
                 }
-                if (u & 1) {
+                if (u % KPH == KPH - 1) {
 #pragma unroll
                     for (int g = 0; g < NHG; ++g)
-                        s_sh[g][u >> 1] = (NCH == 2) ? s_acc[g][0] + s_acc[g][NCH - 1] : s_acc[g][0];
+                        s_sh[g][u / KPH] = (NCH == 2) ? s_acc[g][0] + s_acc[g][NCH - 1] : s_acc[g][0];
                 }
-                if (u == 3) {
+                if (u == NKU - 1) {
                     // online softmax: lane (head n16 of group g, g4) holds rows 4 g4 + i and 16 + 4 g4 + i
 #pragma unroll
                     for (int g = 0; g < NHG; ++g) {
@@ -316,12 +324,12 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
                     }
                 }
             } else {
-                const int h = (u - 4) >> 1;      // value half: rows 16 h + 4 g4 + tt
-                const int tp = 2 * ((u - 4) & 1);  // this unit holds tt = tp, tp + 1
+                const int h = (u - NKU) / VPU;            // value half: rows 16 h + 4 g4 + tt
+                const int tp = TTU * ((u - NKU) % VPU);  // this unit holds tt = tp .. tp + TTU - 1
                 if (nvalid < kRows) {
                     // last block of the sequence: rows past the end hold arbitrary values; zero them
 #pragma unroll
-                    for (int k = 0; k < 2; ++k)
+                    for (int k = 0; k < TTU; ++k)
                         if (16 * h + 4 * g4 + tp + k >= nvalid) {
 #pragma unroll
                             for (int e = 0; e < 4 * C::VP; ++e) cur[4 * k * C::VP + e] = 0u;
@@ -330,7 +338,7 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
 #pragma unroll
                 for (int g = 0; g < NHG; ++g)
 #pragma unroll
-                    for (int k = 0; k < 2; ++k)
+                    for (int k = 0; k < TTU; ++k)
 #pragma unroll
                         for (int p = 0; p < C::VP; ++p)
 #pragma unroll
