@@ -137,6 +137,26 @@ def test_r0_fp32_edges_match_mqa_reference(H, d_h):
     assert torch.equal(got[0], torch.zeros_like(got[0]))  # empty sequence
 
 
+@pytest.mark.parametrize("occ", [1, 2])
+@pytest.mark.parametrize("dtype,H,d_h,r", [("f32", 32, 128, 0), ("f32", 16, 64, 0), ("bf16", 32, 128, 64),
+                                           ("bf16", 16, 128, 48)])
+def test_occupancy_override(occ, dtype, H, d_h, r, monkeypatch):
+    """LRKV_OCCUPANCY (a tuning override) selects the matrix-core kernels built for one or two waves per SIMD,
+    with their own register rings and a grid of 256 x occupancy workgroups: both against the reference."""
+    monkeypatch.setenv("LRKV_OCCUPANCY", str(occ))
+    w = synth.WORKLOADS["ragged"].with_(name=f"occ{occ}_{dtype}_{H}_{r}", batch=5, H=H, d_h=d_h, r=r, dtype=dtype,
+                                        L=2600, L_cap=2624, ragged_lo=None)
+    lens = np.array([2600, 31, 1200, 0, 777], dtype=np.int32)
+    G, chunk = lk.lrkv_decode_num_splits(dims_of(w, 2624), 2600)
+    assert G == min(256 * occ, 5 * ((2600 + chunk - 1) // chunk)) and chunk > 32, (G, chunk)
+    say(f"[case] occupancy {occ}: {dtype} H={H} d_h={d_h} r={r}, G={G}")
+    dev = sdev.fill_layer(w, 0, L_cap=2624, lengths=lens)
+    got = gpu_decode(w, dev, 2600, L_cap=2624)
+    assert torch.equal(got[3], torch.zeros_like(got[3]))
+    pairs = [(b, h) for b in (0, 1, 2, 4) for h in sorted({0, H // 2, H - 1})]
+    compare(w, got, oracle_pairs(w, 0, lens, pairs, mqa=(r == 0)), pairs, f"occupancy {occ}")
+
+
 def test_partial_plus_merge_equals_decode_and_is_deterministic():
     w = synth.WORKLOADS["small_bf16"]
     lens = synth.seq_lengths(w)
