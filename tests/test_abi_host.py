@@ -179,6 +179,22 @@ def test_max_len_and_workspace_rejected():
     assert _status(lk.lrkv_decode_partial, d, c, 256, A, A, 1 << 12, need - 4, 0) == lk.LRKV_ERR_WORKSPACE
 
 
+def test_split_plan_entry_checks_before_any_launch():
+    """lrkv_decode_split_plan rejects invalid dims, max_len outside [0, L_cap], an append flag other than 0 or 1
+    and NULL pointers before anything is enqueued; with max_len 0 there is nothing to plan (no launch)."""
+    d = _dims()
+    bad = lk.make_dims(0, 8, 64, 8, 256, 1)
+    assert _status(lk.lrkv_decode_split_plan, bad, 10, A, 0, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode_split_plan, d, 257, A, 0, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode_split_plan, d, -1, A, 0, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    assert _status(lk.lrkv_decode_split_plan, d, 256, A, 2, A, A, 0) == lk.LRKV_ERR_INVALID_ARG
+    for i in range(3):  # seq_lens, first_wg, splits
+        args = [A, A, A]
+        args[i] = None
+        assert _status(lk.lrkv_decode_split_plan, d, 256, args[0], 1, args[1], args[2], 0) == lk.LRKV_ERR_INVALID_ARG, i
+    assert _status(lk.lrkv_decode_split_plan, d, 0, A, 0, A, A, 0) == lk.LRKV_OK
+
+
 def test_noalloc_checks_before_any_launch():
     """lrkv_decode_noalloc: the same argument checks as lrkv_decode, and a problem whose split records exceed
     its device scratch is rejected with LRKV_ERR_WORKSPACE before anything is enqueued."""
