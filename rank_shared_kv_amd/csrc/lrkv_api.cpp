@@ -113,23 +113,18 @@ int env_int(const char* name, int dflt) {
     return (end && *end == '\0' && x > 0 && x < (1L << 30)) ? (int)x : dflt;
 }
 
-// Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes
-// are known on the host without a device.  A plan is (G workgroups for the
-// whole batch, granule g in rows).  On the device the G workgroups are dealt
-// to the sequences by their lengths, at least one each (lrkv_device.hpp:
-// the fewest splits under a common cap on a row lane's blocks when that cap
-// is long, else in proportion to the lengths); split s of sequence b takes the g-row tiles s, s + S_b,
-// ... of the sequence and writes partial record W_b + s.  G aims at one
-// resident round of workgroups (MI355X has 256 CUs; the matrix-core kernels
-// hold `occupancy` workgroups per CU), never fewer than one per sequence nor
-// more than one per tile of every sequence.  The plan does not depend on r
-// within a kernel, so problems differing only in rank reduce in the same order.
-// Tuning overrides (read at every call, so they must not change between a
-// workspace query and the decode that uses it): LRKV_OCCUPANCY (1 or 2 waves
-// per SIMD; defaults: 2 for the fp32 matrix-core kernel, 2 for the bf16 one at
-// batch >= 32 and 1 below),
-// LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch), LRKV_FORCE_GENERAL (1: the general
-// kernel for the plain decode).
+// Split planning.  Pure arithmetic on (dims, max_len) so that workspace sizes are known on the host without a
+// device.  A plan is (G workgroups for the whole batch, granule g in rows).  On the device the G workgroups are
+// dealt to the sequences by their lengths, at least one each (lrkv_device.hpp: the fewest splits under a common
+// cap on a row lane's blocks when that cap is long, else in proportion to the lengths); split s of sequence b
+// takes the g-row tiles s, s + S_b, ... of the sequence and writes partial record W_b + s.  G aims at one
+// resident round of workgroups (MI355X has 256 CUs; the matrix-core kernels hold `occupancy` workgroups per
+// CU), never fewer than one per sequence nor more than one per tile of every sequence.  The plan does not depend
+// on r within a kernel, so problems differing only in rank reduce in the same order.
+// Tuning overrides (read at every call, so they must not change between a workspace query and the decode that
+// uses it): LRKV_OCCUPANCY (1 or 2 waves per SIMD; defaults: 2 for the fp32 matrix-core kernel, 2 for the bf16
+// one at batch >= 32 and 1 below), LRKV_TARGET_WGS (G before clamping), LRKV_SPLITS (G = splits x batch),
+// LRKV_FORCE_GENERAL (1: the general kernel for the plain decode).
 constexpr long kMaxExtraSplits = 8192;  // G - batch: bounds the merge kernel's LDS
 
 // Which decode the plan is for.  The normalised variant's bf16 matrix-core kernel is built for one wave per
