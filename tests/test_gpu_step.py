@@ -126,6 +126,24 @@ def test_step_two_waves_per_simd():
     _check_equal(case, steps=2)
 
 
+def test_step_fewest_splits_plan_with_edge_lengths():
+    """Long ragged sequences whose plan gives each sequence the fewest splits under a common lane cap (some
+    workgroups of the launch have no split), with an empty sequence, one that grows to L_cap and a full one:
+    the fused step equals the two calls bit for bit over three steps."""
+    case = ("bf16", 6, 32, 128, 64, [32768, 0, 32799, 32800, 31000, 20000], 32800, 32800)
+    w, dev, _, max_len = _setup(case)
+    dims = dims_of(w)
+    G = lk.lrkv_decode_num_splits(dims, max_len)[0]
+    W = torch.empty(6, dtype=torch.int32, device="cuda")
+    S = torch.empty(6, dtype=torch.int32, device="cuda")
+    lk.lrkv_decode_split_plan(dims, max_len, dev["seq_lens"], 1, W, S)
+    torch.cuda.synchronize()
+    S = S.cpu().tolist()
+    say(f"[case] decode step, fewest-splits plan: G={G}, splits {S}")
+    assert sum(S) < G and S[1] == 1
+    _check_equal(case)
+
+
 def test_step_many_merges_runs_the_calls():
     """A batch whose merge workgroups would not fit one resident round runs the two calls; same results."""
     case = _ragged_case(batch=40, H=32)
