@@ -173,11 +173,10 @@ size_t lrkv_decode_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
  * 32-row blocks of sequence b and M the least multiple of granule / 32 for
  * which S_b = max(1, ceil(n_b / M)) add up to at most G: when M is at least
  * 8 * granule / 32, each sequence has one query set and the batch holds at
- * most 64 sequences, sequence b gets those
- * S_b workgroups (workgroups past the sum have no split); otherwise they are
- * dealt in proportion to the n_b.  Split s of sequence b takes the
- * granule-row tiles s, s + S_b, s + 2 S_b, ... of the sequence and holds live
- * rows iff s * granule < seq_lens[b].
+ * most 64 sequences, sequence b gets those S_b workgroups (workgroups past
+ * the sum have no split); otherwise they are dealt in proportion to the n_b.
+ * Split s of sequence b takes the granule-row tiles s, s + S_b, s + 2 S_b, ...
+ * of the sequence and holds live rows iff s * granule < seq_lens[b].
  * Host arithmetic only.  Returns 0 for invalid dims or max_len == 0. */
 int32_t lrkv_decode_num_splits(const lrkv_dims* dims, int32_t max_len, int32_t* chunk_tokens);
 
