@@ -1,7 +1,11 @@
 """GPU parity over seeded random shapes and lengths: single-token decode, multi-token decode and the rotary
-variant, bf16 and fp32, against the fp64 reference through the C ABI.  Lengths mix random values with the
-tile and block edges (0, 1, 31-33, 63-65, 127-129, 255-257).  Metric and tolerances as in
-test_gpu_decode.py."""
+variant, bf16 and fp32, against the fp64 reference through the C ABI; and the fused decode step on random
+shapes, bit for bit against the separate calls (append and absorb, then decode) over two steps in a row.
+Lengths mix random values with the tile and block edges (0, 1, 31-33, 63-65, 127-129, 255-257).  Metric and
+tolerances as in test_gpu_decode.py.  LRKV_SWEEP_CASES and LRKV_SWEEP_SEED (read when the module is collected)
+widen the sweep or draw another one; the defaults are the committed cases."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -17,10 +21,11 @@ pytestmark = pytest.mark.gpu
 from gpu_harness import TOL, cache_of, dims_of, gpu_decode, say  # noqa: E402
 
 EDGE = [0, 1, 2, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 255, 256, 257]
-N_CASES = 36
+N_CASES = int(os.environ.get("LRKV_SWEEP_CASES", "36"))
+SEED = int(os.environ.get("LRKV_SWEEP_SEED", "20261202"))
 
 
-def _cases(seed=20261202, n=N_CASES):
+def _cases(seed=SEED, n=N_CASES):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -98,3 +103,32 @@ def test_random_shape_matches_reference(case):
     err = oracle.relative_error(got[seen].reshape(-1, d_h), ref[seen].reshape(-1, d_h))
     say(f"  max rel err {err:.3e} (tol {TOL[dtype]:.0e})")
     assert err <= TOL[dtype]
+
+
+def _step_cases(seed=SEED + 1, n=max(1, N_CASES // 3)):
+    """(dtype, batch, H, d_h, r, lengths, L_cap, max_len): mostly the fused path's shapes (bf16 matrix-core
+    kernel), some that run the two calls (fp32, r off the kernel's set); lengths include 0, full sequences
+    (L = L_cap, nothing appended) and sequences that grow past max_len (the row written but not seen)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = "bf16" if rng.random() < 0.8 else "f32"
+        H = int(rng.choice([8, 16, 32]))
+        d_h = int(rng.choice([64, 128]))
+        r = int(rng.choice([0, 8, 16, 32, 48, 64] if rng.random() < 0.85 else [4, 12, 20]))
+        B = int(rng.integers(1, 6))
+        L_cap = int(rng.choice([64, 256, 1024, 2048]))
+        lens = [int(rng.choice(EDGE)) if rng.random() < 0.4 else int(rng.integers(1, L_cap + 1)) for _ in range(B)]
+        lens = [min(x, L_cap) for x in lens]
+        max_len = L_cap if rng.random() < 0.7 else int(rng.integers(1, L_cap + 1))
+        out.append((dtype, B, H, d_h, r, tuple(lens), L_cap, max_len))
+    return out
+
+
+@pytest.mark.parametrize("case", _step_cases(),
+                         ids=lambda c: f"step_{c[0]}_B{c[1]}_H{c[2]}_d{c[3]}_r{c[4]}_cap{c[6]}_max{c[7]}")
+def test_random_step_matches_separate_calls(case):
+    from test_gpu_step import _check_equal
+    say(f"[case] step {case}")
+    dtype, B, H, d_h, r, lens, L_cap, max_len = case
+    _check_equal((dtype, B, H, d_h, r, list(lens), L_cap, max_len), steps=2)
