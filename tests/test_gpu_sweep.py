@@ -1,7 +1,8 @@
 """GPU parity over seeded random shapes and lengths: single-token decode, multi-token decode and the rotary
 variant, bf16 and fp32, against the fp64 reference through the C ABI; and the fused decode step on random
-shapes, bit for bit against the separate calls (append and absorb, then decode) over two steps in a row.
-Lengths mix random values with the tile and block edges (0, 1, 31-33, 63-65, 127-129, 255-257).  Metric and
+shapes, bit for bit against the separate calls (append and absorb, then decode) over two steps in a row; the
+paged cache (random page sizes, pool permutations with NaN spare pages) and the normalised variant on random
+shapes, checked as in test_gpu_paged.py and test_gpu_normed.py.  Lengths mix random values with the tile and block edges (0, 1, 31-33, 63-65, 127-129, 255-257).  Metric and
 tolerances as in test_gpu_decode.py.  LRKV_SWEEP_CASES and LRKV_SWEEP_SEED (read when the module is collected)
 widen the sweep or draw another one; the defaults are the committed cases."""
 import os
@@ -132,3 +133,57 @@ def test_random_step_matches_separate_calls(case):
     say(f"[case] step {case}")
     dtype, B, H, d_h, r, lens, L_cap, max_len = case
     _check_equal((dtype, B, H, d_h, r, list(lens), L_cap, max_len), steps=2)
+
+
+def _shape(rng, dtype):
+    """(H, d_h, r): the matrix-core kernels' shapes mostly, the general kernel's now and then."""
+    if rng.random() < 0.2:
+        return (4, 48, 12) if dtype == "bf16" else (4, 16, 4)
+    if dtype == "f32":
+        return (int(rng.choice([8, 32])), int(rng.choice([64, 128])), int(rng.choice([0, 8])))
+    return int(rng.choice([8, 16, 32])), int(rng.choice([64, 128])), int(rng.choice([0, 8, 16, 32, 48, 64]))
+
+
+def _paged_cases(seed=SEED + 2, n=max(1, N_CASES // 6)):
+    """(dtype, batch, H, d_h, r, L_cap, page_rows, lengths) as in test_gpu_paged.py."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        H, d_h, r = _shape(rng, dtype)
+        P = int(rng.choice([32, 64, 128, 256]))
+        L_cap = P * int(rng.integers(1, 9))
+        B = int(rng.integers(1, 5))
+        lens = [int(rng.choice(EDGE)) if rng.random() < 0.4 else int(rng.integers(0, L_cap + 1)) for _ in range(B)]
+        lens = [min(x, L_cap) for x in lens]
+        if max(lens) == 0:
+            lens[0] = 1
+        out.append((dtype, B, H, d_h, r, L_cap, P, lens))
+    return out
+
+
+def _normed_cases(seed=SEED + 3, n=max(1, N_CASES // 6)):
+    """(dtype, batch, H, d_h, r, lengths) as in test_gpu_normed.py."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        H, d_h, r = _shape(rng, dtype)
+        B = int(rng.integers(1, 5))
+        lens = [int(rng.choice(EDGE)) if rng.random() < 0.4 else int(rng.integers(1, 1200)) for _ in range(B)]
+        if max(lens) == 0:
+            lens[0] = 1
+        out.append((dtype, B, H, d_h, r, lens))
+    return out
+
+
+@pytest.mark.parametrize("case", _paged_cases(), ids=lambda c: f"paged_{c[0]}_B{c[1]}_H{c[2]}_d{c[3]}_r{c[4]}_P{c[6]}")
+def test_random_paged_decode(case):
+    from test_gpu_paged import test_paged_decode
+    test_paged_decode(case)
+
+
+@pytest.mark.parametrize("case", _normed_cases(), ids=lambda c: f"normed_{c[0]}_B{c[1]}_H{c[2]}_d{c[3]}_r{c[4]}")
+def test_random_normed_decode(case):
+    from test_gpu_normed import test_decode_normed_matches_reference
+    test_decode_normed_matches_reference(case)
