@@ -384,6 +384,7 @@ def main():
     p, out = ps[0], outs[0]
     S, chunk = lk.lrkv_decode_num_splits(dims, max_len)
     # plain decode: the whole step (append, absorb, split pass, merge) in one launch where the library fuses it
+    # (bf16 matrix-core shapes), or as the split pass with the append and the merge (fp32 rank 0)
     fused = plain and not args.separate and lk.lrkv_decode_step_fused(dims, max_len)
     if fused:
         nbytes_step = lk.lrkv_decode_step_workspace_bytes(dims, max_len)
@@ -679,7 +680,7 @@ def main():
                    "L": int(lens_full.max()), "L_cap": L_cap, "lengths": "uniform" if w.ragged_lo is None else
                    f"uniform integers in [{w.ragged_lo}, {w.L}]", "cache_dtype": w.dtype, "accumulate": "f32",
                    "splits": S, "chunk_tokens": chunk, "queries_per_sequence": Q, "layers": n_layers,
-                   "step_launches": 1 if fused else None},
+                   "step_launches": (2 if w.dtype == "f32" else 1) if fused else None},
         "hbm_gbps_step": step_gbps,
         "hbm_frac_step": step_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": split_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -688,7 +689,9 @@ def main():
                      "lrkv_decode_normed (split pass + merge)" if args.norm else
                      "lrkv_decode_paged (split pass + merge)" if args.paged else
                      "lrkv_decode_rope (split pass + merge)" if args.rope else
-                     "fused decode step (lrkv_decode_step: append, absorb, split pass and merge in one launch)"
+                     ("decode step (lrkv_decode_step: the split pass, which appends the token, then the merge; two "
+                      "launches)" if w.dtype == "f32" else
+                      "fused decode step (lrkv_decode_step: append, absorb, split pass and merge in one launch)")
                      if fused else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3,
                      "timing": f"HIP events around each of the {K * n_layers} decode launches of a second pass "

@@ -245,7 +245,10 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
  * every split of their sequence is done.  They hand work on through counters
  * in the workspace, each waiting only for workgroups placed before it in the
  * launch, so the absorb and the merge run beside the splits instead of in
- * launches of their own.  Other shapes run the two calls one after the other.
+ * launches of their own.  On the fp32 rank-0 matrix-core shapes (no absorb)
+ * the split pass appends the token in the same way and its last workgroup
+ * advances the lengths; the merge kernel follows (two launches, not three).
+ * Other shapes run the two calls one after the other.
  *   max_len    bound of the lengths after the append (as for lrkv_decode)
  *   workspace  device, >= lrkv_decode_step_workspace_bytes(dims, max_len) bytes,
  *              256-byte aligned; the split records, then the step's counter
@@ -260,8 +263,9 @@ lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, in
  * Calls that overlap in time on one workspace race. */
 size_t lrkv_decode_step_workspace_bytes(const lrkv_dims* dims, int32_t max_len);
 size_t lrkv_decode_step_sync_offset(const lrkv_dims* dims, int32_t max_len);
-/* 1 if lrkv_decode_step runs these dims and max_len as one launch, 0 if as the
- * two calls (or the arguments are invalid).  Host arithmetic only. */
+/* 1 if lrkv_decode_step folds the append into the decode's launches (one
+ * launch on the bf16 matrix-core shapes, two on the fp32 rank-0 ones), 0 if it
+ * runs the two calls (or the arguments are invalid).  Host arithmetic only. */
 int32_t lrkv_decode_step_fused(const lrkv_dims* dims, int32_t max_len);
 lrkv_status lrkv_decode_step(const lrkv_dims* dims, const lrkv_cache* cache, int32_t max_len, const void* k_new,
                              const void* v_new, const void* zk_new, const void* zv_new, const void* q,

@@ -21,6 +21,18 @@
 // The kernel writes the same per-split online-softmax records as the bf16
 // kernel; the merge kernel combines them.
 //
+// Decode step (STEP): the split pass also appends the new token.  Every
+// sequence is seen at its appended length, and the workgroup whose split owns
+// the appended row's block writes the row before its first load (the others
+// never read that block).  Every workgroup counts itself finished at its end;
+// the last of the launch, after every workgroup has read the lengths, grows
+// them and clears the counter.  The merge kernel then runs on the grown
+// lengths, which give it the plan this pass used, so the two launches give the
+// results of lrkv_append_absorb followed by lrkv_decode bit for bit; no
+// workgroup waits for another.  (Merging inside this launch, by the last split
+// of each sequence, made the step slower: one workgroup per sequence then
+// merges every head while the merge kernel spreads them over the GPU.)
+//
 // Work decomposition: a workgroup of 4 waves owns one (b, split), splits dealt
 // to sequences by length; each wave is one row lane of 32-row blocks (blocks
 // dealt round-robin over the sequence's (split, row lane) slots) and handles
@@ -43,6 +55,7 @@
 // group g) and register i, o_h at column 64 p + 16 g + 4 i + s.
 #include "lrkv_device.hpp"
 #include "lrkv_internal.hpp"
+#include "lrkv_step.hpp"
 
 // Cache policy of the value-row loads: non-temporal (2).  Each value row is read once, as whole 256-byte
 // pieces; the split pass runs 240-242 us against 245-249 us with ordinary loads.  The key loads read half
@@ -116,7 +129,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int D, int H, int OCC>
+// End of a decode-step workgroup: it counts itself finished; the last of the launch's workgroups grows the
+// lengths and clears the counters (every workgroup has read the lengths by then).  flag: one int of LDS.
+__device__ __forceinline__ void step_tail(const DecodeArgs& a, int* flag) {
+    __syncthreads();  // the workgroup is done with its LDS and its lengths
+    step_finish(a.sync, a.num_splits, a.batch, a.L_cap, a.seq_lens_rw, flag);
+}
+
+template <int D, int H, int OCC, bool STEP = false>
 __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(DecodeArgs a) {
     using C = CfgF32<D, H, OCC>;
     constexpr int NSLOT = C::NSLOT, NU = C::NU, UDW = C::UDW, NHG = C::NHG;
@@ -126,11 +146,33 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     float* mg = (float*)(lds + C::Q_BYTES + C::MW_BYTES);   // [H][REC] merged records
 
     const int tid = threadIdx.x, lane = tid & 63, tl = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, a.chunk, a.qgroup, blockIdx.x);
+    const SplitSlot wslot = split_slot(a.seq_lens, a.batch, a.max_len, a.num_splits, a.chunk, a.qgroup, blockIdx.x,
+                                       a.append_cap);
     const int b = wslot.b, split = wslot.s;
-    if (b < 0) return;
-    const int Lb = clamped_len(a.seq_lens, b, a.max_len);
-    if (split * a.chunk >= Lb) return;        // whole workgroup: no live rows in this split
+    if (b < 0) {
+        if constexpr (STEP) step_tail(a, (int*)lds);
+        return;
+    }
+    const int Lb = __builtin_amdgcn_readfirstlane(clamped_len(a.seq_lens, b, a.max_len, a.append_cap));
+    if constexpr (STEP) {
+        // the appended token's rows (row L0 = stored length, when below L_cap), written before anything reads
+        // them: by the workgroup whose split owns their block when the decode sees them, else by split 0
+        const int L0 = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+        if (L0 >= 0 && L0 < a.L_cap) {
+            const int owner = (L0 < Lb) ? ((L0 / kRows) % (wslot.S_b * C::NTL)) / C::NTL : 0;
+            if (split == owner) {
+                append_row_copy<float>(b, L0, H, D, 0, a.L_cap, (float*)a.k_shared, (float*)a.v_shared, nullptr,
+                                       nullptr, (const float*)a.k_new, (const float*)a.v_new, nullptr, nullptr,
+                                       nullptr, 0, 0);
+                __builtin_amdgcn_s_waitcnt(0);  // the rows are in this XCD's L2 before any wave loads them
+                __syncthreads();
+            }
+        }
+    }
+    if (split * a.chunk >= Lb) {  // whole workgroup: no live rows in this split
+        if constexpr (STEP) step_tail(a, (int*)lds);
+        return;
+    }
     const int nb = (Lb + kRows - 1) / kRows;
 
     const int n16 = lane & 15, g4 = lane >> 4;
@@ -399,22 +441,23 @@ __global__ void __launch_bounds__(kWaves * 64, OCC) split_mfma_f32_kernel(Decode
     }
     float* out = a.ws + (size_t)blockIdx.x * H * C::REC;  // record of workgroup w = W_b + split
     for (int i = tid; i < H * C::REC; i += kWaves * 64) out[i] = mg[i];
+    if constexpr (STEP) step_tail(a, (int*)lds);
 }
 
-template <int D, int H, int OCC>
+template <int D, int H, int OCC, bool STEP>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     using C = CfgF32<D, H, OCC>;
-    auto kern = split_mfma_f32_kernel<D, H, OCC>;
+    auto kern = split_mfma_f32_kernel<D, H, OCC, STEP>;
     hipLaunchKernelGGL(kern, dim3(a.num_splits), dim3(kWaves * 64), C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool STEP>
 hipError_t launch_h(const DecodeArgs& a, int occ, hipStream_t stream) {
     switch (a.H) {
-        case 8: return occ == 1 ? launch_one<D, 8, 1>(a, stream) : launch_one<D, 8, 2>(a, stream);
-        case 16: return occ == 1 ? launch_one<D, 16, 1>(a, stream) : launch_one<D, 16, 2>(a, stream);
-        case 32: return occ == 1 ? launch_one<D, 32, 1>(a, stream) : launch_one<D, 32, 2>(a, stream);
+        case 8: return occ == 1 ? launch_one<D, 8, 1, STEP>(a, stream) : launch_one<D, 8, 2, STEP>(a, stream);
+        case 16: return occ == 1 ? launch_one<D, 16, 1, STEP>(a, stream) : launch_one<D, 16, 2, STEP>(a, stream);
+        case 32: return occ == 1 ? launch_one<D, 32, 1, STEP>(a, stream) : launch_one<D, 32, 2, STEP>(a, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -432,8 +475,14 @@ bool mfma_f32_path_supports(int H, int d_h, int r, int dtype, int L_cap) {
 }
 
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream) {
-    if (a.d_h == 64) return launch_h<64>(a, occupancy, stream);
-    if (a.d_h == 128) return launch_h<128>(a, occupancy, stream);
+    if (a.d_h == 64) return launch_h<64, false>(a, occupancy, stream);
+    if (a.d_h == 128) return launch_h<128, false>(a, occupancy, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_step_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream) {
+    if (a.d_h == 64) return launch_h<64, true>(a, occupancy, stream);
+    if (a.d_h == 128) return launch_h<128, true>(a, occupancy, stream);
     return hipErrorInvalidValue;
 }
 

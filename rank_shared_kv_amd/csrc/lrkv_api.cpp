@@ -483,9 +483,12 @@ namespace {
 // The fused step runs where the plain plan takes the bf16 matrix-core kernel, the absorb has its one-wave
 // vector path (r == 0: no absorb) and the merge workgroups (one per (sequence, head), with the split kernel's
 // registers) fit in one resident round: the 64-sequence ragged batch (2048 of them, four rounds at two per CU)
-// ran 3% slower fused than as three launches.
+// ran 3% slower fused than as three launches.  On the fp32 rank-0 kernel (no absorb) the split pass appends the
+// token and grows the lengths, and the merge kernel follows: two launches instead of three.
 bool step_fused(const lrkv_dims& d, const lrkv::SplitPlan& plan) {
-    return plan.path == lrkv::SplitPath::kMfmaBf16 && plan.num_splits > 0 &&
+    if (plan.num_splits <= 0) return false;
+    if (plan.path == lrkv::SplitPath::kMfmaF32) return true;
+    return plan.path == lrkv::SplitPath::kMfmaBf16 &&
            (d.r == 0 || lrkv::absorb_wave_ok(d.d_h, d.r, 2)) && (long)d.batch * d.H <= 256L * plan.occupancy;
 }
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -574,6 +577,15 @@ lrkv_status lrkv_decode_step(const lrkv_dims* dims, const lrkv_cache* cache, int
     a.B_v = B_v;
     a.out = out;
     a.sync = (uint32_t*)((char*)workspace + lrkv_decode_step_sync_offset(dims, max_len));
+    if (plan.path == SplitPath::kMfmaF32) {
+        // the split pass appends and grows the lengths; the merge reads the grown lengths (the pass's plan)
+        hipError_t e = launch_step_mfma_f32(a, plan.occupancy, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "decode step split kernel launch");
+        e = launch_merge(dims->batch, 1, 1, dims->H, dims->d_h, dims->r, dims->dtype, max_len, plan.chunk,
+                         plan.num_splits, cache->seq_lens, B_v, out, (const float*)workspace, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+        return ok();
+    }
     const hipError_t e = launch_step_mfma(a, plan.occupancy, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode step kernel launch");
     return ok();

@@ -107,6 +107,9 @@ hipError_t launch_split_mfma(const DecodeArgs& a, int occupancy, hipStream_t str
 hipError_t launch_step_mfma(const DecodeArgs& a, int occupancy, hipStream_t stream);
 bool merge_wide(int num_splits, int n_virtual);  // the merge's split grouping (4 groups when true)
 hipError_t launch_split_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
+// decode step's split pass on the fp32 rank-0 matrix-core kernel: a carries the step fields (the pass appends the
+// token and its last workgroup grows the lengths); the merge kernel runs after it on the grown lengths
+hipError_t launch_step_mfma_f32(const DecodeArgs& a, int occupancy, hipStream_t stream);
 // Merge of a decode of `batch` cached sequences with Q query tokens each, split as virtual sequences of qw
 // tokens (ceil(Q / qw) per cached sequence; seq_lens are their lengths, num_splits the split launch's G);
 // out [batch][Q][H][d_h].  Single-token decode: Q = qw = 1.

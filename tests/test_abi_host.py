@@ -217,13 +217,15 @@ def test_noalloc_checks_before_any_launch():
 def test_decode_step_layout_and_fusion():
     """lrkv_decode_step: the workspace holds the split records (lrkv_decode_workspace_bytes, rounded up to 256
     bytes), then the counter words (4 header words and two per sequence); the step runs as one launch on the bf16
-    matrix-core shapes whose merge workgroups fit one resident round, as the two calls elsewhere; its argument
-    checks run before any launch."""
+    matrix-core shapes whose merge workgroups fit one resident round, as a split pass that appends plus the merge
+    on the fp32 rank-0 shapes, as the two calls elsewhere; its argument checks run before any launch."""
     for (B, H, d_h, r, L, dt, fused) in [(4, 32, 128, 64, 32768, 1, True), (16, 16, 128, 48, 8192, 1, True),
                                          (4, 18, 128, 55, 8192, 1, False),   # r = 55: the absorb's scalar path
                                          (64, 32, 128, 32, 32768, 1, False),  # 2048 merge workgroups
                                          (32, 16, 128, 32, 2528, 1, True), (2, 8, 64, 0, 64, 1, True),
-                                         (64, 32, 128, 0, 32768, 0, False), (2, 8, 64, 12, 64, 1, False)]:
+                                         (64, 32, 128, 0, 32768, 0, True), (4, 32, 128, 0, 32768, 0, True),
+                                         (64, 32, 128, 8, 32768, 0, False),  # fp32, r > 0: the general kernel
+                                         (2, 8, 64, 12, 64, 1, False)]:
         d = lk.make_dims(B, H, d_h, r, L, dt)
         rec = lk.lrkv_decode_workspace_bytes(d, L)
         off = lk.lrkv_decode_step_sync_offset(d, L)

@@ -125,7 +125,7 @@ def _bits(t):
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("name", ["long_context", "mid_24layer"])
+@pytest.mark.parametrize("name", ["long_context", "mid_24layer", "ragged_mqa_fp32"])
 def test_fused_step_full_size(name):
     """The decode step the benchmark times at these workloads (lrkv_decode_step: the new token appended, p, the
     split pass and the merge in one launch) at full size: every (sequence, head) pair against the reference on
@@ -143,22 +143,24 @@ def test_fused_step_full_size(name):
     outs, ps = [], []
     for fused, d in ((True, dev), (False, twin)):
         cache = cache_of(d, w.r)
-        p = torch.full((w.batch, w.H, w.r), float("nan"), dtype=torch.float32, device="cuda")
+        zk_new, zv_new = (rows["zk_new"], rows["zv_new"]) if w.r else (None, None)
+        B_k, B_v = (dev["B_k"], dev["B_v"]) if w.r else (None, None)
+        p = torch.full((w.batch, w.H, max(w.r, 1)), float("nan"), dtype=torch.float32, device="cuda")
         out = torch.full((w.batch, w.H, w.d_h), float("nan"), dtype=torch.float32, device="cuda")
         if fused:
             nbytes = lk.lrkv_decode_step_workspace_bytes(dims, max_len)
             ws = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
-            lk.lrkv_decode_step(dims, cache, max_len, rows["k_new"], rows["v_new"], rows["zk_new"], rows["zv_new"],
-                                dev["q"], dev["B_k"], dev["B_v"], p, out, ws, nbytes)
+            lk.lrkv_decode_step(dims, cache, max_len, rows["k_new"], rows["v_new"], zk_new, zv_new, dev["q"], B_k,
+                                B_v, p if w.r else None, out, ws, nbytes)
             torch.cuda.synchronize()
             words = ws[lk.lrkv_decode_step_sync_offset(dims, max_len) // 4:].view(torch.int32)
             assert int(words[1]) == 0 and int(words.abs().sum()) == 0, "step counters not back at zero"
         else:
             nbytes = lk.lrkv_decode_workspace_bytes(dims, max_len)
             ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device="cuda")
-            lk.lrkv_append_absorb(dims, cache, rows["k_new"], rows["v_new"], rows["zk_new"], rows["zv_new"], dev["q"],
-                                  dev["B_k"], p)
-            lk.lrkv_decode(dims, cache, max_len, dev["q"], p, dev["B_v"], out, ws, nbytes)
+            lk.lrkv_append_absorb(dims, cache, rows["k_new"], rows["v_new"], zk_new, zv_new, dev["q"], B_k,
+                                  p if w.r else None)
+            lk.lrkv_decode(dims, cache, max_len, dev["q"], p if w.r else None, B_v, out, ws, nbytes)
             torch.cuda.synchronize()
         outs.append(out)
         ps.append(p)
@@ -167,7 +169,7 @@ def test_fused_step_full_size(name):
     assert torch.equal(dev["seq_lens"], twin["seq_lens"])
     assert torch.equal(_bits(outs[0]), _bits(outs[1])), "fused step and separate calls differ"
     assert torch.equal(_bits(ps[0]), _bits(ps[1]))
-    for k in ("k_shared", "v_shared", "z_k", "z_v"):
+    for k in ("k_shared", "v_shared", "z_k", "z_v") if w.r else ("k_shared", "v_shared"):
         for b in range(w.batch):
             n = int(lens[b])
             assert torch.equal(_bits(dev[k][b, n]), _bits(twin[k][b, n])), f"appended {k} row of sequence {b}"

@@ -2,7 +2,8 @@
 separate calls lrkv_append_absorb then lrkv_decode, through the C ABI: p, the outputs, the cache rows and the
 lengths must be bit for bit the same after every step of several in a row, and the step's counter words must be
 back at zero after every call (they hand work on between the launch's workgroups and are cleared by its last
-workgroup).  The separate calls are checked against the reference in test_gpu_decode.py and its neighbours; one
+workgroup).  On the fp32 rank-0 kernel the split pass appends the token and grows the lengths, and the merge
+kernel follows.  The separate calls are checked against the reference in test_gpu_decode.py and its neighbours; one
 case here also checks the fused step against the reference directly.  Shapes cover the fused path (bf16
 matrix-core shapes: d_h 64 and 128, r 0 to 64, one and two waves per SIMD, one and four merge groups), a full
 sequence, an empty one, a negative length, appends past max_len (rows written but not seen), and shapes that run
@@ -38,7 +39,7 @@ CASES = [  # (dtype, batch, H, d_h, r, lengths, L_cap, max_len)
     ("bf16", 4, 18, 128, 55, [300, 33, 1, 95], 320, 320),  # model-table shape (r = 55: the two calls)
     ("bf16", 3, 32, 128, 32, [100, 500, 64], 512, 128),    # sequence 1 grows past max_len: row written, not seen
     ("bf16", 2, 16, 64, 16, [3000, 2900], 3072, 3072),     # long sequences: four merge groups
-    ("f32", 2, 8, 64, 0, [10, 63], 64, 64),                # fp32: the two calls
+    ("f32", 2, 8, 64, 0, [10, 63], 64, 64),                # fp32 rank 0: split pass with the append, merge
     ("bf16", 2, 8, 64, 12, [5, 40], 64, 64),               # r = 12: the two calls
 ]
 
@@ -149,6 +150,37 @@ def test_step_many_merges_runs_the_calls():
     case = _ragged_case(batch=40, H=32)
     say("[case] decode step, batch 40 x 32 heads (the two calls)")
     _check_equal(case, steps=2)
+
+
+F32_FUSED = [  # (dtype, batch, H, d_h, r, lengths, L_cap, max_len): fp32 rank 0, fused on its matrix-core kernel
+    ("f32", 16, 8, 64, 0, [0, 1, 31, 32, 33, 255, 256, 100, 64, 63, 65, 200, 2, 128, 129, 17], 256, 256),
+    ("f32", 20, 32, 128, 0, [700, 33, 0, 95, 1000, 1023, 1024, 5, 640, 641, 639, 300, 1, 2, 900, 960, 961, 31,
+                             32, 699], 1024, 700),   # max_len below L_cap: rows written past it, not seen
+    ("f32", 17, 16, 128, 0, [2048 - k for k in range(17)], 2048, 2048),  # full and nearly full sequences
+    ("f32", 3, 32, 128, 0, [4000, 4095, 17], 4096, 4096),  # many splits a sequence: four merge groups
+]
+
+
+@pytest.mark.parametrize("case", F32_FUSED, ids=lambda c: f"f32_B{c[1]}_H{c[2]}_d{c[3]}_cap{c[6]}_m{c[7]}")
+def test_step_fp32_rank0_fused(case):
+    w, _, _, max_len = _setup(case)
+    assert lk.lrkv_decode_step_fused(dims_of(w), max_len), "expected the fused launch"
+    say(f"[case] fp32 rank-0 fused step {case[:5]} L_cap {case[6]} max_len {case[7]}")
+    _check_equal(case)
+
+
+def test_step_fp32_rank0_ragged_batch():
+    """64 ragged sequences, 32 heads (the fp32 rank-0 workload's shape at shorter lengths), and one negative
+    length: fused, bit for bit the two calls."""
+    rng = np.random.default_rng(78)
+    lens = rng.integers(1, 2500, size=64).astype(np.int32).tolist()
+    case = ("f32", 64, 32, 128, 0, lens, 2528, 2528)
+    w, _, _, max_len = _setup(case)
+    assert lk.lrkv_decode_step_fused(dims_of(w), max_len), "expected the fused launch"
+    say("[case] fp32 rank-0 fused step, 64 ragged sequences, sequence 5 negative")
+    steps = _check_equal(case, steps=2, negative=5)
+    assert steps[-1]["seq_lens"].cpu().tolist()[5] == -1
+    assert float(steps[-1]["out"][5].abs().max()) == 0.0
 
 
 def test_step_negative_length():
