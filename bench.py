@@ -16,10 +16,13 @@ steps), achieved HBM bandwidth, the roofline of the dominant kernel (the
 split pass, timed live with HIP events on the launch stream) and the CPU
 reference timed on the host on a bounded sample of the same workload.
 
-The steps are timed twice from the same starting lengths: once as they are
-(the step time and the metric), then with a HIP event pair around each decode
-launch (the kernel's own duration).  The events cost 3-6 us per step, so they
-are kept out of the step time.
+The steps are timed three times from the same starting lengths: once as they
+are (the step time and the metric), then with a HIP event pair around each
+decode call (the split pass's own duration), then with one event at every step
+boundary (per-step latency quantiles).  Event pairs cost 3-6 us per step on the
+bf16 kernels and about 20 us on the fp32 rank-0 step, so they are kept out of
+the step time; where the decode call is a fused step (the whole step), its
+duration for the roofline comes from the step-boundary pass.
 """
 from __future__ import annotations
 
@@ -608,7 +611,12 @@ def main():
         new_row_bytes = w.batch * 2 * (w.d_h + w.H * w.r) * s_bytes
         split_bytes = (sum(cache_bytes_per_step) / K + q_bytes + basis_bytes + out_bytes + 2 * new_row_bytes
                        + 2 * p_bytes)
-    split_avg_ms = sum(split_ms) / len(split_ms)
+    split_avg_ms = pair_avg_ms = sum(split_ms) / len(split_ms)
+    if fused:
+        # the fused call is the whole step: its duration comes from the pass with one event at every step
+        # boundary; an event pair around each call perturbs it (2-3 us a step on the bf16 step, about 20 us on
+        # the fp32 rank-0 one, whose two launches the pair separates from the rest of the stream)
+        split_avg_ms = sum(step_us) / len(step_us) / n_layers / 1e3
     split_gbps = split_bytes / (split_avg_ms / 1e3) / 1e9
     step_gbps = step_bytes / (total_ms / K / 1e3) / 1e9
     flops_mfma = 2 * w.d_h * (token_heads / K / n_layers)  # shared-key score tile per split launch
@@ -694,8 +702,11 @@ def main():
                       "fused decode step (lrkv_decode_step: append, absorb, split pass and merge in one launch)")
                      if fused else "split pass (lrkv_decode_partial)",
                      "algorithmic_bytes_per_launch": split_bytes, "avg_launch_us": split_avg_ms * 1e3,
-                     "timing": f"HIP events around each of the {K * n_layers} decode launches of a second pass "
-                               "over the same steps (the step time comes from a pass without them)",
+                     "timing": (f"HIP events at the {K} step boundaries of a third pass over the same steps, "
+                                f"{n_layers} fused call(s) per step (event pairs around each call, a second pass: "
+                                f"{pair_avg_ms * 1e3:.1f} us per call)") if fused else
+                               (f"HIP events around each of the {K * n_layers} decode launches of a second pass "
+                                "over the same steps (the step time comes from a pass without them)"),
                      "stream_read_gbps": stream_gbps,
                      "frac_of_stream_read": (split_gbps / stream_gbps) if stream_gbps else None},
         "mfma_util_shared_score": mfma_util,
