@@ -1,6 +1,7 @@
 """GPU parity over seeded random shapes and lengths: single-token decode, multi-token decode and the rotary
 variant, bf16 and fp32, against the fp64 reference through the C ABI; and the fused decode step on random
-shapes, bit for bit against the separate calls (append and absorb, then decode) over two steps in a row; the
+shapes, bit for bit against the separate calls (append and absorb, then decode) over two steps in a row (and a set
+of fp32 rank-0 steps, whose split pass appends the token and grows the lengths before the merge); the
 paged cache (random page sizes, pool permutations with NaN spare pages) and the normalised variant on random
 shapes, checked as in test_gpu_paged.py and test_gpu_normed.py.  Lengths mix random values with the tile and block edges (0, 1, 31-33, 63-65, 127-129, 255-257).  Metric and
 tolerances as in test_gpu_decode.py.  LRKV_SWEEP_CASES and LRKV_SWEEP_SEED (read when the module is collected)
@@ -187,3 +188,31 @@ def test_random_paged_decode(case):
 def test_random_normed_decode(case):
     from test_gpu_normed import test_decode_normed_matches_reference
     test_decode_normed_matches_reference(case)
+
+
+def _f32_step_cases(seed=SEED + 4, n=max(1, N_CASES // 6)):
+    """fp32 rank-0 decode steps on the fp32 matrix-core kernel: (dtype, batch, H, d_h, r, lengths, L_cap,
+    max_len) with batches from one sequence to 70, lengths at the block and tile edges, empty and full."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H = int(rng.choice([8, 16, 32]))
+        d_h = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 71))
+        L_cap = 32 * int(rng.integers(2, 129))
+        lens = [int(rng.choice(EDGE)) if rng.random() < 0.4 else int(rng.integers(0, L_cap + 1)) for _ in range(B)]
+        lens = [min(x, L_cap) for x in lens]
+        max_len = L_cap if rng.random() < 0.7 else int(rng.integers(1, L_cap + 1))
+        out.append(("f32", B, H, d_h, 0, tuple(lens), L_cap, max_len))
+    return out
+
+
+@pytest.mark.parametrize("case", _f32_step_cases(),
+                         ids=lambda c: f"f32step_B{c[1]}_H{c[2]}_d{c[3]}_cap{c[6]}_max{c[7]}")
+def test_random_fp32_rank0_step(case):
+    from test_gpu_step import _check_equal
+    dtype, B, H, d_h, r, lens, L_cap, max_len = case
+    dims = lk.make_dims(B, H, d_h, r, L_cap, lk.LRKV_F32)
+    assert lk.lrkv_decode_step_fused(dims, max_len), "the fp32 rank-0 step folds the append into its split pass"
+    say(f"[case] fp32 rank-0 step B={B} H={H} d_h={d_h} L_cap={L_cap} max_len={max_len}")
+    _check_equal((dtype, B, H, d_h, r, list(lens), L_cap, max_len), steps=2)
