@@ -232,9 +232,10 @@ lrkv_status lrkv_decode_partial(const lrkv_dims* dims, const lrkv_cache* cache, 
 lrkv_status lrkv_decode_merge(const lrkv_dims* dims, const int32_t* seq_lens, int32_t max_len, const void* B_v,
                               float* out, const void* workspace, size_t workspace_bytes, void* stream);
 
-/* A whole decode step in one launch: lrkv_append_absorb(dims, cache, k_new,
- * v_new, zk_new, zv_new, q, B_k, p) followed by lrkv_decode(dims, cache,
- * max_len, q, p, B_v, out), with the same arguments, layouts and results, bit
+/* A whole decode step in the fewest launches: lrkv_append_absorb(dims,
+ * cache, k_new, v_new, zk_new, zv_new, q, B_k, p) followed by
+ * lrkv_decode(dims, cache, max_len, q, p, B_v, out), with the same
+ * arguments, layouts and results, bit
  * for bit (p and out written, the token appended, seq_lens advanced) -- the
  * per-token work of Algorithms 1 and 2 and the fused online-softmax decode of
  * the review's sec. 3 (reading notes secs. 2.3-2.4, Eqs. (6)-(7)).  On the bf16
